@@ -1,0 +1,245 @@
+/*
+ * sq_oracle.c -- plain CPU reference for the SmoothQuant W8A8 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY: used by tests/, by the smoke check and by the
+ * CPU-baseline leg of the benchmark; never by the product path. It shares no
+ * code with the GPU library. Build: gcc -O2 -ffp-contract=off -fopenmp
+ * (see oracle/build.py). Every outer loop parallelised with OpenMP is over
+ * independent rows or columns, so results do not depend on the thread count.
+ *
+ * Step numbering (O1..O11) and citations are in sq_oracle.h.
+ */
+#include "sq_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+/* The pages' only guard constant: the smoothing factor is clamped to at
+ * least 1e-5 (tbr8.org PyTorch example). It is applied to the statistics
+ * and to the per-row weight maximum so no scale can be zero. */
+#define SQO_FLOOR 1e-5f
+#define SQO_QMAX 127.0f
+
+int sqo_num_threads(void) { return omp_get_max_threads(); }
+
+static float bf16_bits_to_float(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint16_t float_to_bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+/* element i of a float buffer of the given type, widened exactly to fp32 */
+static float elem(const void* p, int type, int64_t i) {
+    if (type == SQO_BF16) return bf16_bits_to_float(((const uint16_t*)p)[i]);
+    return ((const float*)p)[i];
+}
+
+/* symmetric int8 code of an already scaled value (kwkr.cn blog §1.2:
+ * x_q = round(x/s)); round half to even, clamp to [-127, 127] */
+static int8_t quantize_scaled(float v) {
+    float r = rintf(v); /* default rounding mode: nearest, ties to even */
+    if (r > SQO_QMAX) r = SQO_QMAX;
+    if (r < -SQO_QMAX) r = -SQO_QMAX;
+    return (int8_t)r;
+}
+
+/* O1 (activations) and O2 (weights): per-input-channel max |.| over rows.
+ * kwkr.cn blog §3.1; ADR-010 add_batch keeps a running max per channel. */
+void sqo_calib_absmax(const void* x, int xtype, int64_t rows, int64_t k,
+                      float* absmax, int accumulate) {
+    int64_t j;
+#pragma omp parallel for schedule(static)
+    for (j = 0; j < k; ++j) {
+        float mx = accumulate ? absmax[j] : 0.0f;
+        for (int64_t t = 0; t < rows; ++t) {
+            float v = fabsf(elem(x, xtype, t * k + j));
+            if (v > mx) mx = v;
+        }
+        absmax[j] = mx;
+    }
+}
+
+/* O6: closed-form per-tensor activation scale, ADR-010 "Key design" item 1:
+ * max over channels of act_max[j]/s_j, divided by 127. Division by s_j is
+ * taken as the product with inv_s[j] (kwkr.cn blog §2.3 allows either). */
+float sqo_act_scale(const float* act_max, const float* inv_s, int64_t k) {
+    float mx = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+        float a = act_max[j] > SQO_FLOOR ? act_max[j] : SQO_FLOOR;
+        float v = a * inv_s[j];
+        if (v > mx) mx = v;
+    }
+    return mx / SQO_QMAX;
+}
+
+/* O3-O6: s_j = max|X_j|^alpha / max|W_j|^(1-alpha) (kwkr.cn blog §2.2),
+ * evaluated in fp64 and rounded once to fp32; inv_s = fl(1/s). */
+void sqo_smooth_factors(const float* act_max, const float* w_max, int64_t k,
+                        double alpha, float* s, float* inv_s, float* act_scale) {
+    for (int64_t j = 0; j < k; ++j) {
+        float a = act_max[j] > SQO_FLOOR ? act_max[j] : SQO_FLOOR;
+        float w = w_max[j] > SQO_FLOOR ? w_max[j] : SQO_FLOOR;
+        double num = pow((double)a, alpha);
+        double den = pow((double)w, 1.0 - alpha);
+        s[j] = (float)(num / den);
+        inv_s[j] = 1.0f / s[j];
+    }
+    *act_scale = sqo_act_scale(act_max, inv_s, k);
+}
+
+/* O7: W' = W*diag(s) offline (kwkr.cn blog §3.2), then symmetric int8 with
+ * one scale per output row (ADR-010 "Context" item 3; kwkr.cn blog §3.3). */
+void sqo_quant_weight(const void* w, int wtype, int64_t n, int64_t k,
+                      const float* s, int8_t* wq, float* w_scale) {
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < n; ++r) {
+        float* row = (float*)malloc((size_t)k * sizeof(float));
+        float mx = 0.0f;
+        for (int64_t j = 0; j < k; ++j) {
+            row[j] = elem(w, wtype, r * k + j) * s[j];
+            float v = fabsf(row[j]);
+            if (v > mx) mx = v;
+        }
+        if (mx < SQO_FLOOR) mx = SQO_FLOOR;
+        float ws = mx / SQO_QMAX;
+        float inv_ws = 1.0f / ws;
+        for (int64_t j = 0; j < k; ++j) wq[r * k + j] = quantize_scaled(row[j] * inv_ws);
+        w_scale[r] = ws;
+        free(row);
+    }
+}
+
+/* O8: runtime x/s (as x*inv_s) strictly before the per-tensor quantizer
+ * (kwkr.cn blog §3.2 and §5.2; ADR-010 "Key design" items 4-5). */
+void sqo_quant_act(const void* x, int xtype, int64_t m, int64_t k,
+                   const float* inv_s, float act_scale, int8_t* xq) {
+    float inv_a = 1.0f / act_scale;
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < m; ++r) {
+        for (int64_t j = 0; j < k; ++j) {
+            float smoothed = elem(x, xtype, r * k + j) * inv_s[j];
+            xq[r * k + j] = quantize_scaled(smoothed * inv_a);
+        }
+    }
+}
+
+/* O9: the int8 x int8 -> int32 product (pwwt.cn §3.1 kernel signature). */
+void sqo_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n,
+                  int64_t k, int32_t* acc) {
+    int64_t idx;
+#pragma omp parallel for schedule(static)
+    for (idx = 0; idx < m * n; ++idx) {
+        int64_t r = idx / n, c = idx % n;
+        int64_t sum = 0;
+        for (int64_t j = 0; j < k; ++j)
+            sum += (int64_t)xq[r * k + j] * (int64_t)wq[c * k + j];
+        if (sum > INT32_MAX || sum < INT32_MIN) abort(); /* k too large */
+        acc[idx] = (int32_t)sum;
+    }
+}
+
+/* O10: dequant with the two scales merged first (pwwt.cn §3.1 stub: merge the
+ * scale multiplications), then one multiply of the converted accumulator. */
+void sqo_dequant(const int32_t* acc, int64_t m, int64_t n, float act_scale,
+                 const float* w_scale, int ytype, void* y) {
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < m; ++r) {
+        for (int64_t c = 0; c < n; ++c) {
+            float scale = act_scale * w_scale[c];
+            float v = (float)acc[r * n + c] * scale;
+            if (ytype == SQO_BF16)
+                ((uint16_t*)y)[r * n + c] = float_to_bf16_rne(v);
+            else
+                ((float*)y)[r * n + c] = v;
+        }
+    }
+}
+
+void sqo_ref_gemm(const void* x, int xtype, const void* w, int wtype,
+                  int64_t m, int64_t n, int64_t k, float* yref) {
+    int64_t idx;
+#pragma omp parallel for schedule(static)
+    for (idx = 0; idx < m * n; ++idx) {
+        int64_t r = idx / n, c = idx % n;
+        double sum = 0.0;
+        for (int64_t j = 0; j < k; ++j)
+            sum += (double)elem(x, xtype, r * k + j) * (double)elem(w, wtype, c * k + j);
+        yref[idx] = (float)sum;
+    }
+}
+
+double sqo_sse(const float* y, const float* yref, int64_t m, int64_t n) {
+    double* row_sse = (double*)malloc((size_t)(m > 0 ? m : 1) * sizeof(double));
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < m; ++r) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < n; ++c) {
+            double d = (double)y[r * n + c] - (double)yref[r * n + c];
+            acc += d * d;
+        }
+        row_sse[r] = acc;
+    }
+    double total = 0.0;
+    for (r = 0; r < m; ++r) total += row_sse[r];
+    free(row_sse);
+    return total;
+}
+
+/* O11: per-layer alpha grid search with the exact final-layer quantization
+ * math (ADR-010 "Key design" item 2). act_max is taken over all batches; the
+ * error is the mean squared difference against the reference product on the
+ * same batches; ties go to the first alpha in grid order. */
+int sqo_alpha_search(const void* const* x_batches, int xtype, int nb,
+                     int64_t rows, int64_t k, const void* w, int wtype,
+                     int64_t n, const double* alphas, int na, double* mse) {
+    float* act_max = (float*)calloc((size_t)k, sizeof(float));
+    float* w_max = (float*)calloc((size_t)k, sizeof(float));
+    float* s = (float*)malloc((size_t)k * sizeof(float));
+    float* inv_s = (float*)malloc((size_t)k * sizeof(float));
+    int8_t* wq = (int8_t*)malloc((size_t)(n * k));
+    float* w_scale = (float*)malloc((size_t)n * sizeof(float));
+    int8_t* xq = (int8_t*)malloc((size_t)(rows * k));
+    int32_t* acc = (int32_t*)malloc((size_t)(rows * n) * sizeof(int32_t));
+    float* y = (float*)malloc((size_t)(rows * n) * sizeof(float));
+    float* yref = (float*)malloc((size_t)(nb * rows * n) * sizeof(float));
+
+    for (int b = 0; b < nb; ++b) sqo_calib_absmax(x_batches[b], xtype, rows, k, act_max, 1);
+    sqo_calib_absmax(w, wtype, n, k, w_max, 0);
+    for (int b = 0; b < nb; ++b)
+        sqo_ref_gemm(x_batches[b], xtype, w, wtype, rows, n, k, yref + (int64_t)b * rows * n);
+
+    int best = 0;
+    for (int i = 0; i < na; ++i) {
+        float act_scale;
+        sqo_smooth_factors(act_max, w_max, k, alphas[i], s, inv_s, &act_scale);
+        sqo_quant_weight(w, wtype, n, k, s, wq, w_scale);
+        double sse = 0.0;
+        for (int b = 0; b < nb; ++b) {
+            sqo_quant_act(x_batches[b], xtype, rows, k, inv_s, act_scale, xq);
+            sqo_gemm_i32(xq, wq, rows, n, k, acc);
+            sqo_dequant(acc, rows, n, act_scale, w_scale, SQO_F32, y);
+            sse += sqo_sse(y, yref + (int64_t)b * rows * n, rows, n);
+        }
+        mse[i] = sse / ((double)nb * (double)rows * (double)n);
+        if (mse[i] < mse[best]) best = i;
+    }
+
+    free(act_max); free(w_max); free(s); free(inv_s); free(wq); free(w_scale);
+    free(xq); free(acc); free(y); free(yref);
+    return best;
+}

@@ -1,0 +1,91 @@
+/*
+ * sq_oracle.h -- plain CPU reference for the SmoothQuant W8A8 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link or
+ * call this; it exists so the GPU library can be checked against a slow,
+ * obviously correct definition written from the pages' text. It shares no
+ * code, header, table or constant with the GPU library.
+ *
+ * Sources (cited by page and section; "kwkr.cn blog" is the Chinese
+ * engineering write-up on SmoothQuant W8A8 at kwkr.cn/news/621929, "ADR-010"
+ * is "010. SmoothQuant Integration" on blog.yoooo.fun, "pwwt.cn" is
+ * "SmoothQuant技术解析：LLM模型INT8无损量化实践", "tbr8.org" is the page on
+ * activation outliers and SmoothQuant with the PyTorch example):
+ *   - calibration statistics:      kwkr.cn blog §3.1; ADR-010 "Layer 2" (add_batch)
+ *   - smoothing factor s_j:        kwkr.cn blog §2.2; ADR-010 "Context" item 1
+ *   - weight fold + per-row int8:  kwkr.cn blog §3.2, §3.3; ADR-010 "Context" items 2-3
+ *   - activation x/s + per-tensor: ADR-010 "Key design" items 1, 4, 5; kwkr.cn blog §3.2
+ *   - symmetric quantizer:         kwkr.cn blog §1.2
+ *   - int8 GEMM + merged scales:   pwwt.cn §3.1 (quantized_matmul_kernel stub)
+ *   - alpha grid search:           ADR-010 "Key design" item 2
+ *
+ * Conventions: X[m,k] and W[n,k] are row-major with k contiguous; column j is
+ * input channel j. Every floating-point step is one IEEE fp32 operation with
+ * round-to-nearest-even and no fused multiply-add (built with
+ * -ffp-contract=off), except where fp64 is stated. bf16 inputs are widened to
+ * fp32 exactly.
+ *
+ * Parity pins: every function here is pinned by tests/test_oracle_pins.py.
+ */
+#ifndef SQ_ORACLE_H
+#define SQ_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types of floating-point buffers */
+enum { SQO_F32 = 0, SQO_BF16 = 1 };
+
+/* Number of OpenMP threads the oracle's outer loops use. */
+int sqo_num_threads(void);
+
+/* O1/O2: absmax[j] = max(absmax_in[j] if accumulate else 0, max_t |x[t,j]|). */
+void sqo_calib_absmax(const void* x, int xtype, int64_t rows, int64_t k,
+                      float* absmax, int accumulate);
+
+/* O6 alone: mx = max_j fl(max(act_max[j],1e-5) * inv_s[j]); returns fl(mx/127). */
+float sqo_act_scale(const float* act_max, const float* inv_s, int64_t k);
+
+/* O3-O6: s, inv_s (length k) and the per-tensor activation scale. */
+void sqo_smooth_factors(const float* act_max, const float* w_max, int64_t k,
+                        double alpha, float* s, float* inv_s, float* act_scale);
+
+/* O7: W' = W*diag(s) (per column j), per-row symmetric int8. */
+void sqo_quant_weight(const void* w, int wtype, int64_t n, int64_t k,
+                      const float* s, int8_t* wq, float* w_scale);
+
+/* O8: xq = clamp(rne(fl(fl(x*inv_s[j]) * fl(1/act_scale))), -127, 127). */
+void sqo_quant_act(const void* x, int xtype, int64_t m, int64_t k,
+                   const float* inv_s, float act_scale, int8_t* xq);
+
+/* O9: acc[m,n] = sum_j xq[m,j]*wq[n,j], exact in integers. */
+void sqo_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n,
+                  int64_t k, int32_t* acc);
+
+/* O10: y[m,n] = fl(fl(float(acc)) * fl(act_scale*w_scale[n])); ytype F32 or
+ * BF16 (bf16 = round-to-nearest-even of the fp32 value). */
+void sqo_dequant(const int32_t* acc, int64_t m, int64_t n, float act_scale,
+                 const float* w_scale, int ytype, void* y);
+
+/* Reference product: yref[m,n] = (float) sum_j (double)x[m,j]*(double)w[n,j],
+ * summed in ascending j. */
+void sqo_ref_gemm(const void* x, int xtype, const void* w, int wtype,
+                  int64_t m, int64_t n, int64_t k, float* yref);
+
+/* Squared error: sum over (m,n) of ((double)y - (double)yref)^2, rows summed
+ * in ascending order. */
+double sqo_sse(const float* y, const float* yref, int64_t m, int64_t n);
+
+/* O11: alpha grid search. x_batches: nb host pointers, each [rows,k]. Writes
+ * mse[na] and returns the first index attaining the minimum. */
+int sqo_alpha_search(const void* const* x_batches, int xtype, int nb,
+                     int64_t rows, int64_t k, const void* w, int wtype,
+                     int64_t n, const double* alphas, int na, double* mse);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,66 @@
+"""CPU: the oracle against its pins, and planted mistakes against the pins.
+
+Each mutant below is a plausible slip in the oracle (a dropped term, an
+inverted direction, a wrong rounding mode, a wrong index...). The source is
+patched in a temporary directory, compiled, loaded, and every pin is run; at
+least one pin must fail for each mutant, or the pins would not be able to
+catch that mistake in the real oracle.
+"""
+import os
+import subprocess
+
+import pytest
+
+from oracle import oracle as oracle_mod
+from tests import oracle_pins
+
+ORACLE = oracle_mod.Oracle()
+
+
+@pytest.mark.parametrize("pin", oracle_pins.PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(ORACLE)
+
+
+MUTANTS = {
+    "inverted_direction": ("s[j] = (float)(num / den);", "s[j] = (float)(den / num);"),
+    "dropped_weight_term": ("double den = pow((double)w, 1.0 - alpha);", "double den = 1.0;"),
+    "round_half_away": ("float r = rintf(v);", "float r = roundf(v);"),
+    "truncate": ("float r = rintf(v);", "float r = truncf(v);"),
+    "clamp_minus_128": ("if (r < -SQO_QMAX) r = -SQO_QMAX;", "if (r < -128.0f) r = -128.0f;"),
+    "max_without_abs": ("float v = fabsf(elem(x, xtype, t * k + j));", "float v = elem(x, xtype, t * k + j);"),
+    "act_scale_over_128": ("return mx / SQO_QMAX;", "return mx / 128.0f;"),
+    "act_scale_ignores_s": ("float v = a * inv_s[j];", "float v = a;"),
+    "weight_divided_by_s": ("row[j] = elem(w, wtype, r * k + j) * s[j];",
+                            "row[j] = elem(w, wtype, r * k + j) / s[j];"),
+    "act_multiplied_by_s": ("float smoothed = elem(x, xtype, r * k + j) * inv_s[j];",
+                            "float smoothed = elem(x, xtype, r * k + j) / inv_s[j];"),
+    "quantize_before_smoothing": ("xq[r * k + j] = quantize_scaled(smoothed * inv_a);",
+                                  "xq[r * k + j] = quantize_scaled(elem(x, xtype, r * k + j) * inv_a); (void)smoothed;"),
+    "dequant_row_scale": ("float scale = act_scale * w_scale[c];", "float scale = act_scale * w_scale[r % n];"),
+    "gemm_reversed_k": ("(int64_t)wq[c * k + j];", "(int64_t)wq[c * k + (k - 1 - j)];"),
+    "no_row_floor": ("if (mx < SQO_FLOOR) mx = SQO_FLOOR;", ""),
+    "sse_abs": ("acc += d * d;", "acc += fabs(d);"),
+    "argmax_not_argmin": ("if (mse[i] < mse[best]) best = i;", "if (mse[i] > mse[best]) best = i;"),
+    "weight_scale_over_128": ("float ws = mx / SQO_QMAX;", "float ws = mx / 128.0f;"),
+    "ref_gemm_float_accum": ("double sum = 0.0;\n        for (int64_t j = 0; j < k; ++j)\n            sum += (double)elem(x",
+                             "float sum = 0.0f;\n        for (int64_t j = 0; j < k; ++j)\n            sum += (float)elem(x"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle_mod.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    (tmp_path / "sq_oracle.h").write_text(open(os.path.join(oracle_mod.HERE, "sq_oracle.h")).read())
+    (tmp_path / "sq_oracle.c").write_text(src.replace(old, new))
+    lib = oracle_mod.build(str(tmp_path / "sq_oracle.c"), str(tmp_path / f"libmut_{name}.so"))
+    o = oracle_mod.Oracle(oracle_mod.load(lib))
+    failed = []
+    for pin in oracle_pins.PINS:
+        try:
+            pin(o)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches mutant {name}"

@@ -1,0 +1,162 @@
+/*
+ * sq.h -- C ABI of libsq: the SmoothQuant W8A8 linear-layer path on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page and section):
+ *   [kwkr]  the Chinese engineering blog on SmoothQuant W8A8 at kwkr.cn
+ *           (sections 1.2, 2.1-2.3, 3.1-3.3)
+ *   [ADR]   "010. SmoothQuant Integration", blog.yoooo.fun (Context, Key design)
+ *   [pwwt]  "SmoothQuant技术解析：LLM模型INT8无损量化实践", pwwt.cn (§3.1 kernel stub)
+ *   [tbr8]  tbr8.org, activation outliers and SmoothQuant (PyTorch example)
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are row-major with the reduction dimension k contiguous:
+ *     activations X[m,k] (row = token), weights W[n,k] (row = output channel;
+ *     column j = input channel j). The layer computes Y[m,n] = sum_j X[m,j]W[n,j].
+ *   - Every array pointer is a DEVICE pointer unless marked (host). The caller
+ *     owns every buffer; the library allocates nothing and keeps no state
+ *     between calls. Device pointers must be 16-byte aligned.
+ *   - k must be a positive multiple of 64; m, n, rows may be 0 (then nothing is
+ *     launched and SQ_OK is returned; an overwrite of absmax with rows = 0
+ *     writes zeros).
+ *   - Calls are asynchronous on `stream` (0 = the null stream) unless noted.
+ *     Arguments are validated before anything is launched; on any error
+ *     nothing is written. A failed launch returns SQ_ERR_HIP.
+ *   - fp32 arithmetic is IEEE single precision, round-to-nearest-even, with no
+ *     fused multiply-add on the quantization paths. Integer codes are in
+ *     [-127, 127]; rounding of codes is half-to-even.
+ *   - No exception or abort crosses this interface. Functions are reentrant;
+ *     calls on one stream are ordered, calls on different streams that write
+ *     the same buffers race.
+ */
+#ifndef SQ_H
+#define SQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SQ_OK = 0,
+    SQ_ERR_NULL = 1,      /* a required pointer is NULL */
+    SQ_ERR_SHAPE = 2,     /* negative size, k not a positive multiple of 64, size limit exceeded */
+    SQ_ERR_DTYPE = 3,     /* element type not supported for this argument */
+    SQ_ERR_ALPHA = 4,     /* alpha not finite or outside [0, 1] */
+    SQ_ERR_WORKSPACE = 5, /* workspace missing or smaller than sq_alpha_search_workspace reports */
+    SQ_ERR_HIP = 6,       /* a HIP launch or runtime call failed */
+    SQ_ERR_ALIGN = 7      /* a device pointer is not 16-byte aligned */
+} sq_status;
+
+typedef enum { SQ_F32 = 0, SQ_BF16 = 1 } sq_dtype;
+
+/* Largest k accepted by the GEMM: k*127*127 must stay below 2^31 so the
+ * int32 accumulator is exact in any summation order. */
+#define SQ_MAX_GEMM_K 131072
+
+/*
+ * Per-input-channel max |x| (calibration statistic) [kwkr §3.1; ADR Layer 2,
+ * add_batch keeps a running per-channel max-abs]. Also used on the weight
+ * W[n,k] (rows = n) to get max|W_j| over output rows.
+ *   x       [rows, k] of type xt (SQ_F32 or SQ_BF16)
+ *   absmax  [k] fp32, in/out. accumulate = 0: absmax[j] = max_t |x[t,j]|
+ *           (0 when rows = 0); accumulate = 1: absmax[j] = max(absmax[j],
+ *           max_t |x[t,j]|), the running max over calibration batches.
+ * Exact (no rounding). Inputs must be finite.
+ */
+sq_status sq_calib_absmax(const void* x, sq_dtype xt, int64_t rows, int64_t k,
+                          float* absmax, int accumulate, hipStream_t stream);
+
+/*
+ * Smoothing factors [kwkr §2.2; ADR Context item 1] and the closed-form
+ * per-tensor activation scale [ADR Key design item 1]:
+ *   a_j = max(act_max[j], 1e-5), w_j = max(w_max[j], 1e-5)   (floor as in [tbr8])
+ *   s[j]      = fp32( a_j^alpha / w_j^(1-alpha) )   (pow and quotient in fp64)
+ *   inv_s[j]  = fp32(1 / s[j])                       [kwkr §2.3: multiply by 1/s]
+ *   act_scale = fp32( max_j fp32(a_j * inv_s[j]) / 127 )   (one device float)
+ *   act_max, w_max  [k] fp32 input; s, inv_s [k] fp32 output; act_scale [1].
+ *   alpha must be finite and in [0, 1] (SQ_ERR_ALPHA otherwise) [ADR Key design 3].
+ */
+sq_status sq_smooth_factors(const float* act_max, const float* w_max, int64_t k,
+                            float alpha, float* s, float* inv_s, float* act_scale,
+                            hipStream_t stream);
+
+/*
+ * Offline weight transform [kwkr §3.2: W' = W diag(s)] and symmetric int8
+ * with one scale per output row [ADR Context item 3; kwkr §3.3]:
+ *   W'[r,j]    = fp32(W[r,j] * s[j])
+ *   w_scale[r] = fp32( max(max_j |W'[r,j]|, 1e-5) / 127 )
+ *   wq[r,j]    = clamp(rne(fp32(W'[r,j] * fp32(1/w_scale[r]))), -127, 127)
+ *   w [n,k] of type wt; s [k] fp32; wq [n,k] int8 out; w_scale [n] fp32 out.
+ */
+sq_status sq_quant_weight(const void* w, sq_dtype wt, int64_t n, int64_t k,
+                          const float* s, int8_t* wq, float* w_scale,
+                          hipStream_t stream);
+
+/*
+ * Runtime activation path: scale by 1/s strictly before quantizing
+ * [kwkr §3.2, §5.2; ADR Key design items 4-5], symmetric per-tensor int8:
+ *   xq[r,j] = clamp(rne(fp32(fp32(x[r,j]*inv_s[j]) * fp32(1/act_scale[0]))), -127, 127)
+ *   x [m,k] of type xt; inv_s [k] fp32; act_scale [1] fp32 (device, so the
+ *   forward needs no host synchronisation); xq [m,k] int8 out.
+ * Values beyond the calibrated range saturate at +-127.
+ */
+sq_status sq_smooth_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k,
+                              const float* inv_s, const float* act_scale,
+                              int8_t* xq, hipStream_t stream);
+
+/*
+ * INT8 x INT8 -> INT32 product with the dequantization fused into the
+ * epilogue, scales merged before the multiply [pwwt §3.1 kernel stub]:
+ *   acc[r,c] = sum_j xq[r,j] * wq[c,j]            (int32, exact)
+ *   y[r,c]   = fp32( fp32(acc[r,c]) * fp32(act_scale[0] * w_scale[c]) )
+ *   xq [m,k] int8; wq [n,k] int8; act_scale [1]; w_scale [n] fp32;
+ *   y [m,n] of type yt (SQ_F32, or SQ_BF16 = round-to-nearest-even of the
+ *   fp32 value); acc_out [m,n] int32 or NULL (written when non-NULL).
+ *   k <= SQ_MAX_GEMM_K.
+ */
+sq_status sq_w8a8_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n,
+                       int64_t k, const float* act_scale, const float* w_scale,
+                       void* y, sq_dtype yt, int32_t* acc_out, hipStream_t stream);
+
+/*
+ * Workspace bytes needed by sq_alpha_search for the given problem (host
+ * output *bytes). Pure host computation.
+ */
+sq_status sq_alpha_search_workspace(int n_batches, int64_t rows_per_batch,
+                                    int64_t n, int64_t k, int n_alphas,
+                                    size_t* bytes);
+
+/*
+ * Per-layer alpha grid search [ADR Key design item 2]: for each alpha in
+ * alphas (host array, e.g. {0.25, 0.5, 0.75, 1.0}) run the full layer --
+ * act_max over all batches, sq_smooth_factors, sq_quant_weight,
+ * sq_smooth_quant_act, sq_w8a8_gemm with fp32 output -- on the kept
+ * calibration batches, and score it by the mean squared error against the
+ * unquantized product X W^T computed in fp32 (bf16 inputs: exact products,
+ * fp32 accumulation):
+ *   mse[i] = sum_b sum_r sum_c (y - yref)^2 / (n_batches * rows_per_batch * n)
+ *   (squares and sums in fp64); *best = first index attaining the minimum.
+ *   x_batches  (host) array of n_batches device pointers, each [rows_per_batch, k] of type xt
+ *   w          [n, k] of type wt
+ *   workspace  device buffer of at least sq_alpha_search_workspace(...) bytes
+ *   mse        (host) [n_alphas] fp64 out; best (host) out.
+ * Synchronises `stream` before returning (the results are on the host).
+ * 1 <= n_alphas <= 16; every alpha must satisfy the sq_smooth_factors rule.
+ */
+sq_status sq_alpha_search(const void* const* x_batches, sq_dtype xt, int n_batches,
+                          int64_t rows_per_batch, int64_t k, const void* w,
+                          sq_dtype wt, int64_t n, const float* alphas, int n_alphas,
+                          void* workspace, size_t workspace_bytes, double* mse,
+                          int* best, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* sq_status_string(sq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SQ_H */

@@ -1,0 +1,163 @@
+"""Thin Python binding over libsq's C ABI (include/sq.h).
+
+Argument marshalling only: each function takes torch tensors that already
+live on the GPU, checks dtype/contiguity, and passes raw device pointers, the
+shapes and the current HIP stream to the entry point of the same name. Every
+step of the computation runs in the library's HIP kernels. There is no
+fallback: if libsq.so is missing or fails to load, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsq.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "sq.h")
+
+SQ_F32, SQ_BF16 = 0, 1
+STATUS = {0: "SQ_OK", 1: "SQ_ERR_NULL", 2: "SQ_ERR_SHAPE", 3: "SQ_ERR_DTYPE", 4: "SQ_ERR_ALPHA",
+          5: "SQ_ERR_WORKSPACE", 6: "SQ_ERR_HIP", 7: "SQ_ERR_ALIGN"}
+ALPHA_GRID = (0.25, 0.5, 0.75, 1.0)
+
+_lib = None
+_lock = threading.Lock()
+
+
+class SQError(RuntimeError):
+    def __init__(self, name: str, status: int, message: str):
+        super().__init__(f"{name}: {STATUS.get(status, status)} ({message})")
+        self.status = status
+
+
+def declared_functions(header: str = HEADER) -> list[str]:
+    """Names of the functions include/sq.h declares."""
+    text = open(header).read()
+    return sorted(set(re.findall(r"^\s*(?:sq_status|const char\*)\s+(sq_\w+)\s*\(", text, re.M)))
+
+
+def _declare(lib):
+    c = ctypes
+    P, i64, St = c.c_void_p, c.c_int64, c.c_int
+    sigs = {
+        "sq_calib_absmax": [P, c.c_int, i64, i64, P, c.c_int, P],
+        "sq_smooth_factors": [P, P, i64, c.c_float, P, P, P, P],
+        "sq_quant_weight": [P, c.c_int, i64, i64, P, P, P, P],
+        "sq_smooth_quant_act": [P, c.c_int, i64, i64, P, P, P, P],
+        "sq_w8a8_gemm": [P, P, i64, i64, i64, P, P, P, c.c_int, P, P],
+        "sq_alpha_search_workspace": [c.c_int, i64, i64, i64, c.c_int, P],
+        "sq_alpha_search": [P, c.c_int, c.c_int, i64, i64, P, c.c_int, i64, P, c.c_int, P, c.c_size_t, P, P, P],
+    }
+    for name, args in sigs.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = St
+    lib.sq_status_string.argtypes = [c.c_int]
+    lib.sq_status_string.restype = c.c_char_p
+    return lib
+
+
+def load(path: str = LIB_PATH):
+    """Load libsq.so (raises if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+            _lib = _declare(ctypes.CDLL(path))
+    return _lib
+
+
+def _check(name: str, status: int):
+    if status != 0:
+        raise SQError(name, status, load().sq_status_string(status).decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return SQ_F32
+    if t.dtype == torch.bfloat16:
+        return SQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, what: str):
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def sq_calib_absmax(x, absmax, accumulate: bool = False, stream=None):
+    """absmax[j] = max(absmax[j] if accumulate else 0, max_t |x[t, j]|)."""
+    rows, k = x.shape
+    _check("sq_calib_absmax", load().sq_calib_absmax(_dev(x, "x"), _dtype_code(x), rows, k, _dev(absmax, "absmax"),
+                                                     int(bool(accumulate)), _stream(stream)))
+    return absmax
+
+
+def sq_smooth_factors(act_max, w_max, alpha: float, s, inv_s, act_scale, stream=None):
+    k = act_max.shape[0]
+    _check("sq_smooth_factors", load().sq_smooth_factors(_dev(act_max, "act_max"), _dev(w_max, "w_max"), k,
+                                                         float(alpha), _dev(s, "s"), _dev(inv_s, "inv_s"),
+                                                         _dev(act_scale, "act_scale"), _stream(stream)))
+
+
+def sq_quant_weight(w, s, wq, w_scale, stream=None):
+    n, k = w.shape
+    _check("sq_quant_weight", load().sq_quant_weight(_dev(w, "w"), _dtype_code(w), n, k, _dev(s, "s"),
+                                                     _dev(wq, "wq"), _dev(w_scale, "w_scale"), _stream(stream)))
+
+
+def sq_smooth_quant_act(x, inv_s, act_scale, xq, stream=None):
+    m, k = x.shape
+    _check("sq_smooth_quant_act", load().sq_smooth_quant_act(_dev(x, "x"), _dtype_code(x), m, k,
+                                                             _dev(inv_s, "inv_s"), _dev(act_scale, "act_scale"),
+                                                             _dev(xq, "xq"), _stream(stream)))
+
+
+def sq_w8a8_gemm(xq, wq, act_scale, w_scale, y, acc_out=None, stream=None):
+    m, k = xq.shape
+    n = wq.shape[0]
+    acc = _dev(acc_out, "acc_out") if acc_out is not None else ctypes.c_void_p(0)
+    _check("sq_w8a8_gemm", load().sq_w8a8_gemm(_dev(xq, "xq"), _dev(wq, "wq"), m, n, k, _dev(act_scale, "act_scale"),
+                                               _dev(w_scale, "w_scale"), _dev(y, "y"), _dtype_code(y), acc,
+                                               _stream(stream)))
+
+
+def sq_alpha_search_workspace(n_batches: int, rows_per_batch: int, n: int, k: int, n_alphas: int = 4) -> int:
+    out = ctypes.c_size_t(0)
+    _check("sq_alpha_search_workspace",
+           load().sq_alpha_search_workspace(n_batches, rows_per_batch, n, k, n_alphas, ctypes.byref(out)))
+    return out.value
+
+
+def sq_alpha_search(x_batches, w, workspace, alphas=ALPHA_GRID, stream=None):
+    """Returns (mse list, best index). Synchronises the stream."""
+    nb = len(x_batches)
+    rows, k = x_batches[0].shape
+    n = w.shape[0]
+    xt = _dtype_code(x_batches[0])
+    for x in x_batches:
+        if x.shape != (rows, k) or _dtype_code(x) != xt:
+            raise ValueError("all batches must share shape and dtype")
+    ptrs = (ctypes.c_void_p * nb)(*[_dev(x, "x_batches[i]").value for x in x_batches])
+    al = (ctypes.c_float * len(alphas))(*[float(a) for a in alphas])
+    mse = (ctypes.c_double * len(alphas))()
+    best = ctypes.c_int(-1)
+    _check("sq_alpha_search", load().sq_alpha_search(ctypes.cast(ptrs, ctypes.c_void_p), xt, nb, rows, k, _dev(w, "w"),
+                                                     _dtype_code(w), n, ctypes.cast(al, ctypes.c_void_p), len(alphas),
+                                                     _dev(workspace, "workspace"), workspace.numel() *
+                                                     workspace.element_size(), ctypes.cast(mse, ctypes.c_void_p),
+                                                     ctypes.byref(best), _stream(stream)))
+    return list(mse), best.value

@@ -1,0 +1,174 @@
+// calib.hip -- calibration statistics and smoothing factors.
+//
+// absmax: per-input-channel max |x| over the rows of a row-major [rows, k]
+// matrix (the calibration statistic of the kwkr.cn blog §3.1, kept as a
+// running max across batches like ADR-010's add_batch; the same reduction on
+// W[n,k] gives max|W_j| over output rows).
+//
+// The reduction is done on magnitudes as integers: for finite IEEE values
+// |x| ordered as a float equals (bits & ~sign) ordered as an unsigned integer,
+// and bf16 bits widen to fp32 bits by a 16-bit shift, so the maximum is exact
+// and needs no float compare. Each wave reads one row segment of 64 x 16 B
+// (fully coalesced); the four waves of a block take interleaved rows and
+// combine through LDS; one atomicMax per column per block merges blocks.
+#include <algorithm>
+
+#include "sq_device.h"
+#include "sq_kernels.h"
+
+namespace {
+
+using sqd::u32x4;
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kAbsThreads = 256;  // 4 waves
+constexpr int kAbsUnroll = 4;     // rows in flight per wave
+
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+    u16x2 va = __builtin_bit_cast(u16x2, a), vb = __builtin_bit_cast(u16x2, b);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(va, vb));
+}
+
+// per-word running maximum of magnitudes for one 16-byte vector
+template <int EB>
+__device__ __forceinline__ void acc_mag(u32x4& m, const u32x4& v) {
+    if constexpr (EB == 2) {
+        m.x = max_u16x2(m.x, v.x & 0x7fff7fffu);
+        m.y = max_u16x2(m.y, v.y & 0x7fff7fffu);
+        m.z = max_u16x2(m.z, v.z & 0x7fff7fffu);
+        m.w = max_u16x2(m.w, v.w & 0x7fff7fffu);
+    } else {
+        m.x = max(m.x, v.x & 0x7fffffffu);
+        m.y = max(m.y, v.y & 0x7fffffffu);
+        m.z = max(m.z, v.z & 0x7fffffffu);
+        m.w = max(m.w, v.w & 0x7fffffffu);
+    }
+}
+
+template <int EB>
+__global__ __launch_bounds__(kAbsThreads) void absmax_kernel(const u32x4* __restrict__ x, int64_t rows,
+                                                             int64_t kvec, int64_t rows_per_block,
+                                                             unsigned* __restrict__ out_bits) {
+    __shared__ u32x4 part[kAbsThreads];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t v = (int64_t)blockIdx.x * 64 + lane;  // 16-byte column vector
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+    const int64_t r1 = min(rows, r0 + rows_per_block);
+    u32x4 m = u32x4{0u, 0u, 0u, 0u};
+    if (v < kvec) {
+        int64_t r = r0 + wave;
+        const u32x4* p = x + r * kvec + v;
+        const int64_t step = 4 * kvec;
+        for (; r + 4 * (kAbsUnroll - 1) < r1; r += 4 * kAbsUnroll) {
+            u32x4 t[kAbsUnroll];
+#pragma unroll
+            for (int u = 0; u < kAbsUnroll; ++u) t[u] = __builtin_nontemporal_load(p + u * step);
+#pragma unroll
+            for (int u = 0; u < kAbsUnroll; ++u) acc_mag<EB>(m, t[u]);
+            p += kAbsUnroll * step;
+        }
+        for (; r < r1; r += 4) {
+            acc_mag<EB>(m, __builtin_nontemporal_load(p));
+            p += step;
+        }
+    }
+    part[threadIdx.x] = m;
+    __syncthreads();
+    if (wave == 0 && v < kvec) {
+#pragma unroll
+        for (int w = 1; w < 4; ++w) acc_mag<EB>(m, part[w * 64 + lane]);
+        if constexpr (EB == 2) {
+            unsigned* o = out_bits + v * 8;
+            const uint32_t words[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                atomicMax(o + 2 * i, (words[i] & 0xffffu) << 16);
+                atomicMax(o + 2 * i + 1, words[i] & 0xffff0000u);
+            }
+        } else {
+            unsigned* o = out_bits + v * 4;
+            atomicMax(o + 0, m.x);
+            atomicMax(o + 1, m.y);
+            atomicMax(o + 2, m.z);
+            atomicMax(o + 3, m.w);
+        }
+    }
+}
+
+__global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+// One block computes every s_j, inv_s_j and the block-wide maximum of the
+// smoothed channel maxima, from which the per-tensor scale follows in closed
+// form (ADR-010 "Key design" item 1: act_max/s maximised over channels, /127).
+constexpr int kSmoothThreads = 1024;
+
+__global__ __launch_bounds__(kSmoothThreads) void smooth_kernel(const float* __restrict__ act_max,
+                                                                const float* __restrict__ w_max, int64_t k,
+                                                                double alpha, float* __restrict__ s,
+                                                                float* __restrict__ inv_s,
+                                                                float* __restrict__ act_scale) {
+    __shared__ float red[kSmoothThreads / 64];
+    float mx = 0.0f;
+    for (int64_t j = threadIdx.x; j < k; j += kSmoothThreads) {
+        const float a = __builtin_fmaxf(act_max[j], sqd::kFloor);
+        const float w = __builtin_fmaxf(w_max[j], sqd::kFloor);
+        // s_j = max|X_j|^alpha / max|W_j|^(1-alpha) (kwkr.cn blog §2.2), fp64, one rounding
+        const double num = pow((double)a, alpha);
+        const double den = pow((double)w, 1.0 - alpha);
+        const float sj = (float)(num / den);
+        const float inv = __fdiv_rn(1.0f, sj);
+        s[j] = sj;
+        inv_s[j] = inv;
+        mx = __builtin_fmaxf(mx, __fmul_rn(a, inv));
+    }
+    mx = sqd::block_max<kSmoothThreads / 64>(mx, red);
+    if (threadIdx.x == 0) act_scale[0] = __fdiv_rn(mx, sqd::kQmax);
+}
+
+}  // namespace
+
+namespace sqk {
+
+hipError_t absmax(const void* x, int xt, int64_t rows, int64_t k, float* absmax_out, bool accumulate,
+                  hipStream_t stream) {
+    if (!accumulate) {
+        fill_zero_kernel<<<dim3((unsigned)((k + 255) / 256)), dim3(256), 0, stream>>>(absmax_out, k);
+    }
+    if (rows == 0) return hipGetLastError();
+    const int eb = elem_bytes(xt);
+    const int64_t kvec = k * eb / 16;
+    const int64_t strips = (kvec + 63) / 64;
+    // aim for ~4096 blocks so every CU has several resident; rows per block a
+    // multiple of 4 * unroll so each wave runs whole unrolled iterations
+    const int64_t granule = 4 * kAbsUnroll;
+    int64_t target_chunks = std::max<int64_t>(1, 4096 / strips);
+    int64_t rpb = (rows + target_chunks - 1) / target_chunks;
+    rpb = std::max<int64_t>(granule, (rpb + granule - 1) / granule * granule);
+    int64_t chunks = (rows + rpb - 1) / rpb;
+    if (chunks > 65535) {
+        rpb = (rows + 65534) / 65535;
+        rpb = (rpb + granule - 1) / granule * granule;
+        chunks = (rows + rpb - 1) / rpb;
+    }
+    dim3 grid((unsigned)strips, (unsigned)chunks);
+    if (eb == 2)
+        absmax_kernel<2><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x, rows, kvec, rpb,
+                                                                 (unsigned*)absmax_out);
+    else
+        absmax_kernel<4><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x, rows, kvec, rpb,
+                                                                 (unsigned*)absmax_out);
+    return hipGetLastError();
+}
+
+hipError_t smooth_factors(const float* act_max, const float* w_max, int64_t k, float alpha, float* s,
+                          float* inv_s, float* act_scale, hipStream_t stream) {
+    smooth_kernel<<<dim3(1), dim3(kSmoothThreads), 0, stream>>>(act_max, w_max, k, (double)alpha, s, inv_s,
+                                                                act_scale);
+    return hipGetLastError();
+}
+
+}  // namespace sqk

@@ -1,0 +1,205 @@
+// sq_capi.cpp -- the C ABI of libsq (declared in include/sq.h): argument
+// validation, then launches on the caller's stream. No allocation, no state.
+#include "sq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "sq_kernels.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_k(int64_t k) { return k > 0 && k % 64 == 0; }
+
+bool valid_dtype(sq_dtype t) { return t == SQ_F32 || t == SQ_BF16; }
+
+bool valid_alpha(float a) { return std::isfinite(a) && a >= 0.0f && a <= 1.0f; }
+
+sq_status hip_status(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_ERR_HIP; }
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace layout of the alpha search, in this order, each piece 256-byte aligned.
+struct AlphaLayout {
+    size_t act_max, w_max, s, inv_s, act_scale, w_scale, mse, slots, wq, xq, yref, total;
+};
+
+AlphaLayout alpha_layout(int nb, int64_t rows, int64_t n, int64_t k, int na) {
+    AlphaLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += round_up(bytes);
+        return at;
+    };
+    L.act_max = take((size_t)k * 4);
+    L.w_max = take((size_t)k * 4);
+    L.s = take((size_t)k * 4);
+    L.inv_s = take((size_t)k * 4);
+    L.act_scale = take(16);
+    L.w_scale = take((size_t)n * 4);
+    L.mse = take((size_t)na * 8);
+    L.slots = take((size_t)na * nb * sqk::gemm_sse_slots(rows, n) * 8);
+    L.wq = take((size_t)n * k);
+    L.xq = take((size_t)rows * k);
+    L.yref = take((size_t)nb * rows * n * 4);
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sq_status_string(sq_status status) {
+    switch (status) {
+        case SQ_OK: return "ok";
+        case SQ_ERR_NULL: return "a required pointer is NULL";
+        case SQ_ERR_SHAPE: return "invalid shape (negative size, k not a positive multiple of 64, or a size limit)";
+        case SQ_ERR_DTYPE: return "unsupported element type";
+        case SQ_ERR_ALPHA: return "alpha must be finite and in [0, 1]";
+        case SQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case SQ_ERR_HIP: return "HIP launch or runtime error";
+        case SQ_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    }
+    return "unknown status";
+}
+
+sq_status sq_calib_absmax(const void* x, sq_dtype xt, int64_t rows, int64_t k, float* absmax, int accumulate,
+                          hipStream_t stream) {
+    if (!absmax || (rows > 0 && !x)) return SQ_ERR_NULL;
+    if (!valid_dtype(xt)) return SQ_ERR_DTYPE;
+    if (rows < 0 || !valid_k(k)) return SQ_ERR_SHAPE;
+    if (!aligned16(absmax) || (rows > 0 && !aligned16(x))) return SQ_ERR_ALIGN;
+    if (rows == 0 && accumulate) return SQ_OK;
+    return hip_status(sqk::absmax(x, xt, rows, k, absmax, accumulate != 0, stream));
+}
+
+sq_status sq_smooth_factors(const float* act_max, const float* w_max, int64_t k, float alpha, float* s,
+                            float* inv_s, float* act_scale, hipStream_t stream) {
+    if (!act_max || !w_max || !s || !inv_s || !act_scale) return SQ_ERR_NULL;
+    if (!valid_k(k)) return SQ_ERR_SHAPE;
+    if (!valid_alpha(alpha)) return SQ_ERR_ALPHA;
+    if (!aligned16(act_max) || !aligned16(w_max) || !aligned16(s) || !aligned16(inv_s) || !aligned16(act_scale))
+        return SQ_ERR_ALIGN;
+    return hip_status(sqk::smooth_factors(act_max, w_max, k, alpha, s, inv_s, act_scale, stream));
+}
+
+sq_status sq_quant_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, const float* s, int8_t* wq,
+                          float* w_scale, hipStream_t stream) {
+    if (!s || (n > 0 && (!w || !wq || !w_scale))) return SQ_ERR_NULL;
+    if (!valid_dtype(wt)) return SQ_ERR_DTYPE;
+    if (n < 0 || !valid_k(k) || n > INT32_MAX) return SQ_ERR_SHAPE;
+    if (!aligned16(s) || (n > 0 && (!aligned16(w) || !aligned16(wq) || !aligned16(w_scale)))) return SQ_ERR_ALIGN;
+    return hip_status(sqk::quant_weight(w, wt, n, k, s, wq, w_scale, stream));
+}
+
+sq_status sq_smooth_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* inv_s,
+                              const float* act_scale, int8_t* xq, hipStream_t stream) {
+    if (!inv_s || !act_scale || (m > 0 && (!x || !xq))) return SQ_ERR_NULL;
+    if (!valid_dtype(xt)) return SQ_ERR_DTYPE;
+    if (m < 0 || !valid_k(k)) return SQ_ERR_SHAPE;
+    if (!aligned16(inv_s) || !aligned16(act_scale) || (m > 0 && (!aligned16(x) || !aligned16(xq))))
+        return SQ_ERR_ALIGN;
+    return hip_status(sqk::quant_act(x, xt, m, k, inv_s, act_scale, xq, stream));
+}
+
+sq_status sq_w8a8_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
+                       const float* act_scale, const float* w_scale, void* y, sq_dtype yt, int32_t* acc_out,
+                       hipStream_t stream) {
+    const bool work = m > 0 && n > 0;
+    if (!act_scale || (work && (!xq || !wq || !w_scale || !y))) return SQ_ERR_NULL;
+    if (!valid_dtype(yt)) return SQ_ERR_DTYPE;
+    if (m < 0 || n < 0 || !valid_k(k) || k > SQ_MAX_GEMM_K) return SQ_ERR_SHAPE;
+    // tile counts are int on the device side
+    if ((m + 127) / 128 * ((n + 127) / 128) > INT32_MAX / 2) return SQ_ERR_SHAPE;
+    if (!aligned16(act_scale) ||
+        (work && (!aligned16(xq) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) ||
+                  (acc_out && !aligned16(acc_out)))))
+        return SQ_ERR_ALIGN;
+    return hip_status(sqk::gemm_dequant(xq, wq, m, n, k, act_scale, w_scale, y, yt, acc_out, stream));
+}
+
+sq_status sq_alpha_search_workspace(int n_batches, int64_t rows_per_batch, int64_t n, int64_t k, int n_alphas,
+                                    size_t* bytes) {
+    if (!bytes) return SQ_ERR_NULL;
+    if (n_batches < 1 || rows_per_batch < 1 || n < 1 || !valid_k(k) || k > SQ_MAX_GEMM_K) return SQ_ERR_SHAPE;
+    if (n_alphas < 1 || n_alphas > 16) return SQ_ERR_SHAPE;
+    *bytes = alpha_layout(n_batches, rows_per_batch, n, k, n_alphas).total;
+    return SQ_OK;
+}
+
+sq_status sq_alpha_search(const void* const* x_batches, sq_dtype xt, int n_batches, int64_t rows_per_batch,
+                          int64_t k, const void* w, sq_dtype wt, int64_t n, const float* alphas, int n_alphas,
+                          void* workspace, size_t workspace_bytes, double* mse, int* best, hipStream_t stream) {
+    if (!x_batches || !w || !alphas || !mse || !best) return SQ_ERR_NULL;
+    if (!valid_dtype(xt) || !valid_dtype(wt) || xt != wt) return SQ_ERR_DTYPE;
+    size_t need = 0;
+    sq_status st = sq_alpha_search_workspace(n_batches, rows_per_batch, n, k, n_alphas, &need);
+    if (st != SQ_OK) return st;
+    if (n > INT32_MAX) return SQ_ERR_SHAPE;
+    for (int b = 0; b < n_batches; ++b) {
+        if (!x_batches[b]) return SQ_ERR_NULL;
+        if (!aligned16(x_batches[b])) return SQ_ERR_ALIGN;
+    }
+    for (int i = 0; i < n_alphas; ++i)
+        if (!valid_alpha(alphas[i])) return SQ_ERR_ALPHA;
+    if (!workspace || workspace_bytes < need) return SQ_ERR_WORKSPACE;
+    if (!aligned16(w) || !aligned16(workspace)) return SQ_ERR_ALIGN;
+
+    const AlphaLayout L = alpha_layout(n_batches, rows_per_batch, n, k, n_alphas);
+    char* base = (char*)workspace;
+    float* act_max = (float*)(base + L.act_max);
+    float* w_max = (float*)(base + L.w_max);
+    float* s = (float*)(base + L.s);
+    float* inv_s = (float*)(base + L.inv_s);
+    float* act_scale = (float*)(base + L.act_scale);
+    float* w_scale = (float*)(base + L.w_scale);
+    double* mse_dev = (double*)(base + L.mse);
+    double* slots = (double*)(base + L.slots);
+    int8_t* wq = (int8_t*)(base + L.wq);
+    int8_t* xq = (int8_t*)(base + L.xq);
+    float* yref = (float*)(base + L.yref);
+    const int64_t per_gemm = sqk::gemm_sse_slots(rows_per_batch, n);
+    const int64_t ynum = rows_per_batch * n;
+
+    hipError_t e = hipSuccess;
+    auto run = [&](hipError_t r) {
+        if (e == hipSuccess) e = r;
+    };
+    // statistics over all kept batches, then the reference products
+    for (int b = 0; b < n_batches; ++b)
+        run(sqk::absmax(x_batches[b], xt, rows_per_batch, k, act_max, b > 0, stream));
+    run(sqk::absmax(w, wt, n, k, w_max, false, stream));
+    for (int b = 0; b < n_batches; ++b)
+        run(sqk::ref_gemm(x_batches[b], xt, w, wt, rows_per_batch, n, k, yref + b * ynum, stream));
+    // one full quantized forward per alpha, scored in the GEMM epilogue
+    for (int i = 0; i < n_alphas && e == hipSuccess; ++i) {
+        run(sqk::smooth_factors(act_max, w_max, k, alphas[i], s, inv_s, act_scale, stream));
+        run(sqk::quant_weight(w, wt, n, k, s, wq, w_scale, stream));
+        for (int b = 0; b < n_batches; ++b) {
+            run(sqk::quant_act(x_batches[b], xt, rows_per_batch, k, inv_s, act_scale, xq, stream));
+            run(sqk::gemm_sse(xq, wq, rows_per_batch, n, k, act_scale, w_scale, yref + b * ynum,
+                              slots + ((int64_t)i * n_batches + b) * per_gemm, stream));
+        }
+    }
+    const double count = (double)n_batches * (double)rows_per_batch * (double)n;
+    run(sqk::reduce_slots(slots, (int64_t)n_batches * per_gemm, n_alphas, count, mse_dev, stream));
+    if (e != hipSuccess) return SQ_ERR_HIP;
+    run(hipMemcpyAsync(mse, mse_dev, (size_t)n_alphas * sizeof(double), hipMemcpyDeviceToHost, stream));
+    run(hipStreamSynchronize(stream));
+    if (e != hipSuccess) return SQ_ERR_HIP;
+    int b = 0;
+    for (int i = 1; i < n_alphas; ++i)
+        if (mse[i] < mse[b]) b = i;
+    *best = b;
+    return SQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// sq_device.h -- device-side helpers shared by the libsq kernels (gfx950 only).
+//
+// Numerics follow the fixed fp32 op order of the SmoothQuant W8A8 path: every
+// product is one IEEE fp32 multiply (__fmul_rn, no contraction), divisions are
+// correctly rounded (__fdiv_rn), integer codes are round-half-to-even
+// (v_rndne_f32) clamped to [-127, 127] (symmetric quantizer of the kwkr.cn
+// blog §1.2).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sqd {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kFloor = 1e-5f;  // guard floor on statistics (tbr8.org example clamps s at 1e-5)
+constexpr float kQmax = 127.0f;  // symmetric int8 range [-127, 127]
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// round-to-nearest-even fp32 -> bf16 bit pattern (NaN kept quiet)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// symmetric int8 code of an already scaled value
+__device__ __forceinline__ int q8(float v) {
+    float r = __builtin_rintf(v);
+    r = __builtin_fminf(__builtin_fmaxf(r, -kQmax), kQmax);
+    return (int)r;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+           ((uint32_t)(d & 0xff) << 24);
+}
+
+// Widen one 16-byte vector to fp32: 8 bf16 or 4 fp32 values.
+template <int E>
+__device__ __forceinline__ void unpack16(const u32x4& v, float (&e)[E]);
+
+template <>
+__device__ __forceinline__ void unpack16<8>(const u32x4& v, float (&e)[8]) {
+    e[0] = bf16_lo(v.x); e[1] = bf16_hi(v.x);
+    e[2] = bf16_lo(v.y); e[3] = bf16_hi(v.y);
+    e[4] = bf16_lo(v.z); e[5] = bf16_hi(v.z);
+    e[6] = bf16_lo(v.w); e[7] = bf16_hi(v.w);
+}
+
+template <>
+__device__ __forceinline__ void unpack16<4>(const u32x4& v, float (&e)[4]) {
+    e[0] = __uint_as_float(v.x); e[1] = __uint_as_float(v.y);
+    e[2] = __uint_as_float(v.z); e[3] = __uint_as_float(v.w);
+}
+
+// wave-wide maximum (64 lanes)
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// block-wide maximum; every thread gets the result. `red` holds >= NWAVES floats.
+template <int NWAVES>
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < NWAVES; ++i) r = __builtin_fmaxf(r, red[i]);
+    __syncthreads();
+    return r;
+}
+
+}  // namespace sqd

@@ -1,0 +1,55 @@
+// sq_kernels.h -- host-side launchers of the libsq kernels. Internal to the
+// library: the C ABI in include/sq.h validates arguments and calls these.
+// Every launcher enqueues on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sqk {
+
+enum ElemType { kF32 = 0, kBF16 = 1 };
+
+inline int elem_bytes(int t) { return t == kBF16 ? 2 : 4; }
+
+// column max |x| of x[rows,k] into absmax[k] (overwrite or running max)
+hipError_t absmax(const void* x, int xt, int64_t rows, int64_t k, float* absmax, bool accumulate,
+                  hipStream_t stream);
+
+// s, inv_s, act_scale from the two statistics
+hipError_t smooth_factors(const float* act_max, const float* w_max, int64_t k, float alpha, float* s,
+                          float* inv_s, float* act_scale, hipStream_t stream);
+
+// W' = W diag(s), per-row symmetric int8
+hipError_t quant_weight(const void* w, int wt, int64_t n, int64_t k, const float* s, int8_t* wq,
+                        float* w_scale, hipStream_t stream);
+
+// xq = q8((x * inv_s) * (1/act_scale))
+hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const float* inv_s,
+                     const float* act_scale, int8_t* xq, hipStream_t stream);
+
+// y = fp32(acc) * (act_scale * w_scale[n]) in fp32 or bf16, optional int32 acc
+hipError_t gemm_dequant(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
+                        const float* act_scale, const float* w_scale, void* y, int yt, int32_t* acc_out,
+                        hipStream_t stream);
+
+// Number of fp64 partial slots gemm_sse writes for an m x n problem.
+int64_t gemm_sse_slots(int64_t m, int64_t n);
+
+// Per-slot partial sums of ((double)y - (double)yref)^2 with y the fp32
+// dequantized product; slots[gemm_sse_slots(m,n)] fp64.
+hipError_t gemm_sse(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
+                    const float* act_scale, const float* w_scale, const float* yref, double* slots,
+                    hipStream_t stream);
+
+// yref[m,n] = x[m,k] * w[n,k]^T in fp32 (bf16: exact products, fp32 sums)
+hipError_t ref_gemm(const void* x, int xt, const void* w, int wt, int64_t m, int64_t n, int64_t k,
+                    float* yref, hipStream_t stream);
+
+// out[g] = (sum over the slots of group g, in a fixed order) / count, where
+// group g is the `per_group` consecutive slots starting at g * per_group
+hipError_t reduce_slots(const double* slots, int64_t per_group, int groups, double count, double* out,
+                        hipStream_t stream);
+
+}  // namespace sqk

@@ -1,0 +1,65 @@
+"""One SmoothQuant W8A8 linear layer on one GPU: its device buffers and the
+sequence of C-ABI calls that make up the path.
+
+The record kept per layer follows ADR-010's SmoothQuantLinear (int8 weight
+with a per-row scale, a per-tensor activation scale, per-input-channel
+smoothing factors), with fp32 scales. PyTorch only allocates the buffers and
+supplies the stream; all arithmetic is in libsq.so.
+
+    step(x_calib, x) = calibrate(x_calib) -> prepare() -> forward(x)
+      calibrate: act_max  = max |x_calib| per input channel   (sq_calib_absmax)
+      prepare:   w_max    = max |W| per input channel          (sq_calib_absmax)
+                 s, 1/s, act_scale                             (sq_smooth_factors)
+                 Wq, w_scale = per-row int8 of W diag(s)       (sq_quant_weight)
+      forward:   Xq = per-tensor int8 of x * (1/s)             (sq_smooth_quant_act)
+                 Y  = dequant(Xq Wq^T)                         (sq_w8a8_gemm)
+"""
+from __future__ import annotations
+
+from . import capi
+
+
+class W8A8Linear:
+    def __init__(self, w, alpha: float = 0.5, max_tokens: int = 0, out_dtype=None):
+        import torch
+        self.w = w
+        self.alpha = float(alpha)
+        self.n, self.k = w.shape
+        d = w.device
+        f32 = torch.float32
+        self.act_max = torch.zeros(self.k, dtype=f32, device=d)
+        self.w_max = torch.empty(self.k, dtype=f32, device=d)
+        self.s = torch.empty(self.k, dtype=f32, device=d)
+        self.inv_s = torch.empty(self.k, dtype=f32, device=d)
+        self.act_scale = torch.empty(4, dtype=f32, device=d)  # one value, padded to 16 bytes
+        self.wq = torch.empty((self.n, self.k), dtype=torch.int8, device=d)
+        self.w_scale = torch.empty(self.n, dtype=f32, device=d)
+        self.out_dtype = out_dtype if out_dtype is not None else torch.bfloat16
+        self.xq = torch.empty((max_tokens, self.k), dtype=torch.int8, device=d) if max_tokens else None
+        self.y = torch.empty((max_tokens, self.n), dtype=self.out_dtype, device=d) if max_tokens else None
+
+    def calibrate(self, x, accumulate: bool = False, stream=None):
+        capi.sq_calib_absmax(x, self.act_max, accumulate, stream)
+
+    def prepare(self, stream=None):
+        capi.sq_calib_absmax(self.w, self.w_max, False, stream)
+        capi.sq_smooth_factors(self.act_max, self.w_max, self.alpha, self.s, self.inv_s, self.act_scale, stream)
+        capi.sq_quant_weight(self.w, self.s, self.wq, self.w_scale, stream)
+
+    def forward(self, x, y=None, xq=None, acc_out=None, stream=None):
+        import torch
+        m = x.shape[0]
+        if xq is None:
+            xq = self.xq[:m] if self.xq is not None and self.xq.shape[0] >= m else \
+                torch.empty((m, self.k), dtype=torch.int8, device=x.device)
+        if y is None:
+            y = self.y[:m] if self.y is not None and self.y.shape[0] >= m else \
+                torch.empty((m, self.n), dtype=self.out_dtype, device=x.device)
+        capi.sq_smooth_quant_act(x, self.inv_s, self.act_scale, xq, stream)
+        capi.sq_w8a8_gemm(xq, self.wq, self.act_scale, self.w_scale, y, acc_out, stream)
+        return y
+
+    def step(self, x_calib, x, stream=None):
+        self.calibrate(x_calib, False, stream)
+        self.prepare(stream)
+        return self.forward(x, stream=stream)

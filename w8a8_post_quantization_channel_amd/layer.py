@@ -46,18 +46,26 @@ class W8A8Linear:
         capi.sq_smooth_factors(self.act_max, self.w_max, self.alpha, self.s, self.inv_s, self.act_scale, stream)
         capi.sq_quant_weight(self.w, self.s, self.wq, self.w_scale, stream)
 
-    def forward(self, x, y=None, xq=None, acc_out=None, stream=None):
+    def quantize_input(self, x, xq=None, stream=None):
         import torch
         m = x.shape[0]
         if xq is None:
             xq = self.xq[:m] if self.xq is not None and self.xq.shape[0] >= m else \
                 torch.empty((m, self.k), dtype=torch.int8, device=x.device)
+        capi.sq_smooth_quant_act(x, self.inv_s, self.act_scale, xq, stream)
+        return xq
+
+    def matmul(self, xq, y=None, acc_out=None, stream=None):
+        import torch
+        m = xq.shape[0]
         if y is None:
             y = self.y[:m] if self.y is not None and self.y.shape[0] >= m else \
-                torch.empty((m, self.n), dtype=self.out_dtype, device=x.device)
-        capi.sq_smooth_quant_act(x, self.inv_s, self.act_scale, xq, stream)
+                torch.empty((m, self.n), dtype=self.out_dtype, device=xq.device)
         capi.sq_w8a8_gemm(xq, self.wq, self.act_scale, self.w_scale, y, acc_out, stream)
         return y
+
+    def forward(self, x, y=None, xq=None, acc_out=None, stream=None):
+        return self.matmul(self.quantize_input(x, xq, stream), y, acc_out, stream)
 
     def step(self, x_calib, x, stream=None):
         self.calibrate(x_calib, False, stream)

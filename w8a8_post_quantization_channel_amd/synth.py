@@ -44,9 +44,12 @@ def rng(seed: int) -> np.random.Generator:
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 to bf16, nearest-even; returns uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    """Round finite float32 to bf16, nearest-even; returns uint16 bit patterns."""
+    u = np.array(x, dtype=np.float32, copy=True, order="C").view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= np.uint32(16)
     return u.astype(np.uint16)
 
 
@@ -103,6 +106,31 @@ def c1():
     x[:, 50] = 100.0
     w = g.standard_normal((2048, 1024), dtype=np.float32)
     return x, w
+
+
+# One 13B decoder layer: four distinct projection inputs (q/k/v share the
+# attention input, gate/up the MLP input) and seven weights.
+# group name -> (K, outlier seed, activation seed)
+C2_GROUPS = {"attn_in": (5120, 2000, 2200), "mlp_in": (5120, 2001, 2201), "mlp_mid": (13824, 2002, 2202),
+             "attn_out": (5120, 2003, 2203)}
+# (projection, input group, N, K, weight seed)
+C2_PROJECTIONS = [("q", "attn_in", 5120, 5120, 2310), ("k", "attn_in", 5120, 5120, 2311),
+                  ("v", "attn_in", 5120, 5120, 2312), ("o", "attn_out", 5120, 5120, 2313),
+                  ("gate", "mlp_in", 13824, 5120, 2314), ("up", "mlp_in", 13824, 5120, 2315),
+                  ("down", "mlp_mid", 5120, 13824, 2316)]
+C2_TOKENS = 2048
+
+
+def c2_group_x(group: str, rows: int = C2_TOKENS):
+    k, oseed, xseed = C2_GROUPS[group]
+    return activations(xseed, rows, k, outlier_channels(oseed, k))
+
+
+def c2_projection_w(name: str):
+    for p, _, n, k, seed in C2_PROJECTIONS:
+        if p == name:
+            return weights(seed, n, k)
+    raise KeyError(name)
 
 
 def c2_outliers(shape_id: int):

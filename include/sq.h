@@ -123,6 +123,14 @@ sq_status sq_w8a8_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n,
                        void* y, sq_dtype yt, int32_t* acc_out, hipStream_t stream);
 
 /*
+ * Host-only query: the block tile (rows x columns of Y per workgroup) that
+ * sq_w8a8_gemm uses for an m x n output on the current device. The choice
+ * depends only on m, n and the device's compute-unit count; it does not change
+ * the result (the int32 sums are exact in any order). Launches nothing.
+ */
+sq_status sq_gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n);
+
+/*
  * Workspace bytes needed by sq_alpha_search for the given problem (host
  * output *bytes). Pure host computation.
  */

@@ -25,7 +25,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = capi.declared_functions()
     assert set(names) >= {"sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_smooth_quant_act",
-                          "sq_w8a8_gemm", "sq_alpha_search", "sq_alpha_search_workspace", "sq_status_string"}
+                          "sq_w8a8_gemm", "sq_alpha_search", "sq_alpha_search_workspace", "sq_status_string",
+                          "sq_gemm_tiling"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -110,6 +111,14 @@ def test_gemm_validation(lib):
     a = list(base)
     a[2] = 0
     assert f(*a) == OK
+
+
+def test_gemm_tiling_query(lib):
+    bm, bn = ctypes.c_int(0), ctypes.c_int(0)
+    assert lib.sq_gemm_tiling(16, 32, None, ctypes.byref(bn)) == NULL
+    assert lib.sq_gemm_tiling(-1, 32, ctypes.byref(bm), ctypes.byref(bn)) == SHAPE
+    assert lib.sq_gemm_tiling(2048, 5120, ctypes.byref(bm), ctypes.byref(bn)) == OK
+    assert bm.value in (128, 256) and bn.value in (128, 160, 192, 224, 256)
 
 
 def test_alpha_search_validation(lib):

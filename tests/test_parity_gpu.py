@@ -179,8 +179,25 @@ def test_quant_act_ties():
     assert_bitexact("ties", synth.from_torch(xq), ORACLE.quant_act(x, ones, a[0]))
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 16, 64), (5, 48, 1088), (129, 257, 320), (300, 600, 2048), (512, 8192, 128),
-                                   (1024, 8192, 256)])
+GEMM_CASES = [(1, 16, 64), (5, 48, 1088), (129, 257, 320), (300, 600, 2048), (512, 8192, 128),
+              (1024, 8192, 256), (2100, 4112, 192), (2048, 7168, 64), (2048, 11008, 128), (4096, 4096, 64),
+              (4000, 4100, 64)]
+
+
+def reachable_tilings():
+    """Block tiles the library picks over a broad grid of output shapes."""
+    ms = [1, 8, 16, 64, 100, 128, 200, 256, 512, 1000, 1024, 1500, 2048, 3000, 4096, 8192, 16384]
+    ns = [16, 128, 512, 1024, 2048, 3000, 4096, 5120, 7168, 8192, 11008, 13824, 28672]
+    return {capi.sq_gemm_tiling(m, n) for m in ms for n in ns}
+
+
+def test_gemm_cases_cover_every_tiling():
+    """The GEMM cases below exercise every block tile the library can pick."""
+    used = {capi.sq_gemm_tiling(m, n) for m, n, _ in GEMM_CASES}
+    assert reachable_tilings() <= used, (reachable_tilings(), used)
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_CASES)
 @pytest.mark.parametrize("bf16_out", [False, True])
 def test_gemm_cases(m, n, k, bf16_out):
     import torch

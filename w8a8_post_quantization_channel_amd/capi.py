@@ -48,6 +48,7 @@ def _declare(lib):
         "sq_smooth_quant_act": [P, c.c_int, i64, i64, P, P, P, P],
         "sq_w8a8_gemm": [P, P, i64, i64, i64, P, P, P, c.c_int, P, P],
         "sq_alpha_search_workspace": [c.c_int, i64, i64, i64, c.c_int, P],
+        "sq_gemm_tiling": [i64, i64, P, P],
         "sq_alpha_search": [P, c.c_int, c.c_int, i64, i64, P, c.c_int, i64, P, c.c_int, P, c.c_size_t, P, P, P],
     }
     for name, args in sigs.items():
@@ -133,6 +134,13 @@ def sq_w8a8_gemm(xq, wq, act_scale, w_scale, y, acc_out=None, stream=None):
     _check("sq_w8a8_gemm", load().sq_w8a8_gemm(_dev(xq, "xq"), _dev(wq, "wq"), m, n, k, _dev(act_scale, "act_scale"),
                                                _dev(w_scale, "w_scale"), _dev(y, "y"), _dtype_code(y), acc,
                                                _stream(stream)))
+
+
+def sq_gemm_tiling(m: int, n: int) -> tuple[int, int]:
+    """Block tile (rows, columns) sq_w8a8_gemm uses for an m x n output."""
+    bm, bn = ctypes.c_int(0), ctypes.c_int(0)
+    _check("sq_gemm_tiling", load().sq_gemm_tiling(m, n, ctypes.byref(bm), ctypes.byref(bn)))
+    return bm.value, bn.value
 
 
 def sq_alpha_search_workspace(n_batches: int, rows_per_batch: int, n: int, k: int, n_alphas: int = 4) -> int:

@@ -23,7 +23,8 @@ using sqd::u32x4;
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kAbsThreads = 256;  // 4 waves
-constexpr int kAbsUnroll = 4;     // rows in flight per wave
+constexpr int kAbsUnroll = 8;     // 16-byte loads in flight per lane
+constexpr int kAbsMinRows = 128;  // rows per block: amortises the per-block atomics
 
 __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
     u16x2 va = __builtin_bit_cast(u16x2, a), vb = __builtin_bit_cast(u16x2, b);
@@ -46,10 +47,29 @@ __device__ __forceinline__ void acc_mag(u32x4& m, const u32x4& v) {
     }
 }
 
+// fp32 bit pattern of the magnitude of column c of a strip, taken from the
+// per-lane word vector `w` of the lane that loaded it
+template <int EB>
+__device__ __forceinline__ uint32_t column_bits(const uint32_t* words, int c) {
+    if constexpr (EB == 2) {
+        const uint32_t wd = words[(c >> 1) & 3];
+        return (c & 1) ? (wd & 0xffff0000u) : (wd << 16);
+    } else {
+        return words[c & 3];
+    }
+}
+
+// Block = 4 waves over one strip of 64 16-byte column vectors and a chunk of
+// rows; wave w takes rows r0 + w, r0 + w + 4, ... with kAbsUnroll loads in
+// flight per lane. The four wave partials meet in LDS; then every thread
+// merges whole columns so each atomic instruction covers consecutive
+// addresses.
 template <int EB>
 __global__ __launch_bounds__(kAbsThreads) void absmax_kernel(const u32x4* __restrict__ x, int64_t rows,
-                                                             int64_t kvec, int64_t rows_per_block,
+                                                             int64_t kvec, int64_t k, int64_t rows_per_block,
                                                              unsigned* __restrict__ out_bits) {
+    constexpr int E = 16 / EB;          // elements per 16-byte vector
+    constexpr int COLS = 64 * E;        // columns per strip
     __shared__ u32x4 part[kAbsThreads];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t v = (int64_t)blockIdx.x * 64 + lane;  // 16-byte column vector
@@ -75,24 +95,18 @@ __global__ __launch_bounds__(kAbsThreads) void absmax_kernel(const u32x4* __rest
     }
     part[threadIdx.x] = m;
     __syncthreads();
-    if (wave == 0 && v < kvec) {
+    const int64_t col0 = (int64_t)blockIdx.x * COLS;
 #pragma unroll
-        for (int w = 1; w < 4; ++w) acc_mag<EB>(m, part[w * 64 + lane]);
-        if constexpr (EB == 2) {
-            unsigned* o = out_bits + v * 8;
-            const uint32_t words[4] = {m.x, m.y, m.z, m.w};
+    for (int c = threadIdx.x; c < COLS; c += kAbsThreads) {
+        if (col0 + c >= k) break;
+        uint32_t best = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                atomicMax(o + 2 * i, (words[i] & 0xffffu) << 16);
-                atomicMax(o + 2 * i + 1, words[i] & 0xffff0000u);
-            }
-        } else {
-            unsigned* o = out_bits + v * 4;
-            atomicMax(o + 0, m.x);
-            atomicMax(o + 1, m.y);
-            atomicMax(o + 2, m.z);
-            atomicMax(o + 3, m.w);
+        for (int w = 0; w < 4; ++w) {
+            const u32x4 pv = part[w * 64 + c / E];
+            const uint32_t words[4] = {pv.x, pv.y, pv.z, pv.w};
+            best = max(best, column_bits<EB>(words, c));
         }
+        atomicMax(out_bits + col0 + c, best);
     }
 }
 
@@ -101,31 +115,37 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
     if (i < n) p[i] = 0.0f;
 }
 
-// One block computes every s_j, inv_s_j and the block-wide maximum of the
-// smoothed channel maxima, from which the per-tensor scale follows in closed
-// form (ADR-010 "Key design" item 1: act_max/s maximised over channels, /127).
-constexpr int kSmoothThreads = 1024;
+// s_j = max|X_j|^alpha / max|W_j|^(1-alpha) (kwkr.cn blog §2.2): fp64 pow and
+// quotient, one rounding to fp32; inv_s_j = fp32(1/s_j). One thread per channel.
+constexpr int kSmoothThreads = 256;
 
 __global__ __launch_bounds__(kSmoothThreads) void smooth_kernel(const float* __restrict__ act_max,
                                                                 const float* __restrict__ w_max, int64_t k,
                                                                 double alpha, float* __restrict__ s,
-                                                                float* __restrict__ inv_s,
-                                                                float* __restrict__ act_scale) {
-    __shared__ float red[kSmoothThreads / 64];
+                                                                float* __restrict__ inv_s) {
+    const int64_t j = (int64_t)blockIdx.x * kSmoothThreads + threadIdx.x;
+    if (j >= k) return;
+    const float a = __builtin_fmaxf(act_max[j], sqd::kFloor);
+    const float w = __builtin_fmaxf(w_max[j], sqd::kFloor);
+    const double num = pow((double)a, alpha);
+    const double den = pow((double)w, 1.0 - alpha);
+    const float sj = (float)(num / den);
+    s[j] = sj;
+    inv_s[j] = __fdiv_rn(1.0f, sj);
+}
+
+// Closed-form per-tensor activation scale (ADR-010 "Key design" item 1):
+// act_scale = fp32( max_j fp32(max(act_max[j], 1e-5) * inv_s[j]) / 127 ).
+constexpr int kScaleThreads = 1024;
+
+__global__ __launch_bounds__(kScaleThreads) void act_scale_kernel(const float* __restrict__ act_max,
+                                                                  const float* __restrict__ inv_s, int64_t k,
+                                                                  float* __restrict__ act_scale) {
+    __shared__ float red[kScaleThreads / 64];
     float mx = 0.0f;
-    for (int64_t j = threadIdx.x; j < k; j += kSmoothThreads) {
-        const float a = __builtin_fmaxf(act_max[j], sqd::kFloor);
-        const float w = __builtin_fmaxf(w_max[j], sqd::kFloor);
-        // s_j = max|X_j|^alpha / max|W_j|^(1-alpha) (kwkr.cn blog §2.2), fp64, one rounding
-        const double num = pow((double)a, alpha);
-        const double den = pow((double)w, 1.0 - alpha);
-        const float sj = (float)(num / den);
-        const float inv = __fdiv_rn(1.0f, sj);
-        s[j] = sj;
-        inv_s[j] = inv;
-        mx = __builtin_fmaxf(mx, __fmul_rn(a, inv));
-    }
-    mx = sqd::block_max<kSmoothThreads / 64>(mx, red);
+    for (int64_t j = threadIdx.x; j < k; j += kScaleThreads)
+        mx = __builtin_fmaxf(mx, __fmul_rn(__builtin_fmaxf(act_max[j], sqd::kFloor), inv_s[j]));
+    mx = sqd::block_max<kScaleThreads / 64>(mx, red);
     if (threadIdx.x == 0) act_scale[0] = __fdiv_rn(mx, sqd::kQmax);
 }
 
@@ -142,12 +162,13 @@ hipError_t absmax(const void* x, int xt, int64_t rows, int64_t k, float* absmax_
     const int eb = elem_bytes(xt);
     const int64_t kvec = k * eb / 16;
     const int64_t strips = (kvec + 63) / 64;
-    // aim for ~4096 blocks so every CU has several resident; rows per block a
-    // multiple of 4 * unroll so each wave runs whole unrolled iterations
+    // about 2048 blocks, but at least kAbsMinRows rows per block (fewer
+    // atomics), rows per block a multiple of 4 waves x kAbsUnroll
     const int64_t granule = 4 * kAbsUnroll;
-    int64_t target_chunks = std::max<int64_t>(1, 4096 / strips);
+    const int64_t target_chunks = std::max<int64_t>(1, 2048 / strips);
     int64_t rpb = (rows + target_chunks - 1) / target_chunks;
-    rpb = std::max<int64_t>(granule, (rpb + granule - 1) / granule * granule);
+    rpb = std::max<int64_t>(rpb, std::min<int64_t>(rows, kAbsMinRows));
+    rpb = (rpb + granule - 1) / granule * granule;
     int64_t chunks = (rows + rpb - 1) / rpb;
     if (chunks > 65535) {
         rpb = (rows + 65534) / 65535;
@@ -156,18 +177,19 @@ hipError_t absmax(const void* x, int xt, int64_t rows, int64_t k, float* absmax_
     }
     dim3 grid((unsigned)strips, (unsigned)chunks);
     if (eb == 2)
-        absmax_kernel<2><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x, rows, kvec, rpb,
+        absmax_kernel<2><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x, rows, kvec, k, rpb,
                                                                  (unsigned*)absmax_out);
     else
-        absmax_kernel<4><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x, rows, kvec, rpb,
+        absmax_kernel<4><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x, rows, kvec, k, rpb,
                                                                  (unsigned*)absmax_out);
     return hipGetLastError();
 }
 
 hipError_t smooth_factors(const float* act_max, const float* w_max, int64_t k, float alpha, float* s,
                           float* inv_s, float* act_scale, hipStream_t stream) {
-    smooth_kernel<<<dim3(1), dim3(kSmoothThreads), 0, stream>>>(act_max, w_max, k, (double)alpha, s, inv_s,
-                                                                act_scale);
+    smooth_kernel<<<dim3((unsigned)((k + kSmoothThreads - 1) / kSmoothThreads)), dim3(kSmoothThreads), 0,
+                    stream>>>(act_max, w_max, k, (double)alpha, s, inv_s);
+    act_scale_kernel<<<dim3(1), dim3(kScaleThreads), 0, stream>>>(act_max, inv_s, k, act_scale);
     return hipGetLastError();
 }
 

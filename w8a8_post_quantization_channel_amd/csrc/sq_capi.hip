@@ -126,6 +126,13 @@ sq_status sq_w8a8_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n,
     return hip_status(sqk::gemm_dequant(xq, wq, m, n, k, act_scale, w_scale, y, yt, acc_out, stream));
 }
 
+sq_status sq_gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n) {
+    if (!block_m || !block_n) return SQ_ERR_NULL;
+    if (m < 0 || n < 0) return SQ_ERR_SHAPE;
+    sqk::gemm_tiling(m, n, block_m, block_n);
+    return SQ_OK;
+}
+
 sq_status sq_alpha_search_workspace(int n_batches, int64_t rows_per_batch, int64_t n, int64_t k, int n_alphas,
                                     size_t* bytes) {
     if (!bytes) return SQ_ERR_NULL;

@@ -34,6 +34,9 @@ hipError_t gemm_dequant(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n
                         const float* act_scale, const float* w_scale, void* y, int yt, int32_t* acc_out,
                         hipStream_t stream);
 
+// Block tile (rows, columns) the GEMM uses for an m x n output.
+void gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n);
+
 // Number of fp64 partial slots gemm_sse writes for an m x n problem.
 int64_t gemm_sse_slots(int64_t m, int64_t n);
 

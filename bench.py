@@ -49,6 +49,10 @@ def parse():
                     help="output rows of each GEMM the oracle computes in the CPU sample")
     ap.add_argument("--traffic", type=str, default=None,
                     help="JSON file with HBM traffic per GEMM launch (bytes) from rocprofv3 counters")
+    ap.add_argument("--workload", default="layer13b",
+                    choices=["layer13b", "decode7b", "alpha_search", "prefill70b", "hbm_passes"],
+                    help="layer13b (default, the headline line); the others measure the remaining "
+                         "workloads, one JSON line each")
     return ap.parse_args()
 
 
@@ -138,6 +142,199 @@ def cpu_baseline(groups, projs, rows):
                        f"({t_total:.1f} s estimated; {wall:.1f} s of CPU work measured)")}
 
 
+def timed(fn, reps, warmup=3):
+    """Average milliseconds of fn() on the current stream (HIP events)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def workload_decode7b(device):
+    """Llama-2-7B decode: x * (1/s) -> int8 and the int8 GEMM with fused
+    dequant, M in {1, 8, 16, 64}, weights cold (32 layers' weights rotate, more
+    than the 256 MB Infinity Cache). Algorithmic bytes: int8 weight + bf16 x +
+    int8 x + bf16 y + scales."""
+    import torch
+    from w8a8_post_quantization_channel_amd import capi, synth
+    layers = 32
+    out = {}
+    for sid, (name, n, k) in enumerate(synth.SHAPES_7B):
+        wq = [torch.randint(-127, 128, (n, k), dtype=torch.int8, device=device) for _ in range(layers)]
+        ws = torch.rand(n, device=device) * 1e-3 + 1e-4
+        inv_s = torch.rand(k, device=device) + 0.5
+        a = torch.full((4,), 0.05, device=device)
+        for m in synth.DECODE_M:
+            x = torch.randn((m, k), device=device).to(torch.bfloat16)
+            xq = torch.empty((m, k), dtype=torch.int8, device=device)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=device)
+            it = [0]
+
+            def one():
+                capi.sq_smooth_quant_act(x, inv_s, a, xq)
+                capi.sq_w8a8_gemm(xq, wq[it[0] % layers], a, ws, y)
+                it[0] += 1
+            ms = timed(one, 4 * layers)
+            byts = n * k + m * k * 3 + m * n * 2 + n * 4 + k * 4
+            out[f"{name}_{n}x{k}_m{m}"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
+                                          "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del wq
+        torch.cuda.empty_cache()
+    tot_b = sum(v["GB/s"] * v["us"] for v in out.values()) / sum(v["us"] for v in out.values())
+    return {"metric": "W8A8 decode (act quant + int8 GEMM) HBM GB/s, Llama-2-7B shapes, cold weights",
+            "value": tot_b, "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "dtype": "int8",
+            "data": "synthetic", "config": {"workload": "llama2-7b decode, M in {1,8,16,64}, 32 rotating layers"},
+            "per_case": out}
+
+
+def workload_alpha_search(device):
+    """Alpha grid search on a 4096 -> 11008 layer: 8 kept batches of 2048
+    tokens (Student-t, 12 channels x50), grid {0.25, 0.5, 0.75, 1}."""
+    import torch
+    from w8a8_post_quantization_channel_amd import capi, synth
+    xs = [synth.to_torch(x, device) for x in synth.c4_batches(8)]
+    w = synth.to_torch(synth.c4_weight(), device)
+    nbytes = capi.sq_alpha_search_workspace(8, 2048, 11008, 4096, 4)
+    wsp = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    capi.sq_alpha_search(xs, w, wsp)
+    reps = 5
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        mse, best = capi.sq_alpha_search(xs, w, wsp)
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    ops_i8 = 4 * 2.0 * 8 * 2048 * 11008 * 4096
+    ops_ref = 2.0 * 8 * 2048 * 11008 * 4096
+    return {"metric": "alpha grid search time, 4096->11008 layer, 8x2048 tokens", "value": ms, "unit": "ms",
+            "n_gpus": 1, "higher_is_better": False, "dtype": "int8+bf16", "data": "synthetic",
+            "config": {"workload": "alpha search 8x2048 tokens, K=4096, N=11008, grid 0.25/0.5/0.75/1.0"},
+            "mse": mse, "best_alpha": synth.ALPHA_GRID[best],
+            "effective_TOPS": (ops_i8 + ops_ref) / (ms * 1e-3) / 1e12}
+
+
+def workload_prefill70b(device):
+    """Llama-2-70B prefill, 4096 tokens, int8 weights of all 80 layers
+    resident in HBM (68.4 GB): per layer, the runtime path (act quant + int8
+    GEMM) of the 7 projections; weights are random int8 (the values do not
+    change the timing)."""
+    import torch
+    from w8a8_post_quantization_channel_amd import capi, synth
+    layers, m = 80, 4096
+    projs = [("q", 8192, 8192), ("k", 1024, 8192), ("v", 1024, 8192), ("o", 8192, 8192),
+             ("gate", 28672, 8192), ("up", 28672, 8192), ("down", 8192, 28672)]
+    g = torch.Generator(device=device)
+    g.manual_seed(70)
+    weights = []
+    for _ in range(layers):
+        weights.append([torch.randint(-127, 128, (n, k), dtype=torch.int8, device=device, generator=g)
+                        for _, n, k in projs])
+    resident = sum(w.numel() for lw in weights for w in lw)
+    xs = {k: torch.randn((m, k), device=device, generator=g).to(torch.bfloat16) for k in (8192, 28672)}
+    inv_s = {k: torch.rand(k, device=device, generator=g) + 0.5 for k in (8192, 28672)}
+    ws = {n: torch.rand(n, device=device, generator=g) * 1e-3 for n in (1024, 8192, 28672)}
+    a = torch.full((4,), 0.05, device=device)
+    xq = {k: torch.empty((m, k), dtype=torch.int8, device=device) for k in (8192, 28672)}
+    y = {n: torch.empty((m, n), dtype=torch.bfloat16, device=device) for n in (1024, 8192, 28672)}
+
+    def layer(i):
+        for j, (_, n, k) in enumerate(projs):
+            capi.sq_smooth_quant_act(xs[k], inv_s[k], a, xq[k])
+            capi.sq_w8a8_gemm(xq[k], weights[i][j], a, ws[n], y[n])
+    for i in range(2):
+        layer(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(layers):
+        layer(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ops = layers * sum(2.0 * m * n * k for _, n, k in projs)
+    return {"metric": "W8A8 act quant + int8 GEMM TOPS, Llama-2-70B shapes, 80 layers resident",
+            "value": ops / dt / 1e12, "unit": "TOPS", "n_gpus": 1, "higher_is_better": True, "dtype": "int8",
+            "data": "synthetic", "config": {"workload": "llama2-70b prefill 4096 tokens x 80 layers",
+                                            "resident_int8_weight_GB": resident / 1e9,
+                                            "tiling": {p: list(capi.sq_gemm_tiling(m, n)) for p, n, _ in projs}},
+            "ms_per_layer": dt * 1e3 / layers, "frac_of_int8_peak": ops / dt / 1e12 / PEAK_INT8_TOPS}
+
+
+def workload_hbm_passes(device):
+    """The HBM-bound passes at the workloads' largest sizes: calibration
+    absmax over 512 x 512 tokens (K = 5120 and 13824), activation quant at
+    4096 x 28672, weight absmax + quant of a 28672 x 8192 weight."""
+    import torch
+    from w8a8_post_quantization_channel_amd import capi, synth
+    out = {}
+    for k in (5120, 13824):
+        x = synth.device_activations(2100 + k, 512 * 512, k, synth.outlier_channels(2000 + k, k), device)
+        am = torch.empty(k, dtype=torch.float32, device=device)
+        ms = timed(lambda: capi.sq_calib_absmax(x, am, False), 5)
+        byts = x.numel() * 2 + k * 4
+        out[f"calib_absmax_262144x{k}"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
+                                           "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del x
+        torch.cuda.empty_cache()
+    m, k = 4096, 28672
+    x = torch.randn((m, k), device=device).to(torch.bfloat16)
+    inv_s = torch.rand(k, device=device) + 0.5
+    a = torch.full((4,), 0.05, device=device)
+    xq = torch.empty((m, k), dtype=torch.int8, device=device)
+    ms = timed(lambda: capi.sq_smooth_quant_act(x, inv_s, a, xq), 10)
+    byts = m * k * 3 + k * 4
+    out["act_quant_4096x28672"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
+                                   "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    n, k = 28672, 8192
+    w = (torch.randn((n, k), device=device) * 0.02).to(torch.bfloat16)
+    s = torch.rand(k, device=device) + 0.5
+    wm = torch.empty(k, dtype=torch.float32, device=device)
+    wq = torch.empty((n, k), dtype=torch.int8, device=device)
+    wsc = torch.empty(n, dtype=torch.float32, device=device)
+    ms = timed(lambda: capi.sq_calib_absmax(w, wm, False), 10)
+    byts = n * k * 2 + k * 4
+    out["weight_absmax_28672x8192"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
+                                       "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    ms = timed(lambda: capi.sq_quant_weight(w, s, wq, wsc), 10)
+    byts = n * k * 3 + k * 4 + n * 4
+    out["weight_quant_28672x8192"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
+                                      "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    for n, k in ((5120, 5120), (13824, 5120), (5120, 13824)):
+        w = (torch.randn((n, k), device=device) * 0.02).to(torch.bfloat16)
+        s = torch.rand(k, device=device) + 0.5
+        wq = torch.empty((n, k), dtype=torch.int8, device=device)
+        wsc = torch.empty(n, dtype=torch.float32, device=device)
+        ms = timed(lambda: capi.sq_quant_weight(w, s, wq, wsc), 20)
+        byts = n * k * 3 + k * 4 + n * 4
+        out[f"weight_quant_{n}x{k}"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
+                                        "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    # practical ceilings on the same tensor sizes: a plain copy (read = write)
+    # and a plain bf16 -> int8 conversion (2 bytes read per byte written, the
+    # traffic mix of the quantization passes), both torch kernels
+    x = torch.randn((4096, 28672), device=device).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    ms = timed(lambda: y.copy_(x), 10)
+    byts = x.numel() * 4
+    out["ceiling_copy_bf16_4096x28672"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
+                                           "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    yq = torch.empty(x.shape, dtype=torch.int8, device=device)
+    ms = timed(lambda: yq.copy_(x), 10)
+    byts = x.numel() * 3
+    out["ceiling_bf16_to_int8_4096x28672"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
+                                              "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    calib = [v for kk, v in out.items() if kk.startswith("calib")]
+    return {"metric": "HBM GB/s of the calibration absmax (512x512 tokens) and activation quant passes",
+            "value": min(v["GB/s"] for v in calib + [out["act_quant_4096x28672"]]), "unit": "GB/s",
+            "n_gpus": 1, "higher_is_better": True, "dtype": "bf16->fp32/int8", "data": "synthetic",
+            "config": {"workload": "largest HBM passes of the 13B calibration and 70B prefill workloads"},
+            "per_pass": out}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -149,6 +346,13 @@ def main():
     from w8a8_post_quantization_channel_amd import capi
     capi.load()  # fails loudly when libsq.so is missing
     device = torch.device("cuda", 0)
+    other = {"decode7b": workload_decode7b, "alpha_search": workload_alpha_search,
+             "prefill70b": workload_prefill70b, "hbm_passes": workload_hbm_passes}
+    if args.workload in other:
+        out = other[args.workload](device)
+        out["gpu"] = torch.cuda.get_device_name(0)
+        print(json.dumps(out), flush=True)
+        return
     groups, projs = setup(device)
     m = next(iter(groups.values())).x.shape[0]
 

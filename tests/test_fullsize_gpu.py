@@ -116,9 +116,9 @@ def check_search(mse_g, best_g, mse_o, best_o, rtol=1e-4):
     assert best_g == int(np.argmin(mse_g))
 
 
-@pytest.mark.parametrize("bf16", [True, False])
-def test_alpha_search_small(bf16):
-    k, n, rows = 512, 96, 128
+@pytest.mark.parametrize("bf16,rows", [(True, 128), (False, 128), (True, 40)])
+def test_alpha_search_small(bf16, rows):
+    k, n = 512, 96
     out = synth.outlier_channels(4500, k, count=2, fixed=50.0)
     xs = [synth.activations(4501 + b, rows, k, out, dist="t3", bf16=bf16) for b in range(2)]
     w = synth.weights(4510, n, k, bf16=bf16)

@@ -548,6 +548,81 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
     epi.end(st0);
 }
 
+// ---- skinny kernel (decode: m <= 64) -------------------------------------------
+//
+// The product is bound by streaming the int8 weight once from HBM. A block of
+// eight waves owns 16 output columns (16 weight rows) and all of K; wave w
+// takes every eighth 64-byte K step, so the eight waves read disjoint parts
+// of the same rows and their int32 partials are summed in LDS in a fixed
+// order (exact). v_mfma_i32_16x16x64_i8 with the m rows padded to 16 (MT
+// tiles of 16 rows): lane l holds row l % 16 and bytes 16 (l / 16) .. +15 of
+// a 64-byte K step, for both operands. Weight rows past n and activation rows
+// past m are clamped to the last valid row: their outputs are never stored.
+// Each lane keeps U K steps of weight bytes in flight.
+
+constexpr int kSkinnyWaves = 8;
+
+template <int MT, int U, class Epi>
+__global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(const int8_t* __restrict__ A,
+                                                                      const int8_t* __restrict__ B, int64_t M,
+                                                                      int64_t N, int64_t Kb, Epi epi) {
+    __shared__ v4i part[kSkinnyWaves][MT][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t brow = min<int64_t>(n0 + (lane & 15), N - 1);
+    const int kl = (lane >> 4) * 16;  // byte offset within a 64-byte K step
+    const int8_t* bp = B + brow * Kb + kl;
+    const int8_t* ap[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) ap[t] = A + min<int64_t>(16 * t + (lane & 15), M - 1) * Kb + kl;
+
+    v4i acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = v4i{0, 0, 0, 0};
+
+    const int64_t nsteps = Kb / 64;
+    // K steps of this wave: wave, wave + 8, wave + 16, ...
+    int64_t st = wave;
+    for (; st + (int64_t)kSkinnyWaves * (U - 1) < nsteps; st += (int64_t)kSkinnyWaves * U) {
+        v4i b[U], a[U][MT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t off = (st + (int64_t)u * kSkinnyWaves) * 64;
+            b[u] = __builtin_nontemporal_load((const v4i*)(bp + off));
+#pragma unroll
+            for (int t = 0; t < MT; ++t) a[u][t] = *(const v4i*)(ap[t] + off);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][t], b[u], acc[t], 0, 0, 0);
+    }
+    for (; st < nsteps; st += kSkinnyWaves) {
+        const int64_t off = st * 64;
+        const v4i b = __builtin_nontemporal_load((const v4i*)(bp + off));
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(*(const v4i*)(ap[t] + off), b, acc[t], 0, 0, 0);
+    }
+
+#pragma unroll
+    for (int t = 0; t < MT; ++t) part[wave][t][lane] = acc[t];
+    __syncthreads();
+    epi.begin();
+    if (wave == 0) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            v4i sum = part[0][t][lane];
+#pragma unroll
+            for (int w = 1; w < kSkinnyWaves; ++w) sum += part[w][t][lane];
+            // 16x16 accumulator: lane holds column lane % 16, rows 4 (lane / 16) + v
+            epi.template tile<16>(sum, 16 * t + 4 * (lane >> 4), n0 + (lane & 15));
+        }
+    }
+    __syncthreads();
+    epi.end((char*)part);
+}
+
 // Tile configurations.
 //   D256 / D224 / D192 / D160 / D128: the pipelined direct-to-LDS kernel,
 //         256 x BN tiles (BN = 32 * TN); the width is chosen per problem so the
@@ -561,9 +636,9 @@ struct Cfg {
 };
 using CfgS128 = Cfg<128, 128, 64, 64, 32>;
 
-enum TileCfg { kD256, kD224, kD192, kD160, kD128, kS128, kNumCfg };
-constexpr int kCfgBM[kNumCfg] = {256, 256, 256, 256, 256, 128};
-constexpr int kCfgBN[kNumCfg] = {256, 224, 192, 160, 128, 128};
+enum TileCfg { kD256, kD224, kD192, kD160, kD128, kS128, kNumCfg, kK16 = kNumCfg };
+constexpr int kCfgBM[kNumCfg + 1] = {256, 256, 256, 256, 256, 128, 64};
+constexpr int kCfgBN[kNumCfg + 1] = {256, 224, 192, 160, 128, 128, 16};
 // relative per-CU throughput of each tile shape, measured on MI355X over the
 // Llama-2 13B/70B prefill shapes (TOPS per busy CU, normalised to 256 x 192);
 // used only to rank candidates
@@ -586,8 +661,12 @@ int cu_count() {
 }
 
 // Pick the tiling with the least predicted time: (tile rounds over the CUs)
-// x (tile area) / (per-CU efficiency of that tile shape).
+// x (tile area) / (per-CU efficiency of that tile shape). Up to 64 rows of
+// activations (decode) the weight-streaming skinny kernel is used.
+constexpr int64_t kSkinnyMaxM = 64;
+
 TileCfg choose_cfg(int64_t M, int64_t N) {
+    if (M <= kSkinnyMaxM) return kK16;
     const int64_t cus = cu_count();
     TileCfg best = kS128;
     double best_cost = 0.0;
@@ -628,16 +707,32 @@ hipError_t launch_dma(const int8_t* A, const int8_t* B, int64_t M, int64_t N, in
     return hipGetLastError();
 }
 
+template <int MT, class Epi>
+hipError_t launch_skinny(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t Kb, Epi epi,
+                         hipStream_t stream) {
+    constexpr int U = MT == 1 ? 8 : 4;
+    gemm_skinny_kernel<MT, U, Epi>
+        <<<dim3((unsigned)((N + 15) / 16)), dim3(64 * kSkinnyWaves), 0, stream>>>(A, B, M, N, Kb, epi);
+    return hipGetLastError();
+}
+
 template <class Op, class Epi>
 hipError_t dispatch(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t Kb, Epi epi,
                     hipStream_t stream) {
+    if constexpr (std::is_same<Op, OpI8>::value) {
+        if (M <= kSkinnyMaxM) {
+            if (M <= 16) return launch_skinny<1>(A, B, M, N, Kb, epi, stream);
+            if (M <= 32) return launch_skinny<2>(A, B, M, N, Kb, epi, stream);
+            return launch_skinny<4>(A, B, M, N, Kb, epi, stream);
+        }
+    }
     switch (choose_cfg(M, N)) {
         case kD256: return launch_dma<Op, 8>(A, B, M, N, Kb, epi, stream);
         case kD224: return launch_dma<Op, 7>(A, B, M, N, Kb, epi, stream);
         case kD192: return launch_dma<Op, 6>(A, B, M, N, Kb, epi, stream);
         case kD160: return launch_dma<Op, 5>(A, B, M, N, Kb, epi, stream);
         case kD128: return launch_dma<Op, 4>(A, B, M, N, Kb, epi, stream);
-        default: return launch<Op, CfgS128>(A, B, M, N, Kb, epi, stream);
+        default: return launch<Op, CfgS128>(A, B, M, N, Kb, epi, stream);  // S128, and bf16 at m <= 64
     }
 }
 

@@ -68,6 +68,18 @@ struct OpBF16 {
     }
 };
 
+// 32-bit patterns of accumulator elements (taken by value: element access on
+// a vector is not an addressable object)
+__device__ __forceinline__ int as_bits(int v) { return v; }
+__device__ __forceinline__ int as_bits(float v) { return __float_as_int(v); }
+template <class E>
+__device__ __forceinline__ E from_bits(int v) {
+    if constexpr (std::is_same<E, float>::value)
+        return __int_as_float(v);
+    else
+        return v;
+}
+
 // Row of accumulator element v within an S x S output tile, relative to the
 // lane's first row (lane/32*4 for S = 32, lane/16*4 for S = 16); the column is
 // lane % S.
@@ -114,6 +126,60 @@ struct EpiDequant {
             }
         }
     }
+    // eight consecutive columns col .. col + 7 of one row (col % 8 == 0)
+    __device__ void row8(const int (&acc)[8], int64_t row, int64_t col) {
+        if (row >= M || col >= N) return;
+        const bool full = col + 8 <= N;
+        float c[8];
+        if (full && N % 4 == 0) {
+            const v4f s0 = *(const v4f*)(w_scale + col), s1 = *(const v4f*)(w_scale + col + 4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                c[k] = __fmul_rn(a, s0[k]);
+                c[k + 4] = __fmul_rn(a, s1[k]);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) c[k] = col + k < N ? __fmul_rn(a, w_scale[col + k]) : 0.0f;
+        }
+        float val[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) val[k] = __fmul_rn((float)acc[k], c[k]);
+        const int64_t idx = row * N + col;
+        if constexpr (kBF16Out) {
+            if (full && N % 8 == 0) {
+                u32x4 o;
+                o.x = sqd::f32_to_bf16_bits(val[0]) | (sqd::f32_to_bf16_bits(val[1]) << 16);
+                o.y = sqd::f32_to_bf16_bits(val[2]) | (sqd::f32_to_bf16_bits(val[3]) << 16);
+                o.z = sqd::f32_to_bf16_bits(val[4]) | (sqd::f32_to_bf16_bits(val[5]) << 16);
+                o.w = sqd::f32_to_bf16_bits(val[6]) | (sqd::f32_to_bf16_bits(val[7]) << 16);
+                *(u32x4*)((uint16_t*)y + idx) = o;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (col + k < N) ((uint16_t*)y)[idx + k] = (uint16_t)sqd::f32_to_bf16_bits(val[k]);
+            }
+        } else {
+            if (full && N % 4 == 0) {
+                *(v4f*)((float*)y + idx) = v4f{val[0], val[1], val[2], val[3]};
+                *(v4f*)((float*)y + idx + 4) = v4f{val[4], val[5], val[6], val[7]};
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (col + k < N) ((float*)y)[idx + k] = val[k];
+            }
+        }
+        if (acc_out) {
+            if (full && N % 4 == 0) {
+                *(v4i*)(acc_out + idx) = v4i{acc[0], acc[1], acc[2], acc[3]};
+                *(v4i*)(acc_out + idx + 4) = v4i{acc[4], acc[5], acc[6], acc[7]};
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (col + k < N) acc_out[idx + k] = acc[k];
+            }
+        }
+    }
     __device__ void end(char*) {}
 };
 
@@ -145,6 +211,17 @@ struct EpiSSE {
             }
         }
     }
+    __device__ void row8(const int (&acc)[8], int64_t row, int64_t col) {
+        if (row >= M) return;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (col + k < N) {
+                const float val = __fmul_rn((float)acc[k], __fmul_rn(a, w_scale[col + k]));
+                const double d = (double)val - (double)yref[row * N + col + k];
+                sum += d * d;
+            }
+        }
+    }
     __device__ void end(char* lds) {
         double* red = (double*)lds;
         red[threadIdx.x] = sum;
@@ -169,6 +246,18 @@ struct EpiStoreF32 {
         for (int v = 0; v < S * S / 64; ++v) {
             const int64_t row = row0 + acc_row<S>(v);
             if (row < M) y[row * N + col] = (float)acc[v];
+        }
+    }
+    __device__ void row8(const float (&acc)[8], int64_t row, int64_t col) {
+        if (row >= M || col >= N) return;
+        const int64_t idx = row * N + col;
+        if (col + 8 <= N && N % 4 == 0) {
+            *(v4f*)(y + idx) = v4f{acc[0], acc[1], acc[2], acc[3]};
+            *(v4f*)(y + idx + 4) = v4f{acc[4], acc[5], acc[6], acc[7]};
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (col + k < N) y[idx + k] = acc[k];
         }
     }
     __device__ void end(char*) {}
@@ -310,28 +399,38 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(const 
 //
 // Block tile 256 x BN (BN = 32 * TN), four waves, wave w owning output rows
 // [64w, 64w + 64) x all BN columns: 2 x TN accumulators of 32 x 32 (int32, in
-// AGPRs), one wave per SIMD. K advances in 64-byte steps through a ring of
-// four LDS stages filled by buffer_load ... lds (global -> LDS without
-// VGPRs): the loads for step k + 3 are issued while step k is multiplied, so
-// three steps of memory latency are hidden. Rows of A or B beyond M or N lie
-// outside the per-tile buffer descriptor and read as zero; the stage is
-// padded to a multiple of 64 rows (the padding rows are such out-of-range B
-// rows) so every wave issues the same number of loads.
+// AGPRs), one wave per SIMD. K advances in 128-byte steps through a ring of
+// NS LDS stages (three when they fit in LDS, else two) filled by
+// buffer_load ... lds (global -> LDS without VGPRs): the loads for step
+// k + NS - 1 are issued while step k is multiplied.
 //
-// LDS stage layout: rows of 64 bytes (A rows 0..255, then B rows), 16-byte
-// chunk c of row r stored at position c ^ ((r >> 2) & 3): sixteen consecutive
-// rows then cover all sixteen 16-byte bank groups, for any chunk. One load
-// instruction fills 16 consecutive rows (1 KB, lane q -> bytes 16q..16q+15,
-// i.e. row q/4, position q%4), so lane q fetches logical chunk
-// (q % 4) ^ ((q >> 4) & 3) of its row. An MFMA fragment read (lane l: row
-// l % 32, chunk 2*substep + l / 32) is then conflict-free.
+// A step moves whole 128-byte row segments: every 128-byte cache line fetched
+// from L2 is used in full by one instruction. (With 64-byte steps each request
+// used half a line and the L2 -> LDS stream alone ran at about 60% of this
+// rate.) Rows of A or B beyond M or N lie outside the per-tile buffer
+// descriptor and read as zero; when k is an odd multiple of 64 bytes the upper
+// half of the last step is redirected out of range too, so it reads as zero.
 //
-// Each K step is one basic block in the steady state: the fragment reads for
-// the next substep are interleaved one per MFMA (sched_group_barrier), and one
-// barrier per step publishes the next stage after an explicit vmcnt wait.
+// LDS stage layout: rows of 128 bytes (A rows 0..255, then B rows), 16-byte
+// chunk c of row r stored at position c ^ (r & 7). One load instruction
+// fills 8 consecutive rows (1 KB; lane q -> bytes 16q..16q+15, i.e. row q/8,
+// position q%8), so lane q fetches logical chunk (q % 8) ^ (q / 8) of its
+// row. An MFMA fragment read (lane l: row l % 32, chunk 2*substep + l / 32)
+// then touches eight different positions in every group of eight rows.
+//
+// Each step is a fixed instruction stream: MFMAs with the fragment reads of the
+// next substep and the loads of a later step interleaved between them, and
+// one barrier per step that publishes the next stage after an explicit vmcnt
+// wait.
 
-constexpr int kDmaBK = 64;      // bytes of K per stage
+constexpr int kDmaBK = 128;     // bytes of K per stage
 constexpr int kDmaBM = 256;     // rows of A per tile (4 waves x 64)
+constexpr int kLdsBytes = 160 * 1024;
+
+template <int TN>
+constexpr int dma_stages() {
+    return 3 * (kDmaBM + 32 * TN) * kDmaBK <= kLdsBytes ? 3 : 2;
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -351,6 +450,10 @@ __device__ __forceinline__ v4i tile_rsrc(const int8_t* base, int64_t rows_valid,
     return r;
 }
 
+// An offset past every panel's num_records (panels hold at most 256 rows of
+// at most 2^18 bytes): a load from it returns zeros.
+constexpr int kOutOfRange = 0x70000000;
+
 // 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16*lane.
 // Written as asm so that the only waits on these loads are the explicit
 // s_waitcnt vmcnt(...) placed before the barriers that publish each stage
@@ -369,25 +472,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// scheduling-group masks (LLVM AMDGPU)
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
 
 template <class Op, int TN, class Epi>
 __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                                        int64_t M, int64_t N, int64_t Kb, int tiles_m, int tiles_n,
                                                        Epi epi) {
     constexpr int BM = kDmaBM, BN = 32 * TN;
-    constexpr int ROWS = (BM + BN + 63) / 64 * 64;   // padded to whole load rounds
+    constexpr int ROWS = BM + BN;                    // a multiple of 32: whole load rounds
     constexpr int STAGE = ROWS * kDmaBK;
-    constexpr int L = ROWS / 64;                     // 1 KB loads per wave per stage
+    constexpr int NS = dma_stages<TN>();
+    constexpr int L = ROWS / 32;                     // 1 KB loads per wave per stage
+    constexpr int LA = BM / 32;                      // ... of which A rows
     constexpr int NFA = 2, NFB = TN, NF = NFA + NFB; // fragment reads per substep
     constexpr int NMMA = 2 * TN;                     // MFMAs per substep
+    constexpr int NSUB = kDmaBK / 32;                // MFMA substeps per step
     static_assert(NF <= NMMA + 2, "fragment reads interleave with the MFMAs");
-    __shared__ __attribute__((aligned(1024))) char st0[STAGE];
-    __shared__ __attribute__((aligned(1024))) char st1[STAGE];
-    __shared__ __attribute__((aligned(1024))) char st2[STAGE];
-    __shared__ __attribute__((aligned(1024))) char st3[STAGE];
+    static_assert((NS - 2) * L < 64, "vmcnt range");
+    static_assert(4 * 32 * BN * 4 <= NS * STAGE, "the epilogue transpose fits in the stages");
+    __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
 
     const int lane = threadIdx.x & 63;
     // the wave index is uniform across the wave; saying so keeps the load
@@ -413,25 +515,32 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
     const v4i ra = tile_rsrc(A + m0 * Kb, min<int64_t>(BM, M - m0), Kb);
     const v4i rb = tile_rsrc(B + n0 * Kb, min<int64_t>(BN, N - n0), Kb);
 
-    // per-lane byte offset (within its panel) of each load this wave issues;
-    // load j of wave w fills stage rows [16 (4j + w), 16 (4j + w) + 16), which
-    // are A rows exactly when j < BM / 64
-    static_assert(BM % 64 == 0, "A rows fill whole load rounds");
+    // load j of wave w fills stage rows [8 (4j + w), 8 (4j + w) + 8), which
+    // are A rows exactly when j < LA
+    const int chunk = (lane & 7) ^ (lane >> 3);
     int voff[L];
-    uint32_t ldsoff[L];
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-        const int g = 4 * j + wave;
-        const int row = g * 16 + (lane >> 2);
-        const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
-        voff[j] = (j * 64 < BM ? row : row - BM) * (int)Kb + chunk * 16;
-        ldsoff[j] = (uint32_t)(g * 1024);
+        const int row = (4 * j + wave) * 8 + (lane >> 3);
+        voff[j] = (j < LA ? row : row - BM) * (int)Kb + chunk * 16;
     }
-    auto issue = [&](const char* stage, int64_t kstep) {
+    const int64_t nk = (Kb + kDmaBK - 1) / kDmaBK;
+    // k an odd multiple of 64 bytes: chunks 4..7 of the last step lie past k
+    const bool half_tail = (Kb % kDmaBK) != 0;
+    const bool hi_chunk = chunk >= 4;
+    // stages are addressed by byte offset into lds (a uniform value computed
+    // each step, so fragment addresses are one VGPR per substep plus an
+    // immediate offset)
+    // load j of step kstep into stage; `skip` (steps past the end) reads zeros
+    auto dma = [&](int j, uint32_t stage, int64_t kstep, bool skip) {
         const int soff = (int)(kstep * kDmaBK);
-        const uint32_t base = lds_addr(stage);
+        const uint32_t base = lds_addr(lds) + stage + (uint32_t)wave * 1024u;
+        const bool cut = skip || (half_tail && kstep == nk - 1 && hi_chunk);
+        dma16(j < LA ? ra : rb, base + (uint32_t)(j * 4096), cut ? kOutOfRange : voff[j], soff);
+    };
+    auto issue = [&](uint32_t stage, int64_t kstep, bool skip) {
 #pragma unroll
-        for (int j = 0; j < L; ++j) dma16(j * 64 < BM ? ra : rb, base + ldsoff[j], voff[j], soff);
+        for (int j = 0; j < L; ++j) dma(j, stage, kstep, skip);
     };
 
     using Acc = typename Op::template acc_t<32>;
@@ -442,110 +551,116 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
         for (int j = 0; j < TN; ++j) acc[i][j] = Acc{};
 
     // fragment addresses within a stage: row (lane % 32) of each 32-row block,
-    // chunk 2*ks + lane/32 at position ^ ((row >> 2) & 3) = ^ ((lane >> 2) & 3)
+    // chunk 2*ks + lane/32 at position ^ (row & 7) = ^ (lane & 7)
     const int frow = lane & 31;
-    const int sw = (lane >> 2) & 3;
+    const int c0 = (lane >> 5) ^ (lane & 7);  // chunk 2*ks + lane/32 lands at position c0 ^ 2*ks
     const int a_off = (wave * 64 + frow) * kDmaBK;
-    const int b_off = (BM + frow) * kDmaBK;
-    v4i fa[2][NFA], fb[2][NFB];  // [substep][tile]
-    auto read_frag = [&](const char* stage, int ks, int f) {
-        const int ch = ((2 * ks + (lane >> 5)) ^ sw) << 4;
+    const int b_off = frow * kDmaBK;
+    v4i fa[2][NFA], fb[2][NFB];  // [substep parity][tile]
+    auto read_frag = [&](uint32_t stage, int ks, int f) {
+        const int ch = (c0 ^ (2 * ks)) << 4;
+        const char* p = lds + stage;
         if (f < NFA)
-            fa[ks][f] = *(const v4i*)(stage + a_off + f * 32 * kDmaBK + ch);
+            fa[ks & 1][f] = *(const v4i*)(p + (a_off + ch) + f * 32 * kDmaBK);
         else
-            fb[ks][f - NFA] = *(const v4i*)(stage + b_off + (f - NFA) * 32 * kDmaBK + ch);
+            fb[ks & 1][f - NFA] = *(const v4i*)(p + (b_off + ch) + (BM + (f - NFA) * 32) * kDmaBK);
     };
-    auto read_frags = [&](const char* stage, int ks) {
+    auto read_frags = [&](uint32_t stage, int ks) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) read_frag(stage, ks, f);
-    };
-    auto mma = [&](int ks) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = Op::template mfma<32>(fa[ks][i], fb[ks][j], acc[i][j]);
-    };
-    // MFMAs of substep `ks` with the NF reads of (stage, rks) interleaved
-    auto mma_with_reads = [&](int ks, const char* stage, int rks) {
-        read_frags(stage, rks);
-        mma(ks);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMMA - NF > 0 ? NMMA - NF : 0, 0);
     };
     auto publish = [&]() {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
     };
-
-    const int64_t nk = Kb / kDmaBK;  // k is a multiple of 64 elements
-    // prologue: steps 0..2 in flight, then publish step 0
-    issue(st0, 0);
-    if (nk > 1) issue(st1, 1);
-    if (nk > 2) issue(st2, 2);
-    if (nk > 2) wait_vmcnt<2 * L>();
-    else if (nk > 1) wait_vmcnt<L>();
+    // prologue: steps 0 .. NS-2 in flight, then publish step 0
+    issue(0, 0, false);
+    if (NS == 3) issue(STAGE, 1, nk < 2);
+    if (NS == 3) wait_vmcnt<L>();
     else wait_vmcnt<0>();
     publish();
-    read_frags(st0, 0);
+    read_frags(0, 0);
 
-    // steady state: step kb on stage S, with steps kb+1 .. kb+3 in range
-    auto steady = [&](auto S_, int64_t kb) {
-        constexpr int S = decltype(S_)::value;
-        const char* cur = S == 0 ? st0 : S == 1 ? st1 : S == 2 ? st2 : st3;
-        const char* nxt = S == 0 ? st1 : S == 1 ? st2 : S == 2 ? st3 : st0;
-        const char* fill = S == 0 ? st3 : S == 1 ? st0 : S == 2 ? st1 : st2;
-        issue(fill, kb + 3);
-        mma_with_reads(0, cur, 1);
-        wait_vmcnt<2 * L>();  // step kb+1 landed (for this wave); kb+2, kb+3 may fly
-        publish();            // ... and for every wave
-        mma_with_reads(1, nxt, 0);
-    };
-    // tail step: fewer than three steps ahead
-    auto tail = [&](auto S_, int64_t kb) {
-        constexpr int S = decltype(S_)::value;
-        const char* cur = S == 0 ? st0 : S == 1 ? st1 : S == 2 ? st2 : st3;
-        const char* nxt = S == 0 ? st1 : S == 1 ? st2 : S == 2 ? st3 : st0;
-        read_frags(cur, 1);
-        mma(0);
-        if (kb + 1 < nk) {
-            if (kb + 2 < nk) wait_vmcnt<L>();
-            else wait_vmcnt<0>();
-            publish();
-            read_frags(nxt, 0);
+    // One step, in a fixed instruction order (sched_barrier between slots):
+    // NSUB substeps of NMMA MFMAs; after MFMA m of a substep comes fragment
+    // read m of the next substep (m < NF), and across the first NSUB - 1
+    // substeps every DSTRIDE-th slot issues one of the L loads of step
+    // kb + NS - 1 into the stage read during step kb - 1, so the loads queue
+    // behind the matrix cores instead of stalling them. Before the last
+    // substep: wait for step kb + 1 and publish it; the last substep reads
+    // the first fragments of that stage (stale but in bounds after the last
+    // step). Steps past the end load zeros, so every step has the same
+    // instruction stream.
+    constexpr int DSTRIDE = (NSUB - 1) * NMMA / L > 0 ? (NSUB - 1) * NMMA / L : 1;
+    static_assert((L - 1) * DSTRIDE < (NSUB - 1) * NMMA, "the loads fit in the first substeps");
+    uint32_t cur = 0, nxt = STAGE, fill = (NS - 1) * STAGE;  // stages of kb, kb + 1, kb + NS - 1
+    for (int64_t kb = 0; kb < nk; ++kb) {
+        const bool more = kb + NS - 1 < nk;
+#pragma unroll
+        for (int ks = 0; ks < NSUB; ++ks) {
+            if (ks == NSUB - 1 && kb + 1 < nk) {
+                if (NS == 3) wait_vmcnt<(NS - 2) * L>();
+                else wait_vmcnt<0>();
+                publish();
+            }
+            const uint32_t rstage = ks + 1 < NSUB ? cur : nxt;
+            const int rks = (ks + 1) % NSUB;
+#pragma unroll
+            for (int m = 0; m < NMMA; ++m) {
+                const int i = m / TN, j = m % TN;
+                // W rows as the first operand: acc[i][j] is the transposed
+                // 32 x 32 block (lane: one output row, four consecutive columns)
+                acc[i][j] = Op::template mfma<32>(fb[ks & 1][j], fa[ks & 1][i], acc[i][j]);
+                if (m < NF) read_frag(rstage, rks, m);
+                const int slot = ks * NMMA + m;
+                if (ks + 1 < NSUB && slot % DSTRIDE == 0 && slot / DSTRIDE < L)
+                    dma(slot / DSTRIDE, fill, kb + NS - 1, !more);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        mma(1);
-    };
-    int64_t kb = 0;
-    for (; kb + 6 < nk; kb += 4) {
-        steady(std::integral_constant<int, 0>{}, kb);
-        steady(std::integral_constant<int, 1>{}, kb + 1);
-        steady(std::integral_constant<int, 2>{}, kb + 2);
-        steady(std::integral_constant<int, 3>{}, kb + 3);
+        const uint32_t was = cur;
+        cur = nxt;
+        nxt = NS == 3 ? fill : was;
+        fill = was;
     }
-    // the remaining steps (at most six), stage = kb % 4 with kb % 4 == 0 here
-    if (kb + 3 < nk) steady(std::integral_constant<int, 0>{}, kb++);
-    else if (kb < nk) tail(std::integral_constant<int, 0>{}, kb++);
-    if (kb + 3 < nk) steady(std::integral_constant<int, 1>{}, kb++);
-    else if (kb < nk) tail(std::integral_constant<int, 1>{}, kb++);
-    if (kb + 3 < nk) steady(std::integral_constant<int, 2>{}, kb++);
-    else if (kb < nk) tail(std::integral_constant<int, 2>{}, kb++);
-    if (kb < nk) tail(std::integral_constant<int, 3>{}, kb++);
-    if (kb < nk) tail(std::integral_constant<int, 0>{}, kb++);
-    if (kb < nk) tail(std::integral_constant<int, 1>{}, kb++);
+    wait_vmcnt<0>();  // zero-fill loads past the end may still be in flight
 
+    // Epilogue: lane l holds, for row (l % 32) of each 32-row block i and
+    // column block j, columns 8g + 4 (l / 32) + 0..3 in acc[i][j][4g .. 4g+3].
+    // Each wave transposes one 32 x BN block at a time through its own LDS
+    // area (16-byte chunk c of row r at position c ^ (r & 7)), then hands the
+    // epilogue eight consecutive columns per lane for 16-byte row stores.
+    __syncthreads();  // every wave is done with the stages
+    using E = typename std::conditional<std::is_same<Op, OpI8>::value, int, float>::type;
+    char* tw = lds + wave * (32 * BN * 4);
+    const int h = lane >> 5;
+    constexpr int G8 = BN / 8;  // eight-column groups per row
     epi.begin();
-    const int64_t rbase = m0 + wave * 64 + 4 * (lane >> 5);
-    const int64_t cbase = n0 + frow;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) epi.template tile<32>(acc[i][j], rbase + i * 32, cbase + j * 32);
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c = 8 * j + 2 * g + h;
+                const Acc& t = acc[i][j];
+                const v4i o = {as_bits(t[4 * g + 0]), as_bits(t[4 * g + 1]), as_bits(t[4 * g + 2]),
+                               as_bits(t[4 * g + 3])};
+                *(v4i*)(tw + frow * (BN * 4) + ((c ^ (frow & 7)) << 4)) = o;
+            }
+#pragma unroll
+        for (int it = 0; it < 32 * G8 / 64; ++it) {
+            const int t = it * 64 + lane;
+            const int r = t / G8, q = t % G8;
+            const v4i lo = *(const v4i*)(tw + r * (BN * 4) + (((2 * q) ^ (r & 7)) << 4));
+            const v4i hi = *(const v4i*)(tw + r * (BN * 4) + (((2 * q + 1) ^ (r & 7)) << 4));
+            const E v[8] = {from_bits<E>(lo.x), from_bits<E>(lo.y), from_bits<E>(lo.z), from_bits<E>(lo.w),
+                            from_bits<E>(hi.x), from_bits<E>(hi.y), from_bits<E>(hi.z), from_bits<E>(hi.w)};
+            epi.row8(v, m0 + wave * 64 + i * 32 + r, n0 + 8 * q);
+        }
+    }
     __syncthreads();
-    epi.end(st0);
+    epi.end(lds);
 }
 
 // ---- skinny kernel (decode: m <= 64) -------------------------------------------

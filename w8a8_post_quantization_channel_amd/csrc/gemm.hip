@@ -126,57 +126,66 @@ struct EpiDequant {
             }
         }
     }
-    // eight consecutive columns col .. col + 7 of one row (col % 8 == 0)
-    __device__ void row8(const int (&acc)[8], int64_t row, int64_t col) {
-        if (row >= M || col >= N) return;
-        const bool full = col + 8 <= N;
+    // Eight consecutive columns col .. col + 7 (col % 8 == 0) owned by one
+    // lane for a run of rows: their merged scales are loaded once.
+    struct Cols {
         float c[8];
-        if (full && N % 4 == 0) {
+        int64_t col;
+    };
+    __device__ Cols cols8(int64_t col) {
+        Cols cc;
+        cc.col = col;
+        if (col + 8 <= N && N % 4 == 0) {
             const v4f s0 = *(const v4f*)(w_scale + col), s1 = *(const v4f*)(w_scale + col + 4);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                c[k] = __fmul_rn(a, s0[k]);
-                c[k + 4] = __fmul_rn(a, s1[k]);
+                cc.c[k] = __fmul_rn(a, s0[k]);
+                cc.c[k + 4] = __fmul_rn(a, s1[k]);
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) c[k] = col + k < N ? __fmul_rn(a, w_scale[col + k]) : 0.0f;
+            for (int k = 0; k < 8; ++k) cc.c[k] = col + k < N ? __fmul_rn(a, w_scale[col + k]) : 0.0f;
         }
+        return cc;
+    }
+    // fast: the caller's whole tile lies inside M x N and N % 8 == 0 (a
+    // uniform condition), so no bounds checks and 16-byte stores
+    __device__ void row8(const int (&acc)[8], int64_t row, const Cols& cc, bool fast) {
+        const int64_t col = cc.col;
         float val[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) val[k] = __fmul_rn((float)acc[k], c[k]);
+        for (int k = 0; k < 8; ++k) val[k] = __fmul_rn((float)acc[k], cc.c[k]);
         const int64_t idx = row * N + col;
-        if constexpr (kBF16Out) {
-            if (full && N % 8 == 0) {
+        if (fast) {
+            if constexpr (kBF16Out) {
+                // y is a product of a nonzero integer and a scale of at
+                // least 1e-5 / 127 squared, or zero: never subnormal, so the
+                // hardware rounding equals f32_to_bf16_bits here
                 u32x4 o;
-                o.x = sqd::f32_to_bf16_bits(val[0]) | (sqd::f32_to_bf16_bits(val[1]) << 16);
-                o.y = sqd::f32_to_bf16_bits(val[2]) | (sqd::f32_to_bf16_bits(val[3]) << 16);
-                o.z = sqd::f32_to_bf16_bits(val[4]) | (sqd::f32_to_bf16_bits(val[5]) << 16);
-                o.w = sqd::f32_to_bf16_bits(val[6]) | (sqd::f32_to_bf16_bits(val[7]) << 16);
+                o.x = sqd::pack_bf16x2(val[0], val[1]);
+                o.y = sqd::pack_bf16x2(val[2], val[3]);
+                o.z = sqd::pack_bf16x2(val[4], val[5]);
+                o.w = sqd::pack_bf16x2(val[6], val[7]);
                 *(u32x4*)((uint16_t*)y + idx) = o;
             } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if (col + k < N) ((uint16_t*)y)[idx + k] = (uint16_t)sqd::f32_to_bf16_bits(val[k]);
-            }
-        } else {
-            if (full && N % 4 == 0) {
                 *(v4f*)((float*)y + idx) = v4f{val[0], val[1], val[2], val[3]};
                 *(v4f*)((float*)y + idx + 4) = v4f{val[4], val[5], val[6], val[7]};
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if (col + k < N) ((float*)y)[idx + k] = val[k];
             }
-        }
-        if (acc_out) {
-            if (full && N % 4 == 0) {
+            if (acc_out) {
                 *(v4i*)(acc_out + idx) = v4i{acc[0], acc[1], acc[2], acc[3]};
                 *(v4i*)(acc_out + idx + 4) = v4i{acc[4], acc[5], acc[6], acc[7]};
-            } else {
+            }
+            return;
+        }
+        if (row >= M) return;
 #pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if (col + k < N) acc_out[idx + k] = acc[k];
+        for (int k = 0; k < 8; ++k) {
+            if (col + k < N) {
+                if constexpr (kBF16Out)
+                    ((uint16_t*)y)[idx + k] = (uint16_t)sqd::f32_to_bf16_bits(val[k]);
+                else
+                    ((float*)y)[idx + k] = val[k];
+                if (acc_out) acc_out[idx + k] = acc[k];
             }
         }
     }
@@ -211,13 +220,24 @@ struct EpiSSE {
             }
         }
     }
-    __device__ void row8(const int (&acc)[8], int64_t row, int64_t col) {
+    struct Cols {
+        float c[8];
+        int64_t col;
+    };
+    __device__ Cols cols8(int64_t col) {
+        Cols cc;
+        cc.col = col;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) cc.c[k] = col + k < N ? __fmul_rn(a, w_scale[col + k]) : 0.0f;
+        return cc;
+    }
+    __device__ void row8(const int (&acc)[8], int64_t row, const Cols& cc, bool) {
         if (row >= M) return;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            if (col + k < N) {
-                const float val = __fmul_rn((float)acc[k], __fmul_rn(a, w_scale[col + k]));
-                const double d = (double)val - (double)yref[row * N + col + k];
+            if (cc.col + k < N) {
+                const float val = __fmul_rn((float)acc[k], cc.c[k]);
+                const double d = (double)val - (double)yref[row * N + cc.col + k];
                 sum += d * d;
             }
         }
@@ -248,17 +268,22 @@ struct EpiStoreF32 {
             if (row < M) y[row * N + col] = (float)acc[v];
         }
     }
-    __device__ void row8(const float (&acc)[8], int64_t row, int64_t col) {
-        if (row >= M || col >= N) return;
+    struct Cols {
+        int64_t col;
+    };
+    __device__ Cols cols8(int64_t col) { return Cols{col}; }
+    __device__ void row8(const float (&acc)[8], int64_t row, const Cols& cc, bool fast) {
+        const int64_t col = cc.col;
         const int64_t idx = row * N + col;
-        if (col + 8 <= N && N % 4 == 0) {
+        if (fast) {
             *(v4f*)(y + idx) = v4f{acc[0], acc[1], acc[2], acc[3]};
             *(v4f*)(y + idx + 4) = v4f{acc[4], acc[5], acc[6], acc[7]};
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (col + k < N) y[idx + k] = acc[k];
+            return;
         }
+        if (row >= M) return;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (col + k < N) y[idx + k] = acc[k];
     }
     __device__ void end(char*) {}
 };
@@ -512,6 +537,17 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
     const int tm = group * GM + in_group % group_rows, tn = in_group / group_rows;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
+    // epilogue geometry: after the transpose, lane -> (row lane / G8 of each
+    // round, eight-column group lane % G8); its scales are fetched now so
+    // their latency hides under the main loop
+    constexpr int G8 = BN / 8;     // eight-column groups per row
+    constexpr int RPI = 64 / G8;   // rows per read-back round
+    constexpr int ROUNDS = (32 + RPI - 1) / RPI;
+    const int q = lane % G8, rsub = lane / G8;
+    const bool active = lane < RPI * G8;
+    epi.begin();
+    const auto cc = epi.cols8(n0 + 8 * q);
+
     const v4i ra = tile_rsrc(A + m0 * Kb, min<int64_t>(BM, M - m0), Kb);
     const v4i rb = tile_rsrc(B + n0 * Kb, min<int64_t>(BN, N - n0), Kb);
 
@@ -634,8 +670,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
     using E = typename std::conditional<std::is_same<Op, OpI8>::value, int, float>::type;
     char* tw = lds + wave * (32 * BN * 4);
     const int h = lane >> 5;
-    constexpr int G8 = BN / 8;  // eight-column groups per row
-    epi.begin();
+    const bool fast = m0 + BM <= M && n0 + BN <= N && N % 8 == 0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -648,15 +683,21 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
                                as_bits(t[4 * g + 3])};
                 *(v4i*)(tw + frow * (BN * 4) + ((c ^ (frow & 7)) << 4)) = o;
             }
-#pragma unroll
-        for (int it = 0; it < 32 * G8 / 64; ++it) {
-            const int t = it * 64 + lane;
-            const int r = t / G8, q = t % G8;
+        auto rows = [&](int it, bool fast_rows) {
+            const int r = it * RPI + rsub;
+            if (!active || r >= 32) return;
             const v4i lo = *(const v4i*)(tw + r * (BN * 4) + (((2 * q) ^ (r & 7)) << 4));
             const v4i hi = *(const v4i*)(tw + r * (BN * 4) + (((2 * q + 1) ^ (r & 7)) << 4));
             const E v[8] = {from_bits<E>(lo.x), from_bits<E>(lo.y), from_bits<E>(lo.z), from_bits<E>(lo.w),
                             from_bits<E>(hi.x), from_bits<E>(hi.y), from_bits<E>(hi.z), from_bits<E>(hi.w)};
-            epi.row8(v, m0 + wave * 64 + i * 32 + r, n0 + 8 * q);
+            epi.row8(v, m0 + wave * 64 + i * 32 + r, cc, fast_rows);
+        };
+        if (fast) {
+#pragma unroll
+            for (int it = 0; it < ROUNDS; ++it) rows(it, true);
+        } else {
+#pragma unroll 1
+            for (int it = 0; it < ROUNDS; ++it) rows(it, false);
         }
     }
     __syncthreads();
@@ -755,9 +796,10 @@ enum TileCfg { kD256, kD224, kD192, kD160, kD128, kS128, kNumCfg, kK16 = kNumCfg
 constexpr int kCfgBM[kNumCfg + 1] = {256, 256, 256, 256, 256, 128, 64};
 constexpr int kCfgBN[kNumCfg + 1] = {256, 224, 192, 160, 128, 128, 16};
 // relative per-CU throughput of each tile shape, measured on MI355X over the
-// Llama-2 13B/70B prefill shapes (TOPS per busy CU, normalised to 256 x 192);
-// used only to rank candidates
-constexpr double kCfgEff[kNumCfg] = {0.82, 0.78, 1.00, 0.99, 0.88, 0.60};
+// Llama-2 13B/70B prefill shapes (TOPS with many tiles per CU, normalised to
+// 256 x 128; the two-stage widths 192 and 224 are the weakest); used only to
+// rank candidates
+constexpr double kCfgEff[kNumCfg] = {0.97, 0.88, 0.88, 0.95, 1.00, 0.60};
 
 template <class C>
 constexpr int threads_of() {

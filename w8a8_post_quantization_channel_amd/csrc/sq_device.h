@@ -21,12 +21,22 @@ constexpr float kQmax = 127.0f;  // symmetric int8 range [-127, 127]
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// round-to-nearest-even fp32 -> bf16 bit pattern (NaN kept quiet)
+// round-to-nearest-even fp32 -> bf16 bit pattern (NaN kept quiet); written
+// as a select so it compiles without branches
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (u >> 16) | 0x40u;
+    return (u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded;
+}
+
+// two fp32 values -> packed bf16 pair (low half = lo), one v_cvt_pk_bf16_f32:
+// round-to-nearest-even like f32_to_bf16_bits for every normal value, zero
+// and infinity
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // symmetric int8 code of an already scaled value

@@ -181,7 +181,7 @@ def test_quant_act_ties():
 
 GEMM_CASES = [(1, 16, 64), (5, 48, 1088), (129, 257, 320), (300, 600, 2048), (512, 8192, 128),
               (1024, 8192, 256), (2100, 4112, 192), (2048, 7168, 64), (2048, 11008, 128), (4096, 4096, 64),
-              (4000, 4100, 64)]
+              (4000, 4100, 64), (1000, 11008, 320)]
 
 
 def reachable_tilings():

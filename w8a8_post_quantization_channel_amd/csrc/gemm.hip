@@ -799,7 +799,7 @@ constexpr int kCfgBN[kNumCfg + 1] = {256, 224, 192, 160, 128, 128, 16};
 // Llama-2 13B/70B prefill shapes (TOPS with many tiles per CU, normalised to
 // 256 x 128; the two-stage widths 192 and 224 are the weakest); used only to
 // rank candidates
-constexpr double kCfgEff[kNumCfg] = {0.97, 0.88, 0.88, 0.95, 1.00, 0.60};
+constexpr double kCfgEff[kNumCfg] = {0.97, 0.88, 0.88, 0.95, 1.00, 0.45};
 
 template <class C>
 constexpr int threads_of() {

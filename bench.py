@@ -386,7 +386,7 @@ def main():
         traffic = json.load(open(args.traffic)).get("bytes_per_launch")
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                 "frac": achieved / PEAK_INT8_TOPS, "traffic": traffic,
-                "kernel": "gemm_kernel<OpI8, BMxBN, EpiDequant<bf16>>",
+                "kernel": "gemm_dma_kernel<OpI8, TN, EpiDequant<bf16>> (256 x 32*TN tiles)",
                 "tiling": {n: list(capi.sq_gemm_tiling(m, layer.n)) for n, _, layer, _ in projs},
                 "avg_launch_us": avg_launch_ms * 1e3,
                 "per_projection_tops": {n: ops_by_name[n] / (sum(v) / len(v) * 1e-3) / 1e12

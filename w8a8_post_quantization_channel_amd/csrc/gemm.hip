@@ -158,9 +158,9 @@ struct EpiDequant {
         const int64_t idx = row * N + col;
         if (fast) {
             if constexpr (kBF16Out) {
-                // y is a product of a nonzero integer and a scale of at
-                // least 1e-5 / 127 squared, or zero: never subnormal, so the
-                // hardware rounding equals f32_to_bf16_bits here
+                // y is zero or a nonzero integer times a * ws >= 6e-20
+                // (a >= 1e-10 / 127, ws >= 1e-5 / 127): never subnormal, so
+                // the hardware rounding equals f32_to_bf16_bits here
                 u32x4 o;
                 o.x = sqd::pack_bf16x2(val[0], val[1]);
                 o.y = sqd::pack_bf16x2(val[2], val[3]);

@@ -31,6 +31,11 @@
 namespace {
 
 using sqd::u32x4;
+using sqd::dma16;
+using sqd::kOutOfRange;
+using sqd::lds_addr;
+using sqd::tile_rsrc;
+using sqd::wait_vmcnt;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -456,47 +461,6 @@ template <int TN>
 constexpr int dma_stages() {
     return 3 * (kDmaBM + 32 * TN) * kDmaBK <= kLdsBytes ? 3 : 2;
 }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Raw buffer descriptor (stride 0) over one tile's panel: offsets at or past
-// num_records = valid bytes read as zero.
-__device__ __forceinline__ v4i tile_rsrc(const int8_t* base, int64_t rows_valid, int64_t kb) {
-    const uint64_t b = (uint64_t)base;
-    v4i r;
-    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    r.z = __builtin_amdgcn_readfirstlane((int)(rows_valid * kb));
-    r.w = 0x00020000;
-    return r;
-}
-
-// An offset past every panel's num_records (panels hold at most 256 rows of
-// at most 2^18 bytes): a load from it returns zeros.
-constexpr int kOutOfRange = 0x70000000;
-
-// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16*lane.
-// Written as asm so that the only waits on these loads are the explicit
-// s_waitcnt vmcnt(...) placed before the barriers that publish each stage
-// (the compiler would otherwise drain every load in flight before reading
-// any stage). No register receives the data.
-__device__ __forceinline__ void dma16(const v4i& rsrc, uint32_t lds, int voff, int soff) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "buffer_load_dwordx4 %1, %2, %3 offen lds"
-        :
-        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-        : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
 
 template <class Op, int TN, class Epi>
 __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,

@@ -1,11 +1,11 @@
 // quant.hip -- the two quantization passes of the SmoothQuant W8A8 layer.
 //
 // quant_weight: offline fold W' = W diag(s) (kwkr.cn blog §3.2) and symmetric
-//   int8 with one scale per output row (ADR-010 "Context" item 3). A block
-//   spans whole rows with its threads owning fixed columns (their s values in
-//   registers) and reduces R row maxima per barrier; the R rows stay in
-//   registers between the max and the quantize pass, so W is read from HBM
-//   exactly once.
+//   int8 with one scale per output row (ADR-010 "Context" item 3). Rows stream
+//   through an LDS ring (global -> LDS loads running ahead of the math); the
+//   threads of a block own fixed columns (their s values in registers) and
+//   keep W' in registers between the row max and the quantize pass, so W is
+//   read from HBM exactly once.
 // quant_act: runtime x * (1/s) strictly before the per-tensor quantizer
 //   (kwkr.cn blog §3.2 and §5.2; ADR-010 "Key design" items 4-5). A lane owns
 //   one 16-byte column vector and keeps its inv_s values in registers while
@@ -63,76 +63,153 @@ __device__ __forceinline__ void store16(int8_t* __restrict__ dst, const int (&q)
     *(u32x4*)dst = o;
 }
 
-// Thread t of a block owns groups t, t + T, ... (GPL of them; T <= MAXT
-// threads), so every wave load is one contiguous run of the row. R rows per
-// iteration.
-template <int EB, int GPL, int R, int MAXT>
-__global__ __launch_bounds__(MAXT) void quant_weight_kernel(const u32x4* __restrict__ w, int64_t n, int64_t kgroups,
-                                                            const float* __restrict__ s, int8_t* __restrict__ wq,
-                                                            float* __restrict__ w_scale) {
-    constexpr int VG = Group<EB>::V;
-    __shared__ float red[2][16][R];  // [parity][wave][row]
-    const int T = blockDim.x, nw = T >> 6;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float sv[GPL][16];
-    bool own[GPL];
-#pragma unroll
-    for (int g = 0; g < GPL; ++g) {
-        const int64_t gi = threadIdx.x + (int64_t)g * T;
-        own[g] = gi < kgroups;
-        if (own[g]) load16f(s + gi * 16, sv[g]);
+// E int8 codes (E = 8: two dwords, E = 4: one dword)
+template <int E>
+__device__ __forceinline__ void store_codes(int8_t* __restrict__ dst, const int (&q)[E]) {
+    if constexpr (E == 8) {
+        sqd::u32x2 o;
+        o.x = sqd::pack4_i8(q[0], q[1], q[2], q[3]);
+        o.y = sqd::pack4_i8(q[4], q[5], q[6], q[7]);
+        *(sqd::u32x2*)dst = o;
+    } else {
+        *(uint32_t*)dst = sqd::pack4_i8(q[0], q[1], q[2], q[3]);
     }
-    int parity = 0;
-    for (int64_t r0 = (int64_t)blockIdx.x * R; r0 < n; r0 += (int64_t)gridDim.x * R, parity ^= 1) {
-        Group<EB> raw[R][GPL];
-        float mx[R];
+}
+
+// Weight rows streamed through LDS. A persistent block of 512 threads walks
+// "stages" of RB consecutive rows (a contiguous run of W), kept in a ring of NS
+// LDS buffers filled by buffer_load ... lds, so the loads of the next stages
+// fly while this one is reduced and quantized. Thread t owns the 16-byte
+// column vectors t, t + 512, ... (VPT of them) and keeps their s values in
+// registers. Per stage: pass 1 forms W' = W * s in registers and the row
+// maxima (wave shuffles, then one LDS exchange and barrier), pass 2 quantizes
+// the registers and stores 4 or 8 codes per vector. W is read from HBM once.
+constexpr int kQwThreads = 512;
+constexpr int kQwWaves = kQwThreads / 64;
+
+template <int EB, int VPT, int RB, int CPW, int NS>
+__global__ __launch_bounds__(kQwThreads) void quant_weight_stream_kernel(const int8_t* __restrict__ w, int64_t n,
+                                                                        int64_t kvec, const float* __restrict__ s,
+                                                                        int8_t* __restrict__ wq,
+                                                                        float* __restrict__ w_scale) {
+    constexpr int E = 16 / EB;                        // elements per 16-byte vector
+    constexpr int STAGE = CPW * kQwWaves * 1024;      // bytes, >= RB rows (checked by the launcher)
+    static_assert(NS == 2 || NS == 3, "ring depth");
+    static_assert((NS - 1) * CPW < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) char ring[NS * STAGE];
+    __shared__ float part[RB][kQwWaves];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int64_t rowbytes = kvec * 16;
+    const int64_t nstages = (n + RB - 1) / RB;
+
+    float sv[VPT][E];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+    for (int i = 0; i < VPT; ++i) {
+        const int64_t v = t + (int64_t)i * kQwThreads;
 #pragma unroll
-            for (int g = 0; g < GPL; ++g)
-                if (own[g] && r0 + r < n) raw[r][g].load(w + ((r0 + r) * kgroups + threadIdx.x + (int64_t)g * T) * VG);
+        for (int e = 0; e < E; ++e) sv[i][e] = v < kvec ? s[v * E + e] : 0.0f;
+    }
+
+    // stage g -> ring slot b: CPW loads per wave, chunk c = wave + 8 j of the
+    // stage's contiguous bytes (zeros past the last row)
+    auto issue = [&](int64_t g, int slot) {
+        const int64_t r0 = g * RB;
+        const int64_t rows = r0 < n ? min<int64_t>(RB, n - r0) : 0;
+        const sqd::i32x4 rsrc = sqd::tile_rsrc(w + (r0 < n ? r0 : 0) * rowbytes, rows, rowbytes);
+        const uint32_t base = sqd::lds_addr(ring) + (uint32_t)(slot * STAGE) + (uint32_t)wave * 1024u;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
+        for (int j = 0; j < CPW; ++j) sqd::dma16(rsrc, base + (uint32_t)(j * kQwWaves * 1024), lane * 16,
+                                                 (j * kQwWaves + wave) * 1024);
+    };
+
+    // Codes of a stage are stored one round late (after the next stage's
+    // wait), so the wait below, which also counts stores, finds them long
+    // done; it is exact for the loads because loads complete in order and
+    // exactly NS - 2 stages of loads are issued after the awaited one.
+    constexpr int W32 = E / 4;  // dwords of codes per vector
+    uint32_t codes[RB][VPT][W32];
+    float scale[RB];
+    int64_t prev = -1;  // stage whose codes are pending
+    auto flush = [&]() {
+        if (prev < 0) return;
+        const int64_t p0 = prev * RB;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            if (p0 + r >= n) break;
+            int8_t* dst = wq + (p0 + r) * (kvec * E);
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int64_t v = t + (int64_t)i * kQwThreads;
+                if (v < kvec) {
+                    if constexpr (W32 == 2)
+                        *(sqd::u32x2*)(dst + v * E) = sqd::u32x2{codes[r][i][0], codes[r][i][1]};
+                    else
+                        *(uint32_t*)(dst + v * E) = codes[r][i][0];
+                }
+            }
+            if (t == 0) w_scale[p0 + r] = scale[r];
+        }
+    };
+
+    int64_t g = blockIdx.x;
+    int slot = 0;
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p) issue(g + (int64_t)p * gridDim.x, p);
+    for (; g < nstages; g += gridDim.x) {
+        sqd::wait_vmcnt<(NS - 2) * CPW>();  // this stage landed (for this wave's loads) ...
+        __syncthreads();                    // ... and for every wave; the slot read last round is free
+        flush();
+        issue(g + (int64_t)(NS - 1) * gridDim.x, (slot + NS - 1) % NS);
+        const char* st = ring + slot * STAGE;
+        float wv[RB][VPT][E];
+        float mx[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
             mx[r] = 0.0f;
 #pragma unroll
-            for (int g = 0; g < GPL; ++g)
-                if (own[g] && r0 + r < n) {
-                    float e[16];
-                    raw[r][g].widen(e);
+            for (int i = 0; i < VPT; ++i) {
+                const int64_t v = t + (int64_t)i * kQwThreads;
+                if (v < kvec) {
+                    const u32x4 raw = *(const u32x4*)(st + r * rowbytes + v * 16);
+                    float e[E];
+                    sqd::unpack16<E>(raw, e);
 #pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        mx[r] = __builtin_fmaxf(mx[r], __builtin_fabsf(__fmul_rn(e[j], sv[g][j])));
+                    for (int q = 0; q < E; ++q) {
+                        wv[r][i][q] = __fmul_rn(e[q], sv[i][q]);
+                        mx[r] = __builtin_fmaxf(mx[r], __builtin_fabsf(wv[r][i][q]));
+                    }
                 }
+            }
             mx[r] = sqd::wave_max(mx[r]);
-            if (lane == 0) red[parity][wave][r] = mx[r];
+            if (lane == 0) part[r][wave] = mx[r];
         }
-        // one barrier per R rows: the buffer of the other parity is written
-        // again only after the next barrier, when every thread has read it
         __syncthreads();
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float m = red[parity][0][r];
-            for (int i = 1; i < nw; ++i) m = __builtin_fmaxf(m, red[parity][i][r]);
-            mx[r] = __builtin_fmaxf(m, sqd::kFloor);
-        }
+        for (int r = 0; r < RB; ++r) {
+            float m = part[r][0];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (r0 + r >= n) continue;
-            const float ws = __fdiv_rn(mx[r], sqd::kQmax);
+            for (int i = 1; i < kQwWaves; ++i) m = __builtin_fmaxf(m, part[r][i]);
+            m = __builtin_fmaxf(m, sqd::kFloor);
+            const float ws = __fdiv_rn(m, sqd::kQmax);
             const float inv_ws = __fdiv_rn(1.0f, ws);
+            scale[r] = ws;
 #pragma unroll
-            for (int g = 0; g < GPL; ++g)
-                if (own[g]) {
-                    float e[16];
-                    int q[16];
-                    raw[r][g].widen(e);
+            for (int i = 0; i < VPT; ++i) {
+                int q[E];
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) q[j] = sqd::q8(__fmul_rn(__fmul_rn(e[j], sv[g][j]), inv_ws));
-                    store16(wq + ((r0 + r) * kgroups + threadIdx.x + (int64_t)g * T) * 16, q);
-                }
-            if (threadIdx.x == 0) w_scale[r0 + r] = ws;
+                for (int e = 0; e < E; ++e) q[e] = sqd::q8(__fmul_rn(wv[r][i][e], inv_ws));
+#pragma unroll
+                for (int d = 0; d < W32; ++d)
+                    codes[r][i][d] = sqd::pack4_i8(q[4 * d], q[4 * d + 1], q[4 * d + 2], q[4 * d + 3]);
+            }
         }
+        prev = g;
+        slot = (slot + 1) % NS;
     }
+    flush();
+    sqd::wait_vmcnt<0>();  // zero-fill loads past the end may still be in flight
 }
 
 // Rows longer than 4096 groups (k > 65536): one block per row, the row is
@@ -173,19 +250,6 @@ __global__ __launch_bounds__(256) void quant_weight_long_kernel(const u32x4* __r
 
 constexpr int kActThreads = 256;
 constexpr int kActUnroll = 4;
-
-// E int8 codes (E = 8: two dwords, E = 4: one dword)
-template <int E>
-__device__ __forceinline__ void store_codes(int8_t* __restrict__ dst, const int (&q)[E]) {
-    if constexpr (E == 8) {
-        sqd::u32x2 o;
-        o.x = sqd::pack4_i8(q[0], q[1], q[2], q[3]);
-        o.y = sqd::pack4_i8(q[4], q[5], q[6], q[7]);
-        *(sqd::u32x2*)dst = o;
-    } else {
-        *(uint32_t*)dst = sqd::pack4_i8(q[0], q[1], q[2], q[3]);
-    }
-}
 
 // A lane owns one 16-byte column vector (E = 16 / EB elements) of the input
 // and keeps its E inv_s values in registers; the four waves of a block walk
@@ -242,30 +306,34 @@ int device_cus() {
     return cus;
 }
 
-template <int EB, int GPL, int MAXT>
-hipError_t launch_qw(const void* w, int64_t n, int64_t kgroups, const float* s, int8_t* wq, float* w_scale,
+template <int EB, int VPT, int RB, int CPW, int NS>
+hipError_t launch_qw(const void* w, int64_t n, int64_t kvec, const float* s, int8_t* wq, float* w_scale,
                      hipStream_t stream) {
-    // rows per iteration: about 8 bf16 (4 fp32) group loads in flight per thread
-    constexpr int R = ((EB == 2 ? 8 : 4) / GPL) > 0 ? (EB == 2 ? 8 : 4) / GPL : 1;
-    const int64_t lanes = (kgroups + GPL - 1) / GPL;
-    const int threads = (int)((lanes + 63) / 64 * 64);
-    const int64_t row_groups = (n + R - 1) / R;
-    const int64_t blocks = std::min<int64_t>(row_groups, (int64_t)device_cus() * 8);
-    quant_weight_kernel<EB, GPL, R, MAXT><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
-        (const u32x4*)w, n, kgroups, s, wq, w_scale);
+    static_assert(NS * CPW * kQwWaves * 1024 <= 150 * 1024, "the ring fits in LDS");
+    if (RB * kvec * 16 > CPW * kQwWaves * 1024 || kvec > VPT * kQwThreads) return hipErrorInvalidValue;
+    const int64_t nstages = (n + RB - 1) / RB;
+    const int64_t blocks = std::min<int64_t>(nstages, (int64_t)device_cus());
+    quant_weight_stream_kernel<EB, VPT, RB, CPW, NS><<<dim3((unsigned)blocks), dim3(kQwThreads), 0, stream>>>(
+        (const int8_t*)w, n, kvec, s, wq, w_scale);
     return hipGetLastError();
 }
 
 template <int EB>
 hipError_t quant_weight_t(const void* w, int64_t n, int64_t k, const float* s, int8_t* wq, float* w_scale,
                           hipStream_t stream) {
-    const int64_t kgroups = k / 16;
-    // one group per thread in blocks of up to 1024 threads (128 VGPRs each);
-    // longer rows: 512-thread blocks with 4 or 8 groups per thread
-    if (kgroups <= 1024) return launch_qw<EB, 1, 1024>(w, n, kgroups, s, wq, w_scale, stream);
-    if (kgroups <= 2048) return launch_qw<EB, 4, 512>(w, n, kgroups, s, wq, w_scale, stream);
-    if (kgroups <= 4096) return launch_qw<EB, 8, 512>(w, n, kgroups, s, wq, w_scale, stream);
-    quant_weight_long_kernel<EB><<<dim3((unsigned)n), dim3(256), 0, stream>>>((const u32x4*)w, kgroups, s, wq,
+    const int64_t kvec = k * EB / 16;  // 16-byte vectors per row
+    // (vectors per thread, rows per stage, 8 KB units per stage, ring depth):
+    // stages of 32-56 KB so each pair of barriers covers enough bytes, three
+    // in the ring when they fit; rows of more than 4096 vectors are read twice
+    // by a block per row
+    if (kvec <= 256) return launch_qw<EB, 1, 8, 4, 3>(w, n, kvec, s, wq, w_scale, stream);
+    if (kvec <= 512) return launch_qw<EB, 1, 4, 4, 3>(w, n, kvec, s, wq, w_scale, stream);
+    if (kvec <= 640) return launch_qw<EB, 2, 4, 5, 3>(w, n, kvec, s, wq, w_scale, stream);
+    if (kvec <= 1024) return launch_qw<EB, 2, 2, 4, 3>(w, n, kvec, s, wq, w_scale, stream);
+    if (kvec <= 1792) return launch_qw<EB, 4, 2, 7, 2>(w, n, kvec, s, wq, w_scale, stream);
+    if (kvec <= 2048) return launch_qw<EB, 4, 1, 4, 3>(w, n, kvec, s, wq, w_scale, stream);
+    if (kvec <= 4096) return launch_qw<EB, 8, 1, 8, 2>(w, n, kvec, s, wq, w_scale, stream);
+    quant_weight_long_kernel<EB><<<dim3((unsigned)n), dim3(256), 0, stream>>>((const u32x4*)w, k / 16, s, wq,
                                                                             w_scale);
     return hipGetLastError();
 }

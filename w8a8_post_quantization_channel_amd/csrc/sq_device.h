@@ -69,14 +69,23 @@ __device__ __forceinline__ void unpack16<4>(const u32x4& v, float (&e)[4]) {
     e[2] = __uint_as_float(v.z); e[3] = __uint_as_float(v.w);
 }
 
-// wave-wide maximum (64 lanes)
+// Wave-wide maximum of non-negative values (64 lanes, all active). Bit
+// patterns of non-negative floats order like unsigned integers, so the max is
+// an exact integer max: DPP within each 16-lane row (quad swaps, then row
+// rotations by 4 and 8), then the four row maxima read into scalars.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    uint32_t u = __float_as_uint(v);
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x124, 0xF, 0xF, false));  // row_ror:4
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x128, 0xF, 0xF, false));  // row_ror:8
+    const uint32_t r0 = __builtin_amdgcn_readlane(u, 0), r1 = __builtin_amdgcn_readlane(u, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(u, 32), r3 = __builtin_amdgcn_readlane(u, 48);
+    return __uint_as_float(max(max(r0, r1), max(r2, r3)));
 }
 
-// block-wide maximum; every thread gets the result. `red` holds >= NWAVES floats.
+// block-wide maximum of non-negative values; every thread gets the result.
+// `red` holds >= NWAVES floats.
 template <int NWAVES>
 __device__ __forceinline__ float block_max(float v, float* red) {
     v = wave_max(v);
@@ -89,5 +98,51 @@ __device__ __forceinline__ float block_max(float v, float* red) {
     __syncthreads();
     return r;
 }
+
+// ---- global -> LDS direct loads (buffer_load ... lds) --------------------------
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Raw buffer descriptor (stride 0) over rows_valid rows of kb bytes starting at
+// base: offsets at or past num_records = rows_valid * kb (< 2^31) read as zero.
+__device__ __forceinline__ i32x4 tile_rsrc(const int8_t* base, int64_t rows_valid, int64_t kb) {
+    const uint64_t b = (uint64_t)base;
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    r.z = __builtin_amdgcn_readfirstlane((int)(rows_valid * kb));
+    r.w = 0x00020000;
+    return r;
+}
+
+// An offset past every descriptor's num_records (at most 2^28 bytes where it
+// is used): a load from it returns zeros.
+constexpr int kOutOfRange = 0x70000000;
+
+// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16*lane.
+// Written as asm so that the only waits on these loads are the explicit
+// s_waitcnt vmcnt(...) placed before the barriers that publish each stage
+// (the compiler would otherwise drain every load in flight before reading
+// any stage). No register receives the data.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds, int voff, int soff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+
 
 }  // namespace sqd

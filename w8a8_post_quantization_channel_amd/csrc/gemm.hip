@@ -442,11 +442,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(const 
 // half of the last step is redirected out of range too, so it reads as zero.
 //
 // LDS stage layout: rows of 128 bytes (A rows 0..255, then B rows), 16-byte
-// chunk c of row r stored at position c ^ (r & 7). One load instruction
-// fills 8 consecutive rows (1 KB; lane q -> bytes 16q..16q+15, i.e. row q/8,
-// position q%8), so lane q fetches logical chunk (q % 8) ^ (q / 8) of its
-// row. An MFMA fragment read (lane l: row l % 32, chunk 2*substep + l / 32)
-// then touches eight different positions in every group of eight rows.
+// chunk c of row r stored at position c ^ ((r >> 1) & 7). LDS has 64 banks of
+// 4 bytes, so a 128-byte row covers half of them and rows r, r + 1 cover all;
+// with this swizzle the 16 rows read by 16 lanes of one fragment read (lane l:
+// row l % 32, chunk 2*substep + l / 32) land on 16 different 16-byte bank
+// groups. One load instruction fills 8 consecutive rows (1 KB; lane q ->
+// bytes 16q..16q+15, i.e. row q/8, position q%8), so lane q fetches logical
+// chunk (q % 8) ^ ((row >> 1) & 7) of its row.
 //
 // Each step is a fixed instruction stream: MFMAs with the fragment reads of the
 // next substep and the loads of a later step interleaved between them, and
@@ -517,7 +519,8 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
 
     // load j of wave w fills stage rows [8 (4j + w), 8 (4j + w) + 8), which
     // are A rows exactly when j < LA
-    const int chunk = (lane & 7) ^ (lane >> 3);
+    // row = 8 (4j + wave) + lane / 8, so (row >> 1) & 7 = (4 (wave & 1) + lane / 16) & 7 for every j
+    const int chunk = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
     int voff[L];
 #pragma unroll
     for (int j = 0; j < L; ++j) {
@@ -553,7 +556,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
     // fragment addresses within a stage: row (lane % 32) of each 32-row block,
     // chunk 2*ks + lane/32 at position ^ (row & 7) = ^ (lane & 7)
     const int frow = lane & 31;
-    const int c0 = (lane >> 5) ^ (lane & 7);  // chunk 2*ks + lane/32 lands at position c0 ^ 2*ks
+    const int c0 = (lane >> 5) ^ ((lane >> 1) & 7);  // chunk 2*ks + lane/32 lands at position c0 ^ 2*ks
     const int a_off = (wave * 64 + frow) * kDmaBK;
     const int b_off = frow * kDmaBK;
     v4i fa[2][NFA], fb[2][NFB];  // [substep parity][tile]

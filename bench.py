@@ -48,9 +48,10 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="output rows of each GEMM the oracle computes in the CPU sample")
     ap.add_argument("--traffic", type=str, default=None,
-                    help="JSON file with HBM traffic per GEMM launch (bytes) from rocprofv3 counters")
+                    help="counter summary with the HBM bytes per GEMM launch (default: the committed "
+                         "profiles/gemm_traffic__llama13b_prefill2048.md, used only if it matches gemm.hip)")
     ap.add_argument("--workload", default="layer13b",
-                    choices=["layer13b", "decode7b", "alpha_search", "prefill70b", "hbm_passes"],
+                    choices=["layer13b", "decode7b", "alpha_search", "prefill70b", "hbm_passes", "copy_probe"],
                     help="layer13b (default, the headline line); the others measure the remaining "
                          "workloads, one JSON line each")
     return ap.parse_args()
@@ -102,6 +103,31 @@ def run_step(groups, projs, gemm_events=None):
             gemm_events.append((name, e0, e1))
         else:
             layer.matmul(xq)
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_traffic__llama13b_prefill2048.md")
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "w8a8_post_quantization_channel_amd", "csrc", "gemm.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def gemm_traffic(path=None):
+    """HBM bytes per GEMM launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (scaled by a plain copy), read from the committed summary; None when the
+    summary is missing or was taken on a different gemm.hip."""
+    import re
+    path = path or TRAFFIC_SUMMARY
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"^gemm\.hip sha256\[:16\]: ([0-9a-f]{16})$", text, re.M)
+    b = re.search(r"^bytes_per_launch: ([0-9.eE+]+)$", text, re.M)
+    if not h or not b or h.group(1) != gemm_source_hash():
+        return None
+    return float(b.group(1))
 
 
 def gemm_ops(projs, m):
@@ -218,6 +244,20 @@ def workload_alpha_search(device):
             "config": {"workload": "alpha search 8x2048 tokens, K=4096, N=11008, grid 0.25/0.5/0.75/1.0"},
             "mse": mse, "best_alpha": synth.ALPHA_GRID[best],
             "effective_TOPS": (ops_i8 + ops_ref) / (ms * 1e-3) / 1e12}
+
+
+def workload_copy_probe(device):
+    """A plain copy of known size (torch's copy kernel, 1 GiB read + 1 GiB
+    written per launch, 5 launches): the reference that scales the FETCH_SIZE
+    and WRITE_SIZE counters to bytes."""
+    import torch
+    n = 1 << 29  # bf16 elements: 1 GiB
+    x = torch.ones(n, dtype=torch.bfloat16, device=device)
+    y = torch.empty_like(x)
+    ms = timed(lambda: y.copy_(x), 5, warmup=0)
+    return {"metric": "plain copy, bytes per launch", "value": n * 2, "unit": "bytes read (and written) per launch",
+            "n_gpus": 1, "higher_is_better": True, "launches": 5, "us_per_launch": ms * 1e3,
+            "config": {"workload": "copy 1 GiB bf16 -> bf16"}}
 
 
 def workload_prefill70b(device):
@@ -346,7 +386,7 @@ def main():
     from w8a8_post_quantization_channel_amd import capi
     capi.load()  # fails loudly when libsq.so is missing
     device = torch.device("cuda", 0)
-    other = {"decode7b": workload_decode7b, "alpha_search": workload_alpha_search,
+    other = {"decode7b": workload_decode7b, "alpha_search": workload_alpha_search, "copy_probe": workload_copy_probe,
              "prefill70b": workload_prefill70b, "hbm_passes": workload_hbm_passes}
     if args.workload in other:
         out = other[args.workload](device)
@@ -381,9 +421,7 @@ def main():
     avg_launch_ms = sum(gemm_ms) / len(gemm_ms)
     avg_launch_ops = sum(ops_by_name[n] for n, _, _ in events) / len(events)
     achieved = avg_launch_ops / (avg_launch_ms * 1e-3) / 1e12
-    traffic = None
-    if args.traffic:
-        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    traffic = gemm_traffic(args.traffic)
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                 "frac": achieved / PEAK_INT8_TOPS, "traffic": traffic,
                 "kernel": "gemm_dma_kernel<OpI8, TN, EpiDequant<bf16>> (256 x 32*TN tiles)",

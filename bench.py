@@ -15,7 +15,9 @@ whole path over one batch:
         x * (1/s) -> per-tensor int8                   sq_smooth_quant_act
         int8 GEMM + fused dequant -> bf16              sq_w8a8_gemm
 The batch is its own calibration batch (one batch of synthetic input per
-step). Inputs are resident in HBM before timing starts.
+step). Inputs are resident in HBM before timing starts. Everything runs on
+one stream (--overlap: the preparation chain on a second stream, so
+projection p + 1 is prepared while projection p multiplies).
 
 value = int8 GEMM operations of the step (2*M*N*K summed over the seven
 projections) / step time, in TOPS. The JSON line also carries the roofline of
@@ -45,6 +47,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run the preparation chain on a second stream, overlapping the GEMMs (default: one "
+                         "stream; overlapping shortens the step a little but slows the GEMMs it runs beside)")
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="output rows of each GEMM the oracle computes in the CPU sample")
     ap.add_argument("--traffic", type=str, default=None,
@@ -84,25 +89,37 @@ def setup(device):
     return groups, projs
 
 
-def run_step(groups, projs, gemm_events=None):
-    """One pass of the whole path. gemm_events: list to append (start, end)
-    event pairs bracketing each GEMM launch."""
+def run_step(groups, projs, gemm_events=None, side=None):
+    """One pass of the whole path. gemm_events: list to append (name, start,
+    end) event pairs bracketing each GEMM launch, recorded on the stream the
+    GEMM runs on. side: a second stream for the preparation chain (statistics,
+    smoothing, weight and activation quantization), so that projection p + 1
+    is prepared while the GEMM of projection p runs; each GEMM waits for its
+    own preparation, and the step starts after the previous step's GEMMs."""
     import torch
     from w8a8_post_quantization_channel_amd import capi
-    for g in groups.values():
-        capi.sq_calib_absmax(g.x, g.act_max, False)
+    main = torch.cuda.current_stream()
+    prep = side if side is not None else main
+    if side is not None:
+        side.wait_stream(main)
+    with torch.cuda.stream(prep):
+        for g in groups.values():
+            capi.sq_calib_absmax(g.x, g.act_max, False, stream=prep)
     for name, g, layer, _ in projs:
-        layer.prepare()
-        xq = layer.quantize_input(g.x)
+        with torch.cuda.stream(prep):
+            layer.prepare(stream=prep)
+            xq = layer.quantize_input(g.x, stream=prep)
+        if side is not None:
+            main.wait_stream(prep)
         if gemm_events is not None:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            layer.matmul(xq)
-            e1.record()
+            e0.record(main)
+            layer.matmul(xq, stream=main)
+            e1.record(main)
             gemm_events.append((name, e0, e1))
         else:
-            layer.matmul(xq)
+            layer.matmul(xq, stream=main)
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_traffic__llama13b_prefill2048.md")
@@ -431,16 +448,17 @@ def main():
         return
     groups, projs = setup(device)
     m = next(iter(groups.values())).x.shape[0]
+    side = torch.cuda.Stream() if args.overlap else None  # default priority, like the main stream
 
     for _ in range(args.warmup):
-        run_step(groups, projs)
+        run_step(groups, projs, side=side)
     torch.cuda.synchronize()
 
     events = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        run_step(groups, projs, events)
+        run_step(groups, projs, events, side=side)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -476,7 +494,9 @@ def main():
         "config": {"workload": "llama2-13b decoder layer, 7 linear projections, 2048 prefill tokens",
                    "tokens": m, "alpha": 0.5, "in_dtype": "bf16", "out_dtype": "bf16",
                    "projections": {n: [layer.n, layer.k] for n, _, layer, _ in projs},
-                   "step": "calib absmax + weight absmax + smoothing + weight quant + act quant + int8 GEMM"},
+                   "step": "calib absmax + weight absmax + smoothing + weight quant + act quant + int8 GEMM",
+                   "schedule": "two streams: GEMM of projection p overlaps the preparation of projection p + 1"
+                   if args.overlap else "one stream"},
         "roofline": roofline,
         "gemm_share_of_step": gemm_share,
         "gpu": torch.cuda.get_device_name(0),

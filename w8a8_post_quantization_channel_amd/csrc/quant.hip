@@ -249,7 +249,7 @@ __global__ __launch_bounds__(256) void quant_weight_long_kernel(const u32x4* __r
 }
 
 constexpr int kActThreads = 256;
-constexpr int kActUnroll = 4;
+constexpr int kActUnroll = 8;
 
 // A lane owns one 16-byte column vector (E = 16 / EB elements) of the input
 // and keeps its E inv_s values in registers; the four waves of a block walk
@@ -356,7 +356,7 @@ hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const float* i
     const int64_t kvec = k * eb / 16;
     const int64_t strips = (kvec + 63) / 64;
     const int64_t granule = 4 * kActUnroll;
-    int64_t target_chunks = std::max<int64_t>(1, 4096 / strips);
+    int64_t target_chunks = std::max<int64_t>(1, 8192 / strips);
     int64_t rpb = (m + target_chunks - 1) / target_chunks;
     rpb = std::max<int64_t>(granule, (rpb + granule - 1) / granule * granule);
     int64_t chunks = (m + rpb - 1) / rpb;

@@ -195,14 +195,26 @@ __global__ __launch_bounds__(kQwThreads) void quant_weight_stream_kernel(const i
             const float ws = __fdiv_rn(m, sqd::kQmax);
             const float inv_ws = __fdiv_rn(1.0f, ws);
             scale[r] = ws;
+            // Codes by the round-to-nearest-even of the fp32 adder: for
+            // |v| < 2^22, fl(v + 1.5 * 2^23) = rint(v) + 1.5 * 2^23 exactly, and
+            // the low byte of its bit pattern is rint(v) as a two's-complement
+            // int8. No clamp is needed: |W'| <= m and inv_ws = fl(1 / fl(m / 127)),
+            // so |v| <= 127 (1 + 3 * 2^-24) and rint(v) is within [-127, 127]
+            // (below the 1e-5 floor, |v| < 127). Equal to q8() for every value
+            // this row can produce.
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
-                int q[E];
+                uint32_t b[E];
 #pragma unroll
-                for (int e = 0; e < E; ++e) q[e] = sqd::q8(__fmul_rn(wv[r][i][e], inv_ws));
+                for (int e = 0; e < E; ++e)
+                    b[e] = __float_as_uint(__fadd_rn(__fmul_rn(wv[r][i][e], inv_ws), 12582912.0f));
 #pragma unroll
-                for (int d = 0; d < W32; ++d)
-                    codes[r][i][d] = sqd::pack4_i8(q[4 * d], q[4 * d + 1], q[4 * d + 2], q[4 * d + 3]);
+                for (int d = 0; d < W32; ++d) {
+                    // low bytes of b[4d .. 4d+3] -> one dword
+                    const uint32_t lo = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0c0c0400u);
+                    const uint32_t hi = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0c0c0400u);
+                    codes[r][i][d] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                }
             }
         }
         prev = g;

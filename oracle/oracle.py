@@ -54,6 +54,16 @@ def _declare(lib):
     lib.sqo_sse.restype = c.c_double
     lib.sqo_alpha_search.argtypes = [P, c.c_int, c.c_int, i64, i64, P, c.c_int, i64, P, c.c_int, P]
     lib.sqo_alpha_search.restype = c.c_int
+    lib.sqo_dynamic_quant_act.argtypes = [P, c.c_int, i64, i64, P, P, P]
+    lib.sqo_calib_sample_max_sum.argtypes = [P, c.c_int, i64, i64, i64, P]
+    lib.sqo_calib_mean_finalize.argtypes = [P, i64, i64, P]
+    lib.sqo_percentile_rank.argtypes = [c.c_double, i64]
+    lib.sqo_percentile_rank.restype = i64
+    lib.sqo_calib_percentile.argtypes = [P, c.c_int, i64, i64, c.c_double, P]
+    lib.sqo_rms_inv.argtypes = [P, c.c_int, i64, i64, c.c_float, P]
+    lib.sqo_rmsnorm_apply.argtypes = [P, c.c_int, i64, i64, P, P, c.c_int, P]
+    lib.sqo_fold_norm_weight.argtypes = [P, P, i64, P]
+    lib.sqo_norm_quant_apply.argtypes = [P, c.c_int, i64, i64, P, P, c.c_float, P]
     return lib
 
 
@@ -169,6 +179,70 @@ class Oracle:
         best = self.lib.sqo_alpha_search(ctypes.cast(ptrs, ctypes.c_void_p), _ftype(x_batches[0]), nb, rows, k,
                                          _ptr(w), _ftype(w), n, _ptr(al), len(al), _ptr(mse))
         return mse, int(best)
+
+    # O13
+    def dynamic_quant_act(self, x: np.ndarray, inv_s: np.ndarray):
+        m, k = x.shape
+        xq = np.empty((m, k), np.int8)
+        a = np.empty(1, np.float32)
+        self.lib.sqo_dynamic_quant_act(_ptr(x), _ftype(x), m, k, _ptr(inv_s), _ptr(xq), _ptr(a))
+        return xq, a[0]
+
+    # O14
+    def calib_sample_max_sum(self, x: np.ndarray, samples: int, total: np.ndarray | None = None) -> np.ndarray:
+        rows, k = x.shape
+        assert rows % samples == 0
+        out = total if total is not None else np.zeros(k, np.float64)
+        self.lib.sqo_calib_sample_max_sum(_ptr(x), _ftype(x), samples, rows // samples, k, _ptr(out))
+        return out
+
+    def calib_mean_finalize(self, total: np.ndarray, count: int) -> np.ndarray:
+        k = total.shape[0]
+        out = np.empty(k, np.float32)
+        self.lib.sqo_calib_mean_finalize(_ptr(total), count, k, _ptr(out))
+        return out
+
+    # O15
+    def percentile_rank(self, q: float, rows: int) -> int:
+        return int(self.lib.sqo_percentile_rank(float(q), rows))
+
+    def calib_percentile(self, x: np.ndarray, q: float) -> np.ndarray:
+        rows, k = x.shape
+        out = np.empty(k, np.float32)
+        self.lib.sqo_calib_percentile(_ptr(x), _ftype(x), rows, k, float(q), _ptr(out))
+        return out
+
+    # O16
+    def rms_inv(self, h: np.ndarray, eps: float) -> np.ndarray:
+        m, k = h.shape
+        r = np.empty(m, np.float32)
+        self.lib.sqo_rms_inv(_ptr(h), _ftype(h), m, k, float(np.float32(eps)), _ptr(r))
+        return r
+
+    def rmsnorm_apply(self, h: np.ndarray, r: np.ndarray, gamma: np.ndarray, bf16: bool = False) -> np.ndarray:
+        m, k = h.shape
+        y = np.empty((m, k), np.uint16 if bf16 else np.float32)
+        self.lib.sqo_rmsnorm_apply(_ptr(h), _ftype(h), m, k, _ptr(r), _ptr(gamma), BF16 if bf16 else F32, _ptr(y))
+        return y
+
+    # O17
+    def fold_norm_weight(self, gamma: np.ndarray, inv_s: np.ndarray) -> np.ndarray:
+        out = np.empty_like(gamma, dtype=np.float32)
+        self.lib.sqo_fold_norm_weight(_ptr(gamma), _ptr(inv_s), gamma.shape[0], _ptr(out))
+        return out
+
+    # O18
+    def norm_quant_apply(self, h: np.ndarray, r: np.ndarray, gamma_folded: np.ndarray, act_scale) -> np.ndarray:
+        m, k = h.shape
+        xq = np.empty((m, k), np.int8)
+        self.lib.sqo_norm_quant_apply(_ptr(h), _ftype(h), m, k, _ptr(r), _ptr(gamma_folded),
+                                      float(np.float32(act_scale)), _ptr(xq))
+        return xq
+
+    # O16 + O18: the fused norm + quantizer for one batch
+    def rmsnorm_quant_act(self, h: np.ndarray, gamma_folded: np.ndarray, eps: float, act_scale):
+        r = self.rms_inv(h, eps)
+        return self.norm_quant_apply(h, r, gamma_folded, act_scale), r
 
     # the whole layer, O1..O10, for one runtime input (helper for tests)
     def layer_forward(self, x_calib_batches, w: np.ndarray, x: np.ndarray, alpha: float, bf16_out: bool = False):

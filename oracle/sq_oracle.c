@@ -243,3 +243,123 @@ int sqo_alpha_search(const void* const* x_batches, int xtype, int nb,
     free(xq); free(acc); free(y); free(yref);
     return best;
 }
+
+/* O13: dynamic mode (pwwt.cn §2.3): the scale is taken from the batch being
+ * quantized instead of the calibration set; the offline s is kept, so the
+ * closed form of O6 is applied to this batch's channel maxima. */
+void sqo_dynamic_quant_act(const void* x, int xtype, int64_t m, int64_t k,
+                           const float* inv_s, int8_t* xq, float* act_scale) {
+    float* live = (float*)calloc((size_t)(k > 0 ? k : 1), sizeof(float));
+    sqo_calib_absmax(x, xtype, m, k, live, 0);
+    float a = sqo_act_scale(live, inv_s, k);
+    sqo_quant_act(x, xtype, m, k, inv_s, a, xq);
+    *act_scale = a;
+    free(live);
+}
+
+/* O14: the averaged-maxima statistic of kwkr.cn blog §3.1: the maximum of
+ * each calibration sample, averaged over the samples. */
+void sqo_calib_sample_max_sum(const void* x, int xtype, int64_t samples,
+                              int64_t rows_per_sample, int64_t k, double* sum) {
+    int64_t j;
+#pragma omp parallel for schedule(static)
+    for (j = 0; j < k; ++j) {
+        for (int64_t b = 0; b < samples; ++b) {
+            float mx = 0.0f;
+            for (int64_t t = 0; t < rows_per_sample; ++t) {
+                float v = fabsf(elem(x, xtype, (b * rows_per_sample + t) * k + j));
+                if (v > mx) mx = v;
+            }
+            sum[j] += (double)mx;
+        }
+    }
+}
+
+void sqo_calib_mean_finalize(const double* sum, int64_t count, int64_t k,
+                             float* act_max) {
+    for (int64_t j = 0; j < k; ++j) act_max[j] = (float)(sum[j] / (double)count);
+}
+
+/* O15: the percentile statistic of kwkr.cn blog §3.1 (e.g. 99.9% in place of
+ * the absolute maximum), as a nearest rank: the smallest magnitude with at
+ * least ceil(q * rows) magnitudes at or below it. */
+int64_t sqo_percentile_rank(double q, int64_t rows) {
+    int64_t rank = (int64_t)ceil(q * (double)rows);
+    if (rank < 1) rank = 1;
+    if (rank > rows) rank = rows;
+    return rank;
+}
+
+static int cmp_float(const void* a, const void* b) {
+    float x = *(const float*)a, y = *(const float*)b;
+    return (x > y) - (x < y);
+}
+
+void sqo_calib_percentile(const void* x, int xtype, int64_t rows, int64_t k,
+                          double q, float* act_max) {
+    int64_t rank = sqo_percentile_rank(q, rows);
+    int64_t j;
+#pragma omp parallel for schedule(static)
+    for (j = 0; j < k; ++j) {
+        float* col = (float*)malloc((size_t)rows * sizeof(float));
+        for (int64_t t = 0; t < rows; ++t) col[t] = fabsf(elem(x, xtype, t * k + j));
+        qsort(col, (size_t)rows, sizeof(float), cmp_float);
+        act_max[j] = col[rank - 1];
+        free(col);
+    }
+}
+
+/* O16: RMSNorm, the norm that precedes the projections in a Llama block and
+ * whose weight gamma can absorb 1/s (kwkr.cn blog §3.2). */
+void sqo_rms_inv(const void* h, int htype, int64_t m, int64_t k, float eps,
+                 float* r) {
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < m; ++t) {
+        double ss = 0.0;
+        for (int64_t j = 0; j < k; ++j) {
+            double v = (double)elem(h, htype, t * k + j);
+            ss += v * v;
+        }
+        r[t] = (float)(1.0 / sqrt(ss / (double)k + (double)eps));
+    }
+}
+
+void sqo_rmsnorm_apply(const void* h, int htype, int64_t m, int64_t k,
+                       const float* r, const float* gamma, int ytype, void* y) {
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < m; ++t) {
+        for (int64_t j = 0; j < k; ++j) {
+            float v = (elem(h, htype, t * k + j) * r[t]) * gamma[j];
+            if (ytype == SQO_BF16)
+                ((uint16_t*)y)[t * k + j] = float_to_bf16_rne(v);
+            else
+                ((float*)y)[t * k + j] = v;
+        }
+    }
+}
+
+/* O17: kwkr.cn blog §3.2: with a norm in front of the layer, 1/s is
+ * multiplied into the norm's gamma once, offline. */
+void sqo_fold_norm_weight(const float* gamma, const float* inv_s, int64_t k,
+                          float* gamma_folded) {
+    for (int64_t j = 0; j < k; ++j) gamma_folded[j] = gamma[j] * inv_s[j];
+}
+
+/* O18: the norm output with the folded gamma is already X/s, so it goes
+ * straight into the per-tensor quantizer (scaling before quantizing, kwkr.cn
+ * blog §3.2). */
+void sqo_norm_quant_apply(const void* h, int htype, int64_t m, int64_t k,
+                          const float* r, const float* gamma_folded,
+                          float act_scale, int8_t* xq) {
+    float inv_a = 1.0f / act_scale;
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < m; ++t) {
+        for (int64_t j = 0; j < k; ++j) {
+            float smoothed = (elem(h, htype, t * k + j) * r[t]) * gamma_folded[j];
+            xq[t * k + j] = quantize_scaled(smoothed * inv_a);
+        }
+    }
+}

@@ -18,6 +18,10 @@
  *   - symmetric quantizer:         kwkr.cn blog §1.2
  *   - int8 GEMM + merged scales:   pwwt.cn §3.1 (quantized_matmul_kernel stub)
  *   - alpha grid search:           ADR-010 "Key design" item 2
+ *   - dynamic mode:                pwwt.cn §2.3 (static vs dynamic scales)
+ *   - robust calibration:          kwkr.cn blog §3.1 (percentile, mean of maxima)
+ *   - 1/s folded into the norm:    kwkr.cn blog §2.3 and §3.2 (gamma of the
+ *                                  preceding norm absorbs 1/s)
  *
  * Conventions: X[m,k] and W[n,k] are row-major with k contiguous; column j is
  * input channel j. Every floating-point step is one IEEE fp32 operation with
@@ -84,6 +88,50 @@ double sqo_sse(const float* y, const float* yref, int64_t m, int64_t n);
 int sqo_alpha_search(const void* const* x_batches, int xtype, int nb,
                      int64_t rows, int64_t k, const void* w, int wtype,
                      int64_t n, const double* alphas, int na, double* mse);
+
+/* O13: dynamic mode. The smoothing factors stay the offline ones; the
+ * per-tensor activation scale is recomputed from the live batch with the O6
+ * closed form: live[j] = max_t |x[t,j]|, a = O6(live, inv_s), then O8 with a.
+ * Writes xq and a. */
+void sqo_dynamic_quant_act(const void* x, int xtype, int64_t m, int64_t k,
+                           const float* inv_s, int8_t* xq, float* act_scale);
+
+/* O14: mean of per-sample maxima. x holds `samples` consecutive samples of
+ * rows_per_sample rows each; sum[j] += (double) max_{t in sample} |x[t,j]|,
+ * the samples added in ascending order (a running sum across calls). */
+void sqo_calib_sample_max_sum(const void* x, int xtype, int64_t samples,
+                              int64_t rows_per_sample, int64_t k, double* sum);
+
+/* O14 (end): act_max[j] = (float)(sum[j] / (double)count). */
+void sqo_calib_mean_finalize(const double* sum, int64_t count, int64_t k,
+                             float* act_max);
+
+/* O15: nearest-rank percentile of |x[:,j]| over the rows: the rank-th
+ * smallest magnitude, rank = sqo_percentile_rank(q, rows). */
+int64_t sqo_percentile_rank(double q, int64_t rows);
+void sqo_calib_percentile(const void* x, int xtype, int64_t rows, int64_t k,
+                          double q, float* act_max);
+
+/* O16: RMSNorm (the norm in front of every projection of a Llama block).
+ * r[t] = (float)(1 / sqrt(sum_j h[t,j]^2 / k + eps)) evaluated in fp64 with
+ * the squares summed in ascending j and rounded once. */
+void sqo_rms_inv(const void* h, int htype, int64_t m, int64_t k, float eps,
+                 float* r);
+
+/* O16 (apply): y[t,j] = fl(fl(h[t,j] * r[t]) * gamma[j]), fp32 or bf16 (RNE). */
+void sqo_rmsnorm_apply(const void* h, int htype, int64_t m, int64_t k,
+                       const float* r, const float* gamma, int ytype, void* y);
+
+/* O17: 1/s folded into the norm weight: gamma_folded[j] = fl(gamma[j] * inv_s[j]). */
+void sqo_fold_norm_weight(const float* gamma, const float* inv_s, int64_t k,
+                          float* gamma_folded);
+
+/* O18: the norm with the folded weight feeding the per-tensor quantizer
+ * directly: xq[t,j] = q(fl(fl(fl(h[t,j] * r[t]) * gamma_folded[j]) * fl(1/a))),
+ * q = round half to even, clamp to [-127, 127]. Given r (from O16). */
+void sqo_norm_quant_apply(const void* h, int htype, int64_t m, int64_t k,
+                          const float* r, const float* gamma_folded,
+                          float act_scale, int8_t* xq);
 
 #ifdef __cplusplus
 }

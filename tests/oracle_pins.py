@@ -356,4 +356,131 @@ def pin_alpha_search(o):
     assert diff.max() <= 1
 
 
+# ---- O13: dynamic mode ------------------------------------------------------------
+
+def pin_dynamic_scale(o):
+    """pwwt.cn §2.3 dynamic mode: the live batch's own maximum of |x|/s sets
+    the per-tensor scale (the O6 closed form on this batch). With power-of-two
+    1/s every product is exact, so the closed form is exact too."""
+    g = synth.rng(41)
+    k = 256
+    x = (g.standard_normal((40, k)) * 2).astype(np.float32)
+    x[:, 200] *= 30
+    inv_s = (2.0 ** g.integers(-3, 4, k)).astype(np.float32)
+    xq, a = o.dynamic_quant_act(x, inv_s)
+    assert a == np.float32(np.float32(np.abs(x * inv_s).max()) / np.float32(127.0))
+    assert int(np.abs(xq.astype(np.int32)).max()) == 127
+    err = np.abs(xq.astype(np.float64) * float(a) - x.astype(np.float64) * inv_s.astype(np.float64))
+    assert err.max() <= 0.5 * float(a) * (1 + 1e-6)
+    # a power-of-two rescale of the batch moves the scale, not the codes
+    xq2, a2 = o.dynamic_quant_act(x * np.float32(8.0), inv_s)
+    assert np.array_equal(xq2, xq) and a2 == a * np.float32(8.0)
+    # on its own calibration data the dynamic scale is the static one
+    act_max = o.calib_absmax(x)
+    s, inv_s3, a3 = o.smooth_factors(act_max, o.calib_absmax(synth.weights(46, 32, k, bf16=False)), 0.5)
+    xq3, a4 = o.dynamic_quant_act(x, inv_s3)
+    assert a4 == a3 and np.array_equal(xq3, o.quant_act(x, inv_s3, a3))
+    # an all-zero batch: the 1e-5 floor of every channel sets the scale
+    xqz, az = o.dynamic_quant_act(np.zeros((3, k), np.float32), inv_s)
+    assert not xqz.any() and az == np.float32(np.float32(1e-5) * inv_s.max()) / np.float32(127.0)
+
+
+# ---- O14 / O15: robust calibration statistics ---------------------------------------
+
+def pin_mean_of_max(o):
+    """kwkr.cn blog §3.1: the per-sample maxima averaged over the samples, so
+    one sample's extreme value moves the statistic by a fraction of itself."""
+    from fractions import Fraction
+    g = synth.rng(42)
+    b, t, k = 6, 50, 96
+    x = (g.standard_normal((b * t, k)) * g.uniform(0.5, 3.0, k)).astype(np.float32)
+    x[17, 3] = 900.0
+    total = o.calib_sample_max_sum(x, b)
+    got = o.calib_mean_finalize(total, b)
+    per = np.abs(x.reshape(b, t, k)).max(axis=1)
+    expect = np.array([np.float32(float(sum(Fraction(float(v)) for v in per[:, j]) / b)) for j in range(k)],
+                      np.float32)
+    assert np.array_equal(got, expect)
+    assert 900.0 / b < got[3] < 900.0
+    # sample by sample over several calls == all samples in one call
+    tot2 = np.zeros(k, np.float64)
+    for i in range(b):
+        o.calib_sample_max_sum(np.ascontiguousarray(x[i * t:(i + 1) * t]), 1, tot2)
+    assert np.array_equal(tot2, total)
+    # one sample: the plain maximum (O1)
+    first = np.ascontiguousarray(x[:t])
+    assert np.array_equal(o.calib_mean_finalize(o.calib_sample_max_sum(first, 1), 1), o.calib_absmax(first))
+
+
+def pin_percentile(o):
+    """kwkr.cn blog §3.1: a high percentile in place of the absolute maximum,
+    as a nearest rank; numpy's inverted-CDF quantile is the same statistic."""
+    g = synth.rng(43)
+    rows, k = 1000, 40
+    x = (g.standard_normal((rows, k)) * g.uniform(0.5, 2.0, k)).astype(np.float32)
+    x[5, :] = 1000.0
+    ax = np.abs(x)
+    for q in (0.999, 0.9995, 0.5, 0.3333, 1.0):
+        ref = np.quantile(ax, q, axis=0, method="inverted_cdf").astype(np.float32)
+        assert np.array_equal(o.calib_percentile(x, q), ref), q
+    assert np.array_equal(o.calib_percentile(x, 1.0), o.calib_absmax(x))
+    assert np.all(o.calib_percentile(x, 0.999) < 1000.0)
+    assert o.percentile_rank(0.999, 262144) == 261882 and o.percentile_rank(0.0, 10) == 1
+    xb = synth.to_bf16_bits(x)
+    ref = np.quantile(np.abs(synth.bf16_bits_to_f32(xb)), 0.999, axis=0, method="inverted_cdf").astype(np.float32)
+    assert np.array_equal(o.calib_percentile(xb, 0.999), ref)
+
+
+# ---- O16 - O18: RMSNorm and the fold of 1/s into its weight -------------------------
+
+def pin_rmsnorm(o):
+    """O16 against torch's RMSNorm evaluated in fp64, and its closed forms."""
+    import torch
+    g = synth.rng(44)
+    m, k, eps = 12, 320, 1e-5
+    h = (g.standard_normal((m, k)) * g.uniform(0.1, 20.0, (m, 1))).astype(np.float32)
+    gamma = g.uniform(0.5, 1.5, k).astype(np.float32)
+    r = o.rms_inv(h, eps)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(h).double(), (k,), torch.from_numpy(gamma).double(),
+                                       eps=float(np.float32(eps))).numpy()
+    assert np.allclose(o.rmsnorm_apply(h, r, gamma), ref, rtol=5e-7, atol=0)
+    # a constant row c: r = 1/sqrt(c^2 + eps)
+    c = np.full((1, k), 3.0, np.float32)
+    assert o.rms_inv(c, eps)[0] == np.float32(1.0 / np.sqrt(9.0 + float(np.float32(eps))))
+    # +-1 rows with eps = 0: r = 1 and the output is gamma with the input's signs
+    pm = np.where(g.random((2, k)) < 0.5, -1.0, 1.0).astype(np.float32)
+    assert np.all(o.rms_inv(pm, 0.0) == 1.0)
+    assert np.array_equal(o.rmsnorm_apply(pm, np.ones(2, np.float32), gamma), pm * gamma)
+    # bf16 output is the round-to-nearest-even of the fp32 output
+    yb = o.rmsnorm_apply(synth.to_bf16_bits(h), r, gamma, bf16=True)
+    y32 = o.rmsnorm_apply(synth.bf16_bits_to_f32(synth.to_bf16_bits(h)), r, gamma)
+    assert np.array_equal(yb, torch.from_numpy(y32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+def pin_norm_fold(o):
+    """kwkr.cn blog §3.2: 1/s multiplied into the norm weight gives X/s at
+    the norm's output. With power-of-two factors every product is exact, so
+    the fused norm + quantizer equals the plain norm followed by O8."""
+    g = synth.rng(45)
+    m, k, eps = 16, 256, 1e-5
+    h = g.standard_normal((m, k)).astype(np.float32)
+    h[:, 9] *= 40
+    gamma = g.uniform(0.5, 1.5, k).astype(np.float32)
+    inv_s = (2.0 ** g.integers(-4, 3, k)).astype(np.float32)
+    gf = o.fold_norm_weight(gamma, inv_s)
+    assert np.array_equal(gf, gamma * inv_s)
+    r = o.rms_inv(h, eps)
+    y = o.rmsnorm_apply(h, r, gamma)
+    a = o.act_scale(o.calib_absmax(y), inv_s)
+    xq = o.norm_quant_apply(h, r, gf, a)
+    assert np.array_equal(xq, o.quant_act(y, inv_s, a))
+    assert int(np.abs(xq.astype(np.int32)).max()) == 127
+    # general factors: the fold changes only rounding, so codes move by at most one step, rarely
+    inv_s2 = g.uniform(0.05, 3.0, k).astype(np.float32)
+    a2 = o.act_scale(o.calib_absmax(y), inv_s2)
+    d = (o.norm_quant_apply(h, r, o.fold_norm_weight(gamma, inv_s2), a2).astype(np.int32)
+         - o.quant_act(y, inv_s2, a2).astype(np.int32))
+    assert np.abs(d).max() <= 1 and (d != 0).mean() < 0.01
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

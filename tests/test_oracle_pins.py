@@ -45,6 +45,28 @@ MUTANTS = {
     "weight_scale_over_128": ("float ws = mx / SQO_QMAX;", "float ws = mx / 128.0f;"),
     "ref_gemm_float_accum": ("double sum = 0.0;\n        for (int64_t j = 0; j < k; ++j)\n            sum += (double)elem(x",
                              "float sum = 0.0f;\n        for (int64_t j = 0; j < k; ++j)\n            sum += (float)elem(x"),
+    "dynamic_scale_half_channels": ("float a = sqo_act_scale(live, inv_s, k);",
+                                    "float a = sqo_act_scale(live, inv_s, k / 2);"),
+    "dynamic_scale_unsmoothed": ("float a = sqo_act_scale(live, inv_s, k);",
+                                 "float* one = (float*)malloc((size_t)k * sizeof(float));\n    for (int64_t j = 0; j < k; ++j) one[j] = 1.0f;\n    float a = sqo_act_scale(live, one, k);\n    free(one);"),
+    "sample_max_runs_on": ("for (int64_t b = 0; b < samples; ++b) {\n            float mx = 0.0f;",
+                           "float mx = 0.0f;\n        for (int64_t b = 0; b < samples; ++b) {"),
+    "mean_off_by_one": ("act_max[j] = (float)(sum[j] / (double)count);",
+                        "act_max[j] = (float)(sum[j] / (double)(count + 1));"),
+    "percentile_rank_floor": ("int64_t rank = (int64_t)ceil(q * (double)rows);",
+                              "int64_t rank = (int64_t)floor(q * (double)rows);"),
+    "percentile_descending": ("return (x > y) - (x < y);", "return (x < y) - (x > y);"),
+    "rms_sum_not_mean": ("r[t] = (float)(1.0 / sqrt(ss / (double)k + (double)eps));",
+                         "r[t] = (float)(1.0 / sqrt(ss + (double)eps));"),
+    "rms_eps_outside": ("r[t] = (float)(1.0 / sqrt(ss / (double)k + (double)eps));",
+                        "r[t] = (float)(1.0 / sqrt(ss / (double)k) + (double)eps);"),
+    "rms_no_sqrt": ("r[t] = (float)(1.0 / sqrt(ss / (double)k + (double)eps));",
+                    "r[t] = (float)(1.0 / (ss / (double)k + (double)eps));"),
+    "fold_multiplies_s": ("gamma_folded[j] = gamma[j] * inv_s[j];", "gamma_folded[j] = gamma[j] / inv_s[j];"),
+    "norm_quant_drops_gamma": ("float smoothed = (elem(h, htype, t * k + j) * r[t]) * gamma_folded[j];",
+                               "float smoothed = elem(h, htype, t * k + j) * r[t]; (void)gamma_folded;"),
+    "norm_quant_drops_r": ("float smoothed = (elem(h, htype, t * k + j) * r[t]) * gamma_folded[j];",
+                           "float smoothed = elem(h, htype, t * k + j) * gamma_folded[j];"),
 }
 
 

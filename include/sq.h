@@ -7,7 +7,8 @@
  *           (sections 1.2, 2.1-2.3, 3.1-3.3)
  *   [ADR]   "010. SmoothQuant Integration", blog.yoooo.fun (Context, Key design)
  *   [pwwt]  "SmoothQuant技术解析：LLM模型INT8无损量化实践", pwwt.cn (§3.1 kernel stub)
- *   [tbr8]  tbr8.org, activation outliers and SmoothQuant (PyTorch example)
+ *   [tbr8]  tbr8.org, activation outliers and SmoothQuant (PyTorch example);
+ *   [pwwt §2.3] static and dynamic scale modes on the same pwwt.cn page
  *
  * Conventions shared by every entry point
  *   - Matrices are row-major with the reduction dimension k contiguous:
@@ -121,6 +122,83 @@ sq_status sq_smooth_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k,
 sq_status sq_w8a8_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n,
                        int64_t k, const float* act_scale, const float* w_scale,
                        void* y, sq_dtype yt, int32_t* acc_out, hipStream_t stream);
+
+/*
+ * The closed-form per-tensor activation scale alone [ADR Key design item 1],
+ * for a statistic gathered after the smoothing factors were fixed (dynamic
+ * mode, robust calibration statistics):
+ *   act_scale = fp32( max_j fp32(max(act_max[j], 1e-5) * inv_s[j]) / 127 )
+ *   act_max, inv_s [k] fp32; act_scale [1] fp32 out (device).
+ */
+sq_status sq_act_scale(const float* act_max, const float* inv_s, int64_t k,
+                       float* act_scale, hipStream_t stream);
+
+/*
+ * Dynamic mode [pwwt §2.3: scales computed at run time follow the input, at
+ * some extra cost per call]: the offline smoothing factors are kept and the
+ * per-tensor activation scale is recomputed from the batch being quantized:
+ *   live_max[j] = max_t |x[t,j]|                       (0 when m = 0)
+ *   act_scale   = sq_act_scale(live_max, inv_s)
+ *   xq          = sq_smooth_quant_act(x, inv_s, act_scale)
+ *   x [m,k] of type xt; inv_s [k] fp32; live_max [k] fp32 out (the caller's
+ *   buffer, left holding the batch statistic); act_scale [1] fp32 out;
+ *   xq [m,k] int8 out. x is read twice (statistic, then codes).
+ */
+sq_status sq_dynamic_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k,
+                               const float* inv_s, float* live_max, float* act_scale,
+                               int8_t* xq, hipStream_t stream);
+
+/*
+ * Averaged per-sample maxima [kwkr §3.1: averaging the maxima of several
+ * samples makes the statistic less sensitive to one extreme sample]:
+ *   x holds `samples` consecutive samples of rows_per_sample rows each:
+ *   sample_max[b,j] = max over the rows t of sample b of |x[t,j]|
+ *                     ([samples, k] fp32 out)
+ *   sum[j]         += (double) sample_max[b,j] for b = 0, 1, ... in order
+ *                     ([k] fp64 in/out; zero it before the first batch: the
+ *                     additions follow the order of the samples across calls)
+ * samples may be 0 (nothing happens); rows_per_sample >= 1.
+ */
+sq_status sq_calib_sample_max_sum(const void* x, sq_dtype xt, int64_t samples,
+                                  int64_t rows_per_sample, int64_t k, float* sample_max,
+                                  double* sum, hipStream_t stream);
+
+/* act_max[j] = fp32(sum[j] / count), count >= 1 samples seen. */
+sq_status sq_calib_mean_finalize(const double* sum, int64_t count, int64_t k,
+                                 float* act_max, hipStream_t stream);
+
+/*
+ * RMSNorm, the norm in front of the projections of a Llama block; its weight
+ * is where 1/s can be folded [kwkr §3.2]:
+ *   r[t]   = fp32( 1 / sqrt( sum_j h[t,j]^2 / k + eps ) )   (fp64 arithmetic,
+ *            one rounding; the additions of the squares are in an unspecified
+ *            order, so r can differ from a sequential sum by one fp32 ulp)
+ *   y[t,j] = fp32( fp32(h[t,j] * r[t]) * gamma[j] )   (yt SQ_F32 or SQ_BF16 = RNE)
+ *   h [m,k] of type ht; gamma [k] fp32; y [m,k]; r_out [m] fp32 or NULL.
+ *   eps finite and >= 0 (SQ_ERR_SHAPE otherwise); m <= INT32_MAX.
+ */
+sq_status sq_rmsnorm(const void* h, sq_dtype ht, int64_t m, int64_t k, const float* gamma,
+                     float eps, void* y, sq_dtype yt, float* r_out, hipStream_t stream);
+
+/*
+ * 1/s folded into the norm weight, once, offline [kwkr §2.3, §3.2]:
+ *   gamma_folded[j] = fp32(gamma[j] * inv_s[j])      ([k] fp32 in and out)
+ */
+sq_status sq_fold_norm_weight(const float* gamma, const float* inv_s, int64_t k,
+                              float* gamma_folded, hipStream_t stream);
+
+/*
+ * RMSNorm with the folded weight feeding the per-tensor quantizer in the same
+ * pass: the norm's output is already X/s, scaled before it is rounded [kwkr
+ * §3.2], so the separate activation pass disappears:
+ *   xq[t,j] = clamp(rne(fp32( fp32(fp32(h[t,j]*r[t]) * gamma_folded[j])
+ *                             * fp32(1/act_scale[0]) )), -127, 127)
+ *   r as in sq_rmsnorm (r_out [m] or NULL); h [m,k] of type ht;
+ *   gamma_folded [k] fp32; act_scale [1] fp32; xq [m,k] int8 out.
+ */
+sq_status sq_rmsnorm_quant_act(const void* h, sq_dtype ht, int64_t m, int64_t k,
+                               const float* gamma_folded, float eps, const float* act_scale,
+                               int8_t* xq, float* r_out, hipStream_t stream);
 
 /*
  * Host-only query: the block tile (rows x columns of Y per workgroup) that

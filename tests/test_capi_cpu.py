@@ -156,3 +156,96 @@ def test_alpha_search_validation(lib):
     mb = (ctypes.c_void_p * 2)(A, MIS)
     assert call(batches=mb) == ALIGN
     assert best.value == -1  # nothing written on error
+
+
+def test_new_entries_exported(lib):
+    for name in ("sq_act_scale", "sq_dynamic_quant_act", "sq_calib_sample_max_sum", "sq_calib_mean_finalize",
+                 "sq_rmsnorm", "sq_fold_norm_weight", "sq_rmsnorm_quant_act"):
+        assert name in capi.declared_functions()
+        assert hasattr(lib, name)
+
+
+def test_act_scale_and_dynamic_validation(lib):
+    f = lib.sq_act_scale
+    assert f(None, P(A), 1024, P(A), None) == NULL
+    assert f(P(A), P(A), 1000, P(A), None) == SHAPE
+    assert f(P(A), P(A), 1024, P(MIS), None) == ALIGN
+    g = lib.sq_dynamic_quant_act
+    base = [P(A), 1, 16, 1024, P(A), P(A), P(A), P(A), None]
+    for i, code in ((4, NULL), (5, NULL), (6, NULL), (7, NULL)):
+        a = list(base)
+        a[i] = None
+        assert g(*a) == code
+    a = list(base)
+    a[1] = 5
+    assert g(*a) == DTYPE
+    a = list(base)
+    a[2] = -1
+    assert g(*a) == SHAPE
+    a = list(base)
+    a[3] = 96
+    assert g(*a) == SHAPE
+    a = list(base)
+    a[5] = P(MIS)
+    assert g(*a) == ALIGN
+
+
+def test_sample_max_validation(lib):
+    f = lib.sq_calib_sample_max_sum
+    base = [P(A), 1, 4, 512, 1024, P(A), P(A), None]
+    a = list(base)
+    a[6] = None
+    assert f(*a) == NULL
+    a = list(base)
+    a[5] = None
+    assert f(*a) == NULL
+    a = list(base)
+    a[3] = 0
+    assert f(*a) == SHAPE
+    a = list(base)
+    a[2] = -1
+    assert f(*a) == SHAPE
+    a = list(base)
+    a[6] = P(MIS)
+    assert f(*a) == ALIGN
+    # zero samples: nothing to do, x and sample_max may be NULL
+    assert f(None, 1, 0, 512, 1024, None, P(A), None) == OK
+    g = lib.sq_calib_mean_finalize
+    assert g(P(A), 0, 1024, P(A), None) == SHAPE
+    assert g(None, 4, 1024, P(A), None) == NULL
+    assert g(P(A), 4, 1024, P(MIS), None) == ALIGN
+
+
+def test_norm_validation(lib):
+    f = lib.sq_rmsnorm
+    base = [P(A), 1, 8, 1024, P(A), 1e-5, P(A), 1, None, None]
+    a = list(base)
+    a[4] = None
+    assert f(*a) == NULL
+    a = list(base)
+    a[7] = 9
+    assert f(*a) == DTYPE
+    for bad in (float("nan"), float("inf"), -1e-6):
+        a = list(base)
+        a[5] = bad
+        assert f(*a) == SHAPE
+    a = list(base)
+    a[8] = P(MIS)
+    assert f(*a) == ALIGN
+    g = lib.sq_fold_norm_weight
+    assert g(P(A), None, 1024, P(A), None) == NULL
+    assert g(P(A), P(A), 100, P(A), None) == SHAPE
+    h = lib.sq_rmsnorm_quant_act
+    base = [P(A), 1, 8, 1024, P(A), 1e-5, P(A), P(A), None, None]
+    a = list(base)
+    a[6] = None
+    assert h(*a) == NULL
+    a = list(base)
+    a[3] = 1000
+    assert h(*a) == SHAPE
+    a = list(base)
+    a[7] = P(MIS)
+    assert h(*a) == ALIGN
+    a = list(base)
+    a[2] = 0
+    assert h(*a) == OK

@@ -50,6 +50,13 @@ def _declare(lib):
         "sq_alpha_search_workspace": [c.c_int, i64, i64, i64, c.c_int, P],
         "sq_gemm_tiling": [i64, i64, P, P],
         "sq_alpha_search": [P, c.c_int, c.c_int, i64, i64, P, c.c_int, i64, P, c.c_int, P, c.c_size_t, P, P, P],
+        "sq_act_scale": [P, P, i64, P, P],
+        "sq_dynamic_quant_act": [P, c.c_int, i64, i64, P, P, P, P, P],
+        "sq_calib_sample_max_sum": [P, c.c_int, i64, i64, i64, P, P, P],
+        "sq_calib_mean_finalize": [P, i64, i64, P, P],
+        "sq_rmsnorm": [P, c.c_int, i64, i64, P, c.c_float, P, c.c_int, P, P],
+        "sq_fold_norm_weight": [P, P, i64, P, P],
+        "sq_rmsnorm_quant_act": [P, c.c_int, i64, i64, P, c.c_float, P, P, P, P],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -169,3 +176,57 @@ def sq_alpha_search(x_batches, w, workspace, alphas=ALPHA_GRID, stream=None):
                                                      workspace.element_size(), ctypes.cast(mse, ctypes.c_void_p),
                                                      ctypes.byref(best), _stream(stream)))
     return list(mse), best.value
+
+
+def _opt(t, what: str):
+    return _dev(t, what) if t is not None else ctypes.c_void_p(0)
+
+
+def sq_act_scale(act_max, inv_s, act_scale, stream=None):
+    k = act_max.shape[0]
+    _check("sq_act_scale", load().sq_act_scale(_dev(act_max, "act_max"), _dev(inv_s, "inv_s"), k,
+                                               _dev(act_scale, "act_scale"), _stream(stream)))
+
+
+def sq_dynamic_quant_act(x, inv_s, live_max, act_scale, xq, stream=None):
+    m, k = x.shape
+    _check("sq_dynamic_quant_act", load().sq_dynamic_quant_act(_dev(x, "x"), _dtype_code(x), m, k,
+                                                               _dev(inv_s, "inv_s"), _dev(live_max, "live_max"),
+                                                               _dev(act_scale, "act_scale"), _dev(xq, "xq"),
+                                                               _stream(stream)))
+
+
+def sq_calib_sample_max_sum(x, samples: int, sample_max, total, stream=None):
+    rows, k = x.shape
+    if samples < 1 or rows % samples:
+        raise ValueError("rows must be a whole number of samples")
+    _check("sq_calib_sample_max_sum", load().sq_calib_sample_max_sum(_dev(x, "x"), _dtype_code(x), samples,
+                                                                     rows // samples, k,
+                                                                     _dev(sample_max, "sample_max"),
+                                                                     _dev(total, "sum"), _stream(stream)))
+
+
+def sq_calib_mean_finalize(total, count: int, act_max, stream=None):
+    k = total.shape[0]
+    _check("sq_calib_mean_finalize", load().sq_calib_mean_finalize(_dev(total, "sum"), count, k,
+                                                                   _dev(act_max, "act_max"), _stream(stream)))
+
+
+def sq_rmsnorm(h, gamma, eps: float, y, r_out=None, stream=None):
+    m, k = h.shape
+    _check("sq_rmsnorm", load().sq_rmsnorm(_dev(h, "h"), _dtype_code(h), m, k, _dev(gamma, "gamma"), float(eps),
+                                           _dev(y, "y"), _dtype_code(y), _opt(r_out, "r_out"), _stream(stream)))
+
+
+def sq_fold_norm_weight(gamma, inv_s, gamma_folded, stream=None):
+    k = gamma.shape[0]
+    _check("sq_fold_norm_weight", load().sq_fold_norm_weight(_dev(gamma, "gamma"), _dev(inv_s, "inv_s"), k,
+                                                             _dev(gamma_folded, "gamma_folded"), _stream(stream)))
+
+
+def sq_rmsnorm_quant_act(h, gamma_folded, eps: float, act_scale, xq, r_out=None, stream=None):
+    m, k = h.shape
+    _check("sq_rmsnorm_quant_act", load().sq_rmsnorm_quant_act(_dev(h, "h"), _dtype_code(h), m, k,
+                                                               _dev(gamma_folded, "gamma_folded"), float(eps),
+                                                               _dev(act_scale, "act_scale"), _dev(xq, "xq"),
+                                                               _opt(r_out, "r_out"), _stream(stream)))

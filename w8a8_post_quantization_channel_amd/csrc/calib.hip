@@ -63,8 +63,9 @@ __device__ __forceinline__ uint32_t column_bits(const uint32_t* words, int c) {
 // rows; wave w takes rows r0 + w, r0 + w + 4, ... with kAbsUnroll loads in
 // flight per lane. The four wave partials meet in LDS; then every thread
 // merges whole columns so each atomic instruction covers consecutive
-// addresses.
-template <int EB>
+// addresses. kPerChunk: each row chunk is one calibration sample and its
+// maxima are stored to row blockIdx.y of out (no atomics, no zero fill).
+template <int EB, bool kPerChunk>
 __global__ __launch_bounds__(kAbsThreads) void absmax_kernel(const u32x4* __restrict__ x, int64_t rows,
                                                              int64_t kvec, int64_t k, int64_t rows_per_block,
                                                              unsigned* __restrict__ out_bits) {
@@ -106,8 +107,41 @@ __global__ __launch_bounds__(kAbsThreads) void absmax_kernel(const u32x4* __rest
             const uint32_t words[4] = {pv.x, pv.y, pv.z, pv.w};
             best = max(best, column_bits<EB>(words, c));
         }
-        atomicMax(out_bits + col0 + c, best);
+        if constexpr (kPerChunk)
+            out_bits[(int64_t)blockIdx.y * k + col0 + c] = best;
+        else
+            atomicMax(out_bits + col0 + c, best);
     }
+}
+
+// Running fp64 sum of per-sample maxima, one thread per channel, the samples
+// added strictly in order (so the result does not depend on the launch
+// shape); kSumBatch loads are issued before their additions.
+constexpr int kSumThreads = 256;
+constexpr int kSumBatch = 16;
+
+__global__ __launch_bounds__(kSumThreads) void sum_samples_kernel(const float* __restrict__ sample_max,
+                                                                  int64_t samples, int64_t k,
+                                                                  double* __restrict__ sum) {
+    const int64_t j = (int64_t)blockIdx.x * kSumThreads + threadIdx.x;
+    if (j >= k) return;
+    double acc = sum[j];
+    int64_t b = 0;
+    for (; b + kSumBatch <= samples; b += kSumBatch) {
+        float v[kSumBatch];
+#pragma unroll
+        for (int u = 0; u < kSumBatch; ++u) v[u] = sample_max[(b + u) * k + j];
+#pragma unroll
+        for (int u = 0; u < kSumBatch; ++u) acc += (double)v[u];
+    }
+    for (; b < samples; ++b) acc += (double)sample_max[b * k + j];
+    sum[j] = acc;
+}
+
+__global__ __launch_bounds__(kSumThreads) void mean_finalize_kernel(const double* __restrict__ sum, double count,
+                                                                    int64_t k, float* __restrict__ act_max) {
+    const int64_t j = (int64_t)blockIdx.x * kSumThreads + threadIdx.x;
+    if (j < k) act_max[j] = (float)(sum[j] / count);
 }
 
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -177,11 +211,53 @@ hipError_t absmax(const void* x, int xt, int64_t rows, int64_t k, float* absmax_
     }
     dim3 grid((unsigned)strips, (unsigned)chunks);
     if (eb == 2)
-        absmax_kernel<2><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x, rows, kvec, k, rpb,
-                                                                 (unsigned*)absmax_out);
+        absmax_kernel<2, false><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x, rows, kvec, k, rpb,
+                                                                        (unsigned*)absmax_out);
     else
-        absmax_kernel<4><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x, rows, kvec, k, rpb,
-                                                                 (unsigned*)absmax_out);
+        absmax_kernel<4, false><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x, rows, kvec, k, rpb,
+                                                                        (unsigned*)absmax_out);
+    return hipGetLastError();
+}
+
+hipError_t act_scale(const float* act_max, const float* inv_s, int64_t k, float* act_scale_out,
+                     hipStream_t stream) {
+    act_scale_kernel<<<dim3(1), dim3(kScaleThreads), 0, stream>>>(act_max, inv_s, k, act_scale_out);
+    return hipGetLastError();
+}
+
+hipError_t sample_max(const void* x, int xt, int64_t samples, int64_t rows_per_sample, int64_t k,
+                      float* sample_max_out, hipStream_t stream) {
+    const int eb = elem_bytes(xt);
+    const int64_t kvec = k * eb / 16;
+    const int64_t strips = (kvec + 63) / 64;
+    const int64_t rows = samples * rows_per_sample;
+    // one block per (column strip, sample); samples beyond the 65535 grid
+    // rows are taken by further launches
+    for (int64_t b0 = 0; b0 < samples; b0 += 65535) {
+        const int64_t nb = std::min<int64_t>(65535, samples - b0);
+        const dim3 grid((unsigned)strips, (unsigned)nb);
+        const int64_t off = b0 * rows_per_sample * kvec;
+        unsigned* out = (unsigned*)(sample_max_out + b0 * k);
+        const int64_t r = std::min<int64_t>(rows - b0 * rows_per_sample, nb * rows_per_sample);
+        if (eb == 2)
+            absmax_kernel<2, true><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x + off, r, kvec, k,
+                                                                          rows_per_sample, out);
+        else
+            absmax_kernel<4, true><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x + off, r, kvec, k,
+                                                                          rows_per_sample, out);
+    }
+    return hipGetLastError();
+}
+
+hipError_t sum_samples(const float* sample_max_in, int64_t samples, int64_t k, double* sum, hipStream_t stream) {
+    sum_samples_kernel<<<dim3((unsigned)((k + kSumThreads - 1) / kSumThreads)), dim3(kSumThreads), 0, stream>>>(
+        sample_max_in, samples, k, sum);
+    return hipGetLastError();
+}
+
+hipError_t mean_finalize(const double* sum, int64_t count, int64_t k, float* act_max, hipStream_t stream) {
+    mean_finalize_kernel<<<dim3((unsigned)((k + kSumThreads - 1) / kSumThreads)), dim3(kSumThreads), 0,
+                           stream>>>(sum, (double)count, k, act_max);
     return hipGetLastError();
 }
 

@@ -126,6 +126,77 @@ sq_status sq_w8a8_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n,
     return hip_status(sqk::gemm_dequant(xq, wq, m, n, k, act_scale, w_scale, y, yt, acc_out, stream));
 }
 
+sq_status sq_act_scale(const float* act_max, const float* inv_s, int64_t k, float* act_scale, hipStream_t stream) {
+    if (!act_max || !inv_s || !act_scale) return SQ_ERR_NULL;
+    if (!valid_k(k)) return SQ_ERR_SHAPE;
+    if (!aligned16(act_max) || !aligned16(inv_s) || !aligned16(act_scale)) return SQ_ERR_ALIGN;
+    return hip_status(sqk::act_scale(act_max, inv_s, k, act_scale, stream));
+}
+
+sq_status sq_dynamic_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* inv_s,
+                               float* live_max, float* act_scale, int8_t* xq, hipStream_t stream) {
+    if (!inv_s || !live_max || !act_scale || (m > 0 && (!x || !xq))) return SQ_ERR_NULL;
+    if (!valid_dtype(xt)) return SQ_ERR_DTYPE;
+    if (m < 0 || !valid_k(k)) return SQ_ERR_SHAPE;
+    if (!aligned16(inv_s) || !aligned16(live_max) || !aligned16(act_scale) ||
+        (m > 0 && (!aligned16(x) || !aligned16(xq))))
+        return SQ_ERR_ALIGN;
+    hipError_t e = sqk::absmax(x, xt, m, k, live_max, false, stream);
+    if (e == hipSuccess) e = sqk::act_scale(live_max, inv_s, k, act_scale, stream);
+    if (e == hipSuccess && m > 0) e = sqk::quant_act(x, xt, m, k, inv_s, act_scale, xq, stream);
+    return hip_status(e);
+}
+
+sq_status sq_calib_sample_max_sum(const void* x, sq_dtype xt, int64_t samples, int64_t rows_per_sample, int64_t k,
+                                  float* sample_max, double* sum, hipStream_t stream) {
+    if (!sum || (samples > 0 && (!x || !sample_max))) return SQ_ERR_NULL;
+    if (!valid_dtype(xt)) return SQ_ERR_DTYPE;
+    if (samples < 0 || rows_per_sample < 1 || !valid_k(k)) return SQ_ERR_SHAPE;
+    if (!aligned16(sum) || (samples > 0 && (!aligned16(x) || !aligned16(sample_max)))) return SQ_ERR_ALIGN;
+    if (samples == 0) return SQ_OK;
+    hipError_t e = sqk::sample_max(x, xt, samples, rows_per_sample, k, sample_max, stream);
+    if (e == hipSuccess) e = sqk::sum_samples(sample_max, samples, k, sum, stream);
+    return hip_status(e);
+}
+
+sq_status sq_calib_mean_finalize(const double* sum, int64_t count, int64_t k, float* act_max, hipStream_t stream) {
+    if (!sum || !act_max) return SQ_ERR_NULL;
+    if (count < 1 || !valid_k(k)) return SQ_ERR_SHAPE;
+    if (!aligned16(sum) || !aligned16(act_max)) return SQ_ERR_ALIGN;
+    return hip_status(sqk::mean_finalize(sum, count, k, act_max, stream));
+}
+
+static bool valid_eps(float eps) { return std::isfinite(eps) && eps >= 0.0f; }
+
+sq_status sq_rmsnorm(const void* h, sq_dtype ht, int64_t m, int64_t k, const float* gamma, float eps, void* y,
+                     sq_dtype yt, float* r_out, hipStream_t stream) {
+    if (!gamma || (m > 0 && (!h || !y))) return SQ_ERR_NULL;
+    if (!valid_dtype(ht) || !valid_dtype(yt)) return SQ_ERR_DTYPE;
+    if (m < 0 || m > INT32_MAX || !valid_k(k) || !valid_eps(eps)) return SQ_ERR_SHAPE;
+    if (!aligned16(gamma) || (m > 0 && (!aligned16(h) || !aligned16(y))) || (r_out && !aligned16(r_out)))
+        return SQ_ERR_ALIGN;
+    return hip_status(sqk::rmsnorm(h, ht, m, k, gamma, eps, y, yt, r_out, stream));
+}
+
+sq_status sq_fold_norm_weight(const float* gamma, const float* inv_s, int64_t k, float* gamma_folded,
+                              hipStream_t stream) {
+    if (!gamma || !inv_s || !gamma_folded) return SQ_ERR_NULL;
+    if (!valid_k(k)) return SQ_ERR_SHAPE;
+    if (!aligned16(gamma) || !aligned16(inv_s) || !aligned16(gamma_folded)) return SQ_ERR_ALIGN;
+    return hip_status(sqk::fold_norm_weight(gamma, inv_s, k, gamma_folded, stream));
+}
+
+sq_status sq_rmsnorm_quant_act(const void* h, sq_dtype ht, int64_t m, int64_t k, const float* gamma_folded,
+                               float eps, const float* act_scale, int8_t* xq, float* r_out, hipStream_t stream) {
+    if (!gamma_folded || !act_scale || (m > 0 && (!h || !xq))) return SQ_ERR_NULL;
+    if (!valid_dtype(ht)) return SQ_ERR_DTYPE;
+    if (m < 0 || m > INT32_MAX || !valid_k(k) || !valid_eps(eps)) return SQ_ERR_SHAPE;
+    if (!aligned16(gamma_folded) || !aligned16(act_scale) || (m > 0 && (!aligned16(h) || !aligned16(xq))) ||
+        (r_out && !aligned16(r_out)))
+        return SQ_ERR_ALIGN;
+    return hip_status(sqk::rmsnorm_quant(h, ht, m, k, gamma_folded, eps, act_scale, xq, r_out, stream));
+}
+
 sq_status sq_gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n) {
     if (!block_m || !block_n) return SQ_ERR_NULL;
     if (m < 0 || n < 0) return SQ_ERR_SHAPE;

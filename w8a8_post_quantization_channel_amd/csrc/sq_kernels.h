@@ -17,6 +17,32 @@ inline int elem_bytes(int t) { return t == kBF16 ? 2 : 4; }
 hipError_t absmax(const void* x, int xt, int64_t rows, int64_t k, float* absmax, bool accumulate,
                   hipStream_t stream);
 
+// act_scale = fp32(max_j fp32(max(act_max[j], 1e-5) * inv_s[j]) / 127)
+hipError_t act_scale(const float* act_max, const float* inv_s, int64_t k, float* act_scale, hipStream_t stream);
+
+// sample_max[b, j] = max over the rows of sample b of |x[., j]| (samples of
+// rows_per_sample consecutive rows)
+hipError_t sample_max(const void* x, int xt, int64_t samples, int64_t rows_per_sample, int64_t k,
+                      float* sample_max, hipStream_t stream);
+
+// sum[j] += sample_max[b, j] in fp64, b ascending
+hipError_t sum_samples(const float* sample_max, int64_t samples, int64_t k, double* sum, hipStream_t stream);
+
+// act_max[j] = fp32(sum[j] / count)
+hipError_t mean_finalize(const double* sum, int64_t count, int64_t k, float* act_max, hipStream_t stream);
+
+// RMSNorm y = fl(fl(h * r) * gamma) (fp32 or bf16 out), r per row (optional out)
+hipError_t rmsnorm(const void* h, int ht, int64_t m, int64_t k, const float* gamma, float eps, void* y, int yt,
+                   float* r_out, hipStream_t stream);
+
+// RMSNorm with the folded weight, quantized per tensor in the same pass
+hipError_t rmsnorm_quant(const void* h, int ht, int64_t m, int64_t k, const float* gamma_folded, float eps,
+                         const float* act_scale, int8_t* xq, float* r_out, hipStream_t stream);
+
+// gamma_folded = fl(gamma * inv_s)
+hipError_t fold_norm_weight(const float* gamma, const float* inv_s, int64_t k, float* gamma_folded,
+                            hipStream_t stream);
+
 // s, inv_s, act_scale from the two statistics
 hipError_t smooth_factors(const float* act_max, const float* w_max, int64_t k, float alpha, float* s,
                           float* inv_s, float* act_scale, hipStream_t stream);

@@ -56,7 +56,8 @@ def parse():
                     help="counter summary with the HBM bytes per GEMM launch (default: the committed "
                          "profiles/gemm_traffic__llama13b_prefill2048.md, used only if it matches gemm.hip)")
     ap.add_argument("--workload", default="layer13b",
-                    choices=["layer13b", "decode7b", "alpha_search", "prefill70b", "hbm_passes", "copy_probe"],
+                    choices=["layer13b", "decode7b", "alpha_search", "prefill70b", "hbm_passes", "copy_probe",
+                             "variants"],
                     help="layer13b (default, the headline line); the others measure the remaining "
                          "workloads, one JSON line each")
     return ap.parse_args()
@@ -428,6 +429,73 @@ def workload_hbm_passes(device):
             "per_pass": out}
 
 
+def workload_variants(device):
+    """The widened rows, each beside the form it replaces:
+    - dynamic vs static activation scale: the runtime forward (activation
+      quantization + GEMM) of the seven 13B projections at 2048 tokens;
+    - 1/s folded into the RMSNorm weight: one fused norm + quantizer pass
+      against RMSNorm (bf16 out) followed by the activation quantizer, at the
+      13B (2048 x 5120) and 70B (4096 x 8192) norm shapes;
+    - averaged per-sample maxima against the plain running maximum over the
+      13B calibration set (512 samples x 512 tokens x 5120)."""
+    import torch
+    from w8a8_post_quantization_channel_amd import capi, synth
+    out = {}
+    groups, projs = setup(device)
+    for _ in range(2):
+        run_step(groups, projs)  # calibrate + prepare every projection
+    torch.cuda.synchronize()
+    static_ms = timed(lambda: [layer.forward(g.x) for _, g, layer, _ in projs], 20)
+    dynamic_ms = timed(lambda: [layer.forward_dynamic(g.x) for _, g, layer, _ in projs], 20)
+    step_ms = timed(lambda: run_step(groups, projs), 20)
+    out["dynamic_scale_13b"] = {
+        "static_forward_us": static_ms * 1e3, "dynamic_forward_us": dynamic_ms * 1e3,
+        "overhead_vs_static_forward": dynamic_ms / static_ms - 1.0,
+        "overhead_vs_whole_step": (dynamic_ms - static_ms) / step_ms,
+        "forward": "7 projections: activation quantization + int8 GEMM, 2048 tokens"}
+    del groups, projs
+    torch.cuda.empty_cache()
+
+    for name, m, k in (("13b", 2048, 5120), ("70b", 4096, 8192)):
+        h = synth.device_activations(4100 + k, m, k, synth.outlier_channels(4000 + k, k), device)
+        g = torch.rand(k, device=device) + 0.5
+        inv_s = torch.rand(k, device=device) + 0.25
+        gf = torch.empty(k, dtype=torch.float32, device=device)
+        capi.sq_fold_norm_weight(g, inv_s, gf)
+        a = torch.full((4,), 0.05, device=device)
+        y = torch.empty((m, k), dtype=torch.bfloat16, device=device)
+        xq = torch.empty((m, k), dtype=torch.int8, device=device)
+        fused_ms = timed(lambda: capi.sq_rmsnorm_quant_act(h, gf, 1e-5, a, xq), 50)
+        norm_ms = timed(lambda: capi.sq_rmsnorm(h, g, 1e-5, y), 50)
+        quant_ms = timed(lambda: capi.sq_smooth_quant_act(y, inv_s, a, xq), 50)
+        byts = m * k * 3 + k * 4
+        out[f"norm_fold_{name}_{m}x{k}"] = {
+            "fused_us": fused_ms * 1e3, "unfused_norm_us": norm_ms * 1e3, "unfused_quant_us": quant_ms * 1e3,
+            "speedup": (norm_ms + quant_ms) / fused_ms, "fused_GB/s": byts / (fused_ms * 1e-3) / 1e9,
+            "fused_hbm_frac": byts / (fused_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "bytes_per_element": {"fused": 3, "unfused": 7}}
+        del h, y, xq
+        torch.cuda.empty_cache()
+
+    samples, rows, k = 512, 512, 5120
+    x = synth.device_activations(4200, samples * rows, k, synth.outlier_channels(4201, k), device)
+    smax = torch.empty((samples, k), dtype=torch.float32, device=device)
+    total = torch.zeros(k, dtype=torch.float64, device=device)
+    am = torch.empty(k, dtype=torch.float32, device=device)
+    mean_ms = timed(lambda: capi.sq_calib_sample_max_sum(x, samples, smax, total), 5)
+    max_ms = timed(lambda: capi.sq_calib_absmax(x, am, False), 5)
+    byts = x.numel() * 2 + samples * k * 4
+    out["calib_mean_of_max_262144x5120"] = {
+        "us": mean_ms * 1e3, "GB/s": byts / (mean_ms * 1e-3) / 1e9,
+        "hbm_frac": byts / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "plain_max_us": max_ms * 1e3}
+    return {"metric": "widened rows beside the forms they replace (time, GB/s)",
+            "value": out["norm_fold_70b_4096x8192"]["fused_GB/s"], "unit": "GB/s (fused norm + quantizer, 70B shape)",
+            "n_gpus": 1, "higher_is_better": True, "dtype": "bf16->int8", "data": "synthetic",
+            "config": {"workload": "dynamic scale (13B forward), RMSNorm fold (13B/70B norm shapes), "
+                                   "mean of per-sample maxima (13B calibration set)"},
+            "per_row": out}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -440,7 +508,7 @@ def main():
     capi.load()  # fails loudly when libsq.so is missing
     device = torch.device("cuda", 0)
     other = {"decode7b": workload_decode7b, "alpha_search": workload_alpha_search, "copy_probe": workload_copy_probe,
-             "prefill70b": workload_prefill70b, "hbm_passes": workload_hbm_passes}
+             "prefill70b": workload_prefill70b, "hbm_passes": workload_hbm_passes, "variants": workload_variants}
     if args.workload in other:
         out = other[args.workload](device)
         out["gpu"] = torch.cuda.get_device_name(0)

@@ -4,13 +4,13 @@
 // absorbed by the gamma of the preceding norm, once, offline, and the scaling
 // still happens before the rounding).
 //
-// One block of 256 threads per row. The row's sum of squares is taken in
-// fp64 (squares of bf16 or fp32 values are exact in fp64, so only the order
-// of the additions is free), reduced across the block, and
+// The row's sum of squares is taken in fp64 (squares of bf16 or fp32 values
+// are exact in fp64, so only the order of the additions is free) and
 // r = fp32(1 / sqrt(sum / k + eps)) is evaluated in fp64 and rounded once.
-// Rows of up to 256 * 8 16-byte vectors (16384 bf16 or 8192 fp32 values) stay
-// in registers between the reduction and the output pass; longer rows are
-// read a second time (from L2).
+// A block of 256 threads takes one to eight rows, held in registers between
+// the reduction and the output pass up to 256 * 8 16-byte vectors per row
+// (16384 bf16 or 8192 fp32 values); longer rows are read a second time
+// (from L2).
 #include <type_traits>
 
 #include "sq_device.h"
@@ -99,78 +99,104 @@ __device__ __forceinline__ void emit(const u32x4& v, float r, const float (&g)[E
     }
 }
 
-// VPT > 0: the row is held in VPT vectors per thread (kvec <= 256 * VPT).
-// VPT == 0: the row is streamed twice.
-template <int EB, int VPT, NormOut OUT>
-__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const u32x4* __restrict__ h, int64_t kvec, int64_t k,
-                                                               const float* __restrict__ gamma, float eps,
+// One block of 256 threads takes R consecutive rows. VPT > 0: each row is
+// held in VPT vectors per thread (kvec <= 256 * VPT), all R rows loaded
+// before the reduction so R * VPT 16-byte loads per thread are in flight.
+// VPT == 0 (R = 1): the row is streamed twice.
+template <int EB, int VPT, int R, NormOut OUT>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const u32x4* __restrict__ h, int64_t m, int64_t kvec,
+                                                               int64_t k, const float* __restrict__ gamma, float eps,
                                                                const float* __restrict__ act_scale,
                                                                void* __restrict__ out, float* __restrict__ r_out) {
     constexpr int E = 16 / EB;
-    __shared__ double red[kNormWaves];
+    static_assert(VPT > 0 || R == 1, "streamed rows go one per block");
+    __shared__ double red[R][kNormWaves];
     const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x;
-    const u32x4* hr = h + row * kvec;
+    const int64_t row0 = (int64_t)blockIdx.x * R;
 
-    double ss = 0.0;
-    u32x4 v[VPT > 0 ? VPT : 1];
-    if constexpr (VPT > 0) {
+    double ss[R];
+    u32x4 v[R][VPT > 0 ? VPT : 1];
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int64_t c = tid + (int64_t)i * kNormThreads;
-            v[i] = c < kvec ? __builtin_nontemporal_load(hr + c) : u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < R; ++q) {
+        ss[q] = 0.0;
+        const int64_t row = row0 + q;
+        const u32x4* hr = h + (row < m ? row : 0) * kvec;
+        if constexpr (VPT > 0) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int64_t c = tid + (int64_t)i * kNormThreads;
+                v[q][i] = (row < m && c < kvec) ? __builtin_nontemporal_load(hr + c) : u32x4{0u, 0u, 0u, 0u};
+            }
+        } else {
+            for (int64_t c = tid; c < kvec; c += kNormThreads) ss[q] += sum_sq<E>(hr[c]);
         }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) ss += sum_sq<E>(v[i]);
-    } else {
-        for (int64_t c = tid; c < kvec; c += kNormThreads) ss += sum_sq<E>(hr[c]);
     }
-    ss = wave_sum_f64(ss);
-    if ((tid & 63) == 0) red[tid >> 6] = ss;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        if constexpr (VPT > 0) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) ss[q] += sum_sq<E>(v[q][i]);
+        }
+        ss[q] = wave_sum_f64(ss[q]);
+        if ((tid & 63) == 0) red[q][tid >> 6] = ss[q];
+    }
     __syncthreads();
-    double total = red[0];
-#pragma unroll
-    for (int w = 1; w < kNormWaves; ++w) total += red[w];
-    const float r = (float)(1.0 / sqrt(total / (double)k + (double)eps));
-    if (r_out && tid == 0) r_out[row] = r;
     const float inv_a = OUT == kOutI8 ? __fdiv_rn(1.0f, act_scale[0]) : 0.0f;
-
-    if constexpr (VPT > 0) {
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int64_t c = tid + (int64_t)i * kNormThreads;
-            if (c < kvec) {
+    for (int q = 0; q < R; ++q) {
+        const int64_t row = row0 + q;
+        if (row >= m) break;
+        double total = red[q][0];
+#pragma unroll
+        for (int w = 1; w < kNormWaves; ++w) total += red[q][w];
+        const float r = (float)(1.0 / sqrt(total / (double)k + (double)eps));
+        if (r_out && tid == 0) r_out[row] = r;
+        if constexpr (VPT > 0) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int64_t c = tid + (int64_t)i * kNormThreads;
+                if (c < kvec) {
+                    float g[E];
+                    load_gamma<E>(gamma, c, g);
+                    emit<E, OUT>(v[q][i], r, g, inv_a, out, row * k + c * E);
+                }
+            }
+        } else {
+            const u32x4* hr = h + row * kvec;
+            for (int64_t c = tid; c < kvec; c += kNormThreads) {
                 float g[E];
                 load_gamma<E>(gamma, c, g);
-                emit<E, OUT>(v[i], r, g, inv_a, out, row * k + c * E);
+                emit<E, OUT>(hr[c], r, g, inv_a, out, row * k + c * E);
             }
-        }
-    } else {
-        for (int64_t c = tid; c < kvec; c += kNormThreads) {
-            float g[E];
-            load_gamma<E>(gamma, c, g);
-            emit<E, OUT>(hr[c], r, g, inv_a, out, row * k + c * E);
         }
     }
 }
 
+template <int EB, int VPT, int R, NormOut OUT>
+hipError_t launch_rows(const void* h, int64_t m, int64_t kvec, int64_t k, const float* gamma, float eps,
+                       const float* act_scale, void* out, float* r_out, hipStream_t stream) {
+    rmsnorm_kernel<EB, VPT, R, OUT><<<dim3((unsigned)((m + R - 1) / R)), dim3(kNormThreads), 0, stream>>>(
+        (const u32x4*)h, m, kvec, k, gamma, eps, act_scale, out, r_out);
+    return hipGetLastError();
+}
+
+// rows per block so that about eight 16-byte loads per thread are in flight
 template <int EB, NormOut OUT>
 hipError_t launch_norm(const void* h, int64_t m, int64_t k, const float* gamma, float eps, const float* act_scale,
                        void* out, float* r_out, hipStream_t stream) {
     const int64_t kvec = k * EB / 16;
-    const dim3 grid((unsigned)m), block(kNormThreads);
-    const u32x4* hp = (const u32x4*)h;
-    if (kvec <= 1 * kNormThreads)
-        rmsnorm_kernel<EB, 1, OUT><<<grid, block, 0, stream>>>(hp, kvec, k, gamma, eps, act_scale, out, r_out);
-    else if (kvec <= 2 * kNormThreads)
-        rmsnorm_kernel<EB, 2, OUT><<<grid, block, 0, stream>>>(hp, kvec, k, gamma, eps, act_scale, out, r_out);
-    else if (kvec <= 4 * kNormThreads)
-        rmsnorm_kernel<EB, 4, OUT><<<grid, block, 0, stream>>>(hp, kvec, k, gamma, eps, act_scale, out, r_out);
-    else if (kvec <= 8 * kNormThreads)
-        rmsnorm_kernel<EB, 8, OUT><<<grid, block, 0, stream>>>(hp, kvec, k, gamma, eps, act_scale, out, r_out);
-    else
-        rmsnorm_kernel<EB, 0, OUT><<<grid, block, 0, stream>>>(hp, kvec, k, gamma, eps, act_scale, out, r_out);
-    return hipGetLastError();
+    const int64_t per = (kvec + kNormThreads - 1) / kNormThreads;  // vectors per thread per row
+    switch (per) {
+        case 1: return launch_rows<EB, 1, 8, OUT>(h, m, kvec, k, gamma, eps, act_scale, out, r_out, stream);
+        case 2: return launch_rows<EB, 2, 4, OUT>(h, m, kvec, k, gamma, eps, act_scale, out, r_out, stream);
+        case 3: return launch_rows<EB, 3, 2, OUT>(h, m, kvec, k, gamma, eps, act_scale, out, r_out, stream);
+        case 4: return launch_rows<EB, 4, 2, OUT>(h, m, kvec, k, gamma, eps, act_scale, out, r_out, stream);
+        case 5:
+        case 6: return launch_rows<EB, 6, 1, OUT>(h, m, kvec, k, gamma, eps, act_scale, out, r_out, stream);
+        case 7:
+        case 8: return launch_rows<EB, 8, 1, OUT>(h, m, kvec, k, gamma, eps, act_scale, out, r_out, stream);
+        default: return launch_rows<EB, 0, 1, OUT>(h, m, kvec, k, gamma, eps, act_scale, out, r_out, stream);
+    }
 }
 
 // gamma_folded = fl(gamma * inv_s), one thread per channel

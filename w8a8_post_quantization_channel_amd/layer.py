@@ -13,6 +13,8 @@ supplies the stream; all arithmetic is in libsq.so.
                  Wq, w_scale = per-row int8 of W diag(s)       (sq_quant_weight)
       forward:   Xq = per-tensor int8 of x * (1/s)             (sq_smooth_quant_act)
                  Y  = dequant(Xq Wq^T)                         (sq_w8a8_gemm)
+      forward_dynamic: the same with the per-tensor scale taken from x itself
+                 (sq_dynamic_quant_act; pwwt.cn §2.3 dynamic mode)
 """
 from __future__ import annotations
 
@@ -34,6 +36,8 @@ class W8A8Linear:
         self.act_scale = torch.empty(4, dtype=f32, device=d)  # one value, padded to 16 bytes
         self.wq = torch.empty((self.n, self.k), dtype=torch.int8, device=d)
         self.w_scale = torch.empty(self.n, dtype=f32, device=d)
+        self.live_max = torch.empty(self.k, dtype=f32, device=d)  # dynamic mode: the batch statistic
+        self.dyn_scale = torch.empty(4, dtype=f32, device=d)      # dynamic mode: the batch's scale
         self.out_dtype = out_dtype if out_dtype is not None else torch.bfloat16
         self.xq = torch.empty((max_tokens, self.k), dtype=torch.int8, device=d) if max_tokens else None
         self.y = torch.empty((max_tokens, self.n), dtype=self.out_dtype, device=d) if max_tokens else None
@@ -55,17 +59,30 @@ class W8A8Linear:
         capi.sq_smooth_quant_act(x, self.inv_s, self.act_scale, xq, stream)
         return xq
 
-    def matmul(self, xq, y=None, acc_out=None, stream=None):
+    def quantize_input_dynamic(self, x, xq=None, stream=None):
+        import torch
+        m = x.shape[0]
+        if xq is None:
+            xq = self.xq[:m] if self.xq is not None and self.xq.shape[0] >= m else \
+                torch.empty((m, self.k), dtype=torch.int8, device=x.device)
+        capi.sq_dynamic_quant_act(x, self.inv_s, self.live_max, self.dyn_scale, xq, stream)
+        return xq
+
+    def matmul(self, xq, y=None, acc_out=None, stream=None, act_scale=None):
         import torch
         m = xq.shape[0]
         if y is None:
             y = self.y[:m] if self.y is not None and self.y.shape[0] >= m else \
                 torch.empty((m, self.n), dtype=self.out_dtype, device=xq.device)
-        capi.sq_w8a8_gemm(xq, self.wq, self.act_scale, self.w_scale, y, acc_out, stream)
+        a = self.act_scale if act_scale is None else act_scale
+        capi.sq_w8a8_gemm(xq, self.wq, a, self.w_scale, y, acc_out, stream)
         return y
 
     def forward(self, x, y=None, xq=None, acc_out=None, stream=None):
         return self.matmul(self.quantize_input(x, xq, stream), y, acc_out, stream)
+
+    def forward_dynamic(self, x, y=None, xq=None, acc_out=None, stream=None):
+        return self.matmul(self.quantize_input_dynamic(x, xq, stream), y, acc_out, stream, act_scale=self.dyn_scale)
 
     def step(self, x_calib, x, stream=None):
         self.calibrate(x_calib, False, stream)

@@ -168,6 +168,23 @@ sq_status sq_calib_mean_finalize(const double* sum, int64_t count, int64_t k,
                                  float* act_max, hipStream_t stream);
 
 /*
+ * Percentile statistic [kwkr §3.1: a high percentile such as 99.9% in place of
+ * the absolute maximum, trading the clipped extremes for a tighter range],
+ * as a nearest rank over the rows:
+ *   rank       = min(max(ceil(q * rows), 1), rows)   (q in fp64)
+ *   act_max[j] = the rank-th smallest of |x[t,j]| over t   (exact; q = 1 gives the max)
+ *   x [rows, k] of type xt, 1 <= rows <= INT32_MAX; q finite in [0, 1]
+ *   (SQ_ERR_SHAPE otherwise); workspace: device, at least
+ *   sq_calib_percentile_workspace bytes; act_max [k] fp32 out.
+ * Reads x twice (bf16) or four times (fp32): one pass per 8-bit digit of the
+ * magnitude.
+ */
+sq_status sq_calib_percentile_workspace(sq_dtype xt, int64_t k, size_t* bytes);
+sq_status sq_calib_percentile(const void* x, sq_dtype xt, int64_t rows, int64_t k, double q,
+                              void* workspace, size_t workspace_bytes, float* act_max,
+                              hipStream_t stream);
+
+/*
  * RMSNorm, the norm in front of the projections of a Llama block; its weight
  * is where 1/s can be folded [kwkr §3.2]:
  *   r[t]   = fp32( 1 / sqrt( sum_j h[t,j]^2 / k + eps ) )   (fp64 arithmetic,

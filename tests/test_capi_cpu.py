@@ -249,3 +249,36 @@ def test_norm_validation(lib):
     a = list(base)
     a[2] = 0
     assert h(*a) == OK
+
+
+def test_percentile_validation(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.sq_calib_percentile_workspace(1, 1024, None) == NULL
+    assert lib.sq_calib_percentile_workspace(5, 1024, ctypes.byref(n)) == DTYPE
+    assert lib.sq_calib_percentile_workspace(1, 1000, ctypes.byref(n)) == SHAPE
+    assert lib.sq_calib_percentile_workspace(1, 1024, ctypes.byref(n)) == OK
+    need = n.value
+    assert need >= 2 * 1024 * 256 * 4
+    f4 = ctypes.c_size_t(0)
+    assert lib.sq_calib_percentile_workspace(0, 1024, ctypes.byref(f4)) == OK and f4.value > need
+    f = lib.sq_calib_percentile
+    base = [P(A), 1, 4096, 1024, 0.999, P(A), need, P(A), None]
+    a = list(base)
+    a[0] = None
+    assert f(*a) == NULL
+    for bad in (float("nan"), -0.1, 1.5):
+        a = list(base)
+        a[4] = bad
+        assert f(*a) == SHAPE
+    a = list(base)
+    a[2] = 0
+    assert f(*a) == SHAPE
+    a = list(base)
+    a[6] = need - 1
+    assert f(*a) == WORKSPACE
+    a = list(base)
+    a[5] = None
+    assert f(*a) == WORKSPACE
+    a = list(base)
+    a[7] = P(MIS)
+    assert f(*a) == ALIGN

@@ -194,3 +194,42 @@ def test_rmsnorm_quant_act_empty_and_no_r():
     got = _host(xq)
     # with r unchecked, rows whose r differs by one ulp may differ by one code step
     assert np.abs(got.astype(np.int32) - ref.astype(np.int32)).max() <= 1
+
+
+# ---- nearest-rank percentile -----------------------------------------------------------
+
+@pytest.mark.parametrize("rows,k,bf16,qs", [
+    (1000, 320, True, (0.999, 0.5, 0.9995, 1.0, 0.0)),
+    (777, 64, False, (0.999, 0.25, 1.0)),
+    (65536, 1024, True, (0.999,)),
+    (4099, 128, False, (0.9, 0.999)),
+])
+def test_percentile(rows, k, bf16, qs):
+    import torch
+    x = _x(600 + rows, rows, k, bf16)
+    tx = _t(x)
+    ws = torch.empty(capi.sq_calib_percentile_workspace(k, capi.SQ_BF16 if bf16 else capi.SQ_F32),
+                     dtype=torch.uint8, device=dev())
+    out = torch.empty(k, dtype=torch.float32, device=dev())
+    for q in qs:
+        capi.sq_calib_percentile(tx, q, ws, out)
+        torch.cuda.synchronize()
+        assert_bitexact(f"percentile q={q}", _host(out), ORACLE.calib_percentile(x, q))
+
+
+def test_percentile_ties_and_signs():
+    import torch
+    g = synth.rng(620)
+    rows, k = 3000, 64
+    # few distinct magnitudes with both signs, zeros and negative zeros: ties everywhere
+    x = (g.integers(-3, 4, (rows, k)) * 0.5).astype(np.float32)
+    x[g.random((rows, k)) < 0.05] = -0.0
+    x[7, :] = -1000.0
+    xb = synth.to_bf16_bits(x)
+    ws = torch.empty(capi.sq_calib_percentile_workspace(k, capi.SQ_F32), dtype=torch.uint8, device=dev())
+    out = torch.empty(k, dtype=torch.float32, device=dev())
+    for arr in (x, xb):
+        for q in (0.999, 0.9996, 0.5, 1.0, 1.0 / rows):
+            capi.sq_calib_percentile(_t(arr), q, ws, out)
+            torch.cuda.synchronize()
+            assert_bitexact(f"ties q={q}", _host(out), ORACLE.calib_percentile(arr, q))

@@ -54,6 +54,8 @@ def _declare(lib):
         "sq_dynamic_quant_act": [P, c.c_int, i64, i64, P, P, P, P, P],
         "sq_calib_sample_max_sum": [P, c.c_int, i64, i64, i64, P, P, P],
         "sq_calib_mean_finalize": [P, i64, i64, P, P],
+        "sq_calib_percentile_workspace": [c.c_int, i64, P],
+        "sq_calib_percentile": [P, c.c_int, i64, i64, c.c_double, P, c.c_size_t, P, P],
         "sq_rmsnorm": [P, c.c_int, i64, i64, P, c.c_float, P, c.c_int, P, P],
         "sq_fold_norm_weight": [P, P, i64, P, P],
         "sq_rmsnorm_quant_act": [P, c.c_int, i64, i64, P, c.c_float, P, P, P, P],
@@ -230,3 +232,18 @@ def sq_rmsnorm_quant_act(h, gamma_folded, eps: float, act_scale, xq, r_out=None,
                                                                _dev(gamma_folded, "gamma_folded"), float(eps),
                                                                _dev(act_scale, "act_scale"), _dev(xq, "xq"),
                                                                _opt(r_out, "r_out"), _stream(stream)))
+
+
+def sq_calib_percentile_workspace(k: int, dtype_code: int = SQ_BF16) -> int:
+    out = ctypes.c_size_t(0)
+    _check("sq_calib_percentile_workspace", load().sq_calib_percentile_workspace(dtype_code, k, ctypes.byref(out)))
+    return out.value
+
+
+def sq_calib_percentile(x, q: float, workspace, act_max, stream=None):
+    """act_max[j] = nearest-rank q-quantile of |x[:, j]|."""
+    rows, k = x.shape
+    _check("sq_calib_percentile", load().sq_calib_percentile(_dev(x, "x"), _dtype_code(x), rows, k, float(q),
+                                                             _dev(workspace, "workspace"),
+                                                             workspace.numel() * workspace.element_size(),
+                                                             _dev(act_max, "act_max"), _stream(stream)))

@@ -270,3 +270,164 @@ hipError_t smooth_factors(const float* act_max, const float* w_max, int64_t k, f
 }
 
 }  // namespace sqk
+
+// ---- nearest-rank percentile of |x| per channel (kwkr.cn blog §3.1) -----------
+//
+// Radix selection on the magnitude bit patterns (finite IEEE values order like
+// their bits with the sign cleared): 15-bit keys for bf16, 31-bit for fp32,
+// taken 8 bits at a time from the top (bf16: 8 + 7, fp32: 8 + 8 + 8 + 7). A
+// pass histograms the next digit of every key whose higher digits equal the
+// prefix selected so far, then one thread per channel walks its histogram to
+// the bucket holding the remaining rank. All counts are integers, so the
+// result is exact and independent of the launch shape.
+namespace {
+
+constexpr int kPctThreads = 1024;  // 16 waves over interleaved rows
+constexpr int kPctChannels = 64;   // one channel per lane
+constexpr int kPctBins = 256;
+constexpr int kPctStride = kPctBins + 1;  // LDS row stride: lane l's bin d sits in bank (l + d) % 64
+constexpr int kPctUnroll = 8;
+
+template <int EB>
+struct PctKey {
+    static constexpr int BITS = EB == 2 ? 15 : 31;
+    static constexpr int PASSES = (BITS + 7) / 8;
+    // bit position of the lowest bit of digit `pass` and its width
+    __host__ __device__ static constexpr int lo(int pass) { return BITS - 8 * (pass + 1) > 0 ? BITS - 8 * (pass + 1) : 0; }
+    __host__ __device__ static constexpr int width(int pass) { return (BITS - 8 * pass) - lo(pass); }
+};
+
+template <int EB>
+__device__ __forceinline__ uint32_t mag_key(const void* x, int64_t idx) {
+    if constexpr (EB == 2)
+        return (uint32_t)__builtin_nontemporal_load((const uint16_t*)x + idx) & 0x7fffu;
+    else
+        return __builtin_nontemporal_load((const uint32_t*)x + idx) & 0x7fffffffu;
+}
+
+template <int EB, int PASS>
+__global__ __launch_bounds__(kPctThreads) void pct_hist_kernel(const void* __restrict__ x, int64_t rows, int64_t k,
+                                                               int64_t rows_per_block,
+                                                               const uint32_t* __restrict__ prefix,
+                                                               uint32_t* __restrict__ hist) {
+    using K = PctKey<EB>;
+    constexpr int LO = K::lo(PASS), HI = LO + K::width(PASS);
+    constexpr uint32_t DMASK = (1u << K::width(PASS)) - 1u;
+    __shared__ uint32_t h[kPctChannels * kPctStride];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < kPctChannels * kPctStride; i += kPctThreads) h[i] = 0u;
+    __syncthreads();
+    const int64_t c = (int64_t)blockIdx.x * kPctChannels + lane;  // k is a multiple of 64
+    const uint32_t pre = PASS > 0 ? prefix[c] : 0u;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+    const int64_t r1 = min(rows, r0 + rows_per_block);
+    constexpr int W = kPctThreads / 64;
+    auto count = [&](uint32_t key) {
+        if (PASS == 0 || (key >> HI) == pre) atomicAdd(&h[lane * kPctStride + ((key >> LO) & DMASK)], 1u);
+    };
+    int64_t r = r0 + wave;
+    for (; r + W * (kPctUnroll - 1) < r1; r += W * kPctUnroll) {
+        uint32_t key[kPctUnroll];
+#pragma unroll
+        for (int u = 0; u < kPctUnroll; ++u) key[u] = mag_key<EB>(x, (r + W * u) * k + c);
+#pragma unroll
+        for (int u = 0; u < kPctUnroll; ++u) count(key[u]);
+    }
+    for (; r < r1; r += W) count(mag_key<EB>(x, r * k + c));
+    __syncthreads();
+    // merge: thread t takes 16 consecutive bins of channel t / 16
+    const int ch = tid >> 4, b0 = (tid & 15) * 16;
+    uint32_t* g = hist + ((int64_t)blockIdx.x * kPctChannels + ch) * kPctBins;
+#pragma unroll
+    for (int b = b0; b < b0 + 16; ++b) {
+        const uint32_t v = h[ch * kPctStride + b];
+        if (v) atomicAdd(g + b, v);
+    }
+}
+
+// One thread per channel: the bucket of this pass's digit that holds the
+// remaining rank (1-based, counted from the smallest key).
+template <int EB, int PASS>
+__global__ __launch_bounds__(256) void pct_select_kernel(const uint32_t* __restrict__ hist, int64_t k,
+                                                         uint32_t rank0, uint32_t* __restrict__ prefix,
+                                                         uint32_t* __restrict__ rank, float* __restrict__ act_max) {
+    using K = PctKey<EB>;
+    constexpr int NB = 1 << K::width(PASS);
+    constexpr bool LAST = PASS == K::PASSES - 1;
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= k) return;
+    uint32_t r = PASS == 0 ? rank0 : rank[c];
+    const uint32_t* hc = hist + c * kPctBins;
+    uint32_t cum = 0;
+    int d = 0;
+    for (; d < NB - 1; ++d) {
+        const uint32_t n = hc[d];
+        if (cum + n >= r) break;
+        cum += n;
+    }
+    r -= cum;
+    const uint32_t pre = ((PASS == 0 ? 0u : prefix[c]) << K::width(PASS)) | (uint32_t)d;
+    if constexpr (LAST) {
+        act_max[c] = __uint_as_float(EB == 2 ? pre << 16 : pre);
+    } else {
+        prefix[c] = pre;
+        rank[c] = r;
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+template <int EB, int PASS>
+hipError_t pct_pass(const void* x, int64_t rows, int64_t k, uint32_t rank0, uint32_t* hist, uint32_t* prefix,
+                    uint32_t* rank, float* act_max, hipStream_t stream) {
+    const int64_t strips = k / kPctChannels;
+    // about ten blocks per compute unit, at least 1024 rows per block
+    int64_t chunks = std::max<int64_t>(1, 2560 / strips);
+    int64_t rpb = std::max<int64_t>(1024, (rows + chunks - 1) / chunks);
+    chunks = std::min<int64_t>(65535, (rows + rpb - 1) / rpb);
+    rpb = (rows + chunks - 1) / chunks;
+    uint32_t* hp = hist + (int64_t)PASS * k * kPctBins;
+    pct_hist_kernel<EB, PASS><<<dim3((unsigned)strips, (unsigned)chunks), dim3(kPctThreads), 0, stream>>>(
+        x, rows, k, rpb, prefix, hp);
+    pct_select_kernel<EB, PASS><<<dim3((unsigned)((k + 255) / 256)), dim3(256), 0, stream>>>(hp, k, rank0, prefix,
+                                                                                          rank, act_max);
+    return hipGetLastError();
+}
+
+template <int EB>
+hipError_t percentile_t(const void* x, int64_t rows, int64_t k, uint32_t rank0, uint32_t* hist, uint32_t* prefix,
+                        uint32_t* rank, float* act_max, hipStream_t stream) {
+    const int64_t words = (int64_t)PctKey<EB>::PASSES * k * kPctBins;
+    fill_zero_u32_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream>>>(hist, words);
+    pct_pass<EB, 0>(x, rows, k, rank0, hist, prefix, rank, act_max, stream);
+    pct_pass<EB, 1>(x, rows, k, rank0, hist, prefix, rank, act_max, stream);
+    if constexpr (PctKey<EB>::PASSES > 2) {
+        pct_pass<EB, 2>(x, rows, k, rank0, hist, prefix, rank, act_max, stream);
+        pct_pass<EB, 3>(x, rows, k, rank0, hist, prefix, rank, act_max, stream);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+namespace sqk {
+
+size_t percentile_workspace(int xt, int64_t k) {
+    const int passes = xt == kBF16 ? PctKey<2>::PASSES : PctKey<4>::PASSES;
+    return (size_t)passes * (size_t)k * kPctBins * 4 + 2 * (size_t)k * 4;
+}
+
+hipError_t percentile(const void* x, int xt, int64_t rows, int64_t k, int64_t rank, void* workspace,
+                      float* act_max, hipStream_t stream) {
+    const int passes = xt == kBF16 ? PctKey<2>::PASSES : PctKey<4>::PASSES;
+    uint32_t* hist = (uint32_t*)workspace;
+    uint32_t* prefix = hist + (int64_t)passes * k * kPctBins;
+    uint32_t* rnk = prefix + k;
+    if (xt == kBF16) return percentile_t<2>(x, rows, k, (uint32_t)rank, hist, prefix, rnk, act_max, stream);
+    return percentile_t<4>(x, rows, k, (uint32_t)rank, hist, prefix, rnk, act_max, stream);
+}
+
+}  // namespace sqk

@@ -166,6 +166,26 @@ sq_status sq_calib_mean_finalize(const double* sum, int64_t count, int64_t k, fl
     return hip_status(sqk::mean_finalize(sum, count, k, act_max, stream));
 }
 
+sq_status sq_calib_percentile_workspace(sq_dtype xt, int64_t k, size_t* bytes) {
+    if (!bytes) return SQ_ERR_NULL;
+    if (!valid_dtype(xt)) return SQ_ERR_DTYPE;
+    if (!valid_k(k)) return SQ_ERR_SHAPE;
+    *bytes = sqk::percentile_workspace(xt, k);
+    return SQ_OK;
+}
+
+sq_status sq_calib_percentile(const void* x, sq_dtype xt, int64_t rows, int64_t k, double q, void* workspace,
+                              size_t workspace_bytes, float* act_max, hipStream_t stream) {
+    if (!x || !act_max) return SQ_ERR_NULL;
+    if (!valid_dtype(xt)) return SQ_ERR_DTYPE;
+    if (rows < 1 || rows > INT32_MAX || !valid_k(k) || !std::isfinite(q) || q < 0.0 || q > 1.0) return SQ_ERR_SHAPE;
+    if (!workspace || workspace_bytes < sqk::percentile_workspace(xt, k)) return SQ_ERR_WORKSPACE;
+    if (!aligned16(x) || !aligned16(act_max) || !aligned16(workspace)) return SQ_ERR_ALIGN;
+    int64_t rank = (int64_t)std::ceil(q * (double)rows);
+    rank = rank < 1 ? 1 : (rank > rows ? rows : rank);
+    return hip_status(sqk::percentile(x, xt, rows, k, rank, workspace, act_max, stream));
+}
+
 static bool valid_eps(float eps) { return std::isfinite(eps) && eps >= 0.0f; }
 
 sq_status sq_rmsnorm(const void* h, sq_dtype ht, int64_t m, int64_t k, const float* gamma, float eps, void* y,

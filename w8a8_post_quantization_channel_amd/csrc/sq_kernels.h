@@ -31,6 +31,11 @@ hipError_t sum_samples(const float* sample_max, int64_t samples, int64_t k, doub
 // act_max[j] = fp32(sum[j] / count)
 hipError_t mean_finalize(const double* sum, int64_t count, int64_t k, float* act_max, hipStream_t stream);
 
+// nearest-rank percentile of |x[:, j]|: the rank-th smallest magnitude (1-based)
+size_t percentile_workspace(int xt, int64_t k);
+hipError_t percentile(const void* x, int xt, int64_t rows, int64_t k, int64_t rank, void* workspace,
+                      float* act_max, hipStream_t stream);
+
 // RMSNorm y = fl(fl(h * r) * gamma) (fp32 or bf16 out), r per row (optional out)
 hipError_t rmsnorm(const void* h, int ht, int64_t m, int64_t k, const float* gamma, float eps, void* y, int yt,
                    float* r_out, hipStream_t stream);

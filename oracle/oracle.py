@@ -64,6 +64,15 @@ def _declare(lib):
     lib.sqo_rmsnorm_apply.argtypes = [P, c.c_int, i64, i64, P, P, c.c_int, P]
     lib.sqo_fold_norm_weight.argtypes = [P, P, i64, P]
     lib.sqo_norm_quant_apply.argtypes = [P, c.c_int, i64, i64, P, P, c.c_float, P]
+    lib.sqo_e4m3_encode.argtypes = [c.c_float]
+    lib.sqo_e4m3_encode.restype = c.c_uint8
+    lib.sqo_e4m3_decode.argtypes = [c.c_uint8]
+    lib.sqo_e4m3_decode.restype = c.c_float
+    lib.sqo_quant_weight_fp8.argtypes = [P, c.c_int, i64, i64, P, P, P]
+    lib.sqo_act_scale_fp8.argtypes = [P, P, i64]
+    lib.sqo_act_scale_fp8.restype = c.c_float
+    lib.sqo_quant_act_fp8.argtypes = [P, c.c_int, i64, i64, P, c.c_float, P]
+    lib.sqo_gemm_fp8.argtypes = [P, P, i64, i64, i64, c.c_float, P, c.c_int, P, P, P]
     return lib
 
 
@@ -243,6 +252,45 @@ class Oracle:
     def rmsnorm_quant_act(self, h: np.ndarray, gamma_folded: np.ndarray, eps: float, act_scale):
         r = self.rms_inv(h, eps)
         return self.norm_quant_apply(h, r, gamma_folded, act_scale), r
+
+    # O19
+    def e4m3_encode(self, v) -> np.ndarray:
+        v = np.asarray(v, np.float32)
+        return np.array([self.lib.sqo_e4m3_encode(float(x)) for x in v.ravel()], np.uint8).reshape(v.shape)
+
+    def e4m3_decode(self, b) -> np.ndarray:
+        b = np.asarray(b, np.uint8)
+        return np.array([self.lib.sqo_e4m3_decode(int(x)) for x in b.ravel()], np.float32).reshape(b.shape)
+
+    # O20
+    def quant_weight_fp8(self, w: np.ndarray, s: np.ndarray):
+        n, k = w.shape
+        wq = np.empty((n, k), np.uint8)
+        ws = np.empty(n, np.float32)
+        self.lib.sqo_quant_weight_fp8(_ptr(w), _ftype(w), n, k, _ptr(s), _ptr(wq), _ptr(ws))
+        return wq, ws
+
+    # O21
+    def act_scale_fp8(self, act_max: np.ndarray, inv_s: np.ndarray) -> np.float32:
+        return np.float32(self.lib.sqo_act_scale_fp8(_ptr(act_max), _ptr(inv_s), act_max.shape[0]))
+
+    # O22
+    def quant_act_fp8(self, x: np.ndarray, inv_s: np.ndarray, act_scale) -> np.ndarray:
+        m, k = x.shape
+        xq = np.empty((m, k), np.uint8)
+        self.lib.sqo_quant_act_fp8(_ptr(x), _ftype(x), m, k, _ptr(inv_s), float(np.float32(act_scale)), _ptr(xq))
+        return xq
+
+    # O23
+    def gemm_fp8(self, xq: np.ndarray, wq: np.ndarray, act_scale, w_scale: np.ndarray, bf16: bool = False):
+        m, k = xq.shape
+        n = wq.shape[0]
+        y = np.empty((m, n), np.uint16 if bf16 else np.float32)
+        acc = np.empty((m, n), np.float64)
+        absacc = np.empty((m, n), np.float64)
+        self.lib.sqo_gemm_fp8(_ptr(xq), _ptr(wq), m, n, k, float(np.float32(act_scale)), _ptr(w_scale),
+                              BF16 if bf16 else F32, _ptr(y), _ptr(acc), _ptr(absacc))
+        return y, acc, absacc
 
     # the whole layer, O1..O10, for one runtime input (helper for tests)
     def layer_forward(self, x_calib_batches, w: np.ndarray, x: np.ndarray, alpha: float, bf16_out: bool = False):

@@ -363,3 +363,113 @@ void sqo_norm_quant_apply(const void* h, int htype, int64_t m, int64_t k,
         }
     }
 }
+
+/* O19: OCP FP8 E4M3 -- the 8-bit floating-point target that smoothing also
+ * serves (aiunderstanding.org, the section on where SmoothQuant goes next).
+ * Normal values (1 + m/8) * 2^(E-7), E = 1..15 (E = 15, m = 7 is NaN);
+ * subnormals m * 2^-9. */
+uint8_t sqo_e4m3_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    float a = fabsf(v);
+    if (a == 0.0f) return sign;
+    int e;
+    frexpf(a, &e);               /* a = f * 2^e with f in [0.5, 1) */
+    int E = e - 1;               /* a in [2^E, 2^(E+1)) */
+    if (E < -6) {                /* below the smallest normal: steps of 2^-9 */
+        float q = rintf(ldexpf(a, 9));
+        return sign | (uint8_t)q; /* q = 8 is the smallest normal, 0x08 */
+    }
+    float q = rintf(ldexpf(a, 3 - E)); /* 8 .. 16: the significand in eighths */
+    if (q == 16.0f) {
+        q = 8.0f;
+        E += 1;
+    }
+    if (E > 8 || (E == 8 && q > 14.0f)) return sign | 0x7e; /* past 448: saturate */
+    return sign | (uint8_t)(((E + 7) << 3) | ((int)q - 8));
+}
+
+float sqo_e4m3_decode(uint8_t b) {
+    int ef = (b >> 3) & 0xf, m = b & 7;
+    float mag;
+    if ((b & 0x7f) == 0x7f) return NAN;
+    if (ef == 0)
+        mag = ldexpf((float)m, -9);
+    else
+        mag = ldexpf(1.0f + (float)m / 8.0f, ef - 7);
+    return (b & 0x80) ? -mag : mag;
+}
+
+#define SQO_FP8_MAX 448.0f
+
+/* O20: O7 with the e4m3 grid in place of the integer one. */
+void sqo_quant_weight_fp8(const void* w, int wtype, int64_t n, int64_t k,
+                          const float* s, uint8_t* wq, float* w_scale) {
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < n; ++r) {
+        float* row = (float*)malloc((size_t)k * sizeof(float));
+        float mx = 0.0f;
+        for (int64_t j = 0; j < k; ++j) {
+            row[j] = s[j] * elem(w, wtype, r * k + j);
+            float v = fabsf(row[j]);
+            if (v > mx) mx = v;
+        }
+        mx = mx < SQO_FLOOR ? SQO_FLOOR : mx;
+        float ws = mx / SQO_FP8_MAX;
+        float inv_ws = 1.0f / ws;
+        for (int64_t j = 0; j < k; ++j) wq[r * k + j] = sqo_e4m3_encode(row[j] * inv_ws);
+        w_scale[r] = ws;
+        free(row);
+    }
+}
+
+/* O21: O6 with the e4m3 range. */
+float sqo_act_scale_fp8(const float* act_max, const float* inv_s, int64_t k) {
+    float mx = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+        float a = act_max[j] > SQO_FLOOR ? act_max[j] : SQO_FLOOR;
+        float v = inv_s[j] * a;
+        if (v > mx) mx = v;
+    }
+    return mx / SQO_FP8_MAX;
+}
+
+/* O22: O8 with the e4m3 grid: scale by 1/s first, then by 1/a, then encode. */
+void sqo_quant_act_fp8(const void* x, int xtype, int64_t m, int64_t k,
+                       const float* inv_s, float act_scale, uint8_t* xq) {
+    float inv_a = 1.0f / act_scale;
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < m; ++r) {
+        for (int64_t j = 0; j < k; ++j) {
+            float smoothed = inv_s[j] * elem(x, xtype, r * k + j);
+            xq[r * k + j] = sqo_e4m3_encode(smoothed * inv_a);
+        }
+    }
+}
+
+/* O23: the FP8 product: exact fp64 sums of the decoded codes, then the
+ * merged-scale dequantization of O10. */
+void sqo_gemm_fp8(const uint8_t* xq, const uint8_t* wq, int64_t m, int64_t n,
+                  int64_t k, float act_scale, const float* w_scale, int ytype,
+                  void* y, double* acc, double* absacc) {
+    int64_t idx;
+#pragma omp parallel for schedule(static)
+    for (idx = 0; idx < m * n; ++idx) {
+        int64_t r = idx / n, c = idx % n;
+        double sum = 0.0, asum = 0.0;
+        for (int64_t j = 0; j < k; ++j) {
+            double p = (double)sqo_e4m3_decode(xq[r * k + j]) * (double)sqo_e4m3_decode(wq[c * k + j]);
+            sum += p;
+            asum += fabs(p);
+        }
+        float scale = w_scale[c] * act_scale;
+        float v = (float)sum * scale;
+        if (ytype == SQO_BF16)
+            ((uint16_t*)y)[idx] = float_to_bf16_rne(v);
+        else
+            ((float*)y)[idx] = v;
+        if (acc) acc[idx] = sum;
+        if (absacc) absacc[idx] = asum;
+    }
+}

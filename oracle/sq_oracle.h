@@ -22,6 +22,9 @@
  *   - robust calibration:          kwkr.cn blog §3.1 (percentile, mean of maxima)
  *   - 1/s folded into the norm:    kwkr.cn blog §2.3 and §3.2 (gamma of the
  *                                  preceding norm absorbs 1/s)
+ *   - FP8 after smoothing:         aiunderstanding.org, "SmoothQuant 和激活量化"
+ *                                  (the section on where smoothing goes next:
+ *                                  INT8 and FP8 serving)
  *
  * Conventions: X[m,k] and W[n,k] are row-major with k contiguous; column j is
  * input channel j. Every floating-point step is one IEEE fp32 operation with
@@ -132,6 +135,33 @@ void sqo_fold_norm_weight(const float* gamma, const float* inv_s, int64_t k,
 void sqo_norm_quant_apply(const void* h, int htype, int64_t m, int64_t k,
                           const float* r, const float* gamma_folded,
                           float act_scale, int8_t* xq);
+
+/* O19: OCP FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * no infinities, largest finite 448): round-to-nearest-even encoding of a
+ * finite fp32 value; magnitudes that would round past 448 saturate to 448.
+ * Decoding is exact. */
+uint8_t sqo_e4m3_encode(float v);
+float sqo_e4m3_decode(uint8_t b);
+
+/* O20: the FP8 variant of O7: W' = W*diag(s); w_scale[r] = fl(max(max_j
+ * |W'[r,j]|, 1e-5) / 448); wq[r,j] = e4m3(fl(W'[r,j] * fl(1/w_scale[r]))). */
+void sqo_quant_weight_fp8(const void* w, int wtype, int64_t n, int64_t k,
+                          const float* s, uint8_t* wq, float* w_scale);
+
+/* O21: the FP8 variant of O6: fl(max_j fl(max(act_max[j],1e-5)*inv_s[j]) / 448). */
+float sqo_act_scale_fp8(const float* act_max, const float* inv_s, int64_t k);
+
+/* O22: the FP8 variant of O8: xq = e4m3(fl(fl(x*inv_s[j]) * fl(1/act_scale))). */
+void sqo_quant_act_fp8(const void* x, int xtype, int64_t m, int64_t k,
+                       const float* inv_s, float act_scale, uint8_t* xq);
+
+/* O23: acc[r,c] = sum_j decode(xq[r,j]) * decode(wq[c,j]) in fp64 (exact for
+ * k below 2^16: each product has at most 8 significant bits and lies in
+ * [2^-18, 2^18)); then y = fl(fl(acc) * fl(act_scale * w_scale[c])), fp32 or
+ * bf16 (RNE), and the fp64 sums of |products| (for error bounds) in absacc. */
+void sqo_gemm_fp8(const uint8_t* xq, const uint8_t* wq, int64_t m, int64_t n,
+                  int64_t k, float act_scale, const float* w_scale, int ytype,
+                  void* y, double* acc, double* absacc);
 
 #ifdef __cplusplus
 }

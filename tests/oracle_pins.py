@@ -483,4 +483,62 @@ def pin_norm_fold(o):
     assert np.abs(d).max() <= 1 and (d != 0).mean() < 0.01
 
 
+# ---- O19 - O23: the FP8 (E4M3) variant ---------------------------------------------
+
+def pin_e4m3(o):
+    """OCP FP8 E4M3 encode and decode against torch's float8_e4m3fn on every
+    code, on the midpoints between neighbouring codes (ties to even), on
+    subnormals and signed zeros; past 448 the encoder saturates (reading)."""
+    import torch
+    codes = np.array([b for b in range(256) if (b & 0x7f) != 0x7f], np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(o.e4m3_decode(codes).view(np.uint32), ref.view(np.uint32))
+    pos = np.sort(ref[ref > 0]).astype(np.float64)
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    g = synth.rng(47)
+    vals = np.concatenate([mids, -mids, g.uniform(-448, 448, 1500).astype(np.float32),
+                           g.uniform(-0.02, 0.02, 400).astype(np.float32),
+                           np.array([0.0, -0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11, 464.0],
+                                    np.float32)])
+    expect = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(o.e4m3_encode(vals), expect)
+    assert np.array_equal(o.e4m3_encode(np.array([465.0, 1e4, -600.0], np.float32)),
+                          np.array([0x7E, 0x7E, 0xFE], np.uint8))
+
+
+def pin_fp8_layer(o):
+    """The FP8 variant of the layer: each weight row's largest element lands
+    on +-448, every element within half a step of W diag(s); the activation
+    scale is the closed form over 448; the product of the codes is numpy's
+    fp64 matmul of the decoded values (exact here); the smoothed FP8 layer
+    tracks XW."""
+    g = synth.rng(48)
+    m, n, k = 24, 40, 256
+    x = g.standard_normal((m, k)).astype(np.float32)
+    x[:, 17] *= 60
+    w = (g.standard_normal((n, k)) * np.linspace(0.01, 1.0, n)[:, None]).astype(np.float32)
+    act_max, w_max = o.calib_absmax(x), o.calib_absmax(w)
+    s, inv_s, _ = o.smooth_factors(act_max, w_max, 0.5)
+    wq, ws = o.quant_weight_fp8(w, s)
+    wd = o.e4m3_decode(wq).astype(np.float64)
+    assert np.all(np.abs(wd).max(axis=1) == 448.0)
+    wp = w.astype(np.float64) * s.astype(np.float64)
+    err = np.abs(wd * ws[:, None].astype(np.float64) - wp)
+    bound = np.maximum(np.abs(wp) * 2.0 ** -4, 2.0 ** -10 * ws[:, None].astype(np.float64))
+    assert np.all(err <= bound * (1 + 1e-6))
+    a = o.act_scale_fp8(act_max, inv_s)
+    expect_a = (act_max.astype(np.float64) / s.astype(np.float64)).max() / 448.0
+    assert abs(float(a) / expect_a - 1.0) <= 3e-7
+    xq = o.quant_act_fp8(x, inv_s, a)
+    xd = o.e4m3_decode(xq).astype(np.float64)
+    assert np.abs(xd).max() == 448.0
+    y, acc, absacc = o.gemm_fp8(xq, wq, a, ws)
+    assert np.array_equal(acc, xd @ wd.T)
+    assert np.array_equal(absacc, np.abs(xd) @ np.abs(wd).T)
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    assert rel_mse(y, exact) < 1e-3
+    approx = acc * float(a) * ws[None, :].astype(np.float64)
+    assert np.all(np.abs(y.astype(np.float64) - approx) <= 2 * 2.0 ** -23 * np.abs(approx) + 1e-30)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

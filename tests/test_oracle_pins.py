@@ -65,6 +65,14 @@ MUTANTS = {
     "fold_multiplies_s": ("gamma_folded[j] = gamma[j] * inv_s[j];", "gamma_folded[j] = gamma[j] / inv_s[j];"),
     "norm_quant_drops_gamma": ("float smoothed = (elem(h, htype, t * k + j) * r[t]) * gamma_folded[j];",
                                "float smoothed = elem(h, htype, t * k + j) * r[t]; (void)gamma_folded;"),
+    "e4m3_truncates": ("float q = rintf(ldexpf(a, 3 - E));", "float q = truncf(ldexpf(a, 3 - E));"),
+    "e4m3_bias_8": ("return sign | (uint8_t)(((E + 7) << 3) | ((int)q - 8));",
+                    "return sign | (uint8_t)(((E + 8) << 3) | ((int)q - 8));"),
+    "e4m3_subnormal_step": ("float q = rintf(ldexpf(a, 9));", "float q = rintf(ldexpf(a, 10));"),
+    "fp8_weight_scale_127": ("float ws = mx / SQO_FP8_MAX;", "float ws = mx / 127.0f;"),
+    "fp8_act_scale_ignores_s": ("float v = inv_s[j] * a;", "float v = a;"),
+    "fp8_gemm_drops_sign": ("double p = (double)sqo_e4m3_decode(xq[r * k + j]) * (double)sqo_e4m3_decode(wq[c * k + j]);",
+                            "double p = fabs((double)sqo_e4m3_decode(xq[r * k + j])) * (double)sqo_e4m3_decode(wq[c * k + j]);"),
     "norm_quant_drops_r": ("float smoothed = (elem(h, htype, t * k + j) * r[t]) * gamma_folded[j];",
                            "float smoothed = elem(h, htype, t * k + j) * gamma_folded[j];"),
 }

@@ -57,7 +57,7 @@ def parse():
                          "profiles/gemm_traffic__llama13b_prefill2048.md, used only if it matches gemm.hip)")
     ap.add_argument("--workload", default="layer13b",
                     choices=["layer13b", "decode7b", "alpha_search", "prefill70b", "hbm_passes", "copy_probe",
-                             "variants"],
+                             "variants", "fp8"],
                     help="layer13b (default, the headline line); the others measure the remaining "
                          "workloads, one JSON line each")
     return ap.parse_args()
@@ -503,6 +503,61 @@ def workload_variants(device):
             "per_row": out}
 
 
+def workload_fp8(device):
+    """The FP8 (OCP E4M3) variant on the 13B layer (2048 tokens, 7 projections):
+    the whole step with e4m3 codes (statistics, smoothing, FP8 weight and
+    activation quantization, FP8 GEMM) and each projection's FP8 GEMM beside
+    the int8 GEMM on the same shape (both dense 5.0 P/s peaks on MI355X)."""
+    import torch
+    from w8a8_post_quantization_channel_amd import capi
+    groups, projs = setup(device)
+    for _ in range(2):
+        run_step(groups, projs)
+    torch.cuda.synchronize()
+    m = next(iter(groups.values())).x.shape[0]
+    f8 = []
+    for name, g, layer, _ in projs:
+        a8 = torch.empty(4, dtype=torch.float32, device=device)
+        wq8 = torch.empty((layer.n, layer.k), dtype=torch.uint8, device=device)
+        ws8 = torch.empty(layer.n, dtype=torch.float32, device=device)
+        xq8 = torch.empty((m, layer.k), dtype=torch.uint8, device=device)
+        f8.append((name, g, layer, a8, wq8, ws8, xq8))
+
+    def fp8_step():
+        for g in groups.values():
+            capi.sq_calib_absmax(g.x, g.act_max, False)
+        for name, g, layer, a8, wq8, ws8, xq8 in f8:
+            capi.sq_calib_absmax(layer.w, layer.w_max, False)
+            capi.sq_smooth_factors(layer.act_max, layer.w_max, layer.alpha, layer.s, layer.inv_s, layer.act_scale)
+            capi.sq_act_scale_fp8(layer.act_max, layer.inv_s, a8)
+            capi.sq_quant_weight_fp8(layer.w, layer.s, wq8, ws8)
+            capi.sq_smooth_quant_act_fp8(g.x, layer.inv_s, a8, xq8)
+            capi.sq_fp8_gemm(xq8, wq8, a8, ws8, layer.y[:m])
+
+    fp8_step()
+    torch.cuda.synchronize()
+    step8_ms = timed(fp8_step, 50)
+    step_i8_ms = timed(lambda: run_step(groups, projs), 50)
+    per = {}
+    ops_total = 0.0
+    for name, g, layer, a8, wq8, ws8, xq8 in f8:
+        ops = 2.0 * m * layer.n * layer.k
+        ops_total += ops
+        xq = layer.quantize_input(g.x)
+        t8 = timed(lambda: capi.sq_fp8_gemm(xq8, wq8, a8, ws8, layer.y[:m]), 50)
+        ti8 = timed(lambda: layer.matmul(xq), 50)
+        per[name] = {"fp8_gemm_tops": ops / (t8 * 1e-3) / 1e12, "int8_gemm_tops": ops / (ti8 * 1e-3) / 1e12,
+                     "shape": [m, layer.n, layer.k]}
+    gemm8 = sum(2.0 * m * l.n * l.k / (per[n]["fp8_gemm_tops"] * 1e12) for n, _, l, *_ in f8)
+    return {"metric": "W8A8 FP8 (E4M3) step TOPS at 13B shapes", "value": ops_total / (step8_ms * 1e-3) / 1e12,
+            "unit": "TOPS", "n_gpus": 1, "higher_is_better": True, "dtype": "fp8_e4m3", "data": "synthetic",
+            "config": {"workload": "llama2-13b decoder layer, 7 projections, 2048 prefill tokens, FP8 E4M3 codes"},
+            "step_ms": step8_ms, "int8_step_ms": step_i8_ms,
+            "fp8_gemm_tops_all": ops_total / gemm8 / 1e12,
+            "fp8_gemm_frac_of_peak": ops_total / gemm8 / 1e12 / PEAK_INT8_TOPS,
+            "per_projection": per}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -515,7 +570,8 @@ def main():
     capi.load()  # fails loudly when libsq.so is missing
     device = torch.device("cuda", 0)
     other = {"decode7b": workload_decode7b, "alpha_search": workload_alpha_search, "copy_probe": workload_copy_probe,
-             "prefill70b": workload_prefill70b, "hbm_passes": workload_hbm_passes, "variants": workload_variants}
+             "prefill70b": workload_prefill70b, "hbm_passes": workload_hbm_passes, "variants": workload_variants,
+             "fp8": workload_fp8}
     if args.workload in other:
         out = other[args.workload](device)
         out["gpu"] = torch.cuda.get_device_name(0)

@@ -9,6 +9,8 @@
  *   [pwwt]  "SmoothQuant技术解析：LLM模型INT8无损量化实践", pwwt.cn (§3.1 kernel stub)
  *   [tbr8]  tbr8.org, activation outliers and SmoothQuant (PyTorch example);
  *   [pwwt §2.3] static and dynamic scale modes on the same pwwt.cn page
+ *   [aiu]   "SmoothQuant 和激活量化", aiunderstanding.org (the section on where
+ *           smoothing goes next: INT8 and FP8 serving)
  *
  * Conventions shared by every entry point
  *   - Matrices are row-major with the reduction dimension k contiguous:
@@ -216,6 +218,36 @@ sq_status sq_fold_norm_weight(const float* gamma, const float* inv_s, int64_t k,
 sq_status sq_rmsnorm_quant_act(const void* h, sq_dtype ht, int64_t m, int64_t k,
                                const float* gamma_folded, float eps, const float* act_scale,
                                int8_t* xq, float* r_out, hipStream_t stream);
+
+/*
+ * FP8 variant [aiu: smoothing serves FP8 as well as INT8]: the same smoothed
+ * path with OCP FP8 E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, largest finite 448; round to nearest even; magnitudes past 448 are
+ * clamped to 448) in place of int8. Codes are bytes (uint8_t).
+ *   sq_act_scale_fp8:        act_scale = fp32( max_j fp32(max(act_max[j],1e-5) * inv_s[j]) / 448 )
+ *   sq_quant_weight_fp8:     w_scale[r] = fp32(max(max_j |W'[r,j]|, 1e-5) / 448),
+ *                            wq[r,j] = e4m3(fp32(W'[r,j] * fp32(1/w_scale[r]))), W' = W diag(s)
+ *   sq_smooth_quant_act_fp8: xq[r,j] = e4m3(fp32(fp32(x[r,j]*inv_s[j]) * fp32(1/act_scale[0])))
+ *   sq_fp8_gemm:             acc[r,c] = sum_j e4m3(xq[r,j]) * e4m3(wq[c,j]) on the matrix cores,
+ *                            accumulated in fp32; the FP8 instruction aligns each group of
+ *                            64 products to the largest and drops low bits, so acc is within
+ *                            about 2^-12 of sum_j |products| of the exact sum (not bit-exact);
+ *                            y[r,c] = fp32(acc[r,c] * fp32(act_scale[0] * w_scale[c]))
+ *                            (yt SQ_F32 or SQ_BF16 = RNE); acc_out [m,n] fp32 or NULL.
+ *                            k <= SQ_MAX_GEMM_K.
+ * Shapes, alignment and errors as for the int8 entry points.
+ */
+sq_status sq_act_scale_fp8(const float* act_max, const float* inv_s, int64_t k,
+                           float* act_scale, hipStream_t stream);
+sq_status sq_quant_weight_fp8(const void* w, sq_dtype wt, int64_t n, int64_t k,
+                              const float* s, uint8_t* wq, float* w_scale,
+                              hipStream_t stream);
+sq_status sq_smooth_quant_act_fp8(const void* x, sq_dtype xt, int64_t m, int64_t k,
+                                  const float* inv_s, const float* act_scale,
+                                  uint8_t* xq, hipStream_t stream);
+sq_status sq_fp8_gemm(const uint8_t* xq, const uint8_t* wq, int64_t m, int64_t n,
+                      int64_t k, const float* act_scale, const float* w_scale,
+                      void* y, sq_dtype yt, float* acc_out, hipStream_t stream);
 
 /*
  * Host-only query: the block tile (rows x columns of Y per workgroup) that

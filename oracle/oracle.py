@@ -73,6 +73,7 @@ def _declare(lib):
     lib.sqo_act_scale_fp8.restype = c.c_float
     lib.sqo_quant_act_fp8.argtypes = [P, c.c_int, i64, i64, P, c.c_float, P]
     lib.sqo_gemm_fp8.argtypes = [P, P, i64, i64, i64, c.c_float, P, c.c_int, P, P, P]
+    lib.sqo_dequant_f32.argtypes = [P, i64, i64, c.c_float, P, c.c_int, P]
     return lib
 
 
@@ -291,6 +292,14 @@ class Oracle:
         self.lib.sqo_gemm_fp8(_ptr(xq), _ptr(wq), m, n, k, float(np.float32(act_scale)), _ptr(w_scale),
                               BF16 if bf16 else F32, _ptr(y), _ptr(acc), _ptr(absacc))
         return y, acc, absacc
+
+    # O24
+    def dequant_f32(self, acc: np.ndarray, act_scale, w_scale: np.ndarray, bf16: bool = False) -> np.ndarray:
+        m, n = acc.shape
+        y = np.empty((m, n), np.uint16 if bf16 else np.float32)
+        self.lib.sqo_dequant_f32(_ptr(acc), m, n, float(np.float32(act_scale)), _ptr(w_scale),
+                                 BF16 if bf16 else F32, _ptr(y))
+        return y
 
     # the whole layer, O1..O10, for one runtime input (helper for tests)
     def layer_forward(self, x_calib_batches, w: np.ndarray, x: np.ndarray, alpha: float, bf16_out: bool = False):

@@ -473,3 +473,21 @@ void sqo_gemm_fp8(const uint8_t* xq, const uint8_t* wq, int64_t m, int64_t n,
         if (absacc) absacc[idx] = asum;
     }
 }
+
+/* O24: the dequantization of O10 (pwwt.cn §3.1 stub: merged scales) applied to
+ * an fp32 accumulator. */
+void sqo_dequant_f32(const float* acc, int64_t m, int64_t n, float act_scale,
+                     const float* w_scale, int ytype, void* y) {
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < m; ++r) {
+        for (int64_t c = 0; c < n; ++c) {
+            float merged = w_scale[c] * act_scale;
+            float v = acc[r * n + c] * merged;
+            if (ytype == SQO_BF16)
+                ((uint16_t*)y)[r * n + c] = float_to_bf16_rne(v);
+            else
+                ((float*)y)[r * n + c] = v;
+        }
+    }
+}

@@ -163,6 +163,11 @@ void sqo_gemm_fp8(const uint8_t* xq, const uint8_t* wq, int64_t m, int64_t n,
                   int64_t k, float act_scale, const float* w_scale, int ytype,
                   void* y, double* acc, double* absacc);
 
+/* O24: O10 for an fp32 accumulator (the FP8 product's): y = fl(acc *
+ * fl(act_scale * w_scale[n])), fp32 or bf16 (RNE). */
+void sqo_dequant_f32(const float* acc, int64_t m, int64_t n, float act_scale,
+                     const float* w_scale, int ytype, void* y);
+
 #ifdef __cplusplus
 }
 #endif

@@ -539,6 +539,10 @@ def pin_fp8_layer(o):
     assert rel_mse(y, exact) < 1e-3
     approx = acc * float(a) * ws[None, :].astype(np.float64)
     assert np.all(np.abs(y.astype(np.float64) - approx) <= 2 * 2.0 ** -23 * np.abs(approx) + 1e-30)
+    # O24 on an fp32 accumulator holding integers is O10 on the same int32 values
+    ia = g.integers(-2 ** 24, 2 ** 24, (m, n)).astype(np.int32)
+    for bf in (False, True):
+        assert np.array_equal(o.dequant_f32(ia.astype(np.float32), a, ws, bf16=bf), o.dequant(ia, a, ws, bf16=bf))
 
 
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

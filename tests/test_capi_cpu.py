@@ -282,3 +282,33 @@ def test_percentile_validation(lib):
     a = list(base)
     a[7] = P(MIS)
     assert f(*a) == ALIGN
+
+
+def test_fp8_validation(lib):
+    for name in ("sq_act_scale_fp8", "sq_quant_weight_fp8", "sq_smooth_quant_act_fp8", "sq_fp8_gemm"):
+        assert name in capi.declared_functions() and hasattr(lib, name)
+    assert lib.sq_act_scale_fp8(P(A), None, 1024, P(A), None) == NULL
+    assert lib.sq_act_scale_fp8(P(A), P(A), 1000, P(A), None) == SHAPE
+    f = lib.sq_quant_weight_fp8
+    assert f(P(A), 1, 8, 1024, None, P(A), P(A), None) == NULL
+    assert f(P(A), 4, 8, 1024, P(A), P(A), P(A), None) == DTYPE
+    assert f(P(A), 1, 8, 1056, P(A), P(A), P(A), None) == SHAPE
+    assert f(P(A), 1, 8, 1024, P(A), P(MIS), P(A), None) == ALIGN
+    g = lib.sq_smooth_quant_act_fp8
+    assert g(P(A), 1, 8, 1024, P(A), None, P(A), None) == NULL
+    assert g(P(MIS), 1, 8, 1024, P(A), P(A), P(A), None) == ALIGN
+    assert g(None, 1, 0, 1024, P(A), P(A), None, None) == OK
+    h = lib.sq_fp8_gemm
+    base = [P(A), P(A), 16, 32, 1024, P(A), P(A), P(A), 1, None, None]
+    a = list(base)
+    a[5] = None
+    assert h(*a) == NULL
+    a = list(base)
+    a[4] = 131072 + 64
+    assert h(*a) == SHAPE
+    a = list(base)
+    a[9] = P(MIS)
+    assert h(*a) == ALIGN
+    a = list(base)
+    a[3] = 0
+    assert h(*a) == OK

@@ -1,0 +1,147 @@
+"""GPU parity of the FP8 (OCP E4M3) variant against the CPU oracle.
+
+Bar: scales and e4m3 codes bit-exact (weight and activation quantizers, the
+activation scale). The product: the e4m3 products are exact, but the FP8
+matrix instruction (v_mfma_f32_32x32x64_f8f6f4) does not add its 64 products
+exactly: measured on gfx950, a single instruction's result is off the exact
+sum by up to 1.8e-4 (2^-12.4) of sum|products|, thousands of fp32 ulps when
+one product dominates (the small products lose their low bits against the
+largest), and the error does not grow with k beyond that (3e-5 to 6e-5 at
+k = 1024). The fp32 accumulator is therefore compared with the oracle's exact
+fp64 sum within |acc - exact| <= 2^-11 * sum|products| (several times the
+worst measured, far below the e4m3 step of 2^-4 relative), and the
+dequantized output is bit-exact against the oracle's dequantization of the
+GPU's own accumulator (the same stage-wise rule as for s and r).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle.oracle import Oracle
+from tests.gpu_pipeline import assert_bitexact, dev
+from w8a8_post_quantization_channel_amd import capi, synth
+
+pytestmark = pytest.mark.gpu
+ORACLE = Oracle()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    capi.load()
+
+
+def _t(a):
+    return synth.to_torch(a, dev())
+
+
+def _host(t):
+    return synth.from_torch(t)
+
+
+def _u8(t):
+    return synth.from_torch(t).view(np.uint8)
+
+
+def _smoothing(x, w, alpha=0.5):
+    act_max, w_max = ORACLE.calib_absmax(x), ORACLE.calib_absmax(w)
+    s, inv_s, _ = ORACLE.smooth_factors(act_max, w_max, alpha)
+    return act_max, s, inv_s
+
+
+@pytest.mark.parametrize("n,k,bf16", [(40, 320, True), (300, 1088, True), (257, 5120, True), (64, 13824, True),
+                                      (16, 66560, True), (33, 1024, False), (9, 40960, False)])
+def test_quant_weight_fp8(n, k, bf16):
+    import torch
+    w = synth.weights(700 + n, n, k, bf16=bf16)
+    g = synth.rng(701)
+    s = g.uniform(0.05, 20.0, k).astype(np.float32)
+    wq = torch.empty((n, k), dtype=torch.uint8, device=dev())
+    ws = torch.empty(n, dtype=torch.float32, device=dev())
+    capi.sq_quant_weight_fp8(_t(w), _t(s), wq, ws)
+    torch.cuda.synchronize()
+    rq, rs = ORACLE.quant_weight_fp8(w, s)
+    assert_bitexact("w_scale", _host(ws), rs)
+    assert_bitexact("wq (e4m3)", _u8(wq), rq)
+
+
+@pytest.mark.parametrize("m,k,bf16", [(300, 1088, True), (2048, 5120, True), (16, 1024, False), (1, 64, True),
+                                      (4099, 320, False)])
+def test_act_scale_and_quant_act_fp8(m, k, bf16):
+    import torch
+    out = synth.outlier_channels(710 + m, k)
+    xc = synth.activations(711 + m, m, k, out, bf16=bf16)
+    x = synth.activations(712 + m, m, k, out, bf16=bf16)   # runtime batch: may exceed the calibrated range
+    w = synth.weights(713, 48, k, bf16=bf16)
+    act_max, s, inv_s = _smoothing(xc, w)
+    a = torch.empty(4, dtype=torch.float32, device=dev())
+    capi.sq_act_scale_fp8(_t(act_max), _t(inv_s), a)
+    xq = torch.empty((m, k), dtype=torch.uint8, device=dev())
+    capi.sq_smooth_quant_act_fp8(_t(x), _t(inv_s), a, xq)
+    torch.cuda.synchronize()
+    ra = ORACLE.act_scale_fp8(act_max, inv_s)
+    assert_bitexact("act_scale (fp8)", _host(a)[:1], np.array([ra], np.float32))
+    assert_bitexact("xq (e4m3)", _u8(xq), ORACLE.quant_act_fp8(x, inv_s, ra))
+
+
+def test_quant_act_fp8_saturation_and_zeros():
+    import torch
+    k = 256
+    g = synth.rng(720)
+    x = (g.standard_normal((64, k)) * 10).astype(np.float32)
+    x[3, :] = 0.0
+    x[4, :] = -0.0
+    x[5, 7] = 1e6        # far past the scale: clamps to +448
+    x[6, 9] = -1e6
+    inv_s = g.uniform(0.5, 2.0, k).astype(np.float32)
+    a = np.float32(0.01)  # much smaller than max|x|/448: many values saturate
+    ta = torch.tensor([a, 0, 0, 0], dtype=torch.float32, device=dev())
+    xq = torch.empty((64, k), dtype=torch.uint8, device=dev())
+    capi.sq_smooth_quant_act_fp8(_t(x), _t(inv_s), ta, xq)
+    torch.cuda.synchronize()
+    ref = ORACLE.quant_act_fp8(x, inv_s, a)
+    assert_bitexact("xq (saturating)", _u8(xq), ref)
+    assert _u8(xq)[5, 7] == 0x7E and _u8(xq)[6, 9] == 0xFE
+
+
+GEMM_CASES = [(300, 520, 1088, True), (1, 16, 64, False), (257, 272, 192, True), (2100, 4112, 256, True),
+              (64, 4096, 1024, False), (513, 1000, 320, True), (1024, 8192, 256, True), (2048, 5120, 512, False),
+              (700, 2304, 2048, True)]
+
+
+@pytest.mark.parametrize("m,n,k,bf16_out", GEMM_CASES)
+def test_fp8_gemm(m, n, k, bf16_out):
+    import torch
+    g = synth.rng(730 + m)
+    # codes from the FP8 quantizers of a smoothed layer (realistic value spread, signs, subnormals)
+    out = synth.outlier_channels(731, k)
+    x = synth.activations(732 + m, m, k, out, bf16=True)
+    w = synth.weights(733 + n, n, k, bf16=True)
+    act_max, s, inv_s = _smoothing(x, w)
+    a = ORACLE.act_scale_fp8(act_max, inv_s)
+    xq = ORACLE.quant_act_fp8(x, inv_s, a)
+    wq, ws = ORACLE.quant_weight_fp8(w, s)
+    ta = torch.tensor([a, 0, 0, 0], dtype=torch.float32, device=dev())
+    y = torch.empty((m, n), dtype=torch.bfloat16 if bf16_out else torch.float32, device=dev())
+    acc = torch.empty((m, n), dtype=torch.float32, device=dev())
+    capi.sq_fp8_gemm(_t(xq.view(np.uint8)).view(torch.uint8), _t(wq).view(torch.uint8), ta, _t(ws), y, acc)
+    torch.cuda.synchronize()
+    gacc = _host(acc)
+    rows = np.unique(np.concatenate([np.arange(min(m, 64)), g.integers(0, m, 64), [m - 1]]))
+    _, exact, absacc = ORACLE.gemm_fp8(np.ascontiguousarray(xq[rows]), wq, a, ws)
+    bound = 2.0 ** -11 * absacc + 1e-30
+    err = np.abs(gacc[rows].astype(np.float64) - exact)
+    assert np.all(err <= bound), f"accumulator off by {float((err / np.maximum(absacc, 1e-30)).max()):.3g} of sum|p|"
+    assert_bitexact("y given acc", _host(y), ORACLE.dequant_f32(gacc, a, ws, bf16=bf16_out))
+
+
+def test_fp8_gemm_empty():
+    import torch
+    ta = torch.tensor([0.1, 0, 0, 0], dtype=torch.float32, device=dev())
+    y = torch.full((4, 16), 3.0, dtype=torch.float32, device=dev())
+    xq = torch.zeros((0, 64), dtype=torch.uint8, device=dev())
+    wq = torch.zeros((16, 64), dtype=torch.uint8, device=dev())
+    ws = torch.ones(16, dtype=torch.float32, device=dev())
+    capi.sq_fp8_gemm(xq, wq, ta, ws, y[:0])
+    torch.cuda.synchronize()
+    assert (_host(y) == 3.0).all()

@@ -73,6 +73,7 @@ MUTANTS = {
     "fp8_act_scale_ignores_s": ("float v = inv_s[j] * a;", "float v = a;"),
     "fp8_gemm_drops_sign": ("double p = (double)sqo_e4m3_decode(xq[r * k + j]) * (double)sqo_e4m3_decode(wq[c * k + j]);",
                             "double p = fabs((double)sqo_e4m3_decode(xq[r * k + j])) * (double)sqo_e4m3_decode(wq[c * k + j]);"),
+    "dequant_f32_act_scale_only": ("float merged = w_scale[c] * act_scale;", "float merged = act_scale;"),
     "norm_quant_drops_r": ("float smoothed = (elem(h, htype, t * k + j) * r[t]) * gamma_folded[j];",
                            "float smoothed = elem(h, htype, t * k + j) * gamma_folded[j];"),
 }

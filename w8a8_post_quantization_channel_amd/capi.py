@@ -57,6 +57,10 @@ def _declare(lib):
         "sq_calib_percentile_workspace": [c.c_int, i64, P],
         "sq_calib_percentile": [P, c.c_int, i64, i64, c.c_double, P, c.c_size_t, P, P],
         "sq_rmsnorm": [P, c.c_int, i64, i64, P, c.c_float, P, c.c_int, P, P],
+        "sq_act_scale_fp8": [P, P, i64, P, P],
+        "sq_quant_weight_fp8": [P, c.c_int, i64, i64, P, P, P, P],
+        "sq_smooth_quant_act_fp8": [P, c.c_int, i64, i64, P, P, P, P],
+        "sq_fp8_gemm": [P, P, i64, i64, i64, P, P, P, c.c_int, P, P],
         "sq_fold_norm_weight": [P, P, i64, P, P],
         "sq_rmsnorm_quant_act": [P, c.c_int, i64, i64, P, c.c_float, P, P, P, P],
     }
@@ -247,3 +251,34 @@ def sq_calib_percentile(x, q: float, workspace, act_max, stream=None):
                                                              _dev(workspace, "workspace"),
                                                              workspace.numel() * workspace.element_size(),
                                                              _dev(act_max, "act_max"), _stream(stream)))
+
+
+# ---- FP8 (OCP E4M3) variant: codes are torch.uint8 tensors --------------------------
+
+def sq_act_scale_fp8(act_max, inv_s, act_scale, stream=None):
+    k = act_max.shape[0]
+    _check("sq_act_scale_fp8", load().sq_act_scale_fp8(_dev(act_max, "act_max"), _dev(inv_s, "inv_s"), k,
+                                                       _dev(act_scale, "act_scale"), _stream(stream)))
+
+
+def sq_quant_weight_fp8(w, s, wq, w_scale, stream=None):
+    n, k = w.shape
+    _check("sq_quant_weight_fp8", load().sq_quant_weight_fp8(_dev(w, "w"), _dtype_code(w), n, k, _dev(s, "s"),
+                                                             _dev(wq, "wq"), _dev(w_scale, "w_scale"),
+                                                             _stream(stream)))
+
+
+def sq_smooth_quant_act_fp8(x, inv_s, act_scale, xq, stream=None):
+    m, k = x.shape
+    _check("sq_smooth_quant_act_fp8", load().sq_smooth_quant_act_fp8(_dev(x, "x"), _dtype_code(x), m, k,
+                                                                     _dev(inv_s, "inv_s"),
+                                                                     _dev(act_scale, "act_scale"), _dev(xq, "xq"),
+                                                                     _stream(stream)))
+
+
+def sq_fp8_gemm(xq, wq, act_scale, w_scale, y, acc_out=None, stream=None):
+    m, k = xq.shape
+    n = wq.shape[0]
+    _check("sq_fp8_gemm", load().sq_fp8_gemm(_dev(xq, "xq"), _dev(wq, "wq"), m, n, k, _dev(act_scale, "act_scale"),
+                                             _dev(w_scale, "w_scale"), _dev(y, "y"), _dtype_code(y),
+                                             _opt(acc_out, "acc_out"), _stream(stream)))

@@ -174,13 +174,13 @@ constexpr int kScaleThreads = 1024;
 
 __global__ __launch_bounds__(kScaleThreads) void act_scale_kernel(const float* __restrict__ act_max,
                                                                   const float* __restrict__ inv_s, int64_t k,
-                                                                  float* __restrict__ act_scale) {
+                                                                  float qmax, float* __restrict__ act_scale) {
     __shared__ float red[kScaleThreads / 64];
     float mx = 0.0f;
     for (int64_t j = threadIdx.x; j < k; j += kScaleThreads)
         mx = __builtin_fmaxf(mx, __fmul_rn(__builtin_fmaxf(act_max[j], sqd::kFloor), inv_s[j]));
     mx = sqd::block_max<kScaleThreads / 64>(mx, red);
-    if (threadIdx.x == 0) act_scale[0] = __fdiv_rn(mx, sqd::kQmax);
+    if (threadIdx.x == 0) act_scale[0] = __fdiv_rn(mx, qmax);
 }
 
 }  // namespace
@@ -221,7 +221,13 @@ hipError_t absmax(const void* x, int xt, int64_t rows, int64_t k, float* absmax_
 
 hipError_t act_scale(const float* act_max, const float* inv_s, int64_t k, float* act_scale_out,
                      hipStream_t stream) {
-    act_scale_kernel<<<dim3(1), dim3(kScaleThreads), 0, stream>>>(act_max, inv_s, k, act_scale_out);
+    act_scale_kernel<<<dim3(1), dim3(kScaleThreads), 0, stream>>>(act_max, inv_s, k, sqd::kQmax, act_scale_out);
+    return hipGetLastError();
+}
+
+hipError_t act_scale_fp8(const float* act_max, const float* inv_s, int64_t k, float* act_scale_out,
+                         hipStream_t stream) {
+    act_scale_kernel<<<dim3(1), dim3(kScaleThreads), 0, stream>>>(act_max, inv_s, k, sqd::kFp8Max, act_scale_out);
     return hipGetLastError();
 }
 
@@ -265,7 +271,7 @@ hipError_t smooth_factors(const float* act_max, const float* w_max, int64_t k, f
                           float* inv_s, float* act_scale, hipStream_t stream) {
     smooth_kernel<<<dim3((unsigned)((k + kSmoothThreads - 1) / kSmoothThreads)), dim3(kSmoothThreads), 0,
                     stream>>>(act_max, w_max, k, (double)alpha, s, inv_s);
-    act_scale_kernel<<<dim3(1), dim3(kScaleThreads), 0, stream>>>(act_max, inv_s, k, act_scale);
+    act_scale_kernel<<<dim3(1), dim3(kScaleThreads), 0, stream>>>(act_max, inv_s, k, sqd::kQmax, act_scale);
     return hipGetLastError();
 }
 

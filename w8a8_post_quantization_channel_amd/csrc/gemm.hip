@@ -48,6 +48,8 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 // of K per instruction; S = 16 -> 16x16 tile, 4 accumulators per lane, 64
 // bytes of K per instruction. (bf16: the same byte geometry, half the elements.)
 struct OpI8 {
+    static constexpr int KB = 32;  // bytes of K per lane-pair per instruction (16 bytes per lane)
+    using frag_t = v4i;
     template <int S>
     using acc_t = typename std::conditional<S == 32, v16i, v4i>::type;
     template <int S>
@@ -60,6 +62,8 @@ struct OpI8 {
 };
 
 struct OpBF16 {
+    static constexpr int KB = 32;
+    using frag_t = v4i;
     template <int S>
     using acc_t = typename std::conditional<S == 32, v16f, v4f>::type;
     template <int S>
@@ -70,6 +74,22 @@ struct OpBF16 {
         else
             return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b),
                                                            c, 0, 0, 0);
+    }
+};
+
+// OCP FP8 E4M3 x E4M3 -> fp32 on gfx950's v_mfma_f32_32x32x64_f8f6f4 (the
+// scaled form with both scales 0 is the unscaled instruction): 32 bytes of K
+// per lane, 32 x 32 x 64 per instruction, the same rate per byte as int8.
+typedef int v8i __attribute__((ext_vector_type(8)));
+struct OpF8 {
+    static constexpr int KB = 64;
+    using frag_t = v8i;
+    template <int S>
+    using acc_t = v16f;
+    template <int S>
+    __device__ static __forceinline__ acc_t<S> mfma(const v8i& a, const v8i& b, const acc_t<S>& c) {
+        static_assert(S == 32, "32 x 32 tiles only");
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
     }
 };
 
@@ -104,12 +124,12 @@ constexpr int kBK = 128;  // bytes of K per LDS stage
 
 // y = fp32(fp32(acc) * fp32(act_scale * w_scale[col])), fp32 or bf16 store;
 // the raw int32 accumulator is stored too when acc_out is set.
-template <bool kBF16Out>
+template <bool kBF16Out, class AccT = int32_t>
 struct EpiDequant {
     const float* act_scale;
     const float* w_scale;
     void* y;
-    int32_t* acc_out;
+    AccT* acc_out;
     int64_t M, N;
     float a;
     __device__ void begin() { a = act_scale[0]; }
@@ -155,7 +175,7 @@ struct EpiDequant {
     }
     // fast: the caller's whole tile lies inside M x N and N % 8 == 0 (a
     // uniform condition), so no bounds checks and 16-byte stores
-    __device__ void row8(const int (&acc)[8], int64_t row, const Cols& cc, bool fast) {
+    __device__ void row8(const AccT (&acc)[8], int64_t row, const Cols& cc, bool fast) {
         const int64_t col = cc.col;
         float val[8];
 #pragma unroll
@@ -177,8 +197,8 @@ struct EpiDequant {
                 *(v4f*)((float*)y + idx + 4) = v4f{val[4], val[5], val[6], val[7]};
             }
             if (acc_out) {
-                *(v4i*)(acc_out + idx) = v4i{acc[0], acc[1], acc[2], acc[3]};
-                *(v4i*)(acc_out + idx + 4) = v4i{acc[4], acc[5], acc[6], acc[7]};
+                *(v4i*)(acc_out + idx) = v4i{as_bits(acc[0]), as_bits(acc[1]), as_bits(acc[2]), as_bits(acc[3])};
+                *(v4i*)(acc_out + idx + 4) = v4i{as_bits(acc[4]), as_bits(acc[5]), as_bits(acc[6]), as_bits(acc[7])};
             }
             return;
         }
@@ -476,7 +496,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
     constexpr int LA = BM / 32;                      // ... of which A rows
     constexpr int NFA = 2, NFB = TN, NF = NFA + NFB; // fragment reads per substep
     constexpr int NMMA = 2 * TN;                     // MFMAs per substep
-    constexpr int NSUB = kDmaBK / 32;                // MFMA substeps per step
+    constexpr int NSUB = kDmaBK / Op::KB;            // MFMA substeps per step
     static_assert(NF <= NMMA + 2, "fragment reads interleave with the MFMAs");
     static_assert((NS - 2) * L < 64, "vmcnt range");
     static_assert(4 * 32 * BN * 4 <= NS * STAGE, "the epilogue transpose fits in the stages");
@@ -559,14 +579,29 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
     const int c0 = (lane >> 5) ^ ((lane >> 1) & 7);  // chunk 2*ks + lane/32 lands at position c0 ^ 2*ks
     const int a_off = (wave * 64 + frow) * kDmaBK;
     const int b_off = frow * kDmaBK;
-    v4i fa[2][NFA], fb[2][NFB];  // [substep parity][tile]
+    using Frag = typename Op::frag_t;
+    Frag fa[2][NFA], fb[2][NFB];  // [substep parity][tile]
     auto read_frag = [&](uint32_t stage, int ks, int f) {
-        const int ch = (c0 ^ (2 * ks)) << 4;
         const char* p = lds + stage;
-        if (f < NFA)
-            fa[ks & 1][f] = *(const v4i*)(p + (a_off + ch) + f * 32 * kDmaBK);
-        else
-            fb[ks & 1][f - NFA] = *(const v4i*)(p + (b_off + ch) + (BM + (f - NFA) * 32) * kDmaBK);
+        if constexpr (Op::KB == 32) {
+            const int ch = (c0 ^ (2 * ks)) << 4;
+            if (f < NFA)
+                fa[ks & 1][f] = *(const v4i*)(p + (a_off + ch) + f * 32 * kDmaBK);
+            else
+                fb[ks & 1][f - NFA] = *(const v4i*)(p + (b_off + ch) + (BM + (f - NFA) * 32) * kDmaBK);
+        } else {
+            // 64 bytes of K per substep: lane (row, h) takes chunks 4ks + 2h and
+            // 4ks + 2h + 1, stored at positions (chunk ^ ((row >> 1) & 7))
+            const int sw = (lane >> 1) & 7, h2 = 2 * (lane >> 5);
+            const int ch0 = ((4 * ks + h2) ^ sw) << 4, ch1 = ((4 * ks + h2 + 1) ^ sw) << 4;
+            const int base = f < NFA ? a_off + f * 32 * kDmaBK : b_off + (BM + (f - NFA) * 32) * kDmaBK;
+            const v4i lo = *(const v4i*)(p + base + ch0), hi = *(const v4i*)(p + base + ch1);
+            const Frag v = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if (f < NFA)
+                fa[ks & 1][f] = v;
+            else
+                fb[ks & 1][f - NFA] = v;
+        }
     };
     auto read_frags = [&](uint32_t stage, int ks) {
 #pragma unroll
@@ -595,7 +630,10 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
     // step). Steps past the end load zeros, so every step has the same
     // instruction stream.
     constexpr int DSTRIDE = (NSUB - 1) * NMMA / L > 0 ? (NSUB - 1) * NMMA / L : 1;
-    static_assert((L - 1) * DSTRIDE < (NSUB - 1) * NMMA, "the loads fit in the first substeps");
+    static_assert(Op::KB != 32 || (L - 1) * DSTRIDE < (NSUB - 1) * NMMA, "the loads fit in the first substeps");
+    // 64-byte substeps (two per step): the L loads are dealt over the MFMA
+    // slots of the first substep, one or two per slot
+    constexpr int SLOTS1 = (NSUB - 1) * NMMA;
     uint32_t cur = 0, nxt = STAGE, fill = (NS - 1) * STAGE;  // stages of kb, kb + 1, kb + NS - 1
     for (int64_t kb = 0; kb < nk; ++kb) {
         const bool more = kb + NS - 1 < nk;
@@ -616,8 +654,14 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
                 acc[i][j] = Op::template mfma<32>(fb[ks & 1][j], fa[ks & 1][i], acc[i][j]);
                 if (m < NF) read_frag(rstage, rks, m);
                 const int slot = ks * NMMA + m;
-                if (ks + 1 < NSUB && slot % DSTRIDE == 0 && slot / DSTRIDE < L)
-                    dma(slot / DSTRIDE, fill, kb + NS - 1, !more);
+                if constexpr (Op::KB == 32) {
+                    if (ks + 1 < NSUB && slot % DSTRIDE == 0 && slot / DSTRIDE < L)
+                        dma(slot / DSTRIDE, fill, kb + NS - 1, !more);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < L; ++j)
+                        if (ks + 1 < NSUB && (j * SLOTS1) / L == slot) dma(j, fill, kb + NS - 1, !more);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -860,6 +904,30 @@ hipError_t dispatch(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int6
     }
 }
 
+// FP8 products: the pipelined kernel at every size (its tilings only)
+template <class Epi>
+hipError_t dispatch_f8(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t Kb, Epi epi,
+                       hipStream_t stream) {
+    const int64_t cus = cu_count();
+    int best = kD128;
+    double best_cost = 0.0;
+    for (int c = kD256; c <= kD128; ++c) {
+        const int64_t rounds = (tiles_of((TileCfg)c, M, N) + cus - 1) / cus;
+        const double cost = (double)rounds * kCfgBM[c] * kCfgBN[c] / kCfgEff[c];
+        if (c == kD256 || cost < best_cost) {
+            best_cost = cost;
+            best = c;
+        }
+    }
+    switch (best) {
+        case kD256: return launch_dma<OpF8, 8>(A, B, M, N, Kb, epi, stream);
+        case kD224: return launch_dma<OpF8, 7>(A, B, M, N, Kb, epi, stream);
+        case kD192: return launch_dma<OpF8, 6>(A, B, M, N, Kb, epi, stream);
+        case kD160: return launch_dma<OpF8, 5>(A, B, M, N, Kb, epi, stream);
+        default: return launch_dma<OpF8, 4>(A, B, M, N, Kb, epi, stream);
+    }
+}
+
 __global__ __launch_bounds__(256) void reduce_slots_kernel(const double* __restrict__ slots, int64_t per_group,
                                                            double count, double* __restrict__ out) {
     __shared__ double red[256];
@@ -921,6 +989,17 @@ hipError_t gemm_dequant(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n
     }
     EpiDequant<false> e{act_scale, w_scale, y, acc_out, m, n, 0.0f};
     return dispatch<OpI8>(xq, wq, m, n, k, e, stream);
+}
+
+hipError_t gemm_fp8(const uint8_t* xq, const uint8_t* wq, int64_t m, int64_t n, int64_t k, const float* act_scale,
+                    const float* w_scale, void* y, int yt, float* acc_out, hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    if (yt == kBF16) {
+        EpiDequant<true, float> e{act_scale, w_scale, y, acc_out, m, n, 0.0f};
+        return dispatch_f8((const int8_t*)xq, (const int8_t*)wq, m, n, k, e, stream);
+    }
+    EpiDequant<false, float> e{act_scale, w_scale, y, acc_out, m, n, 0.0f};
+    return dispatch_f8((const int8_t*)xq, (const int8_t*)wq, m, n, k, e, stream);
 }
 
 void gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n) {

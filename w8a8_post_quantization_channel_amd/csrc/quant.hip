@@ -87,7 +87,7 @@ __device__ __forceinline__ void store_codes(int8_t* __restrict__ dst, const int 
 constexpr int kQwThreads = 512;
 constexpr int kQwWaves = kQwThreads / 64;
 
-template <int EB, int VPT, int RB, int CPW, int NS>
+template <int EB, int VPT, int RB, int CPW, int NS, bool FP8>
 __global__ __launch_bounds__(kQwThreads) void quant_weight_stream_kernel(const int8_t* __restrict__ w, int64_t n,
                                                                         int64_t kvec, const float* __restrict__ s,
                                                                         int8_t* __restrict__ wq,
@@ -192,9 +192,20 @@ __global__ __launch_bounds__(kQwThreads) void quant_weight_stream_kernel(const i
 #pragma unroll
             for (int i = 1; i < kQwWaves; ++i) m = __builtin_fmaxf(m, part[r][i]);
             m = __builtin_fmaxf(m, sqd::kFloor);
-            const float ws = __fdiv_rn(m, sqd::kQmax);
+            const float ws = __fdiv_rn(m, FP8 ? sqd::kFp8Max : sqd::kQmax);
             const float inv_ws = __fdiv_rn(1.0f, ws);
             scale[r] = ws;
+            if constexpr (FP8) {
+                // e4m3 codes: |W' / ws| <= 448 (1 + 3 * 2^-24), which rounds to 448
+#pragma unroll
+                for (int i = 0; i < VPT; ++i)
+#pragma unroll
+                    for (int d = 0; d < W32; ++d)
+                        codes[r][i][d] = sqd::pack4_e4m3(
+                            __fmul_rn(wv[r][i][4 * d], inv_ws), __fmul_rn(wv[r][i][4 * d + 1], inv_ws),
+                            __fmul_rn(wv[r][i][4 * d + 2], inv_ws), __fmul_rn(wv[r][i][4 * d + 3], inv_ws));
+                continue;
+            }
             // Codes by the round-to-nearest-even of the fp32 adder: for
             // |v| < 2^22, fl(v + 1.5 * 2^23) = rint(v) + 1.5 * 2^23 exactly, and
             // the low byte of its bit pattern is rint(v) as a two's-complement
@@ -226,7 +237,7 @@ __global__ __launch_bounds__(kQwThreads) void quant_weight_stream_kernel(const i
 
 // Rows longer than 4096 groups (k > 65536): one block per row, the row is
 // read twice and s is read from cache.
-template <int EB>
+template <int EB, bool FP8>
 __global__ __launch_bounds__(256) void quant_weight_long_kernel(const u32x4* __restrict__ w, int64_t kgroups,
                                                                 const float* __restrict__ s,
                                                                 int8_t* __restrict__ wq, float* __restrict__ w_scale) {
@@ -244,7 +255,7 @@ __global__ __launch_bounds__(256) void quant_weight_long_kernel(const u32x4* __r
         for (int j = 0; j < 16; ++j) mx = __builtin_fmaxf(mx, __builtin_fabsf(__fmul_rn(e[j], sv[j])));
     }
     mx = __builtin_fmaxf(sqd::block_max<4>(mx, red), sqd::kFloor);
-    const float ws = __fdiv_rn(mx, sqd::kQmax);
+    const float ws = __fdiv_rn(mx, FP8 ? sqd::kFp8Max : sqd::kQmax);
     const float inv_ws = __fdiv_rn(1.0f, ws);
     for (int64_t gi = threadIdx.x; gi < kgroups; gi += 256) {
         Group<EB> raw;
@@ -253,6 +264,15 @@ __global__ __launch_bounds__(256) void quant_weight_long_kernel(const u32x4* __r
         raw.load(w + (row * kgroups + gi) * VG);
         raw.widen(e);
         load16f(s + gi * 16, sv);
+        if constexpr (FP8) {
+            float v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = __fmul_rn(__fmul_rn(e[j], sv[j]), inv_ws);
+            *(u32x4*)(wq + (row * kgroups + gi) * 16) =
+                u32x4{sqd::pack4_e4m3(v[0], v[1], v[2], v[3]), sqd::pack4_e4m3(v[4], v[5], v[6], v[7]),
+                      sqd::pack4_e4m3(v[8], v[9], v[10], v[11]), sqd::pack4_e4m3(v[12], v[13], v[14], v[15])};
+            continue;
+        }
 #pragma unroll
         for (int j = 0; j < 16; ++j) q[j] = sqd::q8(__fmul_rn(__fmul_rn(e[j], sv[j]), inv_ws));
         store16(wq + (row * kgroups + gi) * 16, q);
@@ -266,7 +286,7 @@ constexpr int kActUnroll = 8;
 // A lane owns one 16-byte column vector (E = 16 / EB elements) of the input
 // and keeps its E inv_s values in registers; the four waves of a block walk
 // interleaved rows, so each wave instruction moves one contiguous 1 KB run.
-template <int EB>
+template <int EB, bool FP8>
 __global__ __launch_bounds__(kActThreads) void quant_act_kernel(const u32x4* __restrict__ x, int64_t rows,
                                                                 int64_t kvec, int64_t rows_per_block,
                                                                 const float* __restrict__ inv_s,
@@ -290,11 +310,23 @@ __global__ __launch_bounds__(kActThreads) void quant_act_kernel(const u32x4* __r
     const int64_t r1 = min(rows, r0 + rows_per_block);
     auto quantize = [&](const u32x4& raw, int64_t r) {
         float e[E];
-        int q[E];
         sqd::unpack16<E>(raw, e);
+        if constexpr (FP8) {
+            float t[E];
 #pragma unroll
-        for (int t = 0; t < E; ++t) q[t] = sqd::q8(__fmul_rn(__fmul_rn(e[t], is[t]), inv_a));
-        store_codes<E>(xq + (r * kvec + v) * E, q);
+            for (int u = 0; u < E; ++u) t[u] = __fmul_rn(__fmul_rn(e[u], is[u]), inv_a);
+            int8_t* dst = xq + (r * kvec + v) * E;
+            if constexpr (E == 8)
+                *(sqd::u32x2*)dst = sqd::u32x2{sqd::pack4_e4m3(t[0], t[1], t[2], t[3]),
+                                               sqd::pack4_e4m3(t[4], t[5], t[6], t[7])};
+            else
+                *(uint32_t*)dst = sqd::pack4_e4m3(t[0], t[1], t[2], t[3]);
+        } else {
+            int q[E];
+#pragma unroll
+            for (int t = 0; t < E; ++t) q[t] = sqd::q8(__fmul_rn(__fmul_rn(e[t], is[t]), inv_a));
+            store_codes<E>(xq + (r * kvec + v) * E, q);
+        }
     };
     int64_t r = r0 + wave;
     for (; r + 4 * (kActUnroll - 1) < r1; r += 4 * kActUnroll) {
@@ -318,19 +350,19 @@ int device_cus() {
     return cus;
 }
 
-template <int EB, int VPT, int RB, int CPW, int NS>
+template <int EB, int VPT, int RB, int CPW, int NS, bool FP8>
 hipError_t launch_qw(const void* w, int64_t n, int64_t kvec, const float* s, int8_t* wq, float* w_scale,
                      hipStream_t stream) {
     static_assert(NS * CPW * kQwWaves * 1024 <= 150 * 1024, "the ring fits in LDS");
     if (RB * kvec * 16 > CPW * kQwWaves * 1024 || kvec > VPT * kQwThreads) return hipErrorInvalidValue;
     const int64_t nstages = (n + RB - 1) / RB;
     const int64_t blocks = std::min<int64_t>(nstages, (int64_t)device_cus());
-    quant_weight_stream_kernel<EB, VPT, RB, CPW, NS><<<dim3((unsigned)blocks), dim3(kQwThreads), 0, stream>>>(
+    quant_weight_stream_kernel<EB, VPT, RB, CPW, NS, FP8><<<dim3((unsigned)blocks), dim3(kQwThreads), 0, stream>>>(
         (const int8_t*)w, n, kvec, s, wq, w_scale);
     return hipGetLastError();
 }
 
-template <int EB>
+template <int EB, bool FP8>
 hipError_t quant_weight_t(const void* w, int64_t n, int64_t k, const float* s, int8_t* wq, float* w_scale,
                           hipStream_t stream) {
     const int64_t kvec = k * EB / 16;  // 16-byte vectors per row
@@ -338,14 +370,14 @@ hipError_t quant_weight_t(const void* w, int64_t n, int64_t k, const float* s, i
     // stages of 32-56 KB so each pair of barriers covers enough bytes, three
     // in the ring when they fit; rows of more than 4096 vectors are read twice
     // by a block per row
-    if (kvec <= 256) return launch_qw<EB, 1, 8, 4, 3>(w, n, kvec, s, wq, w_scale, stream);
-    if (kvec <= 512) return launch_qw<EB, 1, 4, 4, 3>(w, n, kvec, s, wq, w_scale, stream);
-    if (kvec <= 640) return launch_qw<EB, 2, 4, 5, 3>(w, n, kvec, s, wq, w_scale, stream);
-    if (kvec <= 1024) return launch_qw<EB, 2, 2, 4, 3>(w, n, kvec, s, wq, w_scale, stream);
-    if (kvec <= 1792) return launch_qw<EB, 4, 2, 7, 2>(w, n, kvec, s, wq, w_scale, stream);
-    if (kvec <= 2048) return launch_qw<EB, 4, 1, 4, 3>(w, n, kvec, s, wq, w_scale, stream);
-    if (kvec <= 4096) return launch_qw<EB, 8, 1, 8, 2>(w, n, kvec, s, wq, w_scale, stream);
-    quant_weight_long_kernel<EB><<<dim3((unsigned)n), dim3(256), 0, stream>>>((const u32x4*)w, k / 16, s, wq,
+    if (kvec <= 256) return launch_qw<EB, 1, 8, 4, 3, FP8>(w, n, kvec, s, wq, w_scale, stream);
+    if (kvec <= 512) return launch_qw<EB, 1, 4, 4, 3, FP8>(w, n, kvec, s, wq, w_scale, stream);
+    if (kvec <= 640) return launch_qw<EB, 2, 4, 5, 3, FP8>(w, n, kvec, s, wq, w_scale, stream);
+    if (kvec <= 1024) return launch_qw<EB, 2, 2, 4, 3, FP8>(w, n, kvec, s, wq, w_scale, stream);
+    if (kvec <= 1792) return launch_qw<EB, 4, 2, 7, 2, FP8>(w, n, kvec, s, wq, w_scale, stream);
+    if (kvec <= 2048) return launch_qw<EB, 4, 1, 4, 3, FP8>(w, n, kvec, s, wq, w_scale, stream);
+    if (kvec <= 4096) return launch_qw<EB, 8, 1, 8, 2, FP8>(w, n, kvec, s, wq, w_scale, stream);
+    quant_weight_long_kernel<EB, FP8><<<dim3((unsigned)n), dim3(256), 0, stream>>>((const u32x4*)w, k / 16, s, wq,
                                                                             w_scale);
     return hipGetLastError();
 }
@@ -357,12 +389,20 @@ namespace sqk {
 hipError_t quant_weight(const void* w, int wt, int64_t n, int64_t k, const float* s, int8_t* wq,
                         float* w_scale, hipStream_t stream) {
     if (n == 0) return hipSuccess;
-    return elem_bytes(wt) == 2 ? quant_weight_t<2>(w, n, k, s, wq, w_scale, stream)
-                               : quant_weight_t<4>(w, n, k, s, wq, w_scale, stream);
+    return elem_bytes(wt) == 2 ? quant_weight_t<2, false>(w, n, k, s, wq, w_scale, stream)
+                               : quant_weight_t<4, false>(w, n, k, s, wq, w_scale, stream);
 }
 
-hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const float* inv_s, const float* act_scale,
-                     int8_t* xq, hipStream_t stream) {
+hipError_t quant_weight_fp8(const void* w, int wt, int64_t n, int64_t k, const float* s, uint8_t* wq,
+                            float* w_scale, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    return elem_bytes(wt) == 2 ? quant_weight_t<2, true>(w, n, k, s, (int8_t*)wq, w_scale, stream)
+                               : quant_weight_t<4, true>(w, n, k, s, (int8_t*)wq, w_scale, stream);
+}
+
+template <bool FP8>
+hipError_t quant_act_t(const void* x, int xt, int64_t m, int64_t k, const float* inv_s, const float* act_scale,
+                       int8_t* xq, hipStream_t stream) {
     if (m == 0) return hipSuccess;
     const int eb = elem_bytes(xt);
     const int64_t kvec = k * eb / 16;
@@ -379,10 +419,20 @@ hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const float* i
     }
     const dim3 grid((unsigned)strips, (unsigned)chunks), block(kActThreads);
     if (eb == 2)
-        quant_act_kernel<2><<<grid, block, 0, stream>>>((const u32x4*)x, m, kvec, rpb, inv_s, act_scale, xq);
+        quant_act_kernel<2, FP8><<<grid, block, 0, stream>>>((const u32x4*)x, m, kvec, rpb, inv_s, act_scale, xq);
     else
-        quant_act_kernel<4><<<grid, block, 0, stream>>>((const u32x4*)x, m, kvec, rpb, inv_s, act_scale, xq);
+        quant_act_kernel<4, FP8><<<grid, block, 0, stream>>>((const u32x4*)x, m, kvec, rpb, inv_s, act_scale, xq);
     return hipGetLastError();
+}
+
+hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const float* inv_s, const float* act_scale,
+                     int8_t* xq, hipStream_t stream) {
+    return quant_act_t<false>(x, xt, m, k, inv_s, act_scale, xq, stream);
+}
+
+hipError_t quant_act_fp8(const void* x, int xt, int64_t m, int64_t k, const float* inv_s, const float* act_scale,
+                         uint8_t* xq, hipStream_t stream) {
+    return quant_act_t<true>(x, xt, m, k, inv_s, act_scale, (int8_t*)xq, stream);
 }
 
 }  // namespace sqk

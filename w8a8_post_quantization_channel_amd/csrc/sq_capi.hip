@@ -166,6 +166,48 @@ sq_status sq_calib_mean_finalize(const double* sum, int64_t count, int64_t k, fl
     return hip_status(sqk::mean_finalize(sum, count, k, act_max, stream));
 }
 
+sq_status sq_act_scale_fp8(const float* act_max, const float* inv_s, int64_t k, float* act_scale,
+                           hipStream_t stream) {
+    if (!act_max || !inv_s || !act_scale) return SQ_ERR_NULL;
+    if (!valid_k(k)) return SQ_ERR_SHAPE;
+    if (!aligned16(act_max) || !aligned16(inv_s) || !aligned16(act_scale)) return SQ_ERR_ALIGN;
+    return hip_status(sqk::act_scale_fp8(act_max, inv_s, k, act_scale, stream));
+}
+
+sq_status sq_quant_weight_fp8(const void* w, sq_dtype wt, int64_t n, int64_t k, const float* s, uint8_t* wq,
+                              float* w_scale, hipStream_t stream) {
+    if (!s || (n > 0 && (!w || !wq || !w_scale))) return SQ_ERR_NULL;
+    if (!valid_dtype(wt)) return SQ_ERR_DTYPE;
+    if (n < 0 || !valid_k(k) || n > INT32_MAX) return SQ_ERR_SHAPE;
+    if (!aligned16(s) || (n > 0 && (!aligned16(w) || !aligned16(wq) || !aligned16(w_scale)))) return SQ_ERR_ALIGN;
+    return hip_status(sqk::quant_weight_fp8(w, wt, n, k, s, wq, w_scale, stream));
+}
+
+sq_status sq_smooth_quant_act_fp8(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* inv_s,
+                                  const float* act_scale, uint8_t* xq, hipStream_t stream) {
+    if (!inv_s || !act_scale || (m > 0 && (!x || !xq))) return SQ_ERR_NULL;
+    if (!valid_dtype(xt)) return SQ_ERR_DTYPE;
+    if (m < 0 || !valid_k(k)) return SQ_ERR_SHAPE;
+    if (!aligned16(inv_s) || !aligned16(act_scale) || (m > 0 && (!aligned16(x) || !aligned16(xq))))
+        return SQ_ERR_ALIGN;
+    if (m == 0) return SQ_OK;
+    return hip_status(sqk::quant_act_fp8(x, xt, m, k, inv_s, act_scale, xq, stream));
+}
+
+sq_status sq_fp8_gemm(const uint8_t* xq, const uint8_t* wq, int64_t m, int64_t n, int64_t k, const float* act_scale,
+                      const float* w_scale, void* y, sq_dtype yt, float* acc_out, hipStream_t stream) {
+    const bool work = m > 0 && n > 0;
+    if (!act_scale || (work && (!xq || !wq || !w_scale || !y))) return SQ_ERR_NULL;
+    if (!valid_dtype(yt)) return SQ_ERR_DTYPE;
+    if (m < 0 || n < 0 || !valid_k(k) || k > SQ_MAX_GEMM_K) return SQ_ERR_SHAPE;
+    if ((m + 127) / 128 * ((n + 127) / 128) > INT32_MAX / 2) return SQ_ERR_SHAPE;
+    if (!aligned16(act_scale) ||
+        (work && (!aligned16(xq) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) ||
+                  (acc_out && !aligned16(acc_out)))))
+        return SQ_ERR_ALIGN;
+    return hip_status(sqk::gemm_fp8(xq, wq, m, n, k, act_scale, w_scale, y, yt, acc_out, stream));
+}
+
 sq_status sq_calib_percentile_workspace(sq_dtype xt, int64_t k, size_t* bytes) {
     if (!bytes) return SQ_ERR_NULL;
     if (!valid_dtype(xt)) return SQ_ERR_DTYPE;

@@ -46,6 +46,18 @@ __device__ __forceinline__ int q8(float v) {
     return (int)r;
 }
 
+// OCP FP8 E4M3 (bias 7, largest finite 448): four fp32 values, clamped to
+// [-448, 448], rounded to nearest even by v_cvt_pk_fp8_f32, one byte each
+// (a in the low byte).
+constexpr float kFp8Max = 448.0f;
+
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+    auto cl = [](float v) { return __builtin_fminf(__builtin_fmaxf(v, -kFp8Max), kFp8Max); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+    return (uint32_t)w;
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
     return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
            ((uint32_t)(d & 0xff) << 24);

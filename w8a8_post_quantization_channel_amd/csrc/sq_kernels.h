@@ -65,6 +65,17 @@ hipError_t gemm_dequant(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n
                         const float* act_scale, const float* w_scale, void* y, int yt, int32_t* acc_out,
                         hipStream_t stream);
 
+// FP8 (OCP E4M3) variant: act scale over 448, e4m3 weight and activation
+// codes, the e4m3 x e4m3 -> fp32 product with the same dequant epilogue
+hipError_t act_scale_fp8(const float* act_max, const float* inv_s, int64_t k, float* act_scale,
+                         hipStream_t stream);
+hipError_t quant_weight_fp8(const void* w, int wt, int64_t n, int64_t k, const float* s, uint8_t* wq,
+                            float* w_scale, hipStream_t stream);
+hipError_t quant_act_fp8(const void* x, int xt, int64_t m, int64_t k, const float* inv_s, const float* act_scale,
+                         uint8_t* xq, hipStream_t stream);
+hipError_t gemm_fp8(const uint8_t* xq, const uint8_t* wq, int64_t m, int64_t n, int64_t k, const float* act_scale,
+                    const float* w_scale, void* y, int yt, float* acc_out, hipStream_t stream);
+
 // Block tile (rows, columns) the GEMM uses for an m x n output.
 void gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n);
 

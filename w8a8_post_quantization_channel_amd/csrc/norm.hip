@@ -11,6 +11,7 @@
 // the reduction and the output pass up to 256 * 8 16-byte vectors per row
 // (16384 bf16 or 8192 fp32 values); longer rows are read a second time
 // (from L2).
+#include <algorithm>
 #include <type_traits>
 
 #include "sq_device.h"
@@ -41,11 +42,13 @@ template <int E>
 __device__ __forceinline__ double sum_sq(const u32x4& v) {
     float e[E];
     widen<E>(v, e);
+    // d * d is exact in fp64 (at most 48 significant bits), so the fused
+    // multiply-add rounds exactly where a product followed by a sum would
     double s = 0.0;
 #pragma unroll
     for (int i = 0; i < E; ++i) {
         const double d = (double)e[i];
-        s += d * d;
+        s = __fma_rn(d, d, s);
     }
     return s;
 }
@@ -88,14 +91,27 @@ __device__ __forceinline__ void emit(const u32x4& v, float r, const float (&g)[E
         else
             *(sqd::u32x2*)((uint16_t*)out + idx) = sqd::u32x2{w[0], w[1]};
     } else {
-        int q[E];
+        // clamp to [-127, 127], then round half to even with the fp32 adder:
+        // for |v| < 2^22, fl(v + 1.5 * 2^23) = rint(v) + 1.5 * 2^23 and the low
+        // byte of its bits is rint(v) as an int8 (rint and the integer-bounded
+        // clamp commute, so this equals clamp(rint(v)))
+        uint32_t b[E];
 #pragma unroll
-        for (int i = 0; i < E; ++i) q[i] = sqd::q8(__fmul_rn(y[i], inv_a));
+        for (int i = 0; i < E; ++i) {
+            const float v = __builtin_fminf(__builtin_fmaxf(__fmul_rn(y[i], inv_a), -sqd::kQmax), sqd::kQmax);
+            b[i] = __float_as_uint(__fadd_rn(v, 12582912.0f));
+        }
+        uint32_t w[E / 4];
+#pragma unroll
+        for (int d = 0; d < E / 4; ++d) {
+            const uint32_t lo = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0c0c0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0c0c0400u);
+            w[d] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
         if constexpr (E == 8)
-            *(sqd::u32x2*)((int8_t*)out + idx) = sqd::u32x2{sqd::pack4_i8(q[0], q[1], q[2], q[3]),
-                                                             sqd::pack4_i8(q[4], q[5], q[6], q[7])};
+            *(sqd::u32x2*)((int8_t*)out + idx) = sqd::u32x2{w[0], w[1]};
         else
-            *(uint32_t*)((int8_t*)out + idx) = sqd::pack4_i8(q[0], q[1], q[2], q[3]);
+            *(uint32_t*)((int8_t*)out + idx) = w[0];
     }
 }
 
@@ -172,11 +188,121 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const u32x4* __re
     }
 }
 
+// Persistent form of the register-resident kernel: a block walks groups of
+// R rows g, g + grid, ... and issues the loads of its next group before it
+// reduces and writes the current one, so every thread keeps R * VPT 16-byte
+// loads in flight through the reduction, the barrier and the stores. A
+// thread's columns are the same in every row, so their weights are loaded
+// once (reloading them per row costs more load traffic than the row itself).
+// The LDS partials alternate between two buffers: one barrier per group.
+template <int EB, int VPT, int R, NormOut OUT>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_stream_kernel(const u32x4* __restrict__ h, int64_t m,
+                                                                      int64_t kvec, int64_t k,
+                                                                      const float* __restrict__ gamma, float eps,
+                                                                      const float* __restrict__ act_scale,
+                                                                      void* __restrict__ out,
+                                                                      float* __restrict__ r_out) {
+    constexpr int E = 16 / EB;
+    static_assert(VPT > 0, "register-resident rows only");
+    __shared__ double red[2][R][kNormWaves];
+    const int tid = threadIdx.x;
+    const int64_t groups = (m + R - 1) / R;
+    const float inv_a = OUT == kOutI8 ? __fdiv_rn(1.0f, act_scale[0]) : 0.0f;
+    auto load = [&](int64_t g, u32x4 (&buf)[R][VPT]) {
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const int64_t row = g * R + q;
+            const bool ok = g < groups && row < m;
+            const u32x4* hr = h + (ok ? row : 0) * kvec;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int64_t c = tid + (int64_t)i * kNormThreads;
+                buf[q][i] = (ok && c < kvec) ? __builtin_nontemporal_load(hr + c) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    // the block's columns are the same for every row: their weights stay in registers
+    float gm[VPT][E];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int64_t c = tid + (int64_t)i * kNormThreads;
+        if (c < kvec)
+            load_gamma<E>(gamma, c, gm[i]);
+        else
+#pragma unroll
+            for (int e = 0; e < E; ++e) gm[i][e] = 0.0f;
+    }
+    auto process = [&](int64_t g, const u32x4 (&buf)[R][VPT], int par) {
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            double ss = 0.0;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) ss += sum_sq<E>(buf[q][i]);
+            ss = wave_sum_f64(ss);
+            if ((tid & 63) == 0) red[par][q][tid >> 6] = ss;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const int64_t row = g * R + q;
+            if (row >= m) break;
+            double total = red[par][q][0];
+#pragma unroll
+            for (int w = 1; w < kNormWaves; ++w) total += red[par][q][w];
+            const float r = (float)(1.0 / sqrt(total / (double)k + (double)eps));
+            if (r_out && tid == 0) r_out[row] = r;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int64_t c = tid + (int64_t)i * kNormThreads;
+                if (c < kvec) emit<E, OUT>(buf[q][i], r, gm[i], inv_a, out, row * k + c * E);
+            }
+        }
+    };
+    u32x4 a[R][VPT], b[R][VPT];
+    const int64_t step = gridDim.x;
+    int64_t g = blockIdx.x;
+    load(g, a);
+    // groups in pairs: the loads of the next group go out before each group is processed
+    for (; g < groups; g += 2 * step) {
+        load(g + step, b);
+        process(g, a, 0);
+        if (g + step >= groups) break;
+        load(g + 2 * step, a);
+        process(g + step, b, 1);
+    }
+}
+
+int norm_cus() {
+    static int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        return n;
+    }();
+    return cus;
+}
+
 template <int EB, int VPT, int R, NormOut OUT>
 hipError_t launch_rows(const void* h, int64_t m, int64_t kvec, int64_t k, const float* gamma, float eps,
                        const float* act_scale, void* out, float* r_out, hipStream_t stream) {
-    rmsnorm_kernel<EB, VPT, R, OUT><<<dim3((unsigned)((m + R - 1) / R)), dim3(kNormThreads), 0, stream>>>(
-        (const u32x4*)h, m, kvec, k, gamma, eps, act_scale, out, r_out);
+    const int64_t groups = (m + R - 1) / R;
+    if constexpr (VPT > 0) {
+        // as many blocks as are resident at once (all groups dealt out evenly)
+        static const int per_cu = [] {
+            int b = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, rmsnorm_stream_kernel<EB, VPT, R, OUT>,
+                                                             kNormThreads, 0) != hipSuccess || b < 1)
+                b = 1;
+            return b;
+        }();
+        const int64_t grid = std::min<int64_t>(groups, (int64_t)per_cu * norm_cus());
+        rmsnorm_stream_kernel<EB, VPT, R, OUT><<<dim3((unsigned)grid), dim3(kNormThreads), 0, stream>>>(
+            (const u32x4*)h, m, kvec, k, gamma, eps, act_scale, out, r_out);
+    } else {
+        rmsnorm_kernel<EB, VPT, R, OUT><<<dim3((unsigned)groups), dim3(kNormThreads), 0, stream>>>(
+            (const u32x4*)h, m, kvec, k, gamma, eps, act_scale, out, r_out);
+    }
     return hipGetLastError();
 }
 

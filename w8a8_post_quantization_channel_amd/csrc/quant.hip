@@ -322,10 +322,29 @@ __global__ __launch_bounds__(kActThreads) void quant_act_kernel(const u32x4* __r
             else
                 *(uint32_t*)dst = sqd::pack4_e4m3(t[0], t[1], t[2], t[3]);
         } else {
-            int q[E];
+            // clamp to [-127, 127], then round half to even with the fp32
+            // adder (fl(v + 1.5 * 2^23) keeps rint(v) in its low byte for
+            // |v| < 2^22; rint and the integer-bounded clamp commute, so this
+            // is clamp(rint(v))), and gather the low bytes with v_perm
+            uint32_t b[E];
 #pragma unroll
-            for (int t = 0; t < E; ++t) q[t] = sqd::q8(__fmul_rn(__fmul_rn(e[t], is[t]), inv_a));
-            store_codes<E>(xq + (r * kvec + v) * E, q);
+            for (int t = 0; t < E; ++t) {
+                const float q = __builtin_fminf(
+                    __builtin_fmaxf(__fmul_rn(__fmul_rn(e[t], is[t]), inv_a), -sqd::kQmax), sqd::kQmax);
+                b[t] = __float_as_uint(__fadd_rn(q, 12582912.0f));
+            }
+            uint32_t w[E / 4];
+#pragma unroll
+            for (int d = 0; d < E / 4; ++d) {
+                const uint32_t lo = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0c0c0400u);
+                const uint32_t hi = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0c0c0400u);
+                w[d] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            }
+            int8_t* dst = xq + (r * kvec + v) * E;
+            if constexpr (E == 8)
+                *(sqd::u32x2*)dst = sqd::u32x2{w[0], w[1]};
+            else
+                *(uint32_t*)dst = w[0];
         }
     };
     int64_t r = r0 + wave;

@@ -292,7 +292,7 @@ constexpr int kPctThreads = 1024;  // 16 waves over interleaved rows
 constexpr int kPctChannels = 64;   // one channel per lane
 constexpr int kPctBins = 256;
 constexpr int kPctStride = kPctBins + 1;  // LDS row stride: lane l's bin d sits in bank (l + d) % 64
-constexpr int kPctUnroll = 8;
+constexpr int kPctUnroll = 16;
 
 template <int EB>
 struct PctKey {
@@ -328,8 +328,12 @@ __global__ __launch_bounds__(kPctThreads) void pct_hist_kernel(const void* __res
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
     const int64_t r1 = min(rows, r0 + rows_per_block);
     constexpr int W = kPctThreads / 64;
+    // branch-free: keys outside the selected prefix are counted in the row's
+    // pad word (index 256, never read), one bank per lane, so the many
+    // non-matching keys of the later passes cause no bank conflicts
     auto count = [&](uint32_t key) {
-        if (PASS == 0 || (key >> HI) == pre) atomicAdd(&h[lane * kPctStride + ((key >> LO) & DMASK)], 1u);
+        const uint32_t bin = (PASS == 0 || (key >> HI) == pre) ? ((key >> LO) & DMASK) : (uint32_t)kPctBins;
+        atomicAdd(&h[lane * kPctStride + bin], 1u);
     };
     int64_t r = r0 + wave;
     for (; r + W * (kPctUnroll - 1) < r1; r += W * kPctUnroll) {

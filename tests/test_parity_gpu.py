@@ -182,7 +182,10 @@ def test_quant_act_ties():
 
 GEMM_CASES = [(1, 16, 64), (5, 48, 1088), (129, 257, 320), (300, 600, 2048), (512, 8192, 128),
               (1024, 8192, 256), (2100, 4112, 192), (2048, 7168, 64), (2048, 11008, 128), (4096, 4096, 64),
-              (4000, 4100, 64), (1000, 11008, 320)]
+              (4000, 4100, 64), (1000, 11008, 320),
+              # decode widths: 17-32 and 33-64 rows, 8-wave blocks (>= 512 column blocks) and
+              # 16-wave blocks, K steps not a multiple of waves x steps in flight
+              (24, 8200, 192), (17, 1000, 4160), (40, 8192, 320), (64, 300, 704), (9, 8208, 1344)]
 
 
 def reachable_tilings():

@@ -718,22 +718,19 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
 // ---- skinny kernel (decode: m <= 64) -------------------------------------------
 //
 // The product is bound by streaming the int8 weight once from HBM. A block of
-// eight waves owns 16 output columns (16 weight rows) and all of K; wave w
-// takes every eighth 64-byte K step, so the eight waves read disjoint parts
-// of the same rows and their int32 partials are summed in LDS in a fixed
-// order (exact). v_mfma_i32_16x16x64_i8 with the m rows padded to 16 (MT
+// W waves owns 16 output columns (16 weight rows) and all of K; wave w takes
+// every W-th 64-byte K step, so the waves read disjoint parts of the same
+// rows and their int32 partials are summed in LDS in a fixed order (exact). v_mfma_i32_16x16x64_i8 with the m rows padded to 16 (MT
 // tiles of 16 rows): lane l holds row l % 16 and bytes 16 (l / 16) .. +15 of
 // a 64-byte K step, for both operands. Weight rows past n and activation rows
 // past m are clamped to the last valid row: their outputs are never stored.
 // Each lane keeps U K steps of weight bytes in flight.
 
-constexpr int kSkinnyWaves = 8;
-
-template <int MT, int U, class Epi>
-__global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(const int8_t* __restrict__ A,
-                                                                      const int8_t* __restrict__ B, int64_t M,
-                                                                      int64_t N, int64_t Kb, Epi epi) {
-    __shared__ v4i part[kSkinnyWaves][MT][64];
+template <int W, int MT, int U, class Epi>
+__global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(const int8_t* __restrict__ A,
+                                                             const int8_t* __restrict__ B, int64_t M, int64_t N,
+                                                             int64_t Kb, Epi epi) {
+    __shared__ v4i part[W][MT][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t n0 = (int64_t)blockIdx.x * 16;
     const int64_t brow = min<int64_t>(n0 + (lane & 15), N - 1);
@@ -748,28 +745,24 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(const in
     for (int t = 0; t < MT; ++t) acc[t] = v4i{0, 0, 0, 0};
 
     const int64_t nsteps = Kb / 64;
-    // K steps of this wave: wave, wave + 8, wave + 16, ...
-    int64_t st = wave;
-    for (; st + (int64_t)kSkinnyWaves * (U - 1) < nsteps; st += (int64_t)kSkinnyWaves * U) {
+    // K steps of this wave: wave, wave + W, wave + 2W, ..., U of them in flight
+    // per batch; in the last batch steps past the end load nothing and add
+    // zeros, so a ragged remainder is not walked one latency at a time
+    for (int64_t st = wave; st < nsteps; st += (int64_t)W * U) {
         v4i b[U], a[U][MT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t off = (st + (int64_t)u * kSkinnyWaves) * 64;
-            b[u] = __builtin_nontemporal_load((const v4i*)(bp + off));
+            const int64_t su = st + (int64_t)u * W;
+            const int64_t off = su * 64;
+            const bool in = su < nsteps;
+            b[u] = in ? __builtin_nontemporal_load((const v4i*)(bp + off)) : v4i{0, 0, 0, 0};
 #pragma unroll
-            for (int t = 0; t < MT; ++t) a[u][t] = *(const v4i*)(ap[t] + off);
+            for (int t = 0; t < MT; ++t) a[u][t] = in ? *(const v4i*)(ap[t] + off) : v4i{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int t = 0; t < MT; ++t) acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][t], b[u], acc[t], 0, 0, 0);
-    }
-    for (; st < nsteps; st += kSkinnyWaves) {
-        const int64_t off = st * 64;
-        const v4i b = __builtin_nontemporal_load((const v4i*)(bp + off));
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(*(const v4i*)(ap[t] + off), b, acc[t], 0, 0, 0);
     }
 
 #pragma unroll
@@ -781,7 +774,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(const in
         for (int t = 0; t < MT; ++t) {
             v4i sum = part[0][t][lane];
 #pragma unroll
-            for (int w = 1; w < kSkinnyWaves; ++w) sum += part[w][t][lane];
+            for (int w = 1; w < W; ++w) sum += part[w][t][lane];
             // 16x16 accumulator: lane holds column lane % 16, rows 4 (lane / 16) + v
             epi.template tile<16>(sum, 16 * t + 4 * (lane >> 4), n0 + (lane & 15));
         }
@@ -875,12 +868,19 @@ hipError_t launch_dma(const int8_t* A, const int8_t* B, int64_t M, int64_t N, in
     return hipGetLastError();
 }
 
+// A column block of 16 outputs holds W waves splitting K. Few column blocks
+// (n below two per compute unit, e.g. a down projection) get 16 waves so each
+// compute unit still keeps enough weight bytes in flight; otherwise 8 waves,
+// and several blocks share a compute unit.
 template <int MT, class Epi>
 hipError_t launch_skinny(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t Kb, Epi epi,
                          hipStream_t stream) {
     constexpr int U = MT == 1 ? 8 : 4;
-    gemm_skinny_kernel<MT, U, Epi>
-        <<<dim3((unsigned)((N + 15) / 16)), dim3(64 * kSkinnyWaves), 0, stream>>>(A, B, M, N, Kb, epi);
+    const unsigned blocks = (unsigned)((N + 15) / 16);
+    if (blocks < 2 * (unsigned)cu_count())
+        gemm_skinny_kernel<16, MT, U, Epi><<<dim3(blocks), dim3(64 * 16), 0, stream>>>(A, B, M, N, Kb, epi);
+    else
+        gemm_skinny_kernel<8, MT, U, Epi><<<dim3(blocks), dim3(64 * 8), 0, stream>>>(A, B, M, N, Kb, epi);
     return hipGetLastError();
 }
 

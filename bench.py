@@ -50,6 +50,15 @@ def parse():
     ap.add_argument("--overlap", action="store_true",
                     help="run the preparation chain on a second stream, overlapping the GEMMs (default: one "
                          "stream; overlapping shortens the step a little but slows the GEMMs it runs beside)")
+    ap.add_argument("--ramp-seconds", type=float, default=0.5,
+                    help="untimed steps for at least this long before the warm-up steps: after the host-side "
+                         "setup the GPU needs a few hundred ms of sustained load before its step time settles")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="bracket the GEMM launches with HIP events on every n-th timed step (each event pair "
+                         "costs a few microseconds of step time)")
+    ap.add_argument("--per-projection", action="store_true",
+                    help="prepare the projections one by one with the single-form entry points (default: the "
+                         "batched entry points, one launch per kind of pass for the whole block)")
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="output rows of each GEMM the oracle computes in the CPU sample")
     ap.add_argument("--traffic", type=str, default=None,
@@ -90,25 +99,33 @@ def setup(device):
     return groups, projs
 
 
-def run_step(groups, projs, gemm_events=None, side=None):
+def run_step(groups, projs, gemm_events=None, side=None, batched=True):
     """One pass of the whole path. gemm_events: list to append (name, start,
     end) event pairs bracketing each GEMM launch, recorded on the stream the
     GEMM runs on. side: a second stream for the preparation chain (statistics,
     smoothing, weight and activation quantization), so that projection p + 1
     is prepared while the GEMM of projection p runs; each GEMM waits for its
-    own preparation, and the step starts after the previous step's GEMMs."""
+    own preparation, and the step starts after the previous step's GEMMs.
+    batched: the statistics (4 inputs + 7 weights), smoothing factors and
+    weight codes of all projections come from the batched entry points before
+    the first GEMM; otherwise they are made projection by projection."""
     import torch
     from w8a8_post_quantization_channel_amd import capi
+    from w8a8_post_quantization_channel_amd.layer import prepare_block
     main = torch.cuda.current_stream()
     prep = side if side is not None else main
     if side is not None:
         side.wait_stream(main)
     with torch.cuda.stream(prep):
-        for g in groups.values():
-            capi.sq_calib_absmax(g.x, g.act_max, False, stream=prep)
+        if batched:
+            prepare_block([layer for _, _, layer, _ in projs], [(g.x, g.act_max) for g in groups.values()], prep)
+        else:
+            for g in groups.values():
+                capi.sq_calib_absmax(g.x, g.act_max, False, stream=prep)
     for name, g, layer, _ in projs:
         with torch.cuda.stream(prep):
-            layer.prepare(stream=prep)
+            if not batched:
+                layer.prepare(stream=prep)
             xq = layer.quantize_input(g.x, stream=prep)
         if side is not None:
             main.wait_stream(prep)
@@ -581,15 +598,24 @@ def main():
     m = next(iter(groups.values())).x.shape[0]
     side = torch.cuda.Stream() if args.overlap else None  # default priority, like the main stream
 
+    batched = not args.per_projection
+    ramp_steps = 0
+    t_ramp = time.perf_counter()
+    while time.perf_counter() - t_ramp < args.ramp_seconds:
+        for _ in range(10):
+            run_step(groups, projs, side=side, batched=batched)
+        torch.cuda.synchronize()
+        ramp_steps += 10
     for _ in range(args.warmup):
-        run_step(groups, projs, side=side)
+        run_step(groups, projs, side=side, batched=batched)
     torch.cuda.synchronize()
 
     events = []
+    every = max(1, args.event_every)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run_step(groups, projs, events, side=side)
+    for i in range(args.steps):
+        run_step(groups, projs, events if i % every == 0 else None, side=side, batched=batched)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -614,7 +640,8 @@ def main():
                 "avg_launch_us": avg_launch_ms * 1e3,
                 "per_projection_tops": {n: ops_by_name[n] / (sum(v) / len(v) * 1e-3) / 1e12
                                         for n, v in by_name.items()}}
-    gemm_share = sum(gemm_ms) / (elapsed * 1e3)
+    sampled_steps = (args.steps + every - 1) // every
+    gemm_share = sum(gemm_ms) / sampled_steps / ms_per_step
 
     out = {
         "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
@@ -626,9 +653,13 @@ def main():
                    "tokens": m, "alpha": 0.5, "in_dtype": "bf16", "out_dtype": "bf16",
                    "projections": {n: [layer.n, layer.k] for n, _, layer, _ in projs},
                    "step": "calib absmax + weight absmax + smoothing + weight quant + act quant + int8 GEMM",
+                   "preparation": "per projection" if args.per_projection else
+                   "batched over the 7 projections (statistics, smoothing, weight codes)",
                    "schedule": "two streams: GEMM of projection p overlaps the preparation of projection p + 1"
                    if args.overlap else "one stream"},
         "roofline": roofline,
+        "ramp_steps": ramp_steps,
+        "gemm_events": f"every {every}th timed step ({len(events)} GEMM launches bracketed)",
         "gemm_share_of_step": gemm_share,
         "gpu": torch.cuda.get_device_name(0),
     }

@@ -288,6 +288,48 @@ sq_status sq_alpha_search(const void* const* x_batches, sq_dtype xt, int n_batch
                           void* workspace, size_t workspace_bytes, double* mse,
                           int* best, hipStream_t stream);
 
+/*
+ * Batched forms, for the several projections of one transformer block
+ * (q, k, v, o, gate, up, down): item i of every per-item array describes one
+ * call of the single form above (same arguments, same rules), and the results
+ * are bit-for-bit those of calling the single form once per item. They exist
+ * to cut launches: the items share one pass of each kernel instead of one
+ * short launch apiece, so the ramp and drain of a launch are paid once.
+ *   count       1 <= count <= SQ_MAX_BATCH (SQ_ERR_SHAPE otherwise)
+ *   arrays      every per-item array is a (host) array of count entries;
+ *               the pointers in them are device pointers as in the single form
+ *   outputs     no item's output range may overlap another item's input or
+ *               output range (SQ_ERR_SHAPE); inputs may be shared (q, k and v
+ *               read one statistic)
+ *   validation  every item is checked as the single form would check it, in
+ *               item order, before anything is launched; the first failure is
+ *               returned and nothing is written
+ *
+ * sq_calib_absmax_batched [kwkr §3.1; ADR Layer 2]: absmax[i] = column max of
+ *   |x[i]| ([rows[i], k[i]] of type xt[i]); accumulate applies to every item.
+ *   One zero fill (overwrite form) and one reduction launch.
+ * sq_smooth_factors_batched [kwkr §2.2; ADR Key design items 1, 3]: s[i],
+ *   inv_s[i], act_scale[i] from act_max[i], w_max[i] with alpha[i]. Two launches.
+ * sq_quant_weight_batched [kwkr §3.2, §3.3; ADR Context item 3]: wq[i],
+ *   w_scale[i] from w[i] ([n[i], k[i]] of type wt[i]) and s[i]. One launch per
+ *   distinct (element type, row-length class) among the items; the 13B block's
+ *   seven weights take two.
+ */
+#define SQ_MAX_BATCH 16
+
+sq_status sq_calib_absmax_batched(int count, const void* const* x, const sq_dtype* xt,
+                                  const int64_t* rows, const int64_t* k, float* const* absmax,
+                                  int accumulate, hipStream_t stream);
+
+sq_status sq_smooth_factors_batched(int count, const float* const* act_max,
+                                    const float* const* w_max, const int64_t* k,
+                                    const float* alpha, float* const* s, float* const* inv_s,
+                                    float* const* act_scale, hipStream_t stream);
+
+sq_status sq_quant_weight_batched(int count, const void* const* w, const sq_dtype* wt,
+                                  const int64_t* n, const int64_t* k, const float* const* s,
+                                  int8_t* const* wq, float* const* w_scale, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* sq_status_string(sq_status status);
 

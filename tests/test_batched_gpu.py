@@ -1,0 +1,149 @@
+"""GPU parity of the batched entry points (several projections per call)
+against the CPU oracle item by item, and against the single-call path on the
+seven projections of a Llama-2-13B block. Bar: bit-exact (statistics, smoothing
+factors, scales and int8 codes are all exact or single-rounded values)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle.oracle import Oracle
+from tests.gpu_pipeline import assert_bitexact, dev
+from w8a8_post_quantization_channel_amd import capi, synth
+
+pytestmark = pytest.mark.gpu
+ORACLE = Oracle()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    capi.load()
+
+
+def _t(a):
+    return synth.to_torch(a, dev())
+
+
+def _h(t):
+    return synth.from_torch(t)
+
+
+# (rows, k, bf16): mixed element types, a zero-row item, ragged rows, K from 64 to 13824
+ABS_ITEMS = [(300, 1088, True), (0, 256, True), (2048, 5120, True), (7, 64, False), (513, 13824, True),
+             (96, 320, False), (1, 4096, True)]
+
+
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_absmax_batched(accumulate):
+    import torch
+    xs = [synth.activations(4000 + i, r, k, synth.outlier_channels(4100 + i, k), bf16=b)
+          for i, (r, k, b) in enumerate(ABS_ITEMS)]
+    g = synth.rng(4200)
+    prev = [g.uniform(0.0, 3.0, k).astype(np.float32) for _, k, _ in ABS_ITEMS]
+    outs = [_t(p) if accumulate else torch.full((k,), 9.0, dtype=torch.float32, device=dev())
+            for p, (_, k, _) in zip(prev, ABS_ITEMS)]
+    capi.sq_calib_absmax_batched([_t(x) for x in xs], outs, accumulate)
+    torch.cuda.synchronize()
+    for i, (x, o) in enumerate(zip(xs, outs)):
+        ref = ORACLE.calib_absmax(x, prev[i].copy() if accumulate else None)
+        assert_bitexact(f"absmax item {i}", _h(o), ref)
+
+
+# (k, alpha): q, k and v share one statistic; a K of 64 and one of 13824
+SMOOTH_ITEMS = [(5120, 0.5, 0), (5120, 0.75, 0), (5120, 0.25, 0), (64, 1.0, 1), (13824, 0.5, 2), (1088, 0.0, 3)]
+
+
+def test_smooth_factors_batched():
+    import torch
+    g = synth.rng(4300)
+    stats = {}
+    for k, _, grp in SMOOTH_ITEMS:
+        if grp not in stats:
+            am = g.uniform(0.01, 60.0, k).astype(np.float32)
+            am[g.integers(0, k, 3)] = 0.0  # floored channels
+            stats[grp] = am
+    act_max = {grp: _t(v) for grp, v in stats.items()}
+    w_max = [g.uniform(0.001, 2.0, k).astype(np.float32) for k, _, _ in SMOOTH_ITEMS]
+    f32 = dict(dtype=torch.float32, device=dev())
+    ss = [torch.empty(k, **f32) for k, _, _ in SMOOTH_ITEMS]
+    inv = [torch.empty(k, **f32) for k, _, _ in SMOOTH_ITEMS]
+    sc = [torch.empty(4, **f32) for _ in SMOOTH_ITEMS]
+    capi.sq_smooth_factors_batched([act_max[grp] for _, _, grp in SMOOTH_ITEMS], [_t(w) for w in w_max],
+                                   [a for _, a, _ in SMOOTH_ITEMS], ss, inv, sc)
+    torch.cuda.synchronize()
+    for i, (k, alpha, grp) in enumerate(SMOOTH_ITEMS):
+        rs, ri, ra = ORACLE.smooth_factors(stats[grp], w_max[i], alpha)
+        assert_bitexact(f"s item {i}", _h(ss[i]), rs)
+        assert_bitexact(f"inv_s item {i}", _h(inv[i]), ri)
+        assert_bitexact(f"act_scale item {i}", _h(sc[i])[:1], np.array([ra], np.float32))
+
+
+# (n, k, bf16): every row-length class of the stream kernel (rows of 64 .. 65536 bf16
+# values), the long-row kernel, several items per class in one launch, ragged row counts
+QW_ITEMS = [(37, 1024, True), (300, 5120, True), (5, 5120, True), (129, 13824, True), (8, 2048, False),
+            (33, 4096, True), (3, 10240, False), (2, 16384, True), (17, 32768, True), (3, 70016, True),
+            (1, 64, True), (64, 1088, True), (9, 640, False), (11, 8192, True), (7, 11008, True),
+            (5, 12288, True)]
+
+
+def test_quant_weight_batched():
+    import torch
+    ws, ss = [], []
+    for i, (n, k, b) in enumerate(QW_ITEMS):
+        w = synth.weights(4400 + i, n, k, std=1.0, bf16=False)
+        w[0, min(7, k - 1)] = 300.0  # a large element in the first row
+        if n > 2:
+            w[n - 1] = 0.0  # a zero row (scale at the floor)
+        ws.append(synth.to_bf16_bits(w) if b else w)
+        ss.append(synth.rng(4500 + i).uniform(0.1, 10.0, k).astype(np.float32))
+    wqs = [torch.empty((n, k), dtype=torch.int8, device=dev()) for n, k, _ in QW_ITEMS]
+    wsc = [torch.empty(n, dtype=torch.float32, device=dev()) for n, _, _ in QW_ITEMS]
+    capi.sq_quant_weight_batched([_t(w) for w in ws], [_t(s) for s in ss], wqs, wsc)
+    torch.cuda.synchronize()
+    for i in range(len(QW_ITEMS)):
+        rq, rs = ORACLE.quant_weight(ws[i], ss[i])
+        assert_bitexact(f"wq item {i}", _h(wqs[i]), rq)
+        assert_bitexact(f"w_scale item {i}", _h(wsc[i]), rs)
+
+
+def test_block_prepare_batched_equals_single_calls():
+    """The 13B block's statistics, smoothing factors and weight codes from the
+    batched calls equal those of one single-form call per projection."""
+    import torch
+    f32 = dict(dtype=torch.float32, device=dev())
+    groups = {g: _t(synth.c2_group_x(g, rows=512)) for g in synth.C2_GROUPS}
+    projs = [(p, g, _t(synth.c2_projection_w(p))) for p, g, *_ in synth.C2_PROJECTIONS]
+
+    def buffers():
+        am = {g: torch.empty(x.shape[1], **f32) for g, x in groups.items()}
+        per = []
+        for _, g, w in projs:
+            n, k = w.shape
+            per.append(dict(w_max=torch.empty(k, **f32), s=torch.empty(k, **f32), inv_s=torch.empty(k, **f32),
+                            a=torch.empty(4, **f32), wq=torch.empty((n, k), dtype=torch.int8, device=dev()),
+                            ws=torch.empty(n, **f32)))
+        return am, per
+
+    am1, per1 = buffers()
+    for g, x in groups.items():
+        capi.sq_calib_absmax(x, am1[g])
+    for (_, g, w), b in zip(projs, per1):
+        capi.sq_calib_absmax(w, b["w_max"])
+        capi.sq_smooth_factors(am1[g], b["w_max"], 0.5, b["s"], b["inv_s"], b["a"])
+        capi.sq_quant_weight(w, b["s"], b["wq"], b["ws"])
+
+    am2, per2 = buffers()
+    gl = list(groups)
+    capi.sq_calib_absmax_batched([groups[g] for g in gl] + [w for _, _, w in projs],
+                                 [am2[g] for g in gl] + [b["w_max"] for b in per2])
+    capi.sq_smooth_factors_batched([am2[g] for _, g, _ in projs], [b["w_max"] for b in per2], [0.5] * len(projs),
+                                   [b["s"] for b in per2], [b["inv_s"] for b in per2], [b["a"] for b in per2])
+    capi.sq_quant_weight_batched([w for _, _, w in projs], [b["s"] for b in per2], [b["wq"] for b in per2],
+                                 [b["ws"] for b in per2])
+    torch.cuda.synchronize()
+    for g in gl:
+        assert torch.equal(am1[g], am2[g]), g
+    for (p, _, _), b1, b2 in zip(projs, per1, per2):
+        for key in ("w_max", "s", "inv_s", "wq", "ws"):
+            assert torch.equal(b1[key], b2[key]), (p, key)
+        assert torch.equal(b1["a"][:1], b2["a"][:1]), (p, "act_scale")

@@ -312,3 +312,76 @@ def test_fp8_validation(lib):
     a = list(base)
     a[3] = 0
     assert h(*a) == OK
+
+
+def _arr(ctype, values):
+    a = (ctype * len(values))(*values)
+    return a, ctypes.cast(a, P)
+
+
+def test_batched_validation(lib):
+    for name in ("sq_calib_absmax_batched", "sq_smooth_factors_batched", "sq_quant_weight_batched"):
+        assert name in capi.declared_functions() and hasattr(lib, name)
+    B = 0x100000  # a second fake address, 1 MiB past A
+    i64, i32, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_float
+
+    # absmax: two bf16 inputs of 16 x 1024
+    def absmax(count, xs, dts, rows, ks, outs, acc=0):
+        keep = [_arr(P, xs), _arr(i32, dts), _arr(i64, rows), _arr(i64, ks), _arr(P, outs)]
+        return lib.sq_calib_absmax_batched(count, *[p for _, p in keep], acc, None)
+
+    good = ([A, B], [1, 1], [16, 16], [1024, 1024], [A + 0x40000, B + 0x40000])
+    assert lib.sq_calib_absmax_batched(2, None, None, None, None, None, 0, None) == NULL
+    assert absmax(0, *good) == SHAPE
+    assert absmax(17, *[v * 9 for v in good]) == SHAPE
+    bad = [list(v) for v in good]
+    bad[1][1] = 7  # item 1: dtype
+    assert absmax(2, *bad) == DTYPE
+    bad = [list(v) for v in good]
+    bad[3][0] = 1000  # item 0: k
+    bad[4][1] = MIS   # item 1: misaligned (item 0 fails first)
+    assert absmax(2, *bad) == SHAPE
+    bad = [list(v) for v in good]
+    bad[4][1] = bad[4][0] + 16  # outputs of items 0 and 1 overlap
+    assert absmax(2, *bad) == SHAPE
+    bad = [list(v) for v in good]
+    bad[4][1] = A + 64  # item 1 writes into item 0's input
+    assert absmax(2, *bad) == SHAPE
+    # zero rows into running maxima: nothing to launch
+    assert absmax(2, [0, 0], [1, 1], [0, 0], [1024, 1024], good[4], acc=1) == OK
+
+    # smoothing: outputs of two items overlapping, alpha of item 1 invalid
+    def smooth(count, am, wm, ks, al, s, inv, sc):
+        keep = [_arr(P, am), _arr(P, wm), _arr(i64, ks), _arr(f32, al), _arr(P, s), _arr(P, inv), _arr(P, sc)]
+        return lib.sq_smooth_factors_batched(count, *[p for _, p in keep], None)
+
+    sg = ([A, A], [A + 0x1000, A + 0x2000], [256, 256], [0.5, 0.5], [B, B + 0x1000], [B + 0x2000, B + 0x3000],
+          [B + 0x4000, B + 0x4010])
+    assert lib.sq_smooth_factors_batched(2, *([None] * 7), None) == NULL
+    bad = [list(v) for v in sg]
+    bad[3][1] = 1.5
+    assert smooth(2, *bad) == ALPHA
+    bad = [list(v) for v in sg]
+    bad[6][1] = bad[6][0]  # both items write one act_scale
+    assert smooth(2, *bad) == SHAPE
+    bad = [list(v) for v in sg]
+    bad[4][1] = A  # item 1's s over the shared statistic act_max
+    assert smooth(2, *bad) == SHAPE
+
+    # weight quant
+    def qw(count, w, wt, n, ks, s, wq, wsc):
+        keep = [_arr(P, w), _arr(i32, wt), _arr(i64, n), _arr(i64, ks), _arr(P, s), _arr(P, wq), _arr(P, wsc)]
+        return lib.sq_quant_weight_batched(count, *[p for _, p in keep], None)
+
+    qg = ([A, A + 0x10000], [1, 1], [8, 8], [1024, 1024], [B, B], [B + 0x1000, B + 0x4000], [B + 0x8000, B + 0x8100])
+    assert lib.sq_quant_weight_batched(2, *([None] * 7), None) == NULL
+    bad = [list(v) for v in qg]
+    bad[2][1] = -1
+    assert qw(2, *bad) == SHAPE
+    bad = [list(v) for v in qg]
+    bad[5][1] = bad[5][0] + 8192  # 8 x 1024 codes of item 0 end exactly where item 1's start: no overlap ...
+    bad[6][1] = bad[6][0] + 16    # ... but the w_scale ranges (32 bytes each) overlap
+    assert qw(2, *bad) == SHAPE
+    bad = [list(v) for v in qg]
+    bad[4][1] = MIS
+    assert qw(2, *bad) == ALIGN

@@ -50,7 +50,8 @@ def _smoothing(x, w, alpha=0.5):
 
 
 @pytest.mark.parametrize("n,k,bf16", [(40, 320, True), (300, 1088, True), (257, 5120, True), (64, 13824, True),
-                                      (16, 66560, True), (33, 1024, False), (9, 40960, False)])
+                                      (16, 66560, True), (33, 1024, False), (9, 40960, False), (50, 4096, True),
+                                      (12, 8192, True), (20, 11008, True), (7, 32768, True)])
 def test_quant_weight_fp8(n, k, bf16):
     import torch
     w = synth.weights(700 + n, n, k, bf16=bf16)

@@ -125,7 +125,7 @@ def test_absmax_cases():
 @pytest.mark.parametrize("k,bf16", [(2048, True), (4096, True), (5120, True), (8192, True), (13824, True),
                                     (16384, True), (28672, True), (33792, True), (66560, True), (1024, False),
                                     (2560, False), (4096, False), (8192, False), (16384, False), (20480, False),
-                                    (40960, False), (66560, False)])
+                                    (40960, False), (66560, False), (11008, True), (6144, False)])
 def test_quant_weight_paths(k, bf16):
     import torch
     d = dev()

@@ -63,6 +63,9 @@ def _declare(lib):
         "sq_fp8_gemm": [P, P, i64, i64, i64, P, P, P, c.c_int, P, P],
         "sq_fold_norm_weight": [P, P, i64, P, P],
         "sq_rmsnorm_quant_act": [P, c.c_int, i64, i64, P, c.c_float, P, P, P, P],
+        "sq_calib_absmax_batched": [c.c_int, P, P, P, P, P, c.c_int, P],
+        "sq_smooth_factors_batched": [c.c_int, P, P, P, P, P, P, P, P],
+        "sq_quant_weight_batched": [c.c_int, P, P, P, P, P, P, P, P],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -182,6 +185,51 @@ def sq_alpha_search(x_batches, w, workspace, alphas=ALPHA_GRID, stream=None):
                                                      workspace.element_size(), ctypes.cast(mse, ctypes.c_void_p),
                                                      ctypes.byref(best), _stream(stream)))
     return list(mse), best.value
+
+
+def _host_array(ctype, values):
+    """A host array for a per-item argument of the batched entry points."""
+    arr = (ctype * len(values))(*values)
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def _ptrs(tensors, what: str):
+    return _host_array(ctypes.c_void_p, [_dev(t, f"{what}[{i}]").value for i, t in enumerate(tensors)])
+
+
+def sq_calib_absmax_batched(xs, absmaxes, accumulate: bool = False, stream=None):
+    """sq_calib_absmax over several inputs in one zero fill + one reduction launch."""
+    if len(xs) != len(absmaxes):
+        raise ValueError("xs and absmaxes differ in length")
+    keep = [_ptrs(xs, "xs"), _host_array(ctypes.c_int, [_dtype_code(x) for x in xs]),
+            _host_array(ctypes.c_int64, [x.shape[0] for x in xs]), _host_array(ctypes.c_int64, [x.shape[1] for x in xs]),
+            _ptrs(absmaxes, "absmaxes")]
+    _check("sq_calib_absmax_batched", load().sq_calib_absmax_batched(len(xs), *[a for _, a in keep],
+                                                                     int(bool(accumulate)), _stream(stream)))
+
+
+def sq_smooth_factors_batched(act_maxes, w_maxes, alphas, ss, inv_ss, act_scales, stream=None):
+    """sq_smooth_factors for several projections in two launches."""
+    count = len(act_maxes)
+    if not all(len(v) == count for v in (w_maxes, alphas, ss, inv_ss, act_scales)):
+        raise ValueError("per-item lists differ in length")
+    keep = [_ptrs(act_maxes, "act_maxes"), _ptrs(w_maxes, "w_maxes"),
+            _host_array(ctypes.c_int64, [t.shape[0] for t in act_maxes]),
+            _host_array(ctypes.c_float, [float(a) for a in alphas]), _ptrs(ss, "ss"), _ptrs(inv_ss, "inv_ss"),
+            _ptrs(act_scales, "act_scales")]
+    _check("sq_smooth_factors_batched", load().sq_smooth_factors_batched(count, *[a for _, a in keep],
+                                                                         _stream(stream)))
+
+
+def sq_quant_weight_batched(ws, ss, wqs, w_scales, stream=None):
+    """sq_quant_weight for several weights, one launch per row-length class."""
+    count = len(ws)
+    if not all(len(v) == count for v in (ss, wqs, w_scales)):
+        raise ValueError("per-item lists differ in length")
+    keep = [_ptrs(ws, "ws"), _host_array(ctypes.c_int, [_dtype_code(w) for w in ws]),
+            _host_array(ctypes.c_int64, [w.shape[0] for w in ws]), _host_array(ctypes.c_int64, [w.shape[1] for w in ws]),
+            _ptrs(ss, "ss"), _ptrs(wqs, "wqs"), _ptrs(w_scales, "w_scales")]
+    _check("sq_quant_weight_batched", load().sq_quant_weight_batched(count, *[a for _, a in keep], _stream(stream)))
 
 
 def _opt(t, what: str):

@@ -64,17 +64,16 @@ __device__ __forceinline__ uint32_t column_bits(const uint32_t* words, int c) {
 // flight per lane. The four wave partials meet in LDS; then every thread
 // merges whole columns so each atomic instruction covers consecutive
 // addresses. kPerChunk: each row chunk is one calibration sample and its
-// maxima are stored to row blockIdx.y of out (no atomics, no zero fill).
+// maxima are stored to row `chunk` of out (no atomics, no zero fill).
 template <int EB, bool kPerChunk>
-__global__ __launch_bounds__(kAbsThreads) void absmax_kernel(const u32x4* __restrict__ x, int64_t rows,
-                                                             int64_t kvec, int64_t k, int64_t rows_per_block,
-                                                             unsigned* __restrict__ out_bits) {
+__device__ __forceinline__ void absmax_block(const u32x4* __restrict__ x, int64_t rows, int64_t kvec, int64_t k,
+                                             int64_t rows_per_block, unsigned* __restrict__ out_bits,
+                                             int64_t strip, int64_t chunk, u32x4* part) {
     constexpr int E = 16 / EB;          // elements per 16-byte vector
     constexpr int COLS = 64 * E;        // columns per strip
-    __shared__ u32x4 part[kAbsThreads];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t v = (int64_t)blockIdx.x * 64 + lane;  // 16-byte column vector
-    const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+    const int64_t v = strip * 64 + lane;  // 16-byte column vector
+    const int64_t r0 = chunk * rows_per_block;
     const int64_t r1 = min(rows, r0 + rows_per_block);
     u32x4 m = u32x4{0u, 0u, 0u, 0u};
     if (v < kvec) {
@@ -96,7 +95,7 @@ __global__ __launch_bounds__(kAbsThreads) void absmax_kernel(const u32x4* __rest
     }
     part[threadIdx.x] = m;
     __syncthreads();
-    const int64_t col0 = (int64_t)blockIdx.x * COLS;
+    const int64_t col0 = strip * COLS;
 #pragma unroll
     for (int c = threadIdx.x; c < COLS; c += kAbsThreads) {
         if (col0 + c >= k) break;
@@ -108,10 +107,66 @@ __global__ __launch_bounds__(kAbsThreads) void absmax_kernel(const u32x4* __rest
             best = max(best, column_bits<EB>(words, c));
         }
         if constexpr (kPerChunk)
-            out_bits[(int64_t)blockIdx.y * k + col0 + c] = best;
+            out_bits[chunk * k + col0 + c] = best;
         else
             atomicMax(out_bits + col0 + c, best);
     }
+}
+
+// per-sample maxima: grid (strips, samples)
+template <int EB>
+__global__ __launch_bounds__(kAbsThreads) void sample_max_kernel(const u32x4* __restrict__ x, int64_t rows,
+                                                                 int64_t kvec, int64_t k, int64_t rows_per_sample,
+                                                                 unsigned* __restrict__ out_bits) {
+    __shared__ u32x4 part[kAbsThreads];
+    absmax_block<EB, true>(x, rows, kvec, k, rows_per_sample, out_bits, blockIdx.x, blockIdx.y, part);
+}
+
+// Several inputs in one launch (the projections of a block): item i owns the
+// blocks [first[i], first[i + 1]) of a 1-D grid, laid out strip-fastest as a
+// (strips, chunks) grid of its own would be. The item is uniform per block.
+struct AbsTable {
+    int count;
+    int32_t first[sqk::kMaxBatch + 1];
+    const u32x4* x[sqk::kMaxBatch];
+    unsigned* out[sqk::kMaxBatch];
+    int64_t rows[sqk::kMaxBatch], kvec[sqk::kMaxBatch], k[sqk::kMaxBatch], rpb[sqk::kMaxBatch];
+    int32_t strips[sqk::kMaxBatch], eb[sqk::kMaxBatch];
+};
+
+__device__ __forceinline__ int item_of(const int32_t* first, int count, int32_t b) {
+    int i = 0;
+    while (i + 1 < count && b >= first[i + 1]) ++i;
+    return i;
+}
+
+__global__ __launch_bounds__(kAbsThreads) void absmax_batched_kernel(const AbsTable tab) {
+    __shared__ u32x4 part[kAbsThreads];
+    const int32_t b = blockIdx.x;
+    const int i = item_of(tab.first, tab.count, b);
+    const int32_t local = b - tab.first[i];
+    const int64_t strip = local % tab.strips[i], chunk = local / tab.strips[i];
+    if (tab.eb[i] == 2)
+        absmax_block<2, false>(tab.x[i], tab.rows[i], tab.kvec[i], tab.k[i], tab.rpb[i], tab.out[i], strip, chunk,
+                               part);
+    else
+        absmax_block<4, false>(tab.x[i], tab.rows[i], tab.kvec[i], tab.k[i], tab.rpb[i], tab.out[i], strip, chunk,
+                               part);
+}
+
+// zeros over several buffers in one launch: buffer i owns blocks
+// [first[i], first[i + 1]) of 256 floats each
+struct FillTable {
+    int count;
+    int32_t first[sqk::kMaxBatch + 1];
+    float* p[sqk::kMaxBatch];
+    int64_t n[sqk::kMaxBatch];
+};
+
+__global__ __launch_bounds__(256) void fill_zero_batched_kernel(const FillTable tab) {
+    const int i = item_of(tab.first, tab.count, blockIdx.x);
+    const int64_t j = (int64_t)(blockIdx.x - tab.first[i]) * 256 + threadIdx.x;
+    if (j < tab.n[i]) tab.p[i][j] = 0.0f;
 }
 
 // Running fp64 sum of per-sample maxima, one thread per channel, the samples
@@ -153,12 +208,9 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
 // quotient, one rounding to fp32; inv_s_j = fp32(1/s_j). One thread per channel.
 constexpr int kSmoothThreads = 256;
 
-__global__ __launch_bounds__(kSmoothThreads) void smooth_kernel(const float* __restrict__ act_max,
-                                                                const float* __restrict__ w_max, int64_t k,
-                                                                double alpha, float* __restrict__ s,
-                                                                float* __restrict__ inv_s) {
-    const int64_t j = (int64_t)blockIdx.x * kSmoothThreads + threadIdx.x;
-    if (j >= k) return;
+__device__ __forceinline__ void smooth_channel(const float* __restrict__ act_max, const float* __restrict__ w_max,
+                                               int64_t j, double alpha, float* __restrict__ s,
+                                               float* __restrict__ inv_s) {
     const float a = __builtin_fmaxf(act_max[j], sqd::kFloor);
     const float w = __builtin_fmaxf(w_max[j], sqd::kFloor);
     const double num = pow((double)a, alpha);
@@ -172,10 +224,8 @@ __global__ __launch_bounds__(kSmoothThreads) void smooth_kernel(const float* __r
 // act_scale = fp32( max_j fp32(max(act_max[j], 1e-5) * inv_s[j]) / 127 ).
 constexpr int kScaleThreads = 1024;
 
-__global__ __launch_bounds__(kScaleThreads) void act_scale_kernel(const float* __restrict__ act_max,
-                                                                  const float* __restrict__ inv_s, int64_t k,
-                                                                  float qmax, float* __restrict__ act_scale) {
-    __shared__ float red[kScaleThreads / 64];
+__device__ __forceinline__ void act_scale_block(const float* __restrict__ act_max, const float* __restrict__ inv_s,
+                                                int64_t k, float qmax, float* __restrict__ act_scale, float* red) {
     float mx = 0.0f;
     for (int64_t j = threadIdx.x; j < k; j += kScaleThreads)
         mx = __builtin_fmaxf(mx, __fmul_rn(__builtin_fmaxf(act_max[j], sqd::kFloor), inv_s[j]));
@@ -183,40 +233,111 @@ __global__ __launch_bounds__(kScaleThreads) void act_scale_kernel(const float* _
     if (threadIdx.x == 0) act_scale[0] = __fdiv_rn(mx, qmax);
 }
 
+__global__ __launch_bounds__(kScaleThreads) void act_scale_kernel(const float* __restrict__ act_max,
+                                                                  const float* __restrict__ inv_s, int64_t k,
+                                                                  float qmax, float* __restrict__ act_scale) {
+    __shared__ float red[kScaleThreads / 64];
+    act_scale_block(act_max, inv_s, k, qmax, act_scale, red);
+}
+
+// Smoothing factors of several projections: item i owns blocks
+// [first[i], first[i + 1]) of the smoothing launch and block i of the scale
+// launch.
+struct SmoothTable {
+    int count;
+    int32_t first[sqk::kMaxBatch + 1];
+    const float* act_max[sqk::kMaxBatch];
+    const float* w_max[sqk::kMaxBatch];
+    int64_t k[sqk::kMaxBatch];
+    double alpha[sqk::kMaxBatch];
+    float* s[sqk::kMaxBatch];
+    float* inv_s[sqk::kMaxBatch];
+    float* act_scale[sqk::kMaxBatch];
+};
+
+__global__ __launch_bounds__(kSmoothThreads) void smooth_batched_kernel(const SmoothTable tab) {
+    const int i = item_of(tab.first, tab.count, blockIdx.x);
+    const int64_t j = (int64_t)(blockIdx.x - tab.first[i]) * kSmoothThreads + threadIdx.x;
+    if (j < tab.k[i]) smooth_channel(tab.act_max[i], tab.w_max[i], j, tab.alpha[i], tab.s[i], tab.inv_s[i]);
+}
+
+__global__ __launch_bounds__(kScaleThreads) void act_scale_batched_kernel(const SmoothTable tab) {
+    __shared__ float red[kScaleThreads / 64];
+    const int i = blockIdx.x;
+    act_scale_block(tab.act_max[i], tab.inv_s[i], tab.k[i], sqd::kQmax, tab.act_scale[i], red);
+}
+
+// launch geometry of one absmax input: about 2048 blocks, but at least
+// kAbsMinRows rows per block (fewer atomics), rows per block a multiple of
+// 4 waves x kAbsUnroll
+struct AbsGeom {
+    int64_t kvec, strips, rpb, chunks;
+};
+
+AbsGeom abs_geom(int eb, int64_t rows, int64_t k) {
+    AbsGeom g;
+    g.kvec = k * eb / 16;
+    g.strips = (g.kvec + 63) / 64;
+    const int64_t granule = 4 * kAbsUnroll;
+    const int64_t target_chunks = std::max<int64_t>(1, 2048 / g.strips);
+    int64_t rpb = (rows + target_chunks - 1) / target_chunks;
+    rpb = std::max<int64_t>(rpb, std::min<int64_t>(rows, kAbsMinRows));
+    g.rpb = std::max<int64_t>(granule, (rpb + granule - 1) / granule * granule);
+    g.chunks = (rows + g.rpb - 1) / g.rpb;
+    return g;
+}
+
 }  // namespace
 
 namespace sqk {
 
+hipError_t absmax_batched(const AbsmaxItem* items, int count, bool accumulate, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    if (!accumulate) {
+        FillTable ft{};
+        ft.count = count;
+        int64_t blocks = 0;
+        for (int i = 0; i < count; ++i) {
+            ft.first[i] = (int32_t)blocks;
+            ft.p[i] = items[i].absmax;
+            ft.n[i] = items[i].k;
+            blocks += (items[i].k + 255) / 256;
+        }
+        if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+        ft.first[count] = (int32_t)blocks;
+        fill_zero_batched_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(ft);
+    }
+    AbsTable tab{};
+    int n = 0;
+    int64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        if (items[i].rows == 0) continue;
+        const int eb = elem_bytes(items[i].xt);
+        const AbsGeom g = abs_geom(eb, items[i].rows, items[i].k);
+        tab.first[n] = (int32_t)blocks;
+        tab.x[n] = (const u32x4*)items[i].x;
+        tab.out[n] = (unsigned*)items[i].absmax;
+        tab.rows[n] = items[i].rows;
+        tab.kvec[n] = g.kvec;
+        tab.k[n] = items[i].k;
+        tab.rpb[n] = g.rpb;
+        tab.strips[n] = (int32_t)g.strips;
+        tab.eb[n] = eb;
+        blocks += g.strips * g.chunks;
+        ++n;
+    }
+    if (n == 0) return hipGetLastError();
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    tab.count = n;
+    tab.first[n] = (int32_t)blocks;
+    absmax_batched_kernel<<<dim3((unsigned)blocks), dim3(kAbsThreads), 0, stream>>>(tab);
+    return hipGetLastError();
+}
+
 hipError_t absmax(const void* x, int xt, int64_t rows, int64_t k, float* absmax_out, bool accumulate,
                   hipStream_t stream) {
-    if (!accumulate) {
-        fill_zero_kernel<<<dim3((unsigned)((k + 255) / 256)), dim3(256), 0, stream>>>(absmax_out, k);
-    }
-    if (rows == 0) return hipGetLastError();
-    const int eb = elem_bytes(xt);
-    const int64_t kvec = k * eb / 16;
-    const int64_t strips = (kvec + 63) / 64;
-    // about 2048 blocks, but at least kAbsMinRows rows per block (fewer
-    // atomics), rows per block a multiple of 4 waves x kAbsUnroll
-    const int64_t granule = 4 * kAbsUnroll;
-    const int64_t target_chunks = std::max<int64_t>(1, 2048 / strips);
-    int64_t rpb = (rows + target_chunks - 1) / target_chunks;
-    rpb = std::max<int64_t>(rpb, std::min<int64_t>(rows, kAbsMinRows));
-    rpb = (rpb + granule - 1) / granule * granule;
-    int64_t chunks = (rows + rpb - 1) / rpb;
-    if (chunks > 65535) {
-        rpb = (rows + 65534) / 65535;
-        rpb = (rpb + granule - 1) / granule * granule;
-        chunks = (rows + rpb - 1) / rpb;
-    }
-    dim3 grid((unsigned)strips, (unsigned)chunks);
-    if (eb == 2)
-        absmax_kernel<2, false><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x, rows, kvec, k, rpb,
-                                                                        (unsigned*)absmax_out);
-    else
-        absmax_kernel<4, false><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x, rows, kvec, k, rpb,
-                                                                        (unsigned*)absmax_out);
-    return hipGetLastError();
+    const AbsmaxItem item{x, xt, rows, k, absmax_out};
+    return absmax_batched(&item, 1, accumulate, stream);
 }
 
 hipError_t act_scale(const float* act_max, const float* inv_s, int64_t k, float* act_scale_out,
@@ -246,10 +367,10 @@ hipError_t sample_max(const void* x, int xt, int64_t samples, int64_t rows_per_s
         unsigned* out = (unsigned*)(sample_max_out + b0 * k);
         const int64_t r = std::min<int64_t>(rows - b0 * rows_per_sample, nb * rows_per_sample);
         if (eb == 2)
-            absmax_kernel<2, true><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x + off, r, kvec, k,
+            sample_max_kernel<2><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x + off, r, kvec, k,
                                                                           rows_per_sample, out);
         else
-            absmax_kernel<4, true><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x + off, r, kvec, k,
+            sample_max_kernel<4><<<grid, dim3(kAbsThreads), 0, stream>>>((const u32x4*)x + off, r, kvec, k,
                                                                           rows_per_sample, out);
     }
     return hipGetLastError();
@@ -267,12 +388,33 @@ hipError_t mean_finalize(const double* sum, int64_t count, int64_t k, float* act
     return hipGetLastError();
 }
 
+hipError_t smooth_factors_batched(const SmoothItem* items, int count, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    SmoothTable tab{};
+    tab.count = count;
+    int64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        tab.first[i] = (int32_t)blocks;
+        tab.act_max[i] = items[i].act_max;
+        tab.w_max[i] = items[i].w_max;
+        tab.k[i] = items[i].k;
+        tab.alpha[i] = (double)items[i].alpha;
+        tab.s[i] = items[i].s;
+        tab.inv_s[i] = items[i].inv_s;
+        tab.act_scale[i] = items[i].act_scale;
+        blocks += (items[i].k + kSmoothThreads - 1) / kSmoothThreads;
+    }
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    tab.first[count] = (int32_t)blocks;
+    smooth_batched_kernel<<<dim3((unsigned)blocks), dim3(kSmoothThreads), 0, stream>>>(tab);
+    act_scale_batched_kernel<<<dim3((unsigned)count), dim3(kScaleThreads), 0, stream>>>(tab);
+    return hipGetLastError();
+}
+
 hipError_t smooth_factors(const float* act_max, const float* w_max, int64_t k, float alpha, float* s,
                           float* inv_s, float* act_scale, hipStream_t stream) {
-    smooth_kernel<<<dim3((unsigned)((k + kSmoothThreads - 1) / kSmoothThreads)), dim3(kSmoothThreads), 0,
-                    stream>>>(act_max, w_max, k, (double)alpha, s, inv_s);
-    act_scale_kernel<<<dim3(1), dim3(kScaleThreads), 0, stream>>>(act_max, inv_s, k, sqd::kQmax, act_scale);
-    return hipGetLastError();
+    const SmoothItem item{act_max, w_max, k, alpha, s, inv_s, act_scale};
+    return smooth_factors_batched(&item, 1, stream);
 }
 
 }  // namespace sqk
@@ -412,13 +554,13 @@ hipError_t percentile_t(const void* x, int64_t rows, int64_t k, uint32_t rank0, 
                         uint32_t* rank, float* act_max, hipStream_t stream) {
     const int64_t words = (int64_t)PctKey<EB>::PASSES * k * kPctBins;
     fill_zero_u32_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream>>>(hist, words);
-    pct_pass<EB, 0>(x, rows, k, rank0, hist, prefix, rank, act_max, stream);
-    pct_pass<EB, 1>(x, rows, k, rank0, hist, prefix, rank, act_max, stream);
+    hipError_t e = pct_pass<EB, 0>(x, rows, k, rank0, hist, prefix, rank, act_max, stream);
+    if (e == hipSuccess) e = pct_pass<EB, 1>(x, rows, k, rank0, hist, prefix, rank, act_max, stream);
     if constexpr (PctKey<EB>::PASSES > 2) {
-        pct_pass<EB, 2>(x, rows, k, rank0, hist, prefix, rank, act_max, stream);
-        pct_pass<EB, 3>(x, rows, k, rank0, hist, prefix, rank, act_max, stream);
+        if (e == hipSuccess) e = pct_pass<EB, 2>(x, rows, k, rank0, hist, prefix, rank, act_max, stream);
+        if (e == hipSuccess) e = pct_pass<EB, 3>(x, rows, k, rank0, hist, prefix, rank, act_max, stream);
     }
-    return hipGetLastError();
+    return e;
 }
 
 }  // namespace

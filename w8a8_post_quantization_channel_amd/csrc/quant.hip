@@ -76,155 +76,203 @@ __device__ __forceinline__ void store_codes(int8_t* __restrict__ dst, const int 
     }
 }
 
-// Weight rows streamed through LDS. A persistent block of 512 threads walks
+// Weight rows streamed through LDS. A persistent block of WV waves walks
 // "stages" of RB consecutive rows (a contiguous run of W), kept in a ring of NS
 // LDS buffers filled by buffer_load ... lds, so the loads of the next stages
-// fly while this one is reduced and quantized. Thread t owns the 16-byte
-// column vectors t, t + 512, ... (VPT of them) and keeps their s values in
-// registers. Per stage: pass 1 forms W' = W * s in registers and the row
-// maxima (wave shuffles, then one LDS exchange and barrier), pass 2 quantizes
-// the registers and stores 4 or 8 codes per vector. W is read from HBM once.
-constexpr int kQwThreads = 512;
-constexpr int kQwWaves = kQwThreads / 64;
+// fly while this one is reduced and quantized. The RB * kvec 16-byte vectors
+// of a stage are dealt out flat: thread t takes vectors j = t, t + T, ...
+// (T threads, at most NV each), so every thread has the same work whatever the
+// row length; the row r_j = j / kvec and column c_j = j % kvec of each of its
+// slots are fixed for a weight, and the thread keeps the s values of its
+// columns in registers. Per stage: pass 1 forms W' = W * s in registers and
+// the row maxima (a select per row, wave shuffles, one LDS exchange and
+// barrier), pass 2 quantizes the registers and stores 4 or 8 codes per vector
+// (the codes of a stage are as contiguous as its input). W is read from HBM
+// once.
+//
+// One launch can cover several weights (the projections of a block): their
+// stages are numbered one after the other, item i owning stages
+// [first[i], first[i + 1]), and a block that moves on to the next item
+// recomputes its slots and reloads its s registers.
 
-template <int EB, int VPT, int RB, int CPW, int NS, bool FP8>
-__global__ __launch_bounds__(kQwThreads) void quant_weight_stream_kernel(const int8_t* __restrict__ w, int64_t n,
-                                                                        int64_t kvec, const float* __restrict__ s,
-                                                                        int8_t* __restrict__ wq,
-                                                                        float* __restrict__ w_scale) {
-    constexpr int E = 16 / EB;                        // elements per 16-byte vector
-    constexpr int STAGE = CPW * kQwWaves * 1024;      // bytes, >= RB rows (checked by the launcher)
+struct QwTable {
+    int count;
+    int64_t first[sqk::kMaxBatch + 1];
+    const int8_t* w[sqk::kMaxBatch];
+    const float* s[sqk::kMaxBatch];
+    int8_t* wq[sqk::kMaxBatch];
+    float* w_scale[sqk::kMaxBatch];
+    int64_t n[sqk::kMaxBatch], kvec[sqk::kMaxBatch];
+};
+
+__device__ __forceinline__ int stage_item(const QwTable& tab, int64_t g) {
+    int i = 0;
+    while (i + 1 < tab.count && g >= tab.first[i + 1]) ++i;
+    return i;
+}
+
+template <int EB, int WV, int NV, int RB, int CPW, int NS, bool FP8>
+__global__ __launch_bounds__(64 * WV) void quant_weight_stream_kernel(const QwTable tab) {
+    constexpr int T = 64 * WV;                 // threads
+    constexpr int E = 16 / EB;                 // elements per 16-byte vector
+    constexpr int STAGE = CPW * WV * 1024;     // bytes, >= RB rows (checked by the launcher)
+    constexpr int W32 = E / 4;                 // dwords of codes per vector
     static_assert(NS == 2 || NS == 3, "ring depth");
     static_assert((NS - 1) * CPW < 64, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) char ring[NS * STAGE];
-    __shared__ float part[RB][kQwWaves];
+    __shared__ float part[RB][WV];
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int64_t rowbytes = kvec * 16;
-    const int64_t nstages = (n + RB - 1) / RB;
+    const int64_t nstages = tab.first[tab.count];
 
-    float sv[VPT][E];
+    // this thread's slots for the current weight: vector j = t + i T of a
+    // stage (live when j < RB * kvec), its row and its s values
+    float sv[NV][E];
+    int row[NV];
+    bool live[NV];
+    int cur = -1;
+    auto setup = [&](int it) {
+        const int kvec = (int)tab.kvec[it];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int64_t v = t + (int64_t)i * kQwThreads;
+        for (int i = 0; i < NV; ++i) {
+            const int j = t + i * T;
+            live[i] = j < RB * kvec;
+            row[i] = live[i] ? j / kvec : RB;
+            const int c = live[i] ? j - row[i] * kvec : 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) sv[i][e] = v < kvec ? s[v * E + e] : 0.0f;
-    }
+            for (int e = 0; e < E; ++e) sv[i][e] = live[i] ? tab.s[it][c * E + e] : 0.0f;
+        }
+        cur = it;
+    };
 
-    // stage g -> ring slot b: CPW loads per wave, chunk c = wave + 8 j of the
-    // stage's contiguous bytes (zeros past the last row)
+    // stage g -> ring slot: CPW loads per wave, chunk c = wave + WV j of the
+    // stage's contiguous bytes (zeros past the last row of its weight, and for
+    // stages past the end)
     auto issue = [&](int64_t g, int slot) {
-        const int64_t r0 = g * RB;
-        const int64_t rows = r0 < n ? min<int64_t>(RB, n - r0) : 0;
-        const sqd::i32x4 rsrc = sqd::tile_rsrc(w + (r0 < n ? r0 : 0) * rowbytes, rows, rowbytes);
+        const bool in = g < nstages;
+        const int it = in ? stage_item(tab, g) : 0;
+        const int64_t rowbytes = tab.kvec[it] * 16;
+        const int64_t r0 = in ? (g - tab.first[it]) * RB : 0;
+        const int64_t rows = in ? min<int64_t>(RB, tab.n[it] - r0) : 0;
+        const sqd::i32x4 rsrc = sqd::tile_rsrc(tab.w[it] + r0 * rowbytes, rows, rowbytes);
         const uint32_t base = sqd::lds_addr(ring) + (uint32_t)(slot * STAGE) + (uint32_t)wave * 1024u;
 #pragma unroll
-        for (int j = 0; j < CPW; ++j) sqd::dma16(rsrc, base + (uint32_t)(j * kQwWaves * 1024), lane * 16,
-                                                 (j * kQwWaves + wave) * 1024);
+        for (int j = 0; j < CPW; ++j)
+            sqd::dma16(rsrc, base + (uint32_t)(j * WV * 1024), lane * 16, (j * WV + wave) * 1024);
     };
 
     // Codes of a stage are stored one round late (after the next stage's
     // wait), so the wait below, which also counts stores, finds them long
     // done; it is exact for the loads because loads complete in order and
-    // exactly NS - 2 stages of loads are issued after the awaited one.
-    constexpr int W32 = E / 4;  // dwords of codes per vector
-    uint32_t codes[RB][VPT][W32];
+    // exactly NS - 2 stages of loads are issued after the awaited one (the s
+    // reloads at an item change only add younger operations, which makes the
+    // wait stricter, never looser).
+    uint32_t codes[NV][W32];
     float scale[RB];
     int64_t prev = -1;  // stage whose codes are pending
     auto flush = [&]() {
         if (prev < 0) return;
-        const int64_t p0 = prev * RB;
+        const int64_t kvec = tab.kvec[cur], n = tab.n[cur];
+        const int64_t p0 = (prev - tab.first[cur]) * RB;
+        int8_t* dst = tab.wq[cur] + p0 * kvec * E;
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            if (p0 + r >= n) break;
-            int8_t* dst = wq + (p0 + r) * (kvec * E);
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int64_t v = t + (int64_t)i * kQwThreads;
-                if (v < kvec) {
-                    if constexpr (W32 == 2)
-                        *(sqd::u32x2*)(dst + v * E) = sqd::u32x2{codes[r][i][0], codes[r][i][1]};
-                    else
-                        *(uint32_t*)(dst + v * E) = codes[r][i][0];
-                }
+        for (int i = 0; i < NV; ++i) {
+            if (live[i] && p0 + row[i] < n) {
+                const int64_t j = t + (int64_t)i * T;
+                if constexpr (W32 == 2)
+                    *(sqd::u32x2*)(dst + j * E) = sqd::u32x2{codes[i][0], codes[i][1]};
+                else
+                    *(uint32_t*)(dst + j * E) = codes[i][0];
             }
-            if (t == 0) w_scale[p0 + r] = scale[r];
         }
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+            if (t == r && p0 + r < n) tab.w_scale[cur][p0 + r] = scale[r];
     };
 
     int64_t g = blockIdx.x;
     int slot = 0;
+    if (g < nstages) setup(stage_item(tab, g));
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p) issue(g + (int64_t)p * gridDim.x, p);
     for (; g < nstages; g += gridDim.x) {
         sqd::wait_vmcnt<(NS - 2) * CPW>();  // this stage landed (for this wave's loads) ...
         __syncthreads();                    // ... and for every wave; the slot read last round is free
-        flush();
+        const int it = stage_item(tab, g);
+        flush();  // the previous stage's codes (its weight is still `cur`)
         issue(g + (int64_t)(NS - 1) * gridDim.x, (slot + NS - 1) % NS);
+        if (it != cur) setup(it);
         const char* st = ring + slot * STAGE;
-        float wv[RB][VPT][E];
+        float wv[NV][E];
         float mx[RB];
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            mx[r] = 0.0f;
+        for (int r = 0; r < RB; ++r) mx[r] = 0.0f;
 #pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int64_t v = t + (int64_t)i * kQwThreads;
-                if (v < kvec) {
-                    const u32x4 raw = *(const u32x4*)(st + r * rowbytes + v * 16);
-                    float e[E];
-                    sqd::unpack16<E>(raw, e);
+        for (int i = 0; i < NV; ++i) {
+            float vm = 0.0f;
+            if (live[i]) {
+                const u32x4 raw = *(const u32x4*)(st + (t + i * T) * 16);
+                float e[E];
+                sqd::unpack16<E>(raw, e);
 #pragma unroll
-                    for (int q = 0; q < E; ++q) {
-                        wv[r][i][q] = __fmul_rn(e[q], sv[i][q]);
-                        mx[r] = __builtin_fmaxf(mx[r], __builtin_fabsf(wv[r][i][q]));
-                    }
+                for (int q = 0; q < E; ++q) {
+                    wv[i][q] = __fmul_rn(e[q], sv[i][q]);
+                    vm = __builtin_fmaxf(vm, __builtin_fabsf(wv[i][q]));
                 }
+            } else {
+#pragma unroll
+                for (int q = 0; q < E; ++q) wv[i][q] = 0.0f;
             }
+#pragma unroll
+            for (int r = 0; r < RB; ++r) mx[r] = row[i] == r ? __builtin_fmaxf(mx[r], vm) : mx[r];
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
             mx[r] = sqd::wave_max(mx[r]);
             if (lane == 0) part[r][wave] = mx[r];
         }
         __syncthreads();
+        float inv[RB];
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             float m = part[r][0];
 #pragma unroll
-            for (int i = 1; i < kQwWaves; ++i) m = __builtin_fmaxf(m, part[r][i]);
+            for (int w = 1; w < WV; ++w) m = __builtin_fmaxf(m, part[r][w]);
             m = __builtin_fmaxf(m, sqd::kFloor);
-            const float ws = __fdiv_rn(m, FP8 ? sqd::kFp8Max : sqd::kQmax);
-            const float inv_ws = __fdiv_rn(1.0f, ws);
-            scale[r] = ws;
+            scale[r] = __fdiv_rn(m, FP8 ? sqd::kFp8Max : sqd::kQmax);
+            inv[r] = __fdiv_rn(1.0f, scale[r]);
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            float inv_ws = inv[0];
+#pragma unroll
+            for (int r = 1; r < RB; ++r) inv_ws = row[i] == r ? inv[r] : inv_ws;
             if constexpr (FP8) {
                 // e4m3 codes: |W' / ws| <= 448 (1 + 3 * 2^-24), which rounds to 448
 #pragma unroll
-                for (int i = 0; i < VPT; ++i)
-#pragma unroll
-                    for (int d = 0; d < W32; ++d)
-                        codes[r][i][d] = sqd::pack4_e4m3(
-                            __fmul_rn(wv[r][i][4 * d], inv_ws), __fmul_rn(wv[r][i][4 * d + 1], inv_ws),
-                            __fmul_rn(wv[r][i][4 * d + 2], inv_ws), __fmul_rn(wv[r][i][4 * d + 3], inv_ws));
-                continue;
-            }
-            // Codes by the round-to-nearest-even of the fp32 adder: for
-            // |v| < 2^22, fl(v + 1.5 * 2^23) = rint(v) + 1.5 * 2^23 exactly, and
-            // the low byte of its bit pattern is rint(v) as a two's-complement
-            // int8. No clamp is needed: |W'| <= m and inv_ws = fl(1 / fl(m / 127)),
-            // so |v| <= 127 (1 + 3 * 2^-24) and rint(v) is within [-127, 127]
-            // (below the 1e-5 floor, |v| < 127). Equal to q8() for every value
-            // this row can produce.
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
+                for (int d = 0; d < W32; ++d)
+                    codes[i][d] = sqd::pack4_e4m3(
+                        __fmul_rn(wv[i][4 * d], inv_ws), __fmul_rn(wv[i][4 * d + 1], inv_ws),
+                        __fmul_rn(wv[i][4 * d + 2], inv_ws), __fmul_rn(wv[i][4 * d + 3], inv_ws));
+            } else {
+                // Codes by the round-to-nearest-even of the fp32 adder: for
+                // |v| < 2^22, fl(v + 1.5 * 2^23) = rint(v) + 1.5 * 2^23 exactly,
+                // and the low byte of its bit pattern is rint(v) as a
+                // two's-complement int8. No clamp is needed: |W'| <= m and
+                // inv_ws = fl(1 / fl(m / 127)), so |v| <= 127 (1 + 3 * 2^-24) and
+                // rint(v) is within [-127, 127] (below the 1e-5 floor, |v| < 127).
+                // Equal to q8() for every value this row can produce.
                 uint32_t b[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    b[e] = __float_as_uint(__fadd_rn(__fmul_rn(wv[r][i][e], inv_ws), 12582912.0f));
+                    b[e] = __float_as_uint(__fadd_rn(__fmul_rn(wv[i][e], inv_ws), 12582912.0f));
 #pragma unroll
                 for (int d = 0; d < W32; ++d) {
                     // low bytes of b[4d .. 4d+3] -> one dword
                     const uint32_t lo = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0c0c0400u);
                     const uint32_t hi = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0c0c0400u);
-                    codes[r][i][d] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                    codes[i][d] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
                 }
             }
         }
@@ -369,36 +417,100 @@ int device_cus() {
     return cus;
 }
 
-template <int EB, int VPT, int RB, int CPW, int NS, bool FP8>
-hipError_t launch_qw(const void* w, int64_t n, int64_t kvec, const float* s, int8_t* wq, float* w_scale,
-                     hipStream_t stream) {
-    static_assert(NS * CPW * kQwWaves * 1024 <= 150 * 1024, "the ring fits in LDS");
-    if (RB * kvec * 16 > CPW * kQwWaves * 1024 || kvec > VPT * kQwThreads) return hipErrorInvalidValue;
-    const int64_t nstages = (n + RB - 1) / RB;
-    const int64_t blocks = std::min<int64_t>(nstages, (int64_t)device_cus());
-    quant_weight_stream_kernel<EB, VPT, RB, CPW, NS, FP8><<<dim3((unsigned)blocks), dim3(kQwThreads), 0, stream>>>(
-        (const int8_t*)w, n, kvec, s, wq, w_scale);
+// WV waves of 64 threads, NV vector slots per thread, RB rows per stage of
+// CPW KB per wave, NS stages in the ring, PER_CU blocks per compute unit (the
+// rings of all of them fit the LDS)
+template <int EB, int WV, int NV, int RB, int CPW, int NS, int PER_CU, bool FP8>
+hipError_t launch_qw(const QwTable& tab, hipStream_t stream) {
+    static_assert(PER_CU * (NS * CPW * WV * 1024 + RB * WV * 4) <= 160 * 1024, "the rings fit in LDS");
+    for (int i = 0; i < tab.count; ++i)
+        if (RB * tab.kvec[i] * 16 > CPW * WV * 1024 || RB * tab.kvec[i] > NV * 64 * WV) return hipErrorInvalidValue;
+    const int64_t blocks = std::min<int64_t>(tab.first[tab.count], (int64_t)PER_CU * device_cus());
+    quant_weight_stream_kernel<EB, WV, NV, RB, CPW, NS, FP8><<<dim3((unsigned)blocks), dim3(64 * WV), 0, stream>>>(
+        tab);
     return hipGetLastError();
 }
 
+// Kernel shape for rows of kvec 16-byte vectors (waves, slots per thread,
+// rows per stage, KB per wave per stage, ring depth, blocks per compute unit),
+// measured on MI355X over the Llama-2 7B/13B/70B projections: stages of
+// 16-64 KB in a two-deep ring and two to four blocks per compute unit, so that
+// while one block reduces and quantizes a stage the others' loads keep HBM
+// busy; the slots per thread divide a stage's vectors (nearly) evenly.
+// Shape 7: rows of more than 4096 vectors, one block per row reading it twice.
+constexpr int kQwLong = 7;
+constexpr int kQwRowsPerStage[kQwLong] = {4, 2, 2, 2, 1, 1, 1};
+
+int qw_shape(int64_t kvec) {
+    if (kvec <= 256) return 0;
+    if (kvec <= 512) return 1;
+    if (kvec <= 640) return 2;
+    if (kvec <= 1024) return 3;
+    if (kvec <= 1536) return 4;
+    if (kvec <= 2048) return 5;
+    if (kvec <= 4096) return 6;
+    return kQwLong;
+}
+
 template <int EB, bool FP8>
-hipError_t quant_weight_t(const void* w, int64_t n, int64_t k, const float* s, int8_t* wq, float* w_scale,
-                          hipStream_t stream) {
-    const int64_t kvec = k * EB / 16;  // 16-byte vectors per row
-    // (vectors per thread, rows per stage, 8 KB units per stage, ring depth):
-    // stages of 32-56 KB so each pair of barriers covers enough bytes, three
-    // in the ring when they fit; rows of more than 4096 vectors are read twice
-    // by a block per row
-    if (kvec <= 256) return launch_qw<EB, 1, 8, 4, 3, FP8>(w, n, kvec, s, wq, w_scale, stream);
-    if (kvec <= 512) return launch_qw<EB, 1, 4, 4, 3, FP8>(w, n, kvec, s, wq, w_scale, stream);
-    if (kvec <= 640) return launch_qw<EB, 2, 4, 5, 3, FP8>(w, n, kvec, s, wq, w_scale, stream);
-    if (kvec <= 1024) return launch_qw<EB, 2, 2, 4, 3, FP8>(w, n, kvec, s, wq, w_scale, stream);
-    if (kvec <= 1792) return launch_qw<EB, 4, 2, 7, 2, FP8>(w, n, kvec, s, wq, w_scale, stream);
-    if (kvec <= 2048) return launch_qw<EB, 4, 1, 4, 3, FP8>(w, n, kvec, s, wq, w_scale, stream);
-    if (kvec <= 4096) return launch_qw<EB, 8, 1, 8, 2, FP8>(w, n, kvec, s, wq, w_scale, stream);
-    quant_weight_long_kernel<EB, FP8><<<dim3((unsigned)n), dim3(256), 0, stream>>>((const u32x4*)w, k / 16, s, wq,
-                                                                            w_scale);
-    return hipGetLastError();
+hipError_t launch_shape(int shape, const QwTable& tab, hipStream_t stream) {
+    switch (shape) {
+        case 0: return launch_qw<EB, 4, 4, 4, 4, 2, 4, FP8>(tab, stream);
+        case 1: return launch_qw<EB, 4, 4, 2, 4, 2, 4, FP8>(tab, stream);
+        case 2: return launch_qw<EB, 4, 5, 2, 5, 2, 3, FP8>(tab, stream);
+        case 3: return launch_qw<EB, 8, 4, 2, 4, 2, 2, FP8>(tab, stream);
+        case 4: return launch_qw<EB, 8, 3, 1, 3, 2, 3, FP8>(tab, stream);
+        case 5: return launch_qw<EB, 8, 4, 1, 4, 2, 2, FP8>(tab, stream);
+        case 6: return launch_qw<EB, 16, 4, 1, 4, 2, 1, FP8>(tab, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Items of one element type and kernel shape share a launch (first-appearance
+// order); long rows get a launch per item.
+template <bool FP8>
+hipError_t quant_weight_items(const sqk::QuantWeightItem* items, int count, hipStream_t stream) {
+    bool done[sqk::kMaxBatch] = {};
+    for (int i = 0; i < count; ++i) {
+        if (done[i]) continue;
+        done[i] = true;
+        if (items[i].n == 0) continue;
+        const int eb = sqk::elem_bytes(items[i].wt);
+        const int shape = qw_shape(items[i].k * eb / 16);
+        if (shape == kQwLong) {
+            const int64_t kgroups = items[i].k / 16;
+            if (eb == 2)
+                quant_weight_long_kernel<2, FP8><<<dim3((unsigned)items[i].n), dim3(256), 0, stream>>>(
+                    (const u32x4*)items[i].w, kgroups, items[i].s, items[i].wq, items[i].w_scale);
+            else
+                quant_weight_long_kernel<4, FP8><<<dim3((unsigned)items[i].n), dim3(256), 0, stream>>>(
+                    (const u32x4*)items[i].w, kgroups, items[i].s, items[i].wq, items[i].w_scale);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            continue;
+        }
+        QwTable tab{};
+        int64_t stages = 0;
+        for (int j = i; j < count; ++j) {
+            if (j > i && (done[j] || items[j].n == 0 || sqk::elem_bytes(items[j].wt) != eb ||
+                          qw_shape(items[j].k * eb / 16) != shape))
+                continue;
+            done[j] = true;
+            const int c = tab.count++;
+            tab.first[c] = stages;
+            tab.w[c] = (const int8_t*)items[j].w;
+            tab.s[c] = items[j].s;
+            tab.wq[c] = items[j].wq;
+            tab.w_scale[c] = items[j].w_scale;
+            tab.n[c] = items[j].n;
+            tab.kvec[c] = items[j].k * eb / 16;
+            stages += (items[j].n + kQwRowsPerStage[shape] - 1) / kQwRowsPerStage[shape];
+        }
+        tab.first[tab.count] = stages;
+        const hipError_t e = eb == 2 ? launch_shape<2, FP8>(shape, tab, stream) : launch_shape<4, FP8>(shape, tab, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -407,16 +519,18 @@ namespace sqk {
 
 hipError_t quant_weight(const void* w, int wt, int64_t n, int64_t k, const float* s, int8_t* wq,
                         float* w_scale, hipStream_t stream) {
-    if (n == 0) return hipSuccess;
-    return elem_bytes(wt) == 2 ? quant_weight_t<2, false>(w, n, k, s, wq, w_scale, stream)
-                               : quant_weight_t<4, false>(w, n, k, s, wq, w_scale, stream);
+    const QuantWeightItem item{w, wt, n, k, s, wq, w_scale};
+    return quant_weight_items<false>(&item, 1, stream);
+}
+
+hipError_t quant_weight_batched(const QuantWeightItem* items, int count, hipStream_t stream) {
+    return quant_weight_items<false>(items, count, stream);
 }
 
 hipError_t quant_weight_fp8(const void* w, int wt, int64_t n, int64_t k, const float* s, uint8_t* wq,
                             float* w_scale, hipStream_t stream) {
-    if (n == 0) return hipSuccess;
-    return elem_bytes(wt) == 2 ? quant_weight_t<2, true>(w, n, k, s, (int8_t*)wq, w_scale, stream)
-                               : quant_weight_t<4, true>(w, n, k, s, (int8_t*)wq, w_scale, stream);
+    const QuantWeightItem item{w, wt, n, k, s, (int8_t*)wq, w_scale};
+    return quant_weight_items<true>(&item, 1, stream);
 }
 
 template <bool FP8>

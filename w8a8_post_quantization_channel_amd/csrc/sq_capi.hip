@@ -53,6 +53,54 @@ AlphaLayout alpha_layout(int nb, int64_t rows, int64_t n, int64_t k, int na) {
     return L;
 }
 
+sq_status check_absmax(const void* x, sq_dtype xt, int64_t rows, int64_t k, const float* absmax) {
+    if (!absmax || (rows > 0 && !x)) return SQ_ERR_NULL;
+    if (!valid_dtype(xt)) return SQ_ERR_DTYPE;
+    if (rows < 0 || !valid_k(k)) return SQ_ERR_SHAPE;
+    if (!aligned16(absmax) || (rows > 0 && !aligned16(x))) return SQ_ERR_ALIGN;
+    return SQ_OK;
+}
+
+sq_status check_smooth(const float* act_max, const float* w_max, int64_t k, float alpha, const float* s,
+                       const float* inv_s, const float* act_scale) {
+    if (!act_max || !w_max || !s || !inv_s || !act_scale) return SQ_ERR_NULL;
+    if (!valid_k(k)) return SQ_ERR_SHAPE;
+    if (!valid_alpha(alpha)) return SQ_ERR_ALPHA;
+    if (!aligned16(act_max) || !aligned16(w_max) || !aligned16(s) || !aligned16(inv_s) || !aligned16(act_scale))
+        return SQ_ERR_ALIGN;
+    return SQ_OK;
+}
+
+sq_status check_quant_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, const float* s, const int8_t* wq,
+                             const float* w_scale) {
+    if (!s || (n > 0 && (!w || !wq || !w_scale))) return SQ_ERR_NULL;
+    if (!valid_dtype(wt)) return SQ_ERR_DTYPE;
+    if (n < 0 || !valid_k(k) || n > INT32_MAX) return SQ_ERR_SHAPE;
+    if (!aligned16(s) || (n > 0 && (!aligned16(w) || !aligned16(wq) || !aligned16(w_scale)))) return SQ_ERR_ALIGN;
+    return SQ_OK;
+}
+
+// Byte ranges named by the items of a batched call: an output range of one
+// item may not overlap any range of another item.
+struct Ranges {
+    struct R {
+        int item;
+        uintptr_t lo, hi;
+        bool out;
+    } r[5 * SQ_MAX_BATCH];
+    int n = 0;
+    void add(int item, const void* p, int64_t bytes, bool out) {
+        if (p && bytes > 0) r[n++] = R{item, (uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes, out};
+    }
+    bool overlap() const {
+        for (int a = 0; a < n; ++a)
+            for (int b = a + 1; b < n; ++b)
+                if (r[a].item != r[b].item && (r[a].out || r[b].out) && r[a].lo < r[b].hi && r[b].lo < r[a].hi)
+                    return true;
+        return false;
+    }
+};
+
 }  // namespace
 
 extern "C" {
@@ -73,31 +121,85 @@ const char* sq_status_string(sq_status status) {
 
 sq_status sq_calib_absmax(const void* x, sq_dtype xt, int64_t rows, int64_t k, float* absmax, int accumulate,
                           hipStream_t stream) {
-    if (!absmax || (rows > 0 && !x)) return SQ_ERR_NULL;
-    if (!valid_dtype(xt)) return SQ_ERR_DTYPE;
-    if (rows < 0 || !valid_k(k)) return SQ_ERR_SHAPE;
-    if (!aligned16(absmax) || (rows > 0 && !aligned16(x))) return SQ_ERR_ALIGN;
+    const sq_status st = check_absmax(x, xt, rows, k, absmax);
+    if (st != SQ_OK) return st;
     if (rows == 0 && accumulate) return SQ_OK;
     return hip_status(sqk::absmax(x, xt, rows, k, absmax, accumulate != 0, stream));
 }
 
 sq_status sq_smooth_factors(const float* act_max, const float* w_max, int64_t k, float alpha, float* s,
                             float* inv_s, float* act_scale, hipStream_t stream) {
-    if (!act_max || !w_max || !s || !inv_s || !act_scale) return SQ_ERR_NULL;
-    if (!valid_k(k)) return SQ_ERR_SHAPE;
-    if (!valid_alpha(alpha)) return SQ_ERR_ALPHA;
-    if (!aligned16(act_max) || !aligned16(w_max) || !aligned16(s) || !aligned16(inv_s) || !aligned16(act_scale))
-        return SQ_ERR_ALIGN;
+    const sq_status st = check_smooth(act_max, w_max, k, alpha, s, inv_s, act_scale);
+    if (st != SQ_OK) return st;
     return hip_status(sqk::smooth_factors(act_max, w_max, k, alpha, s, inv_s, act_scale, stream));
 }
 
 sq_status sq_quant_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, const float* s, int8_t* wq,
                           float* w_scale, hipStream_t stream) {
-    if (!s || (n > 0 && (!w || !wq || !w_scale))) return SQ_ERR_NULL;
-    if (!valid_dtype(wt)) return SQ_ERR_DTYPE;
-    if (n < 0 || !valid_k(k) || n > INT32_MAX) return SQ_ERR_SHAPE;
-    if (!aligned16(s) || (n > 0 && (!aligned16(w) || !aligned16(wq) || !aligned16(w_scale)))) return SQ_ERR_ALIGN;
+    const sq_status st = check_quant_weight(w, wt, n, k, s, wq, w_scale);
+    if (st != SQ_OK) return st;
     return hip_status(sqk::quant_weight(w, wt, n, k, s, wq, w_scale, stream));
+}
+
+sq_status sq_calib_absmax_batched(int count, const void* const* x, const sq_dtype* xt, const int64_t* rows,
+                                  const int64_t* k, float* const* absmax, int accumulate, hipStream_t stream) {
+    if (!x || !xt || !rows || !k || !absmax) return SQ_ERR_NULL;
+    if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
+    Ranges rg;
+    sqk::AbsmaxItem items[SQ_MAX_BATCH];
+    int n = 0;
+    for (int i = 0; i < count; ++i) {
+        const sq_status st = check_absmax(x[i], xt[i], rows[i], k[i], absmax[i]);
+        if (st != SQ_OK) return st;
+        rg.add(i, absmax[i], k[i] * 4, true);
+        rg.add(i, x[i], rows[i] * k[i] * (xt[i] == SQ_BF16 ? 2 : 4), false);
+        if (rows[i] == 0 && accumulate) continue;
+        items[n++] = sqk::AbsmaxItem{x[i], xt[i], rows[i], k[i], absmax[i]};
+    }
+    if (rg.overlap()) return SQ_ERR_SHAPE;
+    if (n == 0) return SQ_OK;
+    return hip_status(sqk::absmax_batched(items, n, accumulate != 0, stream));
+}
+
+sq_status sq_smooth_factors_batched(int count, const float* const* act_max, const float* const* w_max,
+                                    const int64_t* k, const float* alpha, float* const* s, float* const* inv_s,
+                                    float* const* act_scale, hipStream_t stream) {
+    if (!act_max || !w_max || !k || !alpha || !s || !inv_s || !act_scale) return SQ_ERR_NULL;
+    if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
+    Ranges rg;
+    sqk::SmoothItem items[SQ_MAX_BATCH];
+    for (int i = 0; i < count; ++i) {
+        const sq_status st = check_smooth(act_max[i], w_max[i], k[i], alpha[i], s[i], inv_s[i], act_scale[i]);
+        if (st != SQ_OK) return st;
+        rg.add(i, act_max[i], k[i] * 4, false);
+        rg.add(i, w_max[i], k[i] * 4, false);
+        rg.add(i, s[i], k[i] * 4, true);
+        rg.add(i, inv_s[i], k[i] * 4, true);
+        rg.add(i, act_scale[i], 4, true);
+        items[i] = sqk::SmoothItem{act_max[i], w_max[i], k[i], alpha[i], s[i], inv_s[i], act_scale[i]};
+    }
+    if (rg.overlap()) return SQ_ERR_SHAPE;
+    return hip_status(sqk::smooth_factors_batched(items, count, stream));
+}
+
+sq_status sq_quant_weight_batched(int count, const void* const* w, const sq_dtype* wt, const int64_t* n,
+                                  const int64_t* k, const float* const* s, int8_t* const* wq,
+                                  float* const* w_scale, hipStream_t stream) {
+    if (!w || !wt || !n || !k || !s || !wq || !w_scale) return SQ_ERR_NULL;
+    if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
+    Ranges rg;
+    sqk::QuantWeightItem items[SQ_MAX_BATCH];
+    for (int i = 0; i < count; ++i) {
+        const sq_status st = check_quant_weight(w[i], wt[i], n[i], k[i], s[i], wq[i], w_scale[i]);
+        if (st != SQ_OK) return st;
+        rg.add(i, w[i], n[i] * k[i] * (wt[i] == SQ_BF16 ? 2 : 4), false);
+        rg.add(i, s[i], k[i] * 4, false);
+        rg.add(i, wq[i], n[i] * k[i], true);
+        rg.add(i, w_scale[i], n[i] * 4, true);
+        items[i] = sqk::QuantWeightItem{w[i], wt[i], n[i], k[i], s[i], wq[i], w_scale[i]};
+    }
+    if (rg.overlap()) return SQ_ERR_SHAPE;
+    return hip_status(sqk::quant_weight_batched(items, count, stream));
 }
 
 sq_status sq_smooth_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* inv_s,

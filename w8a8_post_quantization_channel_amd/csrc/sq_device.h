@@ -141,7 +141,11 @@ constexpr int kOutOfRange = 0x70000000;
 // Written as asm so that the only waits on these loads are the explicit
 // s_waitcnt vmcnt(...) placed before the barriers that publish each stage
 // (the compiler would otherwise drain every load in flight before reading
-// any stage). No register receives the data.
+// any stage). No register receives the data. The asm sets m0 (the LDS base
+// of the load) itself; the compiler warns that it does not preserve m0 across
+// the statement, which is harmless here because the generated code of these
+// kernels reads m0 nowhere else (no LDS-DMA builtins, GWS, sendmsg or
+// interpolation), as the gfx950 assembly of the library shows.
 __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds, int voff, int soff) {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"

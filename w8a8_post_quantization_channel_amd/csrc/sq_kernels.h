@@ -13,9 +13,21 @@ enum ElemType { kF32 = 0, kBF16 = 1 };
 
 inline int elem_bytes(int t) { return t == kBF16 ? 2 : 4; }
 
+// items per batched call (the projections of one transformer block and more)
+constexpr int kMaxBatch = 16;
+
 // column max |x| of x[rows,k] into absmax[k] (overwrite or running max)
 hipError_t absmax(const void* x, int xt, int64_t rows, int64_t k, float* absmax, bool accumulate,
                   hipStream_t stream);
+
+// the same for up to kMaxBatch inputs: one zero fill and one reduction launch
+struct AbsmaxItem {
+    const void* x;
+    int xt;
+    int64_t rows, k;
+    float* absmax;
+};
+hipError_t absmax_batched(const AbsmaxItem* items, int count, bool accumulate, hipStream_t stream);
 
 // act_scale = fp32(max_j fp32(max(act_max[j], 1e-5) * inv_s[j]) / 127)
 hipError_t act_scale(const float* act_max, const float* inv_s, int64_t k, float* act_scale, hipStream_t stream);
@@ -52,9 +64,33 @@ hipError_t fold_norm_weight(const float* gamma, const float* inv_s, int64_t k, f
 hipError_t smooth_factors(const float* act_max, const float* w_max, int64_t k, float alpha, float* s,
                           float* inv_s, float* act_scale, hipStream_t stream);
 
+// the same for up to kMaxBatch projections: two launches in all
+struct SmoothItem {
+    const float* act_max;
+    const float* w_max;
+    int64_t k;
+    float alpha;
+    float* s;
+    float* inv_s;
+    float* act_scale;
+};
+hipError_t smooth_factors_batched(const SmoothItem* items, int count, hipStream_t stream);
+
 // W' = W diag(s), per-row symmetric int8
 hipError_t quant_weight(const void* w, int wt, int64_t n, int64_t k, const float* s, int8_t* wq,
                         float* w_scale, hipStream_t stream);
+
+// the same for up to kMaxBatch weights: one persistent launch per kernel
+// shape among the items (weights of equal row length share one)
+struct QuantWeightItem {
+    const void* w;
+    int wt;
+    int64_t n, k;
+    const float* s;
+    int8_t* wq;
+    float* w_scale;
+};
+hipError_t quant_weight_batched(const QuantWeightItem* items, int count, hipStream_t stream);
 
 // xq = q8((x * inv_s) * (1/act_scale))
 hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const float* inv_s,

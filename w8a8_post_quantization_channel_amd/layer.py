@@ -15,6 +15,12 @@ supplies the stream; all arithmetic is in libsq.so.
                  Y  = dequant(Xq Wq^T)                         (sq_w8a8_gemm)
       forward_dynamic: the same with the per-tensor scale taken from x itself
                  (sq_dynamic_quant_act; pwwt.cn §2.3 dynamic mode)
+
+prepare_block(layers, calib) does calibrate + prepare for the projections of
+one transformer block with the batched entry points: every statistic (the
+calibration inputs' and the weights') in one launch, the smoothing factors in
+two, the weight codes in one per row-length class, with results identical to
+the per-layer calls.
 """
 from __future__ import annotations
 
@@ -88,3 +94,25 @@ class W8A8Linear:
         self.calibrate(x_calib, False, stream)
         self.prepare(stream)
         return self.forward(x, stream=stream)
+
+
+MAX_BATCH = 16  # SQ_MAX_BATCH, the most items one batched call takes
+
+
+def _chunks(seq):
+    return [seq[i:i + MAX_BATCH] for i in range(0, len(seq), MAX_BATCH)]
+
+
+def prepare_block(layers, calib=(), stream=None):
+    """calibrate + prepare for several W8A8Linear layers in few launches.
+    calib: (x, act_max) pairs; act_max is overwritten with the column max of
+    |x| (layers that share an input hold the same act_max tensor)."""
+    stats = [(x, a) for x, a in calib] + [(l.w, l.w_max) for l in layers]
+    for part in _chunks(stats):
+        capi.sq_calib_absmax_batched([x for x, _ in part], [a for _, a in part], False, stream)
+    for part in _chunks(list(layers)):
+        capi.sq_smooth_factors_batched([l.act_max for l in part], [l.w_max for l in part], [l.alpha for l in part],
+                                       [l.s for l in part], [l.inv_s for l in part], [l.act_scale for l in part],
+                                       stream)
+        capi.sq_quant_weight_batched([l.w for l in part], [l.s for l in part], [l.wq for l in part],
+                                     [l.w_scale for l in part], stream)

@@ -314,6 +314,15 @@ sq_status sq_alpha_search(const void* const* x_batches, sq_dtype xt, int n_batch
  *   w_scale[i] from w[i] ([n[i], k[i]] of type wt[i]) and s[i]. One launch per
  *   distinct (element type, row-length class) among the items; the 13B block's
  *   seven weights take two.
+ * sq_smooth_quant_act_batched [kwkr §3.2, §5.2; ADR Key design items 4-5]:
+ *   xq[i] from x[i] ([m[i], k[i]] of type xt[i]), inv_s[i], act_scale[i]. One
+ *   launch; items that name the same input (same pointer, type and shape: q, k
+ *   and v, or gate and up) read it once, up to four consumers per pass.
+ * sq_w8a8_gemm_batched [pwwt §3.1]: y[i] (type yt[i]) and, when acc_out is
+ *   not NULL and acc_out[i] is not NULL, acc_out[i] from xq[i] [m[i], k[i]],
+ *   wq[i] [n[i], k[i]], act_scale[i], w_scale[i]. Products that pick the same
+ *   large tile and output type share one launch (the next product's tiles
+ *   start as compute units free up); small-m products get a launch each.
  */
 #define SQ_MAX_BATCH 16
 
@@ -329,6 +338,17 @@ sq_status sq_smooth_factors_batched(int count, const float* const* act_max,
 sq_status sq_quant_weight_batched(int count, const void* const* w, const sq_dtype* wt,
                                   const int64_t* n, const int64_t* k, const float* const* s,
                                   int8_t* const* wq, float* const* w_scale, hipStream_t stream);
+
+sq_status sq_smooth_quant_act_batched(int count, const void* const* x, const sq_dtype* xt,
+                                      const int64_t* m, const int64_t* k, const float* const* inv_s,
+                                      const float* const* act_scale, int8_t* const* xq,
+                                      hipStream_t stream);
+
+sq_status sq_w8a8_gemm_batched(int count, const int8_t* const* xq, const int8_t* const* wq,
+                               const int64_t* m, const int64_t* n, const int64_t* k,
+                               const float* const* act_scale, const float* const* w_scale,
+                               void* const* y, const sq_dtype* yt, int32_t* const* acc_out,
+                               hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* sq_status_string(sq_status status);

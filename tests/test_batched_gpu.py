@@ -147,3 +147,106 @@ def test_block_prepare_batched_equals_single_calls():
         for key in ("w_max", "s", "inv_s", "wq", "ws"):
             assert torch.equal(b1[key], b2[key]), (p, key)
         assert torch.equal(b1["a"][:1], b2["a"][:1]), (p, "act_scale")
+
+
+def test_quant_act_batched():
+    """Inputs shared by up to five consumers (five split over two passes), mixed
+    element types, an empty batch; every consumer's codes bit-exact."""
+    import torch
+    g = synth.rng(4600)
+    xa = synth.activations(4601, 300, 1088, synth.outlier_channels(4602, 1088), bf16=True)
+    xb = synth.activations(4603, 2048, 5120, synth.outlier_channels(4604, 5120), bf16=True)
+    xc = synth.activations(4605, 37, 320, None, bf16=False)
+    xd = synth.activations(4606, 513, 13824, synth.outlier_channels(4607, 13824), bf16=True)
+    xe = np.zeros((0, 256), np.uint16)
+    inputs = {"a": xa, "b": xb, "c": xc, "d": xd, "e": xe}
+    dev_in = {n: (_t(v) if v.size else torch.empty((0, 256), dtype=torch.bfloat16, device=dev()))
+              for n, v in inputs.items()}
+    plan = ["a", "a", "a", "a", "a", "b", "b", "c", "d", "e", "b"]  # five consumers of a, three of b
+    inv_s, scales, outs = [], [], []
+    for i, name in enumerate(plan):
+        x = inputs[name]
+        k = x.shape[1]
+        inv = g.uniform(0.02, 3.0, k).astype(np.float32)
+        xf = synth.bf16_bits_to_f32(x) if x.dtype == np.uint16 else x
+        a = np.float32(0.7 * np.abs(xf * inv).max() / 127.0) if x.size else np.float32(0.01)  # some saturation
+        inv_s.append(inv)
+        scales.append(np.array([a, 0, 0, 0], np.float32))
+        outs.append(torch.full(x.shape, 3, dtype=torch.int8, device=dev()))
+    capi.sq_smooth_quant_act_batched([dev_in[n] for n in plan], [_t(v) for v in inv_s], [_t(v) for v in scales],
+                                     outs)
+    torch.cuda.synchronize()
+    for i, name in enumerate(plan):
+        x = inputs[name]
+        if not x.size:
+            assert outs[i].numel() == 0
+            continue
+        assert_bitexact(f"xq item {i} ({name})", _h(outs[i]), ORACLE.quant_act(x, inv_s[i], scales[i][0]))
+
+
+def test_gemm_batched():
+    """Products that share a large tile, one that picks another width, a skinny
+    (m <= 64) and a register-staged one, mixed output types, some with the int32
+    accumulator: every output bit-exact against the oracle."""
+    import torch
+    cases = [(512, 5120, 192, True, True), (300, 5120, 320, False, False), (1024, 8192, 128, True, False),
+             (40, 1000, 704, True, True), (200, 600, 256, False, True), (256, 4112, 64, True, False),
+             (0, 512, 64, True, False), (2048, 5120, 64, True, True)]
+    tilings = {capi.sq_gemm_tiling(m, n) for m, n, *_ in cases if m}
+    assert {(256, 128), (256, 160), (64, 16)} <= tilings, tilings
+    g = synth.rng(4700)
+    xqs, wqs, scs, wss, ys, accs, host = [], [], [], [], [], [], []
+    for m, n, k, bf16, with_acc in cases:
+        xq = g.integers(-127, 128, (m, k), dtype=np.int8)
+        wq = g.integers(-127, 128, (n, k), dtype=np.int8)
+        ws = g.uniform(1e-4, 1e-2, n).astype(np.float32)
+        a = np.array([g.uniform(0.005, 0.05), 0, 0, 0], np.float32)
+        host.append((xq, wq, ws, a))
+        xqs.append(_t(xq) if m else torch.empty((0, k), dtype=torch.int8, device=dev()))
+        wqs.append(_t(wq))
+        scs.append(_t(a))
+        wss.append(_t(ws))
+        ys.append(torch.empty((m, n), dtype=torch.bfloat16 if bf16 else torch.float32, device=dev()))
+        accs.append(torch.empty((m, n), dtype=torch.int32, device=dev()) if with_acc else None)
+    capi.sq_w8a8_gemm_batched(xqs, wqs, scs, wss, ys, accs)
+    torch.cuda.synchronize()
+    for i, ((m, n, k, bf16, with_acc), (xq, wq, ws, a)) in enumerate(zip(cases, host)):
+        if not m:
+            continue
+        racc = ORACLE.gemm_i32(xq, wq)
+        if with_acc:
+            assert_bitexact(f"acc item {i}", _h(accs[i]), racc)
+        assert_bitexact(f"y item {i}", _h(ys[i]), ORACLE.dequant(racc, a[0], ws, bf16=bf16))
+
+
+def test_block_forward_batched_equals_single_calls():
+    """Activation codes and outputs of the 13B block's seven projections from
+    the batched quantizer and the grouped GEMM equal the single calls'."""
+    import torch
+    f32 = dict(dtype=torch.float32, device=dev())
+    rows = 1024
+    groups = {g: _t(synth.c2_group_x(g, rows=rows)) for g in synth.C2_GROUPS}
+    g = synth.rng(4800)
+    projs = []
+    for p, grp, n, k, _ in synth.C2_PROJECTIONS:
+        inv = _t(g.uniform(0.05, 2.0, k).astype(np.float32))
+        a = torch.tensor([g.uniform(0.01, 0.1), 0, 0, 0], **f32)
+        wq = _t(g.integers(-127, 128, (n, k), dtype=np.int8))
+        ws = _t(g.uniform(1e-4, 1e-2, n).astype(np.float32))
+        projs.append((p, groups[grp], inv, a, wq, ws))
+
+    def outputs():
+        return ([torch.empty((rows, x.shape[1]), dtype=torch.int8, device=dev()) for _, x, *_ in projs],
+                [torch.empty((rows, wq.shape[0]), dtype=torch.bfloat16, device=dev()) for *_, wq, _ in projs])
+
+    xq1, y1 = outputs()
+    for (p, x, inv, a, wq, ws), xq, y in zip(projs, xq1, y1):
+        capi.sq_smooth_quant_act(x, inv, a, xq)
+        capi.sq_w8a8_gemm(xq, wq, a, ws, y)
+    xq2, y2 = outputs()
+    capi.sq_smooth_quant_act_batched([x for _, x, *_ in projs], [pr[2] for pr in projs], [pr[3] for pr in projs], xq2)
+    capi.sq_w8a8_gemm_batched(xq2, [pr[4] for pr in projs], [pr[3] for pr in projs], [pr[5] for pr in projs], y2)
+    torch.cuda.synchronize()
+    for (p, *_), a1, a2, b1, b2 in zip(projs, xq1, xq2, y1, y2):
+        assert torch.equal(a1, a2), (p, "xq")
+        assert torch.equal(b1.view(torch.int16), b2.view(torch.int16)), (p, "y")

@@ -385,3 +385,55 @@ def test_batched_validation(lib):
     bad = [list(v) for v in qg]
     bad[4][1] = MIS
     assert qw(2, *bad) == ALIGN
+
+
+def test_batched_act_and_gemm_validation(lib):
+    for name in ("sq_smooth_quant_act_batched", "sq_w8a8_gemm_batched"):
+        assert name in capi.declared_functions() and hasattr(lib, name)
+    B = 0x100000
+    i64, i32 = ctypes.c_int64, ctypes.c_int
+
+    def act(count, xs, dts, ms, ks, inv, sc, xq):
+        keep = [_arr(P, xs), _arr(i32, dts), _arr(i64, ms), _arr(i64, ks), _arr(P, inv), _arr(P, sc), _arr(P, xq)]
+        return lib.sq_smooth_quant_act_batched(count, *[p for _, p in keep], None)
+
+    # two consumers of one input (shared x is allowed)
+    ag = ([A, A], [1, 1], [16, 16], [1024, 1024], [B, B + 0x1000], [B + 0x2000, B + 0x2010],
+          [B + 0x10000, B + 0x20000])
+    assert lib.sq_smooth_quant_act_batched(2, *([None] * 7), None) == NULL
+    assert act(0, *ag) == SHAPE
+    bad = [list(v) for v in ag]
+    bad[3][1] = 1000
+    assert act(2, *bad) == SHAPE
+    bad = [list(v) for v in ag]
+    bad[6][1] = bad[6][0] + 8192  # 16 x 1024 codes of item 0 overlap item 1's output
+    assert act(2, *bad) == SHAPE
+    bad = [list(v) for v in ag]
+    bad[6][1] = A + 1024  # item 1 writes into the input
+    assert act(2, *bad) == SHAPE
+    bad = [list(v) for v in ag]
+    bad[1][0] = 5
+    assert act(2, *bad) == DTYPE
+
+    def gemm(count, xq, wq, ms, ns, ks, sc, ws, ys, yts, acc):
+        keep = [_arr(P, xq), _arr(P, wq), _arr(i64, ms), _arr(i64, ns), _arr(i64, ks), _arr(P, sc), _arr(P, ws),
+                _arr(P, ys), _arr(i32, yts)]
+        acc_arr = _arr(P, acc) if acc is not None else (None, None)
+        return lib.sq_w8a8_gemm_batched(count, *[p for _, p in keep], acc_arr[1], None)
+
+    gg = ([A, A], [A + 0x40000, A + 0x80000], [64, 64], [128, 128], [1024, 1024], [B, B], [B + 0x100, B + 0x300],
+          [B + 0x10000, B + 0x20000], [1, 1], None)
+    assert lib.sq_w8a8_gemm_batched(2, *([None] * 10), None, None) == NULL
+    assert gemm(17, *[v * 9 if isinstance(v, list) else v for v in gg]) == SHAPE
+    bad = [list(v) if isinstance(v, list) else v for v in gg]
+    bad[4][0] = 131072 + 64  # k above SQ_MAX_GEMM_K, the exact-accumulator limit
+    assert gemm(2, *bad) == SHAPE
+    bad = [list(v) if isinstance(v, list) else v for v in gg]
+    bad[7][1] = bad[7][0] + 64  # the two outputs overlap
+    assert gemm(2, *bad) == SHAPE
+    bad = [list(v) if isinstance(v, list) else v for v in gg]
+    bad[9] = [None, MIS]  # item 1's acc_out misaligned
+    assert gemm(2, *bad) == ALIGN
+    bad = [list(v) if isinstance(v, list) else v for v in gg]
+    bad[9] = [bad[7][1], None]  # item 0's acc_out over item 1's y
+    assert gemm(2, *bad) == SHAPE

@@ -66,6 +66,8 @@ def _declare(lib):
         "sq_calib_absmax_batched": [c.c_int, P, P, P, P, P, c.c_int, P],
         "sq_smooth_factors_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_quant_weight_batched": [c.c_int, P, P, P, P, P, P, P, P],
+        "sq_smooth_quant_act_batched": [c.c_int, P, P, P, P, P, P, P, P],
+        "sq_w8a8_gemm_batched": [c.c_int, P, P, P, P, P, P, P, P, P, P, P],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -230,6 +232,38 @@ def sq_quant_weight_batched(ws, ss, wqs, w_scales, stream=None):
             _host_array(ctypes.c_int64, [w.shape[0] for w in ws]), _host_array(ctypes.c_int64, [w.shape[1] for w in ws]),
             _ptrs(ss, "ss"), _ptrs(wqs, "wqs"), _ptrs(w_scales, "w_scales")]
     _check("sq_quant_weight_batched", load().sq_quant_weight_batched(count, *[a for _, a in keep], _stream(stream)))
+
+
+def sq_smooth_quant_act_batched(xs, inv_ss, act_scales, xqs, stream=None):
+    """sq_smooth_quant_act for several projections in one launch (a shared
+    input tensor is read once for all of its consumers)."""
+    count = len(xs)
+    if not all(len(v) == count for v in (inv_ss, act_scales, xqs)):
+        raise ValueError("per-item lists differ in length")
+    keep = [_ptrs(xs, "xs"), _host_array(ctypes.c_int, [_dtype_code(x) for x in xs]),
+            _host_array(ctypes.c_int64, [x.shape[0] for x in xs]), _host_array(ctypes.c_int64, [x.shape[1] for x in xs]),
+            _ptrs(inv_ss, "inv_ss"), _ptrs(act_scales, "act_scales"), _ptrs(xqs, "xqs")]
+    _check("sq_smooth_quant_act_batched", load().sq_smooth_quant_act_batched(count, *[a for _, a in keep],
+                                                                             _stream(stream)))
+
+
+def sq_w8a8_gemm_batched(xqs, wqs, act_scales, w_scales, ys, acc_outs=None, stream=None):
+    """sq_w8a8_gemm for several products; those with the same large tile and
+    output type share one launch."""
+    count = len(xqs)
+    if not all(len(v) == count for v in (wqs, act_scales, w_scales, ys)):
+        raise ValueError("per-item lists differ in length")
+    keep = [_ptrs(xqs, "xqs"), _ptrs(wqs, "wqs"), _host_array(ctypes.c_int64, [x.shape[0] for x in xqs]),
+            _host_array(ctypes.c_int64, [w.shape[0] for w in wqs]), _host_array(ctypes.c_int64, [x.shape[1] for x in xqs]),
+            _ptrs(act_scales, "act_scales"), _ptrs(w_scales, "w_scales"), _ptrs(ys, "ys"),
+            _host_array(ctypes.c_int, [_dtype_code(y) for y in ys])]
+    acc = None
+    if acc_outs is not None:
+        if len(acc_outs) != count:
+            raise ValueError("acc_outs differs in length")
+        acc = _host_array(ctypes.c_void_p, [_opt(a, f"acc_outs[{i}]").value for i, a in enumerate(acc_outs)])
+    _check("sq_w8a8_gemm_batched", load().sq_w8a8_gemm_batched(count, *[a for _, a in keep],
+                                                               acc[1] if acc else ctypes.c_void_p(0), _stream(stream)))
 
 
 def _opt(t, what: str):

@@ -18,6 +18,7 @@
 
 namespace {
 
+using sqd::item_of;
 using sqd::u32x4;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -133,12 +134,6 @@ struct AbsTable {
     int64_t rows[sqk::kMaxBatch], kvec[sqk::kMaxBatch], k[sqk::kMaxBatch], rpb[sqk::kMaxBatch];
     int32_t strips[sqk::kMaxBatch], eb[sqk::kMaxBatch];
 };
-
-__device__ __forceinline__ int item_of(const int32_t* first, int count, int32_t b) {
-    int i = 0;
-    while (i + 1 < count && b >= first[i + 1]) ++i;
-    return i;
-}
 
 __global__ __launch_bounds__(kAbsThreads) void absmax_batched_kernel(const AbsTable tab) {
     __shared__ u32x4 part[kAbsThreads];

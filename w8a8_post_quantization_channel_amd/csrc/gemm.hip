@@ -484,10 +484,24 @@ constexpr int dma_stages() {
     return 3 * (kDmaBM + 32 * TN) * kDmaBK <= kLdsBytes ? 3 : 2;
 }
 
+// XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD takes a
+// contiguous range of tiles (b < ntiles maps onto every tile exactly once)
+__device__ __forceinline__ int xcd_tile(int b, int ntiles) {
+    const int xcd = b & 7, slot = b >> 3;
+    const int per = ntiles >> 3, rem = ntiles & 7;
+    return xcd * per + min(xcd, rem) + slot;
+}
+
+template <int TN>
+constexpr int dma_lds_bytes() {
+    return dma_stages<TN>() * (kDmaBM + 32 * TN) * kDmaBK;
+}
+
+// One 256 x 32*TN output tile; t is the tile's index after the XCD remap.
 template <class Op, int TN, class Epi>
-__global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
-                                                       int64_t M, int64_t N, int64_t Kb, int tiles_m, int tiles_n,
-                                                       Epi epi) {
+__device__ __forceinline__ void dma_tile(const int8_t* __restrict__ A, const int8_t* __restrict__ B, int64_t M,
+                                         int64_t N, int64_t Kb, int tiles_m, int tiles_n, int t, Epi& epi,
+                                         char* lds) {
     constexpr int BM = kDmaBM, BN = 32 * TN;
     constexpr int ROWS = BM + BN;                    // a multiple of 32: whole load rounds
     constexpr int STAGE = ROWS * kDmaBK;
@@ -500,23 +514,14 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
     static_assert(NF <= NMMA + 2, "fragment reads interleave with the MFMAs");
     static_assert((NS - 2) * L < 64, "vmcnt range");
     static_assert(4 * 32 * BN * 4 <= NS * STAGE, "the epilogue transpose fits in the stages");
-    __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
 
     const int lane = threadIdx.x & 63;
     // the wave index is uniform across the wave; saying so keeps the load
     // descriptors and LDS destinations in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // tile order: each XCD (workgroup b runs on XCD b % 8) takes a contiguous
-    // range of tiles, and tiles are grouped 4 tile-rows at a time so an XCD's
-    // range covers a compact block of the output (shared A and B panels in L2)
-    const int ntiles = tiles_m * tiles_n;
-    int t = blockIdx.x;
-    {
-        const int xcd = t & 7, slot = t >> 3;
-        const int per = ntiles >> 3, rem = ntiles & 7;
-        t = xcd * per + min(xcd, rem) + slot;
-    }
+    // tiles are grouped 4 tile-rows at a time so an XCD's range of tiles
+    // covers a compact block of the output (shared A and B panels in L2)
     constexpr int GM = 4;
     const int group = t / (GM * tiles_n), in_group = t % (GM * tiles_n);
     const int group_rows = min(GM, tiles_m - group * GM);
@@ -713,6 +718,43 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict_
     }
     __syncthreads();
     epi.end(lds);
+}
+
+template <class Op, int TN, class Epi>
+__global__ __launch_bounds__(256) void gemm_dma_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+                                                       int64_t M, int64_t N, int64_t Kb, int tiles_m, int tiles_n,
+                                                       Epi epi) {
+    __shared__ __attribute__((aligned(1024))) char lds[dma_lds_bytes<TN>()];
+    dma_tile<Op, TN, Epi>(A, B, M, N, Kb, tiles_m, tiles_n, xcd_tile(blockIdx.x, tiles_m * tiles_n), epi, lds);
+}
+
+// Several products in one launch (the projections of a block): item i owns
+// the blocks [first[i], first[i + 1]), a multiple of 8 apart, so a block's
+// XCD and its tile are those of a launch of item i alone; blocks past the
+// item's tile count return at once. The next product's tiles start as soon
+// as compute units free up, instead of after the previous launch drains.
+struct GemmTable {
+    int count;
+    int32_t first[sqk::kMaxBatch + 1];
+    const int8_t* A[sqk::kMaxBatch];
+    const int8_t* B[sqk::kMaxBatch];
+    const float* act_scale[sqk::kMaxBatch];
+    const float* w_scale[sqk::kMaxBatch];
+    void* y[sqk::kMaxBatch];
+    int32_t* acc_out[sqk::kMaxBatch];
+    int64_t M[sqk::kMaxBatch], N[sqk::kMaxBatch], Kb[sqk::kMaxBatch];
+    int32_t tiles_m[sqk::kMaxBatch], tiles_n[sqk::kMaxBatch];
+};
+
+template <class Op, int TN, bool kBF16Out>
+__global__ __launch_bounds__(256) void gemm_dma_grouped_kernel(const GemmTable tab) {
+    __shared__ __attribute__((aligned(1024))) char lds[dma_lds_bytes<TN>()];
+    const int i = sqd::item_of(tab.first, tab.count, blockIdx.x);
+    const int b = blockIdx.x - tab.first[i], ntiles = tab.tiles_m[i] * tab.tiles_n[i];
+    if (b >= ntiles) return;
+    EpiDequant<kBF16Out> epi{tab.act_scale[i], tab.w_scale[i], tab.y[i], tab.acc_out[i], tab.M[i], tab.N[i], 0.0f};
+    dma_tile<Op, TN, EpiDequant<kBF16Out>>(tab.A[i], tab.B[i], tab.M[i], tab.N[i], tab.Kb[i], tab.tiles_m[i],
+                                           tab.tiles_n[i], xcd_tile(b, ntiles), epi, lds);
 }
 
 // ---- skinny kernel (decode: m <= 64) -------------------------------------------
@@ -978,6 +1020,80 @@ __global__ __launch_bounds__(256) void ref_gemm_f32_kernel(const float* __restri
 }  // namespace
 
 namespace sqk {
+
+template <int TN>
+hipError_t launch_grouped(const GemmTable& tab, int64_t blocks, bool bf16, hipStream_t stream) {
+    if (bf16)
+        gemm_dma_grouped_kernel<OpI8, TN, true><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(tab);
+    else
+        gemm_dma_grouped_kernel<OpI8, TN, false><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(tab);
+    return hipGetLastError();
+}
+
+int dma_width(TileCfg c) {
+    switch (c) {
+        case kD256: return 8;
+        case kD224: return 7;
+        case kD192: return 6;
+        case kD160: return 5;
+        case kD128: return 4;
+        default: return 0;
+    }
+}
+
+hipError_t gemm_dequant_batched(const GemmItem* items, int count, hipStream_t stream) {
+    bool done[kMaxBatch] = {};
+    for (int i = 0; i < count; ++i) {
+        if (done[i]) continue;
+        done[i] = true;
+        const GemmItem& it = items[i];
+        if (it.m == 0 || it.n == 0) continue;
+        const int tn = dma_width(choose_cfg(it.m, it.n));
+        if (tn == 0) {  // small m: the register-staged or skinny kernel, one launch per item
+            const hipError_t e = gemm_dequant(it.xq, it.wq, it.m, it.n, it.k, it.act_scale, it.w_scale, it.y, it.yt,
+                                              it.acc_out, stream);
+            if (e != hipSuccess) return e;
+            continue;
+        }
+        GemmTable tab{};
+        int64_t blocks = 0;
+        for (int j = i; j < count; ++j) {
+            const GemmItem& jt = items[j];
+            if (j > i && (done[j] || jt.m == 0 || jt.n == 0 || jt.yt != it.yt ||
+                          dma_width(choose_cfg(jt.m, jt.n)) != tn))
+                continue;
+            done[j] = true;
+            const int c = tab.count++;
+            const int64_t tiles_m = (jt.m + kDmaBM - 1) / kDmaBM, tiles_n = (jt.n + 32 * tn - 1) / (32 * tn);
+            tab.first[c] = (int32_t)blocks;
+            tab.A[c] = jt.xq;
+            tab.B[c] = jt.wq;
+            tab.act_scale[c] = jt.act_scale;
+            tab.w_scale[c] = jt.w_scale;
+            tab.y[c] = jt.y;
+            tab.acc_out[c] = jt.acc_out;
+            tab.M[c] = jt.m;
+            tab.N[c] = jt.n;
+            tab.Kb[c] = jt.k;
+            tab.tiles_m[c] = (int32_t)tiles_m;
+            tab.tiles_n[c] = (int32_t)tiles_n;
+            blocks += (tiles_m * tiles_n + 7) / 8 * 8;  // whole XCD rounds per item
+            if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+        }
+        tab.first[tab.count] = (int32_t)blocks;
+        const bool bf16 = it.yt == kBF16;
+        hipError_t e = hipErrorInvalidValue;
+        switch (tn) {
+            case 8: e = launch_grouped<8>(tab, blocks, bf16, stream); break;
+            case 7: e = launch_grouped<7>(tab, blocks, bf16, stream); break;
+            case 6: e = launch_grouped<6>(tab, blocks, bf16, stream); break;
+            case 5: e = launch_grouped<5>(tab, blocks, bf16, stream); break;
+            case 4: e = launch_grouped<4>(tab, blocks, bf16, stream); break;
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
 
 hipError_t gemm_dequant(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
                         const float* act_scale, const float* w_scale, void* y, int yt, int32_t* acc_out,

@@ -330,69 +330,95 @@ __global__ __launch_bounds__(256) void quant_weight_long_kernel(const u32x4* __r
 
 constexpr int kActThreads = 256;
 constexpr int kActUnroll = 8;
+constexpr int kActShare = 4;  // consumers of one input quantized in one pass
+
+// Activation inputs of several projections in one launch. Group g is one
+// input x[rows, kvec vectors], read once; its consumers c = cfirst[g] ..
+// cfirst[g + 1] - 1 (the projections fed by that input: q, k and v, or gate
+// and up) each get their codes with their own inv_s and act_scale. Group g
+// owns the blocks [first[g], first[g + 1]), strip-fastest.
+struct ActTable {
+    int count;
+    int32_t first[sqk::kMaxBatch + 1];
+    int32_t cfirst[sqk::kMaxBatch + 1];
+    const u32x4* x[sqk::kMaxBatch];
+    int64_t rows[sqk::kMaxBatch], kvec[sqk::kMaxBatch], rpb[sqk::kMaxBatch];
+    int32_t strips[sqk::kMaxBatch], eb[sqk::kMaxBatch];
+    const float* inv_s[sqk::kMaxBatch];
+    const float* act_scale[sqk::kMaxBatch];
+    int8_t* xq[sqk::kMaxBatch];
+};
 
 // A lane owns one 16-byte column vector (E = 16 / EB elements) of the input
-// and keeps its E inv_s values in registers; the four waves of a block walk
-// interleaved rows, so each wave instruction moves one contiguous 1 KB run.
+// and keeps the E inv_s values of each consumer in registers; the four waves
+// of a block walk interleaved rows, so each wave instruction moves one
+// contiguous 1 KB run.
 template <int EB, bool FP8>
-__global__ __launch_bounds__(kActThreads) void quant_act_kernel(const u32x4* __restrict__ x, int64_t rows,
-                                                                int64_t kvec, int64_t rows_per_block,
-                                                                const float* __restrict__ inv_s,
-                                                                const float* __restrict__ act_scale,
-                                                                int8_t* __restrict__ xq) {
+__device__ __forceinline__ void quant_act_block(const ActTable& tab, int g, int64_t strip, int64_t chunk) {
     constexpr int E = 16 / EB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t v = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t kvec = tab.kvec[g];
+    const int64_t v = strip * 64 + lane;
     if (v >= kvec) return;  // no block-level synchronisation below
-    float is[E];
+    const u32x4* x = tab.x[g];
+    const int cf = tab.cfirst[g], nc = tab.cfirst[g + 1] - cf;
+    float is[kActShare][E];
+    float inv_a[kActShare];
 #pragma unroll
-    for (int h = 0; h < E / 4; ++h) {
-        const u32x4 t = ((const u32x4*)(inv_s + v * E))[h];
-        is[4 * h + 0] = __uint_as_float(t.x);
-        is[4 * h + 1] = __uint_as_float(t.y);
-        is[4 * h + 2] = __uint_as_float(t.z);
-        is[4 * h + 3] = __uint_as_float(t.w);
+    for (int c = 0; c < kActShare; ++c) {
+        if (c >= nc) break;
+#pragma unroll
+        for (int h = 0; h < E / 4; ++h) {
+            const u32x4 t = ((const u32x4*)(tab.inv_s[cf + c] + v * E))[h];
+            is[c][4 * h + 0] = __uint_as_float(t.x);
+            is[c][4 * h + 1] = __uint_as_float(t.y);
+            is[c][4 * h + 2] = __uint_as_float(t.z);
+            is[c][4 * h + 3] = __uint_as_float(t.w);
+        }
+        inv_a[c] = __fdiv_rn(1.0f, tab.act_scale[cf + c][0]);
     }
-    const float inv_a = __fdiv_rn(1.0f, act_scale[0]);
-    const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
-    const int64_t r1 = min(rows, r0 + rows_per_block);
+    const int64_t r0 = chunk * tab.rpb[g];
+    const int64_t r1 = min(tab.rows[g], r0 + tab.rpb[g]);
     auto quantize = [&](const u32x4& raw, int64_t r) {
         float e[E];
         sqd::unpack16<E>(raw, e);
-        if constexpr (FP8) {
-            float t[E];
 #pragma unroll
-            for (int u = 0; u < E; ++u) t[u] = __fmul_rn(__fmul_rn(e[u], is[u]), inv_a);
-            int8_t* dst = xq + (r * kvec + v) * E;
-            if constexpr (E == 8)
-                *(sqd::u32x2*)dst = sqd::u32x2{sqd::pack4_e4m3(t[0], t[1], t[2], t[3]),
-                                               sqd::pack4_e4m3(t[4], t[5], t[6], t[7])};
-            else
-                *(uint32_t*)dst = sqd::pack4_e4m3(t[0], t[1], t[2], t[3]);
-        } else {
-            // clamp to [-127, 127], then round half to even with the fp32
-            // adder (fl(v + 1.5 * 2^23) keeps rint(v) in its low byte for
-            // |v| < 2^22; rint and the integer-bounded clamp commute, so this
-            // is clamp(rint(v))), and gather the low bytes with v_perm
-            uint32_t b[E];
+        for (int c = 0; c < kActShare; ++c) {
+            if (c >= nc) break;
+            int8_t* dst = tab.xq[cf + c] + (r * kvec + v) * E;
+            if constexpr (FP8) {
+                float t[E];
 #pragma unroll
-            for (int t = 0; t < E; ++t) {
-                const float q = __builtin_fminf(
-                    __builtin_fmaxf(__fmul_rn(__fmul_rn(e[t], is[t]), inv_a), -sqd::kQmax), sqd::kQmax);
-                b[t] = __float_as_uint(__fadd_rn(q, 12582912.0f));
+                for (int u = 0; u < E; ++u) t[u] = __fmul_rn(__fmul_rn(e[u], is[c][u]), inv_a[c]);
+                if constexpr (E == 8)
+                    *(sqd::u32x2*)dst = sqd::u32x2{sqd::pack4_e4m3(t[0], t[1], t[2], t[3]),
+                                                   sqd::pack4_e4m3(t[4], t[5], t[6], t[7])};
+                else
+                    *(uint32_t*)dst = sqd::pack4_e4m3(t[0], t[1], t[2], t[3]);
+            } else {
+                // clamp to [-127, 127], then round half to even with the fp32
+                // adder (fl(v + 1.5 * 2^23) keeps rint(v) in its low byte for
+                // |v| < 2^22; rint and the integer-bounded clamp commute, so
+                // this is clamp(rint(v))), and gather the low bytes with v_perm
+                uint32_t b[E];
+#pragma unroll
+                for (int t = 0; t < E; ++t) {
+                    const float q = __builtin_fminf(
+                        __builtin_fmaxf(__fmul_rn(__fmul_rn(e[t], is[c][t]), inv_a[c]), -sqd::kQmax), sqd::kQmax);
+                    b[t] = __float_as_uint(__fadd_rn(q, 12582912.0f));
+                }
+                uint32_t w[E / 4];
+#pragma unroll
+                for (int d = 0; d < E / 4; ++d) {
+                    const uint32_t lo = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0c0c0400u);
+                    const uint32_t hi = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0c0c0400u);
+                    w[d] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                }
+                if constexpr (E == 8)
+                    *(sqd::u32x2*)dst = sqd::u32x2{w[0], w[1]};
+                else
+                    *(uint32_t*)dst = w[0];
             }
-            uint32_t w[E / 4];
-#pragma unroll
-            for (int d = 0; d < E / 4; ++d) {
-                const uint32_t lo = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0c0c0400u);
-                const uint32_t hi = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0c0c0400u);
-                w[d] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-            }
-            int8_t* dst = xq + (r * kvec + v) * E;
-            if constexpr (E == 8)
-                *(sqd::u32x2*)dst = sqd::u32x2{w[0], w[1]};
-            else
-                *(uint32_t*)dst = w[0];
         }
     };
     int64_t r = r0 + wave;
@@ -404,6 +430,17 @@ __global__ __launch_bounds__(kActThreads) void quant_act_kernel(const u32x4* __r
         for (int u = 0; u < kActUnroll; ++u) quantize(t[u], r + 4 * u);
     }
     for (; r < r1; r += 4) quantize(__builtin_nontemporal_load(x + r * kvec + v), r);
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kActThreads) void quant_act_batched_kernel(const ActTable tab) {
+    const int g = sqd::item_of(tab.first, tab.count, blockIdx.x);
+    const int32_t local = blockIdx.x - tab.first[g];
+    const int64_t strip = local % tab.strips[g], chunk = local / tab.strips[g];
+    if (tab.eb[g] == 2)
+        quant_act_block<2, FP8>(tab, g, strip, chunk);
+    else
+        quant_act_block<4, FP8>(tab, g, strip, chunk);
 }
 
 int device_cus() {
@@ -533,39 +570,70 @@ hipError_t quant_weight_fp8(const void* w, int wt, int64_t n, int64_t k, const f
     return quant_weight_items<true>(&item, 1, stream);
 }
 
+// Items with the same input (pointer, type and shape) form one group, up to
+// kActShare consumers each, in first-appearance order.
 template <bool FP8>
-hipError_t quant_act_t(const void* x, int xt, int64_t m, int64_t k, const float* inv_s, const float* act_scale,
-                       int8_t* xq, hipStream_t stream) {
-    if (m == 0) return hipSuccess;
-    const int eb = elem_bytes(xt);
-    const int64_t kvec = k * eb / 16;
-    const int64_t strips = (kvec + 63) / 64;
-    const int64_t granule = 4 * kActUnroll;
-    int64_t target_chunks = std::max<int64_t>(1, 8192 / strips);
-    int64_t rpb = (m + target_chunks - 1) / target_chunks;
-    rpb = std::max<int64_t>(granule, (rpb + granule - 1) / granule * granule);
-    int64_t chunks = (m + rpb - 1) / rpb;
-    if (chunks > 65535) {
-        rpb = (m + 65534) / 65535;
-        rpb = (rpb + granule - 1) / granule * granule;
-        chunks = (m + rpb - 1) / rpb;
+hipError_t quant_act_items(const ActItem* items, int count, hipStream_t stream) {
+    ActTable tab{};
+    bool done[kMaxBatch] = {};
+    int ng = 0, nc = 0;
+    int64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        if (done[i] || items[i].m == 0) continue;
+        const int eb = elem_bytes(items[i].xt);
+        const int64_t kvec = items[i].k * eb / 16;
+        const int64_t strips = (kvec + 63) / 64;
+        const int64_t granule = 4 * kActUnroll;
+        const int64_t target_chunks = std::max<int64_t>(1, 8192 / strips);
+        int64_t rpb = (items[i].m + target_chunks - 1) / target_chunks;
+        rpb = std::max<int64_t>(granule, (rpb + granule - 1) / granule * granule);
+        const int64_t chunks = (items[i].m + rpb - 1) / rpb;
+        tab.first[ng] = (int32_t)blocks;
+        tab.cfirst[ng] = nc;
+        tab.x[ng] = (const u32x4*)items[i].x;
+        tab.rows[ng] = items[i].m;
+        tab.kvec[ng] = kvec;
+        tab.rpb[ng] = rpb;
+        tab.strips[ng] = (int32_t)strips;
+        tab.eb[ng] = eb;
+        int shared = 0;
+        for (int j = i; j < count && shared < kActShare; ++j) {
+            if (done[j] || items[j].x != items[i].x || items[j].xt != items[i].xt || items[j].m != items[i].m ||
+                items[j].k != items[i].k)
+                continue;
+            done[j] = true;
+            tab.inv_s[nc] = items[j].inv_s;
+            tab.act_scale[nc] = items[j].act_scale;
+            tab.xq[nc] = items[j].xq;
+            ++nc;
+            ++shared;
+        }
+        blocks += strips * chunks;
+        ++ng;  // consumers of this input beyond kActShare start a group of their own further on
     }
-    const dim3 grid((unsigned)strips, (unsigned)chunks), block(kActThreads);
-    if (eb == 2)
-        quant_act_kernel<2, FP8><<<grid, block, 0, stream>>>((const u32x4*)x, m, kvec, rpb, inv_s, act_scale, xq);
-    else
-        quant_act_kernel<4, FP8><<<grid, block, 0, stream>>>((const u32x4*)x, m, kvec, rpb, inv_s, act_scale, xq);
+    if (ng == 0) return hipSuccess;
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    tab.count = ng;
+    tab.first[ng] = (int32_t)blocks;
+    tab.cfirst[ng] = nc;
+    quant_act_batched_kernel<FP8><<<dim3((unsigned)blocks), dim3(kActThreads), 0, stream>>>(tab);
     return hipGetLastError();
 }
 
 hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const float* inv_s, const float* act_scale,
                      int8_t* xq, hipStream_t stream) {
-    return quant_act_t<false>(x, xt, m, k, inv_s, act_scale, xq, stream);
+    const ActItem item{x, xt, m, k, inv_s, act_scale, xq};
+    return quant_act_items<false>(&item, 1, stream);
+}
+
+hipError_t quant_act_batched(const ActItem* items, int count, hipStream_t stream) {
+    return quant_act_items<false>(items, count, stream);
 }
 
 hipError_t quant_act_fp8(const void* x, int xt, int64_t m, int64_t k, const float* inv_s, const float* act_scale,
                          uint8_t* xq, hipStream_t stream) {
-    return quant_act_t<true>(x, xt, m, k, inv_s, act_scale, (int8_t*)xq, stream);
+    const ActItem item{x, xt, m, k, inv_s, act_scale, (int8_t*)xq};
+    return quant_act_items<true>(&item, 1, stream);
 }
 
 }  // namespace sqk

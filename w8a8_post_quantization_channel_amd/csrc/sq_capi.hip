@@ -80,6 +80,31 @@ sq_status check_quant_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, c
     return SQ_OK;
 }
 
+sq_status check_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* inv_s,
+                          const float* act_scale, const int8_t* xq) {
+    if (!inv_s || !act_scale || (m > 0 && (!x || !xq))) return SQ_ERR_NULL;
+    if (!valid_dtype(xt)) return SQ_ERR_DTYPE;
+    if (m < 0 || !valid_k(k)) return SQ_ERR_SHAPE;
+    if (!aligned16(inv_s) || !aligned16(act_scale) || (m > 0 && (!aligned16(x) || !aligned16(xq))))
+        return SQ_ERR_ALIGN;
+    return SQ_OK;
+}
+
+sq_status check_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k, const float* act_scale,
+                     const float* w_scale, const void* y, sq_dtype yt, const int32_t* acc_out) {
+    const bool work = m > 0 && n > 0;
+    if (!act_scale || (work && (!xq || !wq || !w_scale || !y))) return SQ_ERR_NULL;
+    if (!valid_dtype(yt)) return SQ_ERR_DTYPE;
+    if (m < 0 || n < 0 || !valid_k(k) || k > SQ_MAX_GEMM_K) return SQ_ERR_SHAPE;
+    // tile counts are int on the device side
+    if ((m + 127) / 128 * ((n + 127) / 128) > INT32_MAX / 2) return SQ_ERR_SHAPE;
+    if (!aligned16(act_scale) ||
+        (work && (!aligned16(xq) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) ||
+                  (acc_out && !aligned16(acc_out)))))
+        return SQ_ERR_ALIGN;
+    return SQ_OK;
+}
+
 // Byte ranges named by the items of a batched call: an output range of one
 // item may not overlap any range of another item.
 struct Ranges {
@@ -87,7 +112,7 @@ struct Ranges {
         int item;
         uintptr_t lo, hi;
         bool out;
-    } r[5 * SQ_MAX_BATCH];
+    } r[6 * SQ_MAX_BATCH];
     int n = 0;
     void add(int item, const void* p, int64_t bytes, bool out) {
         if (p && bytes > 0) r[n++] = R{item, (uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes, out};
@@ -204,28 +229,61 @@ sq_status sq_quant_weight_batched(int count, const void* const* w, const sq_dtyp
 
 sq_status sq_smooth_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* inv_s,
                               const float* act_scale, int8_t* xq, hipStream_t stream) {
-    if (!inv_s || !act_scale || (m > 0 && (!x || !xq))) return SQ_ERR_NULL;
-    if (!valid_dtype(xt)) return SQ_ERR_DTYPE;
-    if (m < 0 || !valid_k(k)) return SQ_ERR_SHAPE;
-    if (!aligned16(inv_s) || !aligned16(act_scale) || (m > 0 && (!aligned16(x) || !aligned16(xq))))
-        return SQ_ERR_ALIGN;
+    const sq_status st = check_quant_act(x, xt, m, k, inv_s, act_scale, xq);
+    if (st != SQ_OK) return st;
     return hip_status(sqk::quant_act(x, xt, m, k, inv_s, act_scale, xq, stream));
+}
+
+sq_status sq_smooth_quant_act_batched(int count, const void* const* x, const sq_dtype* xt, const int64_t* m,
+                                      const int64_t* k, const float* const* inv_s, const float* const* act_scale,
+                                      int8_t* const* xq, hipStream_t stream) {
+    if (!x || !xt || !m || !k || !inv_s || !act_scale || !xq) return SQ_ERR_NULL;
+    if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
+    Ranges rg;
+    sqk::ActItem items[SQ_MAX_BATCH];
+    for (int i = 0; i < count; ++i) {
+        const sq_status st = check_quant_act(x[i], xt[i], m[i], k[i], inv_s[i], act_scale[i], xq[i]);
+        if (st != SQ_OK) return st;
+        rg.add(i, x[i], m[i] * k[i] * (xt[i] == SQ_BF16 ? 2 : 4), false);
+        rg.add(i, inv_s[i], k[i] * 4, false);
+        rg.add(i, act_scale[i], 4, false);
+        rg.add(i, xq[i], m[i] * k[i], true);
+        items[i] = sqk::ActItem{x[i], xt[i], m[i], k[i], inv_s[i], act_scale[i], xq[i]};
+    }
+    if (rg.overlap()) return SQ_ERR_SHAPE;
+    return hip_status(sqk::quant_act_batched(items, count, stream));
 }
 
 sq_status sq_w8a8_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
                        const float* act_scale, const float* w_scale, void* y, sq_dtype yt, int32_t* acc_out,
                        hipStream_t stream) {
-    const bool work = m > 0 && n > 0;
-    if (!act_scale || (work && (!xq || !wq || !w_scale || !y))) return SQ_ERR_NULL;
-    if (!valid_dtype(yt)) return SQ_ERR_DTYPE;
-    if (m < 0 || n < 0 || !valid_k(k) || k > SQ_MAX_GEMM_K) return SQ_ERR_SHAPE;
-    // tile counts are int on the device side
-    if ((m + 127) / 128 * ((n + 127) / 128) > INT32_MAX / 2) return SQ_ERR_SHAPE;
-    if (!aligned16(act_scale) ||
-        (work && (!aligned16(xq) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) ||
-                  (acc_out && !aligned16(acc_out)))))
-        return SQ_ERR_ALIGN;
+    const sq_status st = check_gemm(xq, wq, m, n, k, act_scale, w_scale, y, yt, acc_out);
+    if (st != SQ_OK) return st;
     return hip_status(sqk::gemm_dequant(xq, wq, m, n, k, act_scale, w_scale, y, yt, acc_out, stream));
+}
+
+sq_status sq_w8a8_gemm_batched(int count, const int8_t* const* xq, const int8_t* const* wq, const int64_t* m,
+                               const int64_t* n, const int64_t* k, const float* const* act_scale,
+                               const float* const* w_scale, void* const* y, const sq_dtype* yt,
+                               int32_t* const* acc_out, hipStream_t stream) {
+    if (!xq || !wq || !m || !n || !k || !act_scale || !w_scale || !y || !yt) return SQ_ERR_NULL;
+    if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
+    Ranges rg;
+    sqk::GemmItem items[SQ_MAX_BATCH];
+    for (int i = 0; i < count; ++i) {
+        int32_t* acc = acc_out ? acc_out[i] : nullptr;
+        const sq_status st = check_gemm(xq[i], wq[i], m[i], n[i], k[i], act_scale[i], w_scale[i], y[i], yt[i], acc);
+        if (st != SQ_OK) return st;
+        rg.add(i, xq[i], m[i] * k[i], false);
+        rg.add(i, wq[i], n[i] * k[i], false);
+        rg.add(i, act_scale[i], 4, false);
+        rg.add(i, w_scale[i], n[i] * 4, false);
+        rg.add(i, y[i], m[i] * n[i] * (yt[i] == SQ_BF16 ? 2 : 4), true);
+        rg.add(i, acc, m[i] * n[i] * 4, true);
+        items[i] = sqk::GemmItem{xq[i], wq[i], m[i], n[i], k[i], act_scale[i], w_scale[i], y[i], yt[i], acc};
+    }
+    if (rg.overlap()) return SQ_ERR_SHAPE;
+    return hip_status(sqk::gemm_dequant_batched(items, count, stream));
 }
 
 sq_status sq_act_scale(const float* act_max, const float* inv_s, int64_t k, float* act_scale, hipStream_t stream) {

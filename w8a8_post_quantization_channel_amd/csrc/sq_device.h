@@ -161,4 +161,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 
 
+// Batched launches: item i owns the blocks [first[i], first[i + 1]) of a
+// 1-D grid; the item of block b (uniform per block).
+__device__ __forceinline__ int item_of(const int32_t* first, int count, int32_t b) {
+    int i = 0;
+    while (i + 1 < count && b >= first[i + 1]) ++i;
+    return i;
+}
+
 }  // namespace sqd

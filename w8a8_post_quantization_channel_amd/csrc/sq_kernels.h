@@ -96,10 +96,36 @@ hipError_t quant_weight_batched(const QuantWeightItem* items, int count, hipStre
 hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const float* inv_s,
                      const float* act_scale, int8_t* xq, hipStream_t stream);
 
+// the same for up to kMaxBatch projections in one launch; projections fed by
+// the same input read it once
+struct ActItem {
+    const void* x;
+    int xt;
+    int64_t m, k;
+    const float* inv_s;
+    const float* act_scale;
+    int8_t* xq;
+};
+hipError_t quant_act_batched(const ActItem* items, int count, hipStream_t stream);
+
 // y = fp32(acc) * (act_scale * w_scale[n]) in fp32 or bf16, optional int32 acc
 hipError_t gemm_dequant(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
                         const float* act_scale, const float* w_scale, void* y, int yt, int32_t* acc_out,
                         hipStream_t stream);
+
+// the same for up to kMaxBatch products: those that pick the same large tile
+// (and output type) share one launch
+struct GemmItem {
+    const int8_t* xq;
+    const int8_t* wq;
+    int64_t m, n, k;
+    const float* act_scale;
+    const float* w_scale;
+    void* y;
+    int yt;
+    int32_t* acc_out;
+};
+hipError_t gemm_dequant_batched(const GemmItem* items, int count, hipStream_t stream);
 
 // FP8 (OCP E4M3) variant: act scale over 448, e4m3 weight and activation
 // codes, the e4m3 x e4m3 -> fp32 product with the same dequant epilogue

@@ -19,8 +19,10 @@ supplies the stream; all arithmetic is in libsq.so.
 prepare_block(layers, calib) does calibrate + prepare for the projections of
 one transformer block with the batched entry points: every statistic (the
 calibration inputs' and the weights') in one launch, the smoothing factors in
-two, the weight codes in one per row-length class, with results identical to
-the per-layer calls.
+two, the weight codes in one per row-length class; forward_block(layers, xs)
+quantizes every input in one launch (an input shared by several projections
+is read once) and runs the products in one grouped launch. Results are
+identical to the per-layer calls.
 """
 from __future__ import annotations
 
@@ -116,3 +118,30 @@ def prepare_block(layers, calib=(), stream=None):
                                        stream)
         capi.sq_quant_weight_batched([l.w for l in part], [l.s for l in part], [l.wq for l in part],
                                      [l.w_scale for l in part], stream)
+
+
+def forward_block(layers, xs, stream=None, gemm_stream=None, between=None):
+    """forward for several layers: xs[i] feeds layers[i] (the same tensor for
+    layers that share an input). The activation codes are made on `stream`,
+    the products on `gemm_stream` (default: the same stream; a different one
+    must already be ordered after `stream` by the caller via `between`, a
+    callable run between the two launches). Returns the outputs."""
+    import torch
+    xqs, ys = [], []
+    for l, x in zip(layers, xs):
+        m = x.shape[0]
+        xqs.append(l.xq[:m] if l.xq is not None and l.xq.shape[0] >= m else
+                   torch.empty((m, l.k), dtype=torch.int8, device=x.device))
+        ys.append(l.y[:m] if l.y is not None and l.y.shape[0] >= m else
+                  torch.empty((m, l.n), dtype=l.out_dtype, device=x.device))
+    for part in _chunks(list(range(len(layers)))):
+        capi.sq_smooth_quant_act_batched([xs[i] for i in part], [layers[i].inv_s for i in part],
+                                         [layers[i].act_scale for i in part], [xqs[i] for i in part], stream)
+    if between is not None:
+        between()
+    gs = gemm_stream if gemm_stream is not None else stream
+    for part in _chunks(list(range(len(layers)))):
+        capi.sq_w8a8_gemm_batched([xqs[i] for i in part], [layers[i].wq for i in part],
+                                  [layers[i].act_scale for i in part], [layers[i].w_scale for i in part],
+                                  [ys[i] for i in part], None, gs)
+    return ys

@@ -351,46 +351,63 @@ def workload_copy_probe(device):
 def workload_prefill70b(device):
     """Llama-2-70B prefill, 4096 tokens, int8 weights of all 80 layers
     resident in HBM (68.4 GB): per layer, the runtime path (act quant + int8
-    GEMM) of the 7 projections; weights are random int8 (the values do not
-    change the timing)."""
+    GEMM) of the 7 projections, as one batched activation quantizer (q/k/v read
+    the attention input once, gate/up the MLP input) and one grouped GEMM;
+    the per-projection schedule (14 launches per layer) is timed beside it.
+    Weights are random int8 (the values do not change the timing)."""
     import torch
-    from w8a8_post_quantization_channel_amd import capi, synth
+    from w8a8_post_quantization_channel_amd import capi
     layers, m = 80, 4096
-    projs = [("q", 8192, 8192), ("k", 1024, 8192), ("v", 1024, 8192), ("o", 8192, 8192),
-             ("gate", 28672, 8192), ("up", 28672, 8192), ("down", 8192, 28672)]
+    projs = [("q", 8192, 8192, "attn"), ("k", 1024, 8192, "attn"), ("v", 1024, 8192, "attn"),
+             ("o", 8192, 8192, "attn_out"), ("gate", 28672, 8192, "mlp"), ("up", 28672, 8192, "mlp"),
+             ("down", 8192, 28672, "mlp_mid")]
     g = torch.Generator(device=device)
     g.manual_seed(70)
     weights = []
     for _ in range(layers):
         weights.append([torch.randint(-127, 128, (n, k), dtype=torch.int8, device=device, generator=g)
-                        for _, n, k in projs])
+                        for _, n, k, _ in projs])
     resident = sum(w.numel() for lw in weights for w in lw)
-    xs = {k: torch.randn((m, k), device=device, generator=g).to(torch.bfloat16) for k in (8192, 28672)}
-    inv_s = {k: torch.rand(k, device=device, generator=g) + 0.5 for k in (8192, 28672)}
-    ws = {n: torch.rand(n, device=device, generator=g) * 1e-3 for n in (1024, 8192, 28672)}
-    a = torch.full((4,), 0.05, device=device)
-    xq = {k: torch.empty((m, k), dtype=torch.int8, device=device) for k in (8192, 28672)}
-    y = {n: torch.empty((m, n), dtype=torch.bfloat16, device=device) for n in (1024, 8192, 28672)}
+    ks = {"attn": 8192, "attn_out": 8192, "mlp": 8192, "mlp_mid": 28672}
+    xs = {name: torch.randn((m, k), device=device, generator=g).to(torch.bfloat16) for name, k in ks.items()}
+    inv_s = [torch.rand(k, device=device, generator=g) + 0.5 for _, _, k, _ in projs]
+    ws = [torch.rand(n, device=device, generator=g) * 1e-3 for _, n, _, _ in projs]
+    a = [torch.full((4,), 0.05, device=device) for _ in projs]
+    xq = [torch.empty((m, k), dtype=torch.int8, device=device) for _, _, k, _ in projs]
+    y = [torch.empty((m, n), dtype=torch.bfloat16, device=device) for _, n, _, _ in projs]
+    x_of = [xs[src] for _, _, _, src in projs]
 
-    def layer(i):
-        for j, (_, n, k) in enumerate(projs):
-            capi.sq_smooth_quant_act(xs[k], inv_s[k], a, xq[k])
-            capi.sq_w8a8_gemm(xq[k], weights[i][j], a, ws[n], y[n])
-    for i in range(2):
-        layer(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(layers):
-        layer(i)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ops = layers * sum(2.0 * m * n * k for _, n, k in projs)
+    def layer_batched(i):
+        capi.sq_smooth_quant_act_batched(x_of, inv_s, a, xq)
+        capi.sq_w8a8_gemm_batched(xq, weights[i], a, ws, y)
+
+    def layer_single(i):
+        for j in range(len(projs)):
+            capi.sq_smooth_quant_act(x_of[j], inv_s[j], a[j], xq[j])
+            capi.sq_w8a8_gemm(xq[j], weights[i][j], a[j], ws[j], y[j])
+
+    def run(layer):
+        for i in range(2):
+            layer(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(layers):
+            layer(i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+    run(layer_batched)
+    dt_single = run(layer_single)
+    dt = run(layer_batched)
+    ops = layers * sum(2.0 * m * n * k for _, n, k, _ in projs)
     return {"metric": "W8A8 act quant + int8 GEMM TOPS, Llama-2-70B shapes, 80 layers resident",
             "value": ops / dt / 1e12, "unit": "TOPS", "n_gpus": 1, "higher_is_better": True, "dtype": "int8",
             "data": "synthetic", "config": {"workload": "llama2-70b prefill 4096 tokens x 80 layers",
                                             "resident_int8_weight_GB": resident / 1e9,
-                                            "tiling": {p: list(capi.sq_gemm_tiling(m, n)) for p, n, _ in projs}},
-            "ms_per_layer": dt * 1e3 / layers, "frac_of_int8_peak": ops / dt / 1e12 / PEAK_INT8_TOPS}
+                                            "tiling": {p: list(capi.sq_gemm_tiling(m, n)) for p, n, _, _ in projs},
+                                            "schedule": "per layer: one batched act quant + one grouped GEMM"},
+            "ms_per_layer": dt * 1e3 / layers, "frac_of_int8_peak": ops / dt / 1e12 / PEAK_INT8_TOPS,
+            "per_projection_ms_per_layer": dt_single * 1e3 / layers,
+            "per_projection_tops": ops / dt_single / 1e12}
 
 
 def workload_hbm_passes(device):
@@ -441,6 +458,24 @@ def workload_hbm_passes(device):
         byts = n * k * 3 + k * 4 + n * 4
         out[f"weight_quant_{n}x{k}"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
                                         "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    # the 13B block's seven weights as the step prepares them: statistics and
+    # codes from the batched entry points
+    blk = [(5120, 5120)] * 4 + [(13824, 5120)] * 2 + [(5120, 13824)]
+    W = [(torch.randn(sh, device=device) * 0.02).to(torch.bfloat16) for sh in blk]
+    S = [torch.rand(k, device=device) + 0.5 for _, k in blk]
+    WQ = [torch.empty(sh, dtype=torch.int8, device=device) for sh in blk]
+    WS = [torch.empty(n, dtype=torch.float32, device=device) for n, _ in blk]
+    WM = [torch.empty(k, dtype=torch.float32, device=device) for _, k in blk]
+    ms = timed(lambda: capi.sq_calib_absmax_batched(W, WM, False), 10)
+    byts = sum(n * k * 2 + k * 4 for n, k in blk)
+    out["weight_absmax_13b_block_batched"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
+                                              "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    ms = timed(lambda: capi.sq_quant_weight_batched(W, S, WQ, WS), 10)
+    byts = sum(n * k * 3 + k * 4 + n * 4 for n, k in blk)
+    out["weight_quant_13b_block_batched"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
+                                             "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del W, S, WQ, WS, WM
+    torch.cuda.empty_cache()
     # practical ceilings on the same tensor sizes: a plain copy (read = write)
     # and a plain bf16 -> int8 conversion (2 bytes read per byte written, the
     # traffic mix of the quantization passes), both torch kernels

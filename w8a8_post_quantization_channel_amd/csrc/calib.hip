@@ -140,7 +140,9 @@ __global__ __launch_bounds__(kAbsThreads) void absmax_batched_kernel(const AbsTa
     const int32_t b = blockIdx.x;
     const int i = item_of(tab.first, tab.count, b);
     const int32_t local = b - tab.first[i];
-    const int64_t strip = local % tab.strips[i], chunk = local / tab.strips[i];
+    // integer division has no scalar instruction: bring the block-uniform
+    // quotient back to a scalar register so everything derived from it is too
+    const int32_t chunk = __builtin_amdgcn_readfirstlane(local / tab.strips[i]), strip = local - chunk * tab.strips[i];
     if (tab.eb[i] == 2)
         absmax_block<2, false>(tab.x[i], tab.rows[i], tab.kvec[i], tab.k[i], tab.rpb[i], tab.out[i], strip, chunk,
                                part);

@@ -14,6 +14,7 @@
 // The weight pass works on "groups" of 16 consecutive elements of a row (32
 // bytes of bf16, 64 of fp32), which become 16 int8 codes: one 16-byte store.
 #include <algorithm>
+#include <type_traits>
 
 #include "sq_device.h"
 #include "sq_kernels.h"
@@ -353,48 +354,63 @@ struct ActTable {
 // and keeps the E inv_s values of each consumer in registers; the four waves
 // of a block walk interleaved rows, so each wave instruction moves one
 // contiguous 1 KB run.
-template <int EB, bool FP8>
-__device__ __forceinline__ void quant_act_block(const ActTable& tab, int g, int64_t strip, int64_t chunk) {
+template <int EB, bool FP8, int NC, bool O32 = false>
+__device__ __forceinline__ void quant_act_block(const u32x4* __restrict__ x, int64_t rows, int64_t kvec,
+                                                int64_t rows_per_block, int nc, const float* const (&inv_s)[NC],
+                                                const float* const (&act_scale)[NC], int8_t* const (&xq)[NC],
+                                                int64_t strip, int64_t chunk) {
     constexpr int E = 16 / EB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t kvec = tab.kvec[g];
     const int64_t v = strip * 64 + lane;
     if (v >= kvec) return;  // no block-level synchronisation below
-    const u32x4* x = tab.x[g];
-    const int cf = tab.cfirst[g], nc = tab.cfirst[g + 1] - cf;
-    float is[kActShare][E];
-    float inv_a[kActShare];
+    float is[NC][E];
+    float inv_a[NC];
 #pragma unroll
-    for (int c = 0; c < kActShare; ++c) {
+    for (int c = 0; c < NC; ++c) {
         if (c >= nc) break;
 #pragma unroll
         for (int h = 0; h < E / 4; ++h) {
-            const u32x4 t = ((const u32x4*)(tab.inv_s[cf + c] + v * E))[h];
+            const u32x4 t = ((const u32x4*)(inv_s[c] + v * E))[h];
             is[c][4 * h + 0] = __uint_as_float(t.x);
             is[c][4 * h + 1] = __uint_as_float(t.y);
             is[c][4 * h + 2] = __uint_as_float(t.z);
             is[c][4 * h + 3] = __uint_as_float(t.w);
         }
-        inv_a[c] = __fdiv_rn(1.0f, tab.act_scale[cf + c][0]);
+        inv_a[c] = __fdiv_rn(1.0f, act_scale[c][0]);
     }
-    const int64_t r0 = chunk * tab.rpb[g];
-    const int64_t r1 = min(tab.rows[g], r0 + tab.rpb[g]);
+    const int64_t r0 = chunk * rows_per_block;
+    const int64_t r1 = min(rows, r0 + rows_per_block);
+    // global address space: pointers taken from a table are generic, and
+    // generic (flat) accesses wait on both counters and cannot take a scalar base
+    typedef __attribute__((address_space(1))) const u32x4 gvec;
+    typedef __attribute__((address_space(1))) const char gcbyte;
+    typedef __attribute__((address_space(1))) int8_t gbyte;
+    gvec* gx = (gvec*)x;
+    // O32: every tensor of the launch is below 4 GiB, so byte offsets fit 32
+    // bits and an access is a scalar base plus one 32-bit offset, shared by
+    // the consumers of a row
+    using Off = typename std::conditional<O32, uint32_t, int64_t>::type;
+    auto load = [&](int64_t r) -> u32x4 {
+        const Off vec = (Off)r * (Off)kvec + (Off)v;
+        return __builtin_nontemporal_load((gvec*)((gcbyte*)gx + vec * (Off)16));
+    };
     auto quantize = [&](const u32x4& raw, int64_t r) {
         float e[E];
         sqd::unpack16<E>(raw, e);
+        const Off off = ((Off)r * (Off)kvec + (Off)v) * (Off)E;
 #pragma unroll
-        for (int c = 0; c < kActShare; ++c) {
+        for (int c = 0; c < NC; ++c) {
             if (c >= nc) break;
-            int8_t* dst = tab.xq[cf + c] + (r * kvec + v) * E;
+            gbyte* dst = (gbyte*)xq[c] + off;
             if constexpr (FP8) {
                 float t[E];
 #pragma unroll
                 for (int u = 0; u < E; ++u) t[u] = __fmul_rn(__fmul_rn(e[u], is[c][u]), inv_a[c]);
                 if constexpr (E == 8)
-                    *(sqd::u32x2*)dst = sqd::u32x2{sqd::pack4_e4m3(t[0], t[1], t[2], t[3]),
-                                                   sqd::pack4_e4m3(t[4], t[5], t[6], t[7])};
+                    *(__attribute__((address_space(1))) sqd::u32x2*)dst =
+                        sqd::u32x2{sqd::pack4_e4m3(t[0], t[1], t[2], t[3]), sqd::pack4_e4m3(t[4], t[5], t[6], t[7])};
                 else
-                    *(uint32_t*)dst = sqd::pack4_e4m3(t[0], t[1], t[2], t[3]);
+                    *(__attribute__((address_space(1))) uint32_t*)dst = sqd::pack4_e4m3(t[0], t[1], t[2], t[3]);
             } else {
                 // clamp to [-127, 127], then round half to even with the fp32
                 // adder (fl(v + 1.5 * 2^23) keeps rint(v) in its low byte for
@@ -415,9 +431,9 @@ __device__ __forceinline__ void quant_act_block(const ActTable& tab, int g, int6
                     w[d] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
                 }
                 if constexpr (E == 8)
-                    *(sqd::u32x2*)dst = sqd::u32x2{w[0], w[1]};
+                    *(__attribute__((address_space(1))) sqd::u32x2*)dst = sqd::u32x2{w[0], w[1]};
                 else
-                    *(uint32_t*)dst = w[0];
+                    *(__attribute__((address_space(1))) uint32_t*)dst = w[0];
             }
         }
     };
@@ -425,22 +441,63 @@ __device__ __forceinline__ void quant_act_block(const ActTable& tab, int g, int6
     for (; r + 4 * (kActUnroll - 1) < r1; r += 4 * kActUnroll) {
         u32x4 t[kActUnroll];
 #pragma unroll
-        for (int u = 0; u < kActUnroll; ++u) t[u] = __builtin_nontemporal_load(x + (r + 4 * u) * kvec + v);
+        for (int u = 0; u < kActUnroll; ++u) t[u] = load(r + 4 * u);
 #pragma unroll
         for (int u = 0; u < kActUnroll; ++u) quantize(t[u], r + 4 * u);
     }
-    for (; r < r1; r += 4) quantize(__builtin_nontemporal_load(x + r * kvec + v), r);
+    for (; r < r1; r += 4) quantize(load(r), r);
 }
 
-template <bool FP8>
+// one input, one consumer, arguments in kernel parameters: the single-call form
+template <int EB, bool FP8>
+__global__ __launch_bounds__(kActThreads) void quant_act_kernel(const u32x4* __restrict__ x, int64_t rows,
+                                                                int64_t kvec, int64_t rows_per_block,
+                                                                const float* __restrict__ inv_s,
+                                                                const float* __restrict__ act_scale,
+                                                                int8_t* __restrict__ xq) {
+    const float* is[1] = {inv_s};
+    const float* as[1] = {act_scale};
+    int8_t* q[1] = {xq};
+    quant_act_block<EB, FP8, 1>(x, rows, kvec, rows_per_block, 1, is, as, q, blockIdx.x, blockIdx.y);
+}
+
+// a block-uniform 64-bit value kept in scalar registers (the compiler does not
+// see through the table lookup that the group's fields are uniform)
+template <class T>
+__device__ __forceinline__ T uniform(T v) {
+    static_assert(sizeof(T) == 8, "64-bit values");
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+}
+
+// NC: the most consumers any group of the launch has (1, 2 or 4): a group's
+// inv_s registers scale with it, and a single consumer keeps the occupancy of
+// a plain quantizer
+template <int EB, bool FP8, int NC, bool O32>
 __global__ __launch_bounds__(kActThreads) void quant_act_batched_kernel(const ActTable tab) {
+    // the group's fields as plain scalars: the block then addresses its
+    // input and outputs exactly as a kernel taking them as arguments would
     const int g = sqd::item_of(tab.first, tab.count, blockIdx.x);
-    const int32_t local = blockIdx.x - tab.first[g];
-    const int64_t strip = local % tab.strips[g], chunk = local / tab.strips[g];
-    if (tab.eb[g] == 2)
-        quant_act_block<2, FP8>(tab, g, strip, chunk);
-    else
-        quant_act_block<4, FP8>(tab, g, strip, chunk);
+    const int32_t local = blockIdx.x - tab.first[g], strips = tab.strips[g];
+    const int cf = tab.cfirst[g], nc = tab.cfirst[g + 1] - cf;
+    const float* inv_s[NC];
+    const float* act_scale[NC];
+    int8_t* xq[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int ci = c < nc ? cf + c : cf;
+        inv_s[c] = uniform(tab.inv_s[ci]);
+        act_scale[c] = uniform(tab.act_scale[ci]);
+        xq[c] = uniform(tab.xq[ci]);
+    }
+    const u32x4* x = uniform(tab.x[g]);
+    const int64_t rows = uniform(tab.rows[g]), kvec = uniform(tab.kvec[g]), rpb = uniform(tab.rpb[g]);
+    // integer division has no scalar instruction: bring the block-uniform
+    // quotient back to a scalar register so everything derived from it is too
+    const int32_t chunk = __builtin_amdgcn_readfirstlane(local / strips), strip = local - chunk * strips;
+    quant_act_block<EB, FP8, NC, O32>(x, rows, kvec, rpb, nc, inv_s, act_scale, xq, strip, chunk);
 }
 
 int device_cus() {
@@ -570,60 +627,109 @@ hipError_t quant_weight_fp8(const void* w, int wt, int64_t n, int64_t k, const f
     return quant_weight_items<true>(&item, 1, stream);
 }
 
+template <int EB, bool FP8, int NC>
+void launch_act(const ActTable& tab, int64_t blocks, bool o32, hipStream_t stream) {
+    if (o32)
+        quant_act_batched_kernel<EB, FP8, NC, true><<<dim3((unsigned)blocks), dim3(kActThreads), 0, stream>>>(tab);
+    else
+        quant_act_batched_kernel<EB, FP8, NC, false><<<dim3((unsigned)blocks), dim3(kActThreads), 0, stream>>>(tab);
+}
+
 // Items with the same input (pointer, type and shape) form one group, up to
-// kActShare consumers each, in first-appearance order.
+// kActShare consumers each, in first-appearance order; one launch per element
+// type among the inputs.
 template <bool FP8>
 hipError_t quant_act_items(const ActItem* items, int count, hipStream_t stream) {
-    ActTable tab{};
     bool done[kMaxBatch] = {};
-    int ng = 0, nc = 0;
-    int64_t blocks = 0;
-    for (int i = 0; i < count; ++i) {
-        if (done[i] || items[i].m == 0) continue;
-        const int eb = elem_bytes(items[i].xt);
-        const int64_t kvec = items[i].k * eb / 16;
-        const int64_t strips = (kvec + 63) / 64;
-        const int64_t granule = 4 * kActUnroll;
-        const int64_t target_chunks = std::max<int64_t>(1, 8192 / strips);
-        int64_t rpb = (items[i].m + target_chunks - 1) / target_chunks;
-        rpb = std::max<int64_t>(granule, (rpb + granule - 1) / granule * granule);
-        const int64_t chunks = (items[i].m + rpb - 1) / rpb;
+    for (int eb : {2, 4}) {
+        ActTable tab{};
+        int ng = 0, nc = 0, widest = 1;
+        int64_t blocks = 0;
+        bool o32 = true;  // every input (and so every code tensor) below 4 GiB
+        for (int i = 0; i < count; ++i) {
+            if (done[i] || items[i].m == 0 || elem_bytes(items[i].xt) != eb) continue;
+            const int64_t kvec = items[i].k * eb / 16;
+            const int64_t strips = (kvec + 63) / 64;
+            const int64_t granule = 4 * kActUnroll;
+            const int64_t target_chunks = std::max<int64_t>(1, 8192 / strips);
+            int64_t rpb = (items[i].m + target_chunks - 1) / target_chunks;
+            rpb = std::max<int64_t>(granule, (rpb + granule - 1) / granule * granule);
+            const int64_t chunks = (items[i].m + rpb - 1) / rpb;
+            tab.first[ng] = (int32_t)blocks;
+            tab.cfirst[ng] = nc;
+            tab.x[ng] = (const u32x4*)items[i].x;
+            tab.rows[ng] = items[i].m;
+            tab.kvec[ng] = kvec;
+            tab.rpb[ng] = rpb;
+            tab.strips[ng] = (int32_t)strips;
+            tab.eb[ng] = eb;
+            o32 = o32 && items[i].m * kvec * 16 < ((int64_t)1 << 32);
+            int shared = 0;
+            for (int j = i; j < count && shared < kActShare; ++j) {
+                if (done[j] || items[j].x != items[i].x || items[j].xt != items[i].xt || items[j].m != items[i].m ||
+                    items[j].k != items[i].k)
+                    continue;
+                done[j] = true;
+                tab.inv_s[nc] = items[j].inv_s;
+                tab.act_scale[nc] = items[j].act_scale;
+                tab.xq[nc] = items[j].xq;
+                ++nc;
+                ++shared;
+            }
+            blocks += strips * chunks;
+            widest = std::max(widest, shared);
+            ++ng;  // consumers of this input beyond kActShare start a group of their own further on
+        }
+        if (ng == 0) continue;
+        if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+        tab.count = ng;
         tab.first[ng] = (int32_t)blocks;
         tab.cfirst[ng] = nc;
-        tab.x[ng] = (const u32x4*)items[i].x;
-        tab.rows[ng] = items[i].m;
-        tab.kvec[ng] = kvec;
-        tab.rpb[ng] = rpb;
-        tab.strips[ng] = (int32_t)strips;
-        tab.eb[ng] = eb;
-        int shared = 0;
-        for (int j = i; j < count && shared < kActShare; ++j) {
-            if (done[j] || items[j].x != items[i].x || items[j].xt != items[i].xt || items[j].m != items[i].m ||
-                items[j].k != items[i].k)
-                continue;
-            done[j] = true;
-            tab.inv_s[nc] = items[j].inv_s;
-            tab.act_scale[nc] = items[j].act_scale;
-            tab.xq[nc] = items[j].xq;
-            ++nc;
-            ++shared;
+        if (eb == 2) {
+            if (widest == 1) launch_act<2, FP8, 1>(tab, blocks, o32, stream);
+            else if (widest == 2) launch_act<2, FP8, 2>(tab, blocks, o32, stream);
+            else launch_act<2, FP8, kActShare>(tab, blocks, o32, stream);
+        } else {
+            if (widest == 1) launch_act<4, FP8, 1>(tab, blocks, o32, stream);
+            else if (widest == 2) launch_act<4, FP8, 2>(tab, blocks, o32, stream);
+            else launch_act<4, FP8, kActShare>(tab, blocks, o32, stream);
         }
-        blocks += strips * chunks;
-        ++ng;  // consumers of this input beyond kActShare start a group of their own further on
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    if (ng == 0) return hipSuccess;
-    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    tab.count = ng;
-    tab.first[ng] = (int32_t)blocks;
-    tab.cfirst[ng] = nc;
-    quant_act_batched_kernel<FP8><<<dim3((unsigned)blocks), dim3(kActThreads), 0, stream>>>(tab);
+    return hipSuccess;
+}
+
+// one input and one consumer: the kernel with plain arguments (no table to
+// look the group up in), about 8192 blocks of 4 waves
+template <bool FP8>
+hipError_t quant_act_single(const void* x, int xt, int64_t m, int64_t k, const float* inv_s,
+                            const float* act_scale, int8_t* xq, hipStream_t stream) {
+    if (m == 0) return hipSuccess;
+    const int eb = elem_bytes(xt);
+    const int64_t kvec = k * eb / 16;
+    const int64_t strips = (kvec + 63) / 64;
+    const int64_t granule = 4 * kActUnroll;
+    int64_t target_chunks = std::max<int64_t>(1, 8192 / strips);
+    int64_t rpb = (m + target_chunks - 1) / target_chunks;
+    rpb = std::max<int64_t>(granule, (rpb + granule - 1) / granule * granule);
+    int64_t chunks = (m + rpb - 1) / rpb;
+    if (chunks > 65535) {
+        rpb = (m + 65534) / 65535;
+        rpb = (rpb + granule - 1) / granule * granule;
+        chunks = (m + rpb - 1) / rpb;
+    }
+    const dim3 grid((unsigned)strips, (unsigned)chunks), block(kActThreads);
+    if (eb == 2)
+        quant_act_kernel<2, FP8><<<grid, block, 0, stream>>>((const u32x4*)x, m, kvec, rpb, inv_s, act_scale, xq);
+    else
+        quant_act_kernel<4, FP8><<<grid, block, 0, stream>>>((const u32x4*)x, m, kvec, rpb, inv_s, act_scale, xq);
     return hipGetLastError();
 }
 
 hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const float* inv_s, const float* act_scale,
                      int8_t* xq, hipStream_t stream) {
-    const ActItem item{x, xt, m, k, inv_s, act_scale, xq};
-    return quant_act_items<false>(&item, 1, stream);
+    return quant_act_single<false>(x, xt, m, k, inv_s, act_scale, xq, stream);
 }
 
 hipError_t quant_act_batched(const ActItem* items, int count, hipStream_t stream) {
@@ -632,8 +738,7 @@ hipError_t quant_act_batched(const ActItem* items, int count, hipStream_t stream
 
 hipError_t quant_act_fp8(const void* x, int xt, int64_t m, int64_t k, const float* inv_s, const float* act_scale,
                          uint8_t* xq, hipStream_t stream) {
-    const ActItem item{x, xt, m, k, inv_s, act_scale, (int8_t*)xq};
-    return quant_act_items<true>(&item, 1, stream);
+    return quant_act_single<true>(x, xt, m, k, inv_s, act_scale, (int8_t*)xq, stream);
 }
 
 }  // namespace sqk

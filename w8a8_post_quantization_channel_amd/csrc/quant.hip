@@ -461,17 +461,6 @@ __global__ __launch_bounds__(kActThreads) void quant_act_kernel(const u32x4* __r
     quant_act_block<EB, FP8, 1>(x, rows, kvec, rows_per_block, 1, is, as, q, blockIdx.x, blockIdx.y);
 }
 
-// a block-uniform 64-bit value kept in scalar registers (the compiler does not
-// see through the table lookup that the group's fields are uniform)
-template <class T>
-__device__ __forceinline__ T uniform(T v) {
-    static_assert(sizeof(T) == 8, "64-bit values");
-    const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
-}
-
 // NC: the most consumers any group of the launch has (1, 2 or 4): a group's
 // inv_s registers scale with it, and a single consumer keeps the occupancy of
 // a plain quantizer
@@ -488,12 +477,12 @@ __global__ __launch_bounds__(kActThreads) void quant_act_batched_kernel(const Ac
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int ci = c < nc ? cf + c : cf;
-        inv_s[c] = uniform(tab.inv_s[ci]);
-        act_scale[c] = uniform(tab.act_scale[ci]);
-        xq[c] = uniform(tab.xq[ci]);
+        inv_s[c] = tab.inv_s[ci];
+        act_scale[c] = tab.act_scale[ci];
+        xq[c] = tab.xq[ci];
     }
-    const u32x4* x = uniform(tab.x[g]);
-    const int64_t rows = uniform(tab.rows[g]), kvec = uniform(tab.kvec[g]), rpb = uniform(tab.rpb[g]);
+    const u32x4* x = tab.x[g];
+    const int64_t rows = tab.rows[g], kvec = tab.kvec[g], rpb = tab.rpb[g];
     // integer division has no scalar instruction: bring the block-uniform
     // quotient back to a scalar register so everything derived from it is too
     const int32_t chunk = __builtin_amdgcn_readfirstlane(local / strips), strip = local - chunk * strips;

@@ -430,7 +430,7 @@ namespace {
 constexpr int kPctThreads = 1024;  // 16 waves over interleaved rows
 constexpr int kPctChannels = 64;   // one channel per lane
 constexpr int kPctBins = 256;
-constexpr int kPctStride = kPctBins + 1;  // LDS row stride: lane l's bin d sits in bank (l + d) % 64
+constexpr int kPctRows = kPctBins;        // LDS histogram rows, one per bin
 constexpr int kPctUnroll = 16;
 
 template <int EB>
@@ -458,21 +458,25 @@ __global__ __launch_bounds__(kPctThreads) void pct_hist_kernel(const void* __res
     using K = PctKey<EB>;
     constexpr int LO = K::lo(PASS), HI = LO + K::width(PASS);
     constexpr uint32_t DMASK = (1u << K::width(PASS)) - 1u;
-    __shared__ uint32_t h[kPctChannels * kPctStride];
+    // bin-major: lane l's bin d is word d * 64 + l, in bank l whatever the
+    // digits, so the 64 lanes of an atomic never share a bank (a lane-major
+    // row per channel puts bin d in bank (l + d) % 64, and digits that differ
+    // across lanes, like the low digit of the later passes, then collide)
+    __shared__ uint32_t h[kPctRows * kPctChannels];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int i = tid; i < kPctChannels * kPctStride; i += kPctThreads) h[i] = 0u;
+    for (int i = tid; i < kPctRows * kPctChannels; i += kPctThreads) h[i] = 0u;
     __syncthreads();
     const int64_t c = (int64_t)blockIdx.x * kPctChannels + lane;  // k is a multiple of 64
     const uint32_t pre = PASS > 0 ? prefix[c] : 0u;
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
     const int64_t r1 = min(rows, r0 + rows_per_block);
     constexpr int W = kPctThreads / 64;
-    // branch-free: keys outside the selected prefix are counted in the row's
-    // pad word (index 256, never read), one bank per lane, so the many
-    // non-matching keys of the later passes cause no bank conflicts
+    // keys outside the selected prefix are skipped (their lanes sit the
+    // atomic out): at a high percentile almost every key of the later passes
+    // is outside, and counting them all in one pad word chained 16
+    // read-modify-writes per lane on one address
     auto count = [&](uint32_t key) {
-        const uint32_t bin = (PASS == 0 || (key >> HI) == pre) ? ((key >> LO) & DMASK) : (uint32_t)kPctBins;
-        atomicAdd(&h[lane * kPctStride + bin], 1u);
+        if (PASS == 0 || (key >> HI) == pre) atomicAdd(&h[((key >> LO) & DMASK) * kPctChannels + lane], 1u);
     };
     int64_t r = r0 + wave;
     for (; r + W * (kPctUnroll - 1) < r1; r += W * kPctUnroll) {
@@ -484,12 +488,13 @@ __global__ __launch_bounds__(kPctThreads) void pct_hist_kernel(const void* __res
     }
     for (; r < r1; r += W) count(mag_key<EB>(x, r * k + c));
     __syncthreads();
-    // merge: thread t takes 16 consecutive bins of channel t / 16
-    const int ch = tid >> 4, b0 = (tid & 15) * 16;
+    // merge: lane l takes channel l (bank l again) and each wave 16
+    // consecutive bins
+    const int ch = lane, b0 = wave * 16;
     uint32_t* g = hist + ((int64_t)blockIdx.x * kPctChannels + ch) * kPctBins;
 #pragma unroll
     for (int b = b0; b < b0 + 16; ++b) {
-        const uint32_t v = h[ch * kPctStride + b];
+        const uint32_t v = h[b * kPctChannels + ch];
         if (v) atomicAdd(g + b, v);
     }
 }

@@ -66,7 +66,7 @@ def parse():
                          "profiles/gemm_traffic__llama13b_prefill2048.md, used only if it matches gemm.hip)")
     ap.add_argument("--workload", default="layer13b",
                     choices=["layer13b", "decode7b", "alpha_search", "prefill70b", "hbm_passes", "copy_probe",
-                             "variants", "fp8"],
+                             "variants", "fp8", "ceilings"],
                     help="layer13b (default, the headline line); the others measure the remaining "
                          "workloads, one JSON line each")
     return ap.parse_args()
@@ -505,6 +505,97 @@ def workload_hbm_passes(device):
             "per_pass": out}
 
 
+def ceiling_operand_sets(device):
+    """Register operands for the MFMA-only loop (16 operands x 64 lanes x 16
+    bytes): all-ones bytes; uniform random bytes (seeded); and 32x32 fragments
+    of the 13B step's own codes, chain c's A operand from the weight codes of
+    q_proj (rows 1024 + 32c .., the first operand of the GEMM's MFMAs) and its
+    B operand from the activation codes of the same projection, 32 K bytes at
+    K = 2048 as the GEMM's fragments hold them."""
+    import numpy as np
+    import torch
+    sets = {"ones": np.ones((16, 64, 16), np.int8),
+            "random": np.random.default_rng(20240531).integers(-128, 128, (16, 64, 16)).astype(np.int8)}
+    groups, projs = setup(device)
+    _, g, layer, _ = projs[0]
+    layer.calibrate(g.x)
+    layer.prepare()
+    xq = layer.quantize_input(g.x).cpu().numpy()
+    wq = layer.wq.cpu().numpy()
+    codes = np.empty((16, 64, 16), np.int8)
+    k0 = 2048
+    for c in range(8):
+        for lane in range(64):
+            r, kk = lane % 32, k0 + (lane // 32) * 16
+            codes[2 * c, lane] = wq[1024 + 32 * c + r, kk:kk + 16]
+            codes[2 * c + 1, lane] = xq[1024 + 32 * c + r, kk:kk + 16]
+    sets["codes"] = codes
+    del groups, projs, layer, xq, wq
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return sets
+
+
+def workload_ceilings(device):
+    """Measured ceilings written for this path: an MFMA-only loop (int8
+    v_mfma_i32_32x32x32_i8 on register operands: all-ones bytes, random bytes,
+    or fragments of the step's own codes; 8 independent chains per wave, 1 and
+    2 blocks of 4 waves per compute unit), a 16-byte-vector copy and a
+    16-byte-vector read of 1 GiB each (well past the 256 MB Infinity Cache).
+    Each MFMA run is checked against its closed-form sum, the copy byte for
+    byte, the read against the XOR of its words."""
+    import numpy as np
+    import torch
+    from w8a8_post_quantization_channel_amd import capi
+    out = {}
+    sink = torch.zeros(4, dtype=torch.int32, device=device)
+    iters = 20000
+    for name, ops_host in ceiling_operand_sets(device).items():
+        dots = capi.ceiling_chain_dots(ops_host)
+        if max(abs(d) for d in dots) * iters >= 1 << 31:
+            raise RuntimeError(f"{name}: accumulators would leave int32 ({dots})")
+        operands = torch.from_numpy(ops_host.reshape(-1).copy()).to(device)
+        for per_cu in (1, 2):
+            sink.zero_()
+            ops = capi.sq_ceiling_mfma(iters, per_cu, operands, sink)
+            torch.cuda.synchronize()
+            waves = ops // (8 * iters * 2 * 32 * 32 * 32)
+            expect = capi.ceiling_expected_sink(ops_host, iters, waves)
+            got = int(sink[0].item()) % (1 << 32)
+            if got != expect:
+                raise RuntimeError(f"MFMA loop check failed ({name}): {got} != {expect}")
+            # steady state: half a second of untimed calls, then ~0.2-0.5 s timed (a few
+            # ms of MFMA load is too short for the power manager to settle)
+            ms = timed(lambda: capi.sq_ceiling_mfma(iters, per_cu, operands, sink), 100, warmup=2, warm_ms=500)
+            tops = ops / (ms * 1e-3) / 1e12
+            out[f"mfma_loop_{name}_{per_cu}_blocks_per_cu"] = {
+                "TOPS": tops, "frac_of_int8_peak": tops / PEAK_INT8_TOPS,
+                # the clock at which a matrix pipe issuing every cycle gives this rate
+                "issue_clock_GHz": 2.4 * tops / PEAK_INT8_TOPS}
+    n = 1 << 30
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    capi.sq_ceiling_copy(src, dst)
+    torch.cuda.synchronize()
+    if not torch.equal(src, dst):
+        raise RuntimeError("copy check failed")
+    ms = timed(lambda: capi.sq_ceiling_copy(src, dst), 10)
+    out["copy_1GiB"] = {"GB/s": 2 * n / (ms * 1e-3) / 1e9, "hbm_frac": 2 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del dst
+    xor = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
+    sink.zero_()
+    capi.sq_ceiling_read(src, sink)
+    torch.cuda.synchronize()
+    if int(sink[0].item()) % (1 << 32) != int(xor):
+        raise RuntimeError("read check failed")
+    ms = timed(lambda: capi.sq_ceiling_read(src, sink), 10)
+    out["read_1GiB"] = {"GB/s": n / (ms * 1e-3) / 1e9, "hbm_frac": n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    return {"metric": "measured ceilings: int8 MFMA-only loop TOPS (step's own codes), 16-byte copy and read GB/s",
+            "value": out["mfma_loop_codes_1_blocks_per_cu"]["TOPS"], "unit": "TOPS",
+            "n_gpus": 1, "higher_is_better": True, "dtype": "int8 / bytes", "data": "synthetic",
+            "config": {"workload": "MFMA-only loop on every compute unit; 1 GiB copy and read"}, "per_case": out}
+
+
 def workload_variants(device):
     """The widened rows, each beside the form it replaces:
     - dynamic vs static activation scale: the runtime forward (activation
@@ -652,6 +743,7 @@ def main():
     device = torch.device("cuda", 0)
     other = {"decode7b": workload_decode7b, "alpha_search": workload_alpha_search, "copy_probe": workload_copy_probe,
              "prefill70b": workload_prefill70b, "hbm_passes": workload_hbm_passes, "variants": workload_variants,
+             "ceilings": workload_ceilings,
              "fp8": workload_fp8}
     if args.workload in other:
         out = other[args.workload](device)

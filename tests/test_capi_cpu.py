@@ -437,3 +437,42 @@ def test_batched_act_and_gemm_validation(lib):
     bad = [list(v) if isinstance(v, list) else v for v in gg]
     bad[9] = [bad[7][1], None]  # item 0's acc_out over item 1's y
     assert gemm(2, *bad) == SHAPE
+
+
+def test_ceiling_validation(lib):
+    for name in ("sq_ceiling_mfma", "sq_ceiling_copy", "sq_ceiling_read"):
+        assert name in capi.declared_functions() and hasattr(lib, name)
+    ops = ctypes.c_int64(0)
+    assert lib.sq_ceiling_mfma(100, 1, P(A), None, ctypes.byref(ops), None) == NULL
+    assert lib.sq_ceiling_mfma(100, 1, None, P(A), ctypes.byref(ops), None) == NULL
+    assert lib.sq_ceiling_mfma(100, 1, P(A), P(A), None, None) == NULL
+    assert lib.sq_ceiling_mfma(0, 1, P(A), P(A), ctypes.byref(ops), None) == SHAPE
+    assert lib.sq_ceiling_mfma((1 << 24) + 1, 1, P(A), P(A), ctypes.byref(ops), None) == SHAPE
+    assert lib.sq_ceiling_mfma(100, 9, P(A), P(A), ctypes.byref(ops), None) == SHAPE
+    assert lib.sq_ceiling_mfma(100, 1, P(A), P(A + 2), ctypes.byref(ops), None) == ALIGN
+    assert lib.sq_ceiling_mfma(100, 1, P(MIS), P(A), ctypes.byref(ops), None) == ALIGN
+    assert lib.sq_ceiling_copy(None, P(A), 1024, None) == NULL
+    assert lib.sq_ceiling_copy(P(A), P(A + 0x1000), 1000, None) == SHAPE
+    assert lib.sq_ceiling_copy(P(A), P(A + 512), 1024, None) == SHAPE  # overlapping
+    assert lib.sq_ceiling_copy(P(MIS), P(A + 0x1000), 1024, None) == ALIGN
+    assert lib.sq_ceiling_copy(None, None, 0, None) == OK
+    assert lib.sq_ceiling_read(P(A), 1024, None, None) == NULL
+    assert lib.sq_ceiling_read(None, 1024, P(A), None) == NULL
+    assert lib.sq_ceiling_read(P(A), 1000, P(A), None) == SHAPE
+    assert lib.sq_ceiling_read(P(MIS), 1024, P(A), None) == ALIGN
+    assert lib.sq_ceiling_read(P(A), 1024, P(A + 2), None) == ALIGN
+    assert lib.sq_ceiling_read(None, 0, P(A), None) == OK
+
+
+def test_ceiling_chain_dots():
+    """The host side of the MFMA loop's check: all-ones operands give 32 per
+    chain; one nonzero byte pair at lane 32 lands in its own chain only; bytes
+    of lanes other than 0 and 32 do not enter element 0."""
+    import numpy as np
+    assert capi.ceiling_chain_dots(np.ones(16384, np.int8)) == [32] * 8
+    o = np.zeros((16, 64, 16), np.int8)
+    o[2 * 3, 32, 5], o[2 * 3 + 1, 32, 5] = -7, 9
+    o[2 * 5, 1, 0], o[2 * 5 + 1, 1, 0] = 100, 100  # lane 1: row 1 of A, column 1 of B
+    o[2 * 6, 0, 2], o[2 * 6 + 1, 0, 3] = 50, 50  # different K positions
+    assert capi.ceiling_chain_dots(o.reshape(-1)) == [0, 0, 0, -63, 0, 0, 0, 0]
+    assert capi.ceiling_expected_sink(o.reshape(-1), 3, 10) == (-63 * 30) % (1 << 32)

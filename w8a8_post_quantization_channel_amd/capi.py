@@ -68,6 +68,9 @@ def _declare(lib):
         "sq_quant_weight_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_smooth_quant_act_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_w8a8_gemm_batched": [c.c_int, P, P, P, P, P, P, P, P, P, P, P],
+        "sq_ceiling_mfma": [i64, c.c_int, P, P, P, P],
+        "sq_ceiling_copy": [P, P, i64, P],
+        "sq_ceiling_read": [P, i64, P, P],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -264,6 +267,51 @@ def sq_w8a8_gemm_batched(xqs, wqs, act_scales, w_scales, ys, acc_outs=None, stre
         acc = _host_array(ctypes.c_void_p, [_opt(a, f"acc_outs[{i}]").value for i, a in enumerate(acc_outs)])
     _check("sq_w8a8_gemm_batched", load().sq_w8a8_gemm_batched(count, *[a for _, a in keep],
                                                                acc[1] if acc else ctypes.c_void_p(0), _stream(stream)))
+
+
+CEILING_OPERAND_BYTES = 16384
+
+
+def sq_ceiling_mfma(iters: int, blocks_per_cu: int, operands, sink, stream=None) -> int:
+    """MFMA-only loop on every compute unit over the 16 KiB of register
+    operands in `operands`; returns the int8 ops it issues."""
+    if operands.numel() * operands.element_size() != CEILING_OPERAND_BYTES:
+        raise ValueError(f"operands must hold {CEILING_OPERAND_BYTES} bytes")
+    ops = ctypes.c_int64(0)
+    _check("sq_ceiling_mfma", load().sq_ceiling_mfma(iters, blocks_per_cu, _dev(operands, "operands"),
+                                                     _dev(sink, "sink"), ctypes.byref(ops), _stream(stream)))
+    return ops.value
+
+
+def ceiling_chain_dots(operands) -> list:
+    """Per chain, the dot product sq_ceiling_mfma adds to its sink per
+    iteration: element 0 of a v_mfma_i32_32x32x32_i8 accumulator is row 0 of A
+    times column 0 of B, whose 32 bytes are lanes 0 and 32 of each operand
+    (the same byte order on both sides, so the pairing does not depend on how
+    the instruction numbers K). `operands` is the host copy (16384 int8)."""
+    import numpy as np
+    o = np.asarray(operands, dtype=np.int8).reshape(16, 64, 16).astype(np.int64)
+    return [int((np.concatenate([o[2 * c, 0], o[2 * c, 32]]) *
+                 np.concatenate([o[2 * c + 1, 0], o[2 * c + 1, 32]])).sum()) for c in range(8)]
+
+
+def ceiling_expected_sink(operands, iters: int, waves: int) -> int:
+    """sink[0] after one sq_ceiling_mfma call from zero (mod 2^32)."""
+    return (waves * iters * sum(ceiling_chain_dots(operands))) % (1 << 32)
+
+
+def sq_ceiling_copy(src, dst, stream=None):
+    """16-byte vector copy of src into dst (same number of bytes)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    _check("sq_ceiling_copy", load().sq_ceiling_copy(_dev(src, "src"), _dev(dst, "dst"), nbytes, _stream(stream)))
+
+
+def sq_ceiling_read(src, sink, stream=None):
+    """16-byte vector read of src, every 32-bit word XORed into sink[0]."""
+    _check("sq_ceiling_read", load().sq_ceiling_read(_dev(src, "src"), src.numel() * src.element_size(),
+                                                     _dev(sink, "sink"), _stream(stream)))
 
 
 def _opt(t, what: str):

@@ -502,4 +502,29 @@ sq_status sq_alpha_search(const void* const* x_batches, sq_dtype xt, int n_batch
     return SQ_OK;
 }
 
+sq_status sq_ceiling_mfma(int64_t iters, int blocks_per_cu, const void* operands, uint32_t* sink, int64_t* ops,
+                          hipStream_t stream) {
+    if (!operands || !sink || !ops) return SQ_ERR_NULL;
+    if (iters < 1 || iters > ((int64_t)1 << 24) || blocks_per_cu < 1 || blocks_per_cu > 8) return SQ_ERR_SHAPE;
+    if (!aligned16(operands) || ((uintptr_t)sink & 3u) != 0) return SQ_ERR_ALIGN;
+    *ops = sqk::ceiling_mfma_ops(iters, blocks_per_cu);
+    return hip_status(sqk::ceiling_mfma(iters, blocks_per_cu, operands, sink, stream));
+}
+
+sq_status sq_ceiling_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+    if (bytes > 0 && (!src || !dst)) return SQ_ERR_NULL;
+    if (bytes < 0 || bytes % 16 != 0) return SQ_ERR_SHAPE;
+    if (bytes > 0 && (!aligned16(src) || !aligned16(dst))) return SQ_ERR_ALIGN;
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+    if (bytes > 0 && s0 < d0 + (uintptr_t)bytes && d0 < s0 + (uintptr_t)bytes) return SQ_ERR_SHAPE;
+    return hip_status(sqk::ceiling_copy(src, dst, bytes, stream));
+}
+
+sq_status sq_ceiling_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+    if (!sink || (bytes > 0 && !src)) return SQ_ERR_NULL;
+    if (bytes < 0 || bytes % 16 != 0) return SQ_ERR_SHAPE;
+    if ((bytes > 0 && !aligned16(src)) || ((uintptr_t)sink & 3u) != 0) return SQ_ERR_ALIGN;
+    return hip_status(sqk::ceiling_read(src, bytes, sink, stream));
+}
+
 }  // extern "C"

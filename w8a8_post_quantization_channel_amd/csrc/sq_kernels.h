@@ -159,4 +159,11 @@ hipError_t ref_gemm(const void* x, int xt, const void* w, int wt, int64_t m, int
 hipError_t reduce_slots(const double* slots, int64_t per_group, int groups, double count, double* out,
                         hipStream_t stream);
 
+// measured ceilings: an MFMA-only loop (int8 ops issued), a 16-byte copy and a
+// 16-byte read-only stream
+hipError_t ceiling_mfma(int64_t iters, int blocks_per_cu, const void* operands, unsigned* sink, hipStream_t stream);
+int64_t ceiling_mfma_ops(int64_t iters, int blocks_per_cu);
+hipError_t ceiling_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+hipError_t ceiling_read(const void* src, int64_t bytes, unsigned* sink, hipStream_t stream);
+
 }  // namespace sqk

@@ -145,7 +145,10 @@ def test_quant_weight_paths(k, bf16):
     assert_bitexact("w_scale", synth.from_torch(ws), rs)
 
 
-@pytest.mark.parametrize("m,k,bf16", [(1, 64, True), (7, 1088, True), (300, 4096, False), (1000, 11008, True)])
+@pytest.mark.parametrize("m,k,bf16", [(1, 64, True), (7, 1088, True), (33, 5120, True), (300, 4096, False),
+                                      (1000, 11008, True),
+                                      # more than 65535 blocks of 32 rows: taller blocks, ragged last one
+                                      (65535 * 32 + 37, 64, True)])
 def test_quant_act_cases(m, k, bf16):
     import torch
     d = dev()

@@ -27,6 +27,7 @@ inside the timed steps) and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import itertools
 import json
 import os
 import sys
@@ -48,8 +49,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--overlap", action="store_true",
-                    help="run the preparation chain on a second stream, overlapping the GEMMs (default: one "
-                         "stream; overlapping shortens the step a little but slows the GEMMs it runs beside)")
+                    help="two phases (attention, MLP projections) on two streams: each phase's preparation on a "
+                         "second stream, its grouped GEMM on the main stream, so preparation runs beside the "
+                         "other phase's GEMM")
     ap.add_argument("--ramp-seconds", type=float, default=0.5,
                     help="untimed steps for at least this long before the warm-up steps: after the host-side "
                          "setup the GPU needs a few hundred ms of sustained load before its step time settles")
@@ -66,7 +68,7 @@ def parse():
                          "profiles/gemm_traffic__llama13b_prefill2048.md, used only if it matches gemm.hip)")
     ap.add_argument("--workload", default="layer13b",
                     choices=["layer13b", "decode7b", "alpha_search", "prefill70b", "hbm_passes", "copy_probe",
-                             "variants", "fp8", "ceilings"],
+                             "variants", "fp8", "ceilings", "c1"],
                     help="layer13b (default, the headline line); the others measure the remaining "
                          "workloads, one JSON line each")
     return ap.parse_args()
@@ -97,6 +99,45 @@ def setup(device):
         projs.append((name, groups[g], layer, w_host))
     torch.cuda.synchronize()
     return groups, projs
+
+
+PHASES = (("q", "k", "v", "o"), ("gate", "up", "down"))  # attention, then MLP: no input in common
+
+
+def phased_block(groups, projs):
+    """The 13B block as two phases (attention projections, MLP projections)."""
+    from w8a8_post_quantization_channel_amd.layer import PhasedBlock
+    by_name = {name: (g, layer) for name, g, layer, _ in projs}
+    phases = []
+    for names in PHASES:
+        used = []
+        for n in names:
+            if by_name[n][0] not in used:
+                used.append(by_name[n][0])
+        phases.append(([by_name[n][1] for n in names], [(g.x, g.act_max) for g in used],
+                       [by_name[n][0].x for n in names]))
+    return PhasedBlock(phases)
+
+
+def run_phased(block, side, gemm_events=None):
+    """One pass of the whole path on two streams (preparation on `side`, the
+    two grouped GEMM launches on the current stream); gemm_events as in
+    run_step, one pair per phase ("attn", "mlp")."""
+    import torch
+    main = torch.cuda.current_stream()
+    marks = {}
+
+    def on_gemm(i, before):
+        if gemm_events is None:
+            return
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(main)
+        if before:
+            marks[i] = e
+        else:
+            gemm_events.append((("attn", "mlp")[i], marks[i], e))
+
+    block.step(side, main, on_gemm)
 
 
 def run_step(groups, projs, gemm_events=None, side=None, batched=True):
@@ -186,13 +227,26 @@ def gemm_ops(projs, m):
     return sum(2.0 * m * layer.n * layer.k for _, _, layer, _ in projs)
 
 
-def cpu_baseline(groups, projs, rows):
+def cpu_baseline(groups, projs, rows, one_thread_rows=32):
     """The CPU oracle on a bounded sample of one step: every statistic and
     quantization pass in full, each GEMM on `rows` of the 2048 output rows;
-    the full-step time is extrapolated linearly in GEMM rows."""
-    import numpy as np
+    the full-step time is extrapolated linearly in GEMM rows. Run on all the
+    threads the oracle starts with, then again on one thread (GEMMs on
+    one_thread_rows rows)."""
     from oracle.oracle import Oracle
     o = Oracle()
+    out = oracle_step(o, groups, projs, rows)
+    threads = o.num_threads()
+    o.set_num_threads(1)
+    one = oracle_step(o, groups, projs, one_thread_rows)
+    o.set_num_threads(threads)
+    out["cpu_model"] = cpu_model()
+    out["one_thread"] = {"value": one["value"], "unit": "TOPS", "cores": 1, "sample": one["sample"]}
+    return out
+
+
+def oracle_step(o, groups, projs, rows):
+    import numpy as np
     m = next(iter(groups.values())).x_host.shape[0]
     t_total = 0.0
     wall0 = time.perf_counter()
@@ -313,7 +367,45 @@ def workload_decode7b(device):
             "value": tot_b, "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "dtype": "int8",
             "data": "synthetic",
             "config": {"workload": "llama2-7b decode, M in {1,8,16,64}, 32 rotating layers, HIP-graph replay"},
-            "per_case": out}
+            "per_case": out, "cpu_oracle": decode_oracle_times()}
+
+
+def decode_oracle_times(ms=(1, 64)):
+    """The oracle's act quant + int8 GEMM + bf16 dequant for one decode call
+    of each 7B shape, on all of its threads and on one (median of 3)."""
+    import os as _os
+    import statistics
+    import numpy as np
+    from oracle.oracle import Oracle
+    from w8a8_post_quantization_channel_amd import synth
+    o = Oracle()
+    threads = min(len(_os.sched_getaffinity(0)), 16)
+    g = np.random.default_rng(3100)
+    res = {"cpu_model": cpu_model(), "threads": threads}
+    for name, n, k in synth.SHAPES_7B:
+        wq = g.integers(-127, 128, (n, k), dtype=np.int8)
+        ws = g.uniform(1e-4, 1e-3, n).astype(np.float32)
+        inv_s = g.uniform(0.5, 1.5, k).astype(np.float32)
+        for m in ms:
+            x = g.standard_normal((m, k), dtype=np.float32)
+
+            def call():
+                xq = o.quant_act(x, inv_s, np.float32(0.05))
+                o.dequant(o.gemm_i32(xq, wq), np.float32(0.05), ws, bf16=True)
+
+            row = {}
+            for label, t in (("all_threads_us", threads), ("one_thread_us", 1)):
+                o.set_num_threads(t)
+                call()
+                times = []
+                for _ in range(3):
+                    t0 = time.perf_counter()
+                    call()
+                    times.append((time.perf_counter() - t0) * 1e6)
+                row[label] = statistics.median(times)
+            res[f"{name}_{n}x{k}_m{m}"] = row
+    o.set_num_threads(threads)
+    return res
 
 
 def workload_alpha_search(device):
@@ -420,7 +512,11 @@ def workload_prefill70b(device):
 def workload_hbm_passes(device):
     """The HBM-bound passes at the workloads' largest sizes: calibration
     absmax over 512 x 512 tokens (K = 5120 and 13824), activation quant at
-    4096 x 28672, weight absmax + quant of a 28672 x 8192 weight."""
+    4096 x 28672 and over the 262144 x 5120 calibration-size tensor, weight
+    absmax + quant of a 28672 x 8192 weight and weight quant of each 13B
+    shape and of the 13B block (batched). Passes that move less than 1.1 GB
+    per call cycle through enough buffer sets to exceed it, so repeated calls
+    do not run from the 256 MB Infinity Cache."""
     import torch
     from w8a8_post_quantization_channel_amd import capi, synth
     out = {}
@@ -433,55 +529,73 @@ def workload_hbm_passes(device):
                                            "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
         del x
         torch.cuda.empty_cache()
-    m, k = 4096, 28672
-    x = torch.randn((m, k), device=device).to(torch.bfloat16)
-    inv_s = torch.rand(k, device=device) + 0.5
-    a = torch.full((4,), 0.05, device=device)
-    xq = torch.empty((m, k), dtype=torch.int8, device=device)
-    ms = timed(lambda: capi.sq_smooth_quant_act(x, inv_s, a, xq), 10)
-    byts = m * k * 3 + k * 4
-    out["act_quant_4096x28672"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
-                                   "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    n, k = 28672, 8192
-    w = (torch.randn((n, k), device=device) * 0.02).to(torch.bfloat16)
-    s = torch.rand(k, device=device) + 0.5
-    wm = torch.empty(k, dtype=torch.float32, device=device)
-    wq = torch.empty((n, k), dtype=torch.int8, device=device)
-    wsc = torch.empty(n, dtype=torch.float32, device=device)
-    ms = timed(lambda: capi.sq_calib_absmax(w, wm, False), 10)
-    byts = n * k * 2 + k * 4
-    out["weight_absmax_28672x8192"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
-                                       "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    ms = timed(lambda: capi.sq_quant_weight(w, s, wq, wsc), 10)
-    byts = n * k * 3 + k * 4 + n * 4
-    out["weight_quant_28672x8192"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
-                                      "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    for n, k in ((5120, 5120), (13824, 5120), (5120, 13824)):
-        w = (torch.randn((n, k), device=device) * 0.02).to(torch.bfloat16)
-        s = torch.rand(k, device=device) + 0.5
-        wq = torch.empty((n, k), dtype=torch.int8, device=device)
-        wsc = torch.empty(n, dtype=torch.float32, device=device)
-        ms = timed(lambda: capi.sq_quant_weight(w, s, wq, wsc), 20)
-        byts = n * k * 3 + k * 4 + n * 4
-        out[f"weight_quant_{n}x{k}"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
-                                        "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    # every pass below runs over enough buffer sets (each call the next set)
+    # that one cycle moves more than 1.1 GB, past the 256 MB Infinity Cache
+    def sets_for(nbytes):
+        return max(1, -(-int(1.1e9) // int(nbytes)))
+
+    def cycle(calls):
+        it = itertools.cycle(calls)
+        return lambda: next(it)()
+
+    def record(key, ms, byts, nsets):
+        out[key] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
+                    "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "buffer_sets": nsets}
+
+    # activation quant: the 70B MLP input (4096 x 28672) and the 13B
+    # calibration-size tensor (262144 x 5120, 4.0 GB of traffic)
+    for m, k in ((4096, 28672), (262144, 5120)):
+        byts = m * k * 3 + k * 4
+        nsets = sets_for(byts)
+        inv_s = torch.rand(k, device=device) + 0.5
+        a = torch.full((4,), 0.05, device=device)
+        bufs = [((torch.randn((m, k), device=device) * 0.5).to(torch.bfloat16),
+                 torch.empty((m, k), dtype=torch.int8, device=device)) for _ in range(nsets)]
+        ms = timed(cycle([lambda x=x, xq=xq: capi.sq_smooth_quant_act(x, inv_s, a, xq) for x, xq in bufs]),
+                   max(10, 2 * nsets))
+        record(f"act_quant_{m}x{k}", ms, byts, nsets)
+        if nsets > 1:  # the same call on one buffer set, for comparison
+            x, xq = bufs[0]
+            ms = timed(lambda: capi.sq_smooth_quant_act(x, inv_s, a, xq), 10)
+            record(f"act_quant_{m}x{k}_same_buffers", ms, byts, 1)
+        del bufs
+        torch.cuda.empty_cache()
+    # weight statistics and codes of a 70B MLP weight and of each 13B shape
+    for n, k in ((28672, 8192), (5120, 5120), (13824, 5120), (5120, 13824)):
+        qbytes = n * k * 3 + k * 4 + n * 4
+        nsets = sets_for(qbytes)
+        bufs = [((torch.randn((n, k), device=device) * 0.02).to(torch.bfloat16),
+                 torch.rand(k, device=device) + 0.5, torch.empty(k, dtype=torch.float32, device=device),
+                 torch.empty((n, k), dtype=torch.int8, device=device),
+                 torch.empty(n, dtype=torch.float32, device=device)) for _ in range(nsets)]
+        if n == 28672:
+            ms = timed(cycle([lambda w=w, wm=wm: capi.sq_calib_absmax(w, wm, False) for w, _, wm, _, _ in bufs]),
+                       max(10, 2 * nsets))
+            record(f"weight_absmax_{n}x{k}", ms, n * k * 2 + k * 4, nsets)
+        ms = timed(cycle([lambda w=w, s_=s_, wq=wq, wsc=wsc: capi.sq_quant_weight(w, s_, wq, wsc)
+                          for w, s_, _, wq, wsc in bufs]), max(10, 2 * nsets))
+        record(f"weight_quant_{n}x{k}", ms, qbytes, nsets)
+        del bufs
+        torch.cuda.empty_cache()
     # the 13B block's seven weights as the step prepares them: statistics and
     # codes from the batched entry points
     blk = [(5120, 5120)] * 4 + [(13824, 5120)] * 2 + [(5120, 13824)]
-    W = [(torch.randn(sh, device=device) * 0.02).to(torch.bfloat16) for sh in blk]
-    S = [torch.rand(k, device=device) + 0.5 for _, k in blk]
-    WQ = [torch.empty(sh, dtype=torch.int8, device=device) for sh in blk]
-    WS = [torch.empty(n, dtype=torch.float32, device=device) for n, _ in blk]
-    WM = [torch.empty(k, dtype=torch.float32, device=device) for _, k in blk]
-    ms = timed(lambda: capi.sq_calib_absmax_batched(W, WM, False), 10)
-    byts = sum(n * k * 2 + k * 4 for n, k in blk)
-    out["weight_absmax_13b_block_batched"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
-                                              "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    ms = timed(lambda: capi.sq_quant_weight_batched(W, S, WQ, WS), 10)
-    byts = sum(n * k * 3 + k * 4 + n * 4 for n, k in blk)
-    out["weight_quant_13b_block_batched"] = {"us": ms * 1e3, "GB/s": byts / (ms * 1e-3) / 1e9,
-                                             "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    del W, S, WQ, WS, WM
+    qbytes = sum(n * k * 3 + k * 4 + n * 4 for n, k in blk)
+    nsets = sets_for(qbytes)
+    sets = []
+    for _ in range(nsets):
+        sets.append(([(torch.randn(sh, device=device) * 0.02).to(torch.bfloat16) for sh in blk],
+                     [torch.rand(k, device=device) + 0.5 for _, k in blk],
+                     [torch.empty(sh, dtype=torch.int8, device=device) for sh in blk],
+                     [torch.empty(n, dtype=torch.float32, device=device) for n, _ in blk],
+                     [torch.empty(k, dtype=torch.float32, device=device) for _, k in blk]))
+    ms = timed(cycle([lambda W=W, WM=WM: capi.sq_calib_absmax_batched(W, WM, False) for W, _, _, _, WM in sets]),
+               max(10, 2 * nsets))
+    record("weight_absmax_13b_block_batched", ms, sum(n * k * 2 + k * 4 for n, k in blk), nsets)
+    ms = timed(cycle([lambda W=W, S=S, WQ=WQ, WS=WS: capi.sq_quant_weight_batched(W, S, WQ, WS)
+                      for W, S, WQ, WS, _ in sets]), max(10, 2 * nsets))
+    record("weight_quant_13b_block_batched", ms, qbytes, nsets)
+    del sets
     torch.cuda.empty_cache()
     # practical ceilings on the same tensor sizes: a plain copy (read = write)
     # and a plain bf16 -> int8 conversion (2 bytes read per byte written, the
@@ -499,7 +613,8 @@ def workload_hbm_passes(device):
                                               "hbm_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     calib = [v for kk, v in out.items() if kk.startswith("calib")]
     return {"metric": "HBM GB/s of the calibration absmax (512x512 tokens) and activation quant passes",
-            "value": min(v["GB/s"] for v in calib + [out["act_quant_4096x28672"]]), "unit": "GB/s",
+            "value": min(v["GB/s"] for v in calib + [out["act_quant_4096x28672"], out["act_quant_262144x5120"]]),
+            "unit": "GB/s",
             "n_gpus": 1, "higher_is_better": True, "dtype": "bf16->fp32/int8", "data": "synthetic",
             "config": {"workload": "largest HBM passes of the 13B calibration and 70B prefill workloads"},
             "per_pass": out}
@@ -540,7 +655,8 @@ def workload_ceilings(device):
     """Measured ceilings written for this path: an MFMA-only loop (int8
     v_mfma_i32_32x32x32_i8 on register operands: all-ones bytes, random bytes,
     or fragments of the step's own codes; 8 independent chains per wave, 1 and
-    2 blocks of 4 waves per compute unit), a 16-byte-vector copy and a
+    2 blocks of 4 waves per compute unit), a 16-byte-vector copy, a narrowing
+    copy (2 bytes read per byte written, the quantizers' mix) and a
     16-byte-vector read of 1 GiB each (well past the 256 MB Infinity Cache).
     Each MFMA run is checked against its closed-form sum, the copy byte for
     byte, the read against the XOR of its words."""
@@ -582,6 +698,15 @@ def workload_ceilings(device):
     ms = timed(lambda: capi.sq_ceiling_copy(src, dst), 10)
     out["copy_1GiB"] = {"GB/s": 2 * n / (ms * 1e-3) / 1e9, "hbm_frac": 2 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     del dst
+    half = torch.empty(n // 2, dtype=torch.uint8, device=device)
+    capi.sq_ceiling_narrow(src, half)
+    torch.cuda.synchronize()
+    if not torch.equal(half, src.view(-1, 16)[:, :8].reshape(-1)):
+        raise RuntimeError("narrowing copy check failed")
+    ms = timed(lambda: capi.sq_ceiling_narrow(src, half), 10)
+    out["narrow_1GiB_to_512MiB"] = {"GB/s": 1.5 * n / (ms * 1e-3) / 1e9,
+                                    "hbm_frac": 1.5 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del half
     xor = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
     sink.zero_()
     capi.sq_ceiling_read(src, sink)
@@ -594,6 +719,115 @@ def workload_ceilings(device):
             "value": out["mfma_loop_codes_1_blocks_per_cu"]["TOPS"], "unit": "TOPS",
             "n_gpus": 1, "higher_is_better": True, "dtype": "int8 / bytes", "data": "synthetic",
             "config": {"workload": "MFMA-only loop on every compute unit; 1 GiB copy and read"}, "per_case": out}
+
+
+def workload_c1(device):
+    """The pages' small fp32 example (X 16x1024 with input channel 50 at 100,
+    W 2048x1024, alpha 0.5, calibrated on X itself): latency of the whole path
+    (calibration absmax of X, weight absmax, smoothing factors, weight codes,
+    activation codes, int8 GEMM with fp32 output; six launches), eager and
+    replayed from a HIP graph, each checked bit for bit against the oracle;
+    beside it the oracle's time for the same pass on all host cores and on
+    one. Medians over repeated passes."""
+    import os as _os
+    import statistics
+    import numpy as np
+    import torch
+    from oracle.oracle import Oracle
+    from w8a8_post_quantization_channel_amd import capi, synth
+    xh, wh = synth.c1()
+    n, k = wh.shape
+    m = xh.shape[0]
+    x, w = torch.from_numpy(xh).to(device), torch.from_numpy(wh).to(device)
+    f32 = dict(dtype=torch.float32, device=device)
+    act_max, w_max = torch.empty(k, **f32), torch.empty(k, **f32)
+    s, inv_s, a = torch.empty(k, **f32), torch.empty(k, **f32), torch.empty(4, **f32)
+    wq, ws = torch.empty((n, k), dtype=torch.int8, device=device), torch.empty(n, **f32)
+    xq, y = torch.empty((m, k), dtype=torch.int8, device=device), torch.empty((m, n), **f32)
+
+    def path():
+        capi.sq_calib_absmax(x, act_max, False)
+        capi.sq_calib_absmax(w, w_max, False)
+        capi.sq_smooth_factors(act_max, w_max, 0.5, s, inv_s, a)
+        capi.sq_quant_weight(w, s, wq, ws)
+        capi.sq_smooth_quant_act(x, inv_s, a, xq)
+        capi.sq_w8a8_gemm(xq, wq, a, ws, y)
+
+    o = Oracle()
+    ref = o.layer_forward([xh], wh, xh, 0.5, bf16_out=False)["y"]
+
+    def check(what):
+        torch.cuda.synchronize()
+        if not np.array_equal(y.cpu().numpy(), ref):
+            raise RuntimeError(f"C1 output differs from the oracle ({what})")
+
+    path()
+    check("eager")
+
+    def per_pass(fn, reps=300):
+        wall, gpu = [], []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            wall.append((time.perf_counter() - t0) * 1e6)
+            gpu.append(e0.elapsed_time(e1) * 1e3)
+        return statistics.median(wall), statistics.median(gpu)
+
+    for _ in range(50):
+        path()
+    eager_wall, eager_gpu = per_pass(path)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        path()
+    for rep in range(3):  # every replay checked, eager work between replays
+        y.zero_()
+        graph.replay()
+        check(f"graph replay {rep}")
+        path()
+        check(f"eager after replay {rep}")
+    graph_wall, graph_gpu = per_pass(graph.replay)
+    check("after timed replays")
+
+    def oracle_us(threads, reps=7):
+        o.set_num_threads(threads)
+        t = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            o.layer_forward([xh], wh, xh, 0.5, bf16_out=False)
+            t.append((time.perf_counter() - t0) * 1e6)
+        return statistics.median(t)
+
+    cores = len(_os.sched_getaffinity(0))
+    cpu_all = oracle_us(min(cores, 16))
+    cpu_one = oracle_us(1)
+    o.set_num_threads(min(cores, 16))
+    return {"metric": "C1 (16x1024 -> 2048, fp32) whole-path latency, HIP-graph replay", "value": graph_wall,
+            "unit": "us", "n_gpus": 1, "higher_is_better": False, "dtype": "fp32 in/out, int8 codes",
+            "data": "synthetic (the pages' example shapes: N(0,1)*5, channel 50 = 100; W N(0,1); seed 101)",
+            "config": {"workload": "C1 single fp32 layer, 6 launches per pass", "m": m, "n": n, "k": k},
+            "graph_replay_us": {"host_wall": graph_wall, "gpu_events": graph_gpu},
+            "eager_us": {"host_wall": eager_wall, "gpu_events": eager_gpu},
+            "oracle_us": {"threads": min(cores, 16), "all_threads": cpu_all, "one_thread": cpu_one,
+                          "cpu_model": cpu_model()},
+            "check": "output bit-identical to the oracle (eager, each graph replay)"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def workload_variants(device):
@@ -743,7 +977,7 @@ def main():
     device = torch.device("cuda", 0)
     other = {"decode7b": workload_decode7b, "alpha_search": workload_alpha_search, "copy_probe": workload_copy_probe,
              "prefill70b": workload_prefill70b, "hbm_passes": workload_hbm_passes, "variants": workload_variants,
-             "ceilings": workload_ceilings,
+             "ceilings": workload_ceilings, "c1": workload_c1,
              "fp8": workload_fp8}
     if args.workload in other:
         out = other[args.workload](device)
@@ -755,15 +989,25 @@ def main():
     side = torch.cuda.Stream() if args.overlap else None  # default priority, like the main stream
 
     batched = not args.per_projection
+    if args.overlap:
+        if not batched:
+            raise SystemExit("--overlap runs the batched entry points; drop --per-projection")
+        block = phased_block(groups, projs)
+
+        def one_step(ev=None):
+            run_phased(block, side, ev)
+    else:
+        def one_step(ev=None):
+            run_step(groups, projs, ev, batched=batched)
     ramp_steps = 0
     t_ramp = time.perf_counter()
     while time.perf_counter() - t_ramp < args.ramp_seconds:
         for _ in range(10):
-            run_step(groups, projs, side=side, batched=batched)
+            one_step()
         torch.cuda.synchronize()
         ramp_steps += 10
     for _ in range(args.warmup):
-        run_step(groups, projs, side=side, batched=batched)
+        one_step()
     torch.cuda.synchronize()
 
     events = []
@@ -771,7 +1015,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run_step(groups, projs, events if i % every == 0 else None, side=side, batched=batched)
+        one_step(events if i % every == 0 else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -787,6 +1031,8 @@ def main():
         by_name.setdefault(name, []).append(t)
     ops_by_name = {name: 2.0 * m * layer.n * layer.k for name, _, layer, _ in projs}
     ops_by_name["block"] = ops
+    for tag, names in zip(("attn", "mlp"), PHASES):
+        ops_by_name[tag] = sum(ops_by_name[n] for n in names)
     avg_launch_ms = sum(gemm_ms) / len(gemm_ms)
     avg_launch_ops = sum(ops_by_name[n] for n, _, _ in events) / len(events)
     achieved = avg_launch_ops / (avg_launch_ms * 1e-3) / 1e12
@@ -795,6 +1041,8 @@ def main():
                 "frac": achieved / PEAK_INT8_TOPS, "traffic": traffic,
                 "kernel": "gemm_dma_kernel<OpI8, TN, EpiDequant<bf16>> (256 x 32*TN tiles), one launch per "
                           "projection" if args.per_projection else
+                          "gemm_dma_grouped_kernel<OpI8, TN, bf16> (256 x 32*TN tiles), one launch per phase "
+                          "(q, k, v, o; gate, up, down), beside the other phase's preparation" if args.overlap else
                           "gemm_dma_grouped_kernel<OpI8, TN, bf16> (256 x 32*TN tiles), one launch for the 7 "
                           "projections",
                 "tiling": {n: list(capi.sq_gemm_tiling(m, layer.n)) for n, _, layer, _ in projs},
@@ -816,8 +1064,8 @@ def main():
                    "step": "calib absmax + weight absmax + smoothing + weight quant + act quant + int8 GEMM",
                    "preparation": "per projection" if args.per_projection else
                    "batched over the 7 projections (statistics, smoothing, weight codes)",
-                   "schedule": "two streams: GEMM of projection p overlaps the preparation of projection p + 1"
-                   if args.overlap else "one stream"},
+                   "schedule": "two streams, two phases (q, k, v, o; gate, up, down): a phase's grouped GEMM "
+                   "runs beside the other phase's preparation" if args.overlap else "one stream"},
         "roofline": roofline,
         "ramp_steps": ramp_steps,
         "gemm_events": f"every {every}th timed step ({len(events)} GEMM launches bracketed)",

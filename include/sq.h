@@ -370,6 +370,11 @@ sq_status sq_w8a8_gemm_batched(int count, const int8_t* const* xq, const int8_t*
  * sq_ceiling_copy copies `bytes` (a multiple of 16; src and dst 16-byte
  * aligned, not overlapping) with 16-byte vector loads and stores only.
  *
+ * sq_ceiling_narrow reads src_bytes (a multiple of 16; src 16-byte aligned)
+ * and writes src_bytes / 2 to dst (8-byte aligned, not overlapping src): the
+ * first 8 bytes of every 16-byte vector, in order. Two bytes read per byte
+ * written, the traffic mix of the quantizers.
+ *
  * sq_ceiling_read reads `bytes` (a multiple of 16, src 16-byte aligned) with
  * 16-byte vector loads and XORs every 32-bit word read into sink[0] (device,
  * 4-byte aligned; the caller sets its start value), which keeps the loads
@@ -379,6 +384,7 @@ sq_status sq_w8a8_gemm_batched(int count, const int8_t* const* xq, const int8_t*
 sq_status sq_ceiling_mfma(int64_t iters, int blocks_per_cu, const void* operands, uint32_t* sink,
                           int64_t* ops, hipStream_t stream);
 sq_status sq_ceiling_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+sq_status sq_ceiling_narrow(const void* src, void* dst, int64_t src_bytes, hipStream_t stream);
 sq_status sq_ceiling_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */

@@ -41,6 +41,8 @@ def _declare(lib):
     P = c.c_void_p
     i64 = c.c_int64
     lib.sqo_num_threads.restype = c.c_int
+    lib.sqo_set_num_threads.argtypes = [c.c_int]
+    lib.sqo_set_num_threads.restype = None
     lib.sqo_calib_absmax.argtypes = [P, c.c_int, i64, i64, P, c.c_int]
     lib.sqo_act_scale.argtypes = [P, P, i64]
     lib.sqo_act_scale.restype = c.c_float
@@ -114,6 +116,11 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.lib.sqo_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        """Threads for later calls from this thread (timing only: results do
+        not depend on the count)."""
+        self.lib.sqo_set_num_threads(int(n))
 
     # O1 / O2
     def calib_absmax(self, x: np.ndarray, absmax: np.ndarray | None = None) -> np.ndarray:

@@ -24,6 +24,8 @@
 
 int sqo_num_threads(void) { return omp_get_max_threads(); }
 
+void sqo_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 static float bf16_bits_to_float(uint16_t h) {
     uint32_t u = (uint32_t)h << 16;
     float f;

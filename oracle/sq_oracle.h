@@ -49,6 +49,11 @@ enum { SQO_F32 = 0, SQO_BF16 = 1 };
 /* Number of OpenMP threads the oracle's outer loops use. */
 int sqo_num_threads(void);
 
+/* Set that number for later calls from the calling thread (n < 1 means 1).
+ * Results do not depend on it: the parallel loops run over independent rows
+ * or columns, and per-row partial sums are added in row order afterwards. */
+void sqo_set_num_threads(int n);
+
 /* O1/O2: absmax[j] = max(absmax_in[j] if accumulate else 0, max_t |x[t,j]|). */
 void sqo_calib_absmax(const void* x, int xtype, int64_t rows, int64_t k,
                       float* absmax, int accumulate);

@@ -250,3 +250,55 @@ def test_block_forward_batched_equals_single_calls():
     for (p, *_), a1, a2, b1, b2 in zip(projs, xq1, xq2, y1, y2):
         assert torch.equal(a1, a2), (p, "xq")
         assert torch.equal(b1.view(torch.int16), b2.view(torch.int16)), (p, "y")
+
+
+def test_phased_block_equals_one_stream():
+    """The 13B block run as two phases on two streams (preparation of one
+    phase beside the other's products, passes back to back) gives the same
+    codes and outputs, bit for bit, as the one-stream block on every pass."""
+    import torch
+    from w8a8_post_quantization_channel_amd.layer import PhasedBlock, W8A8Linear, forward_block, prepare_block
+    rows = 512
+    groups = {g: _t(synth.c2_group_x(g, rows=rows)) for g in synth.C2_GROUPS}
+
+    def make():
+        layers, acts = {}, {}
+        for g, x in groups.items():
+            acts[g] = torch.empty(x.shape[1], dtype=torch.float32, device=dev())
+        for p, g, *_ in synth.C2_PROJECTIONS:
+            layer = W8A8Linear(_t(synth.c2_projection_w(p)), alpha=0.5, max_tokens=rows, out_dtype=torch.bfloat16)
+            layer.act_max = acts[g]
+            layers[p] = layer
+        return layers, acts
+
+    names = [p for p, *_ in synth.C2_PROJECTIONS]
+    grp = {p: g for p, g, *_ in synth.C2_PROJECTIONS}
+    ref_layers, ref_acts = make()
+    prepare_block([ref_layers[p] for p in names], [(groups[g], ref_acts[g]) for g in groups])
+    ref_y = forward_block([ref_layers[p] for p in names], [groups[grp[p]] for p in names])
+    torch.cuda.synchronize()
+
+    layers, acts = make()
+    phases = []
+    for part in (("q", "k", "v", "o"), ("gate", "up", "down")):
+        used = sorted({grp[p] for p in part})
+        phases.append(([layers[p] for p in part], [(groups[g], acts[g]) for g in used],
+                       [groups[grp[p]] for p in part]))
+    block = PhasedBlock(phases)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    for rep in range(3):
+        ys = block.step(side, main)
+        torch.cuda.synchronize()
+        for p, y, r in zip(names, ys, ref_y):
+            assert torch.equal(y.view(torch.int16), r.view(torch.int16)), (rep, p)
+            assert torch.equal(layers[p].wq, ref_layers[p].wq), (rep, p)
+            assert torch.equal(layers[p].xq, ref_layers[p].xq), (rep, p)
+    # passes enqueued back to back, synchronised only at the end
+    for p in names:
+        layers[p].y.zero_()
+    for _ in range(4):
+        ys = block.step(side, main)
+    torch.cuda.synchronize()
+    for p, y, r in zip(names, ys, ref_y):
+        assert torch.equal(y.view(torch.int16), r.view(torch.int16)), ("back to back", p)

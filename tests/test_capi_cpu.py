@@ -440,7 +440,7 @@ def test_batched_act_and_gemm_validation(lib):
 
 
 def test_ceiling_validation(lib):
-    for name in ("sq_ceiling_mfma", "sq_ceiling_copy", "sq_ceiling_read"):
+    for name in ("sq_ceiling_mfma", "sq_ceiling_copy", "sq_ceiling_read", "sq_ceiling_narrow"):
         assert name in capi.declared_functions() and hasattr(lib, name)
     ops = ctypes.c_int64(0)
     assert lib.sq_ceiling_mfma(100, 1, P(A), None, ctypes.byref(ops), None) == NULL
@@ -462,6 +462,13 @@ def test_ceiling_validation(lib):
     assert lib.sq_ceiling_read(P(MIS), 1024, P(A), None) == ALIGN
     assert lib.sq_ceiling_read(P(A), 1024, P(A + 2), None) == ALIGN
     assert lib.sq_ceiling_read(None, 0, P(A), None) == OK
+    assert lib.sq_ceiling_narrow(None, P(A), 1024, None) == NULL
+    assert lib.sq_ceiling_narrow(P(A), P(A + 0x1000), 1000, None) == SHAPE
+    assert lib.sq_ceiling_narrow(P(A), P(A + 256), 1024, None) == SHAPE  # dst inside src
+    assert lib.sq_ceiling_narrow(P(A + 0x1000), P(A + 0x1000 - 256), 1024, None) == SHAPE  # dst runs into src
+    assert lib.sq_ceiling_narrow(P(MIS), P(A + 0x1000), 1024, None) == ALIGN
+    assert lib.sq_ceiling_narrow(P(A), P(A + 0x1004), 1024, None) == ALIGN
+    assert lib.sq_ceiling_narrow(None, None, 0, None) == OK
 
 
 def test_ceiling_chain_dots():

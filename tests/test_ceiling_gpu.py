@@ -62,3 +62,16 @@ def test_read(nbytes):
     capi.sq_ceiling_read(src, sink)
     torch.cuda.synchronize()
     assert int(sink[0].item()) % (1 << 32) == expect ^ 0x5A5A5A5A
+
+
+@pytest.mark.parametrize("nbytes", SIZES)
+def test_narrow(nbytes):
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(nbytes + 2)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    dst = torch.full((nbytes // 2 + 64,), 7, dtype=torch.uint8, device="cuda")
+    capi.sq_ceiling_narrow(src, dst[:nbytes // 2])
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes // 2], src.view(-1, 16)[:, :8].reshape(-1))
+    assert bool((dst[nbytes // 2:] == 7).all())

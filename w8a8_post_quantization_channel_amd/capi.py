@@ -71,6 +71,7 @@ def _declare(lib):
         "sq_ceiling_mfma": [i64, c.c_int, P, P, P, P],
         "sq_ceiling_copy": [P, P, i64, P],
         "sq_ceiling_read": [P, i64, P, P],
+        "sq_ceiling_narrow": [P, P, i64, P],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -306,6 +307,16 @@ def sq_ceiling_copy(src, dst, stream=None):
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("src and dst differ in size")
     _check("sq_ceiling_copy", load().sq_ceiling_copy(_dev(src, "src"), _dev(dst, "dst"), nbytes, _stream(stream)))
+
+
+def sq_ceiling_narrow(src, dst, stream=None):
+    """Reads src, writes the first 8 bytes of every 16-byte vector of it to
+    dst (half src's size)."""
+    nbytes = src.numel() * src.element_size()
+    if 2 * dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst must hold half of src's bytes")
+    _check("sq_ceiling_narrow", load().sq_ceiling_narrow(_dev(src, "src"), _dev(dst, "dst"), nbytes,
+                                                         _stream(stream)))
 
 
 def sq_ceiling_read(src, sink, stream=None):

@@ -62,6 +62,29 @@ __global__ __launch_bounds__(256) void copy_kernel(const sqd::u32x4* __restrict_
         dst[i] = src[i];
 }
 
+// Two bytes read per byte written (the traffic mix of the quantizers): each
+// 32 KiB chunk of src gives the first 8 bytes of every 16-byte vector to dst
+// (8-byte stores), in the same chunks and with the same loads in flight as
+// the copy. The last partial chunk goes vector by vector.
+__global__ __launch_bounds__(256) void narrow_kernel(const sqd::u32x4* __restrict__ src, sqd::u32x2* __restrict__ dst,
+                                                     int64_t nvec) {
+    const int64_t nchunk = nvec / (256 * kCopyUnroll);
+    for (int64_t c = blockIdx.x; c < nchunk; c += gridDim.x) {
+        const int64_t base = c * (256 * kCopyUnroll) + threadIdx.x;
+        sqd::u32x4 t[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) t[u] = __builtin_nontemporal_load(src + base + u * 256);
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+            __builtin_nontemporal_store(sqd::u32x2{t[u][0], t[u][1]}, dst + base + u * 256);
+    }
+    for (int64_t i = nchunk * (256 * kCopyUnroll) + (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec;
+         i += (int64_t)gridDim.x * 256) {
+        const sqd::u32x4 t = src[i];
+        dst[i] = sqd::u32x2{t[0], t[1]};
+    }
+}
+
 // Read-only stream over the same chunks: each wave XORs everything it loads
 // and lane 0 XORs the wave's word into sink[0], so the loads stay live and
 // the caller can check the sum against the XOR of all input words.
@@ -122,6 +145,14 @@ hipError_t ceiling_copy(const void* src, void* dst, int64_t bytes, hipStream_t s
     const int64_t nvec = bytes / 16;
     if (nvec == 0) return hipSuccess;
     copy_kernel<<<dim3(stream_blocks(nvec)), dim3(256), 0, stream>>>((const sqd::u32x4*)src, (sqd::u32x4*)dst, nvec);
+    return hipGetLastError();
+}
+
+hipError_t ceiling_narrow(const void* src, void* dst, int64_t src_bytes, hipStream_t stream) {
+    const int64_t nvec = src_bytes / 16;
+    if (nvec == 0) return hipSuccess;
+    narrow_kernel<<<dim3(stream_blocks(nvec)), dim3(256), 0, stream>>>((const sqd::u32x4*)src, (sqd::u32x2*)dst,
+                                                                       nvec);
     return hipGetLastError();
 }
 

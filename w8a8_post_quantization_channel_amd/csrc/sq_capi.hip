@@ -520,6 +520,15 @@ sq_status sq_ceiling_copy(const void* src, void* dst, int64_t bytes, hipStream_t
     return hip_status(sqk::ceiling_copy(src, dst, bytes, stream));
 }
 
+sq_status sq_ceiling_narrow(const void* src, void* dst, int64_t src_bytes, hipStream_t stream) {
+    if (src_bytes > 0 && (!src || !dst)) return SQ_ERR_NULL;
+    if (src_bytes < 0 || src_bytes % 16 != 0) return SQ_ERR_SHAPE;
+    if (src_bytes > 0 && (!aligned16(src) || ((uintptr_t)dst & 7u) != 0)) return SQ_ERR_ALIGN;
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst, db = (uintptr_t)(src_bytes / 2);
+    if (src_bytes > 0 && s0 < d0 + db && d0 < s0 + (uintptr_t)src_bytes) return SQ_ERR_SHAPE;
+    return hip_status(sqk::ceiling_narrow(src, dst, src_bytes, stream));
+}
+
 sq_status sq_ceiling_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
     if (!sink || (bytes > 0 && !src)) return SQ_ERR_NULL;
     if (bytes < 0 || bytes % 16 != 0) return SQ_ERR_SHAPE;

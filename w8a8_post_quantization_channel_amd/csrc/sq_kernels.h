@@ -165,5 +165,6 @@ hipError_t ceiling_mfma(int64_t iters, int blocks_per_cu, const void* operands, 
 int64_t ceiling_mfma_ops(int64_t iters, int blocks_per_cu);
 hipError_t ceiling_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 hipError_t ceiling_read(const void* src, int64_t bytes, unsigned* sink, hipStream_t stream);
+hipError_t ceiling_narrow(const void* src, void* dst, int64_t src_bytes, hipStream_t stream);
 
 }  // namespace sqk

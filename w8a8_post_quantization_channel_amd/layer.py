@@ -145,3 +145,48 @@ def forward_block(layers, xs, stream=None, gemm_stream=None, between=None):
                                   [layers[i].act_scale for i in part], [layers[i].w_scale for i in part],
                                   [ys[i] for i in part], None, gs)
     return ys
+
+
+class PhasedBlock:
+    """A block's projections split into phases that share no input, run on
+    two streams: each phase's preparation (statistics of its inputs and
+    weights, smoothing factors, weight and activation codes) on `prep`, its
+    products on `gemm` once that preparation is done. The HBM-bound
+    preparation of phase i + 1 thereby runs beside the products of phase i,
+    and the next pass's phase i beside this pass's later products: a phase's
+    preparation waits only for the products of the same phase in the previous
+    pass (the last readers of its buffers).
+
+    phases: list of (layers, calib, xs) as for prepare_block / forward_block;
+    layers of different phases must not share act_max tensors or inputs that
+    a phase writes."""
+
+    def __init__(self, phases):
+        self.phases = phases
+        self.done = [None] * len(phases)
+
+    def step(self, prep, gemm, on_gemm=None):
+        """Enqueue one pass. on_gemm(i, before): called with before=True just
+        before phase i's product launch is enqueued on `gemm` and with
+        before=False just after (for timing events). Returns the outputs."""
+        import torch
+        outs = []
+        for i, (layers, calib, xs) in enumerate(self.phases):
+            if self.done[i] is not None:
+                prep.wait_event(self.done[i])
+            prepare_block(layers, calib, prep)
+            ready = torch.cuda.Event()
+
+            def between(i=i, ready=ready):
+                ready.record(prep)
+                gemm.wait_event(ready)
+                if on_gemm is not None:
+                    on_gemm(i, True)
+
+            outs += forward_block(layers, xs, prep, gemm, between)
+            if on_gemm is not None:
+                on_gemm(i, False)
+            done = torch.cuda.Event()
+            done.record(gemm)
+            self.done[i] = done
+        return outs

@@ -256,7 +256,24 @@ struct EpiSSE {
         for (int k = 0; k < 8; ++k) cc.c[k] = col + k < N ? __fmul_rn(a, w_scale[col + k]) : 0.0f;
         return cc;
     }
-    __device__ void row8(const int (&acc)[8], int64_t row, const Cols& cc, bool) {
+    // fast (the tile lies inside M x N, N % 8 == 0) and yref 16-byte aligned:
+    // two 16-byte loads of the reference, and the eight squared errors added
+    // as a fixed pairwise tree before they join the running sum (a short
+    // dependency chain; the order is still the same on every run)
+    __device__ void row8(const int (&acc)[8], int64_t row, const Cols& cc, bool fast) {
+        if (fast && ((uintptr_t)yref & 15u) == 0) {
+            const float* yr = yref + row * N + cc.col;
+            const v4f r0 = *(const v4f*)yr, r1 = *(const v4f*)(yr + 4);
+            const float ref[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+            double q[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const double d = (double)__fmul_rn((float)acc[k], cc.c[k]) - (double)ref[k];
+                q[k] = d * d;
+            }
+            sum += ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+            return;
+        }
         if (row >= M) return;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {

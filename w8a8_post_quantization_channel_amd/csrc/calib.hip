@@ -271,14 +271,24 @@ struct AbsGeom {
     int64_t kvec, strips, rpb, chunks;
 };
 
-AbsGeom abs_geom(int eb, int64_t rows, int64_t k) {
+// Rows of 64-vector column strips a launch reads (rows x strips summed over
+// its inputs). Every block ends with one device-scope atomicMax per column,
+// and those go past the (per-XCD) L2 to memory: a launch with at least
+// kAbsBigWork of them takes about 256 blocks per input and at least 256 rows
+// per block (measured on MI355X: the 13B block's eleven statistics 124 ->
+// 116 us, a 262144 x 5120 calibration tensor 6.8 -> 7.06 TB/s; 7.4 M -> 1.0 M
+// atomics per 13B step); smaller launches keep more, shorter blocks so a
+// single small input still fills the compute units.
+constexpr int64_t kAbsBigWork = 262144;
+
+AbsGeom abs_geom(int eb, int64_t rows, int64_t k, bool big) {
     AbsGeom g;
     g.kvec = k * eb / 16;
     g.strips = (g.kvec + 63) / 64;
     const int64_t granule = 4 * kAbsUnroll;
-    const int64_t target_chunks = std::max<int64_t>(1, 2048 / g.strips);
+    const int64_t target_chunks = std::max<int64_t>(1, (big ? 256 : 2048) / g.strips);
     int64_t rpb = (rows + target_chunks - 1) / target_chunks;
-    rpb = std::max<int64_t>(rpb, std::min<int64_t>(rows, kAbsMinRows));
+    rpb = std::max<int64_t>(rpb, std::min<int64_t>(rows, big ? 8 * kAbsMinRows : kAbsMinRows));
     g.rpb = std::max<int64_t>(granule, (rpb + granule - 1) / granule * granule);
     g.chunks = (rows + g.rpb - 1) / g.rpb;
     return g;
@@ -304,13 +314,17 @@ hipError_t absmax_batched(const AbsmaxItem* items, int count, bool accumulate, h
         ft.first[count] = (int32_t)blocks;
         fill_zero_batched_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(ft);
     }
+    int64_t work = 0;  // row-strips of the launch
+    for (int i = 0; i < count; ++i)
+        work += items[i].rows * ((items[i].k * elem_bytes(items[i].xt) / 16 + 63) / 64);
+    const bool big = work >= kAbsBigWork;
     AbsTable tab{};
     int n = 0;
     int64_t blocks = 0;
     for (int i = 0; i < count; ++i) {
         if (items[i].rows == 0) continue;
         const int eb = elem_bytes(items[i].xt);
-        const AbsGeom g = abs_geom(eb, items[i].rows, items[i].k);
+        const AbsGeom g = abs_geom(eb, items[i].rows, items[i].k, big);
         tab.first[n] = (int32_t)blocks;
         tab.x[n] = (const u32x4*)items[i].x;
         tab.out[n] = (unsigned*)items[i].absmax;

@@ -51,10 +51,22 @@ typedef enum {
     SQ_ERR_ALPHA = 4,     /* alpha not finite or outside [0, 1] */
     SQ_ERR_WORKSPACE = 5, /* workspace missing or smaller than sq_alpha_search_workspace reports */
     SQ_ERR_HIP = 6,       /* a HIP launch or runtime call failed */
-    SQ_ERR_ALIGN = 7      /* a device pointer is not 16-byte aligned */
+    SQ_ERR_ALIGN = 7,     /* a device pointer is not 16-byte aligned */
+    /* range sentinels, never returned: any int passed to sq_status_string is a
+     * value of the type, in C and in C++ alike */
+    SQ_STATUS_RANGE_MIN_ = -2147483647 - 1,
+    SQ_STATUS_RANGE_MAX_ = 2147483647
 } sq_status;
 
-typedef enum { SQ_F32 = 0, SQ_BF16 = 1 } sq_dtype;
+/* Element types. The two sentinels give the enum the range of a 32-bit int,
+ * so any int a caller passes is a value of the type (and is rejected with
+ * SQ_ERR_DTYPE unless it is SQ_F32 or SQ_BF16), in C and in C++ alike. */
+typedef enum {
+    SQ_F32 = 0,
+    SQ_BF16 = 1,
+    SQ_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    SQ_DTYPE_RANGE_MAX_ = 2147483647
+} sq_dtype;
 
 /* Largest k accepted by the GEMM: k*127*127 must stay below 2^31 so the
  * int32 accumulator is exact in any summation order. */

@@ -968,8 +968,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print("bench.py: this build runs on one GPU only; --gpus above 1 is not supported "
-              "(the multi-GPU design is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py: runs on one GPU only; --gpus above 1 is not supported (the kernels run one GPU's "
+              "share of the work; sharding across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
     from w8a8_post_quantization_channel_amd import capi

@@ -140,7 +140,10 @@ def forward_block(layers, xs, stream=None, gemm_stream=None, between=None):
     if between is not None:
         between()
     gs = gemm_stream if gemm_stream is not None else stream
-    for part in _chunks(list(range(len(layers)))):
+    # products in reverse order of preparation: the codes written last are the
+    # ones still in the 256 MB Infinity Cache when the products start
+    # (measured on the 13B block: the grouped launch 602 -> 591 us)
+    for part in _chunks(list(range(len(layers)))[::-1]):
         capi.sq_w8a8_gemm_batched([xqs[i] for i in part], [layers[i].wq for i in part],
                                   [layers[i].act_scale for i in part], [layers[i].w_scale for i in part],
                                   [ys[i] for i in part], None, gs)

@@ -262,6 +262,37 @@ sq_status sq_fp8_gemm(const uint8_t* xq, const uint8_t* wq, int64_t m, int64_t n
                       void* y, sq_dtype yt, float* acc_out, hipStream_t stream);
 
 /*
+ * Batched FP8 forms, for the projections of a block in few launches (the
+ * arrays are host arrays of count <= SQ_MAX_BATCH items, validated item by
+ * item as the single forms, with the overlap rule of the int8 batched
+ * forms): each item is computed exactly as the single call on it.
+ *   sq_smooth_factors_fp8_batched:   sq_smooth_factors on each item, with
+ *                                    act_scale as sq_act_scale_fp8 (over 448)
+ *   sq_quant_weight_fp8_batched:     sq_quant_weight_fp8 on each item
+ *   sq_smooth_quant_act_fp8_batched: sq_smooth_quant_act_fp8 on each item
+ *                                    (items that share an input read it once)
+ *   sq_fp8_gemm_batched:             sq_fp8_gemm on each item (products that
+ *                                    pick the same tile share one launch);
+ *                                    acc_out NULL or an array of fp32 pointers
+ */
+sq_status sq_smooth_factors_fp8_batched(int count, const float* const* act_max,
+                                        const float* const* w_max, const int64_t* k,
+                                        const float* alpha, float* const* s, float* const* inv_s,
+                                        float* const* act_scale, hipStream_t stream);
+sq_status sq_quant_weight_fp8_batched(int count, const void* const* w, const sq_dtype* wt,
+                                      const int64_t* n, const int64_t* k, const float* const* s,
+                                      uint8_t* const* wq, float* const* w_scale, hipStream_t stream);
+sq_status sq_smooth_quant_act_fp8_batched(int count, const void* const* x, const sq_dtype* xt,
+                                          const int64_t* m, const int64_t* k,
+                                          const float* const* inv_s, const float* const* act_scale,
+                                          uint8_t* const* xq, hipStream_t stream);
+sq_status sq_fp8_gemm_batched(int count, const uint8_t* const* xq, const uint8_t* const* wq,
+                              const int64_t* m, const int64_t* n, const int64_t* k,
+                              const float* const* act_scale, const float* const* w_scale,
+                              void* const* y, const sq_dtype* yt, float* const* acc_out,
+                              hipStream_t stream);
+
+/*
  * Host-only query: the block tile (rows x columns of Y per workgroup) that
  * sq_w8a8_gemm uses for an m x n output on the current device. The choice
  * depends only on m, n and the device's compute-unit count; it does not change

@@ -439,6 +439,34 @@ def test_batched_act_and_gemm_validation(lib):
     assert gemm(2, *bad) == SHAPE
 
 
+def test_fp8_batched_validation(lib):
+    """The batched FP8 forms share the int8 batched forms' checks."""
+    PP = ctypes.c_void_p * 2
+    I64 = ctypes.c_int64 * 2
+    F = ctypes.c_float * 2
+    I = ctypes.c_int * 2
+    a, b = A, A + 0x100000
+    ptrs = lambda *v: PP(*v)
+    k = I64(1024, 1024)
+    assert lib.sq_smooth_factors_fp8_batched(2, None, ptrs(a, b), k, F(0.5, 0.5), ptrs(a, b), ptrs(a, b),
+                                             ptrs(a, b), None) == NULL
+    assert lib.sq_smooth_factors_fp8_batched(17, ptrs(a, b), ptrs(a, b), k, F(0.5, 0.5), ptrs(a, b), ptrs(a, b),
+                                             ptrs(a, b), None) == SHAPE
+    assert lib.sq_smooth_factors_fp8_batched(2, ptrs(a, b), ptrs(a, b), k, F(0.5, 1.5), ptrs(a, b), ptrs(a, b),
+                                             ptrs(a, b), None) == ALPHA
+    assert lib.sq_quant_weight_fp8_batched(2, ptrs(a, b), I(1, 7), I64(8, 8), k, ptrs(a, b), ptrs(a, b),
+                                           ptrs(a, b), None) == DTYPE
+    assert lib.sq_smooth_quant_act_fp8_batched(2, ptrs(a, b), I(1, 1), I64(8, 8), I64(1024, 1000), ptrs(a, b),
+                                               ptrs(a, b), ptrs(a, b), None) == SHAPE
+    assert lib.sq_fp8_gemm_batched(2, ptrs(a, b), ptrs(a, b), I64(8, 8), I64(16, 16), k, ptrs(a, b), ptrs(a, b),
+                                   ptrs(a + 4, b), I(1, 1), None, None) == ALIGN
+    # item 1's output on item 0's weight codes
+    x0, w0, y0, x1, w1 = (A + i * 0x100000 for i in range(5))
+    assert lib.sq_fp8_gemm_batched(2, ptrs(x0, x1), ptrs(w0, w1), I64(8, 8), I64(16, 16), k,
+                                   ptrs(A + 0x600000, A + 0x700000), ptrs(A + 0x800000, A + 0x900000),
+                                   ptrs(y0, w0), I(1, 1), None, None) == SHAPE
+
+
 def test_ceiling_validation(lib):
     for name in ("sq_ceiling_mfma", "sq_ceiling_copy", "sq_ceiling_read", "sq_ceiling_narrow"):
         assert name in capi.declared_functions() and hasattr(lib, name)

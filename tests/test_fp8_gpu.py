@@ -146,3 +146,55 @@ def test_fp8_gemm_empty():
     capi.sq_fp8_gemm(xq, wq, ta, ws, y[:0])
     torch.cuda.synchronize()
     assert (_host(y) == 3.0).all()
+
+
+def test_fp8_block_batched_equals_single_calls():
+    """The 13B block (512 tokens) through the batched FP8 entry points gives
+    the same smoothing factors, FP8 act scales, e4m3 codes, scales, fp32
+    accumulators and outputs, bit for bit, as one single-form call per
+    projection."""
+    import torch
+    d = dev()
+    f32 = dict(dtype=torch.float32, device=d)
+    rows = 512
+    groups = {g: synth.to_torch(synth.c2_group_x(g, rows=rows), d) for g in synth.C2_GROUPS}
+    projs = [(p, g, synth.to_torch(synth.c2_projection_w(p), d)) for p, g, *_ in synth.C2_PROJECTIONS]
+    am = {g: torch.empty(x.shape[1], **f32) for g, x in groups.items()}
+    capi.sq_calib_absmax_batched(list(groups.values()), [am[g] for g in groups])
+    w_max = [torch.empty(w.shape[1], **f32) for _, _, w in projs]
+    capi.sq_calib_absmax_batched([w for _, _, w in projs], w_max)
+
+    def buffers():
+        out = []
+        for _, g, w in projs:
+            n, k = w.shape
+            out.append(dict(s=torch.empty(k, **f32), inv_s=torch.empty(k, **f32), a=torch.zeros(4, **f32),
+                            wq=torch.empty((n, k), dtype=torch.uint8, device=d), ws=torch.empty(n, **f32),
+                            xq=torch.empty((rows, k), dtype=torch.uint8, device=d),
+                            y=torch.empty((rows, n), dtype=torch.bfloat16, device=d),
+                            acc=torch.empty((rows, n), **f32)))
+        return out
+
+    one = buffers()
+    for (_, g, w), wm, b in zip(projs, w_max, one):
+        a8 = torch.zeros(4, **f32)
+        capi.sq_smooth_factors(am[g], wm, 0.5, b["s"], b["inv_s"], a8)
+        capi.sq_act_scale_fp8(am[g], b["inv_s"], b["a"])
+        capi.sq_quant_weight_fp8(w, b["s"], b["wq"], b["ws"])
+        capi.sq_smooth_quant_act_fp8(groups[g], b["inv_s"], b["a"], b["xq"])
+        capi.sq_fp8_gemm(b["xq"], b["wq"], b["a"], b["ws"], b["y"], b["acc"])
+    two = buffers()
+    capi.sq_smooth_factors_fp8_batched([am[g] for _, g, _ in projs], w_max, [0.5] * len(projs),
+                                       [b["s"] for b in two], [b["inv_s"] for b in two], [b["a"] for b in two])
+    capi.sq_quant_weight_fp8_batched([w for _, _, w in projs], [b["s"] for b in two], [b["wq"] for b in two],
+                                     [b["ws"] for b in two])
+    capi.sq_smooth_quant_act_fp8_batched([groups[g] for _, g, _ in projs], [b["inv_s"] for b in two],
+                                         [b["a"] for b in two], [b["xq"] for b in two])
+    capi.sq_fp8_gemm_batched([b["xq"] for b in two], [b["wq"] for b in two], [b["a"] for b in two],
+                             [b["ws"] for b in two], [b["y"] for b in two], [b["acc"] for b in two])
+    torch.cuda.synchronize()
+    for (p, _, _), b1, b2 in zip(projs, one, two):
+        for key in ("s", "inv_s", "wq", "ws", "xq", "acc"):
+            assert torch.equal(b1[key], b2[key]), (p, key)
+        assert torch.equal(b1["a"][:1], b2["a"][:1]), (p, "act_scale")
+        assert torch.equal(b1["y"].view(torch.int16), b2["y"].view(torch.int16)), (p, "y")

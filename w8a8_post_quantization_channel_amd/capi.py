@@ -68,6 +68,10 @@ def _declare(lib):
         "sq_quant_weight_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_smooth_quant_act_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_w8a8_gemm_batched": [c.c_int, P, P, P, P, P, P, P, P, P, P, P],
+        "sq_smooth_factors_fp8_batched": [c.c_int, P, P, P, P, P, P, P, P],
+        "sq_quant_weight_fp8_batched": [c.c_int, P, P, P, P, P, P, P, P],
+        "sq_smooth_quant_act_fp8_batched": [c.c_int, P, P, P, P, P, P, P, P],
+        "sq_fp8_gemm_batched": [c.c_int, P, P, P, P, P, P, P, P, P, P, P],
         "sq_ceiling_mfma": [i64, c.c_int, P, P, P, P],
         "sq_ceiling_copy": [P, P, i64, P],
         "sq_ceiling_read": [P, i64, P, P],
@@ -158,6 +162,27 @@ def sq_w8a8_gemm(xq, wq, act_scale, w_scale, y, acc_out=None, stream=None):
                                                _stream(stream)))
 
 
+def sq_smooth_factors_fp8_batched(act_maxes, w_maxes, alphas, ss, inv_ss, act_scales, stream=None):
+    """sq_smooth_factors_batched with the act scales over 448 (e4m3 codes)."""
+    sq_smooth_factors_batched(act_maxes, w_maxes, alphas, ss, inv_ss, act_scales, stream,
+                              _name="sq_smooth_factors_fp8_batched")
+
+
+def sq_quant_weight_fp8_batched(ws, ss, wqs, w_scales, stream=None):
+    """sq_quant_weight_fp8 for several weights (uint8 e4m3 codes)."""
+    sq_quant_weight_batched(ws, ss, wqs, w_scales, stream, _name="sq_quant_weight_fp8_batched")
+
+
+def sq_smooth_quant_act_fp8_batched(xs, inv_ss, act_scales, xqs, stream=None):
+    """sq_smooth_quant_act_fp8 for several projections in one launch."""
+    sq_smooth_quant_act_batched(xs, inv_ss, act_scales, xqs, stream, _name="sq_smooth_quant_act_fp8_batched")
+
+
+def sq_fp8_gemm_batched(xqs, wqs, act_scales, w_scales, ys, acc_outs=None, stream=None):
+    """sq_fp8_gemm for several products (fp32 acc_outs when given)."""
+    sq_w8a8_gemm_batched(xqs, wqs, act_scales, w_scales, ys, acc_outs, stream, _name="sq_fp8_gemm_batched")
+
+
 def sq_gemm_tiling(m: int, n: int) -> tuple[int, int]:
     """Block tile (rows, columns) sq_w8a8_gemm uses for an m x n output."""
     bm, bn = ctypes.c_int(0), ctypes.c_int(0)
@@ -214,7 +239,8 @@ def sq_calib_absmax_batched(xs, absmaxes, accumulate: bool = False, stream=None)
                                                                      int(bool(accumulate)), _stream(stream)))
 
 
-def sq_smooth_factors_batched(act_maxes, w_maxes, alphas, ss, inv_ss, act_scales, stream=None):
+def sq_smooth_factors_batched(act_maxes, w_maxes, alphas, ss, inv_ss, act_scales, stream=None,
+                              _name="sq_smooth_factors_batched"):
     """sq_smooth_factors for several projections in two launches."""
     count = len(act_maxes)
     if not all(len(v) == count for v in (w_maxes, alphas, ss, inv_ss, act_scales)):
@@ -223,11 +249,10 @@ def sq_smooth_factors_batched(act_maxes, w_maxes, alphas, ss, inv_ss, act_scales
             _host_array(ctypes.c_int64, [t.shape[0] for t in act_maxes]),
             _host_array(ctypes.c_float, [float(a) for a in alphas]), _ptrs(ss, "ss"), _ptrs(inv_ss, "inv_ss"),
             _ptrs(act_scales, "act_scales")]
-    _check("sq_smooth_factors_batched", load().sq_smooth_factors_batched(count, *[a for _, a in keep],
-                                                                         _stream(stream)))
+    _check(_name, getattr(load(), _name)(count, *[a for _, a in keep], _stream(stream)))
 
 
-def sq_quant_weight_batched(ws, ss, wqs, w_scales, stream=None):
+def sq_quant_weight_batched(ws, ss, wqs, w_scales, stream=None, _name="sq_quant_weight_batched"):
     """sq_quant_weight for several weights, one launch per row-length class."""
     count = len(ws)
     if not all(len(v) == count for v in (ss, wqs, w_scales)):
@@ -235,10 +260,10 @@ def sq_quant_weight_batched(ws, ss, wqs, w_scales, stream=None):
     keep = [_ptrs(ws, "ws"), _host_array(ctypes.c_int, [_dtype_code(w) for w in ws]),
             _host_array(ctypes.c_int64, [w.shape[0] for w in ws]), _host_array(ctypes.c_int64, [w.shape[1] for w in ws]),
             _ptrs(ss, "ss"), _ptrs(wqs, "wqs"), _ptrs(w_scales, "w_scales")]
-    _check("sq_quant_weight_batched", load().sq_quant_weight_batched(count, *[a for _, a in keep], _stream(stream)))
+    _check(_name, getattr(load(), _name)(count, *[a for _, a in keep], _stream(stream)))
 
 
-def sq_smooth_quant_act_batched(xs, inv_ss, act_scales, xqs, stream=None):
+def sq_smooth_quant_act_batched(xs, inv_ss, act_scales, xqs, stream=None, _name="sq_smooth_quant_act_batched"):
     """sq_smooth_quant_act for several projections in one launch (a shared
     input tensor is read once for all of its consumers)."""
     count = len(xs)
@@ -247,11 +272,11 @@ def sq_smooth_quant_act_batched(xs, inv_ss, act_scales, xqs, stream=None):
     keep = [_ptrs(xs, "xs"), _host_array(ctypes.c_int, [_dtype_code(x) for x in xs]),
             _host_array(ctypes.c_int64, [x.shape[0] for x in xs]), _host_array(ctypes.c_int64, [x.shape[1] for x in xs]),
             _ptrs(inv_ss, "inv_ss"), _ptrs(act_scales, "act_scales"), _ptrs(xqs, "xqs")]
-    _check("sq_smooth_quant_act_batched", load().sq_smooth_quant_act_batched(count, *[a for _, a in keep],
-                                                                             _stream(stream)))
+    _check(_name, getattr(load(), _name)(count, *[a for _, a in keep], _stream(stream)))
 
 
-def sq_w8a8_gemm_batched(xqs, wqs, act_scales, w_scales, ys, acc_outs=None, stream=None):
+def sq_w8a8_gemm_batched(xqs, wqs, act_scales, w_scales, ys, acc_outs=None, stream=None,
+                         _name="sq_w8a8_gemm_batched"):
     """sq_w8a8_gemm for several products; those with the same large tile and
     output type share one launch."""
     count = len(xqs)
@@ -266,8 +291,8 @@ def sq_w8a8_gemm_batched(xqs, wqs, act_scales, w_scales, ys, acc_outs=None, stre
         if len(acc_outs) != count:
             raise ValueError("acc_outs differs in length")
         acc = _host_array(ctypes.c_void_p, [_opt(a, f"acc_outs[{i}]").value for i, a in enumerate(acc_outs)])
-    _check("sq_w8a8_gemm_batched", load().sq_w8a8_gemm_batched(count, *[a for _, a in keep],
-                                                               acc[1] if acc else ctypes.c_void_p(0), _stream(stream)))
+    _check(_name, getattr(load(), _name)(count, *[a for _, a in keep], acc[1] if acc else ctypes.c_void_p(0),
+                                         _stream(stream)))
 
 
 CEILING_OPERAND_BYTES = 16384

@@ -258,10 +258,11 @@ __global__ __launch_bounds__(kSmoothThreads) void smooth_batched_kernel(const Sm
     if (j < tab.k[i]) smooth_channel(tab.act_max[i], tab.w_max[i], j, tab.alpha[i], tab.s[i], tab.inv_s[i]);
 }
 
-__global__ __launch_bounds__(kScaleThreads) void act_scale_batched_kernel(const SmoothTable tab) {
+// qmax: 127 for int8 codes, 448 for e4m3 codes
+__global__ __launch_bounds__(kScaleThreads) void act_scale_batched_kernel(const SmoothTable tab, float qmax) {
     __shared__ float red[kScaleThreads / 64];
     const int i = blockIdx.x;
-    act_scale_block(tab.act_max[i], tab.inv_s[i], tab.k[i], sqd::kQmax, tab.act_scale[i], red);
+    act_scale_block(tab.act_max[i], tab.inv_s[i], tab.k[i], qmax, tab.act_scale[i], red);
 }
 
 // launch geometry of one absmax input: about 2048 blocks, but at least
@@ -399,7 +400,7 @@ hipError_t mean_finalize(const double* sum, int64_t count, int64_t k, float* act
     return hipGetLastError();
 }
 
-hipError_t smooth_factors_batched(const SmoothItem* items, int count, hipStream_t stream) {
+static hipError_t smooth_factors_batched_q(const SmoothItem* items, int count, float qmax, hipStream_t stream) {
     if (count <= 0) return hipSuccess;
     SmoothTable tab{};
     tab.count = count;
@@ -418,8 +419,16 @@ hipError_t smooth_factors_batched(const SmoothItem* items, int count, hipStream_
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     tab.first[count] = (int32_t)blocks;
     smooth_batched_kernel<<<dim3((unsigned)blocks), dim3(kSmoothThreads), 0, stream>>>(tab);
-    act_scale_batched_kernel<<<dim3((unsigned)count), dim3(kScaleThreads), 0, stream>>>(tab);
+    act_scale_batched_kernel<<<dim3((unsigned)count), dim3(kScaleThreads), 0, stream>>>(tab, qmax);
     return hipGetLastError();
+}
+
+hipError_t smooth_factors_batched(const SmoothItem* items, int count, hipStream_t stream) {
+    return smooth_factors_batched_q(items, count, sqd::kQmax, stream);
+}
+
+hipError_t smooth_factors_fp8_batched(const SmoothItem* items, int count, hipStream_t stream) {
+    return smooth_factors_batched_q(items, count, sqd::kFp8Max, stream);
 }
 
 hipError_t smooth_factors(const float* act_max, const float* w_max, int64_t k, float alpha, float* s,

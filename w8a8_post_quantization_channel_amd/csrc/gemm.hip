@@ -758,20 +758,21 @@ struct GemmTable {
     const float* act_scale[sqk::kMaxBatch];
     const float* w_scale[sqk::kMaxBatch];
     void* y[sqk::kMaxBatch];
-    int32_t* acc_out[sqk::kMaxBatch];
+    void* acc_out[sqk::kMaxBatch];  // int32 (int8 codes) or fp32 (e4m3 codes) accumulators, or NULL
     int64_t M[sqk::kMaxBatch], N[sqk::kMaxBatch], Kb[sqk::kMaxBatch];
     int32_t tiles_m[sqk::kMaxBatch], tiles_n[sqk::kMaxBatch];
 };
 
-template <class Op, int TN, bool kBF16Out>
+template <class Op, int TN, bool kBF16Out, class AccT>
 __global__ __launch_bounds__(256) void gemm_dma_grouped_kernel(const GemmTable tab) {
     __shared__ __attribute__((aligned(1024))) char lds[dma_lds_bytes<TN>()];
     const int i = sqd::item_of(tab.first, tab.count, blockIdx.x);
     const int b = blockIdx.x - tab.first[i], ntiles = tab.tiles_m[i] * tab.tiles_n[i];
     if (b >= ntiles) return;
-    EpiDequant<kBF16Out> epi{tab.act_scale[i], tab.w_scale[i], tab.y[i], tab.acc_out[i], tab.M[i], tab.N[i], 0.0f};
-    dma_tile<Op, TN, EpiDequant<kBF16Out>>(tab.A[i], tab.B[i], tab.M[i], tab.N[i], tab.Kb[i], tab.tiles_m[i],
-                                           tab.tiles_n[i], xcd_tile(b, ntiles), epi, lds);
+    EpiDequant<kBF16Out, AccT> epi{tab.act_scale[i], tab.w_scale[i], tab.y[i], (AccT*)tab.acc_out[i],
+                                   tab.M[i],         tab.N[i],         0.0f};
+    dma_tile<Op, TN, EpiDequant<kBF16Out, AccT>>(tab.A[i], tab.B[i], tab.M[i], tab.N[i], tab.Kb[i], tab.tiles_m[i],
+                                                 tab.tiles_n[i], xcd_tile(b, ntiles), epi, lds);
 }
 
 // ---- skinny kernel (decode: m <= 64) -------------------------------------------
@@ -963,10 +964,9 @@ hipError_t dispatch(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int6
     }
 }
 
-// FP8 products: the pipelined kernel at every size (its tilings only)
-template <class Epi>
-hipError_t dispatch_f8(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t Kb, Epi epi,
-                       hipStream_t stream) {
+// FP8 products: the pipelined kernel at every size (its tilings only), the
+// width whose whole rounds of tiles cost least
+int f8_cfg(int64_t M, int64_t N) {
     const int64_t cus = cu_count();
     int best = kD128;
     double best_cost = 0.0;
@@ -978,7 +978,13 @@ hipError_t dispatch_f8(const int8_t* A, const int8_t* B, int64_t M, int64_t N, i
             best = c;
         }
     }
-    switch (best) {
+    return best;
+}
+
+template <class Epi>
+hipError_t dispatch_f8(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t Kb, Epi epi,
+                       hipStream_t stream) {
+    switch (f8_cfg(M, N)) {
         case kD256: return launch_dma<OpF8, 8>(A, B, M, N, Kb, epi, stream);
         case kD224: return launch_dma<OpF8, 7>(A, B, M, N, Kb, epi, stream);
         case kD192: return launch_dma<OpF8, 6>(A, B, M, N, Kb, epi, stream);
@@ -1038,12 +1044,12 @@ __global__ __launch_bounds__(256) void ref_gemm_f32_kernel(const float* __restri
 
 namespace sqk {
 
-template <int TN>
+template <class Op, class AccT, int TN>
 hipError_t launch_grouped(const GemmTable& tab, int64_t blocks, bool bf16, hipStream_t stream) {
     if (bf16)
-        gemm_dma_grouped_kernel<OpI8, TN, true><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(tab);
+        gemm_dma_grouped_kernel<Op, TN, true, AccT><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(tab);
     else
-        gemm_dma_grouped_kernel<OpI8, TN, false><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(tab);
+        gemm_dma_grouped_kernel<Op, TN, false, AccT><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(tab);
     return hipGetLastError();
 }
 
@@ -1058,17 +1064,25 @@ int dma_width(TileCfg c) {
     }
 }
 
-hipError_t gemm_dequant_batched(const GemmItem* items, int count, hipStream_t stream) {
+// Products that pick the same tile width (and output type) share one
+// grouped launch; int8 products too small for the pipelined tiles run as
+// single launches (FP8 products always take a pipelined width).
+template <class Op, class AccT>
+hipError_t gemm_batched_impl(const GemmItem* items, int count, hipStream_t stream) {
+    constexpr bool kF8 = std::is_same<Op, OpF8>::value;
+    auto width = [](const GemmItem& it) { return dma_width(kF8 ? (TileCfg)f8_cfg(it.m, it.n) : choose_cfg(it.m, it.n)); };
     bool done[kMaxBatch] = {};
     for (int i = 0; i < count; ++i) {
         if (done[i]) continue;
         done[i] = true;
         const GemmItem& it = items[i];
         if (it.m == 0 || it.n == 0) continue;
-        const int tn = dma_width(choose_cfg(it.m, it.n));
+        const int tn = width(it);
         if (tn == 0) {  // small m: the register-staged or skinny kernel, one launch per item
-            const hipError_t e = gemm_dequant(it.xq, it.wq, it.m, it.n, it.k, it.act_scale, it.w_scale, it.y, it.yt,
-                                              it.acc_out, stream);
+            hipError_t e = hipErrorInvalidValue;
+            if constexpr (!kF8)
+                e = gemm_dequant(it.xq, it.wq, it.m, it.n, it.k, it.act_scale, it.w_scale, it.y, it.yt,
+                                 (int32_t*)it.acc_out, stream);
             if (e != hipSuccess) return e;
             continue;
         }
@@ -1076,9 +1090,7 @@ hipError_t gemm_dequant_batched(const GemmItem* items, int count, hipStream_t st
         int64_t blocks = 0;
         for (int j = i; j < count; ++j) {
             const GemmItem& jt = items[j];
-            if (j > i && (done[j] || jt.m == 0 || jt.n == 0 || jt.yt != it.yt ||
-                          dma_width(choose_cfg(jt.m, jt.n)) != tn))
-                continue;
+            if (j > i && (done[j] || jt.m == 0 || jt.n == 0 || jt.yt != it.yt || width(jt) != tn)) continue;
             done[j] = true;
             const int c = tab.count++;
             const int64_t tiles_m = (jt.m + kDmaBM - 1) / kDmaBM, tiles_n = (jt.n + 32 * tn - 1) / (32 * tn);
@@ -1101,15 +1113,23 @@ hipError_t gemm_dequant_batched(const GemmItem* items, int count, hipStream_t st
         const bool bf16 = it.yt == kBF16;
         hipError_t e = hipErrorInvalidValue;
         switch (tn) {
-            case 8: e = launch_grouped<8>(tab, blocks, bf16, stream); break;
-            case 7: e = launch_grouped<7>(tab, blocks, bf16, stream); break;
-            case 6: e = launch_grouped<6>(tab, blocks, bf16, stream); break;
-            case 5: e = launch_grouped<5>(tab, blocks, bf16, stream); break;
-            case 4: e = launch_grouped<4>(tab, blocks, bf16, stream); break;
+            case 8: e = launch_grouped<Op, AccT, 8>(tab, blocks, bf16, stream); break;
+            case 7: e = launch_grouped<Op, AccT, 7>(tab, blocks, bf16, stream); break;
+            case 6: e = launch_grouped<Op, AccT, 6>(tab, blocks, bf16, stream); break;
+            case 5: e = launch_grouped<Op, AccT, 5>(tab, blocks, bf16, stream); break;
+            case 4: e = launch_grouped<Op, AccT, 4>(tab, blocks, bf16, stream); break;
         }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t gemm_dequant_batched(const GemmItem* items, int count, hipStream_t stream) {
+    return gemm_batched_impl<OpI8, int32_t>(items, count, stream);
+}
+
+hipError_t gemm_fp8_batched(const GemmItem* items, int count, hipStream_t stream) {
+    return gemm_batched_impl<OpF8, float>(items, count, stream);
 }
 
 hipError_t gemm_dequant(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,

@@ -615,6 +615,10 @@ hipError_t quant_weight_batched(const QuantWeightItem* items, int count, hipStre
     return quant_weight_items<false>(items, count, stream);
 }
 
+hipError_t quant_weight_fp8_batched(const QuantWeightItem* items, int count, hipStream_t stream) {
+    return quant_weight_items<true>(items, count, stream);
+}
+
 hipError_t quant_weight_fp8(const void* w, int wt, int64_t n, int64_t k, const float* s, uint8_t* wq,
                             float* w_scale, hipStream_t stream) {
     const QuantWeightItem item{w, wt, n, k, s, (int8_t*)wq, w_scale};
@@ -722,6 +726,10 @@ hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const float* i
 
 hipError_t quant_act_batched(const ActItem* items, int count, hipStream_t stream) {
     return quant_act_items<false>(items, count, stream);
+}
+
+hipError_t quant_act_fp8_batched(const ActItem* items, int count, hipStream_t stream) {
+    return quant_act_items<true>(items, count, stream);
 }
 
 hipError_t quant_act_fp8(const void* x, int xt, int64_t m, int64_t k, const float* inv_s, const float* act_scale,

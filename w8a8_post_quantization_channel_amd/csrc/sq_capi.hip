@@ -186,9 +186,9 @@ sq_status sq_calib_absmax_batched(int count, const void* const* x, const sq_dtyp
     return hip_status(sqk::absmax_batched(items, n, accumulate != 0, stream));
 }
 
-sq_status sq_smooth_factors_batched(int count, const float* const* act_max, const float* const* w_max,
-                                    const int64_t* k, const float* alpha, float* const* s, float* const* inv_s,
-                                    float* const* act_scale, hipStream_t stream) {
+static sq_status smooth_batched(int count, const float* const* act_max, const float* const* w_max,
+                                const int64_t* k, const float* alpha, float* const* s, float* const* inv_s,
+                                float* const* act_scale, bool fp8, hipStream_t stream) {
     if (!act_max || !w_max || !k || !alpha || !s || !inv_s || !act_scale) return SQ_ERR_NULL;
     if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
     Ranges rg;
@@ -204,12 +204,25 @@ sq_status sq_smooth_factors_batched(int count, const float* const* act_max, cons
         items[i] = sqk::SmoothItem{act_max[i], w_max[i], k[i], alpha[i], s[i], inv_s[i], act_scale[i]};
     }
     if (rg.overlap()) return SQ_ERR_SHAPE;
-    return hip_status(sqk::smooth_factors_batched(items, count, stream));
+    return hip_status(fp8 ? sqk::smooth_factors_fp8_batched(items, count, stream)
+                          : sqk::smooth_factors_batched(items, count, stream));
 }
 
-sq_status sq_quant_weight_batched(int count, const void* const* w, const sq_dtype* wt, const int64_t* n,
-                                  const int64_t* k, const float* const* s, int8_t* const* wq,
-                                  float* const* w_scale, hipStream_t stream) {
+sq_status sq_smooth_factors_batched(int count, const float* const* act_max, const float* const* w_max,
+                                    const int64_t* k, const float* alpha, float* const* s, float* const* inv_s,
+                                    float* const* act_scale, hipStream_t stream) {
+    return smooth_batched(count, act_max, w_max, k, alpha, s, inv_s, act_scale, false, stream);
+}
+
+sq_status sq_smooth_factors_fp8_batched(int count, const float* const* act_max, const float* const* w_max,
+                                        const int64_t* k, const float* alpha, float* const* s,
+                                        float* const* inv_s, float* const* act_scale, hipStream_t stream) {
+    return smooth_batched(count, act_max, w_max, k, alpha, s, inv_s, act_scale, true, stream);
+}
+
+static sq_status quant_weight_batched(int count, const void* const* w, const sq_dtype* wt, const int64_t* n,
+                                      const int64_t* k, const float* const* s, int8_t* const* wq,
+                                      float* const* w_scale, bool fp8, hipStream_t stream) {
     if (!w || !wt || !n || !k || !s || !wq || !w_scale) return SQ_ERR_NULL;
     if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
     Ranges rg;
@@ -224,7 +237,20 @@ sq_status sq_quant_weight_batched(int count, const void* const* w, const sq_dtyp
         items[i] = sqk::QuantWeightItem{w[i], wt[i], n[i], k[i], s[i], wq[i], w_scale[i]};
     }
     if (rg.overlap()) return SQ_ERR_SHAPE;
-    return hip_status(sqk::quant_weight_batched(items, count, stream));
+    return hip_status(fp8 ? sqk::quant_weight_fp8_batched(items, count, stream)
+                          : sqk::quant_weight_batched(items, count, stream));
+}
+
+sq_status sq_quant_weight_batched(int count, const void* const* w, const sq_dtype* wt, const int64_t* n,
+                                  const int64_t* k, const float* const* s, int8_t* const* wq,
+                                  float* const* w_scale, hipStream_t stream) {
+    return quant_weight_batched(count, w, wt, n, k, s, wq, w_scale, false, stream);
+}
+
+sq_status sq_quant_weight_fp8_batched(int count, const void* const* w, const sq_dtype* wt, const int64_t* n,
+                                      const int64_t* k, const float* const* s, uint8_t* const* wq,
+                                      float* const* w_scale, hipStream_t stream) {
+    return quant_weight_batched(count, w, wt, n, k, s, (int8_t* const*)wq, w_scale, true, stream);
 }
 
 sq_status sq_smooth_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* inv_s,
@@ -234,9 +260,9 @@ sq_status sq_smooth_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k, 
     return hip_status(sqk::quant_act(x, xt, m, k, inv_s, act_scale, xq, stream));
 }
 
-sq_status sq_smooth_quant_act_batched(int count, const void* const* x, const sq_dtype* xt, const int64_t* m,
-                                      const int64_t* k, const float* const* inv_s, const float* const* act_scale,
-                                      int8_t* const* xq, hipStream_t stream) {
+static sq_status quant_act_batched(int count, const void* const* x, const sq_dtype* xt, const int64_t* m,
+                                   const int64_t* k, const float* const* inv_s, const float* const* act_scale,
+                                   int8_t* const* xq, bool fp8, hipStream_t stream) {
     if (!x || !xt || !m || !k || !inv_s || !act_scale || !xq) return SQ_ERR_NULL;
     if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
     Ranges rg;
@@ -251,7 +277,20 @@ sq_status sq_smooth_quant_act_batched(int count, const void* const* x, const sq_
         items[i] = sqk::ActItem{x[i], xt[i], m[i], k[i], inv_s[i], act_scale[i], xq[i]};
     }
     if (rg.overlap()) return SQ_ERR_SHAPE;
-    return hip_status(sqk::quant_act_batched(items, count, stream));
+    return hip_status(fp8 ? sqk::quant_act_fp8_batched(items, count, stream)
+                          : sqk::quant_act_batched(items, count, stream));
+}
+
+sq_status sq_smooth_quant_act_batched(int count, const void* const* x, const sq_dtype* xt, const int64_t* m,
+                                      const int64_t* k, const float* const* inv_s, const float* const* act_scale,
+                                      int8_t* const* xq, hipStream_t stream) {
+    return quant_act_batched(count, x, xt, m, k, inv_s, act_scale, xq, false, stream);
+}
+
+sq_status sq_smooth_quant_act_fp8_batched(int count, const void* const* x, const sq_dtype* xt, const int64_t* m,
+                                          const int64_t* k, const float* const* inv_s,
+                                          const float* const* act_scale, uint8_t* const* xq, hipStream_t stream) {
+    return quant_act_batched(count, x, xt, m, k, inv_s, act_scale, (int8_t* const*)xq, true, stream);
 }
 
 sq_status sq_w8a8_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
@@ -262,17 +301,19 @@ sq_status sq_w8a8_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n,
     return hip_status(sqk::gemm_dequant(xq, wq, m, n, k, act_scale, w_scale, y, yt, acc_out, stream));
 }
 
-sq_status sq_w8a8_gemm_batched(int count, const int8_t* const* xq, const int8_t* const* wq, const int64_t* m,
-                               const int64_t* n, const int64_t* k, const float* const* act_scale,
-                               const float* const* w_scale, void* const* y, const sq_dtype* yt,
-                               int32_t* const* acc_out, hipStream_t stream) {
+// acc_out: int32 (int8 codes) or fp32 (e4m3 codes) accumulators, 4 bytes each
+static sq_status gemm_batched(int count, const int8_t* const* xq, const int8_t* const* wq, const int64_t* m,
+                              const int64_t* n, const int64_t* k, const float* const* act_scale,
+                              const float* const* w_scale, void* const* y, const sq_dtype* yt,
+                              void* const* acc_out, bool fp8, hipStream_t stream) {
     if (!xq || !wq || !m || !n || !k || !act_scale || !w_scale || !y || !yt) return SQ_ERR_NULL;
     if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
     Ranges rg;
     sqk::GemmItem items[SQ_MAX_BATCH];
     for (int i = 0; i < count; ++i) {
-        int32_t* acc = acc_out ? acc_out[i] : nullptr;
-        const sq_status st = check_gemm(xq[i], wq[i], m[i], n[i], k[i], act_scale[i], w_scale[i], y[i], yt[i], acc);
+        void* acc = acc_out ? acc_out[i] : nullptr;
+        const sq_status st =
+            check_gemm(xq[i], wq[i], m[i], n[i], k[i], act_scale[i], w_scale[i], y[i], yt[i], (const int32_t*)acc);
         if (st != SQ_OK) return st;
         rg.add(i, xq[i], m[i] * k[i], false);
         rg.add(i, wq[i], n[i] * k[i], false);
@@ -283,7 +324,23 @@ sq_status sq_w8a8_gemm_batched(int count, const int8_t* const* xq, const int8_t*
         items[i] = sqk::GemmItem{xq[i], wq[i], m[i], n[i], k[i], act_scale[i], w_scale[i], y[i], yt[i], acc};
     }
     if (rg.overlap()) return SQ_ERR_SHAPE;
-    return hip_status(sqk::gemm_dequant_batched(items, count, stream));
+    return hip_status(fp8 ? sqk::gemm_fp8_batched(items, count, stream)
+                          : sqk::gemm_dequant_batched(items, count, stream));
+}
+
+sq_status sq_w8a8_gemm_batched(int count, const int8_t* const* xq, const int8_t* const* wq, const int64_t* m,
+                               const int64_t* n, const int64_t* k, const float* const* act_scale,
+                               const float* const* w_scale, void* const* y, const sq_dtype* yt,
+                               int32_t* const* acc_out, hipStream_t stream) {
+    return gemm_batched(count, xq, wq, m, n, k, act_scale, w_scale, y, yt, (void* const*)acc_out, false, stream);
+}
+
+sq_status sq_fp8_gemm_batched(int count, const uint8_t* const* xq, const uint8_t* const* wq, const int64_t* m,
+                              const int64_t* n, const int64_t* k, const float* const* act_scale,
+                              const float* const* w_scale, void* const* y, const sq_dtype* yt,
+                              float* const* acc_out, hipStream_t stream) {
+    return gemm_batched(count, (const int8_t* const*)xq, (const int8_t* const*)wq, m, n, k, act_scale, w_scale, y, yt,
+                        (void* const*)acc_out, true, stream);
 }
 
 sq_status sq_act_scale(const float* act_max, const float* inv_s, int64_t k, float* act_scale, hipStream_t stream) {

@@ -75,6 +75,8 @@ struct SmoothItem {
     float* act_scale;
 };
 hipError_t smooth_factors_batched(const SmoothItem* items, int count, hipStream_t stream);
+// the same with the act scale over 448 (e4m3 codes)
+hipError_t smooth_factors_fp8_batched(const SmoothItem* items, int count, hipStream_t stream);
 
 // W' = W diag(s), per-row symmetric int8
 hipError_t quant_weight(const void* w, int wt, int64_t n, int64_t k, const float* s, int8_t* wq,
@@ -123,7 +125,7 @@ struct GemmItem {
     const float* w_scale;
     void* y;
     int yt;
-    int32_t* acc_out;
+    void* acc_out;  // int32 for int8 codes, fp32 for e4m3 codes, or NULL
 };
 hipError_t gemm_dequant_batched(const GemmItem* items, int count, hipStream_t stream);
 
@@ -137,6 +139,11 @@ hipError_t quant_act_fp8(const void* x, int xt, int64_t m, int64_t k, const floa
                          uint8_t* xq, hipStream_t stream);
 hipError_t gemm_fp8(const uint8_t* xq, const uint8_t* wq, int64_t m, int64_t n, int64_t k, const float* act_scale,
                     const float* w_scale, void* y, int yt, float* acc_out, hipStream_t stream);
+// batched FP8 forms: items as for the int8 forms, with e4m3 code bytes in the
+// int8 fields and fp32 accumulators in GemmItem::acc_out
+hipError_t quant_weight_fp8_batched(const QuantWeightItem* items, int count, hipStream_t stream);
+hipError_t quant_act_fp8_batched(const ActItem* items, int count, hipStream_t stream);
+hipError_t gemm_fp8_batched(const GemmItem* items, int count, hipStream_t stream);
 
 // Block tile (rows, columns) the GEMM uses for an m x n output.
 void gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n);

@@ -842,6 +842,7 @@ def workload_variants(device):
       (512 samples x 512 tokens x 5120)."""
     import torch
     from w8a8_post_quantization_channel_amd import capi, synth
+    from w8a8_post_quantization_channel_amd.layer import forward_block, forward_block_dynamic
     out = {}
     groups, projs = setup(device)
     for _ in range(2):
@@ -849,12 +850,21 @@ def workload_variants(device):
     torch.cuda.synchronize()
     static_ms = timed(lambda: [layer.forward(g.x) for _, g, layer, _ in projs], 20)
     dynamic_ms = timed(lambda: [layer.forward_dynamic(g.x) for _, g, layer, _ in projs], 20)
+    layers = [layer for _, _, layer, _ in projs]
+    xs = [g.x for _, g, _, _ in projs]
+    static_b_ms = timed(lambda: forward_block(layers, xs), 50, warmup=10)
+    dynamic_b_ms = timed(lambda: forward_block_dynamic(layers, xs), 50, warmup=10)
     step_ms = timed(lambda: run_step(groups, projs), 20)
     out["dynamic_scale_13b"] = {
         "static_forward_us": static_ms * 1e3, "dynamic_forward_us": dynamic_ms * 1e3,
         "overhead_vs_static_forward": dynamic_ms / static_ms - 1.0,
         "overhead_vs_whole_step": (dynamic_ms - static_ms) / step_ms,
-        "forward": "7 projections: activation quantization + int8 GEMM, 2048 tokens"}
+        "forward": "7 projections: activation quantization + int8 GEMM, 2048 tokens, one projection at a time",
+        "batched": {"static_forward_us": static_b_ms * 1e3, "dynamic_forward_us": dynamic_b_ms * 1e3,
+                    "overhead_vs_static_forward": dynamic_b_ms / static_b_ms - 1.0,
+                    "overhead_vs_whole_step": (dynamic_b_ms - static_b_ms) / step_ms,
+                    "forward": "the block in few launches: static = batched codes + grouped GEMM; dynamic = "
+                               "batched live statistics of the 4 inputs + batched act scales + the same"}}
     del groups, projs
     torch.cuda.empty_cache()
 

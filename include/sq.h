@@ -148,6 +148,15 @@ sq_status sq_act_scale(const float* act_max, const float* inv_s, int64_t k,
                        float* act_scale, hipStream_t stream);
 
 /*
+ * sq_act_scale for several projections in one launch (host arrays of count
+ * <= SQ_MAX_BATCH items; an output may not overlap another item's buffers).
+ * With the batched absmax over the live inputs it gives the dynamic mode of a
+ * whole block in two launches.
+ */
+sq_status sq_act_scale_batched(int count, const float* const* act_max, const float* const* inv_s,
+                               const int64_t* k, float* const* act_scale, hipStream_t stream);
+
+/*
  * Dynamic mode [pwwt §2.3: scales computed at run time follow the input, at
  * some extra cost per call]: the offline smoothing factors are kept and the
  * per-tensor activation scale is recomputed from the batch being quantized:

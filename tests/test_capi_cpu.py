@@ -439,6 +439,18 @@ def test_batched_act_and_gemm_validation(lib):
     assert gemm(2, *bad) == SHAPE
 
 
+def test_act_scale_batched_validation(lib):
+    PP = ctypes.c_void_p * 2
+    I64 = ctypes.c_int64 * 2
+    a, b = A, A + 0x100000
+    f = lib.sq_act_scale_batched
+    assert f(2, None, PP(a, b), I64(64, 64), PP(a + 0x200000, b + 0x200000), None) == NULL
+    assert f(0, PP(a, b), PP(a, b), I64(64, 64), PP(a + 0x200000, b + 0x200000), None) == SHAPE
+    assert f(2, PP(a, b), PP(a, b), I64(64, 100), PP(a + 0x200000, b + 0x200000), None) == SHAPE
+    assert f(2, PP(a, MIS), PP(a, b), I64(64, 64), PP(a + 0x200000, b + 0x200000), None) == ALIGN
+    assert f(2, PP(a, b), PP(a, b), I64(64, 64), PP(a + 0x200000, a), None) == SHAPE  # item 1's scale on item 0's act_max
+
+
 def test_fp8_batched_validation(lib):
     """The batched FP8 forms share the int8 batched forms' checks."""
     PP = ctypes.c_void_p * 2

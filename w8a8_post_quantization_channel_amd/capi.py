@@ -69,6 +69,7 @@ def _declare(lib):
         "sq_smooth_quant_act_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_w8a8_gemm_batched": [c.c_int, P, P, P, P, P, P, P, P, P, P, P],
         "sq_smooth_factors_fp8_batched": [c.c_int, P, P, P, P, P, P, P, P],
+        "sq_act_scale_batched": [c.c_int, P, P, P, P, P],
         "sq_quant_weight_fp8_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_smooth_quant_act_fp8_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_fp8_gemm_batched": [c.c_int, P, P, P, P, P, P, P, P, P, P, P],
@@ -160,6 +161,16 @@ def sq_w8a8_gemm(xq, wq, act_scale, w_scale, y, acc_out=None, stream=None):
     _check("sq_w8a8_gemm", load().sq_w8a8_gemm(_dev(xq, "xq"), _dev(wq, "wq"), m, n, k, _dev(act_scale, "act_scale"),
                                                _dev(w_scale, "w_scale"), _dev(y, "y"), _dtype_code(y), acc,
                                                _stream(stream)))
+
+
+def sq_act_scale_batched(act_maxes, inv_ss, act_scales, stream=None):
+    """sq_act_scale for several projections in one launch."""
+    count = len(act_maxes)
+    if not all(len(v) == count for v in (inv_ss, act_scales)):
+        raise ValueError("per-item lists differ in length")
+    keep = [_ptrs(act_maxes, "act_maxes"), _ptrs(inv_ss, "inv_ss"),
+            _host_array(ctypes.c_int64, [t.shape[0] for t in act_maxes]), _ptrs(act_scales, "act_scales")]
+    _check("sq_act_scale_batched", load().sq_act_scale_batched(count, *[a for _, a in keep], _stream(stream)))
 
 
 def sq_smooth_factors_fp8_batched(act_maxes, w_maxes, alphas, ss, inv_ss, act_scales, stream=None):

@@ -427,6 +427,20 @@ hipError_t smooth_factors_batched(const SmoothItem* items, int count, hipStream_
     return smooth_factors_batched_q(items, count, sqd::kQmax, stream);
 }
 
+hipError_t act_scale_batched(const SmoothItem* items, int count, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    SmoothTable tab{};
+    tab.count = count;
+    for (int i = 0; i < count; ++i) {
+        tab.act_max[i] = items[i].act_max;
+        tab.inv_s[i] = items[i].inv_s;
+        tab.k[i] = items[i].k;
+        tab.act_scale[i] = items[i].act_scale;
+    }
+    act_scale_batched_kernel<<<dim3((unsigned)count), dim3(kScaleThreads), 0, stream>>>(tab, sqd::kQmax);
+    return hipGetLastError();
+}
+
 hipError_t smooth_factors_fp8_batched(const SmoothItem* items, int count, hipStream_t stream) {
     return smooth_factors_batched_q(items, count, sqd::kFp8Max, stream);
 }

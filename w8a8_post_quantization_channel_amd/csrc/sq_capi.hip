@@ -350,6 +350,27 @@ sq_status sq_act_scale(const float* act_max, const float* inv_s, int64_t k, floa
     return hip_status(sqk::act_scale(act_max, inv_s, k, act_scale, stream));
 }
 
+sq_status sq_act_scale_batched(int count, const float* const* act_max, const float* const* inv_s, const int64_t* k,
+                               float* const* act_scale, hipStream_t stream) {
+    if (!act_max || !inv_s || !k || !act_scale) return SQ_ERR_NULL;
+    if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
+    Ranges rg;
+    sqk::SmoothItem items[SQ_MAX_BATCH];
+    for (int i = 0; i < count; ++i) {
+        if (!act_max[i] || !inv_s[i] || !act_scale[i]) return SQ_ERR_NULL;
+        if (!valid_k(k[i])) return SQ_ERR_SHAPE;
+        if (!aligned16(act_max[i]) || !aligned16(inv_s[i]) || !aligned16(act_scale[i])) return SQ_ERR_ALIGN;
+        rg.add(i, act_max[i], k[i] * 4, false);
+        rg.add(i, inv_s[i], k[i] * 4, false);
+        rg.add(i, act_scale[i], 4, true);
+        // act_scale_batched only reads inv_s (the field is an output of the smoothing kernels)
+        items[i] = sqk::SmoothItem{act_max[i], nullptr, k[i], 0.0f, nullptr, const_cast<float*>(inv_s[i]),
+                                   act_scale[i]};
+    }
+    if (rg.overlap()) return SQ_ERR_SHAPE;
+    return hip_status(sqk::act_scale_batched(items, count, stream));
+}
+
 sq_status sq_dynamic_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* inv_s,
                                float* live_max, float* act_scale, int8_t* xq, hipStream_t stream) {
     if (!inv_s || !live_max || !act_scale || (m > 0 && (!x || !xq))) return SQ_ERR_NULL;

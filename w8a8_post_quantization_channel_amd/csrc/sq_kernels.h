@@ -77,6 +77,8 @@ struct SmoothItem {
 hipError_t smooth_factors_batched(const SmoothItem* items, int count, hipStream_t stream);
 // the same with the act scale over 448 (e4m3 codes)
 hipError_t smooth_factors_fp8_batched(const SmoothItem* items, int count, hipStream_t stream);
+// the act scale alone for several items (act_max, inv_s, k, act_scale used)
+hipError_t act_scale_batched(const SmoothItem* items, int count, hipStream_t stream);
 
 // W' = W diag(s), per-row symmetric int8
 hipError_t quant_weight(const void* w, int wt, int64_t n, int64_t k, const float* s, int8_t* wq,

@@ -150,6 +150,45 @@ def forward_block(layers, xs, stream=None, gemm_stream=None, between=None):
     return ys
 
 
+def forward_block_dynamic(layers, xs, stream=None):
+    """forward_dynamic for several layers in four launches (plus the zero
+    fill of the statistics): the live max of each distinct input (one batched
+    reduction; layers that share an input tensor share its statistic), every
+    layer's dynamic act scale (one launch), the activation codes (one launch)
+    and the products (one grouped launch, newest-first as in forward_block).
+    Every layer's dyn_scale holds its batch scale, as after forward_dynamic;
+    the batch statistic is written to the live_max of the first layer that
+    reads each input (the others' live_max are left as they were). Returns
+    the outputs."""
+    import torch
+    distinct, owner = [], {}
+    for l, x in zip(layers, xs):
+        if id(x) not in owner:
+            owner[id(x)] = l
+            distinct.append((x, l.live_max))
+    for part in _chunks(distinct):
+        capi.sq_calib_absmax_batched([x for x, _ in part], [a for _, a in part], False, stream)
+    live = [owner[id(x)].live_max for x in xs]
+    for part in _chunks(list(range(len(layers)))):
+        capi.sq_act_scale_batched([live[i] for i in part], [layers[i].inv_s for i in part],
+                                  [layers[i].dyn_scale for i in part], stream)
+    xqs, ys = [], []
+    for l, x in zip(layers, xs):
+        m = x.shape[0]
+        xqs.append(l.xq[:m] if l.xq is not None and l.xq.shape[0] >= m else
+                   torch.empty((m, l.k), dtype=torch.int8, device=x.device))
+        ys.append(l.y[:m] if l.y is not None and l.y.shape[0] >= m else
+                  torch.empty((m, l.n), dtype=l.out_dtype, device=x.device))
+    for part in _chunks(list(range(len(layers)))):
+        capi.sq_smooth_quant_act_batched([xs[i] for i in part], [layers[i].inv_s for i in part],
+                                         [layers[i].dyn_scale for i in part], [xqs[i] for i in part], stream)
+    for part in _chunks(list(range(len(layers)))[::-1]):
+        capi.sq_w8a8_gemm_batched([xqs[i] for i in part], [layers[i].wq for i in part],
+                                  [layers[i].dyn_scale for i in part], [layers[i].w_scale for i in part],
+                                  [ys[i] for i in part], None, stream)
+    return ys
+
+
 class PhasedBlock:
     """A block's projections split into phases that share no input, run on
     two streams: each phase's preparation (statistics of its inputs and

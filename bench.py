@@ -886,7 +886,27 @@ def workload_variants(device):
             "speedup": (norm_ms + quant_ms) / fused_ms, "fused_GB/s": byts / (fused_ms * 1e-3) / 1e9,
             "fused_hbm_frac": byts / (fused_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "bytes_per_element": {"fused": 3, "unfused": 7}}
-        del h, y, xq
+        # the norm's consumers as in a block (13B attention norm: q, k, v; 70B
+        # MLP norm: gate, up), each with its own folded weight and act scale:
+        # one fused pass per consumer against one pass writing every
+        # consumer's codes, and against RMSNorm then the batched quantizer
+        n = 3 if name == "13b" else 2
+        gfs = [gf] + [torch.empty(k, dtype=torch.float32, device=device) for _ in range(n - 1)]
+        invs = [inv_s] + [torch.rand(k, device=device) + 0.25 for _ in range(n - 1)]
+        for i in range(1, n):
+            capi.sq_fold_norm_weight(g, invs[i], gfs[i])
+        acs = [torch.full((4,), 0.05 + 0.01 * i, device=device) for i in range(n)]
+        xqs = [torch.empty((m, k), dtype=torch.int8, device=device) for _ in range(n)]
+        per_ms = timed(lambda: [capi.sq_rmsnorm_quant_act(h, gfs[i], 1e-5, acs[i], xqs[i]) for i in range(n)], 50)
+        multi_ms = timed(lambda: capi.sq_rmsnorm_quant_act_multi(h, gfs, 1e-5, acs, xqs), 50)
+        unf_ms = timed(lambda: (capi.sq_rmsnorm(h, g, 1e-5, y),
+                                capi.sq_smooth_quant_act_batched([y] * n, invs, acs, xqs)), 50)
+        mbytes = m * k * (2 + n) + n * k * 4
+        out[f"norm_fold_{name}_{m}x{k}"]["consumers"] = {
+            "n": n, "one_pass_us": multi_ms * 1e3, "pass_per_consumer_us": per_ms * 1e3,
+            "norm_then_batched_quant_us": unf_ms * 1e3, "one_pass_GB/s": mbytes / (multi_ms * 1e-3) / 1e9,
+            "one_pass_hbm_frac": mbytes / (multi_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del h, y, xq, xqs
         torch.cuda.empty_cache()
 
     samples, rows, k = 512, 512, 5120

@@ -241,6 +241,23 @@ sq_status sq_rmsnorm_quant_act(const void* h, sq_dtype ht, int64_t m, int64_t k,
                                int8_t* xq, float* r_out, hipStream_t stream);
 
 /*
+ * The same for n <= SQ_MAX_NORM_CONSUMERS consumers of one norm output (q, k
+ * and v after the attention norm; gate and up after the MLP norm), each with
+ * its own folded weight and act scale: for every consumer c
+ *   xq[c][t,j] = clamp(rne(fp32( fp32(fp32(h[t,j]*r[t]) * gamma_folded[c][j])
+ *                                * fp32(1/act_scale[c][0]) )), -127, 127)
+ * bit-identical to n calls of sq_rmsnorm_quant_act; h is read once when the n
+ * folded weights of a row fit in registers, else once per consumer. The
+ * arrays are host arrays of n device pointers; r_out [m] or NULL; no output
+ * may overlap another buffer of the call (SQ_ERR_SHAPE).
+ */
+#define SQ_MAX_NORM_CONSUMERS 4
+sq_status sq_rmsnorm_quant_act_multi(const void* h, sq_dtype ht, int64_t m, int64_t k, float eps,
+                                     int n, const float* const* gamma_folded,
+                                     const float* const* act_scale, int8_t* const* xq, float* r_out,
+                                     hipStream_t stream);
+
+/*
  * FP8 variant [aiu: smoothing serves FP8 as well as INT8]: the same smoothed
  * path with OCP FP8 E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa
  * bits, largest finite 448; round to nearest even; magnitudes past 448 are

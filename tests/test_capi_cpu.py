@@ -439,6 +439,32 @@ def test_batched_act_and_gemm_validation(lib):
     assert gemm(2, *bad) == SHAPE
 
 
+def test_rmsnorm_quant_multi_validation(lib):
+    PP = ctypes.c_void_p * 3
+    f = lib.sq_rmsnorm_quant_act_multi
+    H, G0, G1, G2, S0, S1, S2, Q0, Q1, Q2 = (A + i * 0x1000000 for i in range(10))
+    base = dict(h=H, ht=1, m=8, k=1024, eps=1e-5, n=3, g=PP(G0, G1, G2), a=PP(S0, S1, S2), q=PP(Q0, Q1, Q2), r=None)
+
+    def call(**ch):
+        v = dict(base, **ch)
+        return f(P(v["h"]) if v["h"] is not None else None, v["ht"], v["m"], v["k"], ctypes.c_float(v["eps"]), v["n"],
+                 v["g"], v["a"], v["q"], P(v["r"]) if v["r"] is not None else None, None)
+    assert call(g=None) == NULL
+    assert call(h=None) == NULL
+    assert call(q=PP(Q0, None, Q2)) == NULL
+    assert call(ht=9) == DTYPE
+    assert call(n=0) == SHAPE
+    assert call(n=5) == SHAPE
+    assert call(k=1000) == SHAPE
+    assert call(eps=-1.0) == SHAPE
+    assert call(h=H + 8) == ALIGN
+    assert call(q=PP(Q0, Q1 + 4, Q2)) == ALIGN
+    assert call(q=PP(Q0, Q0 + 4096, Q2)) == SHAPE   # two consumers' codes overlap
+    assert call(q=PP(Q0, G1, Q2)) == SHAPE          # codes on a consumer's folded weight
+    assert call(q=PP(Q0, Q1, H + 1024)) == SHAPE    # codes on h
+    assert call(r=G2) == SHAPE                      # r on a folded weight
+
+
 def test_act_scale_batched_validation(lib):
     PP = ctypes.c_void_p * 2
     I64 = ctypes.c_int64 * 2

@@ -233,3 +233,29 @@ def test_percentile_ties_and_signs():
             capi.sq_calib_percentile(_t(arr), q, ws, out)
             torch.cuda.synchronize()
             assert_bitexact(f"ties q={q}", _host(out), ORACLE.calib_percentile(arr, q))
+
+
+@pytest.mark.parametrize("m,k,bf16,n", [(37, 5120, True, 3), (2048, 5120, True, 3), (100, 8192, True, 2),
+                                        (64, 2048, False, 4), (5, 16384, True, 3), (300, 64, True, 2),
+                                        (9, 4096, False, 1)])
+def test_rmsnorm_quant_multi_equals_single(m, k, bf16, n):
+    """Several consumers of one norm output in one call: every consumer's
+    codes and r equal the single-consumer call's, bit for bit (one pass over
+    h, or one per consumer when the row is too long for all weights in
+    registers, e.g. k = 16384 with three consumers)."""
+    import torch
+    g = synth.rng(5200 + m + n)
+    h = _t(_x(5201 + m, m, k, bf16))
+    gam = [_t(g.uniform(0.2, 3.0, k).astype(np.float32)) for _ in range(n)]
+    a = [torch.tensor([g.uniform(0.005, 0.05), 0, 0, 0], dtype=torch.float32, device=dev()) for _ in range(n)]
+    one = [torch.empty((m, k), dtype=torch.int8, device=dev()) for _ in range(n)]
+    r1 = torch.empty(m, dtype=torch.float32, device=dev())
+    for c in range(n):
+        capi.sq_rmsnorm_quant_act(h, gam[c], 1e-5, a[c], one[c], r_out=r1)
+    two = [torch.full((m, k), 99, dtype=torch.int8, device=dev()) for _ in range(n)]
+    r2 = torch.zeros(m, dtype=torch.float32, device=dev())
+    capi.sq_rmsnorm_quant_act_multi(h, gam, 1e-5, a, two, r_out=r2)
+    torch.cuda.synchronize()
+    assert torch.equal(r1, r2)
+    for c in range(n):
+        assert torch.equal(one[c], two[c]), c

@@ -70,6 +70,7 @@ def _declare(lib):
         "sq_w8a8_gemm_batched": [c.c_int, P, P, P, P, P, P, P, P, P, P, P],
         "sq_smooth_factors_fp8_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_act_scale_batched": [c.c_int, P, P, P, P, P],
+        "sq_rmsnorm_quant_act_multi": [P, c.c_int, i64, i64, c.c_float, c.c_int, P, P, P, P, P],
         "sq_quant_weight_fp8_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_smooth_quant_act_fp8_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_fp8_gemm_batched": [c.c_int, P, P, P, P, P, P, P, P, P, P, P],
@@ -161,6 +162,21 @@ def sq_w8a8_gemm(xq, wq, act_scale, w_scale, y, acc_out=None, stream=None):
     _check("sq_w8a8_gemm", load().sq_w8a8_gemm(_dev(xq, "xq"), _dev(wq, "wq"), m, n, k, _dev(act_scale, "act_scale"),
                                                _dev(w_scale, "w_scale"), _dev(y, "y"), _dtype_code(y), acc,
                                                _stream(stream)))
+
+
+SQ_MAX_NORM_CONSUMERS = 4
+
+
+def sq_rmsnorm_quant_act_multi(h, gammas_folded, eps: float, act_scales, xqs, r_out=None, stream=None):
+    """sq_rmsnorm_quant_act for several consumers of one norm output (h read
+    once when their folded weights fit in registers)."""
+    m, k = h.shape
+    n = len(gammas_folded)
+    if not (len(act_scales) == n and len(xqs) == n):
+        raise ValueError("per-consumer lists differ in length")
+    g, a, q = _ptrs(gammas_folded, "gammas_folded"), _ptrs(act_scales, "act_scales"), _ptrs(xqs, "xqs")
+    _check("sq_rmsnorm_quant_act_multi", load().sq_rmsnorm_quant_act_multi(
+        _dev(h, "h"), _dtype_code(h), m, k, float(eps), n, g[1], a[1], q[1], _opt(r_out, "r_out"), _stream(stream)))
 
 
 def sq_act_scale_batched(act_maxes, inv_ss, act_scales, stream=None):

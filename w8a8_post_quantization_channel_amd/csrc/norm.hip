@@ -272,6 +272,121 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_stream_kernel(const u32x
     }
 }
 
+// Several consumers of one norm output (q, k and v after the attention norm;
+// gate and up after the MLP norm), each with its own folded weight and act
+// scale: the row is read and reduced once, fl(h r) formed once per element,
+// and every consumer's codes written from it exactly as the single-consumer
+// pass writes them. The consumers' weights stay in registers (NC x VPT x E).
+constexpr int kNormMaxConsumers = 4;
+struct NormConsumers {
+    const float* gamma[kNormMaxConsumers];
+    const float* act_scale[kNormMaxConsumers];
+    int8_t* xq[kNormMaxConsumers];
+};
+
+template <int EB, int VPT, int R, int NC>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_multi_kernel(const u32x4* __restrict__ h, int64_t m,
+                                                                     int64_t kvec, int64_t k, float eps,
+                                                                     const NormConsumers cons,
+                                                                     float* __restrict__ r_out) {
+    constexpr int E = 16 / EB;
+    __shared__ double red[2][R][kNormWaves];
+    const int tid = threadIdx.x;
+    const int64_t groups = (m + R - 1) / R;
+    float inv_a[NC];
+    float gm[NC][VPT][E];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        inv_a[c] = __fdiv_rn(1.0f, cons.act_scale[c][0]);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int64_t v = tid + (int64_t)i * kNormThreads;
+            if (v < kvec)
+                load_gamma<E>(cons.gamma[c], v, gm[c][i]);
+            else
+#pragma unroll
+                for (int e = 0; e < E; ++e) gm[c][i][e] = 0.0f;
+        }
+    }
+    auto load = [&](int64_t g, u32x4 (&buf)[R][VPT]) {
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const int64_t row = g * R + q;
+            const bool ok = g < groups && row < m;
+            const u32x4* hr = h + (ok ? row : 0) * kvec;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int64_t v = tid + (int64_t)i * kNormThreads;
+                buf[q][i] = (ok && v < kvec) ? __builtin_nontemporal_load(hr + v) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto process = [&](int64_t g, const u32x4 (&buf)[R][VPT], int par) {
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            double ss = 0.0;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) ss += sum_sq<E>(buf[q][i]);
+            ss = wave_sum_f64(ss);
+            if ((tid & 63) == 0) red[par][q][tid >> 6] = ss;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const int64_t row = g * R + q;
+            if (row >= m) break;
+            double total = red[par][q][0];
+#pragma unroll
+            for (int w = 1; w < kNormWaves; ++w) total += red[par][q][w];
+            const float r = (float)(1.0 / sqrt(total / (double)k + (double)eps));
+            if (r_out && tid == 0) r_out[row] = r;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int64_t v = tid + (int64_t)i * kNormThreads;
+                if (v >= kvec) continue;
+                float e[E], hr[E];
+                widen<E>(buf[q][i], e);
+#pragma unroll
+                for (int j = 0; j < E; ++j) hr[j] = __fmul_rn(e[j], r);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    // as emit<E, kOutI8>: clamp, then round half to even with the fp32 adder
+                    uint32_t b[E];
+#pragma unroll
+                    for (int j = 0; j < E; ++j) {
+                        const float y = __fmul_rn(hr[j], gm[c][i][j]);
+                        const float t = __builtin_fminf(__builtin_fmaxf(__fmul_rn(y, inv_a[c]), -sqd::kQmax), sqd::kQmax);
+                        b[j] = __float_as_uint(__fadd_rn(t, 12582912.0f));
+                    }
+                    uint32_t w[E / 4];
+#pragma unroll
+                    for (int d = 0; d < E / 4; ++d) {
+                        const uint32_t lo = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0c0c0400u);
+                        const uint32_t hi = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0c0c0400u);
+                        w[d] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                    }
+                    int8_t* dst = cons.xq[c] + row * k + v * E;
+                    if constexpr (E == 8)
+                        *(sqd::u32x2*)dst = sqd::u32x2{w[0], w[1]};
+                    else
+                        *(uint32_t*)dst = w[0];
+                }
+            }
+        }
+    };
+    u32x4 a[R][VPT], b[R][VPT];
+    const int64_t step = gridDim.x;
+    int64_t g = blockIdx.x;
+    load(g, a);
+    for (; g < groups; g += 2 * step) {
+        load(g + step, b);
+        process(g, a, 0);
+        if (g + step >= groups) break;
+        load(g + 2 * step, a);
+        process(g + step, b, 1);
+    }
+}
+
 int norm_cus() {
     static int cus = [] {
         int dev = 0, n = 0;
@@ -325,6 +440,56 @@ hipError_t launch_norm(const void* h, int64_t m, int64_t k, const float* gamma, 
     }
 }
 
+template <int EB, int VPT, int R, int NC>
+hipError_t launch_multi_rows(const void* h, int64_t m, int64_t kvec, int64_t k, float eps,
+                             const NormConsumers& cons, float* r_out, hipStream_t stream) {
+    static const int per_cu = [] {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, rmsnorm_multi_kernel<EB, VPT, R, NC>, kNormThreads, 0) !=
+                hipSuccess ||
+            b < 1)
+            b = 1;
+        return b;
+    }();
+    const int64_t groups = (m + R - 1) / R;
+    const int64_t grid = std::min<int64_t>(groups, (int64_t)per_cu * norm_cus());
+    rmsnorm_multi_kernel<EB, VPT, R, NC><<<dim3((unsigned)grid), dim3(kNormThreads), 0, stream>>>(
+        (const u32x4*)h, m, kvec, k, eps, cons, r_out);
+    return hipGetLastError();
+}
+
+// the single-consumer kernel's rows per block for the same row length; 0
+// when the consumers' weights would not fit the registers (VPT x NC > 12)
+template <int EB, int NC>
+hipError_t launch_multi(const void* h, int64_t m, int64_t k, float eps, const NormConsumers& cons, float* r_out,
+                        hipStream_t stream) {
+    const int64_t kvec = k * EB / 16;
+    const int64_t per = (kvec + kNormThreads - 1) / kNormThreads;
+    if (per * NC > 12) return hipErrorInvalidValue;
+    switch (per) {
+        case 1: return launch_multi_rows<EB, 1, 8, NC>(h, m, kvec, k, eps, cons, r_out, stream);
+        case 2: return launch_multi_rows<EB, 2, 4, NC>(h, m, kvec, k, eps, cons, r_out, stream);
+        case 3: return launch_multi_rows<EB, 3, 2, NC>(h, m, kvec, k, eps, cons, r_out, stream);
+        case 4: return launch_multi_rows<EB, 4, 2, NC>(h, m, kvec, k, eps, cons, r_out, stream);
+        case 5:
+        case 6: return launch_multi_rows<EB, 6, 1, NC>(h, m, kvec, k, eps, cons, r_out, stream);
+        case 7:
+        case 8: return launch_multi_rows<EB, 8, 1, NC>(h, m, kvec, k, eps, cons, r_out, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int EB>
+hipError_t launch_multi_n(int n, const void* h, int64_t m, int64_t k, float eps, const NormConsumers& cons,
+                          float* r_out, hipStream_t stream) {
+    switch (n) {
+        case 2: return launch_multi<EB, 2>(h, m, k, eps, cons, r_out, stream);
+        case 3: return launch_multi<EB, 3>(h, m, k, eps, cons, r_out, stream);
+        case 4: return launch_multi<EB, 4>(h, m, k, eps, cons, r_out, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
 // gamma_folded = fl(gamma * inv_s), one thread per channel
 __global__ __launch_bounds__(256) void fold_kernel(const float* __restrict__ gamma, const float* __restrict__ inv_s,
                                                    int64_t k, float* __restrict__ out) {
@@ -351,6 +516,30 @@ hipError_t rmsnorm_quant(const void* h, int ht, int64_t m, int64_t k, const floa
     if (m == 0) return hipSuccess;
     if (ht == kBF16) return launch_norm<2, kOutI8>(h, m, k, gamma_folded, eps, act_scale, xq, r_out, stream);
     return launch_norm<4, kOutI8>(h, m, k, gamma_folded, eps, act_scale, xq, r_out, stream);
+}
+
+hipError_t rmsnorm_quant_multi(const void* h, int ht, int64_t m, int64_t k, float eps, int n,
+                               const float* const* gamma_folded, const float* const* act_scale, int8_t* const* xq,
+                               float* r_out, hipStream_t stream) {
+    if (m == 0 || n <= 0) return hipSuccess;
+    if (n > kNormMaxConsumers) return hipErrorInvalidValue;
+    const int64_t per = (k * elem_bytes(ht) / 16 + kNormThreads - 1) / kNormThreads;
+    if (n == 1 || per * n > 12) {  // one pass per consumer (rows too long for all weights in registers)
+        for (int c = 0; c < n; ++c) {
+            const hipError_t e = rmsnorm_quant(h, ht, m, k, gamma_folded[c], eps, act_scale[c], xq[c],
+                                               c == 0 ? r_out : nullptr, stream);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    NormConsumers cons{};
+    for (int c = 0; c < n; ++c) {
+        cons.gamma[c] = gamma_folded[c];
+        cons.act_scale[c] = act_scale[c];
+        cons.xq[c] = xq[c];
+    }
+    return ht == kBF16 ? launch_multi_n<2>(n, h, m, k, eps, cons, r_out, stream)
+                       : launch_multi_n<4>(n, h, m, k, eps, cons, r_out, stream);
 }
 
 hipError_t fold_norm_weight(const float* gamma, const float* inv_s, int64_t k, float* out, hipStream_t stream) {

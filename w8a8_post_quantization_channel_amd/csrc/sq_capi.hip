@@ -497,6 +497,30 @@ sq_status sq_rmsnorm_quant_act(const void* h, sq_dtype ht, int64_t m, int64_t k,
     return hip_status(sqk::rmsnorm_quant(h, ht, m, k, gamma_folded, eps, act_scale, xq, r_out, stream));
 }
 
+sq_status sq_rmsnorm_quant_act_multi(const void* h, sq_dtype ht, int64_t m, int64_t k, float eps, int n,
+                                     const float* const* gamma_folded, const float* const* act_scale,
+                                     int8_t* const* xq, float* r_out, hipStream_t stream) {
+    if (!gamma_folded || !act_scale || !xq || (m > 0 && !h)) return SQ_ERR_NULL;
+    if (!valid_dtype(ht)) return SQ_ERR_DTYPE;
+    if (n < 1 || n > SQ_MAX_NORM_CONSUMERS || m < 0 || m > INT32_MAX || !valid_k(k) || !valid_eps(eps))
+        return SQ_ERR_SHAPE;
+    if (m > 0 && !aligned16(h)) return SQ_ERR_ALIGN;
+    if (r_out && !aligned16(r_out)) return SQ_ERR_ALIGN;
+    Ranges rg;  // every buffer its own id: an output may overlap no other buffer
+    rg.add(0, h, m * k * (ht == SQ_BF16 ? 2 : 4), false);
+    rg.add(1, r_out, m * 4, true);
+    for (int c = 0; c < n; ++c) {
+        if (!gamma_folded[c] || !act_scale[c] || (m > 0 && !xq[c])) return SQ_ERR_NULL;
+        if (!aligned16(gamma_folded[c]) || !aligned16(act_scale[c]) || (m > 0 && !aligned16(xq[c])))
+            return SQ_ERR_ALIGN;
+        rg.add(2 + 3 * c, gamma_folded[c], k * 4, false);
+        rg.add(3 + 3 * c, act_scale[c], 4, false);
+        rg.add(4 + 3 * c, xq[c], m * k, true);
+    }
+    if (rg.overlap()) return SQ_ERR_SHAPE;
+    return hip_status(sqk::rmsnorm_quant_multi(h, ht, m, k, eps, n, gamma_folded, act_scale, xq, r_out, stream));
+}
+
 sq_status sq_gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n) {
     if (!block_m || !block_n) return SQ_ERR_NULL;
     if (m < 0 || n < 0) return SQ_ERR_SHAPE;

@@ -55,6 +55,11 @@ hipError_t rmsnorm(const void* h, int ht, int64_t m, int64_t k, const float* gam
 // RMSNorm with the folded weight, quantized per tensor in the same pass
 hipError_t rmsnorm_quant(const void* h, int ht, int64_t m, int64_t k, const float* gamma_folded, float eps,
                          const float* act_scale, int8_t* xq, float* r_out, hipStream_t stream);
+// the same for n <= 4 consumers of one norm output (their own folded weights
+// and act scales): one pass over h when the weights fit the registers
+hipError_t rmsnorm_quant_multi(const void* h, int ht, int64_t m, int64_t k, float eps, int n,
+                               const float* const* gamma_folded, const float* const* act_scale, int8_t* const* xq,
+                               float* r_out, hipStream_t stream);
 
 // gamma_folded = fl(gamma * inv_s)
 hipError_t fold_norm_weight(const float* gamma, const float* inv_s, int64_t k, float* gamma_folded,

@@ -525,9 +525,9 @@ hipError_t launch_qw(const QwTable& tab, hipStream_t stream) {
 // 16-64 KB in a two-deep ring and two to four blocks per compute unit, so that
 // while one block reduces and quantizes a stage the others' loads keep HBM
 // busy; the slots per thread divide a stage's vectors (nearly) evenly.
-// Shape 7: rows of more than 4096 vectors, one block per row reading it twice.
-constexpr int kQwLong = 7;
-constexpr int kQwRowsPerStage[kQwLong] = {4, 2, 2, 2, 1, 1, 1};
+// Shape 8: rows of more than 4096 vectors, one block per row reading it twice.
+constexpr int kQwLong = 8;
+constexpr int kQwRowsPerStage[kQwLong] = {4, 2, 2, 2, 1, 1, 1, 1};
 
 int qw_shape(int64_t kvec) {
     if (kvec <= 256) return 0;
@@ -535,8 +535,9 @@ int qw_shape(int64_t kvec) {
     if (kvec <= 640) return 2;
     if (kvec <= 1024) return 3;
     if (kvec <= 1536) return 4;
-    if (kvec <= 2048) return 5;
-    if (kvec <= 4096) return 6;
+    if (kvec <= 1792) return 5;
+    if (kvec <= 2048) return 6;
+    if (kvec <= 4096) return 7;
     return kQwLong;
 }
 
@@ -548,8 +549,9 @@ hipError_t launch_shape(int shape, const QwTable& tab, hipStream_t stream) {
         case 2: return launch_qw<EB, 4, 5, 2, 5, 2, 3, FP8>(tab, stream);
         case 3: return launch_qw<EB, 8, 4, 2, 4, 2, 2, FP8>(tab, stream);
         case 4: return launch_qw<EB, 8, 3, 1, 3, 2, 3, FP8>(tab, stream);
-        case 5: return launch_qw<EB, 8, 4, 1, 4, 2, 2, FP8>(tab, stream);
-        case 6: return launch_qw<EB, 16, 4, 1, 4, 2, 1, FP8>(tab, stream);
+        case 5: return launch_qw<EB, 4, 7, 1, 7, 2, 2, FP8>(tab, stream);
+        case 6: return launch_qw<EB, 8, 4, 1, 4, 2, 2, FP8>(tab, stream);
+        case 7: return launch_qw<EB, 16, 4, 1, 4, 2, 1, FP8>(tab, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -662,27 +662,27 @@ def workload_ceilings(device):
     byte, the read against the XOR of its words."""
     import numpy as np
     import torch
-    from w8a8_post_quantization_channel_amd import capi
+    from w8a8_post_quantization_channel_amd import capi, ceiling
     out = {}
     sink = torch.zeros(4, dtype=torch.int32, device=device)
     iters = 20000
     for name, ops_host in ceiling_operand_sets(device).items():
-        dots = capi.ceiling_chain_dots(ops_host)
+        dots = ceiling.ceiling_chain_dots(ops_host)
         if max(abs(d) for d in dots) * iters >= 1 << 31:
             raise RuntimeError(f"{name}: accumulators would leave int32 ({dots})")
         operands = torch.from_numpy(ops_host.reshape(-1).copy()).to(device)
         for per_cu in (1, 2):
             sink.zero_()
-            ops = capi.sq_ceiling_mfma(iters, per_cu, operands, sink)
+            ops = ceiling.sq_ceiling_mfma(iters, per_cu, operands, sink)
             torch.cuda.synchronize()
             waves = ops // (8 * iters * 2 * 32 * 32 * 32)
-            expect = capi.ceiling_expected_sink(ops_host, iters, waves)
+            expect = ceiling.ceiling_expected_sink(ops_host, iters, waves)
             got = int(sink[0].item()) % (1 << 32)
             if got != expect:
                 raise RuntimeError(f"MFMA loop check failed ({name}): {got} != {expect}")
             # steady state: half a second of untimed calls, then ~0.2-0.5 s timed (a few
             # ms of MFMA load is too short for the power manager to settle)
-            ms = timed(lambda: capi.sq_ceiling_mfma(iters, per_cu, operands, sink), 100, warmup=2, warm_ms=500)
+            ms = timed(lambda: ceiling.sq_ceiling_mfma(iters, per_cu, operands, sink), 100, warmup=2, warm_ms=500)
             tops = ops / (ms * 1e-3) / 1e12
             out[f"mfma_loop_{name}_{per_cu}_blocks_per_cu"] = {
                 "TOPS": tops, "frac_of_int8_peak": tops / PEAK_INT8_TOPS,
@@ -691,29 +691,29 @@ def workload_ceilings(device):
     n = 1 << 30
     src = torch.randint(0, 256, (n,), dtype=torch.uint8, device=device)
     dst = torch.empty_like(src)
-    capi.sq_ceiling_copy(src, dst)
+    ceiling.sq_ceiling_copy(src, dst)
     torch.cuda.synchronize()
     if not torch.equal(src, dst):
         raise RuntimeError("copy check failed")
-    ms = timed(lambda: capi.sq_ceiling_copy(src, dst), 10)
+    ms = timed(lambda: ceiling.sq_ceiling_copy(src, dst), 10)
     out["copy_1GiB"] = {"GB/s": 2 * n / (ms * 1e-3) / 1e9, "hbm_frac": 2 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     del dst
     half = torch.empty(n // 2, dtype=torch.uint8, device=device)
-    capi.sq_ceiling_narrow(src, half)
+    ceiling.sq_ceiling_narrow(src, half)
     torch.cuda.synchronize()
     if not torch.equal(half, src.view(-1, 16)[:, :8].reshape(-1)):
         raise RuntimeError("narrowing copy check failed")
-    ms = timed(lambda: capi.sq_ceiling_narrow(src, half), 10)
+    ms = timed(lambda: ceiling.sq_ceiling_narrow(src, half), 10)
     out["narrow_1GiB_to_512MiB"] = {"GB/s": 1.5 * n / (ms * 1e-3) / 1e9,
                                     "hbm_frac": 1.5 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     del half
     xor = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
     sink.zero_()
-    capi.sq_ceiling_read(src, sink)
+    ceiling.sq_ceiling_read(src, sink)
     torch.cuda.synchronize()
     if int(sink[0].item()) % (1 << 32) != int(xor):
         raise RuntimeError("read check failed")
-    ms = timed(lambda: capi.sq_ceiling_read(src, sink), 10)
+    ms = timed(lambda: ceiling.sq_ceiling_read(src, sink), 10)
     out["read_1GiB"] = {"GB/s": n / (ms * 1e-3) / 1e9, "hbm_frac": n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     return {"metric": "measured ceilings: int8 MFMA-only loop TOPS (step's own codes), 16-byte copy and read GB/s",
             "value": out["mfma_loop_codes_1_blocks_per_cu"]["TOPS"], "unit": "TOPS",

@@ -350,3 +350,40 @@ def test_dynamic_block_forward_equals_per_layer():
     for (p, *_), l, y, r, rs in zip(synth.C2_PROJECTIONS, layers, ys, ref, ref_scale):
         assert torch.equal(l.dyn_scale[:1], rs), p
         assert torch.equal(y.view(torch.int16), r.view(torch.int16)), p
+
+
+@pytest.mark.gpu
+def test_side_stream_without_preallocated_buffers():
+    """A layer with no preallocated buffers run on a non-current stream: the
+    codes and the output it allocates are recorded on that stream, so work
+    queued afterwards on the current stream cannot take their memory while
+    the layer's kernels still run. Checked against the oracle."""
+    import numpy as np
+    import torch
+
+    from oracle.oracle import Oracle
+    from w8a8_post_quantization_channel_amd import synth
+    from w8a8_post_quantization_channel_amd.layer import W8A8Linear
+
+    d = torch.device("cuda", 0)
+    m, n, k = 1024, 2048, 1024
+    out = synth.outlier_channels(71, k)
+    x = synth.activations(72, m, k, out)
+    w = synth.weights(73, n, k)
+    xt, wt = synth.to_torch(x, d), synth.to_torch(w, d)
+    layer = W8A8Linear(wt, alpha=0.5, max_tokens=0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    layer.calibrate(xt, stream=side)
+    layer.prepare(stream=side)
+    ys = []
+    for _ in range(3):
+        ys.append(layer.forward(xt, stream=side))
+        # churn the allocator on the current stream while the side stream works
+        junk = [torch.full((m, k), 7, dtype=torch.int8, device=d) for _ in range(4)]
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    ref = Oracle().layer_forward([x], w, x, 0.5, bf16_out=True)
+    for y in ys:
+        assert np.array_equal(synth.from_torch(y), ref["y"])

@@ -7,7 +7,7 @@ import math
 import pytest
 
 from w8a8_post_quantization_channel_amd import build as sqbuild
-from w8a8_post_quantization_channel_amd import capi
+from w8a8_post_quantization_channel_amd import capi, ceiling
 
 OK, NULL, SHAPE, DTYPE, ALPHA, WORKSPACE, HIP, ALIGN = range(8)
 A = 0x10000   # a fake, 16-byte-aligned device address (never dereferenced)
@@ -29,6 +29,18 @@ def test_exports_every_declared_symbol(lib):
                           "sq_gemm_tiling"}
     for name in names:
         assert hasattr(lib, name), name
+
+
+def test_measurement_probes_live_in_their_own_library(lib):
+    """libsq.so exports the path only; the measured-ceiling probes are in
+    libsq_ceiling.so, which exports every function include/sq_ceiling.h declares."""
+    names = ceiling.declared_functions()
+    assert names == ["sq_ceiling_copy", "sq_ceiling_mfma", "sq_ceiling_narrow", "sq_ceiling_read"]
+    clib = ceiling.load()
+    for name in names:
+        assert hasattr(clib, name), name
+        assert not hasattr(lib, name), name
+    assert not any(n.startswith("sq_ceiling") for n in capi.declared_functions())
 
 
 def test_status_strings(lib):
@@ -506,8 +518,9 @@ def test_fp8_batched_validation(lib):
 
 
 def test_ceiling_validation(lib):
+    lib = ceiling.load()
     for name in ("sq_ceiling_mfma", "sq_ceiling_copy", "sq_ceiling_read", "sq_ceiling_narrow"):
-        assert name in capi.declared_functions() and hasattr(lib, name)
+        assert name in ceiling.declared_functions() and hasattr(lib, name)
     ops = ctypes.c_int64(0)
     assert lib.sq_ceiling_mfma(100, 1, P(A), None, ctypes.byref(ops), None) == NULL
     assert lib.sq_ceiling_mfma(100, 1, None, P(A), ctypes.byref(ops), None) == NULL
@@ -542,10 +555,76 @@ def test_ceiling_chain_dots():
     chain; one nonzero byte pair at lane 32 lands in its own chain only; bytes
     of lanes other than 0 and 32 do not enter element 0."""
     import numpy as np
-    assert capi.ceiling_chain_dots(np.ones(16384, np.int8)) == [32] * 8
+    assert ceiling.ceiling_chain_dots(np.ones(16384, np.int8)) == [32] * 8
     o = np.zeros((16, 64, 16), np.int8)
     o[2 * 3, 32, 5], o[2 * 3 + 1, 32, 5] = -7, 9
     o[2 * 5, 1, 0], o[2 * 5 + 1, 1, 0] = 100, 100  # lane 1: row 1 of A, column 1 of B
     o[2 * 6, 0, 2], o[2 * 6 + 1, 0, 3] = 50, 50  # different K positions
-    assert capi.ceiling_chain_dots(o.reshape(-1)) == [0, 0, 0, -63, 0, 0, 0, 0]
-    assert capi.ceiling_expected_sink(o.reshape(-1), 3, 10) == (-63 * 30) % (1 << 32)
+    assert ceiling.ceiling_chain_dots(o.reshape(-1)) == [0, 0, 0, -63, 0, 0, 0, 0]
+    assert ceiling.ceiling_expected_sink(o.reshape(-1), 3, 10) == (-63 * 30) % (1 << 32)
+
+
+# ---- the Python binding checks every tensor against the sizes it passes ------------------
+
+def _expect_value_error(call, *words):
+    with pytest.raises(ValueError) as e:
+        call()
+    msg = str(e.value)
+    for w in words:
+        assert w in msg, (w, msg)
+
+
+def test_binding_rejects_mismatched_outputs_before_launch():
+    """Wrong output shapes, element types and sizes raise ValueError naming the
+    argument; CPU tensors with every size right fail only at the GPU check.
+    No call reaches the library (these are CPU tensors)."""
+    import torch
+    bf, f32, i8, u8, i32 = torch.bfloat16, torch.float32, torch.int8, torch.uint8, torch.int32
+    m, n, k = 64, 32, 128
+    x = torch.zeros(m, k, dtype=bf)
+    xq, wq = torch.zeros(m, k, dtype=i8), torch.zeros(n, k, dtype=i8)
+    a, ws, y = torch.ones(4), torch.ones(n), torch.zeros(m, n, dtype=bf)
+    e = _expect_value_error
+    e(lambda: capi.sq_calib_absmax(x, torch.zeros(k - 64)), "absmax", "shape")
+    e(lambda: capi.sq_calib_absmax(x, torch.zeros(k, dtype=torch.float64)), "absmax", "dtype")
+    e(lambda: capi.sq_smooth_factors(torch.ones(k), torch.ones(k), 0.5, torch.ones(k), torch.ones(k - 1), a),
+      "inv_s", "shape")
+    e(lambda: capi.sq_smooth_factors(torch.ones(k), torch.ones(k), 0.5, torch.ones(k), torch.ones(k), torch.ones(0)),
+      "act_scale", "elements")
+    e(lambda: capi.sq_quant_weight(x, torch.ones(k), torch.zeros(m, k, dtype=u8), torch.ones(m)), "wq", "dtype")
+    e(lambda: capi.sq_quant_weight(x, torch.ones(k), torch.zeros(m, k, dtype=i8), torch.ones(m - 1)), "w_scale")
+    e(lambda: capi.sq_smooth_quant_act(x, torch.ones(k), a, torch.zeros(m, k - 64, dtype=i8)), "xq", "shape")
+    e(lambda: capi.sq_smooth_quant_act(x, torch.ones(k), a, torch.zeros(m, k, dtype=u8)), "xq", "dtype")
+    e(lambda: capi.sq_w8a8_gemm(xq, wq, a, ws, torch.zeros(m, n - 1, dtype=bf)), "y", "shape")
+    e(lambda: capi.sq_w8a8_gemm(xq, torch.zeros(n, k + 64, dtype=i8), a, ws, y), "wq", "k")
+    e(lambda: capi.sq_w8a8_gemm(xq, wq, a, torch.ones(n - 16), y), "w_scale", "shape")
+    e(lambda: capi.sq_w8a8_gemm(xq, wq, a, ws, y, torch.zeros(m, n, dtype=f32)), "acc_out", "dtype")
+    e(lambda: capi.sq_w8a8_gemm(xq, wq, a, ws, torch.zeros(m, n, dtype=torch.float16)), "y", "dtype")
+    e(lambda: capi.sq_dynamic_quant_act(x, torch.ones(k), torch.ones(k - 64), a, xq), "live_max")
+    e(lambda: capi.sq_rmsnorm(x, torch.ones(k), 1e-5, torch.zeros(m, k + 64, dtype=bf)), "y", "shape")
+    e(lambda: capi.sq_rmsnorm_quant_act(x, torch.ones(k), 1e-5, a, xq, torch.ones(m - 1)), "r_out")
+    e(lambda: capi.sq_calib_sample_max_sum(x, 4, torch.zeros(4, k), torch.zeros(k)), "sum", "dtype")
+    e(lambda: capi.sq_calib_sample_max_sum(x, 4, torch.zeros(2, k), torch.zeros(k, dtype=torch.float64)),
+      "sample_max")
+    e(lambda: capi.sq_calib_percentile(x, 0.999, torch.zeros(16, dtype=u8), torch.zeros(k - 64)), "act_max")
+    # FP8 variant: codes are uint8, accumulators fp32
+    xq8, wq8 = torch.zeros(m, k, dtype=u8), torch.zeros(n, k, dtype=u8)
+    e(lambda: capi.sq_fp8_gemm(xq, wq, a, ws, y), "xq", "dtype")
+    e(lambda: capi.sq_fp8_gemm(xq8, wq8, a, ws, y, torch.zeros(m, n, dtype=i32)), "acc_out", "dtype")
+    e(lambda: capi.sq_quant_weight_fp8(x, torch.ones(k), torch.zeros(m, k, dtype=i8), torch.ones(m)), "wq")
+    # batched forms name the item
+    e(lambda: capi.sq_w8a8_gemm_batched([xq, xq], [wq, wq], [a, a], [ws, ws], [y, torch.zeros(m, n + 1, dtype=bf)]),
+      "y[1]", "shape")
+    e(lambda: capi.sq_calib_absmax_batched([x, x], [torch.zeros(k), torch.zeros(k + 64)]), "absmaxes[1]")
+    e(lambda: capi.sq_quant_weight_batched([x], [torch.ones(k)], [torch.zeros(m, k, dtype=u8)], [torch.ones(m)]),
+      "wqs[0]", "dtype")
+    e(lambda: capi.sq_quant_weight_fp8_batched([x], [torch.ones(k)], [torch.zeros(m, k, dtype=i8)],
+                                               [torch.ones(m)]), "wqs[0]", "dtype")
+    e(lambda: capi.sq_smooth_quant_act_batched([x], [torch.ones(k)], [a], [torch.zeros(m, k, dtype=u8)]), "xqs[0]")
+    e(lambda: capi.sq_act_scale_batched([torch.ones(k)], [torch.ones(k + 64)], [a]), "inv_ss[0]")
+    e(lambda: capi.sq_w8a8_gemm_batched([], [], [], [], []), "at least one")
+    e(lambda: capi.sq_rmsnorm_quant_act_multi(x, [torch.ones(k), torch.ones(k - 64)], 1e-5, [a, a], [xq, xq]),
+      "gammas_folded[1]")
+    # everything right, but host tensors: rejected at the GPU check, still before any launch
+    e(lambda: capi.sq_w8a8_gemm(xq, wq, a, ws, y), "GPU")
+    e(lambda: capi.sq_calib_absmax(x, torch.zeros(k)), "GPU")

@@ -1,7 +1,9 @@
-"""Build libsq.so (the HIP kernels + C ABI) in-tree for gfx950.
+"""Build libsq.so (the HIP kernels + C ABI) in-tree for gfx950, and beside
+it libsq_ceiling.so, the measured-ceiling probes (measure/).
 
 Every source under csrc/ is compiled with hipcc for gfx950 only, in parallel,
-then linked into w8a8_post_quantization_channel_amd/libsq.so. Flags:
+then linked into w8a8_post_quantization_channel_amd/libsq.so; the sources
+under measure/ are linked into libsq_ceiling.so. Flags:
   -ffp-contract=off   no fused multiply-add: the quantization paths need one
                       IEEE rounding per fp32 operation
   -packed-fp32-ops off (device feature) keep the compiler from emitting packed
@@ -18,9 +20,11 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
+MEASURE = os.path.join(PKG, "measure")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsq.so")
+CEILING_LIB = os.path.join(PKG, "libsq_ceiling.so")
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -35,8 +39,12 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def measure_sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(MEASURE, "*.hip")))
+
+
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    obj = os.path.join(BUILD, os.path.basename(os.path.dirname(src)) + "_" + os.path.basename(src) + ".o")
     cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -44,30 +52,37 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile every csrc/*.hip and link libsq.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    """Compile every csrc/*.hip into libsq.so and every measure/*.hip into
+    libsq_ceiling.so; returns libsq's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs, msrcs = sources(), measure_sources()
+    jobs = jobs or min(len(srcs) + len(msrcs), max(1, min(16, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs + msrcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], CEILING_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING_LIB}")
     return LIB
 
 
 def stale() -> bool:
-    """True when libsq.so is missing or older than a source or header."""
-    if not os.path.exists(LIB):
+    """True when a library is missing or older than a source or header."""
+    if not os.path.exists(LIB) or not os.path.exists(CEILING_LIB):
         return True
-    t = os.path.getmtime(LIB)
-    deps = sources() + glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(INCLUDE, "*.h"))
+    t = min(os.path.getmtime(LIB), os.path.getmtime(CEILING_LIB))
+    deps = sources() + measure_sources() + glob.glob(os.path.join(CSRC, "*.h")) + \
+        glob.glob(os.path.join(INCLUDE, "*.h"))
     return any(os.path.getmtime(d) > t for d in deps)
 
 

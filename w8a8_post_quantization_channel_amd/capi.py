@@ -1,8 +1,10 @@
 """Thin Python binding over libsq's C ABI (include/sq.h).
 
 Argument marshalling only: each function takes torch tensors that already
-live on the GPU, checks dtype/contiguity, and passes raw device pointers, the
-shapes and the current HIP stream to the entry point of the same name. Every
+live on the GPU, checks every tensor's element type, shape (or size), device
+and contiguity against the sizes it passes (the C ABI trusts them), and passes
+raw device pointers, the shapes and the current HIP stream to the entry point
+of the same name. Every
 step of the computation runs in the library's HIP kernels. There is no
 fallback: if libsq.so is missing or fails to load, the call raises.
 """
@@ -74,10 +76,6 @@ def _declare(lib):
         "sq_quant_weight_fp8_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_smooth_quant_act_fp8_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_fp8_gemm_batched": [c.c_int, P, P, P, P, P, P, P, P, P, P, P],
-        "sq_ceiling_mfma": [i64, c.c_int, P, P, P, P],
-        "sq_ceiling_copy": [P, P, i64, P],
-        "sq_ceiling_read": [P, i64, P, P],
-        "sq_ceiling_narrow": [P, P, i64, P],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -121,6 +119,49 @@ def _dev(t, what: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _dtypes(name: str):
+    import torch
+    return {"f32": (torch.float32,), "bf16": (torch.bfloat16,), "act": (torch.float32, torch.bfloat16),
+            "i8": (torch.int8,), "u8": (torch.uint8,), "i32": (torch.int32,), "f64": (torch.float64,)}[name]
+
+
+def _arg(t, what: str, dtype: str, shape=None, numel: int | None = None, device=None):
+    """Check one tensor argument against what the entry point will read or
+    write -- element type, exact shape (or at least `numel` elements), device
+    (the first input's), contiguity -- and return its device pointer. Shape and
+    type are checked first, so a mismatch raises ValueError before anything is
+    launched (the C ABI sizes every buffer from the scalar sizes passed to it)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.dtype not in _dtypes(dtype):
+        raise ValueError(f"{what}: dtype {t.dtype}, expected {' or '.join(str(d) for d in _dtypes(dtype))}")
+    if shape is not None and tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(int(v) for v in shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{what}: {t.numel()} elements, at least {numel} needed")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} is on {t.device}, the call's inputs on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _call(name: str, anchor, *args, stream=None):
+    """Call entry point `name` once every argument has been checked: the
+    anchor input (every other tensor was checked to share its device) must be
+    a GPU tensor; the stream is resolved last."""
+    if not anchor.is_cuda:
+        raise ValueError(f"{name}: inputs must be GPU tensors (got {anchor.device})")
+    _check(name, getattr(load(), name)(*args, _stream(stream)))
+
+
+def _shape2(t, what: str):
+    if t.dim() != 2:
+        raise ValueError(f"{what} must be 2-D, got shape {tuple(t.shape)}")
+    return t.shape[0], t.shape[1]
+
+
 def _stream(stream):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -129,39 +170,54 @@ def _stream(stream):
 
 def sq_calib_absmax(x, absmax, accumulate: bool = False, stream=None):
     """absmax[j] = max(absmax[j] if accumulate else 0, max_t |x[t, j]|)."""
-    rows, k = x.shape
-    _check("sq_calib_absmax", load().sq_calib_absmax(_dev(x, "x"), _dtype_code(x), rows, k, _dev(absmax, "absmax"),
-                                                     int(bool(accumulate)), _stream(stream)))
+    rows, k = _shape2(x, "x")
+    px = _arg(x, "x", "act")
+    pa = _arg(absmax, "absmax", "f32", (k,), device=x.device)
+    _call("sq_calib_absmax", x, px, _dtype_code(x), rows, k, pa, int(bool(accumulate)), stream=stream)
     return absmax
 
 
 def sq_smooth_factors(act_max, w_max, alpha: float, s, inv_s, act_scale, stream=None):
     k = act_max.shape[0]
-    _check("sq_smooth_factors", load().sq_smooth_factors(_dev(act_max, "act_max"), _dev(w_max, "w_max"), k,
-                                                         float(alpha), _dev(s, "s"), _dev(inv_s, "inv_s"),
-                                                         _dev(act_scale, "act_scale"), _stream(stream)))
+    d = act_max.device
+    _call("sq_smooth_factors", act_max, _arg(act_max, "act_max", "f32", (k,)), _arg(w_max, "w_max", "f32", (k,), device=d), k, float(alpha),
+        _arg(s, "s", "f32", (k,), device=d), _arg(inv_s, "inv_s", "f32", (k,), device=d),
+        _arg(act_scale, "act_scale", "f32", numel=1, device=d), stream=stream)
 
 
 def sq_quant_weight(w, s, wq, w_scale, stream=None):
-    n, k = w.shape
-    _check("sq_quant_weight", load().sq_quant_weight(_dev(w, "w"), _dtype_code(w), n, k, _dev(s, "s"),
-                                                     _dev(wq, "wq"), _dev(w_scale, "w_scale"), _stream(stream)))
+    n, k = _shape2(w, "w")
+    pw, d = _arg(w, "w", "act"), w.device
+    _call("sq_quant_weight", w, pw, _dtype_code(w), n, k, _arg(s, "s", "f32", (k,), device=d),
+                                                     _arg(wq, "wq", "i8", (n, k), device=d),
+                                                     _arg(w_scale, "w_scale", "f32", (n,), device=d), stream=stream)
 
 
 def sq_smooth_quant_act(x, inv_s, act_scale, xq, stream=None):
-    m, k = x.shape
-    _check("sq_smooth_quant_act", load().sq_smooth_quant_act(_dev(x, "x"), _dtype_code(x), m, k,
-                                                             _dev(inv_s, "inv_s"), _dev(act_scale, "act_scale"),
-                                                             _dev(xq, "xq"), _stream(stream)))
+    m, k = _shape2(x, "x")
+    px, d = _arg(x, "x", "act"), x.device
+    _call("sq_smooth_quant_act", x, px, _dtype_code(x), m, k, _arg(inv_s, "inv_s", "f32", (k,), device=d),
+        _arg(act_scale, "act_scale", "f32", numel=1, device=d), _arg(xq, "xq", "i8", (m, k), device=d), stream=stream)
+
+
+def _gemm_args(xq, wq, act_scale, w_scale, y, acc_out, code: str, acc_code: str, tag: str = ""):
+    """Pointers and sizes of one product: xq [m,k], wq [n,k] (same code type),
+    act_scale [>=1], w_scale [n] fp32, y [m,n] fp32/bf16, acc_out [m,n] or None
+    (`tag` names the item of a batched call in error messages)."""
+    m, k = _shape2(xq, f"xq{tag}")
+    n, kw = _shape2(wq, f"wq{tag}")
+    if kw != k:
+        raise ValueError(f"wq{tag}: shape {tuple(wq.shape)} does not share k = {k} with xq{tag}")
+    d = xq.device
+    return (m, n, k, _arg(xq, f"xq{tag}", code), _arg(wq, f"wq{tag}", code, device=d),
+            _arg(act_scale, f"act_scale{tag}", "f32", numel=1, device=d),
+            _arg(w_scale, f"w_scale{tag}", "f32", (n,), device=d), _arg(y, f"y{tag}", "act", (m, n), device=d),
+            _arg(acc_out, f"acc_out{tag}", acc_code, (m, n), device=d) if acc_out is not None else ctypes.c_void_p(0))
 
 
 def sq_w8a8_gemm(xq, wq, act_scale, w_scale, y, acc_out=None, stream=None):
-    m, k = xq.shape
-    n = wq.shape[0]
-    acc = _dev(acc_out, "acc_out") if acc_out is not None else ctypes.c_void_p(0)
-    _check("sq_w8a8_gemm", load().sq_w8a8_gemm(_dev(xq, "xq"), _dev(wq, "wq"), m, n, k, _dev(act_scale, "act_scale"),
-                                               _dev(w_scale, "w_scale"), _dev(y, "y"), _dtype_code(y), acc,
-                                               _stream(stream)))
+    m, n, k, px, pw, pa, ps, py, pacc = _gemm_args(xq, wq, act_scale, w_scale, y, acc_out, "i8", "i32")
+    _call("sq_w8a8_gemm", xq, px, pw, m, n, k, pa, ps, py, _dtype_code(y), pacc, stream=stream)
 
 
 SQ_MAX_NORM_CONSUMERS = 4
@@ -170,23 +226,29 @@ SQ_MAX_NORM_CONSUMERS = 4
 def sq_rmsnorm_quant_act_multi(h, gammas_folded, eps: float, act_scales, xqs, r_out=None, stream=None):
     """sq_rmsnorm_quant_act for several consumers of one norm output (h read
     once when their folded weights fit in registers)."""
-    m, k = h.shape
+    m, k = _shape2(h, "h")
+    ph, d = _arg(h, "h", "act"), h.device
     n = len(gammas_folded)
     if not (len(act_scales) == n and len(xqs) == n):
         raise ValueError("per-consumer lists differ in length")
-    g, a, q = _ptrs(gammas_folded, "gammas_folded"), _ptrs(act_scales, "act_scales"), _ptrs(xqs, "xqs")
-    _check("sq_rmsnorm_quant_act_multi", load().sq_rmsnorm_quant_act_multi(
-        _dev(h, "h"), _dtype_code(h), m, k, float(eps), n, g[1], a[1], q[1], _opt(r_out, "r_out"), _stream(stream)))
+    g = _ptrs(gammas_folded, "gammas_folded", "f32", lambda i: (k,), d)
+    a = _ptrs(act_scales, "act_scales", "f32", None, d, numel=1)
+    q = _ptrs(xqs, "xqs", "i8", lambda i: (m, k), d)
+    pr = _arg(r_out, "r_out", "f32", (m,), device=d) if r_out is not None else ctypes.c_void_p(0)
+    _call("sq_rmsnorm_quant_act_multi", h, ph, _dtype_code(h), m, k, float(eps), n, g[1], a[1], q[1], pr, stream=stream)
 
 
 def sq_act_scale_batched(act_maxes, inv_ss, act_scales, stream=None):
     """sq_act_scale for several projections in one launch."""
-    count = len(act_maxes)
+    count = _items(len(act_maxes), "act_maxes")
     if not all(len(v) == count for v in (inv_ss, act_scales)):
         raise ValueError("per-item lists differ in length")
-    keep = [_ptrs(act_maxes, "act_maxes"), _ptrs(inv_ss, "inv_ss"),
-            _host_array(ctypes.c_int64, [t.shape[0] for t in act_maxes]), _ptrs(act_scales, "act_scales")]
-    _check("sq_act_scale_batched", load().sq_act_scale_batched(count, *[a for _, a in keep], _stream(stream)))
+    ks = [t.shape[0] for t in act_maxes]
+    d = act_maxes[0].device if count else None
+    keep = [_ptrs(act_maxes, "act_maxes", "f32", lambda i: (ks[i],), d),
+            _ptrs(inv_ss, "inv_ss", "f32", lambda i: (ks[i],), d),
+            _host_array(ctypes.c_int64, ks), _ptrs(act_scales, "act_scales", "f32", None, d, numel=1)]
+    _call("sq_act_scale_batched", act_maxes[0], count, *[a for _, a in keep], stream=stream)
 
 
 def sq_smooth_factors_fp8_batched(act_maxes, w_maxes, alphas, ss, inv_ss, act_scales, stream=None):
@@ -227,16 +289,27 @@ def sq_alpha_search_workspace(n_batches: int, rows_per_batch: int, n: int, k: in
 def sq_alpha_search(x_batches, w, workspace, alphas=ALPHA_GRID, stream=None):
     """Returns (mse list, best index). Synchronises the stream."""
     nb = len(x_batches)
-    rows, k = x_batches[0].shape
-    n = w.shape[0]
+    rows, k = _shape2(x_batches[0], "x_batches[0]")
+    n, kw = _shape2(w, "w")
+    if kw != k:
+        raise ValueError(f"w: shape {tuple(w.shape)} does not share k = {k} with the batches")
     xt = _dtype_code(x_batches[0])
+    d = x_batches[0].device
     for x in x_batches:
-        if x.shape != (rows, k) or _dtype_code(x) != xt:
+        if tuple(x.shape) != (rows, k) or _dtype_code(x) != xt:
             raise ValueError("all batches must share shape and dtype")
-    ptrs = (ctypes.c_void_p * nb)(*[_dev(x, "x_batches[i]").value for x in x_batches])
+    _arg(w, "w", "act", device=d)
+    need = sq_alpha_search_workspace(nb, rows, n, k, len(alphas))
+    if workspace.device != d:
+        raise ValueError(f"workspace is on {workspace.device}, the call's inputs on {d}")
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace: {workspace.numel() * workspace.element_size()} bytes, {need} needed")
+    ptrs = (ctypes.c_void_p * nb)(*[_arg(x, f"x_batches[{i}]", "act", device=d).value for i, x in enumerate(x_batches)])
     al = (ctypes.c_float * len(alphas))(*[float(a) for a in alphas])
     mse = (ctypes.c_double * len(alphas))()
     best = ctypes.c_int(-1)
+    if not x_batches[0].is_cuda:
+        raise ValueError(f"sq_alpha_search: inputs must be GPU tensors (got {x_batches[0].device})")
     _check("sq_alpha_search", load().sq_alpha_search(ctypes.cast(ptrs, ctypes.c_void_p), xt, nb, rows, k, _dev(w, "w"),
                                                      _dtype_code(w), n, ctypes.cast(al, ctypes.c_void_p), len(alphas),
                                                      _dev(workspace, "workspace"), workspace.numel() *
@@ -245,136 +318,115 @@ def sq_alpha_search(x_batches, w, workspace, alphas=ALPHA_GRID, stream=None):
     return list(mse), best.value
 
 
+def _items(n: int, what: str) -> int:
+    if n < 1:
+        raise ValueError(f"{what}: at least one item is needed")
+    return n
+
+
 def _host_array(ctype, values):
     """A host array for a per-item argument of the batched entry points."""
     arr = (ctype * len(values))(*values)
     return arr, ctypes.cast(arr, ctypes.c_void_p)
 
 
-def _ptrs(tensors, what: str):
-    return _host_array(ctypes.c_void_p, [_dev(t, f"{what}[{i}]").value for i, t in enumerate(tensors)])
+def _ptrs(tensors, what: str, dtype: str | None = None, shape_of=None, device=None, numel: int | None = None):
+    """Host array of the tensors' device pointers, each checked with _arg
+    (shape_of(i) gives item i's expected shape, or None)."""
+    if dtype is None:
+        return _host_array(ctypes.c_void_p, [_dev(t, f"{what}[{i}]").value for i, t in enumerate(tensors)])
+    return _host_array(ctypes.c_void_p, [
+        _arg(t, f"{what}[{i}]", dtype, shape_of(i) if shape_of else None, numel, device).value
+        for i, t in enumerate(tensors)])
 
 
 def sq_calib_absmax_batched(xs, absmaxes, accumulate: bool = False, stream=None):
     """sq_calib_absmax over several inputs in one zero fill + one reduction launch."""
     if len(xs) != len(absmaxes):
         raise ValueError("xs and absmaxes differ in length")
-    keep = [_ptrs(xs, "xs"), _host_array(ctypes.c_int, [_dtype_code(x) for x in xs]),
-            _host_array(ctypes.c_int64, [x.shape[0] for x in xs]), _host_array(ctypes.c_int64, [x.shape[1] for x in xs]),
-            _ptrs(absmaxes, "absmaxes")]
-    _check("sq_calib_absmax_batched", load().sq_calib_absmax_batched(len(xs), *[a for _, a in keep],
-                                                                     int(bool(accumulate)), _stream(stream)))
+    _items(len(xs), "xs")
+    shp = [_shape2(x, f"xs[{i}]") for i, x in enumerate(xs)]
+    d = xs[0].device if xs else None
+    keep = [_ptrs(xs, "xs", "act", None, d), _host_array(ctypes.c_int, [_dtype_code(x) for x in xs]),
+            _host_array(ctypes.c_int64, [r for r, _ in shp]), _host_array(ctypes.c_int64, [k for _, k in shp]),
+            _ptrs(absmaxes, "absmaxes", "f32", lambda i: (shp[i][1],), d)]
+    _call("sq_calib_absmax_batched", xs[0], len(xs), *[a for _, a in keep], int(bool(accumulate)), stream=stream)
 
 
 def sq_smooth_factors_batched(act_maxes, w_maxes, alphas, ss, inv_ss, act_scales, stream=None,
                               _name="sq_smooth_factors_batched"):
     """sq_smooth_factors for several projections in two launches."""
-    count = len(act_maxes)
+    count = _items(len(act_maxes), "act_maxes")
     if not all(len(v) == count for v in (w_maxes, alphas, ss, inv_ss, act_scales)):
         raise ValueError("per-item lists differ in length")
-    keep = [_ptrs(act_maxes, "act_maxes"), _ptrs(w_maxes, "w_maxes"),
-            _host_array(ctypes.c_int64, [t.shape[0] for t in act_maxes]),
-            _host_array(ctypes.c_float, [float(a) for a in alphas]), _ptrs(ss, "ss"), _ptrs(inv_ss, "inv_ss"),
-            _ptrs(act_scales, "act_scales")]
-    _check(_name, getattr(load(), _name)(count, *[a for _, a in keep], _stream(stream)))
+    ks = [t.shape[0] for t in act_maxes]
+    d = act_maxes[0].device if count else None
+    kk = lambda i: (ks[i],)  # noqa: E731
+    keep = [_ptrs(act_maxes, "act_maxes", "f32", kk, d), _ptrs(w_maxes, "w_maxes", "f32", kk, d),
+            _host_array(ctypes.c_int64, ks),
+            _host_array(ctypes.c_float, [float(a) for a in alphas]), _ptrs(ss, "ss", "f32", kk, d),
+            _ptrs(inv_ss, "inv_ss", "f32", kk, d), _ptrs(act_scales, "act_scales", "f32", None, d, numel=1)]
+    _call(_name, act_maxes[0], count, *[a for _, a in keep], stream=stream)
 
 
 def sq_quant_weight_batched(ws, ss, wqs, w_scales, stream=None, _name="sq_quant_weight_batched"):
     """sq_quant_weight for several weights, one launch per row-length class."""
-    count = len(ws)
+    count = _items(len(ws), "ws")
     if not all(len(v) == count for v in (ss, wqs, w_scales)):
         raise ValueError("per-item lists differ in length")
-    keep = [_ptrs(ws, "ws"), _host_array(ctypes.c_int, [_dtype_code(w) for w in ws]),
-            _host_array(ctypes.c_int64, [w.shape[0] for w in ws]), _host_array(ctypes.c_int64, [w.shape[1] for w in ws]),
-            _ptrs(ss, "ss"), _ptrs(wqs, "wqs"), _ptrs(w_scales, "w_scales")]
-    _check(_name, getattr(load(), _name)(count, *[a for _, a in keep], _stream(stream)))
+    shp = [_shape2(w, f"ws[{i}]") for i, w in enumerate(ws)]
+    d = ws[0].device if count else None
+    code = "u8" if "fp8" in _name else "i8"
+    keep = [_ptrs(ws, "ws", "act", None, d), _host_array(ctypes.c_int, [_dtype_code(w) for w in ws]),
+            _host_array(ctypes.c_int64, [n for n, _ in shp]), _host_array(ctypes.c_int64, [k for _, k in shp]),
+            _ptrs(ss, "ss", "f32", lambda i: (shp[i][1],), d), _ptrs(wqs, "wqs", code, lambda i: shp[i], d),
+            _ptrs(w_scales, "w_scales", "f32", lambda i: (shp[i][0],), d)]
+    _call(_name, ws[0], count, *[a for _, a in keep], stream=stream)
 
 
 def sq_smooth_quant_act_batched(xs, inv_ss, act_scales, xqs, stream=None, _name="sq_smooth_quant_act_batched"):
     """sq_smooth_quant_act for several projections in one launch (a shared
     input tensor is read once for all of its consumers)."""
-    count = len(xs)
+    count = _items(len(xs), "xs")
     if not all(len(v) == count for v in (inv_ss, act_scales, xqs)):
         raise ValueError("per-item lists differ in length")
-    keep = [_ptrs(xs, "xs"), _host_array(ctypes.c_int, [_dtype_code(x) for x in xs]),
-            _host_array(ctypes.c_int64, [x.shape[0] for x in xs]), _host_array(ctypes.c_int64, [x.shape[1] for x in xs]),
-            _ptrs(inv_ss, "inv_ss"), _ptrs(act_scales, "act_scales"), _ptrs(xqs, "xqs")]
-    _check(_name, getattr(load(), _name)(count, *[a for _, a in keep], _stream(stream)))
+    shp = [_shape2(x, f"xs[{i}]") for i, x in enumerate(xs)]
+    d = xs[0].device if count else None
+    code = "u8" if "fp8" in _name else "i8"
+    keep = [_ptrs(xs, "xs", "act", None, d), _host_array(ctypes.c_int, [_dtype_code(x) for x in xs]),
+            _host_array(ctypes.c_int64, [m for m, _ in shp]), _host_array(ctypes.c_int64, [k for _, k in shp]),
+            _ptrs(inv_ss, "inv_ss", "f32", lambda i: (shp[i][1],), d),
+            _ptrs(act_scales, "act_scales", "f32", None, d, numel=1), _ptrs(xqs, "xqs", code, lambda i: shp[i], d)]
+    _call(_name, xs[0], count, *[a for _, a in keep], stream=stream)
 
 
 def sq_w8a8_gemm_batched(xqs, wqs, act_scales, w_scales, ys, acc_outs=None, stream=None,
                          _name="sq_w8a8_gemm_batched"):
     """sq_w8a8_gemm for several products; those with the same large tile and
     output type share one launch."""
-    count = len(xqs)
+    count = _items(len(xqs), "xqs")
     if not all(len(v) == count for v in (wqs, act_scales, w_scales, ys)):
         raise ValueError("per-item lists differ in length")
-    keep = [_ptrs(xqs, "xqs"), _ptrs(wqs, "wqs"), _host_array(ctypes.c_int64, [x.shape[0] for x in xqs]),
-            _host_array(ctypes.c_int64, [w.shape[0] for w in wqs]), _host_array(ctypes.c_int64, [x.shape[1] for x in xqs]),
-            _ptrs(act_scales, "act_scales"), _ptrs(w_scales, "w_scales"), _ptrs(ys, "ys"),
+    if acc_outs is not None and len(acc_outs) != count:
+        raise ValueError("acc_outs differs in length")
+    fp8 = "fp8" in _name
+    args = [_gemm_args(xqs[i], wqs[i], act_scales[i], w_scales[i], ys[i],
+                       acc_outs[i] if acc_outs is not None else None, "u8" if fp8 else "i8", "f32" if fp8 else "i32",
+                       f"[{i}]")
+            for i in range(count)]
+    d = xqs[0].device if count else None
+    for i in range(1, count):
+        if xqs[i].device != d:
+            raise ValueError(f"xqs[{i}] is on {xqs[i].device}, the call's inputs on {d}")
+    keep = [_host_array(ctypes.c_void_p, [a[3].value for a in args]), _host_array(ctypes.c_void_p, [a[4].value for a in args]),
+            _host_array(ctypes.c_int64, [a[0] for a in args]), _host_array(ctypes.c_int64, [a[1] for a in args]),
+            _host_array(ctypes.c_int64, [a[2] for a in args]), _host_array(ctypes.c_void_p, [a[5].value for a in args]),
+            _host_array(ctypes.c_void_p, [a[6].value for a in args]), _host_array(ctypes.c_void_p, [a[7].value for a in args]),
             _host_array(ctypes.c_int, [_dtype_code(y) for y in ys])]
     acc = None
     if acc_outs is not None:
-        if len(acc_outs) != count:
-            raise ValueError("acc_outs differs in length")
-        acc = _host_array(ctypes.c_void_p, [_opt(a, f"acc_outs[{i}]").value for i, a in enumerate(acc_outs)])
-    _check(_name, getattr(load(), _name)(count, *[a for _, a in keep], acc[1] if acc else ctypes.c_void_p(0),
-                                         _stream(stream)))
-
-
-CEILING_OPERAND_BYTES = 16384
-
-
-def sq_ceiling_mfma(iters: int, blocks_per_cu: int, operands, sink, stream=None) -> int:
-    """MFMA-only loop on every compute unit over the 16 KiB of register
-    operands in `operands`; returns the int8 ops it issues."""
-    if operands.numel() * operands.element_size() != CEILING_OPERAND_BYTES:
-        raise ValueError(f"operands must hold {CEILING_OPERAND_BYTES} bytes")
-    ops = ctypes.c_int64(0)
-    _check("sq_ceiling_mfma", load().sq_ceiling_mfma(iters, blocks_per_cu, _dev(operands, "operands"),
-                                                     _dev(sink, "sink"), ctypes.byref(ops), _stream(stream)))
-    return ops.value
-
-
-def ceiling_chain_dots(operands) -> list:
-    """Per chain, the dot product sq_ceiling_mfma adds to its sink per
-    iteration: element 0 of a v_mfma_i32_32x32x32_i8 accumulator is row 0 of A
-    times column 0 of B, whose 32 bytes are lanes 0 and 32 of each operand
-    (the same byte order on both sides, so the pairing does not depend on how
-    the instruction numbers K). `operands` is the host copy (16384 int8)."""
-    import numpy as np
-    o = np.asarray(operands, dtype=np.int8).reshape(16, 64, 16).astype(np.int64)
-    return [int((np.concatenate([o[2 * c, 0], o[2 * c, 32]]) *
-                 np.concatenate([o[2 * c + 1, 0], o[2 * c + 1, 32]])).sum()) for c in range(8)]
-
-
-def ceiling_expected_sink(operands, iters: int, waves: int) -> int:
-    """sink[0] after one sq_ceiling_mfma call from zero (mod 2^32)."""
-    return (waves * iters * sum(ceiling_chain_dots(operands))) % (1 << 32)
-
-
-def sq_ceiling_copy(src, dst, stream=None):
-    """16-byte vector copy of src into dst (same number of bytes)."""
-    nbytes = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() != nbytes:
-        raise ValueError("src and dst differ in size")
-    _check("sq_ceiling_copy", load().sq_ceiling_copy(_dev(src, "src"), _dev(dst, "dst"), nbytes, _stream(stream)))
-
-
-def sq_ceiling_narrow(src, dst, stream=None):
-    """Reads src, writes the first 8 bytes of every 16-byte vector of it to
-    dst (half src's size)."""
-    nbytes = src.numel() * src.element_size()
-    if 2 * dst.numel() * dst.element_size() != nbytes:
-        raise ValueError("dst must hold half of src's bytes")
-    _check("sq_ceiling_narrow", load().sq_ceiling_narrow(_dev(src, "src"), _dev(dst, "dst"), nbytes,
-                                                         _stream(stream)))
-
-
-def sq_ceiling_read(src, sink, stream=None):
-    """16-byte vector read of src, every 32-bit word XORed into sink[0]."""
-    _check("sq_ceiling_read", load().sq_ceiling_read(_dev(src, "src"), src.numel() * src.element_size(),
-                                                     _dev(sink, "sink"), _stream(stream)))
+        acc = _host_array(ctypes.c_void_p, [a[8].value for a in args])
+    _call(_name, xqs[0], count, *[a for _, a in keep], acc[1] if acc else ctypes.c_void_p(0), stream=stream)
 
 
 def _opt(t, what: str):
@@ -382,53 +434,55 @@ def _opt(t, what: str):
 
 
 def sq_act_scale(act_max, inv_s, act_scale, stream=None):
-    k = act_max.shape[0]
-    _check("sq_act_scale", load().sq_act_scale(_dev(act_max, "act_max"), _dev(inv_s, "inv_s"), k,
-                                               _dev(act_scale, "act_scale"), _stream(stream)))
+    k, d = act_max.shape[0], act_max.device
+    _call("sq_act_scale", act_max, _arg(act_max, "act_max", "f32", (k,)),
+                                               _arg(inv_s, "inv_s", "f32", (k,), device=d), k,
+                                               _arg(act_scale, "act_scale", "f32", numel=1, device=d), stream=stream)
 
 
 def sq_dynamic_quant_act(x, inv_s, live_max, act_scale, xq, stream=None):
-    m, k = x.shape
-    _check("sq_dynamic_quant_act", load().sq_dynamic_quant_act(_dev(x, "x"), _dtype_code(x), m, k,
-                                                               _dev(inv_s, "inv_s"), _dev(live_max, "live_max"),
-                                                               _dev(act_scale, "act_scale"), _dev(xq, "xq"),
-                                                               _stream(stream)))
+    m, k = _shape2(x, "x")
+    px, d = _arg(x, "x", "act"), x.device
+    _call("sq_dynamic_quant_act", x, px, _dtype_code(x), m, k, _arg(inv_s, "inv_s", "f32", (k,), device=d),
+        _arg(live_max, "live_max", "f32", (k,), device=d), _arg(act_scale, "act_scale", "f32", numel=1, device=d),
+        _arg(xq, "xq", "i8", (m, k), device=d), stream=stream)
 
 
 def sq_calib_sample_max_sum(x, samples: int, sample_max, total, stream=None):
-    rows, k = x.shape
+    rows, k = _shape2(x, "x")
     if samples < 1 or rows % samples:
         raise ValueError("rows must be a whole number of samples")
-    _check("sq_calib_sample_max_sum", load().sq_calib_sample_max_sum(_dev(x, "x"), _dtype_code(x), samples,
-                                                                     rows // samples, k,
-                                                                     _dev(sample_max, "sample_max"),
-                                                                     _dev(total, "sum"), _stream(stream)))
+    px, d = _arg(x, "x", "act"), x.device
+    _call("sq_calib_sample_max_sum", x, px, _dtype_code(x), samples, rows // samples, k,
+        _arg(sample_max, "sample_max", "f32", (samples, k), device=d), _arg(total, "sum", "f64", (k,), device=d), stream=stream)
 
 
 def sq_calib_mean_finalize(total, count: int, act_max, stream=None):
-    k = total.shape[0]
-    _check("sq_calib_mean_finalize", load().sq_calib_mean_finalize(_dev(total, "sum"), count, k,
-                                                                   _dev(act_max, "act_max"), _stream(stream)))
+    k, d = total.shape[0], total.device
+    _call("sq_calib_mean_finalize", total, _arg(total, "sum", "f64", (k,)), count, k,
+                                                                   _arg(act_max, "act_max", "f32", (k,), device=d), stream=stream)
 
 
 def sq_rmsnorm(h, gamma, eps: float, y, r_out=None, stream=None):
-    m, k = h.shape
-    _check("sq_rmsnorm", load().sq_rmsnorm(_dev(h, "h"), _dtype_code(h), m, k, _dev(gamma, "gamma"), float(eps),
-                                           _dev(y, "y"), _dtype_code(y), _opt(r_out, "r_out"), _stream(stream)))
+    m, k = _shape2(h, "h")
+    ph, d = _arg(h, "h", "act"), h.device
+    pr = _arg(r_out, "r_out", "f32", (m,), device=d) if r_out is not None else ctypes.c_void_p(0)
+    _call("sq_rmsnorm", h, ph, _dtype_code(h), m, k, _arg(gamma, "gamma", "f32", (k,), device=d),
+                                           float(eps), _arg(y, "y", "act", (m, k), device=d), _dtype_code(y), pr, stream=stream)
 
 
 def sq_fold_norm_weight(gamma, inv_s, gamma_folded, stream=None):
-    k = gamma.shape[0]
-    _check("sq_fold_norm_weight", load().sq_fold_norm_weight(_dev(gamma, "gamma"), _dev(inv_s, "inv_s"), k,
-                                                             _dev(gamma_folded, "gamma_folded"), _stream(stream)))
+    k, d = gamma.shape[0], gamma.device
+    _call("sq_fold_norm_weight", gamma, _arg(gamma, "gamma", "f32", (k,)), _arg(inv_s, "inv_s", "f32", (k,), device=d), k,
+        _arg(gamma_folded, "gamma_folded", "f32", (k,), device=d), stream=stream)
 
 
 def sq_rmsnorm_quant_act(h, gamma_folded, eps: float, act_scale, xq, r_out=None, stream=None):
-    m, k = h.shape
-    _check("sq_rmsnorm_quant_act", load().sq_rmsnorm_quant_act(_dev(h, "h"), _dtype_code(h), m, k,
-                                                               _dev(gamma_folded, "gamma_folded"), float(eps),
-                                                               _dev(act_scale, "act_scale"), _dev(xq, "xq"),
-                                                               _opt(r_out, "r_out"), _stream(stream)))
+    m, k = _shape2(h, "h")
+    ph, d = _arg(h, "h", "act"), h.device
+    pr = _arg(r_out, "r_out", "f32", (m,), device=d) if r_out is not None else ctypes.c_void_p(0)
+    _call("sq_rmsnorm_quant_act", h, ph, _dtype_code(h), m, k, _arg(gamma_folded, "gamma_folded", "f32", (k,), device=d), float(eps),
+        _arg(act_scale, "act_scale", "f32", numel=1, device=d), _arg(xq, "xq", "i8", (m, k), device=d), pr, stream=stream)
 
 
 def sq_calib_percentile_workspace(k: int, dtype_code: int = SQ_BF16) -> int:
@@ -439,39 +493,40 @@ def sq_calib_percentile_workspace(k: int, dtype_code: int = SQ_BF16) -> int:
 
 def sq_calib_percentile(x, q: float, workspace, act_max, stream=None):
     """act_max[j] = nearest-rank q-quantile of |x[:, j]|."""
-    rows, k = x.shape
-    _check("sq_calib_percentile", load().sq_calib_percentile(_dev(x, "x"), _dtype_code(x), rows, k, float(q),
-                                                             _dev(workspace, "workspace"),
-                                                             workspace.numel() * workspace.element_size(),
-                                                             _dev(act_max, "act_max"), _stream(stream)))
+    rows, k = _shape2(x, "x")
+    px, d = _arg(x, "x", "act"), x.device
+    pa = _arg(act_max, "act_max", "f32", (k,), device=d)
+    if workspace.device != d:
+        raise ValueError(f"workspace is on {workspace.device}, the call's inputs on {d}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _call("sq_calib_percentile", x, px, _dtype_code(x), rows, k, float(q), ctypes.c_void_p(workspace.data_ptr()),
+          workspace.numel() * workspace.element_size(), pa, stream=stream)
 
 
 # ---- FP8 (OCP E4M3) variant: codes are torch.uint8 tensors --------------------------
 
 def sq_act_scale_fp8(act_max, inv_s, act_scale, stream=None):
-    k = act_max.shape[0]
-    _check("sq_act_scale_fp8", load().sq_act_scale_fp8(_dev(act_max, "act_max"), _dev(inv_s, "inv_s"), k,
-                                                       _dev(act_scale, "act_scale"), _stream(stream)))
+    k, d = act_max.shape[0], act_max.device
+    _call("sq_act_scale_fp8", act_max, _arg(act_max, "act_max", "f32", (k,)),
+                                                       _arg(inv_s, "inv_s", "f32", (k,), device=d), k,
+                                                       _arg(act_scale, "act_scale", "f32", numel=1, device=d), stream=stream)
 
 
 def sq_quant_weight_fp8(w, s, wq, w_scale, stream=None):
-    n, k = w.shape
-    _check("sq_quant_weight_fp8", load().sq_quant_weight_fp8(_dev(w, "w"), _dtype_code(w), n, k, _dev(s, "s"),
-                                                             _dev(wq, "wq"), _dev(w_scale, "w_scale"),
-                                                             _stream(stream)))
+    n, k = _shape2(w, "w")
+    pw, d = _arg(w, "w", "act"), w.device
+    _call("sq_quant_weight_fp8", w, pw, _dtype_code(w), n, k, _arg(s, "s", "f32", (k,), device=d), _arg(wq, "wq", "u8", (n, k), device=d),
+        _arg(w_scale, "w_scale", "f32", (n,), device=d), stream=stream)
 
 
 def sq_smooth_quant_act_fp8(x, inv_s, act_scale, xq, stream=None):
-    m, k = x.shape
-    _check("sq_smooth_quant_act_fp8", load().sq_smooth_quant_act_fp8(_dev(x, "x"), _dtype_code(x), m, k,
-                                                                     _dev(inv_s, "inv_s"),
-                                                                     _dev(act_scale, "act_scale"), _dev(xq, "xq"),
-                                                                     _stream(stream)))
+    m, k = _shape2(x, "x")
+    px, d = _arg(x, "x", "act"), x.device
+    _call("sq_smooth_quant_act_fp8", x, px, _dtype_code(x), m, k, _arg(inv_s, "inv_s", "f32", (k,), device=d),
+        _arg(act_scale, "act_scale", "f32", numel=1, device=d), _arg(xq, "xq", "u8", (m, k), device=d), stream=stream)
 
 
 def sq_fp8_gemm(xq, wq, act_scale, w_scale, y, acc_out=None, stream=None):
-    m, k = xq.shape
-    n = wq.shape[0]
-    _check("sq_fp8_gemm", load().sq_fp8_gemm(_dev(xq, "xq"), _dev(wq, "wq"), m, n, k, _dev(act_scale, "act_scale"),
-                                             _dev(w_scale, "w_scale"), _dev(y, "y"), _dtype_code(y),
-                                             _opt(acc_out, "acc_out"), _stream(stream)))
+    m, n, k, px, pw, pa, ps, py, pacc = _gemm_args(xq, wq, act_scale, w_scale, y, acc_out, "u8", "f32")
+    _call("sq_fp8_gemm", xq, px, pw, m, n, k, pa, ps, py, _dtype_code(y), pacc, stream=stream)

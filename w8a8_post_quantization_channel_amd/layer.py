@@ -29,6 +29,21 @@ from __future__ import annotations
 from . import capi
 
 
+def _fresh(shape, dtype, device, *streams):
+    """A new buffer for kernels that run on `streams`: torch's caching
+    allocator ties a block to the stream that allocated it, so the block is
+    also recorded on every other stream that reads or writes it; otherwise,
+    once the caller drops the tensor, the block could be handed to a new
+    allocation on the current stream while those kernels still use it."""
+    import torch
+    t = torch.empty(shape, dtype=dtype, device=device)
+    cur = torch.cuda.current_stream(device)
+    for s in streams:
+        if s is not None and s != cur:
+            t.record_stream(s)
+    return t
+
+
 class W8A8Linear:
     def __init__(self, w, alpha: float = 0.5, max_tokens: int = 0, out_dtype=None):
         import torch
@@ -63,7 +78,7 @@ class W8A8Linear:
         m = x.shape[0]
         if xq is None:
             xq = self.xq[:m] if self.xq is not None and self.xq.shape[0] >= m else \
-                torch.empty((m, self.k), dtype=torch.int8, device=x.device)
+                _fresh((m, self.k), torch.int8, x.device, stream)
         capi.sq_smooth_quant_act(x, self.inv_s, self.act_scale, xq, stream)
         return xq
 
@@ -72,7 +87,7 @@ class W8A8Linear:
         m = x.shape[0]
         if xq is None:
             xq = self.xq[:m] if self.xq is not None and self.xq.shape[0] >= m else \
-                torch.empty((m, self.k), dtype=torch.int8, device=x.device)
+                _fresh((m, self.k), torch.int8, x.device, stream)
         capi.sq_dynamic_quant_act(x, self.inv_s, self.live_max, self.dyn_scale, xq, stream)
         return xq
 
@@ -81,7 +96,7 @@ class W8A8Linear:
         m = xq.shape[0]
         if y is None:
             y = self.y[:m] if self.y is not None and self.y.shape[0] >= m else \
-                torch.empty((m, self.n), dtype=self.out_dtype, device=xq.device)
+                _fresh((m, self.n), self.out_dtype, xq.device, stream)
         a = self.act_scale if act_scale is None else act_scale
         capi.sq_w8a8_gemm(xq, self.wq, a, self.w_scale, y, acc_out, stream)
         return y
@@ -128,18 +143,18 @@ def forward_block(layers, xs, stream=None, gemm_stream=None, between=None):
     callable run between the two launches). Returns the outputs."""
     import torch
     xqs, ys = [], []
+    gs = gemm_stream if gemm_stream is not None else stream
     for l, x in zip(layers, xs):
         m = x.shape[0]
         xqs.append(l.xq[:m] if l.xq is not None and l.xq.shape[0] >= m else
-                   torch.empty((m, l.k), dtype=torch.int8, device=x.device))
+                   _fresh((m, l.k), torch.int8, x.device, stream, gs))
         ys.append(l.y[:m] if l.y is not None and l.y.shape[0] >= m else
-                  torch.empty((m, l.n), dtype=l.out_dtype, device=x.device))
+                  _fresh((m, l.n), l.out_dtype, x.device, gs))
     for part in _chunks(list(range(len(layers)))):
         capi.sq_smooth_quant_act_batched([xs[i] for i in part], [layers[i].inv_s for i in part],
                                          [layers[i].act_scale for i in part], [xqs[i] for i in part], stream)
     if between is not None:
         between()
-    gs = gemm_stream if gemm_stream is not None else stream
     # products in reverse order of preparation: the codes written last are the
     # ones still in the 256 MB Infinity Cache when the products start
     # (measured on the 13B block: the grouped launch 602 -> 591 us)
@@ -176,9 +191,9 @@ def forward_block_dynamic(layers, xs, stream=None):
     for l, x in zip(layers, xs):
         m = x.shape[0]
         xqs.append(l.xq[:m] if l.xq is not None and l.xq.shape[0] >= m else
-                   torch.empty((m, l.k), dtype=torch.int8, device=x.device))
+                   _fresh((m, l.k), torch.int8, x.device, stream))
         ys.append(l.y[:m] if l.y is not None and l.y.shape[0] >= m else
-                  torch.empty((m, l.n), dtype=l.out_dtype, device=x.device))
+                  _fresh((m, l.n), l.out_dtype, x.device, stream))
     for part in _chunks(list(range(len(layers)))):
         capi.sq_smooth_quant_act_batched([xs[i] for i in part], [layers[i].inv_s for i in part],
                                          [layers[i].dyn_scale for i in part], [xqs[i] for i in part], stream)

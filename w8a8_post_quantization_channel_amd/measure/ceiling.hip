@@ -1,11 +1,12 @@
-// ceiling.hip -- measured ceilings of MI355X for the roofline of the path:
+// ceiling.hip -- libsq_ceiling: measured ceilings of MI355X for the roofline
+// of the W8A8 path (a library of its own, beside libsq):
 // the int8 matrix-core rate of a loop that only issues MFMAs, and the HBM
 // rate of a copy that only streams 16-byte vectors. Neither touches the
 // method's data; they bound what the GEMM and the HBM passes can reach.
 #include <algorithm>
 
+#include "sq_ceiling.h"
 #include "sq_device.h"
-#include "sq_kernels.h"
 
 namespace {
 
@@ -123,7 +124,7 @@ int cus() {
 
 }  // namespace
 
-namespace sqk {
+namespace {
 
 hipError_t ceiling_mfma(int64_t iters, int blocks_per_cu, const void* operands, unsigned* sink, hipStream_t stream) {
     mfma_loop_kernel<<<dim3((unsigned)(blocks_per_cu * cus())), dim3(256), 0, stream>>>(iters, (const v4i*)operands,
@@ -163,4 +164,46 @@ hipError_t ceiling_read(const void* src, int64_t bytes, unsigned* sink, hipStrea
     return hipGetLastError();
 }
 
-}  // namespace sqk
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+sq_status hip_status(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+sq_status sq_ceiling_mfma(int64_t iters, int blocks_per_cu, const void* operands, uint32_t* sink, int64_t* ops,
+                          hipStream_t stream) {
+    if (!operands || !sink || !ops) return SQ_ERR_NULL;
+    if (iters < 1 || iters > ((int64_t)1 << 24) || blocks_per_cu < 1 || blocks_per_cu > 8) return SQ_ERR_SHAPE;
+    if (!aligned16(operands) || ((uintptr_t)sink & 3u) != 0) return SQ_ERR_ALIGN;
+    *ops = ceiling_mfma_ops(iters, blocks_per_cu);
+    return hip_status(ceiling_mfma(iters, blocks_per_cu, operands, sink, stream));
+}
+
+sq_status sq_ceiling_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+    if (bytes > 0 && (!src || !dst)) return SQ_ERR_NULL;
+    if (bytes < 0 || bytes % 16 != 0) return SQ_ERR_SHAPE;
+    if (bytes > 0 && (!aligned16(src) || !aligned16(dst))) return SQ_ERR_ALIGN;
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+    if (bytes > 0 && s0 < d0 + (uintptr_t)bytes && d0 < s0 + (uintptr_t)bytes) return SQ_ERR_SHAPE;
+    return hip_status(ceiling_copy(src, dst, bytes, stream));
+}
+
+sq_status sq_ceiling_narrow(const void* src, void* dst, int64_t src_bytes, hipStream_t stream) {
+    if (src_bytes > 0 && (!src || !dst)) return SQ_ERR_NULL;
+    if (src_bytes < 0 || src_bytes % 16 != 0) return SQ_ERR_SHAPE;
+    if (src_bytes > 0 && (!aligned16(src) || ((uintptr_t)dst & 7u) != 0)) return SQ_ERR_ALIGN;
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst, db = (uintptr_t)(src_bytes / 2);
+    if (src_bytes > 0 && s0 < d0 + db && d0 < s0 + (uintptr_t)src_bytes) return SQ_ERR_SHAPE;
+    return hip_status(ceiling_narrow(src, dst, src_bytes, stream));
+}
+
+sq_status sq_ceiling_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+    if (!sink || (bytes > 0 && !src)) return SQ_ERR_NULL;
+    if (bytes < 0 || bytes % 16 != 0) return SQ_ERR_SHAPE;
+    if ((bytes > 0 && !aligned16(src)) || ((uintptr_t)sink & 3u) != 0) return SQ_ERR_ALIGN;
+    return hip_status(ceiling_read(src, bytes, sink, stream));
+}
+
+}  // extern "C"

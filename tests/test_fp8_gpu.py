@@ -107,7 +107,9 @@ def test_quant_act_fp8_saturation_and_zeros():
 
 GEMM_CASES = [(300, 520, 1088, True), (1, 16, 64, False), (257, 272, 192, True), (2100, 4112, 256, True),
               (64, 4096, 1024, False), (513, 1000, 320, True), (1024, 8192, 256, True), (2048, 5120, 512, False),
-              (700, 2304, 2048, True)]
+              (700, 2304, 2048, True),
+              # the FP8 block step's launch shapes: 2048 tokens, K = 5120 and K = 13824
+              (2048, 5120, 5120, True), (2048, 5120, 13824, True), (2048, 13824, 5120, False)]
 
 
 @pytest.mark.parametrize("m,n,k,bf16_out", GEMM_CASES)

@@ -148,3 +148,92 @@ def test_alpha_search_full_size():
     assert all(np.isfinite(mse1)) and min(mse1) > 0
     assert best1 == int(np.argmin(mse1))
     assert mse1[best1] <= min(mse1[0], mse1[-1])
+
+
+# ---- full sizes as the workloads are configured ------------------------------------------
+
+def check_given_stat(g, act_max, w, x, rows, alpha=0.5):
+    """As check(), with the calibration statistic computed elsewhere (the
+    running max over streamed calibration chunks)."""
+    o = ORACLE
+    assert_bitexact("act_max", g["act_max"], act_max)
+    w_max = o.calib_absmax(w)
+    assert_bitexact("w_max", g["w_max"], w_max)
+    s, inv_s, a = o.smooth_factors(act_max, w_max, alpha)
+    assert_rel("s", g["s"], s, 1e-5)
+    assert_bitexact("act_scale", g["act_scale"], np.array([a], np.float32))
+    wq, ws = o.quant_weight(w, s)
+    assert_bitexact("w_scale", g["w_scale"], ws)
+    assert_bitexact("wq", g["wq"], wq)
+    xq = o.quant_act(x, inv_s, a)
+    assert_bitexact("xq", g["xq"], xq)
+    y = o.dequant(o.gemm_i32(np.ascontiguousarray(xq[rows]), wq), a, ws, bf16=True)
+    assert_bitexact("y", g["y"][rows], y)
+
+
+@pytest.mark.parametrize("shape_id", [0, 2])
+def test_llama13b_streamed_calibration(shape_id):
+    """The 13B prefill workload as configured: a 512 x 512-token calibration
+    set streamed as 16 chunks of 16384 rows through sq_calib_absmax with
+    accumulate = 1 (the running max of kwkr.cn blog §3.1 / ADR-010 add_batch),
+    then a separate 2048-token runtime batch (values past the calibrated
+    range saturate). q/k/v/o shape (5120 x 5120) and down (5120 x 13824)."""
+    import torch
+    d = dev()
+    w = synth.c2_weight(shape_id)
+    layer = W8A8Linear(synth.to_torch(w, d), alpha=0.5, max_tokens=synth.C2_TOKENS, out_dtype=torch.bfloat16)
+    ref_max = None
+    for c in range(16):
+        chunk = synth.c2_calib_chunk(shape_id, c)
+        layer.calibrate(synth.to_torch(chunk, d), accumulate=c > 0)
+        ref_max = ORACLE.calib_absmax(chunk, ref_max)
+        torch.cuda.synchronize()  # the chunk's device copy is released before the next is drawn
+    layer.prepare()
+    x = synth.c2_runtime_x(shape_id)
+    xq = layer.quantize_input(synth.to_torch(x, d))
+    y = layer.matmul(xq)
+    torch.cuda.synchronize()
+    g = {k: synth.from_torch(v) for k, v in dict(
+        act_max=layer.act_max, w_max=layer.w_max, s=layer.s, act_scale=layer.act_scale[:1], wq=layer.wq,
+        w_scale=layer.w_scale, xq=xq, y=y).items()}
+    check_given_stat(g, ref_max, w, x, sample_rows(x.shape[0], count=16, seed=10 + shape_id))
+
+
+def test_llama13b_block_step_as_benchmarked():
+    """bench.py's default step itself -- its inputs, its layers, its batched
+    statistics / smoothing / weight codes, the batched activation quantizer
+    and the grouped GEMM launch of all seven projections (256 x 160 tiles at
+    2048 tokens) -- checked against the oracle: every statistic, scale and
+    int8 tensor in full, each projection's bf16 output on sampled rows."""
+    import sys
+    import torch
+    import os
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    groups, projs = bench.setup(dev())
+    bench.run_step(groups, projs)
+    torch.cuda.synchronize()
+    o = ORACLE
+    act_max = {name: o.calib_absmax(g.x_host) for name, g in groups.items()}
+    for i, (name, g, layer, w_host) in enumerate(projs):
+        assert capi.sq_gemm_tiling(g.x_host.shape[0], layer.n) == (256, 160)
+        got = {k: synth.from_torch(v) for k, v in dict(
+            act_max=layer.act_max, w_max=layer.w_max, s=layer.s, act_scale=layer.act_scale[:1], wq=layer.wq,
+            w_scale=layer.w_scale, xq=layer.xq, y=layer.y).items()}
+        check_given_stat(got, act_max[g.name], w_host, g.x_host, sample_rows(g.x_host.shape[0], count=12, seed=i))
+
+
+def test_percentile_262144_rows():
+    """The nearest-rank 99.9 % statistic over 262144 rows (512 x 512 tokens)
+    of the 13B q/k/v input width, bit-exact against the oracle's sort."""
+    import torch
+    d = dev()
+    rows, k = 262144, 5120
+    x = synth.device_activations(2900, rows, k, synth.c2_outliers(0), d)
+    ws = torch.empty(capi.sq_calib_percentile_workspace(k), dtype=torch.uint8, device=d)
+    got = torch.empty(k, dtype=torch.float32, device=d)
+    capi.sq_calib_percentile(x, 0.999, ws, got)
+    torch.cuda.synchronize()
+    xh = synth.from_torch(x)
+    del x
+    assert_bitexact("percentile", synth.from_torch(got), ORACLE.calib_percentile(xh, 0.999))

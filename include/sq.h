@@ -52,6 +52,7 @@ typedef enum {
     SQ_ERR_WORKSPACE = 5, /* workspace missing or smaller than sq_alpha_search_workspace reports */
     SQ_ERR_HIP = 6,       /* a HIP launch or runtime call failed */
     SQ_ERR_ALIGN = 7,     /* a device pointer is not 16-byte aligned */
+    SQ_ERR_SCRATCH = 8,   /* the problem needs more than an allocation-free entry point's static scratch */
     /* range sentinels, never returned: any int passed to sq_status_string is a
      * value of the type, in C and in C++ alike */
     SQ_STATUS_RANGE_MIN_ = -2147483647 - 1,
@@ -206,6 +207,23 @@ sq_status sq_calib_percentile_workspace(sq_dtype xt, int64_t k, size_t* bytes);
 sq_status sq_calib_percentile(const void* x, sq_dtype xt, int64_t rows, int64_t k, double q,
                               void* workspace, size_t workspace_bytes, float* act_max,
                               hipStream_t stream);
+
+/*
+ * sq_calib_percentile without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Same arguments, rules and result as
+ * sq_calib_percentile; the scratch (the per-channel digit histograms, prefixes
+ * and ranks: sq_calib_percentile_workspace bytes) lives in a static device
+ * array of SQ_PERCENTILE_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends. Problems whose scratch exceeds it are rejected with
+ * SQ_ERR_SCRATCH before anything is launched (bf16 input: k <= 16320; fp32:
+ * k <= 8128). The call allocates nothing and clears the part of the array it
+ * uses with a kernel. Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (different streams, or host threads) race.
+ */
+#define SQ_PERCENTILE_SCRATCH_BYTES (32u << 20)
+sq_status sq_calib_percentile_noalloc(const void* x, sq_dtype xt, int64_t rows, int64_t k, double q,
+                                      float* act_max, hipStream_t stream);
 
 /*
  * RMSNorm, the norm in front of the projections of a Llama block; its weight

@@ -44,7 +44,7 @@ def test_measurement_probes_live_in_their_own_library(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         assert lib.sq_status_string(code)
     assert lib.sq_status_string(99) == b"unknown status"
 
@@ -628,3 +628,25 @@ def test_binding_rejects_mismatched_outputs_before_launch():
     # everything right, but host tensors: rejected at the GPU check, still before any launch
     e(lambda: capi.sq_w8a8_gemm(xq, wq, a, ws, y), "GPU")
     e(lambda: capi.sq_calib_absmax(x, torch.zeros(k)), "GPU")
+
+
+def test_percentile_noalloc_validation(lib):
+    """The allocation-free percentile: the percentile's argument rules, and
+    problems whose scratch exceeds the static array rejected before launch."""
+    f = lib.sq_calib_percentile_noalloc
+    assert f(None, 1, 1024, 1024, 0.999, P(A), None) == NULL
+    assert f(P(A), 1, 1024, 1024, 0.999, None, None) == NULL
+    assert f(P(A), 3, 1024, 1024, 0.999, P(A), None) == DTYPE
+    assert f(P(A), 1, 0, 1024, 0.999, P(A), None) == SHAPE
+    assert f(P(A), 1, 1024, 1000, 0.999, P(A), None) == SHAPE
+    assert f(P(A), 1, 1024, 1024, 1.5, P(A), None) == SHAPE
+    assert f(P(A), 1, 1024, 1024, float("nan"), P(A), None) == SHAPE
+    SCRATCH = 8
+    assert capi.SQ_PERCENTILE_SCRATCH_BYTES == 32 << 20
+    # the largest widths that fit (bf16: 2 digit passes, fp32: 4) and the next ones
+    for dt, kmax in ((1, 16320), (0, 8128)):
+        assert capi.sq_calib_percentile_workspace(kmax, dt) <= capi.SQ_PERCENTILE_SCRATCH_BYTES
+        assert capi.sq_calib_percentile_workspace(kmax + 64, dt) > capi.SQ_PERCENTILE_SCRATCH_BYTES
+        assert f(P(A), dt, 1024, kmax + 64, 0.999, P(A), None) == SCRATCH
+    assert f(P(MIS), 1, 1024, 1024, 0.999, P(A), None) == ALIGN
+    assert lib.sq_status_string(SCRATCH) != b"unknown status"

@@ -21,7 +21,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "sq.h")
 
 SQ_F32, SQ_BF16 = 0, 1
 STATUS = {0: "SQ_OK", 1: "SQ_ERR_NULL", 2: "SQ_ERR_SHAPE", 3: "SQ_ERR_DTYPE", 4: "SQ_ERR_ALPHA",
-          5: "SQ_ERR_WORKSPACE", 6: "SQ_ERR_HIP", 7: "SQ_ERR_ALIGN"}
+          5: "SQ_ERR_WORKSPACE", 6: "SQ_ERR_HIP", 7: "SQ_ERR_ALIGN", 8: "SQ_ERR_SCRATCH"}
+SQ_PERCENTILE_SCRATCH_BYTES = 32 << 20
 ALPHA_GRID = (0.25, 0.5, 0.75, 1.0)
 
 _lib = None
@@ -58,6 +59,7 @@ def _declare(lib):
         "sq_calib_mean_finalize": [P, i64, i64, P, P],
         "sq_calib_percentile_workspace": [c.c_int, i64, P],
         "sq_calib_percentile": [P, c.c_int, i64, i64, c.c_double, P, c.c_size_t, P, P],
+        "sq_calib_percentile_noalloc": [P, c.c_int, i64, i64, c.c_double, P, P],
         "sq_rmsnorm": [P, c.c_int, i64, i64, P, c.c_float, P, c.c_int, P, P],
         "sq_act_scale_fp8": [P, P, i64, P, P],
         "sq_quant_weight_fp8": [P, c.c_int, i64, i64, P, P, P, P],
@@ -502,6 +504,15 @@ def sq_calib_percentile(x, q: float, workspace, act_max, stream=None):
         raise ValueError("workspace must be contiguous")
     _call("sq_calib_percentile", x, px, _dtype_code(x), rows, k, float(q), ctypes.c_void_p(workspace.data_ptr()),
           workspace.numel() * workspace.element_size(), pa, stream=stream)
+
+
+def sq_calib_percentile_noalloc(x, q: float, act_max, stream=None):
+    """sq_calib_percentile with the library's static scratch (no workspace,
+    no allocation); calls that overlap on one GPU race."""
+    rows, k = _shape2(x, "x")
+    px, d = _arg(x, "x", "act"), x.device
+    _call("sq_calib_percentile_noalloc", x, px, _dtype_code(x), rows, k, float(q),
+          _arg(act_max, "act_max", "f32", (k,), device=d), stream=stream)
 
 
 # ---- FP8 (OCP E4M3) variant: codes are torch.uint8 tensors --------------------------

@@ -13,6 +13,8 @@
 // combine through LDS; one atomicMax per column per block merges blocks.
 #include <algorithm>
 
+#include <mutex>
+
 #include "sq_device.h"
 #include "sq_kernels.h"
 
@@ -617,7 +619,41 @@ hipError_t percentile_t(const void* x, int64_t rows, int64_t k, uint32_t rank0, 
 
 }  // namespace
 
+// ---- the percentile's scratch without allocation ----------------------------------
+//
+// For callers that cannot allocate, the histograms, prefixes and ranks live
+// in one file-scope device array. Its host-side name is a stand-in, not a
+// device address: every use goes through the address hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+namespace {
+
+constexpr size_t kPctScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint32_t scratch[kPctScratchBytes / 4];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
 namespace sqk {
+
+size_t percentile_scratch_bytes() { return kPctScratchBytes; }
+
+hipError_t percentile_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 size_t percentile_workspace(int xt, int64_t k) {
     const int passes = xt == kBF16 ? PctKey<2>::PASSES : PctKey<4>::PASSES;

@@ -140,6 +140,7 @@ const char* sq_status_string(sq_status status) {
         case SQ_ERR_WORKSPACE: return "workspace missing or too small";
         case SQ_ERR_HIP: return "HIP launch or runtime error";
         case SQ_ERR_ALIGN: return "device pointer not 16-byte aligned";
+        case SQ_ERR_SCRATCH: return "problem larger than the library's static scratch (allocation-free entry point)";
     }
     return "unknown status";
 }
@@ -464,6 +465,20 @@ sq_status sq_calib_percentile(const void* x, sq_dtype xt, int64_t rows, int64_t 
     int64_t rank = (int64_t)std::ceil(q * (double)rows);
     rank = rank < 1 ? 1 : (rank > rows ? rows : rank);
     return hip_status(sqk::percentile(x, xt, rows, k, rank, workspace, act_max, stream));
+}
+
+sq_status sq_calib_percentile_noalloc(const void* x, sq_dtype xt, int64_t rows, int64_t k, double q,
+                                      float* act_max, hipStream_t stream) {
+    if (!x || !act_max) return SQ_ERR_NULL;
+    if (!valid_dtype(xt)) return SQ_ERR_DTYPE;
+    if (rows < 1 || rows > INT32_MAX || !valid_k(k) || !std::isfinite(q) || q < 0.0 || q > 1.0) return SQ_ERR_SHAPE;
+    if (sqk::percentile_workspace(xt, k) > sqk::percentile_scratch_bytes()) return SQ_ERR_SCRATCH;
+    if (!aligned16(x) || !aligned16(act_max)) return SQ_ERR_ALIGN;
+    void* scratch = nullptr;
+    if (sqk::percentile_scratch(&scratch) != hipSuccess) return SQ_ERR_HIP;
+    int64_t rank = (int64_t)std::ceil(q * (double)rows);
+    rank = rank < 1 ? 1 : (rank > rows ? rows : rank);
+    return hip_status(sqk::percentile(x, xt, rows, k, rank, scratch, act_max, stream));
 }
 
 static bool valid_eps(float eps) { return std::isfinite(eps) && eps >= 0.0f; }

@@ -47,6 +47,10 @@ hipError_t mean_finalize(const double* sum, int64_t count, int64_t k, float* act
 size_t percentile_workspace(int xt, int64_t k);
 hipError_t percentile(const void* x, int xt, int64_t rows, int64_t k, int64_t rank, void* workspace,
                       float* act_max, hipStream_t stream);
+// the same scratch in a static device array of percentile_scratch_bytes()
+// (no allocation): its address on the current device
+size_t percentile_scratch_bytes();
+hipError_t percentile_scratch(void** ptr);
 
 // RMSNorm y = fl(fl(h * r) * gamma) (fp32 or bf16 out), r per row (optional out)
 hipError_t rmsnorm(const void* h, int ht, int64_t m, int64_t k, const float* gamma, float eps, void* y, int yt,

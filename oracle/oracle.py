@@ -76,6 +76,18 @@ def _declare(lib):
     lib.sqo_quant_act_fp8.argtypes = [P, c.c_int, i64, i64, P, c.c_float, P]
     lib.sqo_gemm_fp8.argtypes = [P, P, i64, i64, i64, c.c_float, P, c.c_int, P, P, P]
     lib.sqo_dequant_f32.argtypes = [P, i64, i64, c.c_float, P, c.c_int, P]
+    lib.sqo_f16_encode.argtypes = [c.c_float]
+    lib.sqo_f16_encode.restype = c.c_uint16
+    lib.sqo_f16_decode.argtypes = [c.c_uint16]
+    lib.sqo_f16_decode.restype = c.c_float
+    lib.sqo_scale_f16.argtypes = [c.c_float]
+    lib.sqo_scale_f16.restype = c.c_uint16
+    lib.sqo_f16_encode_array.argtypes = [P, i64, P]
+    lib.sqo_f16_decode_array.argtypes = [P, i64, P]
+    lib.sqo_smooth_factors_h.argtypes = [P, P, i64, c.c_double, P, P]
+    lib.sqo_quant_weight_h.argtypes = [P, c.c_int, i64, i64, P, P, P]
+    lib.sqo_quant_act_h.argtypes = [P, c.c_int, i64, i64, P, c.c_uint16, P]
+    lib.sqo_dequant_h.argtypes = [P, i64, i64, c.c_uint16, P, c.c_int, P]
     return lib
 
 
@@ -307,6 +319,68 @@ class Oracle:
         self.lib.sqo_dequant_f32(_ptr(acc), m, n, float(np.float32(act_scale)), _ptr(w_scale),
                                  BF16 if bf16 else F32, _ptr(y))
         return y
+
+    # O25: binary16 values as uint16 bit patterns
+    def f16_encode(self, v) -> np.ndarray:
+        v = np.ascontiguousarray(np.asarray(v, np.float32))
+        out = np.empty(v.shape, np.uint16)
+        self.lib.sqo_f16_encode_array(_ptr(v), v.size, _ptr(out))
+        return out
+
+    def f16_decode(self, h) -> np.ndarray:
+        h = np.ascontiguousarray(np.asarray(h, np.uint16))
+        out = np.empty(h.shape, np.float32)
+        self.lib.sqo_f16_decode_array(_ptr(h), h.size, _ptr(out))
+        return out
+
+    def scale_f16(self, v: float) -> np.uint16:
+        return np.uint16(self.lib.sqo_scale_f16(float(np.float32(v))))
+
+    # O26
+    def smooth_factors_h(self, act_max: np.ndarray, w_max: np.ndarray, alpha: float):
+        k = act_max.shape[0]
+        s16 = np.empty(k, np.uint16)
+        a16 = np.zeros(1, np.uint16)
+        self.lib.sqo_smooth_factors_h(_ptr(act_max), _ptr(w_max), k, float(alpha), _ptr(s16), _ptr(a16))
+        return s16, np.uint16(a16[0])
+
+    # O27
+    def quant_weight_h(self, w: np.ndarray, s16: np.ndarray):
+        n, k = w.shape
+        wq = np.empty((n, k), np.int8)
+        ws16 = np.empty(n, np.uint16)
+        self.lib.sqo_quant_weight_h(_ptr(w), _ftype(w), n, k, _ptr(s16), _ptr(wq), _ptr(ws16))
+        return wq, ws16
+
+    # O28
+    def quant_act_h(self, x: np.ndarray, s16: np.ndarray, act_scale16) -> np.ndarray:
+        m, k = x.shape
+        xq = np.empty((m, k), np.int8)
+        self.lib.sqo_quant_act_h(_ptr(x), _ftype(x), m, k, _ptr(s16), int(act_scale16), _ptr(xq))
+        return xq
+
+    # O29
+    def dequant_h(self, acc: np.ndarray, act_scale16, w_scale16: np.ndarray, bf16: bool = False) -> np.ndarray:
+        m, n = acc.shape
+        y = np.empty((m, n), np.uint16 if bf16 else np.float32)
+        self.lib.sqo_dequant_h(_ptr(np.ascontiguousarray(acc, np.int32)), m, n, int(act_scale16), _ptr(w_scale16),
+                               BF16 if bf16 else F32, _ptr(y))
+        return y
+
+    # the layer with fp16 scale storage (O26-O29) for one runtime input (helper for tests)
+    def layer_forward_h(self, x_calib_batches, w: np.ndarray, x: np.ndarray, alpha: float, bf16_out: bool = False):
+        k = w.shape[1]
+        act_max = np.zeros(k, np.float32)
+        for xc in x_calib_batches:
+            self.calib_absmax(xc, act_max)
+        w_max = self.calib_absmax(w)
+        s16, a16 = self.smooth_factors_h(act_max, w_max, alpha)
+        wq, ws16 = self.quant_weight_h(w, s16)
+        xq = self.quant_act_h(x, s16, a16)
+        acc = self.gemm_i32(xq, wq)
+        y = self.dequant_h(acc, a16, ws16, bf16=bf16_out)
+        return dict(act_max=act_max, w_max=w_max, s16=s16, act_scale16=a16, wq=wq, w_scale16=ws16, xq=xq,
+                    acc=acc, y=y)
 
     # the whole layer, O1..O10, for one runtime input (helper for tests)
     def layer_forward(self, x_calib_batches, w: np.ndarray, x: np.ndarray, alpha: float, bf16_out: bool = False):

@@ -493,3 +493,134 @@ void sqo_dequant_f32(const float* acc, int64_t m, int64_t n, float act_scale,
         }
     }
 }
+
+/* O25: IEEE binary16 -- the storage precision ADR-010 "Consequences" gives the
+ * per-row weight scale, the per-tensor activation scale and the per-channel
+ * smoothing factors (input_scales). Normal values (1 + m/1024) * 2^(E-15),
+ * E = 1..30; subnormals m * 2^-24; rounding to nearest, ties to even; past
+ * the largest finite value (65504) the rounding overflows to infinity. */
+uint16_t sqo_f16_encode(float v) {
+    uint16_t sign = signbit(v) ? 0x8000 : 0x0000;
+    float a = fabsf(v);
+    if (isnan(v)) return 0x7e00;
+    if (a == 0.0f) return sign;
+    if (isinf(a)) return sign | 0x7c00;
+    int e;
+    frexpf(a, &e);                       /* a = f * 2^e with f in [0.5, 1) */
+    int E = e - 1;                       /* a in [2^E, 2^(E+1)) */
+    if (E < -14) {                       /* below the smallest normal: steps of 2^-24 */
+        float q = rintf(ldexpf(a, 24));  /* exact scaling; rintf rounds half to even */
+        return sign | (uint16_t)q;       /* q = 1024 is the smallest normal, 0x0400 */
+    }
+    float q = rintf(ldexpf(a, 10 - E));  /* 1024 .. 2048: the significand in 1024ths */
+    if (q == 2048.0f) {
+        q = 1024.0f;
+        E += 1;
+    }
+    if (E > 15) return sign | 0x7c00;    /* overflow: infinity */
+    return sign | (uint16_t)(((E + 15) << 10) | ((int)q - 1024));
+}
+
+float sqo_f16_decode(uint16_t h) {
+    int ef = (h >> 10) & 0x1f, m = h & 0x3ff;
+    float mag;
+    if (ef == 31) mag = m ? NAN : INFINITY;
+    else if (ef == 0) mag = ldexpf((float)m, -24);
+    else mag = ldexpf(1.0f + (float)m / 1024.0f, ef - 15);
+    return (h & 0x8000) ? -mag : mag;
+}
+
+/* A scale as stored: positive, kept inside the finite positive range of
+ * binary16 ([2^-24, 65504]) so a stored scale is never 0 or infinite, then
+ * rounded to nearest even. */
+#define SQO_F16_MIN 5.9604644775390625e-08f /* 2^-24 */
+#define SQO_F16_MAX 65504.0f
+uint16_t sqo_scale_f16(float v) {
+    if (v < SQO_F16_MIN) v = SQO_F16_MIN;
+    if (v > SQO_F16_MAX) v = SQO_F16_MAX;
+    return sqo_f16_encode(v);
+}
+
+/* O26: O4 with the smoothing factors stored in fp16 (ADR-010: input_scales
+ * is an fp16 buffer, the forward divides by it); the reciprocal every later
+ * step uses is that of the stored value, and the closed-form activation scale
+ * (O6) is formed from it and then stored in fp16 too. */
+void sqo_smooth_factors_h(const float* act_max, const float* w_max, int64_t k,
+                          double alpha, uint16_t* s16, uint16_t* act_scale16) {
+    float mx = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+        float a = act_max[j] > SQO_FLOOR ? act_max[j] : SQO_FLOOR;
+        float w = w_max[j] > SQO_FLOOR ? w_max[j] : SQO_FLOOR;
+        float s = (float)(pow((double)a, alpha) / pow((double)w, 1.0 - alpha));
+        s16[j] = sqo_scale_f16(s);
+        float inv = 1.0f / sqo_f16_decode(s16[j]);
+        float v = a * inv;
+        if (v > mx) mx = v;
+    }
+    *act_scale16 = sqo_scale_f16(mx / SQO_QMAX);
+}
+
+/* O27: O7 with the stored fp16 s folded into W and the row scale stored in
+ * fp16; the codes use the reciprocal of the stored row scale. A stored scale
+ * may sit below the fp32 one (by up to 2^-11 relative for normal values,
+ * more in the subnormal range), so the codes are clamped to +-127. */
+void sqo_quant_weight_h(const void* w, int wtype, int64_t n, int64_t k,
+                        const uint16_t* s16, int8_t* wq, uint16_t* w_scale16) {
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < n; ++r) {
+        float* row = (float*)malloc((size_t)k * sizeof(float));
+        float mx = 0.0f;
+        for (int64_t j = 0; j < k; ++j) {
+            row[j] = elem(w, wtype, r * k + j) * sqo_f16_decode(s16[j]);
+            float v = fabsf(row[j]);
+            if (v > mx) mx = v;
+        }
+        w_scale16[r] = sqo_scale_f16((mx < SQO_FLOOR ? SQO_FLOOR : mx) / SQO_QMAX);
+        float inv_ws = 1.0f / sqo_f16_decode(w_scale16[r]);
+        for (int64_t j = 0; j < k; ++j) wq[r * k + j] = quantize_scaled(row[j] * inv_ws);
+        free(row);
+    }
+}
+
+/* O28: O8 with the stored scales: x times the reciprocal of the stored s_j,
+ * then times the reciprocal of the stored activation scale. */
+void sqo_quant_act_h(const void* x, int xtype, int64_t m, int64_t k,
+                     const uint16_t* s16, uint16_t act_scale16, int8_t* xq) {
+    float inv_a = 1.0f / sqo_f16_decode(act_scale16);
+    float* inv_s = (float*)malloc((size_t)k * sizeof(float));
+    for (int64_t j = 0; j < k; ++j) inv_s[j] = 1.0f / sqo_f16_decode(s16[j]);
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < m; ++r)
+        for (int64_t j = 0; j < k; ++j) xq[r * k + j] = quantize_scaled((elem(x, xtype, r * k + j) * inv_s[j]) * inv_a);
+    free(inv_s);
+}
+
+/* O29: O10 with the stored scales: c[n] = fl(act_scale * w_scale[n]) from the
+ * decoded fp16 values, y = fl(fl(acc) * c[n]). */
+void sqo_dequant_h(const int32_t* acc, int64_t m, int64_t n, uint16_t act_scale16,
+                   const uint16_t* w_scale16, int ytype, void* y) {
+    float a = sqo_f16_decode(act_scale16);
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < m; ++r) {
+        for (int64_t c = 0; c < n; ++c) {
+            float merged = a * sqo_f16_decode(w_scale16[c]);
+            float v = (float)acc[r * n + c] * merged;
+            if (ytype == SQO_BF16)
+                ((uint16_t*)y)[r * n + c] = float_to_bf16_rne(v);
+            else
+                ((float*)y)[r * n + c] = v;
+        }
+    }
+}
+
+/* O25 over arrays (the pins feed every binary16 value through it). */
+void sqo_f16_encode_array(const float* v, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = sqo_f16_encode(v[i]);
+}
+
+void sqo_f16_decode_array(const uint16_t* h, int64_t n, float* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = sqo_f16_decode(h[i]);
+}

@@ -173,6 +173,33 @@ void sqo_gemm_fp8(const uint8_t* xq, const uint8_t* wq, int64_t m, int64_t n,
 void sqo_dequant_f32(const float* acc, int64_t m, int64_t n, float act_scale,
                      const float* w_scale, int ytype, void* y);
 
+/* O25: IEEE binary16 encode (round to nearest even, overflow to infinity)
+ * and decode, for the fp16 scale storage of ADR-010 "Consequences";
+ * sqo_scale_f16 keeps a positive scale inside [2^-24, 65504] first. */
+uint16_t sqo_f16_encode(float v);
+float sqo_f16_decode(uint16_t h);
+uint16_t sqo_scale_f16(float v);
+void sqo_f16_encode_array(const float* v, int64_t n, uint16_t* out);
+void sqo_f16_decode_array(const uint16_t* h, int64_t n, float* out);
+
+/* O26: s16[j] = scale_f16(s_j) with s_j as O4; act_scale16 =
+ * scale_f16(fl(max_j fl(max(act_max[j],1e-5) * fl(1/dec(s16[j]))) / 127)). */
+void sqo_smooth_factors_h(const float* act_max, const float* w_max, int64_t k,
+                          double alpha, uint16_t* s16, uint16_t* act_scale16);
+
+/* O27: W' = fl(W * dec(s16)); w_scale16[r] = scale_f16(fl(max(max_j |W'|,
+ * 1e-5) / 127)); wq = clamp(rne(fl(W' * fl(1/dec(w_scale16[r])))), +-127). */
+void sqo_quant_weight_h(const void* w, int wtype, int64_t n, int64_t k,
+                        const uint16_t* s16, int8_t* wq, uint16_t* w_scale16);
+
+/* O28: xq = clamp(rne(fl(fl(x * fl(1/dec(s16[j]))) * fl(1/dec(act_scale16)))), +-127). */
+void sqo_quant_act_h(const void* x, int xtype, int64_t m, int64_t k,
+                     const uint16_t* s16, uint16_t act_scale16, int8_t* xq);
+
+/* O29: y = fl(fl(acc) * fl(dec(act_scale16) * dec(w_scale16[c]))), fp32 or bf16. */
+void sqo_dequant_h(const int32_t* acc, int64_t m, int64_t n, uint16_t act_scale16,
+                   const uint16_t* w_scale16, int ytype, void* y);
+
 #ifdef __cplusplus
 }
 #endif

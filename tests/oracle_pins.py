@@ -545,4 +545,110 @@ def pin_fp8_layer(o):
         assert np.array_equal(o.dequant_f32(ia.astype(np.float32), a, ws, bf16=bf), o.dequant(ia, a, ws, bf16=bf))
 
 
+# ---- O25-O29: fp16 scale storage (ADR-010 "Consequences") ------------------------------
+
+def pin_f16_codec(o):
+    """IEEE binary16 encode and decode against numpy's float16 (a round to
+    nearest even cast) on every finite value, every midpoint between
+    neighbouring values (ties to even), random values over the whole range,
+    the subnormal range, signed zeros and overflow; the scale store keeps a
+    positive scale inside [2^-24, 65504]."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float32)
+    fin = np.isfinite(ref)
+    dec = o.f16_decode(h)
+    assert np.array_equal(dec[fin].view(np.uint32), ref[fin].view(np.uint32))
+    assert np.all(np.isinf(dec[(h & 0x7fff) == 0x7c00])) and np.all(np.isnan(dec[~fin & ((h & 0x3ff) != 0)]))
+    pos = np.unique(ref[fin & (ref > 0)]).astype(np.float64)
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    g = synth.rng(251)
+    vals = np.concatenate([ref[fin], mids, -mids, g.uniform(-65504, 65504, 4000).astype(np.float32),
+                           g.uniform(-2.0 ** -13, 2.0 ** -13, 4000).astype(np.float32),
+                           np.exp(g.uniform(-30, 11, 4000)).astype(np.float32),
+                           np.array([0.0, -0.0, 65504.0, 65519.0, 65520.0, 1e6, -1e6, 2.0 ** -25,
+                                     3 * 2.0 ** -26, 2.0 ** -26], np.float32)])
+    with np.errstate(over="ignore"):
+        expect = vals.astype(np.float16).view(np.uint16)
+    assert np.array_equal(o.f16_encode(vals), expect)
+    assert o.scale_f16(1e9) == 0x7bff and o.scale_f16(65520.0) == 0x7bff
+    assert o.scale_f16(0.0) == 0x0001 and o.scale_f16(1e-12) == 0x0001
+    assert o.scale_f16(0.1) == np.float16(np.float32(0.1)).view(np.uint16)
+
+
+def _f16(a):
+    return np.asarray(a, np.float32).astype(np.float16).view(np.uint16)
+
+
+def pin_f16_scale_layer(o):
+    """The layer with its scales stored in fp16 (O26-O29) is the fp32 layer
+    fed the stored values: s16 is the fp16 rounding of O4's s; the activation
+    scale is O6's closed form taken from the stored s, then rounded; the
+    activation codes are O8's and the outputs O10's with the decoded stored
+    scales; each weight row's codes reconstruct W diag(s16) within half a step
+    of the stored row scale, the row's largest element coding to +-127; the
+    fp16 layer's error stays that of the fp32 layer and an order of magnitude
+    below unsmoothed W8A8 on outlier data."""
+    x, w, act_max, w_max = _c1_stats(o)
+    for alpha in (0.25, 0.5, 0.75):
+        s, inv_s, a = o.smooth_factors(act_max, w_max, alpha)
+        s16, a16 = o.smooth_factors_h(act_max, w_max, alpha)
+        assert np.array_equal(s16, _f16(s))
+        sd = o.f16_decode(s16)
+        inv16 = (np.float32(1.0) / sd).astype(np.float32)
+        assert a16 == _f16(o.act_scale(act_max, inv16))
+        ad = np.float32(o.f16_decode(np.array([a16]))[0])
+        assert np.array_equal(o.quant_act_h(x, s16, a16), o.quant_act(x, inv16, ad))
+        assert int(np.abs(o.quant_act_h(x, s16, a16).astype(np.int32)).max()) == 127
+        wq16, ws16 = o.quant_weight_h(w, s16)
+        wsd = o.f16_decode(ws16).astype(np.float64)
+        wp = w.astype(np.float64) * sd.astype(np.float64)[None, :]
+        rmax = np.abs(wp).max(axis=1)
+        assert np.all(np.abs(wsd * 127.0 / rmax - 1.0) <= 2.0 ** -11 + 2.0 ** -22)
+        err = np.abs(wp - wq16.astype(np.float64) * wsd[:, None])
+        assert np.all(err <= wsd[:, None] * (0.5 + 2e-5))
+        assert np.all(np.abs(wq16.astype(np.int32)).max(axis=1) == 127)
+        acc = o.gemm_i32(o.quant_act_h(x, s16, a16), wq16)
+        for bf in (False, True):
+            assert np.array_equal(o.dequant_h(acc, a16, ws16, bf16=bf),
+                                  o.dequant(acc, ad, o.f16_decode(ws16), bf16=bf))
+    # the closed form of the stored activation scale on many random statistics,
+    # where rounding s to fp16 moves the channel maximum across an fp16 step
+    g = synth.rng(256)
+    for _ in range(200):
+        kk = int(g.integers(1, 48))
+        am = np.exp(g.uniform(-3, 6, kk)).astype(np.float32)
+        wm = np.exp(g.uniform(-6, 1, kk)).astype(np.float32)
+        al = float(g.choice([0.25, 0.5, 0.6, 0.85]))
+        s16r, a16r = o.smooth_factors_h(am, wm, al)
+        inv16 = (np.float32(1.0) / o.f16_decode(s16r)).astype(np.float32)
+        assert a16r == _f16(o.act_scale(am, inv16))
+    # a row whose stored scale is subnormal in fp16 (rounded 1.9 % below the
+    # fp32 one) still codes within [-127, 127], its largest element to 127
+    wt = np.zeros((2, 64), np.float32)
+    wt[0, 3], wt[0, 9] = 1.0e-4, -0.5e-4
+    wt[1, 5] = 0.75
+    q, sc = o.quant_weight_h(wt, np.full(64, _f16(1.0), np.uint16))
+    assert sc[0] < 0x0400 and int(q[0, 3]) == 127 and int(np.abs(q.astype(np.int32)).max()) == 127
+    # extreme statistics keep every stored scale finite and nonzero
+    am = np.array([1e6, 1e-5, 3.0, 5e-5] * 16, np.float32)
+    wm = np.array([1e-5, 1e6, 0.1, 2e4] * 16, np.float32)
+    for alpha in (0.0, 1.0):
+        s16e, a16e = o.smooth_factors_h(am, wm, alpha)
+        d = o.f16_decode(np.append(s16e, a16e))
+        assert np.all(np.isfinite(d)) and np.all(d > 0)
+    # accuracy: the fp16-scale layer tracks the fp32-scale one on Llama-like outliers
+    g = synth.rng(252)
+    k, n = 1024, 256
+    out = synth.outlier_channels(253, k)
+    xc = synth.bf16_bits_to_f32(synth.activations(254, 256, k, out))
+    wl = synth.bf16_bits_to_f32(synth.weights(255, n, k))
+    exact = xc.astype(np.float64) @ wl.astype(np.float64).T
+    r16 = o.layer_forward_h([xc], wl, xc, 0.5)
+    r32 = o.layer_forward([xc], wl, xc, 0.5)
+    e16, e32 = rel_mse(r16["y"], exact), rel_mse(r32["y"], exact)
+    assert e16 <= 1.5 * e32
+    assert rel_mse(unsmoothed_forward(o, [xc], wl, xc), exact) >= 10 * e16
+    del g
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

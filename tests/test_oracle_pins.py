@@ -76,6 +76,21 @@ MUTANTS = {
     "dequant_f32_act_scale_only": ("float merged = w_scale[c] * act_scale;", "float merged = act_scale;"),
     "norm_quant_drops_r": ("float smoothed = (elem(h, htype, t * k + j) * r[t]) * gamma_folded[j];",
                            "float smoothed = elem(h, htype, t * k + j) * gamma_folded[j];"),
+    # fp16 scale storage (O25-O29)
+    "f16_truncates": ("float q = rintf(ldexpf(a, 10 - E));", "float q = truncf(ldexpf(a, 10 - E));"),
+    "f16_bias_16": ("return sign | (uint16_t)(((E + 15) << 10) | ((int)q - 1024));",
+                    "return sign | (uint16_t)(((E + 16) << 10) | ((int)q - 1024));"),
+    "f16_subnormal_step": ("float q = rintf(ldexpf(a, 24));", "float q = rintf(ldexpf(a, 23));"),
+    "f16_scale_no_floor": ("if (v < SQO_F16_MIN) v = SQO_F16_MIN;", ""),
+    "f16_scale_overflows": ("if (v > SQO_F16_MAX) v = SQO_F16_MAX;", ""),
+    "f16_act_scale_from_unrounded_s": ("float inv = 1.0f / sqo_f16_decode(s16[j]);", "float inv = 1.0f / s;"),
+    "f16_weight_codes_unrounded_scale": ("float inv_ws = 1.0f / sqo_f16_decode(w_scale16[r]);",
+                                         "float inv_ws = 1.0f / ((mx < SQO_FLOOR ? SQO_FLOOR : mx) / SQO_QMAX);"),
+    "f16_fold_reads_s_as_bf16": ("row[j] = elem(w, wtype, r * k + j) * sqo_f16_decode(s16[j]);",
+                                 "row[j] = elem(w, wtype, r * k + j) * bf16_bits_to_float(s16[j]);"),
+    "f16_act_codes_unrounded_act_scale": ("float inv_a = 1.0f / sqo_f16_decode(act_scale16);\n    float* inv_s",
+                                          "float inv_a = 1.0f / sqo_f16_decode(act_scale16 + 1);\n    float* inv_s"),
+    "f16_dequant_drops_weight_scale": ("float merged = a * sqo_f16_decode(w_scale16[c]);", "float merged = a;"),
 }
 
 

@@ -138,16 +138,31 @@ def test_alpha_search_c4_width():
 
 
 def test_alpha_search_full_size():
-    """8 batches x 2048 tokens, 4096 -> 11008: properties that hold at any
-    size (argmin, no worse than the grid's extremes, deterministic reruns)."""
+    """8 batches x 2048 tokens, 4096 -> 11008 (the alpha-search workload in
+    full): the four MSEs within 1e-4 of the oracle's and the same argmin. The
+    oracle's values were written once by tests/golden/make_c4_alpha_search.py
+    (oracle/ only, about 8 CPU-minutes) with a digest of the inputs, which
+    must match the inputs drawn here. Also: deterministic reruns, the argmin,
+    no worse than the grid's extremes."""
+    import hashlib
+    import json
+    import os
     xs = synth.c4_batches(8)
     w = synth.c4_weight()
+    gold = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                       "c4_alpha_search_oracle.json")))
+    h = hashlib.sha256()
+    for a in list(xs) + [w]:
+        h.update(str(a.shape).encode())
+        h.update(a.tobytes())
+    assert h.hexdigest() == gold["input_sha256"], "the input recipe changed: regenerate the golden file"
     mse1, best1 = gpu_alpha_search(xs, w)
     mse2, best2 = gpu_alpha_search(xs, w)
     assert mse1 == mse2 and best1 == best2  # fixed-order reductions
     assert all(np.isfinite(mse1)) and min(mse1) > 0
     assert best1 == int(np.argmin(mse1))
     assert mse1[best1] <= min(mse1[0], mse1[-1])
+    check_search(mse1, best1, [float.fromhex(v) for v in gold["mse_hex"]], gold["best"])
 
 
 # ---- full sizes as the workloads are configured ------------------------------------------

@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--traffic", type=str, default=None,
                     help="counter summary with the HBM bytes per GEMM launch (default: the committed "
                          "profiles/gemm_traffic__llama13b_prefill2048.md, used only if it matches gemm.hip)")
+    ap.add_argument("--scales", default="f32", choices=["f32", "f16"],
+                    help="scale storage of the layer13b step: fp32 (default), or every scale stored in fp16 "
+                         "(smoothing factors, activation scale, per-row weight scales; the _f16 entry points)")
     ap.add_argument("--workload", default="layer13b",
                     choices=["layer13b", "decode7b", "alpha_search", "prefill70b", "hbm_passes", "copy_probe",
                              "variants", "fp8", "ceilings", "c1"],
@@ -84,8 +87,9 @@ class Group:
         self.act_max = torch.zeros(x_host.shape[1], dtype=torch.float32, device=device)
 
 
-def setup(device):
-    """Draw the layer's inputs on the host, move them to HBM, build layers."""
+def setup(device, scales="f32"):
+    """Draw the layer's inputs on the host, move them to HBM, build layers
+    (scale storage `scales`: "f32" or "f16")."""
     import torch
     from w8a8_post_quantization_channel_amd import synth
     from w8a8_post_quantization_channel_amd.layer import W8A8Linear
@@ -94,7 +98,7 @@ def setup(device):
     for name, g, n, k, _ in synth.C2_PROJECTIONS:
         w_host = synth.c2_projection_w(name)
         layer = W8A8Linear(synth.to_torch(w_host, device), alpha=0.5, max_tokens=synth.C2_TOKENS,
-                           out_dtype=torch.bfloat16)
+                           out_dtype=torch.bfloat16, scales=scales)
         layer.act_max = groups[g].act_max  # projections that share an input share its statistic
         projs.append((name, groups[g], layer, w_host))
     torch.cuda.synchronize()
@@ -227,7 +231,7 @@ def gemm_ops(projs, m):
     return sum(2.0 * m * layer.n * layer.k for _, _, layer, _ in projs)
 
 
-def cpu_baseline(groups, projs, rows, one_thread_rows=32):
+def cpu_baseline(groups, projs, rows, one_thread_rows=32, scales="f32"):
     """The CPU oracle on a bounded sample of one step: every statistic and
     quantization pass in full, each GEMM on `rows` of the 2048 output rows;
     the full-step time is extrapolated linearly in GEMM rows. Run on all the
@@ -235,17 +239,17 @@ def cpu_baseline(groups, projs, rows, one_thread_rows=32):
     one_thread_rows rows)."""
     from oracle.oracle import Oracle
     o = Oracle()
-    out = oracle_step(o, groups, projs, rows)
+    out = oracle_step(o, groups, projs, rows, scales)
     threads = o.num_threads()
     o.set_num_threads(1)
-    one = oracle_step(o, groups, projs, one_thread_rows)
+    one = oracle_step(o, groups, projs, one_thread_rows, scales)
     o.set_num_threads(threads)
     out["cpu_model"] = cpu_model()
     out["one_thread"] = {"value": one["value"], "unit": "TOPS", "cores": 1, "sample": one["sample"]}
     return out
 
 
-def oracle_step(o, groups, projs, rows):
+def oracle_step(o, groups, projs, rows, scales="f32"):
     import numpy as np
     m = next(iter(groups.values())).x_host.shape[0]
     t_total = 0.0
@@ -258,12 +262,20 @@ def oracle_step(o, groups, projs, rows):
     for name, g, layer, w_host in projs:
         t0 = time.perf_counter()
         w_max = o.calib_absmax(w_host)
-        s, inv_s, a = o.smooth_factors(act_max[g.name], w_max, 0.5)
-        wq, ws = o.quant_weight(w_host, s)
-        xq = o.quant_act(g.x_host, inv_s, a)
+        if scales == "f16":
+            s16, a16 = o.smooth_factors_h(act_max[g.name], w_max, 0.5)
+            wq, ws16 = o.quant_weight_h(w_host, s16)
+            xq = o.quant_act_h(g.x_host, s16, a16)
+        else:
+            s, inv_s, a = o.smooth_factors(act_max[g.name], w_max, 0.5)
+            wq, ws = o.quant_weight(w_host, s)
+            xq = o.quant_act(g.x_host, inv_s, a)
         t1 = time.perf_counter()
         acc = o.gemm_i32(np.ascontiguousarray(xq[:rows]), wq)
-        o.dequant(acc, a, ws, bf16=True)
+        if scales == "f16":
+            o.dequant_h(acc, a16, ws16, bf16=True)
+        else:
+            o.dequant(acc, a, ws, bf16=True)
         t2 = time.perf_counter()
         t_total += (t1 - t0) + (t2 - t1) * (m / rows)
     wall = time.perf_counter() - wall0
@@ -1041,7 +1053,7 @@ def main():
         out["gpu"] = torch.cuda.get_device_name(0)
         print(json.dumps(out), flush=True)
         return
-    groups, projs = setup(device)
+    groups, projs = setup(device, args.scales)
     m = next(iter(groups.values())).x.shape[0]
     side = torch.cuda.Stream() if args.overlap else None  # default priority, like the main stream
 
@@ -1102,6 +1114,7 @@ def main():
                           "(q, k, v, o; gate, up, down), beside the other phase's preparation" if args.overlap else
                           "gemm_dma_grouped_kernel<OpI8, TN, bf16> (256 x 32*TN tiles), one launch for the 7 "
                           "projections",
+                "scale_storage": args.scales,
                 "tiling": {n: list(capi.sq_gemm_tiling(m, layer.n)) for n, _, layer, _ in projs},
                 "avg_launch_us": avg_launch_ms * 1e3,
                 "per_projection_tops": {n: ops_by_name[n] / (sum(v) / len(v) * 1e-3) / 1e12
@@ -1117,6 +1130,7 @@ def main():
                 "N(0,0.02) weights; bf16)",
         "config": {"workload": "llama2-13b decoder layer, 7 linear projections, 2048 prefill tokens",
                    "tokens": m, "alpha": 0.5, "in_dtype": "bf16", "out_dtype": "bf16",
+                   "scale_storage": "fp16 (every scale)" if args.scales == "f16" else "fp32",
                    "projections": {n: [layer.n, layer.k] for n, _, layer, _ in projs},
                    "step": "calib absmax + weight absmax + smoothing + weight quant + act quant + int8 GEMM",
                    "preparation": "per projection" if args.per_projection else
@@ -1130,7 +1144,7 @@ def main():
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(groups, projs, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(groups, projs, args.cpu_rows, scales=args.scales)
     print(json.dumps(out), flush=True)
 
 

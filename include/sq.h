@@ -5,7 +5,8 @@
  * Sources (cited by page and section):
  *   [kwkr]  the Chinese engineering blog on SmoothQuant W8A8 at kwkr.cn
  *           (sections 1.2, 2.1-2.3, 3.1-3.3)
- *   [ADR]   "010. SmoothQuant Integration", blog.yoooo.fun (Context, Key design)
+ *   [ADR]   "010. SmoothQuant Integration", blog.yoooo.fun (Context, Decision,
+ *           Key design, Consequences)
  *   [pwwt]  "SmoothQuant技术解析：LLM模型INT8无损量化实践", pwwt.cn (§3.1 kernel stub)
  *   [tbr8]  tbr8.org, activation outliers and SmoothQuant (PyTorch example);
  *   [pwwt §2.3] static and dynamic scale modes on the same pwwt.cn page
@@ -436,6 +437,65 @@ sq_status sq_w8a8_gemm_batched(int count, const int8_t* const* xq, const int8_t*
                                const float* const* act_scale, const float* const* w_scale,
                                void* const* y, const sq_dtype* yt, int32_t* const* acc_out,
                                hipStream_t stream);
+
+/*
+ * fp16 scale storage [ADR "Consequences": per-row weight scale, per-tensor act
+ * scale and input_scales kept in fp16; "Decision / Layer 1": input_scales is
+ * an fp16 buffer]. The int8 layer with every scale it keeps stored as IEEE
+ * binary16 bit patterns (uint16_t arrays): each step is the fp32 entry point
+ * fed the DECODED stored values, and every stored scale is
+ *   f16(v) = binary16 round-to-nearest-even of fp32 v clamped to [2^-24, 65504]
+ * (never zero, never infinite). dec() is the exact decode to fp32.
+ *   sq_smooth_factors_f16:   s[j] = f16(s_j), s_j the fp32 factor of
+ *                            sq_smooth_factors; no inv_s is stored: its users form
+ *                            inv_j = fp32(1 / dec(s[j])) themselves;
+ *                            act_scale[0] = f16(fp32(max_j fp32(a_j * inv_j) / 127)).
+ *   sq_quant_weight_f16:     W'[r,j] = fp32(W[r,j] * dec(s[j]));
+ *                            w_scale[r] = f16(fp32(max(max_j |W'[r,j]|, 1e-5) / 127));
+ *                            wq[r,j] = clamp(rne(fp32(W'[r,j] * fp32(1/dec(w_scale[r])))), +-127)
+ *                            (the stored scale can sit below the fp32 one, so the
+ *                            clamp can act).
+ *   sq_smooth_quant_act_f16: xq[r,j] = clamp(rne(fp32(fp32(x[r,j] * inv_j) *
+ *                            fp32(1/dec(act_scale[0])))), +-127).
+ *   sq_w8a8_gemm_f16:        y[r,c] = fp32(fp32(acc[r,c]) * fp32(dec(act_scale[0]) *
+ *                            dec(w_scale[c]))), acc and acc_out as sq_w8a8_gemm.
+ * Batched forms: each item exactly as the single call, with the grouping,
+ * launch counts and overlap rule of the fp32 batched forms. Shapes, alignment
+ * (16 bytes, also for the uint16_t arrays) and errors as for the fp32 entry
+ * points; s and act_scale are outputs of sq_smooth_factors_f16 (act_scale one
+ * binary16 value in a 16-byte aligned slot).
+ */
+sq_status sq_smooth_factors_f16(const float* act_max, const float* w_max, int64_t k,
+                                float alpha, uint16_t* s, uint16_t* act_scale,
+                                hipStream_t stream);
+sq_status sq_quant_weight_f16(const void* w, sq_dtype wt, int64_t n, int64_t k,
+                              const uint16_t* s, int8_t* wq, uint16_t* w_scale,
+                              hipStream_t stream);
+sq_status sq_smooth_quant_act_f16(const void* x, sq_dtype xt, int64_t m, int64_t k,
+                                  const uint16_t* s, const uint16_t* act_scale,
+                                  int8_t* xq, hipStream_t stream);
+sq_status sq_w8a8_gemm_f16(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n,
+                           int64_t k, const uint16_t* act_scale, const uint16_t* w_scale,
+                           void* y, sq_dtype yt, int32_t* acc_out, hipStream_t stream);
+sq_status sq_smooth_factors_f16_batched(int count, const float* const* act_max,
+                                        const float* const* w_max, const int64_t* k,
+                                        const float* alpha, uint16_t* const* s,
+                                        uint16_t* const* act_scale, hipStream_t stream);
+sq_status sq_quant_weight_f16_batched(int count, const void* const* w, const sq_dtype* wt,
+                                      const int64_t* n, const int64_t* k,
+                                      const uint16_t* const* s, int8_t* const* wq,
+                                      uint16_t* const* w_scale, hipStream_t stream);
+sq_status sq_smooth_quant_act_f16_batched(int count, const void* const* x, const sq_dtype* xt,
+                                          const int64_t* m, const int64_t* k,
+                                          const uint16_t* const* s,
+                                          const uint16_t* const* act_scale, int8_t* const* xq,
+                                          hipStream_t stream);
+sq_status sq_w8a8_gemm_f16_batched(int count, const int8_t* const* xq, const int8_t* const* wq,
+                                   const int64_t* m, const int64_t* n, const int64_t* k,
+                                   const uint16_t* const* act_scale,
+                                   const uint16_t* const* w_scale, void* const* y,
+                                   const sq_dtype* yt, int32_t* const* acc_out,
+                                   hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* sq_status_string(sq_status status);

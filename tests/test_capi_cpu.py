@@ -517,6 +517,66 @@ def test_fp8_batched_validation(lib):
                                    ptrs(y0, w0), I(1, 1), None, None) == SHAPE
 
 
+def test_f16_scale_validation(lib):
+    """The fp16-scale entry points: the fp32 forms' checks; smoothing writes
+    no inv_s (none is taken); the overlap rule counts 2-byte scales."""
+    names = ("sq_smooth_factors_f16", "sq_quant_weight_f16", "sq_smooth_quant_act_f16", "sq_w8a8_gemm_f16",
+             "sq_smooth_factors_f16_batched", "sq_quant_weight_f16_batched", "sq_smooth_quant_act_f16_batched",
+             "sq_w8a8_gemm_f16_batched")
+    for name in names:
+        assert name in capi.declared_functions() and hasattr(lib, name)
+    sf = lib.sq_smooth_factors_f16
+    assert sf(P(A), P(A), 1024, 0.5, None, P(A), None) == NULL
+    assert sf(P(A), P(A), 1024, 0.5, P(A), None, None) == NULL
+    assert sf(P(A), P(A), 1000, 0.5, P(A), P(A), None) == SHAPE
+    assert sf(P(A), P(A), 1024, 1.5, P(A), P(A), None) == ALPHA
+    assert sf(P(A), P(A), 1024, float("nan"), P(A), P(A), None) == ALPHA
+    assert sf(P(A), P(A), 1024, 0.5, P(A), P(MIS), None) == ALIGN
+    f = lib.sq_quant_weight_f16
+    assert f(P(A), 1, 8, 1024, None, P(A), P(A), None) == NULL
+    assert f(P(A), 4, 8, 1024, P(A), P(A), P(A), None) == DTYPE
+    assert f(P(A), 1, 8, 1056, P(A), P(A), P(A), None) == SHAPE
+    assert f(P(A), 1, -1, 1024, P(A), P(A), P(A), None) == SHAPE
+    assert f(P(A), 1, 8, 1024, P(A), P(A), P(MIS), None) == ALIGN
+    assert f(None, 1, 0, 1024, P(A), None, None, None) == OK
+    g = lib.sq_smooth_quant_act_f16
+    assert g(P(A), 1, 8, 1024, P(A), None, P(A), None) == NULL
+    assert g(P(A), 1, 8, 1024, P(MIS), P(A), P(A), None) == ALIGN
+    assert g(None, 1, 0, 1024, P(A), P(A), None, None) == OK
+    h = lib.sq_w8a8_gemm_f16
+    base = [P(A), P(A), 16, 32, 1024, P(A), P(A), P(A), 1, None, None]
+    for idx, val, want in ((5, None, NULL), (4, 131072 + 64, SHAPE), (8, 5, DTYPE), (6, P(MIS), ALIGN),
+                           (3, 0, OK)):
+        a = list(base)
+        a[idx] = val
+        assert h(*a) == want, (idx, val)
+    PP = ctypes.c_void_p * 2
+    I64 = ctypes.c_int64 * 2
+    F = ctypes.c_float * 2
+    I = ctypes.c_int * 2
+    a, b = A, A + 0x100000
+    k = I64(1024, 1024)
+    assert lib.sq_smooth_factors_f16_batched(2, PP(a, b), PP(a, b), k, F(0.5, 0.5), None, PP(a, b), None) == NULL
+    assert lib.sq_smooth_factors_f16_batched(17, PP(a, b), PP(a, b), k, F(0.5, 0.5), PP(a, b), PP(a, b),
+                                             None) == SHAPE
+    assert lib.sq_smooth_factors_f16_batched(2, PP(a, b), PP(a, b), k, F(0.5, -0.5), PP(a, b), PP(a, b),
+                                             None) == ALPHA
+    # s of item 1 (2 KB of binary16) starting 1 KB into s of item 0: overlap
+    assert lib.sq_smooth_factors_f16_batched(2, PP(A, A + 0x4000), PP(A + 0x8000, A + 0xc000), k, F(0.5, 0.5),
+                                             PP(A + 0x10000, A + 0x10400), PP(A + 0x20000, A + 0x20010),
+                                             None) == SHAPE
+    # the same 2 KB apart: no overlap -- rejected only by a bad alpha, so no launch
+    assert lib.sq_smooth_factors_f16_batched(2, PP(A, A + 0x4000), PP(A + 0x8000, A + 0xc000), k, F(0.5, 2.0),
+                                             PP(A + 0x10000, A + 0x10800), PP(A + 0x20000, A + 0x20010),
+                                             None) == ALPHA
+    assert lib.sq_quant_weight_f16_batched(2, PP(a, b), I(1, 7), I64(8, 8), k, PP(a, b), PP(a, b), PP(a, b),
+                                           None) == DTYPE
+    assert lib.sq_smooth_quant_act_f16_batched(2, PP(a, b), I(1, 1), I64(8, 8), I64(1024, 1000), PP(a, b),
+                                               PP(a, b), PP(a, b), None) == SHAPE
+    assert lib.sq_w8a8_gemm_f16_batched(2, PP(a, b), PP(a, b), I64(8, 8), I64(16, 16), k, PP(a, b), PP(a, b),
+                                        PP(a + 4, b), I(1, 1), None, None) == ALIGN
+
+
 def test_ceiling_validation(lib):
     lib = ceiling.load()
     for name in ("sq_ceiling_mfma", "sq_ceiling_copy", "sq_ceiling_read", "sq_ceiling_narrow"):
@@ -612,6 +672,25 @@ def test_binding_rejects_mismatched_outputs_before_launch():
     e(lambda: capi.sq_fp8_gemm(xq, wq, a, ws, y), "xq", "dtype")
     e(lambda: capi.sq_fp8_gemm(xq8, wq8, a, ws, y, torch.zeros(m, n, dtype=i32)), "acc_out", "dtype")
     e(lambda: capi.sq_quant_weight_fp8(x, torch.ones(k), torch.zeros(m, k, dtype=i8), torch.ones(m)), "wq")
+    # fp16 scale storage: every scale a float16 tensor
+    f16 = torch.float16
+    s16, a16, ws16 = torch.ones(k, dtype=f16), torch.ones(4, dtype=f16), torch.ones(n, dtype=f16)
+    e(lambda: capi.sq_smooth_factors_f16(torch.ones(k), torch.ones(k), 0.5, torch.ones(k), a16), "s", "dtype")
+    e(lambda: capi.sq_smooth_factors_f16(torch.ones(k), torch.ones(k), 0.5, s16, torch.ones(0, dtype=f16)),
+      "act_scale", "elements")
+    e(lambda: capi.sq_quant_weight_f16(x, torch.ones(k), torch.zeros(m, k, dtype=i8), torch.ones(m, dtype=f16)),
+      "s", "dtype")
+    e(lambda: capi.sq_quant_weight_f16(x, s16, torch.zeros(m, k, dtype=i8), torch.ones(m)), "w_scale", "dtype")
+    e(lambda: capi.sq_smooth_quant_act_f16(x, s16, a, xq), "act_scale", "dtype")
+    e(lambda: capi.sq_w8a8_gemm_f16(xq, wq, a16, ws, y), "w_scale", "dtype")
+    e(lambda: capi.sq_w8a8_gemm_f16(xq, wq, a16, torch.ones(n - 1, dtype=f16), y), "w_scale", "shape")
+    e(lambda: capi.sq_w8a8_gemm_f16_batched([xq], [wq], [a], [ws16], [y]), "act_scale[0]", "dtype")
+    e(lambda: capi.sq_smooth_quant_act_f16_batched([x], [torch.ones(k)], [a16], [xq]), "inv_ss[0]", "dtype")
+    e(lambda: capi.sq_quant_weight_f16_batched([x], [s16], [torch.zeros(m, k, dtype=i8)], [torch.ones(m)]),
+      "w_scales[0]", "dtype")
+    e(lambda: capi.sq_smooth_factors_f16_batched([torch.ones(k)], [torch.ones(k)], [0.5], [torch.ones(k)], [a16]),
+      "ss[0]", "dtype")
+    e(lambda: capi.sq_w8a8_gemm_f16(xq, wq, a16, ws16, y), "GPU")
     # batched forms name the item
     e(lambda: capi.sq_w8a8_gemm_batched([xq, xq], [wq, wq], [a, a], [ws, ws], [y, torch.zeros(m, n + 1, dtype=bf)]),
       "y[1]", "shape")

@@ -78,6 +78,14 @@ def _declare(lib):
         "sq_quant_weight_fp8_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_smooth_quant_act_fp8_batched": [c.c_int, P, P, P, P, P, P, P, P],
         "sq_fp8_gemm_batched": [c.c_int, P, P, P, P, P, P, P, P, P, P, P],
+        "sq_smooth_factors_f16": [P, P, i64, c.c_float, P, P, P],
+        "sq_quant_weight_f16": [P, c.c_int, i64, i64, P, P, P, P],
+        "sq_smooth_quant_act_f16": [P, c.c_int, i64, i64, P, P, P, P],
+        "sq_w8a8_gemm_f16": [P, P, i64, i64, i64, P, P, P, c.c_int, P, P],
+        "sq_smooth_factors_f16_batched": [c.c_int, P, P, P, P, P, P, P],
+        "sq_quant_weight_f16_batched": [c.c_int, P, P, P, P, P, P, P, P],
+        "sq_smooth_quant_act_f16_batched": [c.c_int, P, P, P, P, P, P, P, P],
+        "sq_w8a8_gemm_f16_batched": [c.c_int, P, P, P, P, P, P, P, P, P, P, P],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -124,7 +132,14 @@ def _dev(t, what: str):
 def _dtypes(name: str):
     import torch
     return {"f32": (torch.float32,), "bf16": (torch.bfloat16,), "act": (torch.float32, torch.bfloat16),
-            "i8": (torch.int8,), "u8": (torch.uint8,), "i32": (torch.int32,), "f64": (torch.float64,)}[name]
+            "i8": (torch.int8,), "u8": (torch.uint8,), "i32": (torch.int32,), "f64": (torch.float64,),
+            "f16": (torch.float16,)}[name]
+
+
+def _sdt(name: str) -> str:
+    """Scale storage of a batched entry point: binary16 for the _f16 forms
+    (torch.float16 tensors hold the bit patterns), fp32 otherwise."""
+    return "f16" if "_f16" in name else "f32"
 
 
 def _arg(t, what: str, dtype: str, shape=None, numel: int | None = None, device=None):
@@ -202,24 +217,56 @@ def sq_smooth_quant_act(x, inv_s, act_scale, xq, stream=None):
         _arg(act_scale, "act_scale", "f32", numel=1, device=d), _arg(xq, "xq", "i8", (m, k), device=d), stream=stream)
 
 
-def _gemm_args(xq, wq, act_scale, w_scale, y, acc_out, code: str, acc_code: str, tag: str = ""):
+def _gemm_args(xq, wq, act_scale, w_scale, y, acc_out, code: str, acc_code: str, tag: str = "", sdt: str = "f32"):
     """Pointers and sizes of one product: xq [m,k], wq [n,k] (same code type),
-    act_scale [>=1], w_scale [n] fp32, y [m,n] fp32/bf16, acc_out [m,n] or None
-    (`tag` names the item of a batched call in error messages)."""
+    act_scale [>=1], w_scale [n] (fp32, or float16 for sdt "f16"), y [m,n]
+    fp32/bf16, acc_out [m,n] or None (`tag` names the item of a batched call in
+    error messages)."""
     m, k = _shape2(xq, f"xq{tag}")
     n, kw = _shape2(wq, f"wq{tag}")
     if kw != k:
         raise ValueError(f"wq{tag}: shape {tuple(wq.shape)} does not share k = {k} with xq{tag}")
     d = xq.device
     return (m, n, k, _arg(xq, f"xq{tag}", code), _arg(wq, f"wq{tag}", code, device=d),
-            _arg(act_scale, f"act_scale{tag}", "f32", numel=1, device=d),
-            _arg(w_scale, f"w_scale{tag}", "f32", (n,), device=d), _arg(y, f"y{tag}", "act", (m, n), device=d),
+            _arg(act_scale, f"act_scale{tag}", sdt, numel=1, device=d),
+            _arg(w_scale, f"w_scale{tag}", sdt, (n,), device=d), _arg(y, f"y{tag}", "act", (m, n), device=d),
             _arg(acc_out, f"acc_out{tag}", acc_code, (m, n), device=d) if acc_out is not None else ctypes.c_void_p(0))
 
 
 def sq_w8a8_gemm(xq, wq, act_scale, w_scale, y, acc_out=None, stream=None):
     m, n, k, px, pw, pa, ps, py, pacc = _gemm_args(xq, wq, act_scale, w_scale, y, acc_out, "i8", "i32")
     _call("sq_w8a8_gemm", xq, px, pw, m, n, k, pa, ps, py, _dtype_code(y), pacc, stream=stream)
+
+
+# ---- fp16 scale storage: every scale a torch.float16 tensor (binary16) ----------
+
+def sq_smooth_factors_f16(act_max, w_max, alpha: float, s, act_scale, stream=None):
+    """s = f16(fp32 s_j); act_scale = f16(closed form from the stored s)."""
+    k = act_max.shape[0]
+    d = act_max.device
+    _call("sq_smooth_factors_f16", act_max, _arg(act_max, "act_max", "f32", (k,)),
+          _arg(w_max, "w_max", "f32", (k,), device=d), k, float(alpha), _arg(s, "s", "f16", (k,), device=d),
+          _arg(act_scale, "act_scale", "f16", numel=1, device=d), stream=stream)
+
+
+def sq_quant_weight_f16(w, s, wq, w_scale, stream=None):
+    n, k = _shape2(w, "w")
+    pw, d = _arg(w, "w", "act"), w.device
+    _call("sq_quant_weight_f16", w, pw, _dtype_code(w), n, k, _arg(s, "s", "f16", (k,), device=d),
+          _arg(wq, "wq", "i8", (n, k), device=d), _arg(w_scale, "w_scale", "f16", (n,), device=d), stream=stream)
+
+
+def sq_smooth_quant_act_f16(x, s, act_scale, xq, stream=None):
+    m, k = _shape2(x, "x")
+    px, d = _arg(x, "x", "act"), x.device
+    _call("sq_smooth_quant_act_f16", x, px, _dtype_code(x), m, k, _arg(s, "s", "f16", (k,), device=d),
+          _arg(act_scale, "act_scale", "f16", numel=1, device=d), _arg(xq, "xq", "i8", (m, k), device=d),
+          stream=stream)
+
+
+def sq_w8a8_gemm_f16(xq, wq, act_scale, w_scale, y, acc_out=None, stream=None):
+    m, n, k, px, pw, pa, ps, py, pacc = _gemm_args(xq, wq, act_scale, w_scale, y, acc_out, "i8", "i32", sdt="f16")
+    _call("sq_w8a8_gemm_f16", xq, px, pw, m, n, k, pa, ps, py, _dtype_code(y), pacc, stream=stream)
 
 
 SQ_MAX_NORM_CONSUMERS = 4
@@ -357,18 +404,29 @@ def sq_calib_absmax_batched(xs, absmaxes, accumulate: bool = False, stream=None)
 
 def sq_smooth_factors_batched(act_maxes, w_maxes, alphas, ss, inv_ss, act_scales, stream=None,
                               _name="sq_smooth_factors_batched"):
-    """sq_smooth_factors for several projections in two launches."""
+    """sq_smooth_factors for several projections in two launches (the _f16
+    form stores no inv_s: pass inv_ss=None)."""
     count = _items(len(act_maxes), "act_maxes")
-    if not all(len(v) == count for v in (w_maxes, alphas, ss, inv_ss, act_scales)):
+    sdt = _sdt(_name)
+    if (inv_ss is None) != (sdt == "f16"):
+        raise ValueError("inv_ss is written by the fp32 forms only")
+    if not all(len(v) == count for v in (w_maxes, alphas, ss, act_scales) + ((inv_ss,) if inv_ss is not None else ())):
         raise ValueError("per-item lists differ in length")
     ks = [t.shape[0] for t in act_maxes]
     d = act_maxes[0].device if count else None
     kk = lambda i: (ks[i],)  # noqa: E731
     keep = [_ptrs(act_maxes, "act_maxes", "f32", kk, d), _ptrs(w_maxes, "w_maxes", "f32", kk, d),
             _host_array(ctypes.c_int64, ks),
-            _host_array(ctypes.c_float, [float(a) for a in alphas]), _ptrs(ss, "ss", "f32", kk, d),
-            _ptrs(inv_ss, "inv_ss", "f32", kk, d), _ptrs(act_scales, "act_scales", "f32", None, d, numel=1)]
+            _host_array(ctypes.c_float, [float(a) for a in alphas]), _ptrs(ss, "ss", sdt, kk, d)]
+    if inv_ss is not None:
+        keep.append(_ptrs(inv_ss, "inv_ss", "f32", kk, d))
+    keep.append(_ptrs(act_scales, "act_scales", sdt, None, d, numel=1))
     _call(_name, act_maxes[0], count, *[a for _, a in keep], stream=stream)
+
+
+def sq_smooth_factors_f16_batched(act_maxes, w_maxes, alphas, ss, act_scales, stream=None):
+    sq_smooth_factors_batched(act_maxes, w_maxes, alphas, ss, None, act_scales, stream,
+                              _name="sq_smooth_factors_f16_batched")
 
 
 def sq_quant_weight_batched(ws, ss, wqs, w_scales, stream=None, _name="sq_quant_weight_batched"):
@@ -378,12 +436,16 @@ def sq_quant_weight_batched(ws, ss, wqs, w_scales, stream=None, _name="sq_quant_
         raise ValueError("per-item lists differ in length")
     shp = [_shape2(w, f"ws[{i}]") for i, w in enumerate(ws)]
     d = ws[0].device if count else None
-    code = "u8" if "fp8" in _name else "i8"
+    code, sdt = "u8" if "fp8" in _name else "i8", _sdt(_name)
     keep = [_ptrs(ws, "ws", "act", None, d), _host_array(ctypes.c_int, [_dtype_code(w) for w in ws]),
             _host_array(ctypes.c_int64, [n for n, _ in shp]), _host_array(ctypes.c_int64, [k for _, k in shp]),
-            _ptrs(ss, "ss", "f32", lambda i: (shp[i][1],), d), _ptrs(wqs, "wqs", code, lambda i: shp[i], d),
-            _ptrs(w_scales, "w_scales", "f32", lambda i: (shp[i][0],), d)]
+            _ptrs(ss, "ss", sdt, lambda i: (shp[i][1],), d), _ptrs(wqs, "wqs", code, lambda i: shp[i], d),
+            _ptrs(w_scales, "w_scales", sdt, lambda i: (shp[i][0],), d)]
     _call(_name, ws[0], count, *[a for _, a in keep], stream=stream)
+
+
+def sq_quant_weight_f16_batched(ws, ss, wqs, w_scales, stream=None):
+    sq_quant_weight_batched(ws, ss, wqs, w_scales, stream, _name="sq_quant_weight_f16_batched")
 
 
 def sq_smooth_quant_act_batched(xs, inv_ss, act_scales, xqs, stream=None, _name="sq_smooth_quant_act_batched"):
@@ -394,12 +456,17 @@ def sq_smooth_quant_act_batched(xs, inv_ss, act_scales, xqs, stream=None, _name=
         raise ValueError("per-item lists differ in length")
     shp = [_shape2(x, f"xs[{i}]") for i, x in enumerate(xs)]
     d = xs[0].device if count else None
-    code = "u8" if "fp8" in _name else "i8"
+    code, sdt = "u8" if "fp8" in _name else "i8", _sdt(_name)
     keep = [_ptrs(xs, "xs", "act", None, d), _host_array(ctypes.c_int, [_dtype_code(x) for x in xs]),
             _host_array(ctypes.c_int64, [m for m, _ in shp]), _host_array(ctypes.c_int64, [k for _, k in shp]),
-            _ptrs(inv_ss, "inv_ss", "f32", lambda i: (shp[i][1],), d),
-            _ptrs(act_scales, "act_scales", "f32", None, d, numel=1), _ptrs(xqs, "xqs", code, lambda i: shp[i], d)]
+            _ptrs(inv_ss, "inv_ss", sdt, lambda i: (shp[i][1],), d),
+            _ptrs(act_scales, "act_scales", sdt, None, d, numel=1), _ptrs(xqs, "xqs", code, lambda i: shp[i], d)]
     _call(_name, xs[0], count, *[a for _, a in keep], stream=stream)
+
+
+def sq_smooth_quant_act_f16_batched(xs, ss, act_scales, xqs, stream=None):
+    """The binary16 form: ss are the stored s (the kernel forms 1 / s)."""
+    sq_smooth_quant_act_batched(xs, ss, act_scales, xqs, stream, _name="sq_smooth_quant_act_f16_batched")
 
 
 def sq_w8a8_gemm_batched(xqs, wqs, act_scales, w_scales, ys, acc_outs=None, stream=None,
@@ -414,7 +481,7 @@ def sq_w8a8_gemm_batched(xqs, wqs, act_scales, w_scales, ys, acc_outs=None, stre
     fp8 = "fp8" in _name
     args = [_gemm_args(xqs[i], wqs[i], act_scales[i], w_scales[i], ys[i],
                        acc_outs[i] if acc_outs is not None else None, "u8" if fp8 else "i8", "f32" if fp8 else "i32",
-                       f"[{i}]")
+                       f"[{i}]", _sdt(_name))
             for i in range(count)]
     d = xqs[0].device if count else None
     for i in range(1, count):
@@ -429,6 +496,10 @@ def sq_w8a8_gemm_batched(xqs, wqs, act_scales, w_scales, ys, acc_outs=None, stre
     if acc_outs is not None:
         acc = _host_array(ctypes.c_void_p, [a[8].value for a in args])
     _call(_name, xqs[0], count, *[a for _, a in keep], acc[1] if acc else ctypes.c_void_p(0), stream=stream)
+
+
+def sq_w8a8_gemm_f16_batched(xqs, wqs, act_scales, w_scales, ys, acc_outs=None, stream=None):
+    sq_w8a8_gemm_batched(xqs, wqs, act_scales, w_scales, ys, acc_outs, stream, _name="sq_w8a8_gemm_f16_batched")
 
 
 def _opt(t, what: str):

@@ -207,24 +207,42 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
 // quotient, one rounding to fp32; inv_s_j = fp32(1/s_j). One thread per channel.
 constexpr int kSmoothThreads = 256;
 
+// H: s is stored as binary16 (ADR-010 "Consequences") and inv_s is not
+// written: its users form fl(1 / decoded s) themselves.
+template <bool H>
 __device__ __forceinline__ void smooth_channel(const float* __restrict__ act_max, const float* __restrict__ w_max,
-                                               int64_t j, double alpha, float* __restrict__ s,
+                                               int64_t j, double alpha, void* __restrict__ s,
                                                float* __restrict__ inv_s) {
     const float a = __builtin_fmaxf(act_max[j], sqd::kFloor);
     const float w = __builtin_fmaxf(w_max[j], sqd::kFloor);
     const double num = pow((double)a, alpha);
     const double den = pow((double)w, 1.0 - alpha);
     const float sj = (float)(num / den);
-    s[j] = sj;
-    inv_s[j] = __fdiv_rn(1.0f, sj);
+    if constexpr (H) {
+        ((uint16_t*)s)[j] = sqd::scale_f16(sj);
+    } else {
+        ((float*)s)[j] = sj;
+        inv_s[j] = __fdiv_rn(1.0f, sj);
+    }
 }
 
 // Closed-form per-tensor activation scale (ADR-010 "Key design" item 1):
 // act_scale = fp32( max_j fp32(max(act_max[j], 1e-5) * inv_s[j]) / 127 ).
 constexpr int kScaleThreads = 1024;
 
-__device__ __forceinline__ void act_scale_block(const float* __restrict__ act_max, const float* __restrict__ inv_s,
-                                                int64_t k, float qmax, float* __restrict__ act_scale, float* red) {
+// H: the factors are the stored binary16 s (inv = fl(1 / decoded s)) and the
+// scale is stored as binary16.
+template <bool H>
+__device__ __forceinline__ float inv_at(const void* __restrict__ inv_s, int64_t j) {
+    if constexpr (H)
+        return sqd::f16_inv(((const uint16_t*)inv_s)[j]);
+    else
+        return ((const float*)inv_s)[j];
+}
+
+template <bool H>
+__device__ __forceinline__ void act_scale_block(const float* __restrict__ act_max, const void* __restrict__ inv_s,
+                                                int64_t k, float qmax, void* __restrict__ act_scale, float* red) {
     // four channels per thread per round, their eight loads issued together
     // (the max is exact, so the order does not change the result)
     float mx = 0.0f;
@@ -234,22 +252,28 @@ __device__ __forceinline__ void act_scale_block(const float* __restrict__ act_ma
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             a[u] = act_max[j + u * kScaleThreads];
-            b[u] = inv_s[j + u * kScaleThreads];
+            b[u] = inv_at<H>(inv_s, j + u * kScaleThreads);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) mx = __builtin_fmaxf(mx, __fmul_rn(__builtin_fmaxf(a[u], sqd::kFloor), b[u]));
     }
     for (; j < k; j += kScaleThreads)
-        mx = __builtin_fmaxf(mx, __fmul_rn(__builtin_fmaxf(act_max[j], sqd::kFloor), inv_s[j]));
+        mx = __builtin_fmaxf(mx, __fmul_rn(__builtin_fmaxf(act_max[j], sqd::kFloor), inv_at<H>(inv_s, j)));
     mx = sqd::block_max<kScaleThreads / 64>(mx, red);
-    if (threadIdx.x == 0) act_scale[0] = __fdiv_rn(mx, qmax);
+    if (threadIdx.x == 0) {
+        const float sc = __fdiv_rn(mx, qmax);
+        if constexpr (H)
+            ((uint16_t*)act_scale)[0] = sqd::scale_f16(sc);
+        else
+            ((float*)act_scale)[0] = sc;
+    }
 }
 
 __global__ __launch_bounds__(kScaleThreads) void act_scale_kernel(const float* __restrict__ act_max,
                                                                   const float* __restrict__ inv_s, int64_t k,
                                                                   float qmax, float* __restrict__ act_scale) {
     __shared__ float red[kScaleThreads / 64];
-    act_scale_block(act_max, inv_s, k, qmax, act_scale, red);
+    act_scale_block<false>(act_max, inv_s, k, qmax, act_scale, red);
 }
 
 // Smoothing factors of several projections: item i owns blocks
@@ -262,22 +286,25 @@ struct SmoothTable {
     const float* w_max[sqk::kMaxBatch];
     int64_t k[sqk::kMaxBatch];
     double alpha[sqk::kMaxBatch];
-    float* s[sqk::kMaxBatch];
+    void* s[sqk::kMaxBatch];
     float* inv_s[sqk::kMaxBatch];
-    float* act_scale[sqk::kMaxBatch];
+    void* act_scale[sqk::kMaxBatch];
 };
 
+template <bool H>
 __global__ __launch_bounds__(kSmoothThreads) void smooth_batched_kernel(const SmoothTable tab) {
     const int i = item_of(tab.first, tab.count, blockIdx.x);
     const int64_t j = (int64_t)(blockIdx.x - tab.first[i]) * kSmoothThreads + threadIdx.x;
-    if (j < tab.k[i]) smooth_channel(tab.act_max[i], tab.w_max[i], j, tab.alpha[i], tab.s[i], tab.inv_s[i]);
+    if (j < tab.k[i]) smooth_channel<H>(tab.act_max[i], tab.w_max[i], j, tab.alpha[i], tab.s[i], tab.inv_s[i]);
 }
 
-// qmax: 127 for int8 codes, 448 for e4m3 codes
+// qmax: 127 for int8 codes, 448 for e4m3 codes; H: the factors are read from
+// the stored binary16 s
+template <bool H>
 __global__ __launch_bounds__(kScaleThreads) void act_scale_batched_kernel(const SmoothTable tab, float qmax) {
     __shared__ float red[kScaleThreads / 64];
     const int i = blockIdx.x;
-    act_scale_block(tab.act_max[i], tab.inv_s[i], tab.k[i], qmax, tab.act_scale[i], red);
+    act_scale_block<H>(tab.act_max[i], H ? tab.s[i] : tab.inv_s[i], tab.k[i], qmax, tab.act_scale[i], red);
 }
 
 // launch geometry of one absmax input: about 2048 blocks, but at least
@@ -415,8 +442,12 @@ hipError_t mean_finalize(const double* sum, int64_t count, int64_t k, float* act
     return hipGetLastError();
 }
 
+// every item of one call has the same storage (items[0].h)
 static hipError_t smooth_factors_batched_q(const SmoothItem* items, int count, float qmax, hipStream_t stream) {
     if (count <= 0) return hipSuccess;
+    const bool h = items[0].h;
+    for (int i = 1; i < count; ++i)
+        if (items[i].h != h) return hipErrorInvalidValue;
     SmoothTable tab{};
     tab.count = count;
     int64_t blocks = 0;
@@ -433,8 +464,13 @@ static hipError_t smooth_factors_batched_q(const SmoothItem* items, int count, f
     }
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     tab.first[count] = (int32_t)blocks;
-    smooth_batched_kernel<<<dim3((unsigned)blocks), dim3(kSmoothThreads), 0, stream>>>(tab);
-    act_scale_batched_kernel<<<dim3((unsigned)count), dim3(kScaleThreads), 0, stream>>>(tab, qmax);
+    if (h) {
+        smooth_batched_kernel<true><<<dim3((unsigned)blocks), dim3(kSmoothThreads), 0, stream>>>(tab);
+        act_scale_batched_kernel<true><<<dim3((unsigned)count), dim3(kScaleThreads), 0, stream>>>(tab, qmax);
+    } else {
+        smooth_batched_kernel<false><<<dim3((unsigned)blocks), dim3(kSmoothThreads), 0, stream>>>(tab);
+        act_scale_batched_kernel<false><<<dim3((unsigned)count), dim3(kScaleThreads), 0, stream>>>(tab, qmax);
+    }
     return hipGetLastError();
 }
 
@@ -452,7 +488,7 @@ hipError_t act_scale_batched(const SmoothItem* items, int count, hipStream_t str
         tab.k[i] = items[i].k;
         tab.act_scale[i] = items[i].act_scale;
     }
-    act_scale_batched_kernel<<<dim3((unsigned)count), dim3(kScaleThreads), 0, stream>>>(tab, sqd::kQmax);
+    act_scale_batched_kernel<false><<<dim3((unsigned)count), dim3(kScaleThreads), 0, stream>>>(tab, sqd::kQmax);
     return hipGetLastError();
 }
 
@@ -462,7 +498,7 @@ hipError_t smooth_factors_fp8_batched(const SmoothItem* items, int count, hipStr
 
 hipError_t smooth_factors(const float* act_max, const float* w_max, int64_t k, float alpha, float* s,
                           float* inv_s, float* act_scale, hipStream_t stream) {
-    const SmoothItem item{act_max, w_max, k, alpha, s, inv_s, act_scale};
+    const SmoothItem item{act_max, w_max, k, alpha, s, inv_s, act_scale, false};
     return smooth_factors_batched(&item, 1, stream);
 }
 

@@ -123,20 +123,33 @@ constexpr int kBK = 128;  // bytes of K per LDS stage
 // `col` and the rows row0 + acc_row<S>(v) for its accumulator elements v.
 
 // y = fp32(fp32(acc) * fp32(act_scale * w_scale[col])), fp32 or bf16 store;
-// the raw int32 accumulator is stored too when acc_out is set.
-template <bool kBF16Out, class AccT = int32_t>
+// the raw int32 accumulator is stored too when acc_out is set. kH: both
+// scales are stored as binary16 (ADR-010 "Consequences") and decoded
+// (exactly) before the merge.
+template <bool kBF16Out, class AccT = int32_t, bool kH = false>
 struct EpiDequant {
-    const float* act_scale;
-    const float* w_scale;
+    const void* act_scale;
+    const void* w_scale;
     void* y;
     AccT* acc_out;
     int64_t M, N;
     float a;
-    __device__ void begin() { a = act_scale[0]; }
+    __device__ float ws(int64_t c) const {
+        if constexpr (kH)
+            return sqd::f16_dec(((const uint16_t*)w_scale)[c]);
+        else
+            return ((const float*)w_scale)[c];
+    }
+    __device__ void begin() {
+        if constexpr (kH)
+            a = sqd::f16_dec(*(const uint16_t*)act_scale);
+        else
+            a = *(const float*)act_scale;
+    }
     template <int S, class Acc>
     __device__ void tile(const Acc& acc, int64_t row0, int64_t col) {
         if (col >= N) return;
-        const float c = __fmul_rn(a, w_scale[col]);
+        const float c = __fmul_rn(a, ws(col));
 #pragma unroll
         for (int v = 0; v < S * S / 64; ++v) {
             const int64_t row = row0 + acc_row<S>(v);
@@ -160,17 +173,29 @@ struct EpiDequant {
     __device__ Cols cols8(int64_t col) {
         Cols cc;
         cc.col = col;
-        if (col + 8 <= N && N % 4 == 0) {
-            const v4f s0 = *(const v4f*)(w_scale + col), s1 = *(const v4f*)(w_scale + col + 4);
+        if constexpr (kH) {
+            if (col + 8 <= N) {  // eight binary16 scales: one 16-byte load (col % 8 == 0)
+                const u32x4 h = *(const u32x4*)((const uint16_t*)w_scale + col);
+                const uint32_t d[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    cc.c[2 * k] = __fmul_rn(a, sqd::f16_dec((uint16_t)(d[k] & 0xffffu)));
+                    cc.c[2 * k + 1] = __fmul_rn(a, sqd::f16_dec((uint16_t)(d[k] >> 16)));
+                }
+                return cc;
+            }
+        } else if (col + 8 <= N && N % 4 == 0) {
+            const float* w = (const float*)w_scale;
+            const v4f s0 = *(const v4f*)(w + col), s1 = *(const v4f*)(w + col + 4);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 cc.c[k] = __fmul_rn(a, s0[k]);
                 cc.c[k + 4] = __fmul_rn(a, s1[k]);
             }
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) cc.c[k] = col + k < N ? __fmul_rn(a, w_scale[col + k]) : 0.0f;
+            return cc;
         }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) cc.c[k] = col + k < N ? __fmul_rn(a, ws(col + k)) : 0.0f;
         return cc;
     }
     // fast: the caller's whole tile lies inside M x N and N % 8 == 0 (a
@@ -184,8 +209,9 @@ struct EpiDequant {
         if (fast) {
             if constexpr (kBF16Out) {
                 // y is zero or a nonzero integer times a * ws >= 6e-20
-                // (a >= 1e-10 / 127, ws >= 1e-5 / 127): never subnormal, so
-                // the hardware rounding equals f32_to_bf16_bits here
+                // (a >= 1e-10 / 127, ws >= 1e-5 / 127; binary16 scales are
+                // >= 2^-24 each): never subnormal, so the hardware rounding
+                // equals f32_to_bf16_bits here
                 u32x4 o;
                 o.x = sqd::pack_bf16x2(val[0], val[1]);
                 o.y = sqd::pack_bf16x2(val[2], val[3]);
@@ -755,24 +781,24 @@ struct GemmTable {
     int32_t first[sqk::kMaxBatch + 1];
     const int8_t* A[sqk::kMaxBatch];
     const int8_t* B[sqk::kMaxBatch];
-    const float* act_scale[sqk::kMaxBatch];
-    const float* w_scale[sqk::kMaxBatch];
+    const void* act_scale[sqk::kMaxBatch];  // fp32, or binary16 (kH)
+    const void* w_scale[sqk::kMaxBatch];    // fp32, or binary16 (kH)
     void* y[sqk::kMaxBatch];
     void* acc_out[sqk::kMaxBatch];  // int32 (int8 codes) or fp32 (e4m3 codes) accumulators, or NULL
     int64_t M[sqk::kMaxBatch], N[sqk::kMaxBatch], Kb[sqk::kMaxBatch];
     int32_t tiles_m[sqk::kMaxBatch], tiles_n[sqk::kMaxBatch];
 };
 
-template <class Op, int TN, bool kBF16Out, class AccT>
+template <class Op, int TN, bool kBF16Out, class AccT, bool kH>
 __global__ __launch_bounds__(256) void gemm_dma_grouped_kernel(const GemmTable tab) {
     __shared__ __attribute__((aligned(1024))) char lds[dma_lds_bytes<TN>()];
     const int i = sqd::item_of(tab.first, tab.count, blockIdx.x);
     const int b = blockIdx.x - tab.first[i], ntiles = tab.tiles_m[i] * tab.tiles_n[i];
     if (b >= ntiles) return;
-    EpiDequant<kBF16Out, AccT> epi{tab.act_scale[i], tab.w_scale[i], tab.y[i], (AccT*)tab.acc_out[i],
-                                   tab.M[i],         tab.N[i],         0.0f};
-    dma_tile<Op, TN, EpiDequant<kBF16Out, AccT>>(tab.A[i], tab.B[i], tab.M[i], tab.N[i], tab.Kb[i], tab.tiles_m[i],
-                                                 tab.tiles_n[i], xcd_tile(b, ntiles), epi, lds);
+    using Epi = EpiDequant<kBF16Out, AccT, kH>;
+    Epi epi{tab.act_scale[i], tab.w_scale[i], tab.y[i], (AccT*)tab.acc_out[i], tab.M[i], tab.N[i], 0.0f};
+    dma_tile<Op, TN, Epi>(tab.A[i], tab.B[i], tab.M[i], tab.N[i], tab.Kb[i], tab.tiles_m[i], tab.tiles_n[i],
+                          xcd_tile(b, ntiles), epi, lds);
 }
 
 // ---- skinny kernel (decode: m <= 64) -------------------------------------------
@@ -1045,11 +1071,23 @@ __global__ __launch_bounds__(256) void ref_gemm_f32_kernel(const float* __restri
 namespace sqk {
 
 template <class Op, class AccT, int TN>
-hipError_t launch_grouped(const GemmTable& tab, int64_t blocks, bool bf16, hipStream_t stream) {
+hipError_t launch_grouped(const GemmTable& tab, int64_t blocks, bool bf16, bool h, hipStream_t stream) {
+    const dim3 grid((unsigned)blocks), block(256);
+    if constexpr (std::is_same<Op, OpI8>::value) {
+        if (h) {
+            if (bf16)
+                gemm_dma_grouped_kernel<Op, TN, true, AccT, true><<<grid, block, 0, stream>>>(tab);
+            else
+                gemm_dma_grouped_kernel<Op, TN, false, AccT, true><<<grid, block, 0, stream>>>(tab);
+            return hipGetLastError();
+        }
+    } else if (h) {
+        return hipErrorInvalidValue;  // binary16 scales are for int8 codes
+    }
     if (bf16)
-        gemm_dma_grouped_kernel<Op, TN, true, AccT><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(tab);
+        gemm_dma_grouped_kernel<Op, TN, true, AccT, false><<<grid, block, 0, stream>>>(tab);
     else
-        gemm_dma_grouped_kernel<Op, TN, false, AccT><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(tab);
+        gemm_dma_grouped_kernel<Op, TN, false, AccT, false><<<grid, block, 0, stream>>>(tab);
     return hipGetLastError();
 }
 
@@ -1064,9 +1102,10 @@ int dma_width(TileCfg c) {
     }
 }
 
-// Products that pick the same tile width (and output type) share one
-// grouped launch; int8 products too small for the pipelined tiles run as
-// single launches (FP8 products always take a pipelined width).
+// Products that pick the same tile width (and output type and scale
+// storage) share one grouped launch; int8 products too small for the
+// pipelined tiles run as single launches (FP8 products always take a
+// pipelined width).
 template <class Op, class AccT>
 hipError_t gemm_batched_impl(const GemmItem* items, int count, hipStream_t stream) {
     constexpr bool kF8 = std::is_same<Op, OpF8>::value;
@@ -1082,7 +1121,7 @@ hipError_t gemm_batched_impl(const GemmItem* items, int count, hipStream_t strea
             hipError_t e = hipErrorInvalidValue;
             if constexpr (!kF8)
                 e = gemm_dequant(it.xq, it.wq, it.m, it.n, it.k, it.act_scale, it.w_scale, it.y, it.yt,
-                                 (int32_t*)it.acc_out, stream);
+                                 (int32_t*)it.acc_out, it.h, stream);
             if (e != hipSuccess) return e;
             continue;
         }
@@ -1090,7 +1129,8 @@ hipError_t gemm_batched_impl(const GemmItem* items, int count, hipStream_t strea
         int64_t blocks = 0;
         for (int j = i; j < count; ++j) {
             const GemmItem& jt = items[j];
-            if (j > i && (done[j] || jt.m == 0 || jt.n == 0 || jt.yt != it.yt || width(jt) != tn)) continue;
+            if (j > i && (done[j] || jt.m == 0 || jt.n == 0 || jt.yt != it.yt || jt.h != it.h || width(jt) != tn))
+                continue;
             done[j] = true;
             const int c = tab.count++;
             const int64_t tiles_m = (jt.m + kDmaBM - 1) / kDmaBM, tiles_n = (jt.n + 32 * tn - 1) / (32 * tn);
@@ -1113,11 +1153,11 @@ hipError_t gemm_batched_impl(const GemmItem* items, int count, hipStream_t strea
         const bool bf16 = it.yt == kBF16;
         hipError_t e = hipErrorInvalidValue;
         switch (tn) {
-            case 8: e = launch_grouped<Op, AccT, 8>(tab, blocks, bf16, stream); break;
-            case 7: e = launch_grouped<Op, AccT, 7>(tab, blocks, bf16, stream); break;
-            case 6: e = launch_grouped<Op, AccT, 6>(tab, blocks, bf16, stream); break;
-            case 5: e = launch_grouped<Op, AccT, 5>(tab, blocks, bf16, stream); break;
-            case 4: e = launch_grouped<Op, AccT, 4>(tab, blocks, bf16, stream); break;
+            case 8: e = launch_grouped<Op, AccT, 8>(tab, blocks, bf16, it.h, stream); break;
+            case 7: e = launch_grouped<Op, AccT, 7>(tab, blocks, bf16, it.h, stream); break;
+            case 6: e = launch_grouped<Op, AccT, 6>(tab, blocks, bf16, it.h, stream); break;
+            case 5: e = launch_grouped<Op, AccT, 5>(tab, blocks, bf16, it.h, stream); break;
+            case 4: e = launch_grouped<Op, AccT, 4>(tab, blocks, bf16, it.h, stream); break;
         }
         if (e != hipSuccess) return e;
     }
@@ -1133,9 +1173,17 @@ hipError_t gemm_fp8_batched(const GemmItem* items, int count, hipStream_t stream
 }
 
 hipError_t gemm_dequant(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
-                        const float* act_scale, const float* w_scale, void* y, int yt, int32_t* acc_out,
+                        const void* act_scale, const void* w_scale, void* y, int yt, int32_t* acc_out, bool h,
                         hipStream_t stream) {
     if (m == 0 || n == 0) return hipSuccess;
+    if (h) {
+        if (yt == kBF16) {
+            EpiDequant<true, int32_t, true> e{act_scale, w_scale, y, acc_out, m, n, 0.0f};
+            return dispatch<OpI8>(xq, wq, m, n, k, e, stream);
+        }
+        EpiDequant<false, int32_t, true> e{act_scale, w_scale, y, acc_out, m, n, 0.0f};
+        return dispatch<OpI8>(xq, wq, m, n, k, e, stream);
+    }
     if (yt == kBF16) {
         EpiDequant<true> e{act_scale, w_scale, y, acc_out, m, n, 0.0f};
         return dispatch<OpI8>(xq, wq, m, n, k, e, stream);

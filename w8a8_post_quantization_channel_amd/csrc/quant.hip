@@ -100,11 +100,45 @@ struct QwTable {
     int count;
     int64_t first[sqk::kMaxBatch + 1];
     const int8_t* w[sqk::kMaxBatch];
-    const float* s[sqk::kMaxBatch];
+    const void* s[sqk::kMaxBatch];  // fp32, or binary16 (H)
     int8_t* wq[sqk::kMaxBatch];
-    float* w_scale[sqk::kMaxBatch];
+    void* w_scale[sqk::kMaxBatch];  // fp32, or binary16 (H)
     int64_t n[sqk::kMaxBatch], kvec[sqk::kMaxBatch];
 };
+
+// element i of a scale array stored in fp32, or in binary16 (H)
+template <bool H>
+__device__ __forceinline__ float scale_at(const void* p, int64_t i) {
+    if constexpr (H)
+        return sqd::f16_dec(((const uint16_t*)p)[i]);
+    else
+        return ((const float*)p)[i];
+}
+
+// The row scale of a row whose max |W'| is m (floored), and the reciprocal
+// the codes use. H: the scale is stored as binary16 and the reciprocal is
+// that of the stored value (ADR-010 "Consequences"); the returned bits are
+// the binary16 pattern, otherwise the fp32 pattern.
+template <bool H>
+__device__ __forceinline__ uint32_t row_scale(float m, float qmax, float& inv) {
+    const float ws = __fdiv_rn(m, qmax);
+    if constexpr (H) {
+        const uint16_t h = sqd::scale_f16(ws);
+        inv = sqd::f16_inv(h);
+        return h;
+    } else {
+        inv = __fdiv_rn(1.0f, ws);
+        return __float_as_uint(ws);
+    }
+}
+
+template <bool H>
+__device__ __forceinline__ void store_scale(void* p, int64_t i, uint32_t bits) {
+    if constexpr (H)
+        ((uint16_t*)p)[i] = (uint16_t)bits;
+    else
+        ((float*)p)[i] = __uint_as_float(bits);
+}
 
 __device__ __forceinline__ int stage_item(const QwTable& tab, int64_t g) {
     int i = 0;
@@ -112,8 +146,9 @@ __device__ __forceinline__ int stage_item(const QwTable& tab, int64_t g) {
     return i;
 }
 
-template <int EB, int WV, int NV, int RB, int CPW, int NS, bool FP8>
+template <int EB, int WV, int NV, int RB, int CPW, int NS, bool FP8, bool H>
 __global__ __launch_bounds__(64 * WV) void quant_weight_stream_kernel(const QwTable tab) {
+    static_assert(!(FP8 && H), "binary16 scales are for int8 codes");
     constexpr int T = 64 * WV;                 // threads
     constexpr int E = 16 / EB;                 // elements per 16-byte vector
     constexpr int STAGE = CPW * WV * 1024;     // bytes, >= RB rows (checked by the launcher)
@@ -142,7 +177,7 @@ __global__ __launch_bounds__(64 * WV) void quant_weight_stream_kernel(const QwTa
             row[i] = live[i] ? j / kvec : RB;
             const int c = live[i] ? j - row[i] * kvec : 0;
 #pragma unroll
-            for (int e = 0; e < E; ++e) sv[i][e] = live[i] ? tab.s[it][c * E + e] : 0.0f;
+            for (int e = 0; e < E; ++e) sv[i][e] = live[i] ? scale_at<H>(tab.s[it], c * E + e) : 0.0f;
         }
         cur = it;
     };
@@ -170,7 +205,7 @@ __global__ __launch_bounds__(64 * WV) void quant_weight_stream_kernel(const QwTa
     // reloads at an item change only add younger operations, which makes the
     // wait stricter, never looser).
     uint32_t codes[NV][W32];
-    float scale[RB];
+    uint32_t scale[RB];  // bit patterns (fp32, or binary16 when H)
     int64_t prev = -1;  // stage whose codes are pending
     auto flush = [&]() {
         if (prev < 0) return;
@@ -189,7 +224,7 @@ __global__ __launch_bounds__(64 * WV) void quant_weight_stream_kernel(const QwTa
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r)
-            if (t == r && p0 + r < n) tab.w_scale[cur][p0 + r] = scale[r];
+            if (t == r && p0 + r < n) store_scale<H>(tab.w_scale[cur], p0 + r, scale[r]);
     };
 
     int64_t g = blockIdx.x;
@@ -241,8 +276,7 @@ __global__ __launch_bounds__(64 * WV) void quant_weight_stream_kernel(const QwTa
 #pragma unroll
             for (int w = 1; w < WV; ++w) m = __builtin_fmaxf(m, part[r][w]);
             m = __builtin_fmaxf(m, sqd::kFloor);
-            scale[r] = __fdiv_rn(m, FP8 ? sqd::kFp8Max : sqd::kQmax);
-            inv[r] = __fdiv_rn(1.0f, scale[r]);
+            scale[r] = row_scale<H>(m, FP8 ? sqd::kFp8Max : sqd::kQmax, inv[r]);
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
@@ -263,11 +297,17 @@ __global__ __launch_bounds__(64 * WV) void quant_weight_stream_kernel(const QwTa
                 // two's-complement int8. No clamp is needed: |W'| <= m and
                 // inv_ws = fl(1 / fl(m / 127)), so |v| <= 127 (1 + 3 * 2^-24) and
                 // rint(v) is within [-127, 127] (below the 1e-5 floor, |v| < 127).
-                // Equal to q8() for every value this row can produce.
+                // Equal to q8() for every value this row can produce. A
+                // binary16 row scale can sit below the fp32 one (by 2^-11
+                // relative, far more where it is subnormal), so H clamps
+                // first (rint and the integer clamp commute).
                 uint32_t b[E];
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    b[e] = __float_as_uint(__fadd_rn(__fmul_rn(wv[i][e], inv_ws), 12582912.0f));
+                for (int e = 0; e < E; ++e) {
+                    float v = __fmul_rn(wv[i][e], inv_ws);
+                    if constexpr (H) v = __builtin_fminf(__builtin_fmaxf(v, -sqd::kQmax), sqd::kQmax);
+                    b[e] = __float_as_uint(__fadd_rn(v, 12582912.0f));
+                }
 #pragma unroll
                 for (int d = 0; d < W32; ++d) {
                     // low bytes of b[4d .. 4d+3] -> one dword
@@ -286,11 +326,28 @@ __global__ __launch_bounds__(64 * WV) void quant_weight_stream_kernel(const QwTa
 
 // Rows longer than 4096 groups (k > 65536): one block per row, the row is
 // read twice and s is read from cache.
-template <int EB, bool FP8>
+template <int EB, bool FP8, bool H>
 __global__ __launch_bounds__(256) void quant_weight_long_kernel(const u32x4* __restrict__ w, int64_t kgroups,
-                                                                const float* __restrict__ s,
-                                                                int8_t* __restrict__ wq, float* __restrict__ w_scale) {
+                                                                const void* __restrict__ s,
+                                                                int8_t* __restrict__ wq, void* __restrict__ w_scale) {
+    static_assert(!(FP8 && H), "binary16 scales are for int8 codes");
     constexpr int VG = Group<EB>::V;
+    auto load_s = [&](int64_t gi, float (&sv)[16]) {
+        if constexpr (H) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const u32x4 t = ((const u32x4*)((const uint16_t*)s + gi * 16))[q];
+                const uint32_t d[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    sv[8 * q + 2 * u] = sqd::f16_dec((uint16_t)(d[u] & 0xffffu));
+                    sv[8 * q + 2 * u + 1] = sqd::f16_dec((uint16_t)(d[u] >> 16));
+                }
+            }
+        } else {
+            load16f((const float*)s + gi * 16, sv);
+        }
+    };
     __shared__ float red[4];
     const int64_t row = blockIdx.x;
     float mx = 0.0f;
@@ -299,20 +356,20 @@ __global__ __launch_bounds__(256) void quant_weight_long_kernel(const u32x4* __r
         float e[16], sv[16];
         raw.load(w + (row * kgroups + gi) * VG);
         raw.widen(e);
-        load16f(s + gi * 16, sv);
+        load_s(gi, sv);
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = __builtin_fmaxf(mx, __builtin_fabsf(__fmul_rn(e[j], sv[j])));
     }
     mx = __builtin_fmaxf(sqd::block_max<4>(mx, red), sqd::kFloor);
-    const float ws = __fdiv_rn(mx, FP8 ? sqd::kFp8Max : sqd::kQmax);
-    const float inv_ws = __fdiv_rn(1.0f, ws);
+    float inv_ws;
+    const uint32_t ws = row_scale<H>(mx, FP8 ? sqd::kFp8Max : sqd::kQmax, inv_ws);
     for (int64_t gi = threadIdx.x; gi < kgroups; gi += 256) {
         Group<EB> raw;
         float e[16], sv[16];
         int q[16];
         raw.load(w + (row * kgroups + gi) * VG);
         raw.widen(e);
-        load16f(s + gi * 16, sv);
+        load_s(gi, sv);
         if constexpr (FP8) {
             float v[16];
 #pragma unroll
@@ -326,7 +383,7 @@ __global__ __launch_bounds__(256) void quant_weight_long_kernel(const u32x4* __r
         for (int j = 0; j < 16; ++j) q[j] = sqd::q8(__fmul_rn(__fmul_rn(e[j], sv[j]), inv_ws));
         store16(wq + (row * kgroups + gi) * 16, q);
     }
-    if (threadIdx.x == 0) w_scale[row] = ws;
+    if (threadIdx.x == 0) store_scale<H>(w_scale, row, ws);
 }
 
 constexpr int kActThreads = 256;
@@ -350,8 +407,8 @@ struct ActTable {
     const u32x4* x[sqk::kMaxBatch];
     int64_t rows[sqk::kMaxBatch], kvec[sqk::kMaxBatch], rpb[sqk::kMaxBatch];
     int32_t strips[sqk::kMaxBatch], eb[sqk::kMaxBatch];
-    const float* inv_s[sqk::kMaxBatch];
-    const float* act_scale[sqk::kMaxBatch];
+    const void* inv_s[sqk::kMaxBatch];      // fp32 inv_s, or the binary16 s (H)
+    const void* act_scale[sqk::kMaxBatch];  // fp32, or binary16 (H)
     int8_t* xq[sqk::kMaxBatch];
 };
 
@@ -359,11 +416,16 @@ struct ActTable {
 // and keeps the E inv_s values of each consumer in registers; the four waves
 // of a block walk interleaved rows, so each wave instruction moves one
 // contiguous 1 KB run.
-template <int EB, bool FP8, int NC, bool O32 = false>
+//
+// H: the scales are stored as binary16 (ADR-010 "Consequences"): inv_s[c]
+// holds s itself and the lane forms fl(1 / s) of its columns once, and
+// act_scale[c] is binary16; the arithmetic per element is unchanged.
+template <int EB, bool FP8, int NC, bool O32 = false, bool H = false>
 __device__ __forceinline__ void quant_act_block(const u32x4* __restrict__ x, int64_t rows, int64_t kvec,
-                                                int64_t rows_per_block, int nc, const float* const (&inv_s)[NC],
-                                                const float* const (&act_scale)[NC], int8_t* const (&xq)[NC],
+                                                int64_t rows_per_block, int nc, const void* const (&inv_s)[NC],
+                                                const void* const (&act_scale)[NC], int8_t* const (&xq)[NC],
                                                 int64_t strip, int64_t chunk) {
+    static_assert(!(FP8 && H), "binary16 scales are for int8 codes");
     constexpr int E = 16 / EB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t v = strip * 64 + lane;
@@ -373,15 +435,34 @@ __device__ __forceinline__ void quant_act_block(const u32x4* __restrict__ x, int
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         if (c >= nc) break;
+        if constexpr (H) {
+            // E binary16 values: 16 bytes (E = 8) or 8 bytes (E = 4)
+            const uint16_t* sp = (const uint16_t*)inv_s[c] + v * E;
+            uint32_t d[E / 2];
+            if constexpr (E == 8) {
+                const u32x4 t = *(const u32x4*)sp;
+                d[0] = t.x; d[1] = t.y; d[2] = t.z; d[3] = t.w;
+            } else {
+                const sqd::u32x2 t = *(const sqd::u32x2*)sp;
+                d[0] = t.x; d[1] = t.y;
+            }
 #pragma unroll
-        for (int h = 0; h < E / 4; ++h) {
-            const u32x4 t = ((const u32x4*)(inv_s[c] + v * E))[h];
-            is[c][4 * h + 0] = __uint_as_float(t.x);
-            is[c][4 * h + 1] = __uint_as_float(t.y);
-            is[c][4 * h + 2] = __uint_as_float(t.z);
-            is[c][4 * h + 3] = __uint_as_float(t.w);
+            for (int u = 0; u < E / 2; ++u) {
+                is[c][2 * u] = sqd::f16_inv((uint16_t)(d[u] & 0xffffu));
+                is[c][2 * u + 1] = sqd::f16_inv((uint16_t)(d[u] >> 16));
+            }
+            inv_a[c] = sqd::f16_inv(*(const uint16_t*)act_scale[c]);
+        } else {
+#pragma unroll
+            for (int h = 0; h < E / 4; ++h) {
+                const u32x4 t = ((const u32x4*)((const float*)inv_s[c] + v * E))[h];
+                is[c][4 * h + 0] = __uint_as_float(t.x);
+                is[c][4 * h + 1] = __uint_as_float(t.y);
+                is[c][4 * h + 2] = __uint_as_float(t.z);
+                is[c][4 * h + 3] = __uint_as_float(t.w);
+            }
+            inv_a[c] = __fdiv_rn(1.0f, *(const float*)act_scale[c]);
         }
-        inv_a[c] = __fdiv_rn(1.0f, act_scale[c][0]);
     }
     const int64_t r0 = chunk * rows_per_block;
     const int64_t r1 = min(rows, r0 + rows_per_block);
@@ -454,30 +535,30 @@ __device__ __forceinline__ void quant_act_block(const u32x4* __restrict__ x, int
 }
 
 // one input, one consumer, arguments in kernel parameters: the single-call form
-template <int EB, bool FP8>
+template <int EB, bool FP8, bool H>
 __global__ __launch_bounds__(kActThreads) void quant_act_kernel(const u32x4* __restrict__ x, int64_t rows,
                                                                 int64_t kvec, int64_t rows_per_block,
-                                                                const float* __restrict__ inv_s,
-                                                                const float* __restrict__ act_scale,
+                                                                const void* __restrict__ inv_s,
+                                                                const void* __restrict__ act_scale,
                                                                 int8_t* __restrict__ xq) {
-    const float* is[1] = {inv_s};
-    const float* as[1] = {act_scale};
+    const void* is[1] = {inv_s};
+    const void* as[1] = {act_scale};
     int8_t* q[1] = {xq};
-    quant_act_block<EB, FP8, 1>(x, rows, kvec, rows_per_block, 1, is, as, q, blockIdx.x, blockIdx.y);
+    quant_act_block<EB, FP8, 1, false, H>(x, rows, kvec, rows_per_block, 1, is, as, q, blockIdx.x, blockIdx.y);
 }
 
 // NC: the most consumers any group of the launch has (1, 2 or 4): a group's
 // inv_s registers scale with it, and a single consumer keeps the occupancy of
 // a plain quantizer
-template <int EB, bool FP8, int NC, bool O32>
+template <int EB, bool FP8, int NC, bool O32, bool H>
 __global__ __launch_bounds__(kActThreads) void quant_act_batched_kernel(const ActTable tab) {
     // the group's fields as plain scalars: the block then addresses its
     // input and outputs exactly as a kernel taking them as arguments would
     const int g = sqd::item_of(tab.first, tab.count, blockIdx.x);
     const int32_t local = blockIdx.x - tab.first[g], strips = tab.strips[g];
     const int cf = tab.cfirst[g], nc = tab.cfirst[g + 1] - cf;
-    const float* inv_s[NC];
-    const float* act_scale[NC];
+    const void* inv_s[NC];
+    const void* act_scale[NC];
     int8_t* xq[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -491,7 +572,7 @@ __global__ __launch_bounds__(kActThreads) void quant_act_batched_kernel(const Ac
     // integer division has no scalar instruction: bring the block-uniform
     // quotient back to a scalar register so everything derived from it is too
     const int32_t chunk = __builtin_amdgcn_readfirstlane(local / strips), strip = local - chunk * strips;
-    quant_act_block<EB, FP8, NC, O32>(x, rows, kvec, rpb, nc, inv_s, act_scale, xq, strip, chunk);
+    quant_act_block<EB, FP8, NC, O32, H>(x, rows, kvec, rpb, nc, inv_s, act_scale, xq, strip, chunk);
 }
 
 int device_cus() {
@@ -508,13 +589,13 @@ int device_cus() {
 // WV waves of 64 threads, NV vector slots per thread, RB rows per stage of
 // CPW KB per wave, NS stages in the ring, PER_CU blocks per compute unit (the
 // rings of all of them fit the LDS)
-template <int EB, int WV, int NV, int RB, int CPW, int NS, int PER_CU, bool FP8>
+template <int EB, int WV, int NV, int RB, int CPW, int NS, int PER_CU, bool FP8, bool H>
 hipError_t launch_qw(const QwTable& tab, hipStream_t stream) {
     static_assert(PER_CU * (NS * CPW * WV * 1024 + RB * WV * 4) <= 160 * 1024, "the rings fit in LDS");
     for (int i = 0; i < tab.count; ++i)
         if (RB * tab.kvec[i] * 16 > CPW * WV * 1024 || RB * tab.kvec[i] > NV * 64 * WV) return hipErrorInvalidValue;
     const int64_t blocks = std::min<int64_t>(tab.first[tab.count], (int64_t)PER_CU * device_cus());
-    quant_weight_stream_kernel<EB, WV, NV, RB, CPW, NS, FP8><<<dim3((unsigned)blocks), dim3(64 * WV), 0, stream>>>(
+    quant_weight_stream_kernel<EB, WV, NV, RB, CPW, NS, FP8, H><<<dim3((unsigned)blocks), dim3(64 * WV), 0, stream>>>(
         tab);
     return hipGetLastError();
 }
@@ -541,28 +622,28 @@ int qw_shape(int64_t kvec) {
     return kQwLong;
 }
 
-template <int EB, bool FP8>
+template <int EB, bool FP8, bool H>
 hipError_t launch_shape(int shape, const QwTable& tab, hipStream_t stream) {
     switch (shape) {
-        case 0: return launch_qw<EB, 4, 4, 4, 4, 2, 4, FP8>(tab, stream);
-        case 1: return launch_qw<EB, 4, 4, 2, 4, 2, 4, FP8>(tab, stream);
-        case 2: return launch_qw<EB, 4, 5, 2, 5, 2, 3, FP8>(tab, stream);
-        case 3: return launch_qw<EB, 8, 4, 2, 4, 2, 2, FP8>(tab, stream);
-        case 4: return launch_qw<EB, 8, 3, 1, 3, 2, 3, FP8>(tab, stream);
-        case 5: return launch_qw<EB, 4, 7, 1, 7, 2, 2, FP8>(tab, stream);
-        case 6: return launch_qw<EB, 8, 4, 1, 4, 2, 2, FP8>(tab, stream);
-        case 7: return launch_qw<EB, 16, 4, 1, 4, 2, 1, FP8>(tab, stream);
+        case 0: return launch_qw<EB, 4, 4, 4, 4, 2, 4, FP8, H>(tab, stream);
+        case 1: return launch_qw<EB, 4, 4, 2, 4, 2, 4, FP8, H>(tab, stream);
+        case 2: return launch_qw<EB, 4, 5, 2, 5, 2, 3, FP8, H>(tab, stream);
+        case 3: return launch_qw<EB, 8, 4, 2, 4, 2, 2, FP8, H>(tab, stream);
+        case 4: return launch_qw<EB, 8, 3, 1, 3, 2, 3, FP8, H>(tab, stream);
+        case 5: return launch_qw<EB, 4, 7, 1, 7, 2, 2, FP8, H>(tab, stream);
+        case 6: return launch_qw<EB, 8, 4, 1, 4, 2, 2, FP8, H>(tab, stream);
+        case 7: return launch_qw<EB, 16, 4, 1, 4, 2, 1, FP8, H>(tab, stream);
     }
     return hipErrorInvalidValue;
 }
 
-// Items of one element type and kernel shape share a launch (first-appearance
-// order); long rows get a launch per item.
-template <bool FP8>
+// Items of one element type, scale storage and kernel shape share a launch
+// (first-appearance order); long rows get a launch per item.
+template <bool FP8, bool H>
 hipError_t quant_weight_items(const sqk::QuantWeightItem* items, int count, hipStream_t stream) {
     bool done[sqk::kMaxBatch] = {};
     for (int i = 0; i < count; ++i) {
-        if (done[i]) continue;
+        if (done[i] || items[i].h != H) continue;
         done[i] = true;
         if (items[i].n == 0) continue;
         const int eb = sqk::elem_bytes(items[i].wt);
@@ -570,10 +651,10 @@ hipError_t quant_weight_items(const sqk::QuantWeightItem* items, int count, hipS
         if (shape == kQwLong) {
             const int64_t kgroups = items[i].k / 16;
             if (eb == 2)
-                quant_weight_long_kernel<2, FP8><<<dim3((unsigned)items[i].n), dim3(256), 0, stream>>>(
+                quant_weight_long_kernel<2, FP8, H><<<dim3((unsigned)items[i].n), dim3(256), 0, stream>>>(
                     (const u32x4*)items[i].w, kgroups, items[i].s, items[i].wq, items[i].w_scale);
             else
-                quant_weight_long_kernel<4, FP8><<<dim3((unsigned)items[i].n), dim3(256), 0, stream>>>(
+                quant_weight_long_kernel<4, FP8, H><<<dim3((unsigned)items[i].n), dim3(256), 0, stream>>>(
                     (const u32x4*)items[i].w, kgroups, items[i].s, items[i].wq, items[i].w_scale);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
@@ -582,7 +663,7 @@ hipError_t quant_weight_items(const sqk::QuantWeightItem* items, int count, hipS
         QwTable tab{};
         int64_t stages = 0;
         for (int j = i; j < count; ++j) {
-            if (j > i && (done[j] || items[j].n == 0 || sqk::elem_bytes(items[j].wt) != eb ||
+            if (j > i && (done[j] || items[j].n == 0 || items[j].h != H || sqk::elem_bytes(items[j].wt) != eb ||
                           qw_shape(items[j].k * eb / 16) != shape))
                 continue;
             done[j] = true;
@@ -597,7 +678,8 @@ hipError_t quant_weight_items(const sqk::QuantWeightItem* items, int count, hipS
             stages += (items[j].n + kQwRowsPerStage[shape] - 1) / kQwRowsPerStage[shape];
         }
         tab.first[tab.count] = stages;
-        const hipError_t e = eb == 2 ? launch_shape<2, FP8>(shape, tab, stream) : launch_shape<4, FP8>(shape, tab, stream);
+        const hipError_t e =
+            eb == 2 ? launch_shape<2, FP8, H>(shape, tab, stream) : launch_shape<4, FP8, H>(shape, tab, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -607,40 +689,46 @@ hipError_t quant_weight_items(const sqk::QuantWeightItem* items, int count, hipS
 
 namespace sqk {
 
-hipError_t quant_weight(const void* w, int wt, int64_t n, int64_t k, const float* s, int8_t* wq,
-                        float* w_scale, hipStream_t stream) {
-    const QuantWeightItem item{w, wt, n, k, s, wq, w_scale};
-    return quant_weight_items<false>(&item, 1, stream);
+hipError_t quant_weight(const void* w, int wt, int64_t n, int64_t k, const void* s, int8_t* wq,
+                        void* w_scale, bool h, hipStream_t stream) {
+    const QuantWeightItem item{w, wt, n, k, s, wq, w_scale, h};
+    return quant_weight_batched(&item, 1, stream);
 }
 
 hipError_t quant_weight_batched(const QuantWeightItem* items, int count, hipStream_t stream) {
-    return quant_weight_items<false>(items, count, stream);
+    const hipError_t e = quant_weight_items<false, false>(items, count, stream);
+    return e != hipSuccess ? e : quant_weight_items<false, true>(items, count, stream);
 }
 
 hipError_t quant_weight_fp8_batched(const QuantWeightItem* items, int count, hipStream_t stream) {
-    return quant_weight_items<true>(items, count, stream);
+    for (int i = 0; i < count; ++i)
+        if (items[i].h) return hipErrorInvalidValue;
+    return quant_weight_items<true, false>(items, count, stream);
 }
 
 hipError_t quant_weight_fp8(const void* w, int wt, int64_t n, int64_t k, const float* s, uint8_t* wq,
                             float* w_scale, hipStream_t stream) {
-    const QuantWeightItem item{w, wt, n, k, s, (int8_t*)wq, w_scale};
-    return quant_weight_items<true>(&item, 1, stream);
+    const QuantWeightItem item{w, wt, n, k, s, (int8_t*)wq, w_scale, false};
+    return quant_weight_items<true, false>(&item, 1, stream);
 }
 
-template <int EB, bool FP8, int NC>
+template <int EB, bool FP8, int NC, bool H>
 void launch_act(const ActTable& tab, int64_t blocks, bool o32, hipStream_t stream) {
     if (o32)
-        quant_act_batched_kernel<EB, FP8, NC, true><<<dim3((unsigned)blocks), dim3(kActThreads), 0, stream>>>(tab);
+        quant_act_batched_kernel<EB, FP8, NC, true, H><<<dim3((unsigned)blocks), dim3(kActThreads), 0, stream>>>(tab);
     else
-        quant_act_batched_kernel<EB, FP8, NC, false><<<dim3((unsigned)blocks), dim3(kActThreads), 0, stream>>>(tab);
+        quant_act_batched_kernel<EB, FP8, NC, false, H><<<dim3((unsigned)blocks), dim3(kActThreads), 0, stream>>>(
+            tab);
 }
 
 // Items with the same input (pointer, type and shape) form one group, up to
 // kActShare consumers each, in first-appearance order; one launch per element
-// type among the inputs.
-template <bool FP8>
+// type among the inputs. H: only the items with binary16 scales (the others
+// only those without).
+template <bool FP8, bool H>
 hipError_t quant_act_items(const ActItem* items, int count, hipStream_t stream) {
     bool done[kMaxBatch] = {};
+    for (int i = 0; i < count; ++i) done[i] = items[i].h != H;
     for (int eb : {2, 4}) {
         ActTable tab{};
         int ng = 0, nc = 0, widest = 1;
@@ -683,13 +771,13 @@ hipError_t quant_act_items(const ActItem* items, int count, hipStream_t stream) 
         tab.first[ng] = (int32_t)blocks;
         tab.cfirst[ng] = nc;
         if (eb == 2) {
-            if (widest == 1) launch_act<2, FP8, 1>(tab, blocks, o32, stream);
-            else if (widest == 2) launch_act<2, FP8, 2>(tab, blocks, o32, stream);
-            else launch_act<2, FP8, kActShare>(tab, blocks, o32, stream);
+            if (widest == 1) launch_act<2, FP8, 1, H>(tab, blocks, o32, stream);
+            else if (widest == 2) launch_act<2, FP8, 2, H>(tab, blocks, o32, stream);
+            else launch_act<2, FP8, kActShare, H>(tab, blocks, o32, stream);
         } else {
-            if (widest == 1) launch_act<4, FP8, 1>(tab, blocks, o32, stream);
-            else if (widest == 2) launch_act<4, FP8, 2>(tab, blocks, o32, stream);
-            else launch_act<4, FP8, kActShare>(tab, blocks, o32, stream);
+            if (widest == 1) launch_act<4, FP8, 1, H>(tab, blocks, o32, stream);
+            else if (widest == 2) launch_act<4, FP8, 2, H>(tab, blocks, o32, stream);
+            else launch_act<4, FP8, kActShare, H>(tab, blocks, o32, stream);
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -699,9 +787,9 @@ hipError_t quant_act_items(const ActItem* items, int count, hipStream_t stream) 
 
 // one input and one consumer: the kernel with plain arguments (no table to
 // look the group up in), blocks of 4 waves over 32 rows of a 64-vector strip
-template <bool FP8>
-hipError_t quant_act_single(const void* x, int xt, int64_t m, int64_t k, const float* inv_s,
-                            const float* act_scale, int8_t* xq, hipStream_t stream) {
+template <bool FP8, bool H>
+hipError_t quant_act_single(const void* x, int xt, int64_t m, int64_t k, const void* inv_s,
+                            const void* act_scale, int8_t* xq, hipStream_t stream) {
     if (m == 0) return hipSuccess;
     const int eb = elem_bytes(xt);
     const int64_t kvec = k * eb / 16;
@@ -715,28 +803,32 @@ hipError_t quant_act_single(const void* x, int xt, int64_t m, int64_t k, const f
     }
     const dim3 grid((unsigned)strips, (unsigned)chunks), block(kActThreads);
     if (eb == 2)
-        quant_act_kernel<2, FP8><<<grid, block, 0, stream>>>((const u32x4*)x, m, kvec, rpb, inv_s, act_scale, xq);
+        quant_act_kernel<2, FP8, H><<<grid, block, 0, stream>>>((const u32x4*)x, m, kvec, rpb, inv_s, act_scale, xq);
     else
-        quant_act_kernel<4, FP8><<<grid, block, 0, stream>>>((const u32x4*)x, m, kvec, rpb, inv_s, act_scale, xq);
+        quant_act_kernel<4, FP8, H><<<grid, block, 0, stream>>>((const u32x4*)x, m, kvec, rpb, inv_s, act_scale, xq);
     return hipGetLastError();
 }
 
-hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const float* inv_s, const float* act_scale,
-                     int8_t* xq, hipStream_t stream) {
-    return quant_act_single<false>(x, xt, m, k, inv_s, act_scale, xq, stream);
+hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const void* inv_s, const void* act_scale,
+                     int8_t* xq, bool h, hipStream_t stream) {
+    return h ? quant_act_single<false, true>(x, xt, m, k, inv_s, act_scale, xq, stream)
+             : quant_act_single<false, false>(x, xt, m, k, inv_s, act_scale, xq, stream);
 }
 
 hipError_t quant_act_batched(const ActItem* items, int count, hipStream_t stream) {
-    return quant_act_items<false>(items, count, stream);
+    const hipError_t e = quant_act_items<false, false>(items, count, stream);
+    return e != hipSuccess ? e : quant_act_items<false, true>(items, count, stream);
 }
 
 hipError_t quant_act_fp8_batched(const ActItem* items, int count, hipStream_t stream) {
-    return quant_act_items<true>(items, count, stream);
+    for (int i = 0; i < count; ++i)
+        if (items[i].h) return hipErrorInvalidValue;
+    return quant_act_items<true, false>(items, count, stream);
 }
 
 hipError_t quant_act_fp8(const void* x, int xt, int64_t m, int64_t k, const float* inv_s, const float* act_scale,
                          uint8_t* xq, hipStream_t stream) {
-    return quant_act_single<true>(x, xt, m, k, inv_s, act_scale, (int8_t*)xq, stream);
+    return quant_act_single<true, false>(x, xt, m, k, inv_s, act_scale, (int8_t*)xq, stream);
 }
 
 }  // namespace sqk

@@ -61,18 +61,26 @@ sq_status check_absmax(const void* x, sq_dtype xt, int64_t rows, int64_t k, cons
     return SQ_OK;
 }
 
-sq_status check_smooth(const float* act_max, const float* w_max, int64_t k, float alpha, const float* s,
-                       const float* inv_s, const float* act_scale) {
-    if (!act_max || !w_max || !s || !inv_s || !act_scale) return SQ_ERR_NULL;
+// Scale storage of an entry point: fp32 with int8 codes, fp32 with e4m3
+// codes, or binary16 with int8 codes (ADR-010 "Consequences").
+enum Mode { kI8 = 0, kF8 = 1, kI8H = 2 };
+
+int64_t scale_bytes(Mode md) { return md == kI8H ? 2 : 4; }
+
+// h: binary16 storage, which writes no inv_s (it may be NULL)
+sq_status check_smooth(const float* act_max, const float* w_max, int64_t k, float alpha, const void* s,
+                       const float* inv_s, const void* act_scale, bool h = false) {
+    if (!act_max || !w_max || !s || (!h && !inv_s) || !act_scale) return SQ_ERR_NULL;
     if (!valid_k(k)) return SQ_ERR_SHAPE;
     if (!valid_alpha(alpha)) return SQ_ERR_ALPHA;
-    if (!aligned16(act_max) || !aligned16(w_max) || !aligned16(s) || !aligned16(inv_s) || !aligned16(act_scale))
+    if (!aligned16(act_max) || !aligned16(w_max) || !aligned16(s) || (!h && !aligned16(inv_s)) ||
+        !aligned16(act_scale))
         return SQ_ERR_ALIGN;
     return SQ_OK;
 }
 
-sq_status check_quant_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, const float* s, const int8_t* wq,
-                             const float* w_scale) {
+sq_status check_quant_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, const void* s, const int8_t* wq,
+                             const void* w_scale) {
     if (!s || (n > 0 && (!w || !wq || !w_scale))) return SQ_ERR_NULL;
     if (!valid_dtype(wt)) return SQ_ERR_DTYPE;
     if (n < 0 || !valid_k(k) || n > INT32_MAX) return SQ_ERR_SHAPE;
@@ -80,8 +88,8 @@ sq_status check_quant_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, c
     return SQ_OK;
 }
 
-sq_status check_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* inv_s,
-                          const float* act_scale, const int8_t* xq) {
+sq_status check_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k, const void* inv_s,
+                          const void* act_scale, const int8_t* xq) {
     if (!inv_s || !act_scale || (m > 0 && (!x || !xq))) return SQ_ERR_NULL;
     if (!valid_dtype(xt)) return SQ_ERR_DTYPE;
     if (m < 0 || !valid_k(k)) return SQ_ERR_SHAPE;
@@ -90,8 +98,8 @@ sq_status check_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k, cons
     return SQ_OK;
 }
 
-sq_status check_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k, const float* act_scale,
-                     const float* w_scale, const void* y, sq_dtype yt, const int32_t* acc_out) {
+sq_status check_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k, const void* act_scale,
+                     const void* w_scale, const void* y, sq_dtype yt, const void* acc_out) {
     const bool work = m > 0 && n > 0;
     if (!act_scale || (work && (!xq || !wq || !w_scale || !y))) return SQ_ERR_NULL;
     if (!valid_dtype(yt)) return SQ_ERR_DTYPE;
@@ -164,7 +172,37 @@ sq_status sq_quant_weight(const void* w, sq_dtype wt, int64_t n, int64_t k, cons
                           float* w_scale, hipStream_t stream) {
     const sq_status st = check_quant_weight(w, wt, n, k, s, wq, w_scale);
     if (st != SQ_OK) return st;
-    return hip_status(sqk::quant_weight(w, wt, n, k, s, wq, w_scale, stream));
+    return hip_status(sqk::quant_weight(w, wt, n, k, s, wq, w_scale, false, stream));
+}
+
+sq_status sq_smooth_factors_f16(const float* act_max, const float* w_max, int64_t k, float alpha, uint16_t* s,
+                                uint16_t* act_scale, hipStream_t stream) {
+    const sq_status st = check_smooth(act_max, w_max, k, alpha, s, nullptr, act_scale, true);
+    if (st != SQ_OK) return st;
+    const sqk::SmoothItem item{act_max, w_max, k, alpha, s, nullptr, act_scale, true};
+    return hip_status(sqk::smooth_factors_batched(&item, 1, stream));
+}
+
+sq_status sq_quant_weight_f16(const void* w, sq_dtype wt, int64_t n, int64_t k, const uint16_t* s, int8_t* wq,
+                              uint16_t* w_scale, hipStream_t stream) {
+    const sq_status st = check_quant_weight(w, wt, n, k, s, wq, w_scale);
+    if (st != SQ_OK) return st;
+    return hip_status(sqk::quant_weight(w, wt, n, k, s, wq, w_scale, true, stream));
+}
+
+sq_status sq_smooth_quant_act_f16(const void* x, sq_dtype xt, int64_t m, int64_t k, const uint16_t* s,
+                                  const uint16_t* act_scale, int8_t* xq, hipStream_t stream) {
+    const sq_status st = check_quant_act(x, xt, m, k, s, act_scale, xq);
+    if (st != SQ_OK) return st;
+    return hip_status(sqk::quant_act(x, xt, m, k, s, act_scale, xq, true, stream));
+}
+
+sq_status sq_w8a8_gemm_f16(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
+                           const uint16_t* act_scale, const uint16_t* w_scale, void* y, sq_dtype yt,
+                           int32_t* acc_out, hipStream_t stream) {
+    const sq_status st = check_gemm(xq, wq, m, n, k, act_scale, w_scale, y, yt, acc_out);
+    if (st != SQ_OK) return st;
+    return hip_status(sqk::gemm_dequant(xq, wq, m, n, k, act_scale, w_scale, y, yt, acc_out, true, stream));
 }
 
 sq_status sq_calib_absmax_batched(int count, const void* const* x, const sq_dtype* xt, const int64_t* rows,
@@ -187,111 +225,144 @@ sq_status sq_calib_absmax_batched(int count, const void* const* x, const sq_dtyp
     return hip_status(sqk::absmax_batched(items, n, accumulate != 0, stream));
 }
 
+// s, act_scale: fp32 (kI8, kF8) or binary16 (kI8H) arrays; inv_s is
+// ignored (and may be NULL) for kI8H
 static sq_status smooth_batched(int count, const float* const* act_max, const float* const* w_max,
-                                const int64_t* k, const float* alpha, float* const* s, float* const* inv_s,
-                                float* const* act_scale, bool fp8, hipStream_t stream) {
-    if (!act_max || !w_max || !k || !alpha || !s || !inv_s || !act_scale) return SQ_ERR_NULL;
+                                const int64_t* k, const float* alpha, void* const* s, float* const* inv_s,
+                                void* const* act_scale, Mode md, hipStream_t stream) {
+    const bool h = md == kI8H;
+    if (!act_max || !w_max || !k || !alpha || !s || (!h && !inv_s) || !act_scale) return SQ_ERR_NULL;
     if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
+    const int64_t sb = scale_bytes(md);
     Ranges rg;
     sqk::SmoothItem items[SQ_MAX_BATCH];
     for (int i = 0; i < count; ++i) {
-        const sq_status st = check_smooth(act_max[i], w_max[i], k[i], alpha[i], s[i], inv_s[i], act_scale[i]);
+        float* is = h ? nullptr : inv_s[i];
+        const sq_status st = check_smooth(act_max[i], w_max[i], k[i], alpha[i], s[i], is, act_scale[i], h);
         if (st != SQ_OK) return st;
         rg.add(i, act_max[i], k[i] * 4, false);
         rg.add(i, w_max[i], k[i] * 4, false);
-        rg.add(i, s[i], k[i] * 4, true);
-        rg.add(i, inv_s[i], k[i] * 4, true);
-        rg.add(i, act_scale[i], 4, true);
-        items[i] = sqk::SmoothItem{act_max[i], w_max[i], k[i], alpha[i], s[i], inv_s[i], act_scale[i]};
+        rg.add(i, s[i], k[i] * sb, true);
+        rg.add(i, is, k[i] * 4, true);
+        rg.add(i, act_scale[i], sb, true);
+        items[i] = sqk::SmoothItem{act_max[i], w_max[i], k[i], alpha[i], s[i], is, act_scale[i], h};
     }
     if (rg.overlap()) return SQ_ERR_SHAPE;
-    return hip_status(fp8 ? sqk::smooth_factors_fp8_batched(items, count, stream)
-                          : sqk::smooth_factors_batched(items, count, stream));
+    return hip_status(md == kF8 ? sqk::smooth_factors_fp8_batched(items, count, stream)
+                                : sqk::smooth_factors_batched(items, count, stream));
 }
 
 sq_status sq_smooth_factors_batched(int count, const float* const* act_max, const float* const* w_max,
                                     const int64_t* k, const float* alpha, float* const* s, float* const* inv_s,
                                     float* const* act_scale, hipStream_t stream) {
-    return smooth_batched(count, act_max, w_max, k, alpha, s, inv_s, act_scale, false, stream);
+    return smooth_batched(count, act_max, w_max, k, alpha, (void* const*)s, inv_s, (void* const*)act_scale, kI8,
+                          stream);
 }
 
 sq_status sq_smooth_factors_fp8_batched(int count, const float* const* act_max, const float* const* w_max,
                                         const int64_t* k, const float* alpha, float* const* s,
                                         float* const* inv_s, float* const* act_scale, hipStream_t stream) {
-    return smooth_batched(count, act_max, w_max, k, alpha, s, inv_s, act_scale, true, stream);
+    return smooth_batched(count, act_max, w_max, k, alpha, (void* const*)s, inv_s, (void* const*)act_scale, kF8,
+                          stream);
+}
+
+sq_status sq_smooth_factors_f16_batched(int count, const float* const* act_max, const float* const* w_max,
+                                        const int64_t* k, const float* alpha, uint16_t* const* s,
+                                        uint16_t* const* act_scale, hipStream_t stream) {
+    return smooth_batched(count, act_max, w_max, k, alpha, (void* const*)s, nullptr, (void* const*)act_scale, kI8H,
+                          stream);
 }
 
 static sq_status quant_weight_batched(int count, const void* const* w, const sq_dtype* wt, const int64_t* n,
-                                      const int64_t* k, const float* const* s, int8_t* const* wq,
-                                      float* const* w_scale, bool fp8, hipStream_t stream) {
+                                      const int64_t* k, const void* const* s, int8_t* const* wq,
+                                      void* const* w_scale, Mode md, hipStream_t stream) {
     if (!w || !wt || !n || !k || !s || !wq || !w_scale) return SQ_ERR_NULL;
     if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
+    const int64_t sb = scale_bytes(md);
     Ranges rg;
     sqk::QuantWeightItem items[SQ_MAX_BATCH];
     for (int i = 0; i < count; ++i) {
         const sq_status st = check_quant_weight(w[i], wt[i], n[i], k[i], s[i], wq[i], w_scale[i]);
         if (st != SQ_OK) return st;
         rg.add(i, w[i], n[i] * k[i] * (wt[i] == SQ_BF16 ? 2 : 4), false);
-        rg.add(i, s[i], k[i] * 4, false);
+        rg.add(i, s[i], k[i] * sb, false);
         rg.add(i, wq[i], n[i] * k[i], true);
-        rg.add(i, w_scale[i], n[i] * 4, true);
-        items[i] = sqk::QuantWeightItem{w[i], wt[i], n[i], k[i], s[i], wq[i], w_scale[i]};
+        rg.add(i, w_scale[i], n[i] * sb, true);
+        items[i] = sqk::QuantWeightItem{w[i], wt[i], n[i], k[i], s[i], wq[i], w_scale[i], md == kI8H};
     }
     if (rg.overlap()) return SQ_ERR_SHAPE;
-    return hip_status(fp8 ? sqk::quant_weight_fp8_batched(items, count, stream)
-                          : sqk::quant_weight_batched(items, count, stream));
+    return hip_status(md == kF8 ? sqk::quant_weight_fp8_batched(items, count, stream)
+                                : sqk::quant_weight_batched(items, count, stream));
 }
 
 sq_status sq_quant_weight_batched(int count, const void* const* w, const sq_dtype* wt, const int64_t* n,
                                   const int64_t* k, const float* const* s, int8_t* const* wq,
                                   float* const* w_scale, hipStream_t stream) {
-    return quant_weight_batched(count, w, wt, n, k, s, wq, w_scale, false, stream);
+    return quant_weight_batched(count, w, wt, n, k, (const void* const*)s, wq, (void* const*)w_scale, kI8, stream);
 }
 
 sq_status sq_quant_weight_fp8_batched(int count, const void* const* w, const sq_dtype* wt, const int64_t* n,
                                       const int64_t* k, const float* const* s, uint8_t* const* wq,
                                       float* const* w_scale, hipStream_t stream) {
-    return quant_weight_batched(count, w, wt, n, k, s, (int8_t* const*)wq, w_scale, true, stream);
+    return quant_weight_batched(count, w, wt, n, k, (const void* const*)s, (int8_t* const*)wq,
+                                (void* const*)w_scale, kF8, stream);
+}
+
+sq_status sq_quant_weight_f16_batched(int count, const void* const* w, const sq_dtype* wt, const int64_t* n,
+                                      const int64_t* k, const uint16_t* const* s, int8_t* const* wq,
+                                      uint16_t* const* w_scale, hipStream_t stream) {
+    return quant_weight_batched(count, w, wt, n, k, (const void* const*)s, wq, (void* const*)w_scale, kI8H, stream);
 }
 
 sq_status sq_smooth_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k, const float* inv_s,
                               const float* act_scale, int8_t* xq, hipStream_t stream) {
     const sq_status st = check_quant_act(x, xt, m, k, inv_s, act_scale, xq);
     if (st != SQ_OK) return st;
-    return hip_status(sqk::quant_act(x, xt, m, k, inv_s, act_scale, xq, stream));
+    return hip_status(sqk::quant_act(x, xt, m, k, inv_s, act_scale, xq, false, stream));
 }
 
+// inv_s: fp32 inv_s (kI8, kF8) or the binary16 s itself (kI8H)
 static sq_status quant_act_batched(int count, const void* const* x, const sq_dtype* xt, const int64_t* m,
-                                   const int64_t* k, const float* const* inv_s, const float* const* act_scale,
-                                   int8_t* const* xq, bool fp8, hipStream_t stream) {
+                                   const int64_t* k, const void* const* inv_s, const void* const* act_scale,
+                                   int8_t* const* xq, Mode md, hipStream_t stream) {
     if (!x || !xt || !m || !k || !inv_s || !act_scale || !xq) return SQ_ERR_NULL;
     if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
+    const int64_t sb = scale_bytes(md);
     Ranges rg;
     sqk::ActItem items[SQ_MAX_BATCH];
     for (int i = 0; i < count; ++i) {
         const sq_status st = check_quant_act(x[i], xt[i], m[i], k[i], inv_s[i], act_scale[i], xq[i]);
         if (st != SQ_OK) return st;
         rg.add(i, x[i], m[i] * k[i] * (xt[i] == SQ_BF16 ? 2 : 4), false);
-        rg.add(i, inv_s[i], k[i] * 4, false);
-        rg.add(i, act_scale[i], 4, false);
+        rg.add(i, inv_s[i], k[i] * sb, false);
+        rg.add(i, act_scale[i], sb, false);
         rg.add(i, xq[i], m[i] * k[i], true);
-        items[i] = sqk::ActItem{x[i], xt[i], m[i], k[i], inv_s[i], act_scale[i], xq[i]};
+        items[i] = sqk::ActItem{x[i], xt[i], m[i], k[i], inv_s[i], act_scale[i], xq[i], md == kI8H};
     }
     if (rg.overlap()) return SQ_ERR_SHAPE;
-    return hip_status(fp8 ? sqk::quant_act_fp8_batched(items, count, stream)
-                          : sqk::quant_act_batched(items, count, stream));
+    return hip_status(md == kF8 ? sqk::quant_act_fp8_batched(items, count, stream)
+                                : sqk::quant_act_batched(items, count, stream));
 }
 
 sq_status sq_smooth_quant_act_batched(int count, const void* const* x, const sq_dtype* xt, const int64_t* m,
                                       const int64_t* k, const float* const* inv_s, const float* const* act_scale,
                                       int8_t* const* xq, hipStream_t stream) {
-    return quant_act_batched(count, x, xt, m, k, inv_s, act_scale, xq, false, stream);
+    return quant_act_batched(count, x, xt, m, k, (const void* const*)inv_s, (const void* const*)act_scale, xq, kI8,
+                             stream);
 }
 
 sq_status sq_smooth_quant_act_fp8_batched(int count, const void* const* x, const sq_dtype* xt, const int64_t* m,
                                           const int64_t* k, const float* const* inv_s,
                                           const float* const* act_scale, uint8_t* const* xq, hipStream_t stream) {
-    return quant_act_batched(count, x, xt, m, k, inv_s, act_scale, (int8_t* const*)xq, true, stream);
+    return quant_act_batched(count, x, xt, m, k, (const void* const*)inv_s, (const void* const*)act_scale,
+                             (int8_t* const*)xq, kF8, stream);
+}
+
+sq_status sq_smooth_quant_act_f16_batched(int count, const void* const* x, const sq_dtype* xt, const int64_t* m,
+                                          const int64_t* k, const uint16_t* const* s,
+                                          const uint16_t* const* act_scale, int8_t* const* xq, hipStream_t stream) {
+    return quant_act_batched(count, x, xt, m, k, (const void* const*)s, (const void* const*)act_scale, xq, kI8H,
+                             stream);
 }
 
 sq_status sq_w8a8_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
@@ -299,49 +370,61 @@ sq_status sq_w8a8_gemm(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n,
                        hipStream_t stream) {
     const sq_status st = check_gemm(xq, wq, m, n, k, act_scale, w_scale, y, yt, acc_out);
     if (st != SQ_OK) return st;
-    return hip_status(sqk::gemm_dequant(xq, wq, m, n, k, act_scale, w_scale, y, yt, acc_out, stream));
+    return hip_status(sqk::gemm_dequant(xq, wq, m, n, k, act_scale, w_scale, y, yt, acc_out, false, stream));
 }
 
-// acc_out: int32 (int8 codes) or fp32 (e4m3 codes) accumulators, 4 bytes each
+// acc_out: int32 (int8 codes) or fp32 (e4m3 codes) accumulators, 4 bytes each;
+// act_scale, w_scale: fp32, or binary16 (kI8H)
 static sq_status gemm_batched(int count, const int8_t* const* xq, const int8_t* const* wq, const int64_t* m,
-                              const int64_t* n, const int64_t* k, const float* const* act_scale,
-                              const float* const* w_scale, void* const* y, const sq_dtype* yt,
-                              void* const* acc_out, bool fp8, hipStream_t stream) {
+                              const int64_t* n, const int64_t* k, const void* const* act_scale,
+                              const void* const* w_scale, void* const* y, const sq_dtype* yt,
+                              void* const* acc_out, Mode md, hipStream_t stream) {
     if (!xq || !wq || !m || !n || !k || !act_scale || !w_scale || !y || !yt) return SQ_ERR_NULL;
     if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
+    const int64_t sb = scale_bytes(md);
     Ranges rg;
     sqk::GemmItem items[SQ_MAX_BATCH];
     for (int i = 0; i < count; ++i) {
         void* acc = acc_out ? acc_out[i] : nullptr;
-        const sq_status st =
-            check_gemm(xq[i], wq[i], m[i], n[i], k[i], act_scale[i], w_scale[i], y[i], yt[i], (const int32_t*)acc);
+        const sq_status st = check_gemm(xq[i], wq[i], m[i], n[i], k[i], act_scale[i], w_scale[i], y[i], yt[i], acc);
         if (st != SQ_OK) return st;
         rg.add(i, xq[i], m[i] * k[i], false);
         rg.add(i, wq[i], n[i] * k[i], false);
-        rg.add(i, act_scale[i], 4, false);
-        rg.add(i, w_scale[i], n[i] * 4, false);
+        rg.add(i, act_scale[i], sb, false);
+        rg.add(i, w_scale[i], n[i] * sb, false);
         rg.add(i, y[i], m[i] * n[i] * (yt[i] == SQ_BF16 ? 2 : 4), true);
         rg.add(i, acc, m[i] * n[i] * 4, true);
-        items[i] = sqk::GemmItem{xq[i], wq[i], m[i], n[i], k[i], act_scale[i], w_scale[i], y[i], yt[i], acc};
+        items[i] =
+            sqk::GemmItem{xq[i], wq[i], m[i], n[i], k[i], act_scale[i], w_scale[i], y[i], yt[i], acc, md == kI8H};
     }
     if (rg.overlap()) return SQ_ERR_SHAPE;
-    return hip_status(fp8 ? sqk::gemm_fp8_batched(items, count, stream)
-                          : sqk::gemm_dequant_batched(items, count, stream));
+    return hip_status(md == kF8 ? sqk::gemm_fp8_batched(items, count, stream)
+                                : sqk::gemm_dequant_batched(items, count, stream));
 }
 
 sq_status sq_w8a8_gemm_batched(int count, const int8_t* const* xq, const int8_t* const* wq, const int64_t* m,
                                const int64_t* n, const int64_t* k, const float* const* act_scale,
                                const float* const* w_scale, void* const* y, const sq_dtype* yt,
                                int32_t* const* acc_out, hipStream_t stream) {
-    return gemm_batched(count, xq, wq, m, n, k, act_scale, w_scale, y, yt, (void* const*)acc_out, false, stream);
+    return gemm_batched(count, xq, wq, m, n, k, (const void* const*)act_scale, (const void* const*)w_scale, y, yt,
+                        (void* const*)acc_out, kI8, stream);
 }
 
 sq_status sq_fp8_gemm_batched(int count, const uint8_t* const* xq, const uint8_t* const* wq, const int64_t* m,
                               const int64_t* n, const int64_t* k, const float* const* act_scale,
                               const float* const* w_scale, void* const* y, const sq_dtype* yt,
                               float* const* acc_out, hipStream_t stream) {
-    return gemm_batched(count, (const int8_t* const*)xq, (const int8_t* const*)wq, m, n, k, act_scale, w_scale, y, yt,
-                        (void* const*)acc_out, true, stream);
+    return gemm_batched(count, (const int8_t* const*)xq, (const int8_t* const*)wq, m, n, k,
+                        (const void* const*)act_scale, (const void* const*)w_scale, y, yt, (void* const*)acc_out, kF8,
+                        stream);
+}
+
+sq_status sq_w8a8_gemm_f16_batched(int count, const int8_t* const* xq, const int8_t* const* wq, const int64_t* m,
+                                   const int64_t* n, const int64_t* k, const uint16_t* const* act_scale,
+                                   const uint16_t* const* w_scale, void* const* y, const sq_dtype* yt,
+                                   int32_t* const* acc_out, hipStream_t stream) {
+    return gemm_batched(count, xq, wq, m, n, k, (const void* const*)act_scale, (const void* const*)w_scale, y, yt,
+                        (void* const*)acc_out, kI8H, stream);
 }
 
 sq_status sq_act_scale(const float* act_max, const float* inv_s, int64_t k, float* act_scale, hipStream_t stream) {
@@ -366,7 +449,7 @@ sq_status sq_act_scale_batched(int count, const float* const* act_max, const flo
         rg.add(i, act_scale[i], 4, true);
         // act_scale_batched only reads inv_s (the field is an output of the smoothing kernels)
         items[i] = sqk::SmoothItem{act_max[i], nullptr, k[i], 0.0f, nullptr, const_cast<float*>(inv_s[i]),
-                                   act_scale[i]};
+                                   act_scale[i], false};
     }
     if (rg.overlap()) return SQ_ERR_SHAPE;
     return hip_status(sqk::act_scale_batched(items, count, stream));
@@ -382,7 +465,7 @@ sq_status sq_dynamic_quant_act(const void* x, sq_dtype xt, int64_t m, int64_t k,
         return SQ_ERR_ALIGN;
     hipError_t e = sqk::absmax(x, xt, m, k, live_max, false, stream);
     if (e == hipSuccess) e = sqk::act_scale(live_max, inv_s, k, act_scale, stream);
-    if (e == hipSuccess && m > 0) e = sqk::quant_act(x, xt, m, k, inv_s, act_scale, xq, stream);
+    if (e == hipSuccess && m > 0) e = sqk::quant_act(x, xt, m, k, inv_s, act_scale, xq, false, stream);
     return hip_status(e);
 }
 
@@ -599,9 +682,9 @@ sq_status sq_alpha_search(const void* const* x_batches, sq_dtype xt, int n_batch
     // one full quantized forward per alpha, scored in the GEMM epilogue
     for (int i = 0; i < n_alphas && e == hipSuccess; ++i) {
         run(sqk::smooth_factors(act_max, w_max, k, alphas[i], s, inv_s, act_scale, stream));
-        run(sqk::quant_weight(w, wt, n, k, s, wq, w_scale, stream));
+        run(sqk::quant_weight(w, wt, n, k, s, wq, w_scale, false, stream));
         for (int b = 0; b < n_batches; ++b) {
-            run(sqk::quant_act(x_batches[b], xt, rows_per_batch, k, inv_s, act_scale, xq, stream));
+            run(sqk::quant_act(x_batches[b], xt, rows_per_batch, k, inv_s, act_scale, xq, false, stream));
             run(sqk::gemm_sse(xq, wq, rows_per_batch, n, k, act_scale, w_scale, yref + b * ynum,
                               slots + ((int64_t)i * n_batches + b) * per_gemm, stream));
         }

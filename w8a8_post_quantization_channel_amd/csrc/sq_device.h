@@ -46,6 +46,24 @@ __device__ __forceinline__ int q8(float v) {
     return (int)r;
 }
 
+// IEEE binary16 scale storage (ADR-010 "Consequences": the per-row weight
+// scale, the per-tensor activation scale and the smoothing factors kept in
+// fp16). v_cvt_f16_f32 rounds to nearest even in the default rounding mode
+// and yields binary16 subnormals (fp16 denormals are kept in the default
+// float mode of gfx950 kernels); v_cvt_f32_f16 is exact. A stored scale is
+// clamped into [2^-24, 65504] first, so it is never zero nor infinite.
+constexpr float kF16Min = 0x1p-24f;
+constexpr float kF16Max = 65504.0f;
+
+__device__ __forceinline__ float f16_dec(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+__device__ __forceinline__ uint16_t scale_f16(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)__builtin_fminf(__builtin_fmaxf(v, kF16Min), kF16Max));
+}
+
+// fl(1 / decoded stored scale): the reciprocal the quantizers multiply by
+__device__ __forceinline__ float f16_inv(uint16_t h) { return __fdiv_rn(1.0f, f16_dec(h)); }
+
 // OCP FP8 E4M3 (bias 7, largest finite 448): four fp32 values, clamped to
 // [-448, 448], rounded to nearest even by v_cvt_pk_fp8_f32, one byte each
 // (a in the low byte).

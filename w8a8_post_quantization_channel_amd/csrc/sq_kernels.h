@@ -74,14 +74,17 @@ hipError_t smooth_factors(const float* act_max, const float* w_max, int64_t k, f
                           float* inv_s, float* act_scale, hipStream_t stream);
 
 // the same for up to kMaxBatch projections: two launches in all
+// h: the fp16 scale storage of ADR-010 "Consequences" (s and act_scale are
+// then binary16 arrays, inv_s is not written); otherwise fp32 throughout
 struct SmoothItem {
     const float* act_max;
     const float* w_max;
     int64_t k;
     float alpha;
-    float* s;
+    void* s;
     float* inv_s;
-    float* act_scale;
+    void* act_scale;
+    bool h;
 };
 hipError_t smooth_factors_batched(const SmoothItem* items, int count, hipStream_t stream);
 // the same with the act scale over 448 (e4m3 codes)
@@ -89,41 +92,49 @@ hipError_t smooth_factors_fp8_batched(const SmoothItem* items, int count, hipStr
 // the act scale alone for several items (act_max, inv_s, k, act_scale used)
 hipError_t act_scale_batched(const SmoothItem* items, int count, hipStream_t stream);
 
-// W' = W diag(s), per-row symmetric int8
-hipError_t quant_weight(const void* w, int wt, int64_t n, int64_t k, const float* s, int8_t* wq,
-                        float* w_scale, hipStream_t stream);
+// W' = W diag(s), per-row symmetric int8 (h: binary16 s and w_scale)
+hipError_t quant_weight(const void* w, int wt, int64_t n, int64_t k, const void* s, int8_t* wq,
+                        void* w_scale, bool h, hipStream_t stream);
 
 // the same for up to kMaxBatch weights: one persistent launch per kernel
 // shape among the items (weights of equal row length share one)
+// h: s and w_scale are binary16 (the codes then use the reciprocal of the
+// stored row scale, clamped to +-127)
 struct QuantWeightItem {
     const void* w;
     int wt;
     int64_t n, k;
-    const float* s;
+    const void* s;
     int8_t* wq;
-    float* w_scale;
+    void* w_scale;
+    bool h;
 };
 hipError_t quant_weight_batched(const QuantWeightItem* items, int count, hipStream_t stream);
 
-// xq = q8((x * inv_s) * (1/act_scale))
-hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const float* inv_s,
-                     const float* act_scale, int8_t* xq, hipStream_t stream);
+// xq = q8((x * inv_s) * (1/act_scale)) (h: binary16 s in place of inv_s and a
+// binary16 act_scale)
+hipError_t quant_act(const void* x, int xt, int64_t m, int64_t k, const void* inv_s,
+                     const void* act_scale, int8_t* xq, bool h, hipStream_t stream);
 
 // the same for up to kMaxBatch projections in one launch; projections fed by
 // the same input read it once
+// h: inv_s holds the binary16 s (the kernel forms fl(1 / s) itself) and
+// act_scale is binary16
 struct ActItem {
     const void* x;
     int xt;
     int64_t m, k;
-    const float* inv_s;
-    const float* act_scale;
+    const void* inv_s;
+    const void* act_scale;
     int8_t* xq;
+    bool h;
 };
 hipError_t quant_act_batched(const ActItem* items, int count, hipStream_t stream);
 
 // y = fp32(acc) * (act_scale * w_scale[n]) in fp32 or bf16, optional int32 acc
+// (h: binary16 act_scale and w_scale, decoded before the product)
 hipError_t gemm_dequant(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
-                        const float* act_scale, const float* w_scale, void* y, int yt, int32_t* acc_out,
+                        const void* act_scale, const void* w_scale, void* y, int yt, int32_t* acc_out, bool h,
                         hipStream_t stream);
 
 // the same for up to kMaxBatch products: those that pick the same large tile
@@ -132,11 +143,12 @@ struct GemmItem {
     const int8_t* xq;
     const int8_t* wq;
     int64_t m, n, k;
-    const float* act_scale;
-    const float* w_scale;
+    const void* act_scale;  // fp32, or binary16 when h
+    const void* w_scale;    // fp32, or binary16 when h
     void* y;
     int yt;
     void* acc_out;  // int32 for int8 codes, fp32 for e4m3 codes, or NULL
+    bool h;
 };
 hipError_t gemm_dequant_batched(const GemmItem* items, int count, hipStream_t stream);
 

@@ -3,7 +3,9 @@ sequence of C-ABI calls that make up the path.
 
 The record kept per layer follows ADR-010's SmoothQuantLinear (int8 weight
 with a per-row scale, a per-tensor activation scale, per-input-channel
-smoothing factors), with fp32 scales. PyTorch only allocates the buffers and
+smoothing factors), with fp32 scales, or with every scale stored in fp16 as
+the ADR's "Consequences" section has it (scales="f16": float16 tensors, the
+_f16 entry points, no stored 1/s). PyTorch only allocates the buffers and
 supplies the stream; all arithmetic is in libsq.so.
 
     step(x_calib, x) = calibrate(x_calib) -> prepare() -> forward(x)
@@ -45,20 +47,25 @@ def _fresh(shape, dtype, device, *streams):
 
 
 class W8A8Linear:
-    def __init__(self, w, alpha: float = 0.5, max_tokens: int = 0, out_dtype=None):
+    def __init__(self, w, alpha: float = 0.5, max_tokens: int = 0, out_dtype=None, scales: str = "f32"):
         import torch
+        if scales not in ("f32", "f16"):
+            raise ValueError(f"scales must be 'f32' or 'f16', got {scales!r}")
         self.w = w
         self.alpha = float(alpha)
+        self.scales = scales
         self.n, self.k = w.shape
         d = w.device
         f32 = torch.float32
+        sd = torch.float16 if scales == "f16" else f32
         self.act_max = torch.zeros(self.k, dtype=f32, device=d)
         self.w_max = torch.empty(self.k, dtype=f32, device=d)
-        self.s = torch.empty(self.k, dtype=f32, device=d)
-        self.inv_s = torch.empty(self.k, dtype=f32, device=d)
-        self.act_scale = torch.empty(4, dtype=f32, device=d)  # one value, padded to 16 bytes
+        self.s = torch.empty(self.k, dtype=sd, device=d)
+        # fp16 storage keeps no 1/s: the kernels form fl(1 / s) from the stored s
+        self.inv_s = torch.empty(self.k, dtype=f32, device=d) if scales == "f32" else None
+        self.act_scale = torch.empty(16 // sd.itemsize, dtype=sd, device=d)  # one value, padded to 16 bytes
         self.wq = torch.empty((self.n, self.k), dtype=torch.int8, device=d)
-        self.w_scale = torch.empty(self.n, dtype=f32, device=d)
+        self.w_scale = torch.empty(self.n, dtype=sd, device=d)
         self.live_max = torch.empty(self.k, dtype=f32, device=d)  # dynamic mode: the batch statistic
         self.dyn_scale = torch.empty(4, dtype=f32, device=d)      # dynamic mode: the batch's scale
         self.out_dtype = out_dtype if out_dtype is not None else torch.bfloat16
@@ -70,6 +77,10 @@ class W8A8Linear:
 
     def prepare(self, stream=None):
         capi.sq_calib_absmax(self.w, self.w_max, False, stream)
+        if self.scales == "f16":
+            capi.sq_smooth_factors_f16(self.act_max, self.w_max, self.alpha, self.s, self.act_scale, stream)
+            capi.sq_quant_weight_f16(self.w, self.s, self.wq, self.w_scale, stream)
+            return
         capi.sq_smooth_factors(self.act_max, self.w_max, self.alpha, self.s, self.inv_s, self.act_scale, stream)
         capi.sq_quant_weight(self.w, self.s, self.wq, self.w_scale, stream)
 
@@ -79,11 +90,16 @@ class W8A8Linear:
         if xq is None:
             xq = self.xq[:m] if self.xq is not None and self.xq.shape[0] >= m else \
                 _fresh((m, self.k), torch.int8, x.device, stream)
-        capi.sq_smooth_quant_act(x, self.inv_s, self.act_scale, xq, stream)
+        if self.scales == "f16":
+            capi.sq_smooth_quant_act_f16(x, self.s, self.act_scale, xq, stream)
+        else:
+            capi.sq_smooth_quant_act(x, self.inv_s, self.act_scale, xq, stream)
         return xq
 
     def quantize_input_dynamic(self, x, xq=None, stream=None):
         import torch
+        if self.scales != "f32":
+            raise ValueError("the dynamic scale mode keeps fp32 scales")
         m = x.shape[0]
         if xq is None:
             xq = self.xq[:m] if self.xq is not None and self.xq.shape[0] >= m else \
@@ -98,7 +114,10 @@ class W8A8Linear:
             y = self.y[:m] if self.y is not None and self.y.shape[0] >= m else \
                 _fresh((m, self.n), self.out_dtype, xq.device, stream)
         a = self.act_scale if act_scale is None else act_scale
-        capi.sq_w8a8_gemm(xq, self.wq, a, self.w_scale, y, acc_out, stream)
+        if self.scales == "f16":
+            capi.sq_w8a8_gemm_f16(xq, self.wq, a, self.w_scale, y, acc_out, stream)
+        else:
+            capi.sq_w8a8_gemm(xq, self.wq, a, self.w_scale, y, acc_out, stream)
         return y
 
     def forward(self, x, y=None, xq=None, acc_out=None, stream=None):
@@ -120,14 +139,30 @@ def _chunks(seq):
     return [seq[i:i + MAX_BATCH] for i in range(0, len(seq), MAX_BATCH)]
 
 
+def _storage(layers):
+    """The scale storage shared by every layer of a block call."""
+    kinds = {l.scales for l in layers}
+    if len(kinds) > 1:
+        raise ValueError("the layers of one block call must share their scale storage")
+    return kinds.pop() if kinds else "f32"
+
+
 def prepare_block(layers, calib=(), stream=None):
     """calibrate + prepare for several W8A8Linear layers in few launches.
     calib: (x, act_max) pairs; act_max is overwritten with the column max of
     |x| (layers that share an input hold the same act_max tensor)."""
+    f16 = _storage(layers) == "f16"
     stats = [(x, a) for x, a in calib] + [(l.w, l.w_max) for l in layers]
     for part in _chunks(stats):
         capi.sq_calib_absmax_batched([x for x, _ in part], [a for _, a in part], False, stream)
     for part in _chunks(list(layers)):
+        if f16:
+            capi.sq_smooth_factors_f16_batched([l.act_max for l in part], [l.w_max for l in part],
+                                               [l.alpha for l in part], [l.s for l in part],
+                                               [l.act_scale for l in part], stream)
+            capi.sq_quant_weight_f16_batched([l.w for l in part], [l.s for l in part], [l.wq for l in part],
+                                             [l.w_scale for l in part], stream)
+            continue
         capi.sq_smooth_factors_batched([l.act_max for l in part], [l.w_max for l in part], [l.alpha for l in part],
                                        [l.s for l in part], [l.inv_s for l in part], [l.act_scale for l in part],
                                        stream)
@@ -142,6 +177,9 @@ def forward_block(layers, xs, stream=None, gemm_stream=None, between=None):
     must already be ordered after `stream` by the caller via `between`, a
     callable run between the two launches). Returns the outputs."""
     import torch
+    f16 = _storage(layers) == "f16"
+    quant = capi.sq_smooth_quant_act_f16_batched if f16 else capi.sq_smooth_quant_act_batched
+    gemm = capi.sq_w8a8_gemm_f16_batched if f16 else capi.sq_w8a8_gemm_batched
     xqs, ys = [], []
     gs = gemm_stream if gemm_stream is not None else stream
     for l, x in zip(layers, xs):
@@ -151,17 +189,16 @@ def forward_block(layers, xs, stream=None, gemm_stream=None, between=None):
         ys.append(l.y[:m] if l.y is not None and l.y.shape[0] >= m else
                   _fresh((m, l.n), l.out_dtype, x.device, gs))
     for part in _chunks(list(range(len(layers)))):
-        capi.sq_smooth_quant_act_batched([xs[i] for i in part], [layers[i].inv_s for i in part],
-                                         [layers[i].act_scale for i in part], [xqs[i] for i in part], stream)
+        quant([xs[i] for i in part], [layers[i].s if f16 else layers[i].inv_s for i in part],
+              [layers[i].act_scale for i in part], [xqs[i] for i in part], stream)
     if between is not None:
         between()
     # products in reverse order of preparation: the codes written last are the
     # ones still in the 256 MB Infinity Cache when the products start
     # (measured on the 13B block: the grouped launch 602 -> 591 us)
     for part in _chunks(list(range(len(layers)))[::-1]):
-        capi.sq_w8a8_gemm_batched([xqs[i] for i in part], [layers[i].wq for i in part],
-                                  [layers[i].act_scale for i in part], [layers[i].w_scale for i in part],
-                                  [ys[i] for i in part], None, gs)
+        gemm([xqs[i] for i in part], [layers[i].wq for i in part], [layers[i].act_scale for i in part],
+             [layers[i].w_scale for i in part], [ys[i] for i in part], None, gs)
     return ys
 
 
@@ -176,6 +213,8 @@ def forward_block_dynamic(layers, xs, stream=None):
     reads each input (the others' live_max are left as they were). Returns
     the outputs."""
     import torch
+    if _storage(layers) != "f32":
+        raise ValueError("the dynamic scale mode keeps fp32 scales")
     distinct, owner = [], {}
     for l, x in zip(layers, xs):
         if id(x) not in owner:

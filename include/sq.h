@@ -341,7 +341,9 @@ sq_status sq_fp8_gemm_batched(int count, const uint8_t* const* xq, const uint8_t
  * Host-only query: the block tile (rows x columns of Y per workgroup) that
  * sq_w8a8_gemm uses for an m x n output on the current device. The choice
  * depends only on m, n and the device's compute-unit count; it does not change
- * the result (the int32 sums are exact in any order). Launches nothing.
+ * the result (the int32 sums are exact in any order). Launches nothing. For
+ * m <= 4 the product runs on the vector ALUs, a workgroup per 4 weight rows:
+ * the reported tile is (m rounded up to 1, 2 or 4) x 4.
  */
 sq_status sq_gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n);
 

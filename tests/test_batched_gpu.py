@@ -186,14 +186,15 @@ def test_quant_act_batched():
 
 def test_gemm_batched():
     """Products that share a large tile, one that picks another width, a skinny
-    (m <= 64) and a register-staged one, mixed output types, some with the int32
-    accumulator: every output bit-exact against the oracle."""
+    (m <= 64), a vector-ALU (m <= 4) and a register-staged one, mixed output
+    types, some with the int32 accumulator: every output bit-exact against the
+    oracle."""
     import torch
     cases = [(512, 5120, 192, True, True), (300, 5120, 320, False, False), (1024, 8192, 128, True, False),
              (40, 1000, 704, True, True), (200, 600, 256, False, True), (256, 4112, 64, True, False),
-             (0, 512, 64, True, False), (2048, 5120, 64, True, True)]
+             (0, 512, 64, True, False), (2048, 5120, 64, True, True), (3, 1003, 4160, False, True)]
     tilings = {capi.sq_gemm_tiling(m, n) for m, n, *_ in cases if m}
-    assert {(256, 128), (256, 160), (64, 16)} <= tilings, tilings
+    assert {(256, 128), (256, 160), (64, 16), (4, 4)} <= tilings, tilings
     g = synth.rng(4700)
     xqs, wqs, scs, wss, ys, accs, host = [], [], [], [], [], [], []
     for m, n, k, bf16, with_acc in cases:

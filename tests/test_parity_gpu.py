@@ -188,7 +188,11 @@ GEMM_CASES = [(1, 16, 64), (5, 48, 1088), (129, 257, 320), (300, 600, 2048), (51
               (4000, 4100, 64), (1000, 11008, 320),
               # decode widths: 17-32 and 33-64 rows, 8-wave blocks (>= 512 column blocks) and
               # 16-wave blocks, K steps not a multiple of waves x steps in flight
-              (24, 8200, 192), (17, 1000, 4160), (40, 8192, 320), (64, 300, 704), (9, 8208, 1344)]
+              (24, 8200, 192), (17, 1000, 4160), (40, 8192, 320), (64, 300, 704), (9, 8208, 1344),
+              # the vector-ALU kernel (m <= 4): 2 and 4 activation rows, ragged weight-row blocks, a
+              # partial last 1 KB chunk, up to 4 chunks per wave in flight and, past 16 KB of K,
+              # a second group of chunks
+              (2, 1003, 4160), (3, 4100, 11008), (4, 262, 20480), (1, 4097, 13824)]
 
 
 def reachable_tilings():

@@ -164,6 +164,17 @@ struct EpiDequant {
             }
         }
     }
+    // one output element (the vector-ALU decode kernel)
+    __device__ void one(AccT v, int64_t row, int64_t col) {
+        if (row >= M || col >= N) return;
+        const float val = __fmul_rn((float)v, __fmul_rn(a, ws(col)));
+        const int64_t idx = row * N + col;
+        if constexpr (kBF16Out)
+            ((uint16_t*)y)[idx] = (uint16_t)sqd::f32_to_bf16_bits(val);
+        else
+            ((float*)y)[idx] = val;
+        if (acc_out) acc_out[idx] = v;
+    }
     // Eight consecutive columns col .. col + 7 (col % 8 == 0) owned by one
     // lane for a run of rows: their merged scales are loaded once.
     struct Cols {
@@ -869,6 +880,110 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(const int8_t* __res
     epi.end((char*)part);
 }
 
+// ---- vector-ALU kernel (decode: m <= 4) -------------------------------------------
+//
+// At m <= 4 the product is the weight stream and nothing else, so it runs on
+// the vector ALUs where every weight load can be fully coalesced: a block of 4
+// waves owns kGemvR consecutive weight rows; wave w takes the 1 KB K chunks w,
+// w + 4, w + 8, ... (CH chunks of them in flight per group); a lane holds 16
+// bytes of each activation row per chunk and loads 16 contiguous bytes of each
+// weight row per chunk (one wave instruction reads 1 KB of one row), and
+// accumulates `v_dot4_i32_i8` products into one int32 per (weight row,
+// activation row). The partials are added across the wave (DPP) and across
+// the 4 waves (LDS): integer sums, exact in any order. (The 16-row MFMA tiles
+// of the skinny kernel read 64 bytes of each of 16 rows per instruction and an
+// activation fragment per weight fragment; measured on the 7B decode shapes at
+// m = 1, this kernel takes 4.8 / 8.8 / 8.8 us where that one takes 5.5 / 11.2 /
+// 12.8 us for 4096x4096 / 11008x4096 / 4096x11008, cold weights.)
+constexpr int kGemvMaxM = 4;
+constexpr int kGemvR = 4;    // weight rows per block
+constexpr int kGemvCH = 4;   // most 1 KB chunks per wave in flight
+
+template <int MB, int CH, class Epi>
+__global__ __launch_bounds__(256) void gemv_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+                                                   int64_t M, int64_t N, int64_t Kb, Epi epi) {
+    constexpr int R = kGemvR;
+    __shared__ int red[4][R][MB];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t r0 = (int64_t)blockIdx.x * R;
+    const int64_t nchunk = (Kb + 1023) / 1024;
+    int acc[R][MB];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[r][m] = 0;
+    for (int64_t c0 = wave; c0 < nchunk; c0 += 4 * CH) {
+        v4i xv[CH][MB], wv[R][CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int64_t kc = (c0 + 4 * c) * 1024 + 16 * lane;
+            const bool in = c0 + 4 * c < nchunk && kc < Kb;
+#pragma unroll
+            for (int m = 0; m < MB; ++m) xv[c][m] = in && m < M ? *(const v4i*)(A + m * Kb + kc) : v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                wv[r][c] = in && r0 + r < N ? __builtin_nontemporal_load((const v4i*)(B + (r0 + r) * Kb + kc))
+                                            : v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    int t = acc[r][m];
+                    t = __builtin_amdgcn_sdot4(wv[r][c].x, xv[c][m].x, t, false);
+                    t = __builtin_amdgcn_sdot4(wv[r][c].y, xv[c][m].y, t, false);
+                    t = __builtin_amdgcn_sdot4(wv[r][c].z, xv[c][m].z, t, false);
+                    acc[r][m] = __builtin_amdgcn_sdot4(wv[r][c].w, xv[c][m].w, t, false);
+                }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            const int t = sqd::wave_sum(acc[r][m]);
+            if (lane == 0) red[wave][r][m] = t;
+        }
+    __syncthreads();
+    epi.begin();
+    if (threadIdx.x < R * MB) {
+        const int r = threadIdx.x / MB, m = threadIdx.x % MB;
+        epi.one(red[0][r][m] + red[1][r][m] + red[2][r][m] + red[3][r][m], m, r0 + r);
+    }
+}
+
+template <class E>
+struct IsDequant : std::false_type {};
+template <bool kBF16Out, class AccT, bool kH>
+struct IsDequant<EpiDequant<kBF16Out, AccT, kH>> : std::is_same<AccT, int32_t> {};
+
+inline int gemv_rows(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
+
+template <int MB, class Epi>
+hipError_t launch_gemv_m(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t Kb, Epi epi,
+                         hipStream_t stream) {
+    const int64_t per_wave = ((Kb + 1023) / 1024 + 3) / 4;  // chunks of the busiest wave
+    const dim3 grid((unsigned)((N + kGemvR - 1) / kGemvR)), block(256);
+    switch (per_wave >= kGemvCH ? kGemvCH : (int)per_wave) {
+        case 1: gemv_kernel<MB, 1, Epi><<<grid, block, 0, stream>>>(A, B, M, N, Kb, epi); break;
+        case 2: gemv_kernel<MB, 2, Epi><<<grid, block, 0, stream>>>(A, B, M, N, Kb, epi); break;
+        case 3: gemv_kernel<MB, 3, Epi><<<grid, block, 0, stream>>>(A, B, M, N, Kb, epi); break;
+        default: gemv_kernel<MB, kGemvCH, Epi><<<grid, block, 0, stream>>>(A, B, M, N, Kb, epi); break;
+    }
+    return hipGetLastError();
+}
+
+template <class Epi>
+hipError_t launch_gemv(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t Kb, Epi epi,
+                       hipStream_t stream) {
+    switch (gemv_rows(M)) {
+        case 1: return launch_gemv_m<1>(A, B, M, N, Kb, epi, stream);
+        case 2: return launch_gemv_m<2>(A, B, M, N, Kb, epi, stream);
+        default: return launch_gemv_m<4>(A, B, M, N, Kb, epi, stream);
+    }
+}
+
 // Tile configurations.
 //   D256 / D224 / D192 / D160 / D128: the pipelined direct-to-LDS kernel,
 //         256 x BN tiles (BN = 32 * TN); the width is chosen per problem so the
@@ -974,6 +1089,8 @@ template <class Op, class Epi>
 hipError_t dispatch(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t Kb, Epi epi,
                     hipStream_t stream) {
     if constexpr (std::is_same<Op, OpI8>::value) {
+        if constexpr (IsDequant<Epi>::value)
+            if (M <= kGemvMaxM) return launch_gemv(A, B, M, N, Kb, epi, stream);
         if (M <= kSkinnyMaxM) {
             if (M <= 16) return launch_skinny<1>(A, B, M, N, Kb, epi, stream);
             if (M <= 32) return launch_skinny<2>(A, B, M, N, Kb, epi, stream);
@@ -1204,6 +1321,11 @@ hipError_t gemm_fp8(const uint8_t* xq, const uint8_t* wq, int64_t m, int64_t n, 
 }
 
 void gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n) {
+    if (m <= kGemvMaxM) {  // the vector-ALU kernel: gemv_rows(m) activation rows x kGemvR weight rows
+        *block_m = gemv_rows(m);
+        *block_n = kGemvR;
+        return;
+    }
     const TileCfg c = choose_cfg(m, n);
     *block_m = kCfgBM[c];
     *block_n = kCfgBN[c];

@@ -114,6 +114,17 @@ __device__ __forceinline__ float wave_max(float v) {
     return __uint_as_float(max(max(r0, r1), max(r2, r3)));
 }
 
+// Wave-wide sum of int32 values (64 lanes, all active): the same DPP pattern
+// as wave_max with integer adds, which are exact in any order.
+__device__ __forceinline__ int wave_sum(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // row_ror:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+           __builtin_amdgcn_readlane(v, 48);
+}
+
 // block-wide maximum of non-negative values; every thread gets the result.
 // `red` holds >= NWAVES floats.
 template <int NWAVES>

@@ -343,7 +343,9 @@ sq_status sq_fp8_gemm_batched(int count, const uint8_t* const* xq, const uint8_t
  * depends only on m, n and the device's compute-unit count; it does not change
  * the result (the int32 sums are exact in any order). Launches nothing. For
  * m <= 4 the product runs on the vector ALUs, a workgroup per 4 weight rows:
- * the reported tile is (m rounded up to 1, 2 or 4) x 4.
+ * the reported tile is (m rounded up to 1, 2 or 4) x 4; for 4 < m <= 64 the
+ * skinny matrix-core kernel: (16, 32 or 64 activation rows) x (16 weight rows,
+ * or 48 when m > 32 and n >= 8192).
  */
 sq_status sq_gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n);
 

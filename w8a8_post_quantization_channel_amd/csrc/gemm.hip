@@ -812,72 +812,114 @@ __global__ __launch_bounds__(256) void gemm_dma_grouped_kernel(const GemmTable t
                           xcd_tile(b, ntiles), epi, lds);
 }
 
-// ---- skinny kernel (decode: m <= 64) -------------------------------------------
+// ---- skinny kernel (decode: 4 < m <= 64) ------------------------------------------
 //
 // The product is bound by streaming the int8 weight once from HBM. A block of
-// W waves owns 16 output columns (16 weight rows) and all of K; wave w takes
-// every W-th 64-byte K step, so the waves read disjoint parts of the same
-// rows and their int32 partials are summed in LDS in a fixed order (exact). v_mfma_i32_16x16x64_i8 with the m rows padded to 16 (MT
-// tiles of 16 rows): lane l holds row l % 16 and bytes 16 (l / 16) .. +15 of
-// a 64-byte K step, for both operands. Weight rows past n and activation rows
-// past m are clamped to the last valid row: their outputs are never stored.
-// Each lane keeps U K steps of weight bytes in flight.
-
-template <int W, int MT, int U, class Epi>
-__global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(const int8_t* __restrict__ A,
-                                                             const int8_t* __restrict__ B, int64_t M, int64_t N,
-                                                             int64_t Kb, Epi epi) {
-    __shared__ v4i part[W][MT][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int64_t brow = min<int64_t>(n0 + (lane & 15), N - 1);
-    const int kl = (lane >> 4) * 16;  // byte offset within a 64-byte K step
-    const int8_t* bp = B + brow * Kb + kl;
-    const int8_t* ap[MT];
+// 4 waves owns BNR weight rows (16 or 48) and walks K in 512-byte chunks
+// through NS LDS stages. A stage holds AR = max(16, MB) activation rows and
+// the BNR weight rows, 512 bytes each, filled by buffer_load ... lds two rows
+// per instruction (lanes 0-31 one row, 32-63 the next: four whole cache lines
+// each). Loading the rows whole matters: measured on the 7B decode shapes, the
+// same weight bytes read as 16 rows x 64 bytes per instruction (the MFMA
+// fragment layout, straight into registers) stream at about two thirds of the
+// rate. Activation rows >= MB are never loaded (they only feed output rows that
+// are never stored); rows in [m, MB) and bytes past k read as zero. 16-byte
+// chunk c of a row r sits at position c ^ (r & 15), so the 16 rows of a
+// fragment read land in distinct banks. Wave w computes the 64-byte K steps w
+// and w + 4 of each chunk with v_mfma_i32_16x16x64_i8 (lane l: row l % 16,
+// bytes 16 (l / 16) .. +15 of the step, for both operands); the four waves'
+// int32 partials are added through LDS at the end (exact in any order).
+template <int MB, int BNR, int NS, class Epi>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const int8_t* __restrict__ A,
+                                                          const int8_t* __restrict__ B, int64_t M, int64_t N,
+                                                          int64_t Kb, Epi epi) {
+    constexpr int AR = MB < 16 ? 16 : MB, MT = AR / 16, NR = BNR / 16;
+    constexpr int L = (MB + BNR) / 8;  // load instructions per wave per chunk (2 rows each)
+    static_assert((MB + BNR) % 8 == 0 && MB % 2 == 0, "whole load rounds; a load's two rows on one side");
+    constexpr int KC = 512, STAGE = (AR + BNR) * KC;
+    static_assert(NS * STAGE <= 160 * 1024 && (NS - 2) * L < 64, "stages fit; vmcnt range");
+    static_assert(4 * NR * MT * 64 * 16 <= NS * STAGE, "the partial sums fit in the stages");
+    __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t n0 = (int64_t)blockIdx.x * BNR;
+    const int64_t nchunk = (Kb + KC - 1) / KC;
+    const v4i ra = tile_rsrc(A, M, Kb);
+    const v4i rb = tile_rsrc(B + n0 * Kb, min<int64_t>(BNR, N - n0), Kb);
+    // load j of wave w fills loaded rows idx0 = 2 (4 j + w) and idx0 + 1:
+    // activation rows while idx0 < MB, else weight rows idx0 - MB
+    const int half = lane >> 5, pos = lane & 31;
+    int voff[L];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) ap[t] = A + min<int64_t>(16 * t + (lane & 15), M - 1) * Kb + kl;
-
-    v4i acc[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = v4i{0, 0, 0, 0};
-
-    const int64_t nsteps = Kb / 64;
-    // K steps of this wave: wave, wave + W, wave + 2W, ..., U of them in flight
-    // per batch; in the last batch steps past the end load nothing and add
-    // zeros, so a ragged remainder is not walked one latency at a time
-    for (int64_t st = wave; st < nsteps; st += (int64_t)W * U) {
-        v4i b[U], a[U][MT];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t su = st + (int64_t)u * W;
-            const int64_t off = su * 64;
-            const bool in = su < nsteps;
-            b[u] = in ? __builtin_nontemporal_load((const v4i*)(bp + off)) : v4i{0, 0, 0, 0};
-#pragma unroll
-            for (int t = 0; t < MT; ++t) a[u][t] = in ? *(const v4i*)(ap[t] + off) : v4i{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int t = 0; t < MT; ++t) acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][t], b[u], acc[t], 0, 0, 0);
+    for (int j = 0; j < L; ++j) {
+        const int idx0 = 2 * (4 * j + wave);
+        const int row = (idx0 < MB ? idx0 : idx0 - MB) + half;
+        voff[j] = row * (int)Kb + ((pos ^ (row & 15)) << 4);
     }
-
+    auto issue = [&](int64_t c, int stage) {
+        const int soff = (int)(c * KC);
 #pragma unroll
-    for (int t = 0; t < MT; ++t) part[wave][t][lane] = acc[t];
+        for (int j = 0; j < L; ++j) {
+            const int idx0 = __builtin_amdgcn_readfirstlane(2 * (4 * j + wave));
+            const bool isa = idx0 < MB;
+            const int row = (isa ? idx0 : idx0 - MB) + half;
+            const bool cut = c * KC + ((pos ^ (row & 15)) << 4) >= Kb;  // past the end of the row
+            const int srow0 = isa ? idx0 : AR + idx0 - MB;
+            dma16(isa ? ra : rb, lds_addr(lds) + (uint32_t)(stage * STAGE + srow0 * KC), cut ? kOutOfRange : voff[j],
+                  soff);
+        }
+    };
+    v4i acc[NR][MT];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = v4i{0, 0, 0, 0};
+    const int frow = lane & 15, kg = lane >> 4;
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+        if (p < nchunk) issue(p, p);
+    for (int64_t c = 0; c < nchunk; ++c) {
+        // chunk c landed (NS - 2 younger chunks may be in flight, fewer at the end)
+        if (c + NS - 2 < nchunk)
+            wait_vmcnt<(NS - 2) * L>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();  // ... for every wave; the stage read at chunk c - 1 is free
+        if (c + NS - 1 < nchunk) issue(c + NS - 1, (int)((c + NS - 1) % NS));
+        const char* st = lds + (c % NS) * STAGE;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int ch = ((4 * (wave + 4 * q) + kg) ^ frow) << 4;
+            v4i a[MT], b[NR];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) a[t] = *(const v4i*)(st + (16 * t + frow) * KC + ch);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) b[r] = *(const v4i*)(st + (AR + 16 * r + frow) * KC + ch);
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    acc[r][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b[r], acc[r][t], 0, 0, 0);
+        }
+    }
+    __syncthreads();  // every wave is done with the stages
+    v4i* part = (v4i*)lds;  // [wave][r][t][lane]
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) part[((wave * NR + r) * MT + t) * 64 + lane] = acc[r][t];
     __syncthreads();
     epi.begin();
-    if (wave == 0) {
+    for (int rt = wave; rt < NR * MT; rt += 4) {
+        const int r = rt / MT, t = rt % MT;
+        v4i sum = part[(r * MT + t) * 64 + lane];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            v4i sum = part[0][t][lane];
-#pragma unroll
-            for (int w = 1; w < W; ++w) sum += part[w][t][lane];
-            // 16x16 accumulator: lane holds column lane % 16, rows 4 (lane / 16) + v
-            epi.template tile<16>(sum, 16 * t + 4 * (lane >> 4), n0 + (lane & 15));
-        }
+        for (int w = 1; w < 4; ++w) sum += part[((w * NR + r) * MT + t) * 64 + lane];
+        // 16x16 accumulator: lane holds column lane % 16, rows 4 (lane / 16) + v
+        epi.template tile<16>(sum, 16 * t + 4 * (lane >> 4), n0 + 16 * r + (lane & 15));
     }
     __syncthreads();
-    epi.end((char*)part);
+    epi.end(lds);
 }
 
 // ---- vector-ALU kernel (decode: m <= 4) -------------------------------------------
@@ -1069,20 +1111,41 @@ hipError_t launch_dma(const int8_t* A, const int8_t* B, int64_t M, int64_t N, in
     return hipGetLastError();
 }
 
-// A column block of 16 outputs holds W waves splitting K. Few column blocks
-// (n below two per compute unit, e.g. a down projection) get 16 waves so each
-// compute unit still keeps enough weight bytes in flight; otherwise 8 waves,
-// and several blocks share a compute unit.
-template <int MT, class Epi>
+// Skinny configurations (activation rows MB, weight rows per block BNR, LDS
+// stages NS), measured on the 7B decode shapes with cold weights: many blocks
+// (n >= 32 x compute units of 16 rows) favour two stages and more blocks per
+// compute unit, few blocks four stages; at m > 32, wide outputs take 48 weight
+// rows per block (the activation bytes per weight byte drop 3x). Epilogues
+// other than the dequantization keep one block per 16 weight rows (the
+// squared-error slots are counted that way).
+template <int MB, class Epi>
+hipError_t launch_skinny_mb(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t Kb, Epi epi,
+                            hipStream_t stream) {
+    const dim3 block(256);
+    const unsigned b16 = (unsigned)((N + 15) / 16);
+    if constexpr (MB == 64) {
+        if (IsDequant<Epi>::value && N >= 8192) {
+            gemm_skinny_kernel<64, 48, 2, Epi><<<dim3((unsigned)((N + 47) / 48)), block, 0, stream>>>(A, B, M, N, Kb, epi);
+            return hipGetLastError();
+        }
+        gemm_skinny_kernel<64, 16, 3, Epi><<<dim3(b16), block, 0, stream>>>(A, B, M, N, Kb, epi);
+        return hipGetLastError();
+    } else {
+        if (IsDequant<Epi>::value && b16 >= 2 * (unsigned)cu_count())
+            gemm_skinny_kernel<MB, 16, 2, Epi><<<dim3(b16), block, 0, stream>>>(A, B, M, N, Kb, epi);
+        else
+            gemm_skinny_kernel<MB, 16, 4, Epi><<<dim3(b16), block, 0, stream>>>(A, B, M, N, Kb, epi);
+        return hipGetLastError();
+    }
+}
+
+template <class Epi>
 hipError_t launch_skinny(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t Kb, Epi epi,
                          hipStream_t stream) {
-    constexpr int U = MT == 1 ? 8 : 4;
-    const unsigned blocks = (unsigned)((N + 15) / 16);
-    if (blocks < 2 * (unsigned)cu_count())
-        gemm_skinny_kernel<16, MT, U, Epi><<<dim3(blocks), dim3(64 * 16), 0, stream>>>(A, B, M, N, Kb, epi);
-    else
-        gemm_skinny_kernel<8, MT, U, Epi><<<dim3(blocks), dim3(64 * 8), 0, stream>>>(A, B, M, N, Kb, epi);
-    return hipGetLastError();
+    if (M <= 8) return launch_skinny_mb<8>(A, B, M, N, Kb, epi, stream);
+    if (M <= 16) return launch_skinny_mb<16>(A, B, M, N, Kb, epi, stream);
+    if (M <= 32) return launch_skinny_mb<32>(A, B, M, N, Kb, epi, stream);
+    return launch_skinny_mb<64>(A, B, M, N, Kb, epi, stream);
 }
 
 template <class Op, class Epi>
@@ -1091,11 +1154,7 @@ hipError_t dispatch(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int6
     if constexpr (std::is_same<Op, OpI8>::value) {
         if constexpr (IsDequant<Epi>::value)
             if (M <= kGemvMaxM) return launch_gemv(A, B, M, N, Kb, epi, stream);
-        if (M <= kSkinnyMaxM) {
-            if (M <= 16) return launch_skinny<1>(A, B, M, N, Kb, epi, stream);
-            if (M <= 32) return launch_skinny<2>(A, B, M, N, Kb, epi, stream);
-            return launch_skinny<4>(A, B, M, N, Kb, epi, stream);
-        }
+        if (M <= kSkinnyMaxM) return launch_skinny(A, B, M, N, Kb, epi, stream);
     }
     switch (choose_cfg(M, N)) {
         case kD256: return launch_dma<Op, 8>(A, B, M, N, Kb, epi, stream);
@@ -1324,6 +1383,11 @@ void gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n) {
     if (m <= kGemvMaxM) {  // the vector-ALU kernel: gemv_rows(m) activation rows x kGemvR weight rows
         *block_m = gemv_rows(m);
         *block_n = kGemvR;
+        return;
+    }
+    if (m <= kSkinnyMaxM) {  // the skinny kernel: activation rows x weight rows per block
+        *block_m = m <= 16 ? 16 : m <= 32 ? 32 : 64;
+        *block_n = m > 32 && n >= 8192 ? 48 : 16;
         return;
     }
     const TileCfg c = choose_cfg(m, n);

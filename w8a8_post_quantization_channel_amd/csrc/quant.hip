@@ -1,18 +1,18 @@
 // quant.hip -- the two quantization passes of the SmoothQuant W8A8 layer.
 //
 // quant_weight: offline fold W' = W diag(s) (kwkr.cn blog §3.2) and symmetric
-//   int8 with one scale per output row (ADR-010 "Context" item 3). Rows stream
-//   through an LDS ring (global -> LDS loads running ahead of the math); the
-//   threads of a block own fixed columns (their s values in registers) and
-//   keep W' in registers between the row max and the quantize pass, so W is
-//   read from HBM exactly once.
+//   int8 with one scale per output row (ADR-010 "Context" item 3). A block
+//   owns whole rows: its threads load every vector of them at once, keep W'
+//   in registers between the row max and the quantize pass, and store the
+//   codes with streaming stores, so W is read from HBM exactly once.
 // quant_act: runtime x * (1/s) strictly before the per-tensor quantizer
 //   (kwkr.cn blog §3.2 and §5.2; ADR-010 "Key design" items 4-5). A lane owns
 //   one 16-byte column vector and keeps its inv_s values in registers while
 //   the four waves of a block walk interleaved rows.
 //
-// The weight pass works on "groups" of 16 consecutive elements of a row (32
-// bytes of bf16, 64 of fp32), which become 16 int8 codes: one 16-byte store.
+// The pass for rows longer than 4096 vectors works on "groups" of 16
+// consecutive elements of a row (32 bytes of bf16, 64 of fp32), which become
+// 16 int8 codes: one 16-byte store.
 #include <algorithm>
 #include <type_traits>
 
@@ -77,29 +77,27 @@ __device__ __forceinline__ void store_codes(int8_t* __restrict__ dst, const int 
     }
 }
 
-// Weight rows streamed through LDS. A persistent block of WV waves walks
-// "stages" of RB consecutive rows (a contiguous run of W), kept in a ring of NS
-// LDS buffers filled by buffer_load ... lds, so the loads of the next stages
-// fly while this one is reduced and quantized. The RB * kvec 16-byte vectors
-// of a stage are dealt out flat: thread t takes vectors j = t, t + T, ...
-// (T threads, at most NV each), so every thread has the same work whatever the
-// row length; the row r_j = j / kvec and column c_j = j % kvec of each of its
-// slots are fixed for a weight, and the thread keeps the s values of its
-// columns in registers. Per stage: pass 1 forms W' = W * s in registers and
-// the row maxima (a select per row, wave shuffles, one LDS exchange and
-// barrier), pass 2 quantizes the registers and stores 4 or 8 codes per vector
-// (the codes of a stage are as contiguous as its input). W is read from HBM
-// once.
+// Weight rows as whole-row blocks. A block of T = 64 WV threads (WV <= 16,
+// chosen per weight so that NV * T just covers a row of kvec 16-byte vectors)
+// quantizes RPB consecutive rows. Thread t owns the vectors t, t + T, ... (NV
+// of them) of each of the rows and issues all RPB * NV loads at once; it
+// loads the s values of its columns once for the RPB rows, forms W' = W * s in
+// registers, and the row maxima come from wave reductions and one LDS
+// exchange. The codes then go out with streaming stores (the codes of a
+// weight are read back only by later GEMMs). W is read from HBM once.
 //
-// One launch can cover several weights (the projections of a block): their
-// stages are numbered one after the other, item i owning stages
-// [first[i], first[i + 1]), and a block that moves on to the next item
-// recomputes its slots and reloads its s registers.
+// No block is persistent: a compute unit holds several blocks at a time and
+// starts the next one as one retires, which keeps more of W in flight than a
+// persistent block ring: measured on MI355X over the Llama-2 projections, the
+// whole-row blocks are 10-25 % faster than an LDS ring of prefetched stages.
+//
+// One launch can cover several weights of equal block size (the projections
+// of a block): item i owns the blocks [first[i], first[i + 1]).
 
 struct QwTable {
     int count;
-    int64_t first[sqk::kMaxBatch + 1];
-    const int8_t* w[sqk::kMaxBatch];
+    int32_t first[sqk::kMaxBatch + 1];
+    const u32x4* w[sqk::kMaxBatch];
     const void* s[sqk::kMaxBatch];  // fp32, or binary16 (H)
     int8_t* wq[sqk::kMaxBatch];
     void* w_scale[sqk::kMaxBatch];  // fp32, or binary16 (H)
@@ -140,189 +138,149 @@ __device__ __forceinline__ void store_scale(void* p, int64_t i, uint32_t bits) {
         ((float*)p)[i] = __uint_as_float(bits);
 }
 
-__device__ __forceinline__ int stage_item(const QwTable& tab, int64_t g) {
-    int i = 0;
-    while (i + 1 < tab.count && g >= tab.first[i + 1]) ++i;
-    return i;
+// the E scale values of column vector c (E = 8: bf16 weights, E = 4: fp32)
+template <int E, bool H>
+__device__ __forceinline__ void load_scales(const void* __restrict__ s, int64_t c, float (&sv)[E]) {
+    if constexpr (H) {
+        uint32_t d[E / 2];
+        if constexpr (E == 8) {
+            const u32x4 t = ((const u32x4*)s)[c];
+            d[0] = t.x; d[1] = t.y; d[2] = t.z; d[3] = t.w;
+        } else {
+            const sqd::u32x2 t = ((const sqd::u32x2*)s)[c];
+            d[0] = t.x; d[1] = t.y;
+        }
+#pragma unroll
+        for (int u = 0; u < E / 2; ++u) {
+            sv[2 * u] = sqd::f16_dec((uint16_t)(d[u] & 0xffffu));
+            sv[2 * u + 1] = sqd::f16_dec((uint16_t)(d[u] >> 16));
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < E / 4; ++h) {
+            const u32x4 t = ((const u32x4*)s)[c * (E / 4) + h];
+            sv[4 * h + 0] = __uint_as_float(t.x);
+            sv[4 * h + 1] = __uint_as_float(t.y);
+            sv[4 * h + 2] = __uint_as_float(t.z);
+            sv[4 * h + 3] = __uint_as_float(t.w);
+        }
+    }
 }
 
-template <int EB, int WV, int NV, int RB, int CPW, int NS, bool FP8, bool H>
-__global__ __launch_bounds__(64 * WV) void quant_weight_stream_kernel(const QwTable tab) {
+template <int EB, int NV, int RPB, bool FP8, bool H>
+__global__ __launch_bounds__(1024) void quant_weight_rows_kernel(const QwTable tab) {
     static_assert(!(FP8 && H), "binary16 scales are for int8 codes");
-    constexpr int T = 64 * WV;                 // threads
-    constexpr int E = 16 / EB;                 // elements per 16-byte vector
-    constexpr int STAGE = CPW * WV * 1024;     // bytes, >= RB rows (checked by the launcher)
-    constexpr int W32 = E / 4;                 // dwords of codes per vector
-    static_assert(NS == 2 || NS == 3, "ring depth");
-    static_assert((NS - 1) * CPW < 64, "vmcnt range");
-    __shared__ __attribute__((aligned(1024))) char ring[NS * STAGE];
-    __shared__ float part[RB][WV];
+    constexpr int E = 16 / EB;    // elements per 16-byte vector
+    constexpr int W32 = E / 4;    // dwords of codes per vector
+    __shared__ float part[RPB][16];
 
-    const int t = threadIdx.x, lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int64_t nstages = tab.first[tab.count];
+    const int b = blockIdx.x;
+    int it = 0;
+    while (it + 1 < tab.count && b >= tab.first[it + 1]) ++it;
+    const u32x4* __restrict__ w = tab.w[it];
+    const int64_t n = tab.n[it], kvec = tab.kvec[it];
+    const int64_t r0 = (int64_t)(b - tab.first[it]) * RPB;
+    const int T = blockDim.x, WV = T >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 
-    // this thread's slots for the current weight: vector j = t + i T of a
-    // stage (live when j < RB * kvec), its row and its s values
-    float sv[NV][E];
-    int row[NV];
     bool live[NV];
-    int cur = -1;
-    auto setup = [&](int it) {
-        const int kvec = (int)tab.kvec[it];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int j = t + i * T;
-            live[i] = j < RB * kvec;
-            row[i] = live[i] ? j / kvec : RB;
-            const int c = live[i] ? j - row[i] * kvec : 0;
+    for (int i = 0; i < NV; ++i) live[i] = t + i * T < kvec;
+    u32x4 raw[RPB][NV];
 #pragma unroll
-            for (int e = 0; e < E; ++e) sv[i][e] = live[i] ? scale_at<H>(tab.s[it], c * E + e) : 0.0f;
+    for (int p = 0; p < RPB; ++p)
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            raw[p][i] = live[i] && r0 + p < n ? __builtin_nontemporal_load(w + (r0 + p) * kvec + t + i * T)
+                                              : u32x4{0, 0, 0, 0};
+    float sv[NV][E];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        if (live[i]) {
+            load_scales<E, H>(tab.s[it], t + i * T, sv[i]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) sv[i][e] = 0.0f;
         }
-        cur = it;
-    };
+    }
 
-    // stage g -> ring slot: CPW loads per wave, chunk c = wave + WV j of the
-    // stage's contiguous bytes (zeros past the last row of its weight, and for
-    // stages past the end)
-    auto issue = [&](int64_t g, int slot) {
-        const bool in = g < nstages;
-        const int it = in ? stage_item(tab, g) : 0;
-        const int64_t rowbytes = tab.kvec[it] * 16;
-        const int64_t r0 = in ? (g - tab.first[it]) * RB : 0;
-        const int64_t rows = in ? min<int64_t>(RB, tab.n[it] - r0) : 0;
-        const sqd::i32x4 rsrc = sqd::tile_rsrc(tab.w[it] + r0 * rowbytes, rows, rowbytes);
-        const uint32_t base = sqd::lds_addr(ring) + (uint32_t)(slot * STAGE) + (uint32_t)wave * 1024u;
+    // pass 1: W' = W * s in registers and the row maxima
+    float wv[RPB][NV][E];
 #pragma unroll
-        for (int j = 0; j < CPW; ++j)
-            sqd::dma16(rsrc, base + (uint32_t)(j * WV * 1024), lane * 16, (j * WV + wave) * 1024);
-    };
-
-    // Codes of a stage are stored one round late (after the next stage's
-    // wait), so the wait below, which also counts stores, finds them long
-    // done; it is exact for the loads because loads complete in order and
-    // exactly NS - 2 stages of loads are issued after the awaited one (the s
-    // reloads at an item change only add younger operations, which makes the
-    // wait stricter, never looser).
-    uint32_t codes[NV][W32];
-    uint32_t scale[RB];  // bit patterns (fp32, or binary16 when H)
-    int64_t prev = -1;  // stage whose codes are pending
-    auto flush = [&]() {
-        if (prev < 0) return;
-        const int64_t kvec = tab.kvec[cur], n = tab.n[cur];
-        const int64_t p0 = (prev - tab.first[cur]) * RB;
-        int8_t* dst = tab.wq[cur] + p0 * kvec * E;
+    for (int p = 0; p < RPB; ++p) {
+        float mx = 0.0f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            if (live[i] && p0 + row[i] < n) {
-                const int64_t j = t + (int64_t)i * T;
-                if constexpr (W32 == 2)
-                    *(sqd::u32x2*)(dst + j * E) = sqd::u32x2{codes[i][0], codes[i][1]};
-                else
-                    *(uint32_t*)(dst + j * E) = codes[i][0];
+            float e8[E];
+            sqd::unpack16<E>(raw[p][i], e8);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                wv[p][i][e] = __fmul_rn(e8[e], sv[i][e]);
+                mx = __builtin_fmaxf(mx, __builtin_fabsf(wv[p][i][e]));
             }
         }
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-            if (t == r && p0 + r < n) store_scale<H>(tab.w_scale[cur], p0 + r, scale[r]);
-    };
+        mx = sqd::wave_max(mx);
+        if (lane == 0) part[p][wave] = mx;
+    }
+    __syncthreads();
 
-    int64_t g = blockIdx.x;
-    int slot = 0;
-    if (g < nstages) setup(stage_item(tab, g));
+    // pass 2: the row scale and the codes
 #pragma unroll
-    for (int p = 0; p < NS - 1; ++p) issue(g + (int64_t)p * gridDim.x, p);
-    for (; g < nstages; g += gridDim.x) {
-        sqd::wait_vmcnt<(NS - 2) * CPW>();  // this stage landed (for this wave's loads) ...
-        __syncthreads();                    // ... and for every wave; the slot read last round is free
-        const int it = stage_item(tab, g);
-        flush();  // the previous stage's codes (its weight is still `cur`)
-        issue(g + (int64_t)(NS - 1) * gridDim.x, (slot + NS - 1) % NS);
-        if (it != cur) setup(it);
-        const char* st = ring + slot * STAGE;
-        float wv[NV][E];
-        float mx[RB];
-#pragma unroll
-        for (int r = 0; r < RB; ++r) mx[r] = 0.0f;
+    for (int p = 0; p < RPB; ++p) {
+        if (r0 + p >= n) break;
+        float m = part[p][0];
+        for (int q = 1; q < WV; ++q) m = __builtin_fmaxf(m, part[p][q]);
+        m = __builtin_fmaxf(m, sqd::kFloor);
+        float inv_ws;
+        const uint32_t scale = row_scale<H>(m, FP8 ? sqd::kFp8Max : sqd::kQmax, inv_ws);
+        int8_t* dst = tab.wq[it] + (r0 + p) * kvec * E;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            float vm = 0.0f;
-            if (live[i]) {
-                const u32x4 raw = *(const u32x4*)(st + (t + i * T) * 16);
-                float e[E];
-                sqd::unpack16<E>(raw, e);
-#pragma unroll
-                for (int q = 0; q < E; ++q) {
-                    wv[i][q] = __fmul_rn(e[q], sv[i][q]);
-                    vm = __builtin_fmaxf(vm, __builtin_fabsf(wv[i][q]));
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < E; ++q) wv[i][q] = 0.0f;
-            }
-#pragma unroll
-            for (int r = 0; r < RB; ++r) mx[r] = row[i] == r ? __builtin_fmaxf(mx[r], vm) : mx[r];
-        }
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            mx[r] = sqd::wave_max(mx[r]);
-            if (lane == 0) part[r][wave] = mx[r];
-        }
-        __syncthreads();
-        float inv[RB];
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            float m = part[r][0];
-#pragma unroll
-            for (int w = 1; w < WV; ++w) m = __builtin_fmaxf(m, part[r][w]);
-            m = __builtin_fmaxf(m, sqd::kFloor);
-            scale[r] = row_scale<H>(m, FP8 ? sqd::kFp8Max : sqd::kQmax, inv[r]);
-        }
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            float inv_ws = inv[0];
-#pragma unroll
-            for (int r = 1; r < RB; ++r) inv_ws = row[i] == r ? inv[r] : inv_ws;
+            if (!live[i]) continue;
+            uint32_t codes[W32];
             if constexpr (FP8) {
                 // e4m3 codes: |W' / ws| <= 448 (1 + 3 * 2^-24), which rounds to 448
 #pragma unroll
                 for (int d = 0; d < W32; ++d)
-                    codes[i][d] = sqd::pack4_e4m3(
-                        __fmul_rn(wv[i][4 * d], inv_ws), __fmul_rn(wv[i][4 * d + 1], inv_ws),
-                        __fmul_rn(wv[i][4 * d + 2], inv_ws), __fmul_rn(wv[i][4 * d + 3], inv_ws));
+                    codes[d] = sqd::pack4_e4m3(
+                        __fmul_rn(wv[p][i][4 * d], inv_ws), __fmul_rn(wv[p][i][4 * d + 1], inv_ws),
+                        __fmul_rn(wv[p][i][4 * d + 2], inv_ws), __fmul_rn(wv[p][i][4 * d + 3], inv_ws));
             } else {
                 // Codes by the round-to-nearest-even of the fp32 adder: for
                 // |v| < 2^22, fl(v + 1.5 * 2^23) = rint(v) + 1.5 * 2^23 exactly,
                 // and the low byte of its bit pattern is rint(v) as a
-                // two's-complement int8. No clamp is needed: |W'| <= m and
-                // inv_ws = fl(1 / fl(m / 127)), so |v| <= 127 (1 + 3 * 2^-24) and
-                // rint(v) is within [-127, 127] (below the 1e-5 floor, |v| < 127).
-                // Equal to q8() for every value this row can produce. A
-                // binary16 row scale can sit below the fp32 one (by 2^-11
-                // relative, far more where it is subnormal), so H clamps
-                // first (rint and the integer clamp commute).
-                uint32_t b[E];
+                // two's-complement int8. No clamp is needed for fp32 scales:
+                // |W'| <= m and inv_ws = fl(1 / fl(m / 127)), so
+                // |v| <= 127 (1 + 3 * 2^-24) and rint(v) is within [-127, 127]
+                // (below the 1e-5 floor, |v| < 127). A binary16 row scale can
+                // sit below the fp32 one (by 2^-11 relative, far more where it
+                // is subnormal), so H clamps first (rint and the integer clamp
+                // commute). Equal to q8() for every value the row can produce.
+                uint32_t bits[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    float v = __fmul_rn(wv[i][e], inv_ws);
+                    float v = __fmul_rn(wv[p][i][e], inv_ws);
                     if constexpr (H) v = __builtin_fminf(__builtin_fmaxf(v, -sqd::kQmax), sqd::kQmax);
-                    b[e] = __float_as_uint(__fadd_rn(v, 12582912.0f));
+                    bits[e] = __float_as_uint(__fadd_rn(v, 12582912.0f));
                 }
 #pragma unroll
                 for (int d = 0; d < W32; ++d) {
-                    // low bytes of b[4d .. 4d+3] -> one dword
-                    const uint32_t lo = __builtin_amdgcn_perm(b[4 * d + 1], b[4 * d], 0x0c0c0400u);
-                    const uint32_t hi = __builtin_amdgcn_perm(b[4 * d + 3], b[4 * d + 2], 0x0c0c0400u);
-                    codes[i][d] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                    // low bytes of bits[4d .. 4d+3] -> one dword
+                    const uint32_t lo = __builtin_amdgcn_perm(bits[4 * d + 1], bits[4 * d], 0x0c0c0400u);
+                    const uint32_t hi = __builtin_amdgcn_perm(bits[4 * d + 3], bits[4 * d + 2], 0x0c0c0400u);
+                    codes[d] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
                 }
             }
+            int8_t* q = dst + (int64_t)(t + i * T) * E;
+            if constexpr (W32 == 2)
+                __builtin_nontemporal_store(sqd::u32x2{codes[0], codes[1]}, (sqd::u32x2*)q);
+            else
+                __builtin_nontemporal_store(codes[0], (uint32_t*)q);
         }
-        prev = g;
-        slot = (slot + 1) % NS;
+        if (t == 0) store_scale<H>(tab.w_scale[it], r0 + p, scale);
     }
-    flush();
-    sqd::wait_vmcnt<0>();  // zero-fill loads past the end may still be in flight
 }
+
 
 // Rows longer than 4096 groups (k > 65536): one block per row, the row is
 // read twice and s is read from cache.
@@ -575,70 +533,31 @@ __global__ __launch_bounds__(kActThreads) void quant_act_batched_kernel(const Ac
     quant_act_block<EB, FP8, NC, O32, H>(x, rows, kvec, rpb, nc, inv_s, act_scale, xq, strip, chunk);
 }
 
-int device_cus() {
-    static int cus = [] {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        return n;
-    }();
-    return cus;
+// Vector slots per thread and rows per block for rows of kvec 16-byte
+// vectors: (2, 2) for rows of up to 1024 vectors (blocks of up to 512
+// threads), (4, 1) up to 4096 (up to 1024 threads); longer rows take
+// quant_weight_long_kernel. Measured on MI355X over Llama-2 7B/13B/70B
+// projection shapes against 1-6 slots and 1-6 rows: these two are within a
+// few percent of the best on every shape.
+constexpr int64_t kQwShortRow = 1024, kQwMaxRow = 4096;
+
+int qw_slots(int64_t kvec) { return kvec <= kQwShortRow ? 2 : 4; }
+int qw_rows(int64_t kvec) { return kvec <= kQwShortRow ? 2 : 1; }
+// threads per block: the multiple of 64 that NV slots each just cover
+int qw_threads(int64_t kvec) {
+    const int64_t nv = qw_slots(kvec);
+    return (int)((kvec + nv - 1) / nv + 63) / 64 * 64;
 }
 
-// WV waves of 64 threads, NV vector slots per thread, RB rows per stage of
-// CPW KB per wave, NS stages in the ring, PER_CU blocks per compute unit (the
-// rings of all of them fit the LDS)
-template <int EB, int WV, int NV, int RB, int CPW, int NS, int PER_CU, bool FP8, bool H>
-hipError_t launch_qw(const QwTable& tab, hipStream_t stream) {
-    static_assert(PER_CU * (NS * CPW * WV * 1024 + RB * WV * 4) <= 160 * 1024, "the rings fit in LDS");
-    for (int i = 0; i < tab.count; ++i)
-        if (RB * tab.kvec[i] * 16 > CPW * WV * 1024 || RB * tab.kvec[i] > NV * 64 * WV) return hipErrorInvalidValue;
-    const int64_t blocks = std::min<int64_t>(tab.first[tab.count], (int64_t)PER_CU * device_cus());
-    quant_weight_stream_kernel<EB, WV, NV, RB, CPW, NS, FP8, H><<<dim3((unsigned)blocks), dim3(64 * WV), 0, stream>>>(
+template <int EB, int NV, int RPB, bool FP8, bool H>
+void launch_rows(const QwTable& tab, int threads, hipStream_t stream) {
+    quant_weight_rows_kernel<EB, NV, RPB, FP8, H><<<dim3((unsigned)tab.first[tab.count]), dim3(threads), 0, stream>>>(
         tab);
-    return hipGetLastError();
 }
 
-// Kernel shape for rows of kvec 16-byte vectors (waves, slots per thread,
-// rows per stage, KB per wave per stage, ring depth, blocks per compute unit),
-// measured on MI355X over the Llama-2 7B/13B/70B projections: stages of
-// 16-64 KB in a two-deep ring and two to four blocks per compute unit, so that
-// while one block reduces and quantizes a stage the others' loads keep HBM
-// busy; the slots per thread divide a stage's vectors (nearly) evenly.
-// Shape 8: rows of more than 4096 vectors, one block per row reading it twice.
-constexpr int kQwLong = 8;
-constexpr int kQwRowsPerStage[kQwLong] = {4, 2, 2, 2, 1, 1, 1, 1};
-
-int qw_shape(int64_t kvec) {
-    if (kvec <= 256) return 0;
-    if (kvec <= 512) return 1;
-    if (kvec <= 640) return 2;
-    if (kvec <= 1024) return 3;
-    if (kvec <= 1536) return 4;
-    if (kvec <= 1792) return 5;
-    if (kvec <= 2048) return 6;
-    if (kvec <= 4096) return 7;
-    return kQwLong;
-}
-
-template <int EB, bool FP8, bool H>
-hipError_t launch_shape(int shape, const QwTable& tab, hipStream_t stream) {
-    switch (shape) {
-        case 0: return launch_qw<EB, 4, 4, 4, 4, 2, 4, FP8, H>(tab, stream);
-        case 1: return launch_qw<EB, 4, 4, 2, 4, 2, 4, FP8, H>(tab, stream);
-        case 2: return launch_qw<EB, 4, 5, 2, 5, 2, 3, FP8, H>(tab, stream);
-        case 3: return launch_qw<EB, 8, 4, 2, 4, 2, 2, FP8, H>(tab, stream);
-        case 4: return launch_qw<EB, 8, 3, 1, 3, 2, 3, FP8, H>(tab, stream);
-        case 5: return launch_qw<EB, 4, 7, 1, 7, 2, 2, FP8, H>(tab, stream);
-        case 6: return launch_qw<EB, 8, 4, 1, 4, 2, 2, FP8, H>(tab, stream);
-        case 7: return launch_qw<EB, 16, 4, 1, 4, 2, 1, FP8, H>(tab, stream);
-    }
-    return hipErrorInvalidValue;
-}
-
-// Items of one element type, scale storage and kernel shape share a launch
-// (first-appearance order); long rows get a launch per item.
+// Items of one element type and scale storage whose rows take the same block
+// size share a launch (first-appearance order); long rows get a launch per
+// item.
 template <bool FP8, bool H>
 hipError_t quant_weight_items(const sqk::QuantWeightItem* items, int count, hipStream_t stream) {
     bool done[sqk::kMaxBatch] = {};
@@ -647,8 +566,8 @@ hipError_t quant_weight_items(const sqk::QuantWeightItem* items, int count, hipS
         done[i] = true;
         if (items[i].n == 0) continue;
         const int eb = sqk::elem_bytes(items[i].wt);
-        const int shape = qw_shape(items[i].k * eb / 16);
-        if (shape == kQwLong) {
+        const int64_t kvec = items[i].k * eb / 16;
+        if (kvec > kQwMaxRow) {
             const int64_t kgroups = items[i].k / 16;
             if (eb == 2)
                 quant_weight_long_kernel<2, FP8, H><<<dim3((unsigned)items[i].n), dim3(256), 0, stream>>>(
@@ -660,26 +579,36 @@ hipError_t quant_weight_items(const sqk::QuantWeightItem* items, int count, hipS
             if (e != hipSuccess) return e;
             continue;
         }
+        const int threads = qw_threads(kvec);
+        const bool short_rows = kvec <= kQwShortRow;
         QwTable tab{};
-        int64_t stages = 0;
+        int64_t blocks = 0;
         for (int j = i; j < count; ++j) {
-            if (j > i && (done[j] || items[j].n == 0 || items[j].h != H || sqk::elem_bytes(items[j].wt) != eb ||
-                          qw_shape(items[j].k * eb / 16) != shape))
+            if (j > i && (done[j] || items[j].n == 0 || items[j].h != H || sqk::elem_bytes(items[j].wt) != eb))
+                continue;
+            const int64_t kv = items[j].k * eb / 16;
+            if (j > i && (kv > kQwMaxRow || (kv <= kQwShortRow) != short_rows || qw_threads(kv) != threads))
                 continue;
             done[j] = true;
             const int c = tab.count++;
-            tab.first[c] = stages;
-            tab.w[c] = (const int8_t*)items[j].w;
+            tab.first[c] = (int32_t)blocks;
+            tab.w[c] = (const u32x4*)items[j].w;
             tab.s[c] = items[j].s;
             tab.wq[c] = items[j].wq;
             tab.w_scale[c] = items[j].w_scale;
             tab.n[c] = items[j].n;
-            tab.kvec[c] = items[j].k * eb / 16;
-            stages += (items[j].n + kQwRowsPerStage[shape] - 1) / kQwRowsPerStage[shape];
+            tab.kvec[c] = kv;
+            blocks += (items[j].n + qw_rows(kv) - 1) / qw_rows(kv);
+            if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
         }
-        tab.first[tab.count] = stages;
-        const hipError_t e =
-            eb == 2 ? launch_shape<2, FP8, H>(shape, tab, stream) : launch_shape<4, FP8, H>(shape, tab, stream);
+        tab.first[tab.count] = (int32_t)blocks;
+        if (eb == 2)
+            short_rows ? launch_rows<2, 2, 2, FP8, H>(tab, threads, stream)
+                       : launch_rows<2, 4, 1, FP8, H>(tab, threads, stream);
+        else
+            short_rows ? launch_rows<4, 2, 2, FP8, H>(tab, threads, stream)
+                       : launch_rows<4, 4, 1, FP8, H>(tab, threads, stream);
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

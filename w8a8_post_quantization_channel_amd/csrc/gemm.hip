@@ -812,6 +812,20 @@ __global__ __launch_bounds__(256) void gemm_dma_grouped_kernel(const GemmTable t
                           xcd_tile(b, ntiles), epi, lds);
 }
 
+// The fp32 reference products of several bf16 activation batches (items of
+// the table; act_scale, w_scale and acc_out unused): the plain fp32 store of
+// the accumulator, every batch's tiles in one launch.
+template <int TN>
+__global__ __launch_bounds__(256) void ref_gemm_grouped_kernel(const GemmTable tab) {
+    __shared__ __attribute__((aligned(1024))) char lds[dma_lds_bytes<TN>()];
+    const int i = sqd::item_of(tab.first, tab.count, blockIdx.x);
+    const int b = blockIdx.x - tab.first[i], ntiles = tab.tiles_m[i] * tab.tiles_n[i];
+    if (b >= ntiles) return;
+    EpiStoreF32 epi{(float*)tab.y[i], tab.M[i], tab.N[i]};
+    dma_tile<OpBF16, TN, EpiStoreF32>(tab.A[i], tab.B[i], tab.M[i], tab.N[i], tab.Kb[i], tab.tiles_m[i],
+                                      tab.tiles_n[i], xcd_tile(b, ntiles), epi, lds);
+}
+
 // ---- skinny kernel (decode: 4 < m <= 64) ------------------------------------------
 //
 // The product is bound by streaming the int8 weight once from HBM. A block of
@@ -1418,6 +1432,53 @@ hipError_t ref_gemm(const void* x, int xt, const void* w, int wt, int64_t m, int
         return hipGetLastError();
     }
     return hipErrorInvalidValue;  // mixed input types are rejected by the C ABI
+}
+
+hipError_t ref_gemm_batched(const void* const* x, int xt, int nb, int64_t rows, const void* w, int wt, int64_t n,
+                            int64_t k, float* yref, hipStream_t stream) {
+    if (nb <= 0 || rows == 0 || n == 0) return hipSuccess;
+    // the grouped launch covers nb x (tiles of one batch): the tile width of
+    // the whole problem
+    const int tn = xt == kBF16 && wt == kBF16 ? dma_width(choose_cfg((int64_t)nb * rows, n)) : 0;
+    if (tn == 0 || rows <= kSkinnyMaxM) {
+        for (int b = 0; b < nb; ++b) {
+            const hipError_t e = ref_gemm(x[b], xt, w, wt, rows, n, k, yref + (int64_t)b * rows * n, stream);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    const int64_t tiles_m = (rows + kDmaBM - 1) / kDmaBM, tiles_n = (n + 32 * tn - 1) / (32 * tn);
+    const int64_t per = (tiles_m * tiles_n + 7) / 8 * 8;  // whole XCD rounds per batch
+    for (int b0 = 0; b0 < nb; b0 += kMaxBatch) {
+        GemmTable tab{};
+        int64_t blocks = 0;
+        for (int b = b0; b < nb && b < b0 + kMaxBatch; ++b) {
+            const int c = tab.count++;
+            tab.first[c] = (int32_t)blocks;
+            tab.A[c] = (const int8_t*)x[b];
+            tab.B[c] = (const int8_t*)w;
+            tab.y[c] = yref + (int64_t)b * rows * n;
+            tab.M[c] = rows;
+            tab.N[c] = n;
+            tab.Kb[c] = 2 * k;
+            tab.tiles_m[c] = (int32_t)tiles_m;
+            tab.tiles_n[c] = (int32_t)tiles_n;
+            blocks += per;
+            if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+        }
+        tab.first[tab.count] = (int32_t)blocks;
+        const dim3 grid((unsigned)blocks), block(256);
+        switch (tn) {
+            case 8: ref_gemm_grouped_kernel<8><<<grid, block, 0, stream>>>(tab); break;
+            case 7: ref_gemm_grouped_kernel<7><<<grid, block, 0, stream>>>(tab); break;
+            case 6: ref_gemm_grouped_kernel<6><<<grid, block, 0, stream>>>(tab); break;
+            case 5: ref_gemm_grouped_kernel<5><<<grid, block, 0, stream>>>(tab); break;
+            default: ref_gemm_grouped_kernel<4><<<grid, block, 0, stream>>>(tab); break;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t reduce_slots(const double* slots, int64_t per_group, int groups, double count, double* out,

@@ -451,10 +451,12 @@ __device__ __forceinline__ void quant_act_block(const u32x4* __restrict__ x, int
 #pragma unroll
                 for (int u = 0; u < E; ++u) t[u] = __fmul_rn(__fmul_rn(e[u], is[c][u]), inv_a[c]);
                 if constexpr (E == 8)
-                    *(__attribute__((address_space(1))) sqd::u32x2*)dst =
-                        sqd::u32x2{sqd::pack4_e4m3(t[0], t[1], t[2], t[3]), sqd::pack4_e4m3(t[4], t[5], t[6], t[7])};
+                    __builtin_nontemporal_store(
+                        sqd::u32x2{sqd::pack4_e4m3(t[0], t[1], t[2], t[3]), sqd::pack4_e4m3(t[4], t[5], t[6], t[7])},
+                        (__attribute__((address_space(1))) sqd::u32x2*)dst);
                 else
-                    *(__attribute__((address_space(1))) uint32_t*)dst = sqd::pack4_e4m3(t[0], t[1], t[2], t[3]);
+                    __builtin_nontemporal_store(sqd::pack4_e4m3(t[0], t[1], t[2], t[3]),
+                                                (__attribute__((address_space(1))) uint32_t*)dst);
             } else {
                 // clamp to [-127, 127], then round half to even with the fp32
                 // adder (fl(v + 1.5 * 2^23) keeps rint(v) in its low byte for
@@ -475,9 +477,9 @@ __device__ __forceinline__ void quant_act_block(const u32x4* __restrict__ x, int
                     w[d] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
                 }
                 if constexpr (E == 8)
-                    *(__attribute__((address_space(1))) sqd::u32x2*)dst = sqd::u32x2{w[0], w[1]};
+                    __builtin_nontemporal_store(sqd::u32x2{w[0], w[1]}, (__attribute__((address_space(1))) sqd::u32x2*)dst);
                 else
-                    *(__attribute__((address_space(1))) uint32_t*)dst = w[0];
+                    __builtin_nontemporal_store(w[0], (__attribute__((address_space(1))) uint32_t*)dst);
             }
         }
     };

@@ -45,9 +45,9 @@ AlphaLayout alpha_layout(int nb, int64_t rows, int64_t n, int64_t k, int na) {
     L.act_scale = take(16);
     L.w_scale = take((size_t)n * 4);
     L.mse = take((size_t)na * 8);
-    L.slots = take((size_t)na * nb * sqk::gemm_sse_slots(rows, n) * 8);
+    L.slots = take((size_t)na * sqk::gemm_sse_slots((int64_t)nb * rows, n) * 8);
     L.wq = take((size_t)n * k);
-    L.xq = take((size_t)rows * k);
+    L.xq = take((size_t)nb * rows * k);
     L.yref = take((size_t)nb * rows * n * 4);
     L.total = off;
     return L;
@@ -666,8 +666,8 @@ sq_status sq_alpha_search(const void* const* x_batches, sq_dtype xt, int n_batch
     int8_t* wq = (int8_t*)(base + L.wq);
     int8_t* xq = (int8_t*)(base + L.xq);
     float* yref = (float*)(base + L.yref);
-    const int64_t per_gemm = sqk::gemm_sse_slots(rows_per_batch, n);
-    const int64_t ynum = rows_per_batch * n;
+    const int64_t rows_total = (int64_t)n_batches * rows_per_batch;
+    const int64_t per_gemm = sqk::gemm_sse_slots(rows_total, n);
 
     hipError_t e = hipSuccess;
     auto run = [&](hipError_t r) {
@@ -677,20 +677,26 @@ sq_status sq_alpha_search(const void* const* x_batches, sq_dtype xt, int n_batch
     for (int b = 0; b < n_batches; ++b)
         run(sqk::absmax(x_batches[b], xt, rows_per_batch, k, act_max, b > 0, stream));
     run(sqk::absmax(w, wt, n, k, w_max, false, stream));
-    for (int b = 0; b < n_batches; ++b)
-        run(sqk::ref_gemm(x_batches[b], xt, w, wt, rows_per_batch, n, k, yref + b * ynum, stream));
-    // one full quantized forward per alpha, scored in the GEMM epilogue
+    run(sqk::ref_gemm_batched(x_batches, xt, n_batches, rows_per_batch, w, wt, n, k, yref, stream));
+    // One full quantized forward per alpha, scored in the GEMM epilogue. The
+    // batches' codes are stacked (batch b at rows b * rows_per_batch, as the
+    // reference products are), so one product covers every batch.
     for (int i = 0; i < n_alphas && e == hipSuccess; ++i) {
         run(sqk::smooth_factors(act_max, w_max, k, alphas[i], s, inv_s, act_scale, stream));
         run(sqk::quant_weight(w, wt, n, k, s, wq, w_scale, false, stream));
-        for (int b = 0; b < n_batches; ++b) {
-            run(sqk::quant_act(x_batches[b], xt, rows_per_batch, k, inv_s, act_scale, xq, false, stream));
-            run(sqk::gemm_sse(xq, wq, rows_per_batch, n, k, act_scale, w_scale, yref + b * ynum,
-                              slots + ((int64_t)i * n_batches + b) * per_gemm, stream));
+        for (int b0 = 0; b0 < n_batches; b0 += sqk::kMaxBatch) {
+            sqk::ActItem items[sqk::kMaxBatch];
+            int cnt = 0;
+            for (int b = b0; b < n_batches && b < b0 + sqk::kMaxBatch; ++b)
+                items[cnt++] = sqk::ActItem{x_batches[b], xt, rows_per_batch, k, inv_s, act_scale,
+                                            xq + (int64_t)b * rows_per_batch * k, false};
+            run(sqk::quant_act_batched(items, cnt, stream));
         }
+        run(sqk::gemm_sse(xq, wq, rows_total, n, k, act_scale, w_scale, yref, slots + (int64_t)i * per_gemm,
+                          stream));
     }
-    const double count = (double)n_batches * (double)rows_per_batch * (double)n;
-    run(sqk::reduce_slots(slots, (int64_t)n_batches * per_gemm, n_alphas, count, mse_dev, stream));
+    const double count = (double)rows_total * (double)n;
+    run(sqk::reduce_slots(slots, per_gemm, n_alphas, count, mse_dev, stream));
     if (e != hipSuccess) return SQ_ERR_HIP;
     run(hipMemcpyAsync(mse, mse_dev, (size_t)n_alphas * sizeof(double), hipMemcpyDeviceToHost, stream));
     run(hipStreamSynchronize(stream));

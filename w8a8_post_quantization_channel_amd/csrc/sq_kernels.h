@@ -184,6 +184,11 @@ hipError_t gemm_sse(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, in
 hipError_t ref_gemm(const void* x, int xt, const void* w, int wt, int64_t m, int64_t n, int64_t k,
                     float* yref, hipStream_t stream);
 
+// the same for nb activation batches x[b] of rows x k against one weight:
+// yref + b * rows * n; bf16 batches share one grouped launch (per 16)
+hipError_t ref_gemm_batched(const void* const* x, int xt, int nb, int64_t rows, const void* w, int wt, int64_t n,
+                            int64_t k, float* yref, hipStream_t stream);
+
 // out[g] = (sum over the slots of group g, in a fixed order) / count, where
 // group g is the `per_group` consecutive slots starting at g * per_group
 hipError_t reduce_slots(const double* slots, int64_t per_group, int groups, double count, double* out,

@@ -607,7 +607,14 @@ def workload_hbm_passes(device):
     ms = timed(cycle([lambda W=W, S=S, WQ=WQ, WS=WS: capi.sq_quant_weight_batched(W, S, WQ, WS)
                       for W, S, WQ, WS, _ in sets]), max(10, 2 * nsets))
     record("weight_quant_13b_block_batched", ms, qbytes, nsets)
-    del sets
+    # the same with binary16 scale storage: s and w_scale in fp16 (half the
+    # s bytes every block reads from L2)
+    h16 = [([s.half() for s in S], [torch.empty(n, dtype=torch.float16, device=device) for n, _ in blk])
+           for _, S, _, _, _ in sets]
+    ms = timed(cycle([lambda W=W, S16=S16, WQ=WQ, WS16=WS16: capi.sq_quant_weight_f16_batched(W, S16, WQ, WS16)
+                      for (W, _, WQ, _, _), (S16, WS16) in zip(sets, h16)]), max(10, 2 * nsets))
+    record("weight_quant_13b_block_batched_f16_scales", ms, sum(n * k * 3 + k * 2 + n * 2 for n, k in blk), nsets)
+    del sets, h16
     torch.cuda.empty_cache()
     # practical ceilings on the same tensor sizes: a plain copy (read = write)
     # and a plain bf16 -> int8 conversion (2 bytes read per byte written, the

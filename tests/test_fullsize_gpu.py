@@ -127,6 +127,19 @@ def test_alpha_search_small(bf16, rows):
     check_search(mse_g, best_g, mse_o, best_o)
 
 
+def test_alpha_search_many_batches():
+    """17 batches (more than one grouped reference launch and one batched
+    quantizer launch hold) of 72 rows (ragged 256-row tiles, stacked into
+    1224 rows for the squared-error product)."""
+    k, n = 128, 256
+    out = synth.outlier_channels(4520, k, count=2, fixed=40.0)
+    xs = [synth.activations(4521 + b, 72, k, out, dist="t3", bf16=True) for b in range(17)]
+    w = synth.weights(4540, n, k, bf16=True)
+    mse_g, best_g = gpu_alpha_search(xs, w)
+    mse_o, best_o = ORACLE.alpha_search(xs, w)
+    check_search(mse_g, best_g, mse_o, best_o)
+
+
 def test_alpha_search_c4_width():
     """K = 4096 (the alpha-search workload's width), N reduced to 1024 and
     two batches of 256 tokens so the oracle runs in seconds."""

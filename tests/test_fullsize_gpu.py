@@ -116,7 +116,9 @@ def check_search(mse_g, best_g, mse_o, best_o, rtol=1e-4):
     assert best_g == int(np.argmin(mse_g))
 
 
-@pytest.mark.parametrize("bf16,rows", [(True, 128), (False, 128), (True, 40)])
+# the two batches' rows are stacked for the squared-error product: 2 x 24 and
+# 2 x 2 rows take the skinny kernel's epilogue, the others the tiled kernel's
+@pytest.mark.parametrize("bf16,rows", [(True, 128), (False, 128), (True, 40), (True, 24), (False, 2)])
 def test_alpha_search_small(bf16, rows):
     k, n = 512, 96
     out = synth.outlier_channels(4500, k, count=2, fixed=50.0)

@@ -375,11 +375,43 @@ def workload_decode7b(device):
         del wq
         torch.cuda.empty_cache()
     tot_b = sum(v["GB/s"] * v["us"] for v in out.values()) / sum(v["us"] for v in out.values())
+    # the projections that read one input, as one batched GEMM call per layer
+    # (one vector-ALU or skinny launch for all of them) against a call each
+    grouped = {}
+    for gname, n, k, cnt in (("qkv", 4096, 4096, 3), ("gate_up", 11008, 4096, 2)):
+        wq = [[torch.randint(-127, 128, (n, k), dtype=torch.int8, device=device) for _ in range(cnt)]
+              for _ in range(layers)]
+        ws = [torch.rand(n, device=device) * 1e-3 + 1e-4 for _ in range(cnt)]
+        a = [torch.full((4,), 0.05, device=device) for _ in range(cnt)]
+        for m in (1, 2, 4, 8, 16, 64):
+            xq = torch.randint(-127, 128, (m, k), dtype=torch.int8, device=device)
+            ys = [torch.empty((m, n), dtype=torch.bfloat16, device=device) for _ in range(cnt)]
+            g_b, g_s = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_b, stream=stream):
+                for l in range(layers):
+                    capi.sq_w8a8_gemm_batched([xq] * cnt, wq[l], a, ws, ys)
+            with torch.cuda.graph(g_s, stream=stream):
+                for l in range(layers):
+                    for j in range(cnt):
+                        capi.sq_w8a8_gemm(xq, wq[l][j], a[j], ws[j], ys[j])
+            us_b = replay_ms(g_b) * 1e3 / layers
+            y_b = [y.clone() for y in ys]
+            us_s = replay_ms(g_s) * 1e3 / layers
+            if not all(torch.equal(p.view(torch.int16), q.view(torch.int16)) for p, q in zip(y_b, ys)):
+                raise RuntimeError(f"batched decode GEMM differs from the single calls ({gname}, m={m})")
+            gbytes = cnt * (n * k + m * k + m * n * 2 + n * 4)
+            grouped[f"{gname}_{cnt}x{n}x{k}_m{m}"] = {
+                "batched_us": us_b, "batched_GB/s": gbytes / (us_b * 1e-6) / 1e9,
+                "batched_hbm_frac": gbytes / (us_b * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                "single_calls_us": us_s, "single_calls_hbm_frac": gbytes / (us_s * 1e-6) / 1e9 / PEAK_HBM_GBS}
+            del g_b, g_s
+        del wq
+        torch.cuda.empty_cache()
     return {"metric": "W8A8 decode (act quant + int8 GEMM) HBM GB/s, Llama-2-7B shapes, cold weights",
             "value": tot_b, "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "dtype": "int8",
             "data": "synthetic",
             "config": {"workload": "llama2-7b decode, M in {1,8,16,64}, 32 rotating layers, HIP-graph replay"},
-            "per_case": out, "cpu_oracle": decode_oracle_times()}
+            "per_case": out, "grouped_gemm": grouped, "cpu_oracle": decode_oracle_times()}
 
 
 def decode_oracle_times(ms=(1, 64)):

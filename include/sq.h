@@ -414,7 +414,12 @@ sq_status sq_alpha_search(const void* const* x_batches, sq_dtype xt, int n_batch
  *   not NULL and acc_out[i] is not NULL, acc_out[i] from xq[i] [m[i], k[i]],
  *   wq[i] [n[i], k[i]], act_scale[i], w_scale[i]. Products that pick the same
  *   large tile and output type share one launch (the next product's tiles
- *   start as compute units free up); small-m products get a launch each.
+ *   start as compute units free up); products with m <= 4 (decode: q, k and
+ *   v, or gate and up) share one vector-ALU launch when their row class
+ *   (m rounded up to 1, 2 or 4), K chunk class and output type match;
+ *   products with 4 < m <= 64 share one skinny launch when their skinny
+ *   configuration (sq_gemm_tiling) and output type match, unless each alone
+ *   already fills the compute units twice over (then a launch each).
  */
 #define SQ_MAX_BATCH 16
 

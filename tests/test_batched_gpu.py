@@ -220,6 +220,61 @@ def test_gemm_batched():
         assert_bitexact(f"y item {i}", _h(ys[i]), ORACLE.dequant(racc, a[0], ws, bf16=bf16))
 
 
+@pytest.mark.parametrize("f16", [False, True])
+def test_gemm_batched_decode_grouped(f16):
+    """Decode-sized products in one batched call: those with m <= 4 and the
+    same activation-row class, chunks in flight, output type and scale storage
+    share a vector-ALU launch (q, k, v of a decode step; ragged n; K from 64 to
+    20480, which spans the chunk classes); those with 4 < m <= 64 and the same
+    skinny configuration share a skinny launch. Every output and accumulator
+    bit-exact against the oracle and against the single calls."""
+    import torch
+    cases = [(1, 4096, 4096, True, False), (1, 4096, 4096, True, True), (1, 4096, 4096, True, False),
+             (1, 1003, 4096, True, True), (2, 512, 4160, False, True), (3, 600, 11008, True, False),
+             (4, 260, 11008, True, True), (1, 256, 64, False, False), (4, 130, 20480, True, True),
+             (2, 77, 192, True, False),
+             # 4 < m <= 64: the skinny kernel, grouped by configuration (ragged n and m)
+             (8, 4096, 4096, True, False), (8, 4096, 4096, True, True), (5, 1003, 4096, True, False),
+             (16, 600, 4160, False, True), (13, 8200, 1088, True, False), (40, 1000, 704, True, True),
+             (64, 9000, 448, True, True), (33, 8200, 320, True, False), (24, 200, 11008, False, False)]
+    g = synth.rng(4750 + int(f16))
+    xqs, wqs, scs, wss, ys, accs, host = [], [], [], [], [], [], []
+    for m, n, k, bf16, with_acc in cases:
+        xq = g.integers(-127, 128, (m, k), dtype=np.int8)
+        wq = g.integers(-127, 128, (n, k), dtype=np.int8)
+        ws = g.uniform(1e-4, 1e-2, n).astype(np.float32)
+        a = np.float32(g.uniform(0.005, 0.05))
+        if f16:
+            ws16 = ORACLE.f16_encode(ws)
+            a16 = np.array([ORACLE.scale_f16(a), 0, 0, 0, 0, 0, 0, 0], np.uint16)
+            host.append((xq, wq, ws16, a16))
+            scs.append(_t(a16.view(np.float16)))
+            wss.append(_t(ws16.view(np.float16)))
+        else:
+            host.append((xq, wq, ws, np.array([a, 0, 0, 0], np.float32)))
+            scs.append(_t(host[-1][3]))
+            wss.append(_t(ws))
+        xqs.append(_t(xq))
+        wqs.append(_t(wq))
+        ys.append(torch.empty((m, n), dtype=torch.bfloat16 if bf16 else torch.float32, device=dev()))
+        accs.append(torch.empty((m, n), dtype=torch.int32, device=dev()) if with_acc else None)
+    batched = capi.sq_w8a8_gemm_f16_batched if f16 else capi.sq_w8a8_gemm_batched
+    single = capi.sq_w8a8_gemm_f16 if f16 else capi.sq_w8a8_gemm
+    for lo, hi in ((0, 10), (10, len(cases))):  # the m <= 4 items, then the skinny ones (at most 16 per call)
+        batched(xqs[lo:hi], wqs[lo:hi], scs[lo:hi], wss[lo:hi], ys[lo:hi], accs[lo:hi])
+    torch.cuda.synchronize()
+    for i, ((m, n, k, bf16, with_acc), (xq, wq, ws, a)) in enumerate(zip(cases, host)):
+        racc = ORACLE.gemm_i32(xq, wq)
+        if with_acc:
+            assert_bitexact(f"acc item {i}", _h(accs[i]), racc)
+        ref = ORACLE.dequant_h(racc, a[0], ws, bf16=bf16) if f16 else ORACLE.dequant(racc, a[0], ws, bf16=bf16)
+        assert_bitexact(f"y item {i}", _h(ys[i]), ref)
+        y1 = torch.empty_like(ys[i])
+        single(xqs[i], wqs[i], scs[i], wss[i], y1)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int8), ys[i].view(torch.int8)), f"item {i}: batched differs from single"
+
+
 def test_block_forward_batched_equals_single_calls():
     """Activation codes and outputs of the 13B block's seven projections from
     the batched quantizer and the grouped GEMM equal the single calls'."""

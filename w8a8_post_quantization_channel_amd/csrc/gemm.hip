@@ -843,20 +843,23 @@ __global__ __launch_bounds__(256) void ref_gemm_grouped_kernel(const GemmTable t
 // and w + 4 of each chunk with v_mfma_i32_16x16x64_i8 (lane l: row l % 16,
 // bytes 16 (l / 16) .. +15 of the step, for both operands); the four waves'
 // int32 partials are added through LDS at the end (exact in any order).
+template <int MB, int BNR, int NS>
+constexpr int skinny_lds_bytes() {
+    return NS * ((MB < 16 ? 16 : MB) + BNR) * 512;
+}
+
+// the BNR weight rows from n0 of one product
 template <int MB, int BNR, int NS, class Epi>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(const int8_t* __restrict__ A,
-                                                          const int8_t* __restrict__ B, int64_t M, int64_t N,
-                                                          int64_t Kb, Epi epi) {
+__device__ __forceinline__ void skinny_block(const int8_t* __restrict__ A, const int8_t* __restrict__ B, int64_t M,
+                                             int64_t N, int64_t Kb, Epi& epi, int64_t n0, char* lds) {
     constexpr int AR = MB < 16 ? 16 : MB, MT = AR / 16, NR = BNR / 16;
     constexpr int L = (MB + BNR) / 8;  // load instructions per wave per chunk (2 rows each)
     static_assert((MB + BNR) % 8 == 0 && MB % 2 == 0, "whole load rounds; a load's two rows on one side");
     constexpr int KC = 512, STAGE = (AR + BNR) * KC;
     static_assert(NS * STAGE <= 160 * 1024 && (NS - 2) * L < 64, "stages fit; vmcnt range");
     static_assert(4 * NR * MT * 64 * 16 <= NS * STAGE, "the partial sums fit in the stages");
-    __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t n0 = (int64_t)blockIdx.x * BNR;
     const int64_t nchunk = (Kb + KC - 1) / KC;
     const v4i ra = tile_rsrc(A, M, Kb);
     const v4i rb = tile_rsrc(B + n0 * Kb, min<int64_t>(BNR, N - n0), Kb);
@@ -936,6 +939,27 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const int8_t* __restri
     epi.end(lds);
 }
 
+template <int MB, int BNR, int NS, class Epi>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const int8_t* __restrict__ A,
+                                                          const int8_t* __restrict__ B, int64_t M, int64_t N,
+                                                          int64_t Kb, Epi epi) {
+    __shared__ __attribute__((aligned(1024))) char lds[skinny_lds_bytes<MB, BNR, NS>()];
+    skinny_block<MB, BNR, NS, Epi>(A, B, M, N, Kb, epi, (int64_t)blockIdx.x * BNR, lds);
+}
+
+// Several decode products in one launch: item i owns the blocks
+// [first[i], first[i + 1]), one per BNR weight rows; the items share the
+// activation-row class MB and the (BNR, NS) configuration.
+template <int MB, int BNR, int NS, bool kBF16Out, bool kH>
+__global__ __launch_bounds__(256) void gemm_skinny_grouped_kernel(const GemmTable tab) {
+    __shared__ __attribute__((aligned(1024))) char lds[skinny_lds_bytes<MB, BNR, NS>()];
+    const int i = sqd::item_of(tab.first, tab.count, blockIdx.x);
+    using Epi = EpiDequant<kBF16Out, int32_t, kH>;
+    Epi epi{tab.act_scale[i], tab.w_scale[i], tab.y[i], (int32_t*)tab.acc_out[i], tab.M[i], tab.N[i], 0.0f};
+    skinny_block<MB, BNR, NS, Epi>(tab.A[i], tab.B[i], tab.M[i], tab.N[i], tab.Kb[i], epi,
+                                   (int64_t)(blockIdx.x - tab.first[i]) * BNR, lds);
+}
+
 // ---- vector-ALU kernel (decode: m <= 4) -------------------------------------------
 //
 // At m <= 4 the product is the weight stream and nothing else, so it runs on
@@ -955,13 +979,13 @@ constexpr int kGemvMaxM = 4;
 constexpr int kGemvR = 4;    // weight rows per block
 constexpr int kGemvCH = 4;   // most 1 KB chunks per wave in flight
 
+// the kGemvR weight rows from r0 of one product
 template <int MB, int CH, class Epi>
-__global__ __launch_bounds__(256) void gemv_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
-                                                   int64_t M, int64_t N, int64_t Kb, Epi epi) {
+__device__ __forceinline__ void gemv_block(const int8_t* __restrict__ A, const int8_t* __restrict__ B, int64_t M,
+                                           int64_t N, int64_t Kb, Epi& epi, int64_t r0,
+                                           int (&red)[4][kGemvR][MB]) {
     constexpr int R = kGemvR;
-    __shared__ int red[4][R][MB];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t r0 = (int64_t)blockIdx.x * R;
     const int64_t nchunk = (Kb + 1023) / 1024;
     int acc[R][MB];
 #pragma unroll
@@ -1009,6 +1033,28 @@ __global__ __launch_bounds__(256) void gemv_kernel(const int8_t* __restrict__ A,
     }
 }
 
+template <int MB, int CH, class Epi>
+__global__ __launch_bounds__(256) void gemv_kernel(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+                                                   int64_t M, int64_t N, int64_t Kb, Epi epi) {
+    __shared__ int red[4][kGemvR][MB];
+    gemv_block<MB, CH, Epi>(A, B, M, N, Kb, epi, (int64_t)blockIdx.x * kGemvR, red);
+}
+
+// Several products in one launch (the projections of a decode step that read
+// their inputs at once: q, k and v, or gate and up): item i owns the blocks
+// [first[i], first[i + 1]), one per kGemvR weight rows. The items share MB (at
+// most MB activation rows each) and CH (the chunks in flight per wave); the
+// launch ramps and drains once instead of once per product.
+template <int MB, int CH, bool kBF16Out, bool kH>
+__global__ __launch_bounds__(256) void gemv_grouped_kernel(const GemmTable tab) {
+    __shared__ int red[4][kGemvR][MB];
+    const int i = sqd::item_of(tab.first, tab.count, blockIdx.x);
+    using Epi = EpiDequant<kBF16Out, int32_t, kH>;
+    Epi epi{tab.act_scale[i], tab.w_scale[i], tab.y[i], (int32_t*)tab.acc_out[i], tab.M[i], tab.N[i], 0.0f};
+    gemv_block<MB, CH, Epi>(tab.A[i], tab.B[i], tab.M[i], tab.N[i], tab.Kb[i], epi,
+                            (int64_t)(blockIdx.x - tab.first[i]) * kGemvR, red);
+}
+
 template <class E>
 struct IsDequant : std::false_type {};
 template <bool kBF16Out, class AccT, bool kH>
@@ -1016,12 +1062,17 @@ struct IsDequant<EpiDequant<kBF16Out, AccT, kH>> : std::is_same<AccT, int32_t> {
 
 inline int gemv_rows(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
 
+// chunks in flight per wave: those of the busiest wave, at most kGemvCH
+inline int gemv_ch(int64_t Kb) {
+    const int64_t per_wave = ((Kb + 1023) / 1024 + 3) / 4;
+    return per_wave >= kGemvCH ? kGemvCH : (int)per_wave;
+}
+
 template <int MB, class Epi>
 hipError_t launch_gemv_m(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t Kb, Epi epi,
                          hipStream_t stream) {
-    const int64_t per_wave = ((Kb + 1023) / 1024 + 3) / 4;  // chunks of the busiest wave
     const dim3 grid((unsigned)((N + kGemvR - 1) / kGemvR)), block(256);
-    switch (per_wave >= kGemvCH ? kGemvCH : (int)per_wave) {
+    switch (gemv_ch(Kb)) {
         case 1: gemv_kernel<MB, 1, Epi><<<grid, block, 0, stream>>>(A, B, M, N, Kb, epi); break;
         case 2: gemv_kernel<MB, 2, Epi><<<grid, block, 0, stream>>>(A, B, M, N, Kb, epi); break;
         case 3: gemv_kernel<MB, 3, Epi><<<grid, block, 0, stream>>>(A, B, M, N, Kb, epi); break;
@@ -1281,6 +1332,67 @@ hipError_t launch_grouped(const GemmTable& tab, int64_t blocks, bool bf16, bool 
     return hipGetLastError();
 }
 
+template <int MB, int CH>
+void launch_gemv_grouped_ch(const GemmTable& tab, int64_t blocks, bool bf16, bool h, hipStream_t stream) {
+    const dim3 grid((unsigned)blocks), block(256);
+    if (h) {
+        if (bf16) gemv_grouped_kernel<MB, CH, true, true><<<grid, block, 0, stream>>>(tab);
+        else gemv_grouped_kernel<MB, CH, false, true><<<grid, block, 0, stream>>>(tab);
+    } else {
+        if (bf16) gemv_grouped_kernel<MB, CH, true, false><<<grid, block, 0, stream>>>(tab);
+        else gemv_grouped_kernel<MB, CH, false, false><<<grid, block, 0, stream>>>(tab);
+    }
+}
+
+template <int MB>
+void launch_gemv_grouped_mb(const GemmTable& tab, int64_t blocks, int ch, bool bf16, bool h, hipStream_t stream) {
+    switch (ch) {
+        case 1: launch_gemv_grouped_ch<MB, 1>(tab, blocks, bf16, h, stream); break;
+        case 2: launch_gemv_grouped_ch<MB, 2>(tab, blocks, bf16, h, stream); break;
+        case 3: launch_gemv_grouped_ch<MB, 3>(tab, blocks, bf16, h, stream); break;
+        default: launch_gemv_grouped_ch<MB, kGemvCH>(tab, blocks, bf16, h, stream); break;
+    }
+}
+
+// the skinny kernel's configuration for an int8 product with the
+// dequantizing epilogue (as launch_skinny_mb picks it)
+struct SkinnyCfg {
+    int mb, bnr, ns;
+    bool operator==(const SkinnyCfg& o) const { return mb == o.mb && bnr == o.bnr && ns == o.ns; }
+};
+SkinnyCfg skinny_cfg(int64_t M, int64_t N) {
+    const int mb = M <= 8 ? 8 : M <= 16 ? 16 : M <= 32 ? 32 : 64;
+    if (mb == 64) return N >= 8192 ? SkinnyCfg{64, 48, 2} : SkinnyCfg{64, 16, 3};
+    const int64_t b16 = (N + 15) / 16;
+    return SkinnyCfg{mb, 16, b16 >= 2 * (int64_t)cu_count() ? 2 : 4};
+}
+
+template <int MB, int BNR, int NS>
+void launch_skinny_grouped_cfg(const GemmTable& tab, int64_t blocks, bool bf16, bool h, hipStream_t stream) {
+    const dim3 grid((unsigned)blocks), block(256);
+    if (h) {
+        if (bf16) gemm_skinny_grouped_kernel<MB, BNR, NS, true, true><<<grid, block, 0, stream>>>(tab);
+        else gemm_skinny_grouped_kernel<MB, BNR, NS, false, true><<<grid, block, 0, stream>>>(tab);
+    } else {
+        if (bf16) gemm_skinny_grouped_kernel<MB, BNR, NS, true, false><<<grid, block, 0, stream>>>(tab);
+        else gemm_skinny_grouped_kernel<MB, BNR, NS, false, false><<<grid, block, 0, stream>>>(tab);
+    }
+}
+
+hipError_t launch_skinny_grouped(const GemmTable& tab, int64_t blocks, SkinnyCfg c, bool bf16, bool h,
+                                 hipStream_t stream) {
+    if (c == SkinnyCfg{64, 48, 2}) launch_skinny_grouped_cfg<64, 48, 2>(tab, blocks, bf16, h, stream);
+    else if (c == SkinnyCfg{64, 16, 3}) launch_skinny_grouped_cfg<64, 16, 3>(tab, blocks, bf16, h, stream);
+    else if (c == SkinnyCfg{32, 16, 2}) launch_skinny_grouped_cfg<32, 16, 2>(tab, blocks, bf16, h, stream);
+    else if (c == SkinnyCfg{32, 16, 4}) launch_skinny_grouped_cfg<32, 16, 4>(tab, blocks, bf16, h, stream);
+    else if (c == SkinnyCfg{16, 16, 2}) launch_skinny_grouped_cfg<16, 16, 2>(tab, blocks, bf16, h, stream);
+    else if (c == SkinnyCfg{16, 16, 4}) launch_skinny_grouped_cfg<16, 16, 4>(tab, blocks, bf16, h, stream);
+    else if (c == SkinnyCfg{8, 16, 2}) launch_skinny_grouped_cfg<8, 16, 2>(tab, blocks, bf16, h, stream);
+    else if (c == SkinnyCfg{8, 16, 4}) launch_skinny_grouped_cfg<8, 16, 4>(tab, blocks, bf16, h, stream);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 int dma_width(TileCfg c) {
     switch (c) {
         case kD256: return 8;
@@ -1307,7 +1419,82 @@ hipError_t gemm_batched_impl(const GemmItem* items, int count, hipStream_t strea
         const GemmItem& it = items[i];
         if (it.m == 0 || it.n == 0) continue;
         const int tn = width(it);
-        if (tn == 0) {  // small m: the register-staged or skinny kernel, one launch per item
+        if constexpr (!kF8) {
+            if (it.m <= kGemvMaxM) {
+                // m <= 4: the vector-ALU kernel; products with the same row
+                // class, chunks in flight, output type and scale storage share
+                // one launch
+                const int mb = gemv_rows(it.m), ch = gemv_ch(it.k);
+                GemmTable tab{};
+                int64_t blocks = 0;
+                for (int j = i; j < count; ++j) {
+                    const GemmItem& jt = items[j];
+                    if (j > i && (done[j] || jt.m == 0 || jt.n == 0 || jt.m > kGemvMaxM || gemv_rows(jt.m) != mb ||
+                                  gemv_ch(jt.k) != ch || jt.yt != it.yt || jt.h != it.h))
+                        continue;
+                    done[j] = true;
+                    const int c = tab.count++;
+                    tab.first[c] = (int32_t)blocks;
+                    tab.A[c] = jt.xq;
+                    tab.B[c] = jt.wq;
+                    tab.act_scale[c] = jt.act_scale;
+                    tab.w_scale[c] = jt.w_scale;
+                    tab.y[c] = jt.y;
+                    tab.acc_out[c] = jt.acc_out;
+                    tab.M[c] = jt.m;
+                    tab.N[c] = jt.n;
+                    tab.Kb[c] = jt.k;
+                    blocks += (jt.n + kGemvR - 1) / kGemvR;
+                    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+                }
+                tab.first[tab.count] = (int32_t)blocks;
+                const bool bf16 = it.yt == kBF16;
+                if (mb == 1) launch_gemv_grouped_mb<1>(tab, blocks, ch, bf16, it.h, stream);
+                else if (mb == 2) launch_gemv_grouped_mb<2>(tab, blocks, ch, bf16, it.h, stream);
+                else launch_gemv_grouped_mb<4>(tab, blocks, ch, bf16, it.h, stream);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                continue;
+            }
+        }
+        if constexpr (!kF8) {
+            // 4 < m <= 64: the skinny kernel. Products with the same
+            // configuration, output type and scale storage share a launch,
+            // except in the two-stage 16-row configuration (outputs of at
+            // least 2 x CUs blocks on their own): measured on the 7B decode
+            // shapes, q/k/v at m = 8-64 run 10-19 % faster in one launch, but
+            // gate/up at m = 8-16, already that wide, 3-6 % slower.
+            const SkinnyCfg cfg = skinny_cfg(it.m, it.n);
+            if (it.m <= kSkinnyMaxM && !(cfg.bnr == 16 && cfg.ns == 2)) {
+                GemmTable tab{};
+                int64_t blocks = 0;
+                for (int j = i; j < count; ++j) {
+                    const GemmItem& jt = items[j];
+                    if (j > i && (done[j] || jt.m == 0 || jt.n == 0 || jt.m <= kGemvMaxM || jt.m > kSkinnyMaxM ||
+                                  !(skinny_cfg(jt.m, jt.n) == cfg) || jt.yt != it.yt || jt.h != it.h))
+                        continue;
+                    done[j] = true;
+                    const int c = tab.count++;
+                    tab.first[c] = (int32_t)blocks;
+                    tab.A[c] = jt.xq;
+                    tab.B[c] = jt.wq;
+                    tab.act_scale[c] = jt.act_scale;
+                    tab.w_scale[c] = jt.w_scale;
+                    tab.y[c] = jt.y;
+                    tab.acc_out[c] = jt.acc_out;
+                    tab.M[c] = jt.m;
+                    tab.N[c] = jt.n;
+                    tab.Kb[c] = jt.k;
+                    blocks += (jt.n + cfg.bnr - 1) / cfg.bnr;
+                    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+                }
+                tab.first[tab.count] = (int32_t)blocks;
+                const hipError_t e = launch_skinny_grouped(tab, blocks, cfg, it.yt == kBF16, it.h, stream);
+                if (e != hipSuccess) return e;
+                continue;
+            }
+        }
+        if (tn == 0) {  // the register-staged kernel: one launch per item
             hipError_t e = hipErrorInvalidValue;
             if constexpr (!kF8)
                 e = gemm_dequant(it.xq, it.wq, it.m, it.n, it.k, it.act_scale, it.w_scale, it.y, it.yt,

@@ -144,6 +144,20 @@ def run_phased(block, side, gemm_events=None):
     block.step(side, main, on_gemm)
 
 
+def block_tiling(m, projs, phases=False):
+    """The tile of each projection in the block's grouped GEMM launch (one
+    launch, or one per phase), as the library chooses it for the group; the
+    launch lists the products newest-first."""
+    from w8a8_post_quantization_channel_amd import capi
+    names = [n for n, _, _, _ in projs]
+    shape = {n: (m, layer.n, layer.k) for n, _, layer, _ in projs}
+    out = {}
+    for part in (PHASES if phases else [names]):
+        part = [n for n in names if n in part][::-1]
+        out.update(zip(part, map(list, capi.sq_gemm_batched_tiling([shape[n] for n in part]))))
+    return {n: out[n] for n in names}
+
+
 def run_step(groups, projs, gemm_events=None, side=None, batched=True):
     """One pass of the whole path. gemm_events: list to append (name, start,
     end) event pairs bracketing each GEMM launch, recorded on the stream the
@@ -546,7 +560,8 @@ def workload_prefill70b(device):
             "value": ops / dt / 1e12, "unit": "TOPS", "n_gpus": 1, "higher_is_better": True, "dtype": "int8",
             "data": "synthetic", "config": {"workload": "llama2-70b prefill 4096 tokens x 80 layers",
                                             "resident_int8_weight_GB": resident / 1e9,
-                                            "tiling": {p: list(capi.sq_gemm_tiling(m, n)) for p, n, _, _ in projs},
+                                            "tiling": dict(zip([p for p, _, _, _ in projs], map(list, capi.sq_gemm_batched_tiling(
+                                                [(m, n, k) for _, n, k, _ in projs])))),
                                             "schedule": "per layer: one batched act quant + one grouped GEMM"},
             "ms_per_layer": dt * 1e3 / layers, "frac_of_int8_peak": ops / dt / 1e12 / PEAK_INT8_TOPS,
             "per_projection_ms_per_layer": dt_single * 1e3 / layers,
@@ -1154,7 +1169,8 @@ def main():
                           "gemm_dma_grouped_kernel<OpI8, TN, bf16> (256 x 32*TN tiles), one launch for the 7 "
                           "projections",
                 "scale_storage": args.scales,
-                "tiling": {n: list(capi.sq_gemm_tiling(m, layer.n)) for n, _, layer, _ in projs},
+                "tiling": ({n: list(capi.sq_gemm_tiling(m, layer.n)) for n, _, layer, _ in projs}
+                           if args.per_projection else block_tiling(m, projs, args.overlap)),
                 "avg_launch_us": avg_launch_ms * 1e3,
                 "per_projection_tops": {n: ops_by_name[n] / (sum(v) / len(v) * 1e-3) / 1e12
                                         for n, v in by_name.items()}}

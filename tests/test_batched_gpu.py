@@ -185,10 +185,11 @@ def test_quant_act_batched():
 
 
 def test_gemm_batched():
-    """Products that share a large tile, one that picks another width, a skinny
-    (m <= 64), a vector-ALU (m <= 4) and a register-staged one, mixed output
-    types, some with the int32 accumulator: every output bit-exact against the
-    oracle."""
+    """Products that take the pipelined tiles (with single-call widths of 128
+    and 160; each output type's group runs at one width chosen for the group),
+    a skinny (m <= 64), a vector-ALU (m <= 4) and a register-staged one, mixed
+    output types, some with the int32 accumulator: every output bit-exact
+    against the oracle."""
     import torch
     cases = [(512, 5120, 192, True, True), (300, 5120, 320, False, False), (1024, 8192, 128, True, False),
              (40, 1000, 704, True, True), (200, 600, 256, False, True), (256, 4112, 64, True, False),

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(lib):
     names = capi.declared_functions()
     assert set(names) >= {"sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_smooth_quant_act",
                           "sq_w8a8_gemm", "sq_alpha_search", "sq_alpha_search_workspace", "sq_status_string",
-                          "sq_gemm_tiling"}
+                          "sq_gemm_tiling", "sq_gemm_batched_tiling"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -131,6 +131,32 @@ def test_gemm_tiling_query(lib):
     assert lib.sq_gemm_tiling(-1, 32, ctypes.byref(bm), ctypes.byref(bn)) == SHAPE
     assert lib.sq_gemm_tiling(2048, 5120, ctypes.byref(bm), ctypes.byref(bn)) == OK
     assert bm.value in (128, 256) and bn.value in (128, 160, 192, 224, 256)
+
+
+def test_gemm_batched_tiling_query(lib):
+    """One width for the products of a grouped launch, chosen for the group;
+    decode and small products keep their single-call tiles; argument errors
+    are statuses."""
+    blk = [(2048, 5120, 5120)] * 4 + [(2048, 13824, 5120)] * 2 + [(2048, 5120, 13824)]
+    tiles = capi.sq_gemm_batched_tiling(blk)
+    assert len(set(tiles)) == 1 and tiles[0][0] == 256, tiles
+    # one product: the single call's choice
+    for m, n, k in [(2048, 5120, 5120), (4096, 8192, 8192), (300, 600, 2048), (16, 4096, 4096), (1, 4096, 4096)]:
+        assert capi.sq_gemm_batched_tiling([(m, n, k)]) == [capi.sq_gemm_tiling(m, n)]
+    # decode products and empty ones keep their own tiles beside a grouped launch
+    mixed = [(1, 4096, 4096), (16, 4096, 4096), (2048, 5120, 5120), (0, 512, 64), (2048, 13824, 5120)]
+    got = capi.sq_gemm_batched_tiling(mixed)
+    assert got[0] == capi.sq_gemm_tiling(1, 4096) and got[1] == capi.sq_gemm_tiling(16, 4096)
+    assert got[2] == got[4] and got[2][0] == 256
+    m, n, k = (ctypes.c_int64 * 2)(2048, 2048), (ctypes.c_int64 * 2)(5120, 5120), (ctypes.c_int64 * 2)(64, 64)
+    bm, bn = (ctypes.c_int * 2)(), (ctypes.c_int * 2)()
+    assert lib.sq_gemm_batched_tiling(2, m, n, None, bm, bn) == NULL
+    assert lib.sq_gemm_batched_tiling(0, m, n, k, bm, bn) == SHAPE
+    assert lib.sq_gemm_batched_tiling(17, m, n, k, bm, bn) == SHAPE
+    k[1] = 0
+    assert lib.sq_gemm_batched_tiling(2, m, n, k, bm, bn) == SHAPE
+    k[1] = 64
+    assert lib.sq_gemm_batched_tiling(2, m, n, k, bm, bn) == OK and bm[0] == bm[1] and bn[0] == bn[1]
 
 
 def test_alpha_search_validation(lib):

@@ -245,8 +245,9 @@ def test_llama13b_block_step_as_benchmarked():
     torch.cuda.synchronize()
     o = ORACLE
     act_max = {name: o.calib_absmax(g.x_host) for name, g in groups.items()}
+    # the grouped launch's tile, as the benchmark reports it
+    assert set(map(tuple, bench.block_tiling(2048, projs).values())) == {(256, 256)}
     for i, (name, g, layer, w_host) in enumerate(projs):
-        assert capi.sq_gemm_tiling(g.x_host.shape[0], layer.n) == (256, 160)
         got = {k: synth.from_torch(v) for k, v in dict(
             act_max=layer.act_max, w_max=layer.w_max, s=layer.s, act_scale=layer.act_scale[:1], wq=layer.wq,
             w_scale=layer.w_scale, xq=layer.xq, y=layer.y).items()}

@@ -52,6 +52,7 @@ def _declare(lib):
         "sq_w8a8_gemm": [P, P, i64, i64, i64, P, P, P, c.c_int, P, P],
         "sq_alpha_search_workspace": [c.c_int, i64, i64, i64, c.c_int, P],
         "sq_gemm_tiling": [i64, i64, P, P],
+        "sq_gemm_batched_tiling": [c.c_int, P, P, P, P, P],
         "sq_alpha_search": [P, c.c_int, c.c_int, i64, i64, P, c.c_int, i64, P, c.c_int, P, c.c_size_t, P, P, P],
         "sq_act_scale": [P, P, i64, P, P],
         "sq_dynamic_quant_act": [P, c.c_int, i64, i64, P, P, P, P, P],
@@ -326,6 +327,16 @@ def sq_gemm_tiling(m: int, n: int) -> tuple[int, int]:
     bm, bn = ctypes.c_int(0), ctypes.c_int(0)
     _check("sq_gemm_tiling", load().sq_gemm_tiling(m, n, ctypes.byref(bm), ctypes.byref(bn)))
     return bm.value, bn.value
+
+
+def sq_gemm_batched_tiling(shapes) -> list[tuple[int, int]]:
+    """Block tile (rows, columns) of each product of an sq_w8a8_gemm_batched
+    call with these (m, n, k) shapes (one output type and scale storage)."""
+    count = len(shapes)
+    ms, ns, ks = (_host_array(ctypes.c_int64, [int(s[i]) for s in shapes]) for i in range(3))
+    bm, bn = (ctypes.c_int * max(count, 1))(), (ctypes.c_int * max(count, 1))()
+    _check("sq_gemm_batched_tiling", load().sq_gemm_batched_tiling(count, ms[1], ns[1], ks[1], bm, bn))
+    return [(bm[i], bn[i]) for i in range(count)]
 
 
 def sq_alpha_search_workspace(n_batches: int, rows_per_batch: int, n: int, k: int, n_alphas: int = 4) -> int:

@@ -23,6 +23,7 @@
 //   * The tile index is remapped so consecutive tiles of one XCD share an A
 //     row panel (workgroups are dealt round-robin over the 8 XCDs).
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "sq_device.h"
@@ -533,10 +534,19 @@ constexpr int kDmaBK = 128;     // bytes of K per stage
 constexpr int kDmaBM = 256;     // rows of A per tile (4 waves x 64)
 constexpr int kLdsBytes = 160 * 1024;
 
+// LDS rings of the pipelined tile. Up to 256 x 160, three joint stages (the
+// A rows, then the B rows, 128 bytes of K each) fit in the 160 KB. Wider
+// tiles split the rings: one panel keeps three stages and the other two, so
+// the loads of the first run two steps ahead and those of the second one.
 template <int TN>
-constexpr int dma_stages() {
-    return 3 * (kDmaBM + 32 * TN) * kDmaBK <= kLdsBytes ? 3 : 2;
-}
+struct DmaRing {
+    static constexpr int SA = kDmaBM * kDmaBK, SB = 32 * TN * kDmaBK;  // bytes per stage
+    static constexpr bool kJoint = 3 * (SA + SB) <= kLdsBytes;
+    static constexpr bool kDeepA = false;  // split rings: B (the weight panel) three stages deep
+    static constexpr int NSA = kJoint || kDeepA ? 3 : 2, NSB = kJoint || !kDeepA ? 3 : 2;
+    static constexpr int bytes = NSA * SA + NSB * SB;
+    static_assert(bytes <= kLdsBytes, "the rings fit in LDS");
+};
 
 // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD takes a
 // contiguous range of tiles (b < ntiles maps onto every tile exactly once)
@@ -548,7 +558,7 @@ __device__ __forceinline__ int xcd_tile(int b, int ntiles) {
 
 template <int TN>
 constexpr int dma_lds_bytes() {
-    return dma_stages<TN>() * (kDmaBM + 32 * TN) * kDmaBK;
+    return DmaRing<TN>::bytes;
 }
 
 // One 256 x 32*TN output tile; t is the tile's index after the XCD remap.
@@ -556,18 +566,27 @@ template <class Op, int TN, class Epi>
 __device__ __forceinline__ void dma_tile(const int8_t* __restrict__ A, const int8_t* __restrict__ B, int64_t M,
                                          int64_t N, int64_t Kb, int tiles_m, int tiles_n, int t, Epi& epi,
                                          char* lds) {
+    using R = DmaRing<TN>;
+    constexpr bool JOINT = R::kJoint;
     constexpr int BM = kDmaBM, BN = 32 * TN;
-    constexpr int ROWS = BM + BN;                    // a multiple of 32: whole load rounds
-    constexpr int STAGE = ROWS * kDmaBK;
-    constexpr int NS = dma_stages<TN>();
-    constexpr int L = ROWS / 32;                     // 1 KB loads per wave per stage
-    constexpr int LA = BM / 32;                      // ... of which A rows
+    constexpr int L = (BM + BN) / 32;                // 1 KB loads per wave per step
+    constexpr int LA = BM / 32, LB = L - LA;         // ... of A rows, of B rows
     constexpr int NFA = 2, NFB = TN, NF = NFA + NFB; // fragment reads per substep
     constexpr int NMMA = 2 * TN;                     // MFMAs per substep
     constexpr int NSUB = kDmaBK / Op::KB;            // MFMA substeps per step
+    constexpr bool DEEPA = R::kDeepA;
+    // loads a step leaves in flight when it publishes the next one: those of
+    // the step after next (every row with joint stages, the deep ring's rows
+    // with split rings)
+    constexpr int AHEAD = JOINT ? L : DEEPA ? LA : LB;
     static_assert(NF <= NMMA + 2, "fragment reads interleave with the MFMAs");
-    static_assert((NS - 2) * L < 64, "vmcnt range");
-    static_assert(4 * 32 * BN * 4 <= NS * STAGE, "the epilogue transpose fits in the stages");
+    static_assert(AHEAD < 64, "vmcnt range");
+    static_assert(4 * 32 * BN * 4 <= R::bytes, "the epilogue transpose fits in the rings");
+    // byte offsets of A stage s and B stage s
+    constexpr auto aoff = [](int s) { return (uint32_t)(JOINT ? s * (R::SA + R::SB) : s * R::SA); };
+    constexpr auto boff = [](int s) {
+        return (uint32_t)(JOINT ? s * (R::SA + R::SB) + R::SA : R::NSA * R::SA + s * R::SB);
+    };
 
     const int lane = threadIdx.x & 63;
     // the wave index is uniform across the wave; saying so keeps the load
@@ -596,8 +615,8 @@ __device__ __forceinline__ void dma_tile(const int8_t* __restrict__ A, const int
     const v4i ra = tile_rsrc(A + m0 * Kb, min<int64_t>(BM, M - m0), Kb);
     const v4i rb = tile_rsrc(B + n0 * Kb, min<int64_t>(BN, N - n0), Kb);
 
-    // load j of wave w fills stage rows [8 (4j + w), 8 (4j + w) + 8), which
-    // are A rows exactly when j < LA
+    // load j of wave w fills rows [8 (4j + w), 8 (4j + w) + 8) of the A stage
+    // (j < LA), or rows [8 (4(j - LA) + w), ...) of the B stage
     // row = 8 (4j + wave) + lane / 8, so (row >> 1) & 7 = (4 (wave & 1) + lane / 16) & 7 for every j
     const int chunk = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
     int voff[L];
@@ -610,19 +629,17 @@ __device__ __forceinline__ void dma_tile(const int8_t* __restrict__ A, const int
     // k an odd multiple of 64 bytes: chunks 4..7 of the last step lie past k
     const bool half_tail = (Kb % kDmaBK) != 0;
     const bool hi_chunk = chunk >= 4;
-    // stages are addressed by byte offset into lds (a uniform value computed
+    // stages are addressed by byte offset into lds (uniform values updated
     // each step, so fragment addresses are one VGPR per substep plus an
     // immediate offset)
-    // load j of step kstep into stage; `skip` (steps past the end) reads zeros
-    auto dma = [&](int j, uint32_t stage, int64_t kstep, bool skip) {
+    // load j of step kstep into A stage sa or B stage sb; `skip` (steps past
+    // the end) reads zeros
+    auto dma = [&](int j, uint32_t sa, uint32_t sb, int64_t kstep, bool skip) {
         const int soff = (int)(kstep * kDmaBK);
-        const uint32_t base = lds_addr(lds) + stage + (uint32_t)wave * 1024u;
+        const uint32_t dst = lds_addr(lds) + (j < LA ? sa + (uint32_t)(j * 4096) : sb + (uint32_t)((j - LA) * 4096)) +
+                             (uint32_t)wave * 1024u;
         const bool cut = skip || (half_tail && kstep == nk - 1 && hi_chunk);
-        dma16(j < LA ? ra : rb, base + (uint32_t)(j * 4096), cut ? kOutOfRange : voff[j], soff);
-    };
-    auto issue = [&](uint32_t stage, int64_t kstep, bool skip) {
-#pragma unroll
-        for (int j = 0; j < L; ++j) dma(j, stage, kstep, skip);
+        dma16(j < LA ? ra : rb, dst, cut ? kOutOfRange : voff[j], soff);
     };
 
     using Acc = typename Op::template acc_t<32>;
@@ -640,21 +657,22 @@ __device__ __forceinline__ void dma_tile(const int8_t* __restrict__ A, const int
     const int b_off = frow * kDmaBK;
     using Frag = typename Op::frag_t;
     Frag fa[2][NFA], fb[2][NFB];  // [substep parity][tile]
-    auto read_frag = [&](uint32_t stage, int ks, int f) {
-        const char* p = lds + stage;
+    auto read_frag = [&](uint32_t sa, uint32_t sb, int ks, int f) {
+        const char* pa = lds + sa;
+        const char* pb = lds + sb;
         if constexpr (Op::KB == 32) {
             const int ch = (c0 ^ (2 * ks)) << 4;
             if (f < NFA)
-                fa[ks & 1][f] = *(const v4i*)(p + (a_off + ch) + f * 32 * kDmaBK);
+                fa[ks & 1][f] = *(const v4i*)(pa + (a_off + ch) + f * 32 * kDmaBK);
             else
-                fb[ks & 1][f - NFA] = *(const v4i*)(p + (b_off + ch) + (BM + (f - NFA) * 32) * kDmaBK);
+                fb[ks & 1][f - NFA] = *(const v4i*)(pb + (b_off + ch) + (f - NFA) * 32 * kDmaBK);
         } else {
             // 64 bytes of K per substep: lane (row, h) takes chunks 4ks + 2h and
             // 4ks + 2h + 1, stored at positions (chunk ^ ((row >> 1) & 7))
             const int sw = (lane >> 1) & 7, h2 = 2 * (lane >> 5);
             const int ch0 = ((4 * ks + h2) ^ sw) << 4, ch1 = ((4 * ks + h2 + 1) ^ sw) << 4;
-            const int base = f < NFA ? a_off + f * 32 * kDmaBK : b_off + (BM + (f - NFA) * 32) * kDmaBK;
-            const v4i lo = *(const v4i*)(p + base + ch0), hi = *(const v4i*)(p + base + ch1);
+            const char* p = f < NFA ? pa + a_off + f * 32 * kDmaBK : pb + b_off + (f - NFA) * 32 * kDmaBK;
+            const v4i lo = *(const v4i*)(p + ch0), hi = *(const v4i*)(p + ch1);
             const Frag v = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             if (f < NFA)
                 fa[ks & 1][f] = v;
@@ -662,48 +680,70 @@ __device__ __forceinline__ void dma_tile(const int8_t* __restrict__ A, const int
                 fb[ks & 1][f - NFA] = v;
         }
     };
-    auto read_frags = [&](uint32_t stage, int ks) {
+    auto read_frags = [&](uint32_t sa, uint32_t sb, int ks) {
 #pragma unroll
-        for (int f = 0; f < NF; ++f) read_frag(stage, ks, f);
+        for (int f = 0; f < NF; ++f) read_frag(sa, sb, ks, f);
     };
     auto publish = [&]() {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
     };
-    // prologue: steps 0 .. NS-2 in flight, then publish step 0
-    issue(0, 0, false);
-    if (NS == 3) issue(STAGE, 1, nk < 2);
-    if (NS == 3) wait_vmcnt<L>();
-    else wait_vmcnt<0>();
+    // stages of steps kb, kb + 1 and (three-deep rings) kb + 2
+    uint32_t ca = aoff(0), na = aoff(1), fla = aoff(2);
+    uint32_t cb = boff(0), nb = boff(1), flb = boff(2);
+    // load o of step kb's issue order: joint stages, every row of step kb + 2
+    // (A rows first); split rings, the shallow ring's rows of step kb + 1,
+    // then the deep ring's rows of step kb + 2, so one in-order wait covers
+    // both stages the next step reads
+    auto load = [&](int o, int64_t kb) {
+        if constexpr (JOINT) {
+            dma(o, fla, fla + R::SA, kb + 2, !(kb + 2 < nk));
+        } else if constexpr (DEEPA) {
+            if (o < LB)
+                dma(LA + o, 0, nb, kb + 1, !(kb + 1 < nk));
+            else
+                dma(o - LB, fla, 0, kb + 2, !(kb + 2 < nk));
+        } else {
+            if (o < LA)
+                dma(o, na, 0, kb + 1, !(kb + 1 < nk));
+            else
+                dma(o, 0, flb, kb + 2, !(kb + 2 < nk));
+        }
+    };
+    // prologue: step 0 and the rows of step 1 that run two steps ahead in
+    // flight, then publish step 0
+#pragma unroll
+    for (int j = 0; j < L; ++j) dma(j, ca, cb, 0, false);
+#pragma unroll
+    for (int j = 0; j < L; ++j)
+        if (JOINT || (DEEPA ? j < LA : j >= LA)) dma(j, na, JOINT ? na + R::SA : nb, 1, nk < 2);
+    wait_vmcnt<AHEAD>();
     publish();
-    read_frags(0, 0);
+    read_frags(ca, cb, 0);
 
     // One step, in a fixed instruction order (sched_barrier between slots):
     // NSUB substeps of NMMA MFMAs; after MFMA m of a substep comes fragment
     // read m of the next substep (m < NF), and across the first NSUB - 1
-    // substeps every DSTRIDE-th slot issues one of the L loads of step
-    // kb + NS - 1 into the stage read during step kb - 1, so the loads queue
-    // behind the matrix cores instead of stalling them. Before the last
-    // substep: wait for step kb + 1 and publish it; the last substep reads
-    // the first fragments of that stage (stale but in bounds after the last
-    // step). Steps past the end load zeros, so every step has the same
+    // substeps every DSTRIDE-th slot issues one of the step's L loads, so the
+    // loads queue behind the matrix cores instead of stalling them. Before the
+    // last substep: wait for step kb + 1 and publish it; the last substep
+    // reads the first fragments of that stage (stale but in bounds after the
+    // last step). Steps past the end load zeros, so every step has the same
     // instruction stream.
     constexpr int DSTRIDE = (NSUB - 1) * NMMA / L > 0 ? (NSUB - 1) * NMMA / L : 1;
     static_assert(Op::KB != 32 || (L - 1) * DSTRIDE < (NSUB - 1) * NMMA, "the loads fit in the first substeps");
     // 64-byte substeps (two per step): the L loads are dealt over the MFMA
     // slots of the first substep, one or two per slot
     constexpr int SLOTS1 = (NSUB - 1) * NMMA;
-    uint32_t cur = 0, nxt = STAGE, fill = (NS - 1) * STAGE;  // stages of kb, kb + 1, kb + NS - 1
     for (int64_t kb = 0; kb < nk; ++kb) {
-        const bool more = kb + NS - 1 < nk;
 #pragma unroll
         for (int ks = 0; ks < NSUB; ++ks) {
             if (ks == NSUB - 1 && kb + 1 < nk) {
-                if (NS == 3) wait_vmcnt<(NS - 2) * L>();
-                else wait_vmcnt<0>();
+                wait_vmcnt<AHEAD>();
                 publish();
             }
-            const uint32_t rstage = ks + 1 < NSUB ? cur : nxt;
+            const uint32_t rsa = ks + 1 < NSUB ? ca : na;
+            const uint32_t rsb = JOINT ? rsa + R::SA : (ks + 1 < NSUB ? cb : nb);
             const int rks = (ks + 1) % NSUB;
 #pragma unroll
             for (int m = 0; m < NMMA; ++m) {
@@ -711,23 +751,26 @@ __device__ __forceinline__ void dma_tile(const int8_t* __restrict__ A, const int
                 // W rows as the first operand: acc[i][j] is the transposed
                 // 32 x 32 block (lane: one output row, four consecutive columns)
                 acc[i][j] = Op::template mfma<32>(fb[ks & 1][j], fa[ks & 1][i], acc[i][j]);
-                if (m < NF) read_frag(rstage, rks, m);
+                if (m < NF) read_frag(rsa, rsb, rks, m);
                 const int slot = ks * NMMA + m;
                 if constexpr (Op::KB == 32) {
-                    if (ks + 1 < NSUB && slot % DSTRIDE == 0 && slot / DSTRIDE < L)
-                        dma(slot / DSTRIDE, fill, kb + NS - 1, !more);
+                    if (ks + 1 < NSUB && slot % DSTRIDE == 0 && slot / DSTRIDE < L) load(slot / DSTRIDE, kb);
                 } else {
 #pragma unroll
                     for (int j = 0; j < L; ++j)
-                        if (ks + 1 < NSUB && (j * SLOTS1) / L == slot) dma(j, fill, kb + NS - 1, !more);
+                        if (ks + 1 < NSUB && (j * SLOTS1) / L == slot) load(j, kb);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        const uint32_t was = cur;
-        cur = nxt;
-        nxt = NS == 3 ? fill : was;
-        fill = was;
+        // rotate the rings (a two-deep ring swaps its stages)
+        const uint32_t wa = ca, wb = cb;
+        ca = na;
+        na = R::NSA == 3 ? fla : wa;
+        fla = wa;
+        cb = nb;
+        nb = R::NSB == 3 ? flb : wb;
+        flb = wb;
     }
     wait_vmcnt<0>();  // zero-fill loads past the end may still be in flight
 
@@ -1107,11 +1150,11 @@ using CfgS128 = Cfg<128, 128, 64, 64, 32>;
 enum TileCfg { kD256, kD224, kD192, kD160, kD128, kS128, kNumCfg, kK16 = kNumCfg };
 constexpr int kCfgBM[kNumCfg + 1] = {256, 256, 256, 256, 256, 128, 64};
 constexpr int kCfgBN[kNumCfg + 1] = {256, 224, 192, 160, 128, 128, 16};
-// relative per-CU throughput of each tile shape, measured on MI355X over the
-// Llama-2 13B/70B prefill shapes (TOPS with many tiles per CU, normalised to
-// 256 x 128; the two-stage widths 192 and 224 are the weakest); used only to
-// rank candidates
-constexpr double kCfgEff[kNumCfg] = {0.97, 0.88, 0.88, 0.95, 1.00, 0.45};
+// relative per-CU throughput of each tile shape, measured on MI355X on the
+// Llama-2 70B MLP products (4096 tokens, many tiles per CU; TOPS normalised to
+// 256 x 128): 256 x 256 with split rings leads by 11 %, the other widths are
+// within 1 % of each other; used only to rank candidates
+constexpr double kCfgEff[kNumCfg] = {1.11, 1.01, 1.00, 0.99, 1.00, 0.45};
 
 template <class C>
 constexpr int threads_of() {
@@ -1243,6 +1286,75 @@ int f8_cfg(int64_t M, int64_t N) {
         if (c == kD256 || cost < best_cost) {
             best_cost = cost;
             best = c;
+        }
+    }
+    return best;
+}
+
+// Predicted duration of a grouped launch of the selected products at tiling
+// c (in tile-area x 128-byte K steps / efficiency units): the tiles are dealt
+// in launch order to the compute unit that frees first, as the dispatcher
+// does, so one product's partial round fills with the next product's tiles.
+// The units' free times are kept as at most kTimes (time, units) groups; past
+// that a group joins the one nearest in time.
+double group_time(const sqk::GemmItem* items, const bool* sel, int count, int c) {
+    constexpr int kTimes = 16;
+    double t[kTimes];
+    int64_t u[kTimes];
+    int ng = 1;
+    t[0] = 0.0;
+    u[0] = cu_count();
+    const double per = (double)kCfgBM[c] * kCfgBN[c] / kCfgEff[c];
+    for (int p = 0; p < count; ++p) {
+        if (!sel[p]) continue;
+        const double d = (double)((items[p].k + kDmaBK - 1) / kDmaBK) * per;
+        int64_t left = tiles_of((TileCfg)c, items[p].m, items[p].n);
+        while (left > 0) {
+            int g = 0;
+            for (int q = 1; q < ng; ++q)
+                if (t[q] < t[g]) g = q;
+            const int64_t take = std::min(left, u[g]);
+            const double nt = t[g] + d;
+            left -= take;
+            u[g] -= take;
+            if (u[g] == 0) {
+                t[g] = t[ng - 1];
+                u[g] = u[ng - 1];
+                --ng;
+            }
+            int h = -1;
+            for (int q = 0; q < ng; ++q)
+                if (t[q] == nt) h = q;
+            if (h < 0 && ng == kTimes) {
+                h = 0;
+                for (int q = 1; q < ng; ++q)
+                    if (std::fabs(t[q] - nt) < std::fabs(t[h] - nt)) h = q;
+            }
+            if (h < 0) {
+                t[ng] = nt;
+                u[ng] = take;
+                ++ng;
+            } else {
+                u[h] += take;
+            }
+        }
+    }
+    double end = 0.0;
+    for (int q = 0; q < ng; ++q) end = std::max(end, t[q]);
+    return end;
+}
+
+// The pipelined tiling of products that share one grouped launch: the width
+// with the least predicted grouped time (for one product, the same choice as
+// choose_cfg among the pipelined widths).
+TileCfg group_cfg(const sqk::GemmItem* items, const bool* sel, int count) {
+    TileCfg best = kD128;
+    double best_t = 0.0;
+    for (int c = kD256; c <= kD128; ++c) {
+        const double t = group_time(items, sel, count, c);
+        if (c == kD256 || t < best_t) {
+            best_t = t;
+            best = (TileCfg)c;
         }
     }
     return best;
@@ -1404,8 +1516,24 @@ int dma_width(TileCfg c) {
     }
 }
 
-// Products that pick the same tile width (and output type and scale
-// storage) share one grouped launch; int8 products too small for the
+// The products that join item i's grouped launch: those not yet launched
+// that take the pipelined tiles (their own choice is a pipelined width) and
+// share its output type and scale storage; returns their common tiling, the
+// one with the least predicted grouped time.
+template <bool kF8>
+TileCfg pipelined_group(const GemmItem* items, int count, int i, const bool* done, bool* sel) {
+    auto width = [](const GemmItem& it) { return dma_width(kF8 ? (TileCfg)f8_cfg(it.m, it.n) : choose_cfg(it.m, it.n)); };
+    const GemmItem& it = items[i];
+    for (int j = 0; j < count; ++j) {
+        const GemmItem& jt = items[j];
+        sel[j] = j == i || (j > i && !done[j] && jt.m != 0 && jt.n != 0 && jt.yt == it.yt && jt.h == it.h &&
+                            width(jt) != 0);
+    }
+    return group_cfg(items, sel, count);
+}
+
+// Products that take the pipelined tiles (and share the output type and
+// scale storage) share one grouped launch, at one width for all of them; int8 products too small for the
 // pipelined tiles run as single launches (FP8 products always take a
 // pipelined width).
 template <class Op, class AccT>
@@ -1502,15 +1630,16 @@ hipError_t gemm_batched_impl(const GemmItem* items, int count, hipStream_t strea
             if (e != hipSuccess) return e;
             continue;
         }
+        bool sel[kMaxBatch] = {};
+        const int gtn = dma_width(pipelined_group<kF8>(items, count, i, done, sel));
         GemmTable tab{};
         int64_t blocks = 0;
         for (int j = i; j < count; ++j) {
+            if (!sel[j]) continue;
             const GemmItem& jt = items[j];
-            if (j > i && (done[j] || jt.m == 0 || jt.n == 0 || jt.yt != it.yt || jt.h != it.h || width(jt) != tn))
-                continue;
             done[j] = true;
             const int c = tab.count++;
-            const int64_t tiles_m = (jt.m + kDmaBM - 1) / kDmaBM, tiles_n = (jt.n + 32 * tn - 1) / (32 * tn);
+            const int64_t tiles_m = (jt.m + kDmaBM - 1) / kDmaBM, tiles_n = (jt.n + 32 * gtn - 1) / (32 * gtn);
             tab.first[c] = (int32_t)blocks;
             tab.A[c] = jt.xq;
             tab.B[c] = jt.wq;
@@ -1529,7 +1658,7 @@ hipError_t gemm_batched_impl(const GemmItem* items, int count, hipStream_t strea
         tab.first[tab.count] = (int32_t)blocks;
         const bool bf16 = it.yt == kBF16;
         hipError_t e = hipErrorInvalidValue;
-        switch (tn) {
+        switch (gtn) {
             case 8: e = launch_grouped<Op, AccT, 8>(tab, blocks, bf16, it.h, stream); break;
             case 7: e = launch_grouped<Op, AccT, 7>(tab, blocks, bf16, it.h, stream); break;
             case 6: e = launch_grouped<Op, AccT, 6>(tab, blocks, bf16, it.h, stream); break;
@@ -1594,6 +1723,27 @@ void gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n) {
     const TileCfg c = choose_cfg(m, n);
     *block_m = kCfgBM[c];
     *block_n = kCfgBN[c];
+}
+
+void gemm_batched_tiling(const GemmItem* items, int count, int* block_m, int* block_n) {
+    bool done[kMaxBatch] = {};
+    for (int i = 0; i < count; ++i) {
+        if (done[i]) continue;
+        const GemmItem& it = items[i];
+        if (it.m <= kSkinnyMaxM || it.n == 0 || choose_cfg(it.m, it.n) == kS128) {
+            done[i] = true;
+            gemm_tiling(it.m, it.n, &block_m[i], &block_n[i]);
+            continue;
+        }
+        bool sel[kMaxBatch] = {};
+        const TileCfg c = pipelined_group<false>(items, count, i, done, sel);
+        for (int j = i; j < count; ++j)
+            if (sel[j]) {
+                done[j] = true;
+                block_m[j] = kCfgBM[c];
+                block_n[j] = kCfgBN[c];
+            }
+    }
 }
 
 int64_t gemm_sse_slots(int64_t m, int64_t n) { return tiles_of(choose_cfg(m, n), m, n); }

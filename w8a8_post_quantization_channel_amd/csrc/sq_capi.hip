@@ -626,6 +626,21 @@ sq_status sq_gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n) {
     return SQ_OK;
 }
 
+sq_status sq_gemm_batched_tiling(int count, const int64_t* m, const int64_t* n, const int64_t* k, int* block_m,
+                                 int* block_n) {
+    if (!m || !n || !k || !block_m || !block_n) return SQ_ERR_NULL;
+    if (count < 1 || count > SQ_MAX_BATCH) return SQ_ERR_SHAPE;
+    sqk::GemmItem items[SQ_MAX_BATCH] = {};
+    for (int i = 0; i < count; ++i) {
+        if (m[i] < 0 || n[i] < 0 || k[i] < 1) return SQ_ERR_SHAPE;
+        items[i].m = m[i];
+        items[i].n = n[i];
+        items[i].k = k[i];
+    }
+    sqk::gemm_batched_tiling(items, count, block_m, block_n);
+    return SQ_OK;
+}
+
 sq_status sq_alpha_search_workspace(int n_batches, int64_t rows_per_batch, int64_t n, int64_t k, int n_alphas,
                                     size_t* bytes) {
     if (!bytes) return SQ_ERR_NULL;

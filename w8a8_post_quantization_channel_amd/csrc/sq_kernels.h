@@ -170,6 +170,9 @@ hipError_t gemm_fp8_batched(const GemmItem* items, int count, hipStream_t stream
 
 // Block tile (rows, columns) the GEMM uses for an m x n output.
 void gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n);
+// the tile of each item of a gemm_dequant_batched call (items of one output
+// type and scale storage)
+void gemm_batched_tiling(const GemmItem* items, int count, int* block_m, int* block_n);
 
 // Number of fp64 partial slots gemm_sse writes for an m x n problem.
 int64_t gemm_sse_slots(int64_t m, int64_t n);

@@ -221,6 +221,38 @@ def test_gemm_batched():
         assert_bitexact(f"y item {i}", _h(ys[i]), ORACLE.dequant(racc, a[0], ws, bf16=bf16))
 
 
+def test_gemm_grouped_split_rings():
+    """One grouped launch on 256 x 256 tiles (split LDS rings: the weight panel
+    three stages deep, the activation panel two), chosen for the group: ragged
+    m and n in every product, K of 1.5 to 5.5 steps of 128 bytes (a half last
+    step in each), some items with the int32 accumulator; every output
+    bit-exact against the oracle."""
+    import torch
+    cases = [(1900, 5000, 320, True), (1900, 13800, 192, False), (1900, 13800, 448, True), (700, 5000, 704, False)]
+    assert set(capi.sq_gemm_batched_tiling([(m, n, k) for m, n, k, _ in cases])) == {(256, 256)}
+    g = synth.rng(4810)
+    xqs, wqs, scs, wss, ys, accs, host = [], [], [], [], [], [], []
+    for m, n, k, with_acc in cases:
+        xq = g.integers(-127, 128, (m, k), dtype=np.int8)
+        wq = g.integers(-127, 128, (n, k), dtype=np.int8)
+        ws = g.uniform(1e-4, 1e-2, n).astype(np.float32)
+        a = np.array([g.uniform(0.005, 0.05), 0, 0, 0], np.float32)
+        host.append((xq, wq, ws, a))
+        xqs.append(_t(xq))
+        wqs.append(_t(wq))
+        scs.append(_t(a))
+        wss.append(_t(ws))
+        ys.append(torch.empty((m, n), dtype=torch.bfloat16, device=dev()))
+        accs.append(torch.empty((m, n), dtype=torch.int32, device=dev()) if with_acc else None)
+    capi.sq_w8a8_gemm_batched(xqs, wqs, scs, wss, ys, accs)
+    torch.cuda.synchronize()
+    for i, ((m, n, k, with_acc), (xq, wq, ws, a)) in enumerate(zip(cases, host)):
+        racc = ORACLE.gemm_i32(xq, wq)
+        if with_acc:
+            assert_bitexact(f"acc item {i}", _h(accs[i]), racc)
+        assert_bitexact(f"y item {i}", _h(ys[i]), ORACLE.dequant(racc, a[0], ws, bf16=True))
+
+
 @pytest.mark.parametrize("f16", [False, True])
 def test_gemm_batched_decode_grouped(f16):
     """Decode-sized products in one batched call: those with m <= 4 and the

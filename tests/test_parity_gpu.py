@@ -190,6 +190,9 @@ def test_quant_act_ties():
 GEMM_CASES = [(1, 16, 64), (5, 48, 1088), (129, 257, 320), (300, 600, 2048), (512, 8192, 128),
               (1024, 8192, 256), (2100, 4112, 192), (2048, 7168, 64), (2048, 11008, 128), (4096, 4096, 64),
               (4000, 4100, 64), (1000, 11008, 320),
+              # the split LDS rings of the wide tiles over several K steps, ragged m and n and a
+              # half last step: 256 x 256 (1100 x 12000) and 256 x 224 (1500 x 9000)
+              (1100, 12000, 704), (1500, 9000, 448),
               # decode widths: 17-32 and 33-64 rows, 8-wave blocks (>= 512 column blocks) and
               # 16-wave blocks, K steps not a multiple of waves x steps in flight
               (24, 8200, 192), (17, 1000, 4160), (40, 8192, 320), (64, 300, 704), (9, 8208, 1344),

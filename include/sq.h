@@ -355,8 +355,9 @@ sq_status sq_gemm_tiling(int64_t m, int64_t n, int* block_m, int* block_n);
  * these shapes uses, all items of one output type and scale storage (items
  * that differ in either are grouped apart; query each group on its own).
  * Products that take the pipelined tiles share one width, chosen for the
- * group, so an item's tile here can differ from its sq_gemm_tiling; the
- * others report their sq_gemm_tiling. Launches nothing; the result does not
+ * group (on 256 x 256, up to the last three of them may take 256 x 128), so
+ * an item's tile here can differ from its sq_gemm_tiling; the others report
+ * their sq_gemm_tiling. Launches nothing; the result does not
  * depend on the data (the int32 sums are exact in any order).
  *   count             1 <= count <= SQ_MAX_BATCH (SQ_ERR_SHAPE otherwise)
  *   m, n, k           host arrays of count shapes (m, n >= 0, k > 0)
@@ -429,10 +430,12 @@ sq_status sq_alpha_search(const void* const* x_batches, sq_dtype xt, int n_batch
  * sq_w8a8_gemm_batched [pwwt §3.1]: y[i] (type yt[i]) and, when acc_out is
  *   not NULL and acc_out[i] is not NULL, acc_out[i] from xq[i] [m[i], k[i]],
  *   wq[i] [n[i], k[i]], act_scale[i], w_scale[i]. Products that take the
- *   pipelined tiles and share the output type share one launch at one tile
- *   width (the next product's tiles start as compute units free up; the width
- *   is the one with the least predicted time for the whole group, reported by
- *   sq_gemm_batched_tiling); products with m <= 4 (decode: q, k and
+ *   pipelined tiles and share the output type share one launch (the next
+ *   product's tiles start as compute units free up) at one tile width, the
+ *   one with the least predicted time for the whole group; a launch on
+ *   256 x 256 tiles may run up to its last three products on 256 x 128 when
+ *   that evens out its last round (sq_gemm_batched_tiling reports each
+ *   product's tile); products with m <= 4 (decode: q, k and
  *   v, or gate and up) share one vector-ALU launch when their row class
  *   (m rounded up to 1, 2 or 4), K chunk class and output type match;
  *   products with 4 < m <= 64 share one skinny launch when their skinny

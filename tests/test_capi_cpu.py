@@ -134,12 +134,16 @@ def test_gemm_tiling_query(lib):
 
 
 def test_gemm_batched_tiling_query(lib):
-    """One width for the products of a grouped launch, chosen for the group;
-    decode and small products keep their single-call tiles; argument errors
-    are statuses."""
+    """One width for the products of a grouped launch, chosen for the group,
+    except that a 256 x 256 launch may run up to its last three products (never
+    all of them) on 256 x 128 tiles; decode and small products keep their
+    single-call tiles; argument errors are statuses."""
     blk = [(2048, 5120, 5120)] * 4 + [(2048, 13824, 5120)] * 2 + [(2048, 5120, 13824)]
-    tiles = capi.sq_gemm_batched_tiling(blk)
-    assert len(set(tiles)) == 1 and tiles[0][0] == 256, tiles
+    for order in (blk, blk[::-1]):
+        tiles = capi.sq_gemm_batched_tiling(order)
+        assert tiles[0] == (256, 256) and set(tiles) <= {(256, 256), (256, 128)}, tiles
+        narrow = [i for i, t in enumerate(tiles) if t == (256, 128)]
+        assert len(narrow) <= 3 and narrow == list(range(len(tiles) - len(narrow), len(tiles))), tiles
     # one product: the single call's choice
     for m, n, k in [(2048, 5120, 5120), (4096, 8192, 8192), (300, 600, 2048), (16, 4096, 4096), (1, 4096, 4096)]:
         assert capi.sq_gemm_batched_tiling([(m, n, k)]) == [capi.sq_gemm_tiling(m, n)]

@@ -841,16 +841,27 @@ struct GemmTable {
     void* acc_out[sqk::kMaxBatch];  // int32 (int8 codes) or fp32 (e4m3 codes) accumulators, or NULL
     int64_t M[sqk::kMaxBatch], N[sqk::kMaxBatch], Kb[sqk::kMaxBatch];
     int32_t tiles_m[sqk::kMaxBatch], tiles_n[sqk::kMaxBatch];
+    int32_t tn[sqk::kMaxBatch];  // the item's tile width / 32 (grouped launches with a second width)
 };
 
-template <class Op, int TN, bool kBF16Out, class AccT, bool kH>
+template <class Op, int TN, bool kBF16Out, class AccT, bool kH, int TN2 = 0>
 __global__ __launch_bounds__(256) void gemm_dma_grouped_kernel(const GemmTable tab) {
-    __shared__ __attribute__((aligned(1024))) char lds[dma_lds_bytes<TN>()];
+    __shared__ __attribute__((aligned(1024))) char
+        lds[TN2 != 0 && dma_lds_bytes<TN2>() > dma_lds_bytes<TN>() ? dma_lds_bytes<TN2>() : dma_lds_bytes<TN>()];
     const int i = sqd::item_of(tab.first, tab.count, blockIdx.x);
     const int b = blockIdx.x - tab.first[i], ntiles = tab.tiles_m[i] * tab.tiles_n[i];
     if (b >= ntiles) return;
     using Epi = EpiDequant<kBF16Out, AccT, kH>;
     Epi epi{tab.act_scale[i], tab.w_scale[i], tab.y[i], (AccT*)tab.acc_out[i], tab.M[i], tab.N[i], 0.0f};
+    if constexpr (TN2 != 0) {
+        // items on the second (narrower) width: the launch's last products,
+        // so that its final round of tiles drains more evenly
+        if (tab.tn[i] == TN2) {
+            dma_tile<Op, TN2, Epi>(tab.A[i], tab.B[i], tab.M[i], tab.N[i], tab.Kb[i], tab.tiles_m[i], tab.tiles_n[i],
+                                   xcd_tile(b, ntiles), epi, lds);
+            return;
+        }
+    }
     dma_tile<Op, TN, Epi>(tab.A[i], tab.B[i], tab.M[i], tab.N[i], tab.Kb[i], tab.tiles_m[i], tab.tiles_n[i],
                           xcd_tile(b, ntiles), epi, lds);
 }
@@ -1297,16 +1308,17 @@ int f8_cfg(int64_t M, int64_t N) {
 // does, so one product's partial round fills with the next product's tiles.
 // The units' free times are kept as at most kTimes (time, units) groups; past
 // that a group joins the one nearest in time.
-double group_time(const sqk::GemmItem* items, const bool* sel, int count, int c) {
+double group_time(const sqk::GemmItem* items, const bool* sel, int count, const int* cfg) {
     constexpr int kTimes = 16;
     double t[kTimes];
     int64_t u[kTimes];
     int ng = 1;
     t[0] = 0.0;
     u[0] = cu_count();
-    const double per = (double)kCfgBM[c] * kCfgBN[c] / kCfgEff[c];
     for (int p = 0; p < count; ++p) {
         if (!sel[p]) continue;
+        const int c = cfg[p];
+        const double per = (double)kCfgBM[c] * kCfgBN[c] / kCfgEff[c];
         const double d = (double)((items[p].k + kDmaBK - 1) / kDmaBK) * per;
         int64_t left = tiles_of((TileCfg)c, items[p].m, items[p].n);
         while (left > 0) {
@@ -1351,12 +1363,52 @@ TileCfg group_cfg(const sqk::GemmItem* items, const bool* sel, int count) {
     TileCfg best = kD128;
     double best_t = 0.0;
     for (int c = kD256; c <= kD128; ++c) {
-        const double t = group_time(items, sel, count, c);
+        int cfg[sqk::kMaxBatch];
+        for (int p = 0; p < count; ++p) cfg[p] = c;
+        const double t = group_time(items, sel, count, cfg);
         if (c == kD256 || t < best_t) {
             best_t = t;
             best = (TileCfg)c;
         }
     }
+    return best;
+}
+
+// A launch on 256 x 256 tiles may run its last selected products on 256 x 128
+// tiles (the kernel's second width), so that its final round of tiles drains
+// more evenly: the number of last products to narrow (0 to 3) with the least
+// predicted grouped time; cfg receives every selected item's tiling.
+int group_tail(const sqk::GemmItem* items, const bool* sel, int count, TileCfg main, int* cfg) {
+    for (int p = 0; p < count; ++p) cfg[p] = main;
+    if (main != kD256) return 0;
+    double best_t = group_time(items, sel, count, cfg);
+    int best = 0;
+    for (int j = 1; j <= 3; ++j) {
+        int trial[sqk::kMaxBatch];
+        int left = j, nsel = 0;
+        for (int p = count - 1; p >= 0; --p) {
+            trial[p] = main;
+            if (sel[p]) {
+                ++nsel;
+                if (left > 0) {
+                    trial[p] = kD128;
+                    --left;
+                }
+            }
+        }
+        if (nsel <= j) break;  // at least one product keeps the main width
+        const double t = group_time(items, sel, count, trial);
+        if (t < best_t) {
+            best_t = t;
+            best = j;
+        }
+    }
+    int left = best;
+    for (int p = count - 1; p >= 0 && left > 0; --p)
+        if (sel[p]) {
+            cfg[p] = kD128;
+            --left;
+        }
     return best;
 }
 
@@ -1423,24 +1475,25 @@ __global__ __launch_bounds__(256) void ref_gemm_f32_kernel(const float* __restri
 
 namespace sqk {
 
-template <class Op, class AccT, int TN>
+// TN2: a second tile width some items of the launch take (0: none)
+template <class Op, class AccT, int TN, int TN2 = 0>
 hipError_t launch_grouped(const GemmTable& tab, int64_t blocks, bool bf16, bool h, hipStream_t stream) {
     const dim3 grid((unsigned)blocks), block(256);
     if constexpr (std::is_same<Op, OpI8>::value) {
         if (h) {
             if (bf16)
-                gemm_dma_grouped_kernel<Op, TN, true, AccT, true><<<grid, block, 0, stream>>>(tab);
+                gemm_dma_grouped_kernel<Op, TN, true, AccT, true, TN2><<<grid, block, 0, stream>>>(tab);
             else
-                gemm_dma_grouped_kernel<Op, TN, false, AccT, true><<<grid, block, 0, stream>>>(tab);
+                gemm_dma_grouped_kernel<Op, TN, false, AccT, true, TN2><<<grid, block, 0, stream>>>(tab);
             return hipGetLastError();
         }
     } else if (h) {
         return hipErrorInvalidValue;  // binary16 scales are for int8 codes
     }
     if (bf16)
-        gemm_dma_grouped_kernel<Op, TN, true, AccT, false><<<grid, block, 0, stream>>>(tab);
+        gemm_dma_grouped_kernel<Op, TN, true, AccT, false, TN2><<<grid, block, 0, stream>>>(tab);
     else
-        gemm_dma_grouped_kernel<Op, TN, false, AccT, false><<<grid, block, 0, stream>>>(tab);
+        gemm_dma_grouped_kernel<Op, TN, false, AccT, false, TN2><<<grid, block, 0, stream>>>(tab);
     return hipGetLastError();
 }
 
@@ -1631,7 +1684,10 @@ hipError_t gemm_batched_impl(const GemmItem* items, int count, hipStream_t strea
             continue;
         }
         bool sel[kMaxBatch] = {};
-        const int gtn = dma_width(pipelined_group<kF8>(items, count, i, done, sel));
+        int cfg[kMaxBatch];
+        const TileCfg main = pipelined_group<kF8>(items, count, i, done, sel);
+        const int gtn = dma_width(main);
+        const bool mixed = group_tail(items, sel, count, main, cfg) > 0;
         GemmTable tab{};
         int64_t blocks = 0;
         for (int j = i; j < count; ++j) {
@@ -1639,7 +1695,9 @@ hipError_t gemm_batched_impl(const GemmItem* items, int count, hipStream_t strea
             const GemmItem& jt = items[j];
             done[j] = true;
             const int c = tab.count++;
-            const int64_t tiles_m = (jt.m + kDmaBM - 1) / kDmaBM, tiles_n = (jt.n + 32 * gtn - 1) / (32 * gtn);
+            const int tnj = dma_width((TileCfg)cfg[j]);
+            const int64_t tiles_m = (jt.m + kDmaBM - 1) / kDmaBM, tiles_n = (jt.n + 32 * tnj - 1) / (32 * tnj);
+            tab.tn[c] = tnj;
             tab.first[c] = (int32_t)blocks;
             tab.A[c] = jt.xq;
             tab.B[c] = jt.wq;
@@ -1659,7 +1717,10 @@ hipError_t gemm_batched_impl(const GemmItem* items, int count, hipStream_t strea
         const bool bf16 = it.yt == kBF16;
         hipError_t e = hipErrorInvalidValue;
         switch (gtn) {
-            case 8: e = launch_grouped<Op, AccT, 8>(tab, blocks, bf16, it.h, stream); break;
+            case 8:
+                e = mixed ? launch_grouped<Op, AccT, 8, 4>(tab, blocks, bf16, it.h, stream)
+                          : launch_grouped<Op, AccT, 8>(tab, blocks, bf16, it.h, stream);
+                break;
             case 7: e = launch_grouped<Op, AccT, 7>(tab, blocks, bf16, it.h, stream); break;
             case 6: e = launch_grouped<Op, AccT, 6>(tab, blocks, bf16, it.h, stream); break;
             case 5: e = launch_grouped<Op, AccT, 5>(tab, blocks, bf16, it.h, stream); break;
@@ -1736,12 +1797,13 @@ void gemm_batched_tiling(const GemmItem* items, int count, int* block_m, int* bl
             continue;
         }
         bool sel[kMaxBatch] = {};
-        const TileCfg c = pipelined_group<false>(items, count, i, done, sel);
+        int cfg[kMaxBatch];
+        group_tail(items, sel, count, pipelined_group<false>(items, count, i, done, sel), cfg);
         for (int j = i; j < count; ++j)
             if (sel[j]) {
                 done[j] = true;
-                block_m[j] = kCfgBM[c];
-                block_n[j] = kCfgBN[c];
+                block_m[j] = kCfgBM[cfg[j]];
+                block_n[j] = kCfgBN[cfg[j]];
             }
     }
 }
